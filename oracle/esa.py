@@ -1,0 +1,156 @@
+"""ESA (Efficient Selective Attention): compression, importance, neighbour
+influence, top-k token selection and attention over the fused parts.
+
+Source: ESA write-up (hlszyjy.com/post/6872.html), the paragraphs on
+token-level selection, the four-part token split with chunked prefill,
+merging of heads, the one-layer compression MLP, score correction and
+neighbour influence; the re-post (qqssy.cn) repeats them. The page's text
+keeps the lead-in of each formula but drops the formulas themselves, so the
+steps marked READING below are this library's stated definitions.
+
+One sequence, chunk C = [c0, c0 + m) of queries (decode: m = 1, c0 = T - 1),
+0-based positions:
+
+1. Partition (four parts; READING): initial I = [0, min(n_init, c0)); local
+   L = the W tokens just before the chunk, [max(n_init, c0 - W), c0); middle
+   M = [n_init, max(n_init, c0 - W)); the chunk itself attends causally.
+   Each query therefore sees at least W previous raw tokens, with the window
+   aligned to the chunk (as the CCA write-up's locality module aligns its
+   window to its group size).
+2. Compression (one-layer MLP; READING: a single affine map, no activation):
+   q~_i = Wq concat_h(q_i^h) + bq kept in float64; the compressed key cache
+   holds k~_j = bf16(Wk concat_h(k_j^h) + bk), rounded to nearest even.
+   Merging the heads into one 4096-wide vector is the write-up's head
+   merging: one score, one selection for all heads.
+3. Raw score s_ij = <q~_i, k~_j> for i in C, j in M.
+4. Correction (READING; the formula is dropped, the text says it keeps the
+   relative size of scores and stops one token from dominating):
+   s^_ij = max(s_ij - max_j' s_ij', -clip).
+5. Importance u_j = sum_i s^_ij over all queries of the chunk ("takes every
+   current query into account"); decode has one query.
+6. Neighbour influence (READING; the formula is dropped, the text says a
+   token's score is also shaped by the tokens around it and that a larger
+   setting favours longer segments): u'_j = max{u_t : t in M, |t - j| <= r}.
+7. Top-k: the min(k, |M|) largest u'_j, ties to the smaller position,
+   returned in ascending order.
+8. Attention: query t attends I u S u L u [c0, t], one joint softmax per
+   head with the same S for every head (global part I u S and window part
+   L u chunk fused, see oracle.attention.merge).
+
+Parity: steps 1-3 and 5, 7, 8 are pinned by CPU tests (k >= |M| equals dense
+causal attention; clip = inf and r = 0 reduce selection to one matrix-vector
+product and a sort; exhaustive sort on tiny inputs; maximum_filter1d for the
+neighbour step; bf16 rounding against torch). Steps 4 and 6 are pinned only
+against this module's own READING (special cases clip -> 0, r = 0 and
+plateau structure): their agreement with the original ESA formulas is
+parity unpinned, since the pages do not carry those formulas.
+"""
+import numpy as np
+
+from .attention import attend_heads
+from .numerics import round_to_bf16
+
+
+def partition(c0, n_init, window):
+    """Returns (I, M, L) as numpy index ranges for a chunk starting at c0."""
+    I = np.arange(0, min(n_init, c0))
+    if c0 > n_init:
+        lstart = max(n_init, c0 - window)
+        M = np.arange(n_init, lstart)
+        L = np.arange(lstart, c0)
+    else:
+        M = np.arange(0)
+        L = np.arange(0)
+    return I, M, L
+
+
+def compress(x, W, b=None):
+    """x [n, D] (concatenated heads), W [d_c, D] -> [n, d_c] in float64."""
+    out = np.asarray(x, np.float64) @ np.asarray(W, np.float64).T
+    if b is not None:
+        out = out + np.asarray(b, np.float64)
+    return out
+
+
+def key_cache(k, Wk, bk=None):
+    """k [T, H, d] -> compressed key cache [T, d_c], rounded to bf16."""
+    T = k.shape[0]
+    return round_to_bf16(compress(np.asarray(k, np.float64).reshape(T, -1), Wk, bk))
+
+
+def importance(qc, kc_mid, clip, row_chunk=256):
+    """qc [m, d_c], kc_mid [n_M, d_c] -> (u [n_M], rowmax [m]).
+    Steps 3-5: u_j = sum_i max(s_ij - max_j' s_ij', -clip)."""
+    qc = np.asarray(qc, np.float64)
+    kc_mid = np.asarray(kc_mid, np.float64)
+    n_mid = kc_mid.shape[0]
+    u = np.zeros(n_mid)
+    rowmax = np.full(qc.shape[0], -np.inf)
+    if n_mid == 0:
+        return u, rowmax
+    for i0 in range(0, qc.shape[0], row_chunk):
+        s = qc[i0:i0 + row_chunk] @ kc_mid.T
+        mrow = s.max(axis=1)
+        rowmax[i0:i0 + row_chunk] = mrow
+        u += np.maximum(s - mrow[:, None], -clip).sum(axis=0)
+    return u, rowmax
+
+
+def neighbour(u, radius):
+    """Step 6: u'_j = max of u over the positions within distance r of j that
+    lie inside the middle part."""
+    u = np.asarray(u, np.float64)
+    out = u.copy()
+    n = u.shape[0]
+    for off in range(1, radius + 1):
+        if off >= n:
+            break
+        out[:-off] = np.maximum(out[:-off], u[off:])
+        out[off:] = np.maximum(out[off:], u[:-off])
+    return out
+
+
+def top_k(scores, k):
+    """Step 7: indices of the min(k, n) largest scores, ties to the smaller
+    index, ascending. Full sort on (-score, index)."""
+    scores = np.asarray(scores, np.float64)
+    order = np.lexsort((np.arange(scores.shape[0]), -scores))
+    return np.sort(order[:min(k, scores.shape[0])])
+
+
+def select(q, Wq, bq, kc_cache, c0, n_init, window, topk, radius, clip):
+    """Selection for one sequence and chunk.
+
+    q [m, H, d] the chunk's queries, kc_cache [T, d_c] the compressed key
+    cache (bf16 values). Returns (sel: absolute positions ascending,
+    scores u' over M, importance u over M, rowmax [m]).
+    """
+    m = q.shape[0]
+    _, M, _ = partition(c0, n_init, window)
+    qc = compress(np.asarray(q, np.float64).reshape(m, -1), Wq, bq)
+    u, rowmax = importance(qc, np.asarray(kc_cache, np.float64)[M], clip)
+    up = neighbour(u, radius)
+    sel = M[top_k(up, topk)] if M.size else np.zeros(0, dtype=np.int64)
+    return sel, up, u, rowmax
+
+
+def key_list(sel, c0, n_init, window, t):
+    I, _, L = partition(c0, n_init, window)
+    return np.concatenate([I, np.asarray(sel, np.int64), L, np.arange(c0, t + 1)])
+
+
+def attend(q, K, V, sel, c0, n_init, window, scale, rows=None):
+    """Step 8 for one sequence. q [m, H, d] (chunk rows), K/V [T, H, d].
+    rows: chunk-relative query indices (default all). Returns o [len(rows),
+    H, d], lse [len(rows), H]."""
+    m, H, d = q.shape
+    if rows is None:
+        rows = list(range(m))
+    o = np.zeros((len(rows), H, V.shape[2]))
+    lse = np.zeros((len(rows), H))
+    for r, i in enumerate(rows):
+        idx = key_list(sel, c0, n_init, window, c0 + i)
+        o[r], lse[r] = attend_heads(np.asarray(q[i], np.float64),
+                                    np.asarray(K[idx], np.float64),
+                                    np.asarray(V[idx], np.float64), scale)
+    return o, lse

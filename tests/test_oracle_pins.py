@@ -1,0 +1,450 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle function to a closed form, a special case that
+reduces to a library routine (torch's float64 scaled_dot_product_attention,
+numpy sorts, scipy's maximum filter, torch's bfloat16 cast), a brute-force
+property check on tiny inputs, or a number printed on the source pages
+(tests/golden/pages_numbers.json). No GPU is needed.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.ndimage as ndi
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+from oracle import attention as oatt
+from oracle import esa as oesa
+from oracle import moba as omoba
+from oracle.numerics import round_to_bf16
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def sdpa_causal(q, k, v, scale):
+    """Library dense causal attention in float64. q [N,H,d], k/v [N,Hkv,d]
+    (KV heads repeated contiguously for grouped queries)."""
+    hq, hkv = q.shape[1], k.shape[1]
+    rep = hq // hkv
+    Q = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None]
+    K = torch.from_numpy(np.ascontiguousarray(np.repeat(k, rep, axis=1).transpose(1, 0, 2)))[None]
+    V = torch.from_numpy(np.ascontiguousarray(np.repeat(v, rep, axis=1).transpose(1, 0, 2)))[None]
+    o = F.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=scale)
+    return o[0].numpy().transpose(1, 0, 2)
+
+
+def sdpa_masked(q, k, v, mask, scale):
+    """mask [H, N, N] boolean (True = attend)."""
+    hq, hkv = q.shape[1], k.shape[1]
+    rep = hq // hkv
+    Q = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None]
+    K = torch.from_numpy(np.ascontiguousarray(np.repeat(k, rep, axis=1).transpose(1, 0, 2)))[None]
+    V = torch.from_numpy(np.ascontiguousarray(np.repeat(v, rep, axis=1).transpose(1, 0, 2)))[None]
+    o = F.scaled_dot_product_attention(Q, K, V, attn_mask=torch.from_numpy(mask)[None], scale=scale)
+    return o[0].numpy().transpose(1, 0, 2)
+
+
+# ------------------------------------------------------------------ generator
+def test_generator_torch_matches_numpy_integer_stream():
+    base = synth.gen.stream_base(7, 3)
+    c = np.arange(1000, 6000, dtype=np.uint64)
+    ref = synth.splitmix64_np(base, c).view(np.int64)
+    t = torch.from_numpy(c.astype(np.int64))
+    got = synth.gen._mix_t(synth.gen._signed(base) + (t + 1) * synth.gen._signed(synth.gen.GOLDEN))
+    assert np.array_equal(ref, got.numpy())
+
+
+def test_generator_known_splitmix_value():
+    # splitmix64 of state 0 after one increment: first output of the
+    # published generator seeded with 0 is 0xE220A8397B1DCDAF.
+    assert int(synth.splitmix64_np(0, np.array([0], dtype=np.uint64))[0]) == 0xE220A8397B1DCDAF
+
+
+def test_generator_rounded_outputs_agree_and_are_normal():
+    a = synth.normal_np(11, 2, 200000, start=99)
+    b = synth.normal(11, 2, (200000,), torch.float32, start=99).numpy().astype(np.float64)
+    assert np.array_equal(a.astype(np.float32).astype(np.float64), b)
+    assert abs(a.mean()) < 0.01 and abs(a.std() - 1) < 0.01
+
+
+# ------------------------------------------------------------------ rounding
+def test_round_to_bf16_matches_torch_on_f32_exact_values():
+    x = rng(0).standard_normal(100000).astype(np.float32)
+    # include exact ties at bf16 half-ulp
+    ties = (np.arange(1, 2000, dtype=np.float32) * 2 + 1) * np.float32(2.0 ** -9) + 1
+    x = np.concatenate([x, ties.astype(np.float32), -ties.astype(np.float32), [0.0]])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = round_to_bf16(x.astype(np.float64))
+    assert np.array_equal(ref, got)
+
+
+# ------------------------------------------------------------------ attention
+def test_attend_matches_library_dense_causal():
+    r = rng(1)
+    N, H, d = 37, 3, 16
+    q, k, v = (r.standard_normal((N, H, d)) for _ in range(3))
+    ref = sdpa_causal(q, k, v, 0.3)
+    for t in range(N):
+        o, _ = oatt.attend_heads(q[t], k[:t + 1], v[:t + 1], 0.3)
+        np.testing.assert_allclose(o, ref[t], rtol=1e-12, atol=1e-12)
+
+
+def test_attend_closed_forms():
+    r = rng(2)
+    V = r.standard_normal((9, 5))
+    q = r.standard_normal(4)
+    K = np.tile(r.standard_normal(4), (9, 1))          # identical keys
+    o, lse = oatt.attend(q, K, V, 0.7)
+    np.testing.assert_allclose(o, V.mean(0), atol=1e-13)
+    np.testing.assert_allclose(lse, 0.7 * K[0] @ q + math.log(9), atol=1e-12)
+    o, lse = oatt.attend(q, r.standard_normal((9, 4)), V, 0.0)   # scale 0
+    np.testing.assert_allclose(o, V.mean(0), atol=1e-13)
+    np.testing.assert_allclose(lse, math.log(9), atol=1e-13)
+    K = r.standard_normal((9, 4)) * 1e-3
+    K[4] = q * 1e3                                      # one dominant key
+    o, _ = oatt.attend(q, K, V, 1.0)
+    np.testing.assert_allclose(o, V[4], atol=1e-12)
+    o, lse = oatt.attend(q, np.zeros((0, 4)), V[:0], 1.0)
+    assert np.isneginf(lse) and np.all(o == 0)
+
+
+def test_merge_of_disjoint_splits_equals_union():
+    r = rng(3)
+    q = r.standard_normal(8)
+    K = r.standard_normal((50, 8))
+    V = r.standard_normal((50, 6))
+    full = oatt.attend(q, K, V, 0.5)
+    for trial in range(5):
+        perm = r.permutation(50)
+        cuts = sorted(r.choice(np.arange(1, 50), size=3, replace=False))
+        parts = [oatt.attend(q, K[s], V[s], 0.5) for s in np.split(perm, cuts)]
+        parts.append(oatt.attend(q, K[:0], V[:0], 0.5))   # an empty part
+        o, lse = oatt.merge(parts)
+        np.testing.assert_allclose(o, full[0], atol=1e-12)
+        np.testing.assert_allclose(lse, full[1], atol=1e-12)
+
+
+# ------------------------------------------------------------------ MoBA
+def test_moba_block_means_closed_form():
+    N, B = 40, 8
+    k = np.zeros((N, 2, 3))
+    for t in range(N):
+        k[t, 0, :] = t // B            # constant per block
+        k[t, 1, :] = t                 # arithmetic progression
+    kb = omoba.block_means(k, B)
+    for b in range(N // B):
+        np.testing.assert_allclose(kb[b, 0], b)
+        np.testing.assert_allclose(kb[b, 1], b * B + (B - 1) / 2)
+    kb = omoba.block_means(k[:37], B)   # trailing partial block
+    np.testing.assert_allclose(kb[4, 1], np.mean(np.arange(32, 37)))
+
+
+def _moba_full(q, k, v, B, topk, scale, window=0):
+    blk, sc, o, lse = omoba.forward(q, k, v, B, topk, scale, window)
+    return blk, sc, o
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2)])
+def test_moba_all_blocks_equals_dense_causal(hq, hkv):
+    r = rng(4)
+    N, d, B = 48, 8, 8
+    q = r.standard_normal((N, hq, d))
+    k = r.standard_normal((N, hkv, d))
+    v = r.standard_normal((N, hkv, d))
+    _, _, o = _moba_full(q, k, v, B, topk=N // B, scale=0.35)
+    np.testing.assert_allclose(o, sdpa_causal(q, k, v, 0.35), atol=1e-12)
+
+
+def test_moba_k1_equals_block_diagonal_causal():
+    r = rng(5)
+    N, H, d, B = 40, 2, 8, 8
+    q, k, v = (r.standard_normal((N, H, d)) for _ in range(3))
+    _, _, o = _moba_full(q, k, v, B, topk=1, scale=0.4)
+    mask = np.zeros((H, N, N), dtype=bool)
+    for t in range(N):
+        mask[:, t, (t // B) * B:t + 1] = True
+    np.testing.assert_allclose(o, sdpa_masked(q, k, v, mask, 0.4), atol=1e-12)
+
+
+def test_moba_block1_equals_token_topk_bruteforce():
+    r = rng(6)
+    N, H, d, topk = 30, 2, 6, 4
+    q, k, v = (r.standard_normal((N, H, d)) for _ in range(3))
+    blk, _, o = _moba_full(q, k, v, 1, topk=topk, scale=0.5)
+    mask = np.zeros((H, N, N), dtype=bool)
+    for t in range(N):
+        for h in range(H):
+            s = [(-(q[t, h] @ k[j, h]), j) for j in range(t)]
+            chosen = sorted(j for _, j in sorted(s)[:topk - 1]) + [t]
+            got = [b for b in blk[t, h] if b >= 0]
+            assert got == sorted(chosen)
+            mask[h, t, chosen] = True
+    np.testing.assert_allclose(o, sdpa_masked(q, k, v, mask, 0.5), atol=1e-12)
+
+
+def test_moba_gqa_equals_mha_with_repeated_kv():
+    r = rng(7)
+    N, d, B = 32, 8, 4
+    q = r.standard_normal((N, 6, d))
+    k = r.standard_normal((N, 2, d))
+    v = r.standard_normal((N, 2, d))
+    blk_g, _, o_g = _moba_full(q, k, v, B, 3, 0.3)
+    blk_m, _, o_m = _moba_full(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), B, 3, 0.3)
+    assert np.array_equal(blk_g, blk_m)
+    np.testing.assert_allclose(o_g, o_m, atol=1e-13)
+
+
+def test_moba_selection_exhaustive_with_ties():
+    """Every (k-1)-subset of the candidates is tried; the gated set must be
+    the one whose members all beat every non-member on (score, -index)."""
+    r = rng(8)
+    N, H, d, B, topk = 24, 1, 4, 2, 4
+    # small integer entries make exact score ties common
+    q = r.integers(-1, 2, (N, H, d)).astype(np.float64)
+    k = r.integers(-1, 2, (N, H, d)).astype(np.float64)
+    kb = omoba.block_means(k, B)
+    ties_seen = 0
+    for t in range(N):
+        cur = t // B
+        blk, sc = omoba.select_row(q[t, 0], kb[:, 0], t, B, topk)
+        s = [q[t, 0] @ kb[b, 0] for b in range(cur)]
+        ties_seen += len(s) - len(set(s))
+        want = None
+        for sub in itertools.combinations(range(cur), min(topk - 1, cur)):
+            rest = [b for b in range(cur) if b not in sub]
+            if all((s[a] > s[b]) or (s[a] == s[b] and a < b) for a in sub for b in rest):
+                assert want is None
+                want = sorted(sub)
+        want = sorted(want + [cur])
+        assert [b for b in blk if b >= 0] == want
+        assert list(blk[len(want):]) == [-1] * (topk - len(want))
+        assert np.all(np.isneginf(sc[cur:]))
+    assert ties_seen > 0
+
+
+def test_moba_is_causal():
+    r = rng(9)
+    N, H, d, B = 32, 2, 8, 4
+    q, k, v = (r.standard_normal((N, H, d)) for _ in range(3))
+    _, _, o1 = _moba_full(q, k, v, B, 3, 0.3)
+    k2, v2 = k.copy(), v.copy()
+    k2[20:] = r.standard_normal(k2[20:].shape)
+    v2[20:] = r.standard_normal(v2[20:].shape)
+    _, _, o2 = _moba_full(q, k2, v2, B, 3, 0.3)
+    np.testing.assert_array_equal(o1[:20], o2[:20])
+
+
+def test_moba_window_adds_local_keys_once():
+    r = rng(10)
+    N, H, d, B, w = 24, 1, 4, 8, 5
+    q, k, v = (r.standard_normal((N, H, d)) for _ in range(3))
+    blk, _, o = _moba_full(q, k, v, B, 2, 0.5, window=w)
+    for t in range(N):
+        keys = omoba.key_set(blk[t, 0], t, B, w)
+        assert len(keys) == len(set(keys.tolist()))
+        want = set(range((t // B) * B, t + 1)) | set(range(max(0, t - w + 1), t + 1))
+        for b in blk[t, 0]:
+            if 0 <= b < t // B:
+                want |= set(range(b * B, (b + 1) * B))
+        assert set(keys.tolist()) == want
+
+
+def test_moba_sparsity_matches_page():
+    g = json.load(open(GOLDEN))["moba_fixed_sparsity"]
+    nb, topk = g["shape"]["n_blocks"], g["shape"]["topk"]
+    # a late query of a 64-block sequence gates exactly topk blocks
+    r = rng(11)
+    B = 2
+    q = r.standard_normal((nb * B, 1, 4))
+    k = r.standard_normal((nb * B, 1, 4))
+    blk, _ = omoba.select(q, k, B, topk, rows=[nb * B - 1])
+    attended = int((blk[0, 0] >= 0).sum())
+    assert attended == topk
+    assert abs((1 - attended / nb) - g["value"]) <= g["abs_tol"]
+    assert abs(oracle.cost.moba_sparsity(nb, topk) - g["value"]) <= g["abs_tol"]
+
+
+# ------------------------------------------------------------------ ESA
+def test_esa_partition_covers_prefix_disjointly():
+    for c0, n_init, W in [(0, 4, 8), (3, 4, 8), (10, 4, 8), (13, 4, 8), (100, 4, 8), (63488, 128, 4096)]:
+        I, M, L = oesa.partition(c0, n_init, W)
+        allp = np.concatenate([I, M, L])
+        assert np.array_equal(np.sort(allp), np.arange(c0))
+        assert len(L) <= W
+    I, M, L = oesa.partition(63488, 128, 4096)
+    assert (len(I), len(M), len(L)) == (128, 59264, 4096)
+    I, M, L = oesa.partition(131071, 128, 4096)
+    assert len(M) == 126847 and len(I) + 2048 + len(L) + 1 == 6273
+
+
+def test_esa_compress_concatenates_heads_in_order():
+    r = rng(12)
+    H, d, d_c = 3, 4, 5
+    x = r.standard_normal((7, H, d))
+    W = np.zeros((d_c, H * d))
+    picks = [(0, 1), (2, 3), (1, 0), (2, 0), (0, 3)]
+    for c, (h, j) in enumerate(picks):
+        W[c, h * d + j] = 1.0
+    out = oesa.compress(x.reshape(7, -1), W, np.arange(d_c, dtype=np.float64))
+    for c, (h, j) in enumerate(picks):
+        np.testing.assert_array_equal(out[:, c], x[:, h, j] + c)
+
+
+def test_esa_key_cache_is_rounded_compression():
+    r = rng(13)
+    k = r.standard_normal((20, 2, 4)).astype(np.float32).astype(np.float64)
+    W = np.eye(3, 8)                      # picks exact float32 values
+    kc = oesa.key_cache(k, W)
+    ref = torch.from_numpy(k.reshape(20, 8)[:, :3].astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(kc, ref)
+
+
+def test_esa_neighbour_matches_library_filter():
+    r = rng(14)
+    for n, rad in [(1, 2), (2, 2), (7, 0), (50, 1), (50, 2), (50, 7), (5, 9)]:
+        u = r.integers(-5, 5, n).astype(np.float64)
+        ref = ndi.maximum_filter1d(u, size=2 * rad + 1, mode="constant", cval=-np.inf)
+        np.testing.assert_array_equal(oesa.neighbour(u, rad), ref)
+
+
+def test_esa_topk_exhaustive_with_ties():
+    r = rng(15)
+    for trial in range(30):
+        n = int(r.integers(1, 9))
+        k = int(r.integers(1, 10))
+        s = r.integers(-2, 3, n).astype(np.float64)
+        got = oesa.top_k(s, k)
+        kk = min(k, n)
+        wants = [sorted(sub) for sub in itertools.combinations(range(n), kk)
+                 if all((s[a] > s[b]) or (s[a] == s[b] and a < b)
+                        for a in sub for b in range(n) if b not in sub)]
+        assert len(wants) == 1 and list(got) == wants[0]
+
+
+def test_esa_no_clip_no_radius_reduces_to_summed_query():
+    """clip = inf, r = 0: u_j = <sum_i q~_i, k~_j> - const, so the selection is
+    a sort of one matrix-vector product."""
+    r = rng(16)
+    m, H, d, T, d_c = 6, 2, 8, 90, 5
+    q = r.standard_normal((m, H, d))
+    Wq = r.standard_normal((d_c, H * d))
+    kc = round_to_bf16(r.standard_normal((T, d_c)))
+    c0, n_init, W, topk = 84, 4, 10, 9
+    sel, up, u, _ = oesa.select(q, Wq, None, kc, c0, n_init, W, topk, radius=0, clip=np.inf)
+    _, M, _ = oesa.partition(c0, n_init, W)
+    qsum = (q.reshape(m, -1) @ Wq.T).sum(0)
+    score = kc[M] @ qsum
+    want = np.sort(M[np.argsort(-score, kind="stable")[:topk]])
+    assert np.array_equal(sel, want)
+
+
+def test_esa_zero_clip_gives_all_ties_lowest_positions():
+    r = rng(17)
+    q = r.standard_normal((3, 2, 4))
+    kc = r.standard_normal((60, 5))
+    Wq = r.standard_normal((5, 8))
+    sel, up, _, _ = oesa.select(q, Wq, None, kc, 55, 3, 6, 7, radius=2, clip=0.0)
+    assert np.all(up == 0)
+    assert np.array_equal(sel, np.arange(3, 10))
+
+
+def test_esa_decode_monotone_correction_keeps_raw_ranking():
+    r = rng(18)
+    T, H, d, d_c = 300, 2, 4, 6
+    q = r.standard_normal((1, H, d))
+    Wq = r.standard_normal((d_c, H * d))
+    kc = round_to_bf16(r.standard_normal((T, d_c)))
+    c0 = T - 1
+    sel, _, _, _ = oesa.select(q, Wq, None, kc, c0, 5, 20, 12, radius=0, clip=1e9)
+    _, M, _ = oesa.partition(c0, 5, 20)
+    raw = kc[M] @ (q.reshape(1, -1) @ Wq.T)[0]
+    assert np.array_equal(sel, np.sort(M[np.argsort(-raw, kind="stable")[:12]]))
+
+
+def test_esa_radius_lifts_neighbours_of_a_peak():
+    u = np.zeros(20)
+    u[7] = 5.0
+    up = oesa.neighbour(u, 2)
+    assert np.array_equal(np.nonzero(up == 5.0)[0], np.arange(5, 10))
+    # top-5 then picks the whole segment around the peak
+    assert np.array_equal(oesa.top_k(up, 5), np.arange(5, 10))
+
+
+@pytest.mark.parametrize("c0,m", [(40, 8), (5, 6), (0, 4)])
+def test_esa_full_selection_equals_dense_causal(c0, m):
+    r = rng(19)
+    H, d, d_c = 2, 8, 4
+    T = c0 + m
+    q_all = r.standard_normal((T, H, d))
+    k = r.standard_normal((T, H, d))
+    v = r.standard_normal((T, H, d))
+    Wq = r.standard_normal((d_c, H * d))
+    kc = round_to_bf16(r.standard_normal((T, d_c)))
+    n_init, W = 3, 5
+    q = q_all[c0:]
+    sel, _, _, _ = oesa.select(q, Wq, None, kc, c0, n_init, W, topk=10 ** 6, radius=1, clip=3.0)
+    _, M, _ = oesa.partition(c0, n_init, W)
+    assert np.array_equal(sel, M)
+    o, _ = oesa.attend(q, k, v, sel, c0, n_init, W, 0.3)
+    ref = sdpa_causal(q_all, k, v, 0.3)[c0:]
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+
+
+def test_esa_parts_are_one_joint_softmax():
+    """Attention over I u S u L u chunk equals the merge of the global part
+    (I u S) and the window part (L u chunk)."""
+    r = rng(20)
+    T, H, d = 60, 2, 4
+    k, v = r.standard_normal((T, H, d)), r.standard_normal((T, H, d))
+    c0, n_init, W = 50, 4, 8
+    q = r.standard_normal((10, H, d))
+    sel = np.array([6, 9, 20, 33])
+    o, lse = oesa.attend(q, k, v, sel, c0, n_init, W, 0.4)
+    I, _, L = oesa.partition(c0, n_init, W)
+    for i in range(10):
+        g = np.concatenate([I, sel])
+        w = np.concatenate([L, np.arange(c0, c0 + i + 1)])
+        for h in range(H):
+            pg = oatt.attend(q[i, h], k[g, h], v[g, h], 0.4)
+            pw = oatt.attend(q[i, h], k[w, h], v[w, h], 0.4)
+            oo, ll = oatt.merge([pg, pw])
+            np.testing.assert_allclose(oo, o[i, h], atol=1e-12)
+            np.testing.assert_allclose(ll, lse[i, h], atol=1e-12)
+
+
+def test_esa_needles_are_selected_in_decode():
+    """Planted needles (keys equal to the decode query in every head) win
+    the compressed scoring under the unit-variance random compression; each
+    lifts its +-r neighbours onto the same plateau."""
+    T, H, d, d_c = 4096, 8, 32, 64
+    seed = 4
+    q, k, v, info = synth.esa_inputs(seed, 1, T, 1, H, d, torch.float32, needles=6,
+                                     needle_lo=64, needle_hi=T - 1 - 512, needle_gap=5,
+                                     needle_scale=1.0)
+    Wq = synth.compression_weights(seed, d_c, H * d, dtype=torch.float32).double().numpy()
+    kc = oesa.key_cache(k[0].double().numpy(), Wq)
+    sel, _, _, _ = oesa.select(q[0].double().numpy(), Wq, None, kc, T - 1, 64, 512, 128, 2, 48.0)
+    for p in info["needles"][0]:
+        assert set(range(p - 2, p + 3)) <= set(sel.tolist())
+
+
+def test_esa_step_ratio_matches_page():
+    g = json.load(open(GOLDEN))
+    e = g["esa_step_ratio_long_sequence"]
+    s = e["shape"]
+    ratio = oracle.cost.esa_step_ratio(s["T"], s["D"], s["d_c"], s["n_init"], s["k_sel"], s["window"])
+    assert abs(ratio - e["value"]) <= e["abs_tol"]
+    c = g["esa_compression_ratio"]
+    assert abs(c["shape"]["d_c"] / c["shape"]["D"] - c["value"]) <= c["abs_tol"]
+    # the ratio falls with T towards d_c / (2 D)
+    assert oracle.cost.esa_step_ratio(2 ** 17) > oracle.cost.esa_step_ratio(2 ** 20) > 128 / 8192
