@@ -1,0 +1,198 @@
+/*
+ * qat.h -- C ABI of the query-aware selective sparse attention library
+ * (ESA token selection and MoBA block selection) for AMD MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are caller-owned, contiguous, row-major DEVICE pointers in the
+ *   token-major layout [batch, tokens, heads, head_dim] ("BTHD") unless a
+ *   stride argument says otherwise. Nothing is retained after a call returns;
+ *   no ownership moves across the boundary.
+ * - Element types: QAT_BF16 (bfloat16) or QAT_F32 (float32) as stated per
+ *   argument; selections are int32; log-sum-exp outputs are float32 in the
+ *   natural-log domain.
+ * - Scratch memory comes only from the caller's workspace (`ws`, `ws_bytes`),
+ *   sized by the matching *_workspace_size() query; the library itself never
+ *   allocates device memory. `ws` must be 256-byte aligned.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Work is enqueued asynchronously on it; no call synchronises the host.
+ * - Every call returns a qat_status. Arguments are validated on the host
+ *   before anything is enqueued; on QAT_EINVAL / QAT_EUNSUPPORTED /
+ *   QAT_EWORKSPACE nothing has been launched and outputs are untouched.
+ *   QAT_EHIP reports a failed kernel launch. qat_last_error() returns a
+ *   thread-local description of the last non-OK status.
+ * - Calls that share a workspace must not overlap in time.
+ *
+ * Sources (the pages this library implements):
+ *   [ESA]  Efficient Selective Attention write-up (hlszyjy.com/post/6872.html)
+ *   [MoBA] Mixture of Block Attention write-up (dtcms.com/wzjs/567377.html)
+ *   [CCA]  CCA-Attention ICML 2025 write-up (m.jxzklqfsx.com/article/817694.html)
+ */
+#ifndef QAT_H_
+#define QAT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum qat_status {
+  QAT_OK = 0,
+  QAT_EINVAL = -1,        /* bad argument (null pointer, size, range) */
+  QAT_EUNSUPPORTED = -2,  /* valid request this build does not implement */
+  QAT_EWORKSPACE = -3,    /* workspace null, misaligned or too small */
+  QAT_EHIP = -4           /* a HIP launch failed */
+};
+
+enum qat_dtype { QAT_F32 = 0, QAT_BF16 = 1 };
+
+#define QAT_ABI_VERSION 1
+
+/* Thread-local text for the last non-OK status of this thread ("" if none). */
+const char* qat_last_error(void);
+/* Returns QAT_ABI_VERSION of the loaded library. */
+int qat_abi_version(void);
+
+/* ======================================================================
+ * ESA -- token-level selection by compressed q/k   [ESA]
+ * ====================================================================== */
+
+/*
+ * One sequence chunk of queries at positions [chunk_start, chunk_start +
+ * chunk_len) against a KV cache of ctx_len rows per sequence
+ * (chunk_start + chunk_len <= ctx_len). Decode is chunk_len == 1.
+ * The keys before the chunk are split into four parts ([ESA], paragraph on
+ * the four-part token split): initial I = [0, min(n_init, c0)), local
+ * L = [max(n_init, c0 - window), c0), middle M = [n_init, max(n_init,
+ * c0 - window)) (the candidates), and the chunk itself (causal).
+ */
+typedef struct {
+  int64_t batch;        /* sequences */
+  int64_t n_heads;      /* H */
+  int64_t head_dim;     /* d: 64 or 128 */
+  int64_t d_c;          /* compressed dimension: multiple of 32, <= 256 */
+  int64_t ctx_len;      /* rows of the KV and compressed-key caches per sequence */
+  int64_t chunk_start;  /* c0 */
+  int64_t chunk_len;    /* m >= 1 */
+  int32_t n_init;       /* initial tokens always attended, >= 0 */
+  int32_t window;       /* local tokens before the chunk, >= 0 */
+  int32_t topk;         /* middle tokens selected, >= 1 */
+  int32_t radius;       /* neighbour-influence radius r >= 0 */
+  float clip;           /* score-correction floor C > 0 (may be +inf) */
+  float scale;          /* softmax scale, e.g. 1/sqrt(d) */
+  int32_t dtype;        /* qat_dtype of q, K, V and outputs */
+} qat_esa_params;
+
+/* Workspace bytes for esa_select + esa_sparse_attn with these parameters. */
+int esa_workspace_size(const qat_esa_params* p, size_t* bytes);
+
+/*
+ * Compression by the one-layer map of [ESA] (paragraph on compressing q and
+ * k to about 3.2% with a one-layer MLP; read as one affine map):
+ *   out[i, :] = round(W x[i, :] + bias)
+ * x: n rows of d_model elements (in_dtype), row i at x + i*x_stride elements.
+ * W: [d_c, d_model] (in_dtype), bias: [d_c] float32 or NULL.
+ * out: row i at out + i*out_stride elements, out_dtype QAT_F32 or QAT_BF16.
+ * Accumulation is float64, rounded once (nearest even) to out_dtype, so the
+ * bf16 compressed-key cache holds the correctly rounded exact products.
+ * ws may be NULL when ws_bytes from esa_compress_workspace_size() is 0.
+ */
+int esa_compress_workspace_size(int64_t n, int64_t d_model, int64_t d_c, size_t* bytes);
+int esa_compress(const void* x, int64_t n, int64_t x_stride, int64_t d_model, int32_t in_dtype,
+                 const void* W, const float* bias, int64_t d_c,
+                 void* out, int64_t out_stride, int32_t out_dtype,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Token selection ([ESA], paragraphs on query-aware importance, head merging,
+ * score correction, neighbour influence and top-k):
+ *   q~_i   = Wq concat_h(q_i^h) + bq                 (float64 -> float32)
+ *   s_ij   = <q~_i, k~_j>,  j in M                     (k~ = compressed cache)
+ *   u_j    = sum_i max(s_ij - max_j' s_ij', -clip)     (correction; READING)
+ *   u'_j   = max{u_t : t in M, |t - j| <= radius}       (neighbour; READING)
+ *   sel    = positions of the min(topk, |M|) largest u'_j, ties to the
+ *            smaller position, ascending, -1 padded.
+ * q: [batch, chunk_len, H, d] (dtype), Wq: [d_c, H*d] (dtype), bq: [d_c]
+ * float32 or NULL, kc_cache: [batch, ctx_len, d_c] bfloat16 (as written by
+ * esa_compress). Outputs: sel [batch, topk] int32, n_sel [batch] int32,
+ * scores [batch, |M|] float32 (u'_j, may be NULL).
+ */
+int esa_select(const qat_esa_params* p, const void* q, const void* Wq, const float* bq,
+               const void* kc_cache, int32_t* sel, int32_t* n_sel, float* scores,
+               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Attention over the fused parts ([ESA], global attention over initial plus
+ * selected tokens fused with window attention over local tokens; [CCA],
+ * global-local fusion into one unified K/V): query t = c0 + i attends
+ * I u S u L u [c0, t] with one joint softmax per head, S = sel[0:n_sel]
+ * shared by all heads.
+ * q: [batch, chunk_len, H, d]; k_cache, v_cache: [batch, ctx_len, H, d];
+ * sel/n_sel: as produced by esa_select (positions must lie in M).
+ * out: [batch, chunk_len, H, d] (dtype); lse: [batch, chunk_len, H] float32
+ * or NULL.
+ */
+int esa_sparse_attn(const qat_esa_params* p, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* sel, const int32_t* n_sel,
+                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ======================================================================
+ * MoBA -- block-level selection by mean-pooled keys   [MoBA]
+ * ====================================================================== */
+
+/*
+ * Sequences of seq_len tokens split into blocks of `block` keys (block b =
+ * keys [b*block, (b+1)*block), [MoBA] section 3 partition). Queries
+ * [q_start, q_start + q_len) are processed. Query head h reads KV head
+ * h / (n_q_heads / n_kv_heads).
+ */
+typedef struct {
+  int64_t batch;
+  int64_t seq_len;      /* N */
+  int64_t n_q_heads;    /* Hq */
+  int64_t n_kv_heads;   /* Hkv, divides Hq */
+  int64_t head_dim;     /* 64 or 128 */
+  int64_t q_start;      /* first query position processed */
+  int64_t q_len;        /* number of query positions processed */
+  int32_t block;        /* B >= 1 */
+  int32_t topk;         /* blocks per query INCLUDING the forced current one, 1..16 */
+  int32_t window;       /* extra local keys [t - window + 1, t], >= 0 */
+  float scale;          /* softmax scale */
+  int32_t dtype;        /* qat_dtype of q, k, v and out */
+} qat_moba_params;
+
+int moba_workspace_size(const qat_moba_params* p, size_t* bytes);
+
+/*
+ * Block gating ([MoBA] section 3: affinity s_b = <q, mean_pool(K[block b])>,
+ * top-k gate, causality, forced current block):
+ *   for b < cur(t) = floor(t / block): s_b = <q_{t,h}, mean(K[block b, g(h)])>
+ *   blk[t, h] = ascending( top-(topk-1) blocks by s_b, ties to the smaller
+ *               block  U  {cur(t)} ), -1 padded to topk.
+ * Block means are accumulated in float64 and held in float32; scores are
+ * float32.
+ * q: [batch, seq_len, Hq, d], k: [batch, seq_len, Hkv, d].
+ * blk: [batch, q_len, Hq, topk] int32 for the rows q_start .. q_start+q_len-1.
+ */
+int moba_block_select(const qat_moba_params* p, const void* q, const void* k, int32_t* blk,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block-sparse attention ([MoBA] section 2, Softmax(q K[I]^T) V[I]): query t
+ * attends the union of its gated earlier blocks (whole), the causal part
+ * [cur(t)*block, t] of its own block and, if window > 0, the keys
+ * [max(0, t - window + 1), t]; one softmax per (t, h), each key once.
+ * blk: as written by moba_block_select for the same q_start/q_len.
+ * out: [batch, q_len, Hq, d] (dtype); lse: [batch, q_len, Hq] float32 or NULL.
+ */
+int moba_sparse_attn(const qat_moba_params* p, const void* q, const void* k, const void* v,
+                     const int32_t* blk, void* out, float* lse, void* ws, size_t ws_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QAT_H_ */

@@ -1,0 +1,242 @@
+"""ctypes marshalling for libqat.so (see include/qat.h for the contract)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libqat.so")
+
+QAT_F32, QAT_BF16 = 0, 1
+_STATUS = {0: "QAT_OK", -1: "QAT_EINVAL", -2: "QAT_EUNSUPPORTED", -3: "QAT_EWORKSPACE", -4: "QAT_EHIP"}
+
+EXPORTED_SYMBOLS = (
+    "qat_last_error", "qat_abi_version",
+    "esa_workspace_size", "esa_compress_workspace_size", "esa_compress", "esa_select", "esa_sparse_attn",
+    "moba_workspace_size", "moba_block_select", "moba_sparse_attn",
+)
+
+
+class QatError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class EsaParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("n_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+        ("d_c", ctypes.c_int64), ("ctx_len", ctypes.c_int64), ("chunk_start", ctypes.c_int64),
+        ("chunk_len", ctypes.c_int64), ("n_init", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("topk", ctypes.c_int32), ("radius", ctypes.c_int32), ("clip", ctypes.c_float),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
+
+
+class MobaParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64), ("n_q_heads", ctypes.c_int64),
+        ("n_kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64), ("q_start", ctypes.c_int64),
+        ("q_len", ctypes.c_int64), ("block", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Loads libqat.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is missing: build it with `python -m query_aware_top_amd.build`")
+        L = ctypes.CDLL(lib_path)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        L.qat_last_error.restype = ctypes.c_char_p
+        L.qat_abi_version.restype = ctypes.c_int
+        L.esa_workspace_size.argtypes = [ctypes.POINTER(EsaParams), ctypes.POINTER(sz)]
+        L.esa_compress_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
+        L.esa_compress.argtypes = [vp, i64, i64, i64, ctypes.c_int32, vp, vp, i64, vp, i64, ctypes.c_int32,
+                                   vp, sz, vp]
+        L.esa_select.argtypes = [ctypes.POINTER(EsaParams), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.esa_sparse_attn.argtypes = [ctypes.POINTER(EsaParams), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moba_workspace_size.argtypes = [ctypes.POINTER(MobaParams), ctypes.POINTER(sz)]
+        L.moba_block_select.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, sz, vp]
+        L.moba_sparse_attn.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name in EXPORTED_SYMBOLS:
+            getattr(L, name).restype = ctypes.c_int if name != "qat_last_error" else ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().qat_abi_version()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise QatError(rc, lib().qat_last_error().decode())
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return QAT_BF16
+    if t == torch.float32:
+        return QAT_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, device=True):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _workspace(nbytes: int, device, ws=None):
+    if ws is not None:
+        _need(ws, "ws", torch.uint8)
+        if ws.numel() < nbytes:
+            raise ValueError(f"workspace of {ws.numel()} bytes is smaller than the {nbytes} needed")
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ ESA
+def esa_params(*, batch, n_heads, head_dim, d_c, ctx_len, chunk_start, chunk_len, n_init, window, topk,
+               radius, clip, scale=None, dtype=torch.bfloat16) -> EsaParams:
+    return EsaParams(batch, n_heads, head_dim, d_c, ctx_len, chunk_start, chunk_len, n_init, window, topk,
+                     radius, float(clip), float(scale if scale is not None else 1.0 / math.sqrt(head_dim)),
+                     _dt(dtype))
+
+
+def esa_workspace_size(p: EsaParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().esa_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def esa_compress(x, W, bias=None, out=None, out_dtype=torch.bfloat16, n=None, x_stride=None, out_stride=None,
+                 ws=None):
+    """out[i] = round(W x[i] + bias) (float64 accumulation). x: [n, d_model]
+    rows (or a strided view described by n/x_stride over a contiguous base);
+    W: [d_c, d_model]."""
+    d_c, d_model = W.shape
+    _need(W, "W", x.dtype)
+    _need(bias, "bias", torch.float32)
+    if n is None:
+        _need(x, "x")
+        n = x.shape[0]
+        x_stride = d_model
+    if out is None:
+        out = torch.empty(n, d_c, dtype=out_dtype, device=x.device)
+        out_stride = d_c
+    elif out_stride is None:
+        _need(out, "out")
+        out_stride = d_c
+    nb = ctypes.c_size_t(0)
+    _check(lib().esa_compress_workspace_size(n, d_model, d_c, ctypes.byref(nb)))
+    ws = _workspace(nb.value, x.device, ws)
+    _check(lib().esa_compress(_ptr(x), n, x_stride, d_model, _dt(x.dtype), _ptr(W), _ptr(bias), d_c,
+                              _ptr(out), out_stride, _dt(out.dtype), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def esa_select(p: EsaParams, q, Wq, bq, kc_cache, sel=None, n_sel=None, scores=None, want_scores=False, ws=None):
+    """Returns (sel [batch, topk] int32, n_sel [batch] int32, scores or None)."""
+    dt = torch.bfloat16 if p.dtype == QAT_BF16 else torch.float32
+    _need(q, "q", dt)
+    _need(Wq, "Wq", dt)
+    _need(bq, "bq", torch.float32)
+    _need(kc_cache, "kc_cache", torch.bfloat16)
+    dev = q.device
+    if sel is None:
+        sel = torch.empty(p.batch, p.topk, dtype=torch.int32, device=dev)
+    if n_sel is None:
+        n_sel = torch.empty(p.batch, dtype=torch.int32, device=dev)
+    if scores is None and want_scores:
+        n_mid = max(0, max(p.n_init, p.chunk_start - p.window) - p.n_init) if p.chunk_start > p.n_init else 0
+        scores = torch.empty(p.batch, max(n_mid, 1), dtype=torch.float32, device=dev)
+    ws = _workspace(esa_workspace_size(p), dev, ws)
+    _check(lib().esa_select(ctypes.byref(p), _ptr(q), _ptr(Wq), _ptr(bq), _ptr(kc_cache), _ptr(sel),
+                            _ptr(n_sel), _ptr(scores), _ptr(ws), ws.numel(), _stream()))
+    return sel, n_sel, scores
+
+
+def esa_sparse_attn(p: EsaParams, q, k_cache, v_cache, sel, n_sel, out=None, lse=None, want_lse=True, ws=None):
+    """Returns (out [batch, chunk_len, H, d], lse [batch, chunk_len, H] or None)."""
+    dt = torch.bfloat16 if p.dtype == QAT_BF16 else torch.float32
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, name, dt)
+    _need(sel, "sel", torch.int32)
+    _need(n_sel, "n_sel", torch.int32)
+    dev = q.device
+    if out is None:
+        out = torch.empty(p.batch, p.chunk_len, p.n_heads, p.head_dim, dtype=dt, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(p.batch, p.chunk_len, p.n_heads, dtype=torch.float32, device=dev)
+    ws = _workspace(esa_workspace_size(p), dev, ws)
+    _check(lib().esa_sparse_attn(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sel), _ptr(n_sel),
+                                 _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return out, lse
+
+
+# ------------------------------------------------------------------ MoBA
+def moba_params(*, batch, seq_len, n_q_heads, n_kv_heads, head_dim, q_start=0, q_len=None, block, topk,
+                window=0, scale=None, dtype=torch.bfloat16) -> MobaParams:
+    return MobaParams(batch, seq_len, n_q_heads, n_kv_heads, head_dim, q_start,
+                      seq_len - q_start if q_len is None else q_len, block, topk, window,
+                      float(scale if scale is not None else 1.0 / math.sqrt(head_dim)), _dt(dtype))
+
+
+def moba_workspace_size(p: MobaParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moba_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def moba_block_select(p: MobaParams, q, k, blk=None, ws=None):
+    """Returns blk [batch, q_len, Hq, topk] int32 (ascending, -1 padded)."""
+    dt = torch.bfloat16 if p.dtype == QAT_BF16 else torch.float32
+    _need(q, "q", dt)
+    _need(k, "k", dt)
+    if blk is None:
+        blk = torch.empty(p.batch, p.q_len, p.n_q_heads, p.topk, dtype=torch.int32, device=q.device)
+    ws = _workspace(moba_workspace_size(p), q.device, ws)
+    _check(lib().moba_block_select(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(blk), _ptr(ws), ws.numel(), _stream()))
+    return blk
+
+
+def moba_sparse_attn(p: MobaParams, q, k, v, blk, out=None, lse=None, want_lse=True, ws=None):
+    """Returns (out [batch, q_len, Hq, d], lse [batch, q_len, Hq] or None)."""
+    dt = torch.bfloat16 if p.dtype == QAT_BF16 else torch.float32
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, dt)
+    _need(blk, "blk", torch.int32)
+    dev = q.device
+    if out is None:
+        out = torch.empty(p.batch, p.q_len, p.n_q_heads, p.head_dim, dtype=dt, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(p.batch, p.q_len, p.n_q_heads, dtype=torch.float32, device=dev)
+    ws = _workspace(moba_workspace_size(p), dev, ws)
+    _check(lib().moba_sparse_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(blk), _ptr(out), _ptr(lse),
+                                  _ptr(ws), ws.numel(), _stream()))
+    return out, lse

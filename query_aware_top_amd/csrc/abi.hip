@@ -1,0 +1,353 @@
+// C ABI of the library: argument validation, workspace layout and the
+// sequence of kernel launches behind each entry point declared in qat.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/qat.h"
+#include "common.h"
+#include "launch.h"
+
+#define QAT_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return QAT_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QAT_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool pow2_dc(int64_t d_c) { return d_c == 32 || d_c == 64 || d_c == 128 || d_c == 256; }
+
+// ---------------------------------------------------------------- ESA
+struct EsaLayout {
+  int nsplit_q = 1, nkeysplit = 1, nqsplit = 1, nscan = 1, ndec = 1;
+  int64_t n_mid = 0, mid0 = 0, rows = 0;
+  double* qpart = nullptr;
+  float* qc = nullptr;
+  qat::bf16* qhi = nullptr;
+  qat::bf16* qlo = nullptr;
+  float* rowmax_part = nullptr;
+  float* rowmax = nullptr;
+  float* upart = nullptr;
+  float* sraw = nullptr;
+  float* smax = nullptr;
+  float* u_tmp = nullptr;
+  uint32_t* keys = nullptr;
+  float* po = nullptr;
+  float* pm = nullptr;
+  float* pl = nullptr;
+  size_t bytes = 0;
+};
+
+int esa_check(const qat_esa_params* p) {
+  if (!p) return fail(QAT_EINVAL, "params is NULL");
+  if (p->batch < 1 || p->n_heads < 1) return fail(QAT_EINVAL, "batch and n_heads must be >= 1");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(QAT_EUNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)p->head_dim);
+  if (!pow2_dc(p->d_c)) return fail(QAT_EUNSUPPORTED, "d_c %lld not supported (32, 64, 128, 256)", (long long)p->d_c);
+  if (p->ctx_len < 1 || p->ctx_len >= (1ll << 31)) return fail(QAT_EINVAL, "ctx_len out of range");
+  if (p->chunk_start < 0 || p->chunk_len < 1 || p->chunk_start + p->chunk_len > p->ctx_len)
+    return fail(QAT_EINVAL, "chunk [%lld, %lld) outside the cache of %lld rows", (long long)p->chunk_start,
+                (long long)(p->chunk_start + p->chunk_len), (long long)p->ctx_len);
+  if (p->n_init < 0 || p->window < 0 || p->radius < 0) return fail(QAT_EINVAL, "n_init, window, radius must be >= 0");
+  if (p->topk < 1) return fail(QAT_EINVAL, "topk must be >= 1");
+  if (!(p->clip > 0.f)) return fail(QAT_EINVAL, "clip must be > 0 (or +inf)");
+  if (!std::isfinite(p->scale)) return fail(QAT_EINVAL, "scale must be finite");
+  if (p->dtype != QAT_F32 && p->dtype != QAT_BF16) return fail(QAT_EINVAL, "unknown dtype %d", p->dtype);
+  if (p->batch * p->chunk_len * p->n_heads >= (1ll << 31)) return fail(QAT_EUNSUPPORTED, "too many query rows");
+  return QAT_OK;
+}
+
+EsaLayout esa_layout(const qat_esa_params* p, void* ws) {
+  EsaLayout L;
+  const int64_t B = p->batch, m = p->chunk_len, c0 = p->chunk_start;
+  L.rows = B * m;
+  L.mid0 = p->n_init;
+  L.n_mid = c0 > p->n_init ? std::max<int64_t>(p->n_init, c0 - p->window) - p->n_init : 0;
+  const int64_t D = p->n_heads * p->head_dim;
+  L.nsplit_q = qat::compress_splits(L.rows, D, p->d_c);
+  L.nkeysplit = qat::esa_key_splits(L.n_mid > 0 ? L.n_mid : 1, m);
+  L.nqsplit = qat::esa_prefill_qsplits_eff(L.n_mid > 0 ? L.n_mid : 1, m);
+  L.nscan = qat::esa_scan_wgs(L.n_mid > 0 ? L.n_mid : 1);
+  L.ndec = qat::esa_decode_splits(p->n_init, p->topk, p->window);
+  qat::Carver c(ws);
+  L.qpart = c.take<double>((size_t)L.nsplit_q * L.rows * p->d_c);
+  L.qc = c.take<float>((size_t)L.rows * p->d_c);
+  L.qhi = c.take<qat::bf16>((size_t)L.rows * p->d_c);
+  L.qlo = c.take<qat::bf16>((size_t)L.rows * p->d_c);
+  const size_t nm = (size_t)(L.n_mid > 0 ? L.n_mid : 1);
+  if (m > 1) {
+    L.rowmax_part = c.take<float>((size_t)L.rows * L.nkeysplit);
+    L.rowmax = c.take<float>((size_t)L.rows);
+    L.upart = c.take<float>((size_t)B * L.nqsplit * nm);
+  } else {
+    L.sraw = c.take<float>((size_t)B * nm);
+    L.smax = c.take<float>((size_t)B * L.nscan);
+  }
+  L.u_tmp = c.take<float>((size_t)B * nm);
+  L.keys = c.take<uint32_t>((size_t)B * nm);
+  if (m == 1) {
+    L.po = c.take<float>((size_t)B * L.ndec * D);
+    L.pm = c.take<float>((size_t)B * L.ndec * p->n_heads);
+    L.pl = c.take<float>((size_t)B * L.ndec * p->n_heads);
+  }
+  L.bytes = c.bytes();
+  return L;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return QAT_OK;
+  if (!ws) return fail(QAT_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (((uintptr_t)ws) & 255) return fail(QAT_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(QAT_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return QAT_OK;
+}
+
+// ---------------------------------------------------------------- MoBA
+struct MobaLayout {
+  int64_t nbc = 0, nrows = 0, nbuckets = 0, max_tiles = 0;
+  double* mp_part = nullptr;
+  float* kbar = nullptr;
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* cursor = nullptr;
+  int32_t* entries = nullptr;
+  int2* tiles = nullptr;
+  int32_t* ntiles = nullptr;
+  void* part_o = nullptr;
+  float* part_lse = nullptr;
+  size_t bytes = 0;
+};
+
+int moba_check(const qat_moba_params* p) {
+  if (!p) return fail(QAT_EINVAL, "params is NULL");
+  if (p->batch < 1 || p->seq_len < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1)
+    return fail(QAT_EINVAL, "batch, seq_len and head counts must be >= 1");
+  if (p->n_q_heads % p->n_kv_heads) return fail(QAT_EINVAL, "n_kv_heads must divide n_q_heads");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(QAT_EUNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)p->head_dim);
+  if (p->seq_len >= (1ll << 31)) return fail(QAT_EUNSUPPORTED, "seq_len too large");
+  if (p->q_start < 0 || p->q_len < 1 || p->q_start + p->q_len > p->seq_len)
+    return fail(QAT_EINVAL, "query rows [%lld, %lld) outside the sequence of %lld", (long long)p->q_start,
+                (long long)(p->q_start + p->q_len), (long long)p->seq_len);
+  if (p->block < 1) return fail(QAT_EINVAL, "block must be >= 1");
+  if (p->topk < 1 || p->topk > 16) return fail(QAT_EINVAL, "topk must be in 1..16");
+  if (p->window < 0) return fail(QAT_EINVAL, "window must be >= 0");
+  if (!std::isfinite(p->scale)) return fail(QAT_EINVAL, "scale must be finite");
+  if (p->dtype != QAT_F32 && p->dtype != QAT_BF16) return fail(QAT_EINVAL, "unknown dtype %d", p->dtype);
+  if (p->batch * p->q_len * p->n_q_heads >= (1ll << 27)) return fail(QAT_EUNSUPPORTED, "too many query rows");
+  return QAT_OK;
+}
+
+MobaLayout moba_layout(const qat_moba_params* p, void* ws) {
+  MobaLayout L;
+  L.nbc = p->seq_len / p->block;
+  L.nrows = p->batch * p->q_len * p->n_q_heads;
+  L.nbuckets = p->batch * p->n_kv_heads * L.nbc;
+  L.max_tiles = qat::moba_max_tiles(L.nrows, p->topk, L.nbuckets);
+  const int64_t cols = p->n_kv_heads * p->head_dim;
+  const size_t esz = p->dtype == QAT_BF16 ? 2 : 4;
+  qat::Carver c(ws);
+  L.mp_part = c.take<double>((size_t)p->batch * L.nbc * qat::meanpool_splits(p->block) * cols);
+  L.kbar = c.take<float>((size_t)p->batch * L.nbc * cols);
+  L.counts = c.take<int32_t>((size_t)L.nbuckets + 1);
+  L.offsets = c.take<int32_t>((size_t)L.nbuckets + 1);
+  L.cursor = c.take<int32_t>((size_t)L.nbuckets + 1);
+  L.entries = c.take<int32_t>((size_t)L.nrows * (p->topk - 1) + 1);
+  L.tiles = c.take<int2>((size_t)L.max_tiles + 1);
+  L.ntiles = c.take<int32_t>(1);
+  L.part_o = (void*)c.take<char>((size_t)L.nrows * (p->topk - 1) * p->head_dim * esz + 1);
+  L.part_lse = c.take<float>((size_t)L.nrows * (p->topk - 1) + 1);
+  L.bytes = c.bytes();
+  return L;
+}
+
+}  // namespace
+
+// ======================================================================
+QAT_EXPORT const char* qat_last_error(void) { return g_last_error.c_str(); }
+QAT_EXPORT int qat_abi_version(void) { return QAT_ABI_VERSION; }
+
+// ---------------------------------------------------------------- ESA
+QAT_EXPORT int esa_workspace_size(const qat_esa_params* p, size_t* bytes) {
+  int rc = esa_check(p);
+  if (rc) return rc;
+  if (!bytes) return fail(QAT_EINVAL, "bytes is NULL");
+  *bytes = esa_layout(p, nullptr).bytes;
+  return ok();
+}
+
+QAT_EXPORT int esa_compress_workspace_size(int64_t n, int64_t d_model, int64_t d_c, size_t* bytes) {
+  if (!bytes) return fail(QAT_EINVAL, "bytes is NULL");
+  if (n < 1 || d_model < 32 || d_model % 32 || !pow2_dc(d_c))
+    return fail(QAT_EINVAL, "bad compression shape n=%lld d_model=%lld d_c=%lld", (long long)n,
+                (long long)d_model, (long long)d_c);
+  qat::Carver c(nullptr);
+  c.take<double>((size_t)qat::compress_splits(n, d_model, d_c) * n * d_c);
+  *bytes = c.bytes();
+  return ok();
+}
+
+QAT_EXPORT int esa_compress(const void* x, int64_t n, int64_t x_stride, int64_t d_model, int32_t in_dtype,
+                            const void* W, const float* bias, int64_t d_c, void* out, int64_t out_stride,
+                            int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !W || !out) return fail(QAT_EINVAL, "x, W and out must be non-NULL");
+  if (n < 1 || d_model < 32 || d_model % 32) return fail(QAT_EINVAL, "n >= 1 and d_model a multiple of 32 required");
+  if (!pow2_dc(d_c)) return fail(QAT_EUNSUPPORTED, "d_c %lld not supported", (long long)d_c);
+  if (x_stride < d_model || out_stride < d_c) return fail(QAT_EINVAL, "row strides shorter than the rows");
+  if ((in_dtype != QAT_F32 && in_dtype != QAT_BF16) || (out_dtype != QAT_F32 && out_dtype != QAT_BF16))
+    return fail(QAT_EINVAL, "unknown dtype");
+  size_t need = 0;
+  esa_compress_workspace_size(n, d_model, d_c, &need);
+  int rc = check_ws(ws, ws_bytes, need);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int ns = qat::compress_splits(n, d_model, d_c);
+  const bool bf = in_dtype == QAT_BF16;
+  hipError_t e = qat::launch_compress_partial(x, n, x_stride, d_model, bf, W, bf, d_c, ns, (double*)ws, s);
+  if (e == hipSuccess)
+    e = qat::launch_compress_finalize((const double*)ws, ns, n, d_c, bias, out, out_stride,
+                                      out_dtype == QAT_BF16 ? 1 : 0, nullptr, nullptr, s);
+  return hip_status(e, "esa_compress");
+}
+
+QAT_EXPORT int esa_select(const qat_esa_params* p, const void* q, const void* Wq, const float* bq,
+                          const void* kc_cache, int32_t* sel, int32_t* n_sel, float* scores, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int rc = esa_check(p);
+  if (rc) return rc;
+  if (!q || !Wq || !kc_cache || !sel || !n_sel) return fail(QAT_EINVAL, "q, Wq, kc_cache, sel, n_sel must be non-NULL");
+  EsaLayout L = esa_layout(p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  L = esa_layout(p, ws);
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = p->dtype == QAT_BF16;
+  const int64_t D = p->n_heads * p->head_dim;
+  // q~ = Wq concat_h(q) + bq, float64 accumulation -> float32 + hi/lo bf16
+  hipError_t e = qat::launch_compress_partial(q, L.rows, D, D, bf, Wq, bf, p->d_c, L.nsplit_q, L.qpart, s);
+  if (e == hipSuccess)
+    e = qat::launch_compress_finalize(L.qpart, L.nsplit_q, L.rows, p->d_c, bq, L.qc, p->d_c, 2, L.qhi, L.qlo, s);
+  if (e != hipSuccess) return hip_status(e, "esa_select: query compression");
+  const qat::bf16* kc = (const qat::bf16*)kc_cache;
+  int mode;
+  if (p->chunk_len > 1) {
+    mode = 0;
+    e = qat::launch_esa_prefill_scores(L.qhi, L.qlo, kc, p->batch, p->chunk_len, p->ctx_len, L.mid0, L.n_mid,
+                                       p->d_c, p->clip, L.rowmax_part, L.rowmax, L.upart, s);
+  } else {
+    mode = 1;
+    e = qat::launch_esa_decode_scan(L.qc, kc, p->batch, p->ctx_len, L.mid0, L.n_mid, p->d_c, L.sraw, L.smax, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "esa_select: scoring");
+  e = qat::launch_esa_topk(mode, L.upart, L.nqsplit, L.sraw, L.smax, L.nscan, p->clip, p->batch, L.n_mid,
+                           p->radius, p->topk, L.mid0, L.u_tmp, L.keys, scores, sel, n_sel, s);
+  return hip_status(e, "esa_select: top-k");
+}
+
+QAT_EXPORT int esa_sparse_attn(const qat_esa_params* p, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* sel, const int32_t* n_sel, void* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  int rc = esa_check(p);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !sel || !n_sel || !out)
+    return fail(QAT_EINVAL, "q, k_cache, v_cache, sel, n_sel, out must be non-NULL");
+  EsaLayout L = esa_layout(p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  L = esa_layout(p, ws);
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = p->dtype == QAT_BF16;
+  hipError_t e;
+  if (bf && p->chunk_len == 1 && qat::esa_decode_supported(p->n_heads, p->head_dim)) {
+    e = qat::launch_esa_decode_attn(q, k_cache, v_cache, sel, n_sel, L.po, L.pm, L.pl, out, lse, p->batch,
+                                    p->n_heads, p->head_dim, p->ctx_len, p->chunk_start, p->n_init, p->window,
+                                    p->topk, p->scale, s);
+  } else if (bf) {
+    e = qat::launch_esa_prefill_attn(q, k_cache, v_cache, sel, n_sel, out, lse, p->batch, p->n_heads, p->head_dim,
+                                     p->ctx_len, p->chunk_start, p->chunk_len, p->n_init, p->window, p->topk,
+                                     p->scale, s);
+  } else {
+    e = qat::launch_esa_generic(q, k_cache, v_cache, sel, n_sel, out, lse, false, p->batch, p->n_heads,
+                                p->head_dim, p->ctx_len, p->chunk_start, p->chunk_len, p->n_init, p->window,
+                                p->topk, p->scale, s);
+  }
+  return hip_status(e, "esa_sparse_attn");
+}
+
+// ---------------------------------------------------------------- MoBA
+QAT_EXPORT int moba_workspace_size(const qat_moba_params* p, size_t* bytes) {
+  int rc = moba_check(p);
+  if (rc) return rc;
+  if (!bytes) return fail(QAT_EINVAL, "bytes is NULL");
+  *bytes = moba_layout(p, nullptr).bytes;
+  return ok();
+}
+
+QAT_EXPORT int moba_block_select(const qat_moba_params* p, const void* q, const void* k, int32_t* blk, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  int rc = moba_check(p);
+  if (rc) return rc;
+  if (!q || !k || !blk) return fail(QAT_EINVAL, "q, k, blk must be non-NULL");
+  MobaLayout L = moba_layout(p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  L = moba_layout(p, ws);
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = p->dtype == QAT_BF16;
+  // only blocks that can be candidates of the processed rows are pooled
+  const int64_t nbc_need = std::min<int64_t>(L.nbc, (p->q_start + p->q_len - 1) / p->block);
+  hipError_t e = hipSuccess;
+  if (p->topk > 1 && nbc_need > 0) {
+    e = qat::launch_moba_meanpool(k, bf, p->batch, p->seq_len, p->n_kv_heads, p->head_dim, p->block, nbc_need,
+                                  L.mp_part, L.kbar, s);
+    if (e != hipSuccess) return hip_status(e, "moba_block_select: mean pool");
+  }
+  e = qat::launch_moba_select(q, bf, L.kbar, blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim,
+                              nbc_need, p->q_start, p->q_len, p->block, p->topk, s);
+  return hip_status(e, "moba_block_select: scoring");
+}
+
+QAT_EXPORT int moba_sparse_attn(const qat_moba_params* p, const void* q, const void* k, const void* v,
+                                const int32_t* blk, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int rc = moba_check(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !blk || !out) return fail(QAT_EINVAL, "q, k, v, blk, out must be non-NULL");
+  MobaLayout L = moba_layout(p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  L = moba_layout(p, ws);
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = p->dtype == QAT_BF16;
+  hipError_t e;
+  if (bf && p->window == 0) {
+    if (p->topk > 1 && L.nbuckets > 0) {
+      e = qat::launch_moba_dispatch(blk, p->batch, p->n_q_heads, p->n_kv_heads, p->q_start, p->q_len, p->block,
+                                    p->topk, L.nbc, L.counts, L.offsets, L.cursor, L.entries, L.tiles, L.ntiles, s);
+      if (e != hipSuccess) return hip_status(e, "moba_sparse_attn: dispatch");
+    }
+    e = qat::launch_moba_attn_mfma(q, k, v, blk, L.tiles, L.ntiles, L.offsets, L.entries, L.part_o, L.part_lse, out,
+                                   lse, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim, L.nbc,
+                                   p->q_start, p->q_len, p->block, p->topk, p->scale,
+                                   L.nbuckets > 0 ? L.max_tiles : 0, s);
+  } else {
+    e = qat::launch_moba_generic(q, k, v, blk, out, lse, bf, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads,
+                                 p->head_dim, p->q_start, p->q_len, p->block, p->topk, p->window, p->scale, s);
+  }
+  return hip_status(e, "moba_sparse_attn");
+}

@@ -1,0 +1,62 @@
+// Internal helpers shared by the HIP kernels of the library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qat {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Round a finite double to the nearest bfloat16 (ties to even) without an
+// intermediate float rounding: add half an ulp of the 45 discarded mantissa
+// bits (plus the kept LSB for ties-to-even) and truncate.
+__device__ __forceinline__ bf16 f64_to_bf16_rne(double x) {
+  uint64_t b = (uint64_t)__double_as_longlong(x);
+  uint64_t lsb = (b >> 45) & 1ull;
+  b += ((1ull << 44) - 1ull) + lsb;
+  b &= ~((1ull << 45) - 1ull);
+  return (bf16)(float)__longlong_as_double((long long)b);   // exact from here
+}
+
+// Order-preserving map float -> uint32 (larger float, larger key).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+__host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workspace carving helper: 256-byte aligned regions.
+struct Carver {
+  char* base;
+  size_t off;
+  __host__ explicit Carver(void* b) : base((char*)b), off(0) {}
+  template <typename T>
+  __host__ T* take(size_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+  __host__ size_t bytes() const { return (off + 255) & ~(size_t)255; }
+};
+
+}  // namespace qat

@@ -1,0 +1,121 @@
+// Compression of concatenated-head rows by one affine map, accumulated in
+// float64 on the fp64 matrix cores and rounded once.
+//
+// ESA write-up (hlszyjy.com/post/6872.html), paragraph on compressing query
+// and key from 4096 to 128 dimensions with a one-layer MLP: read as one
+// affine map out = W x + b. The products of two bf16 (or two fp32) values are
+// exact in float64 and the float64 sum of d_model of them is far below the
+// bf16 rounding grid, so the bf16 compressed-key cache written here is the
+// correctly rounded value of the exact product.
+#include "common.h"
+#include "launch.h"
+
+namespace qat {
+
+// One wave: 16 rows x 16 output columns over k in [k0, k1). The fp64 MFMA
+// 16x16x4 takes A[row = lane%16][k = lane/16], B[k = lane/16][col =
+// lane%16] and returns D[row = lane/16 + 4i][col = lane%16]. Each lane
+// loads 8 consecutive k of its row (and of its W row) per step; step s of 8
+// pairs k-slot j with k = kb + 8 j + s on both operands.
+template <typename TX, typename TW>
+__global__ __launch_bounds__(256) void compress_partial_kernel(
+    const TX* __restrict__ x, int64_t n, int64_t x_stride, int64_t d_model,
+    const TW* __restrict__ W, int64_t d_c, int64_t k_per_split, double* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int64_t col0 = ((int64_t)blockIdx.y * 4 + wave) * 16;
+  if (col0 >= d_c) return;
+  const int split = blockIdx.z;
+  const int64_t k0 = (int64_t)split * k_per_split;
+  const int64_t k1 = min(d_model, k0 + k_per_split);
+  const int r = lane & 15, j = lane >> 4;
+  const int64_t row = row0 + r;
+  const bool row_ok = row < n;
+  const TX* xr = x + (row_ok ? row : 0) * x_stride;
+  const TW* wr = W + (col0 + r) * d_model;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  for (int64_t kb = k0; kb < k1; kb += 32) {
+    const int64_t kk = kb + 8 * j;
+    double a[8], b[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      a[s] = row_ok ? (double)to_f32(xr[kk + s]) : 0.0;
+      b[s] = (double)to_f32(wr[kk + s]);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc, 0, 0, 0);
+  }
+  double* dst = partial + (int64_t)split * n * d_c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t orow = row0 + j + 4 * i;
+    if (orow < n) dst[orow * d_c + col0 + r] = acc[i];
+  }
+}
+
+// Sum the split partials in split order, add the bias, round once.
+// kind 0: float32 out; 1: bf16 out; 2: float32 out plus bf16 hi/lo split
+// (hi = bf16(v), lo = bf16(v - hi)) used by the two-term bf16 scoring.
+__global__ void compress_finalize_kernel(const double* __restrict__ partial, int nsplit, int64_t n,
+                                         int64_t d_c, const float* __restrict__ bias, void* out,
+                                         int64_t out_stride, int kind, bf16* __restrict__ hi,
+                                         bf16* __restrict__ lo) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * d_c) return;
+  const int64_t row = idx / d_c, col = idx % d_c;
+  double v = 0.0;
+  for (int s = 0; s < nsplit; ++s) v += partial[(int64_t)s * n * d_c + idx];
+  if (bias) v += (double)bias[col];
+  if (kind == 1) {
+    ((bf16*)out)[row * out_stride + col] = f64_to_bf16_rne(v);
+  } else {
+    const float f = (float)v;
+    ((float*)out)[row * out_stride + col] = f;
+    if (kind == 2) {
+      const bf16 h = (bf16)f;
+      hi[idx] = h;
+      lo[idx] = (bf16)(f - (float)h);
+    }
+  }
+}
+
+int compress_splits(int64_t n, int64_t d_model, int64_t d_c) {
+  const int64_t waves = cdiv(n, 16) * cdiv(d_c, 16);
+  int64_t ns = cdiv(2048, waves);
+  const int64_t max_ns = d_model / 256 > 0 ? d_model / 256 : 1;
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  return (int)ns;
+}
+
+hipError_t launch_compress_partial(const void* x, int64_t n, int64_t x_stride, int64_t d_model,
+                                   bool x_bf16, const void* W, bool w_bf16, int64_t d_c, int nsplit,
+                                   double* partial, hipStream_t s) {
+  const int64_t k_per_split = cdiv(d_model / 32, nsplit) * 32;
+  dim3 grid((unsigned)cdiv(n, 16), (unsigned)cdiv(d_c, 64), (unsigned)nsplit);
+  if (x_bf16 && w_bf16)
+    hipLaunchKernelGGL((compress_partial_kernel<bf16, bf16>), grid, dim3(256), 0, s, (const bf16*)x, n,
+                       x_stride, d_model, (const bf16*)W, d_c, k_per_split, partial);
+  else if (!x_bf16 && !w_bf16)
+    hipLaunchKernelGGL((compress_partial_kernel<float, float>), grid, dim3(256), 0, s, (const float*)x,
+                       n, x_stride, d_model, (const float*)W, d_c, k_per_split, partial);
+  else if (x_bf16)
+    hipLaunchKernelGGL((compress_partial_kernel<bf16, float>), grid, dim3(256), 0, s, (const bf16*)x, n,
+                       x_stride, d_model, (const float*)W, d_c, k_per_split, partial);
+  else
+    hipLaunchKernelGGL((compress_partial_kernel<float, bf16>), grid, dim3(256), 0, s, (const float*)x,
+                       n, x_stride, d_model, (const bf16*)W, d_c, k_per_split, partial);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_finalize(const double* partial, int nsplit, int64_t n, int64_t d_c,
+                                    const float* bias, void* out, int64_t out_stride, int kind,
+                                    bf16* hi, bf16* lo, hipStream_t s) {
+  const int64_t total = n * d_c;
+  hipLaunchKernelGGL(compress_finalize_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
+                     partial, nsplit, n, d_c, bias, out, out_stride, kind, hi, lo);
+  return hipGetLastError();
+}
+
+}  // namespace qat

@@ -1,0 +1,270 @@
+// ESA attention over the fused parts: initial + selected middle tokens
+// ("global") and local window + the chunk itself ("window"), one joint
+// softmax per head.
+//
+// ESA write-up (hlszyjy.com/post/6872.html), paragraph on the four-part
+// token split: initial tokens and the selected top-k middle tokens form the
+// global attention, local tokens the window attention, and the two are fused
+// into the final output; decode uses the single current query. CCA write-up
+// (m.jxzklqfsx.com/article/817694.html), global-local fusion section: both
+// parts' keys and values form one unified K/V, i.e. one softmax.
+//
+// Key list of a sequence (ascending positions, all before the chunk):
+//   j <  n_I                 -> j                      (initial)
+//   j <  n_I + n_sel         -> sel[j - n_I]           (selected middle)
+//   j <  n_I + n_sel + n_L   -> L0 + (j - n_I - n_sel) (local window)
+// followed by the chunk's own keys [c0, t] under the causal mask.
+#include "attn_core.h"
+#include "common.h"
+#include "launch.h"
+
+namespace qat {
+
+struct EsaKeys {
+  const int32_t* sel;
+  int64_t n_init, l0, n_l;
+  int32_t n_sel;
+  __device__ __forceinline__ int64_t count() const { return n_init + n_sel + n_l; }
+  __device__ __forceinline__ int64_t pos(int64_t j) const {
+    if (j < n_init) return j;
+    if (j < n_init + n_sel) return sel[j - n_init];
+    return l0 + (j - n_init - n_sel);
+  }
+};
+
+__device__ __forceinline__ EsaKeys esa_keys(const int32_t* sel, const int32_t* n_sel, int64_t bi, int topk,
+                                            int64_t c0, int64_t n_init, int64_t window) {
+  EsaKeys kl;
+  kl.sel = sel + bi * topk;
+  kl.n_sel = n_sel[bi];
+  kl.n_init = min(n_init, c0);
+  if (c0 > n_init) {
+    kl.l0 = max(n_init, c0 - window);
+    kl.n_l = c0 - kl.l0;
+  } else {
+    kl.l0 = c0;
+    kl.n_l = 0;
+  }
+  return kl;
+}
+
+// ---------------------------------------------------------------------------
+// Prefill / chunk attention on the matrix cores: grid (128-row tiles of the
+// chunk, head, sequence).
+template <int D>
+__global__ __launch_bounds__(256, 2) void esa_prefill_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, bf16* __restrict__ out,
+    float* __restrict__ lse_out, int64_t H, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
+    int64_t window, int topk, float scale_log2) {
+  extern __shared__ __align__(16) char smem_raw[];
+  FaSmem<D>& sm = *reinterpret_cast<FaSmem<D>*>(smem_raw);
+  const int64_t bi = blockIdx.z, h = blockIdx.y;
+  const int64_t i0 = (int64_t)blockIdx.x * 128;
+  const int64_t i_last = min(m, i0 + 128) - 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t i = i0 + wave * 32 + (lane & 31);
+  const bool valid = i <= i_last;
+  const bf16* qrow = q + ((bi * m + (valid ? i : i0)) * H + h) * D;
+  FaState<D> st;
+  fa_init<D>(st, qrow, valid);
+  const EsaKeys kl = esa_keys(sel, n_sel, bi, topk, c0, n_init, window);
+  const int64_t seq0 = bi * ctx_len;
+  fa_segment<D>(st, sm, kc, vc, kl.count(), scale_log2,
+                [=](int64_t j) -> int64_t { return ((seq0 + kl.pos(j)) * H + h) * D; },
+                [=](int64_t) { return valid; });
+  const int64_t qi = valid ? i : -1;
+  fa_segment<D>(st, sm, kc, vc, i_last + 1, scale_log2,
+                [=](int64_t j) -> int64_t { return ((seq0 + c0 + j) * H + h) * D; },
+                [=](int64_t j) { return j <= qi; });
+  float inv_l, lse;
+  fa_finish<D>(st, inv_l, lse);
+  if (!valid) return;
+  bf16* dst = out + ((bi * m + i) * H + h) * D;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (bf16)(st.o[t][i4 * 4 + e] * inv_l);
+      *(bf16x4*)(dst + fa_d_of(t, i4 * 4)) = w;
+    }
+  if (lse_out && (lane >> 5) == 0) lse_out[(bi * m + i) * H + h] = lse;
+}
+
+// ---------------------------------------------------------------------------
+// Decode (one query per sequence): split-K over the key list. A workgroup of
+// 256 threads covers the whole concatenated-head row (E = H*D/256 elements
+// per thread, D/E lanes per head) and a contiguous slice of the key list;
+// every gathered key row is one contiguous H*D*2-byte read. Partial
+// (o, m, l) per (sequence, split, head) go to scratch; a second kernel merges
+// them by log-sum-exp.
+constexpr int kDecKeysPerSplit = 64;
+constexpr int kDecUnroll = 4;
+
+template <int E>
+__global__ __launch_bounds__(256) void esa_decode_attn_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, float* __restrict__ po,
+    float* __restrict__ pm, float* __restrict__ pl, int64_t H, int64_t D, int64_t ctx_len, int64_t c0,
+    int64_t n_init, int64_t window, int topk, int nsplit, float scale_log2) {
+  const int64_t bi = blockIdx.y;
+  const int split = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t HD = H * D;
+  const EsaKeys kl = esa_keys(sel, n_sel, bi, topk, c0, n_init, window);
+  const int64_t nkeys = kl.count() + 1;   // + the query's own position c0
+  const int64_t j0 = (int64_t)split * kDecKeysPerSplit;
+  const int64_t j1 = min(nkeys, j0 + kDecKeysPerSplit);
+  const int lph = (int)(D / E);          // lanes per head
+  const int64_t e0 = (int64_t)tid * E;   // element offset in the row
+  float qv[E], o[E];
+  {
+    const bf16* qr = q + bi * HD + e0;
+#pragma unroll
+    for (int e = 0; e < E; e += 8) {
+      const bf16x8 t8 = *(const bf16x8*)(qr + e);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) qv[e + x] = (float)t8[x];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  float m = -__builtin_inff(), l = 0.f;
+  const bf16* kb = kc + bi * ctx_len * HD + e0;
+  const bf16* vb = vc + bi * ctx_len * HD + e0;
+  for (int64_t jb = j0; jb < j1; jb += kDecUnroll) {
+    bf16x8 kr[kDecUnroll][E / 8], vr[kDecUnroll][E / 8];
+    bool ok[kDecUnroll];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int64_t j = jb + u;
+      ok[u] = j < j1;
+      const int64_t p = ok[u] ? (j < nkeys - 1 ? kl.pos(j) : c0) : c0;
+#pragma unroll
+      for (int e = 0; e < E / 8; ++e) {
+        kr[u][e] = *(const bf16x8*)(kb + p * HD + 8 * e);
+        vr[u][e] = *(const bf16x8*)(vb + p * HD + 8 * e);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < E / 8; ++e)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) s = fmaf(qv[8 * e + x], (float)kr[u][e][x], s);
+      for (int off = 1; off < lph; off <<= 1) s += __shfl_xor(s, off, 64);
+      const float x = ok[u] ? s * scale_log2 : -__builtin_inff();
+      const float m_new = fmaxf(m, x);
+      const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+      const float alpha = exp2f(m - m_use);
+      const float p = exp2f(x - m_use);
+      l = l * alpha + p;
+#pragma unroll
+      for (int e = 0; e < E / 8; ++e)
+#pragma unroll
+        for (int xx = 0; xx < 8; ++xx) o[8 * e + xx] = o[8 * e + xx] * alpha + p * (float)vr[u][e][xx];
+      m = m_new;
+    }
+  }
+  const int64_t head = e0 / D;
+  const int64_t pidx = (bi * nsplit + split) * H + head;
+  float* dst = po + pidx * D + (e0 % D);
+#pragma unroll
+  for (int e = 0; e < E; ++e) dst[e] = o[e];
+  if ((e0 % D) == 0) {
+    pm[pidx] = m;
+    pl[pidx] = l;
+  }
+}
+
+__global__ void esa_decode_combine_kernel(const float* __restrict__ po, const float* __restrict__ pm,
+                                          const float* __restrict__ pl, const int32_t* __restrict__ n_sel,
+                                          bf16* __restrict__ out, float* __restrict__ lse_out, int64_t H, int64_t D,
+                                          int64_t c0, int64_t n_init, int64_t window, int nsplit_max) {
+  const int64_t bi = blockIdx.y;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // element of the H*D row
+  if (idx >= H * D) return;
+  const int64_t head = idx / D;
+  // number of splits actually holding keys for this sequence
+  int64_t n_i = min(n_init, c0), n_l = 0;
+  if (c0 > n_init) n_l = c0 - max(n_init, c0 - window);
+  const int64_t nkeys = n_i + n_sel[bi] + n_l + 1;
+  const int ns = (int)min((int64_t)nsplit_max, cdiv(nkeys, kDecKeysPerSplit));
+  float M = -__builtin_inff();
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[(bi * nsplit_max + s) * H + head]);
+  float L = 0.f, O = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const int64_t p = (bi * nsplit_max + s) * H + head;
+    const float w = exp2f(pm[p] - M);
+    L += pl[p] * w;
+    O += po[p * D + (idx % D)] * w;
+  }
+  out[bi * H * D + idx] = (bf16)(O / L);
+  if (lse_out && (idx % D) == 0) lse_out[bi * H + head] = M * kLn2 + logf(L);
+}
+
+// ---------------------------------------------------------------------------
+int esa_decode_splits(int64_t n_init, int64_t topk, int64_t window) {
+  return (int)cdiv(n_init + topk + window + 1, kDecKeysPerSplit);
+}
+
+hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, const int32_t* sel,
+                                   const int32_t* n_sel, void* out, float* lse, int64_t batch, int64_t H,
+                                   int64_t D, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
+                                   int64_t window, int topk, float scale, hipStream_t s) {
+  dim3 grid((unsigned)cdiv(m, 128), (unsigned)H, (unsigned)batch);
+  const float sl2 = scale * kLog2e;
+  hipError_t e;
+  if (D == 64) {
+    const size_t smem = sizeof(FaSmem<64>);
+    e = hipFuncSetAttribute((const void*)esa_prefill_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(esa_prefill_kernel<64>, grid, dim3(256), smem, s, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, sel, n_sel, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2);
+  } else {
+    const size_t smem = sizeof(FaSmem<128>);
+    e = hipFuncSetAttribute((const void*)esa_prefill_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(esa_prefill_kernel<128>, grid, dim3(256), smem, s, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, sel, n_sel, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2);
+  }
+  return hipGetLastError();
+}
+
+bool esa_decode_supported(int64_t H, int64_t D) {
+  const int64_t HD = H * D;
+  if (HD % 256) return false;
+  const int64_t E = HD / 256;
+  return (E == 8 || E == 16 || E == 32) && D % E == 0 && (D / E) <= 64;
+}
+
+hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, const int32_t* sel,
+                                  const int32_t* n_sel, float* po, float* pm, float* pl, void* out, float* lse,
+                                  int64_t batch, int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t n_init,
+                                  int64_t window, int topk, float scale, hipStream_t s) {
+  const int nsplit = esa_decode_splits(n_init, topk, window);
+  dim3 grid((unsigned)nsplit, (unsigned)batch);
+  const float sl2 = scale * kLog2e;
+  const int64_t E = H * D / 256;
+#define QAT_DEC(E_)                                                                                         \
+  hipLaunchKernelGGL(esa_decode_attn_kernel<E_>, grid, dim3(256), 0, s, (const bf16*)q, (const bf16*)k,     \
+                     (const bf16*)v, sel, n_sel, po, pm, pl, H, D, ctx_len, c0, n_init, window, topk, nsplit, \
+                     sl2)
+  if (E == 8) QAT_DEC(8);
+  else if (E == 16) QAT_DEC(16);
+  else QAT_DEC(32);
+#undef QAT_DEC
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2((unsigned)cdiv(H * D, 256), (unsigned)batch);
+  hipLaunchKernelGGL(esa_decode_combine_kernel, g2, dim3(256), 0, s, po, pm, pl, n_sel, (bf16*)out, lse, H, D, c0,
+                     n_init, window, nsplit);
+  return hipGetLastError();
+}
+
+}  // namespace qat

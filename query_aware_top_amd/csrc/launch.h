@@ -1,0 +1,79 @@
+// Host-side launchers of the HIP kernels, called by the C ABI layer after it
+// has validated the arguments. Each enqueues on stream `s` and returns
+// hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace qat {
+
+// ---- compression (compress.hip) -------------------------------------------
+int compress_splits(int64_t n, int64_t d_model, int64_t d_c);
+hipError_t launch_compress_partial(const void* x, int64_t n, int64_t x_stride, int64_t d_model, bool x_bf16,
+                                   const void* W, bool w_bf16, int64_t d_c, int nsplit, double* partial,
+                                   hipStream_t s);
+// kind 0: float32 out, 1: bf16 out, 2: float32 out plus bf16 hi/lo rows.
+hipError_t launch_compress_finalize(const double* partial, int nsplit, int64_t n, int64_t d_c, const float* bias,
+                                    void* out, int64_t out_stride, int kind, bf16* hi, bf16* lo, hipStream_t s);
+
+// ---- MoBA gating (moba_select.hip) ----------------------------------------
+int meanpool_splits(int block);
+hipError_t launch_moba_meanpool(const void* k, bool bf, int64_t batch, int64_t seq_len, int64_t hkv, int64_t d,
+                                int block, int64_t nbc, double* partial, float* kbar, hipStream_t s);
+hipError_t launch_moba_select(const void* q, bool bf, const float* kbar, int32_t* blk, int64_t batch,
+                              int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t nbc, int64_t q_start,
+                              int64_t q_len, int block, int topk, hipStream_t s);
+
+// ---- MoBA attention (moba_attn.hip) ---------------------------------------
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+int64_t moba_max_tiles(int64_t nrows, int topk, int64_t nbuckets);
+hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t hq, int64_t hkv, int64_t q_start,
+                                int64_t q_len, int block, int topk, int64_t nbc, int32_t* counts, int32_t* offsets,
+                                int32_t* cursor, int32_t* entries, int2* tiles, int32_t* ntiles, hipStream_t s);
+hipError_t launch_moba_attn_mfma(const void* q, const void* k, const void* v, const int32_t* blk, const int2* tiles,
+                                 const int32_t* ntiles, const int32_t* offsets, const int32_t* entries,
+                                 void* part_o, float* part_lse, void* out, float* lse, int64_t batch,
+                                 int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t nbc, int64_t q_start,
+                                 int64_t q_len, int block, int topk, float scale, int64_t max_tiles, hipStream_t s);
+
+// ---- generic per-row attention (attn_generic.hip) -------------------------
+hipError_t launch_moba_generic(const void* q, const void* k, const void* v, const int32_t* blk, void* out,
+                               float* lse, bool bf, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
+                               int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int window,
+                               float scale, hipStream_t s);
+hipError_t launch_esa_generic(const void* q, const void* k, const void* v, const int32_t* sel, const int32_t* n_sel,
+                              void* out, float* lse, bool bf, int64_t batch, int64_t H, int64_t d, int64_t ctx_len,
+                              int64_t c0, int64_t m, int64_t n_init, int64_t window, int topk, float scale,
+                              hipStream_t s);
+
+// ---- ESA selection (esa_select.hip) ---------------------------------------
+int esa_key_splits(int64_t n_mid, int64_t m);
+int esa_prefill_qsplits_eff(int64_t n_mid, int64_t m);
+int esa_scan_wgs(int64_t n_mid);
+hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const bf16* kc, int64_t batch, int64_t m,
+                                     int64_t ctx_len, int64_t mid0, int64_t n_mid, int64_t d_c, float clip,
+                                     float* rowmax_part, float* rowmax, float* upart, hipStream_t s);
+hipError_t launch_esa_decode_scan(const float* qc, const bf16* kc, int64_t batch, int64_t ctx_len, int64_t mid0,
+                                  int64_t n_mid, int64_t d_c, float* s_out, float* smax_part, hipStream_t s);
+hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const float* s_in, const float* smax_part,
+                           int nsmax, float clip, int64_t batch, int64_t n_mid, int radius, int topk, int64_t mid0,
+                           float* u_tmp, uint32_t* keys, float* scores_out, int32_t* sel, int32_t* n_sel,
+                           hipStream_t s);
+
+// ---- ESA attention (esa_attn.hip) -----------------------------------------
+int esa_decode_splits(int64_t n_init, int64_t topk, int64_t window);
+bool esa_decode_supported(int64_t H, int64_t D);
+hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, const int32_t* sel,
+                                   const int32_t* n_sel, void* out, float* lse, int64_t batch, int64_t H, int64_t D,
+                                   int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init, int64_t window, int topk,
+                                   float scale, hipStream_t s);
+hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, const int32_t* sel,
+                                  const int32_t* n_sel, float* po, float* pm, float* pl, void* out, float* lse,
+                                  int64_t batch, int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t n_init,
+                                  int64_t window, int topk, float scale, hipStream_t s);
+
+}  // namespace qat
