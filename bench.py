@@ -1,0 +1,397 @@
+"""Benchmark of the query-aware sparse attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+block gating (mean pool, block scores, top-k with the forced block) and
+block-sparse attention for MoBA; key compression of the new tokens, query
+compression, scoring, correction, neighbour pooling, top-k and fused
+attention for ESA. Inputs are generated on the GPU (seeded) and resident in
+HBM before timing starts; outputs and workspaces are preallocated.
+
+Prints one JSON line. Default workload: MoBA prefill at the 8B-style GQA
+shape (32 query / 8 KV heads x 128, N = 32768, block 512, top-k 3 with the
+forced block, 8 planted key blocks), reported as query tokens per second.
+Other workloads (--workload): moba_fp32_4k, esa_prefill_64k,
+esa_decode_128k, moba_long_512k.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn prefill query-tokens/s + decode us/step; % MFMA peak / % HBM BW"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+CSRC = os.path.join(ROOT, "query_aware_top_amd", "csrc")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or
+    None when absent or taken on different kernel sources."""
+    try:
+        with open(COUNTERS) as fh:
+            c = json.load(fh)
+    except OSError:
+        return None
+    e = c.get(f"{workload}/{kernel}")
+    if not e or e.get("source_sha") != kernel_source_sha():
+        return None
+    return e["hbm_bytes_per_launch"]
+
+
+# ----------------------------------------------------------------- workloads
+class Workload:
+    name = ""
+    unit = ""
+    higher_is_better = True
+    dtype = "bf16"
+    dominant = ""
+    bound = "mfma"
+
+    def step(self):
+        raise NotImplementedError
+
+    def value(self, sec_per_step):
+        raise NotImplementedError
+
+    def dominant_work(self):
+        """Algorithmic FLOPs (mfma) or bytes (hbm) per launch of the dominant kernel."""
+        raise NotImplementedError
+
+
+class MobaWorkload(Workload):
+    def __init__(self, name, seed, n, hq, hkv, d, block, topk, dtype, planted=0, attn_rows=None):
+        import query_aware_top_amd as qat
+        import synth
+        self.qat = qat
+        self.name = name
+        self.unit = "query-tokens/s"
+        self.dtype = "bf16" if dtype == torch.bfloat16 else "f32"
+        self.n, self.hq, self.hkv, self.d, self.block, self.topk = n, hq, hkv, d, block, topk
+        self.q, self.k, self.v, _ = synth.moba_inputs(seed, 1, n, hq, hkv, d, dtype, "cuda", planted=planted,
+                                                      block=block)
+        self.q_start = 0 if attn_rows is None else n - attn_rows
+        self.p_sel = qat.moba_params(batch=1, seq_len=n, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, block=block,
+                                     topk=topk, dtype=dtype)
+        self.p_att = qat.moba_params(batch=1, seq_len=n, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                                     q_start=self.q_start, q_len=n - self.q_start, block=block, topk=topk,
+                                     dtype=dtype)
+        ws = max(qat.moba_workspace_size(self.p_sel), qat.moba_workspace_size(self.p_att))
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        self.blk = torch.empty(1, n, hq, topk, dtype=torch.int32, device="cuda")
+        self.out = torch.empty(1, n - self.q_start, hq, d, dtype=dtype, device="cuda")
+        self.lse = torch.empty(1, n - self.q_start, hq, dtype=torch.float32, device="cuda")
+        self.dominant = "moba_past_attn"
+        self.bound = "mfma" if dtype == torch.bfloat16 else "alu"
+        if dtype != torch.bfloat16:
+            self.dominant = "moba_generic_attn"
+
+    def step(self):
+        qat = self.qat
+        qat.moba_block_select(self.p_sel, self.q, self.k, blk=self.blk, ws=self.ws)
+        qat.moba_sparse_attn(self.p_att, self.q, self.k, self.v, self.blk[:, self.q_start:], out=self.out,
+                             lse=self.lse, ws=self.ws)
+
+    def value(self, sec):
+        return (self.n - self.q_start) / sec
+
+    def pair_counts(self):
+        blk = self.blk[0, self.q_start:].to(torch.int64)
+        t = torch.arange(self.q_start, self.n, device="cuda")
+        cur = (t // self.block)[:, None, None]
+        past = ((blk >= 0) & (blk < cur)).sum().item()
+        cur_pairs = ((t % self.block) + 1).sum().item() * self.hq
+        return past * self.block, cur_pairs
+
+    def dominant_work(self):
+        past_pairs, cur_pairs = self.pair_counts()
+        if self.dominant == "moba_past_attn":
+            return past_pairs * 4 * self.d
+        return (past_pairs + cur_pairs) * 4 * self.d
+
+    def config(self):
+        return {"workload": self.name, "batch": 1, "seq_len": self.n, "n_q_heads": self.hq,
+                "n_kv_heads": self.hkv, "head_dim": self.d, "block": self.block, "topk_incl_current": self.topk,
+                "query_rows": self.n - self.q_start}
+
+    def cpu_baseline(self, budget_s=12.0):
+        """The float64 oracle on host cores over a bounded sample of query rows
+        (block gating + attention for every head of each sampled row)."""
+        import numpy as np
+        from oracle import attention as oatt
+        from oracle import moba as omoba
+        t0 = time.perf_counter()
+        kn = self.k[0].to("cpu").to(torch.float64).numpy()
+        vn = self.v[0].to("cpu").to(torch.float64).numpy()
+        kbar = omoba.block_means(kn, self.block)
+        rows_all = np.random.default_rng(0).permutation(np.arange(self.q_start, self.n))
+        qcpu = self.q[0].to("cpu")
+        done = 0
+        while done < len(rows_all) and (time.perf_counter() - t0 < budget_s or done < 16):
+            t = int(rows_all[done])
+            qt = qcpu[t].to(torch.float64).numpy()
+            for h in range(self.hq):
+                g = omoba.kv_head(h, self.hq, self.hkv)
+                blk, _ = omoba.select_row(qt[h], kbar[:, g], t, self.block, self.topk)
+                idx = omoba.key_set(blk, t, self.block)
+                oatt.attend(qt[h], kn[idx, g], vn[idx, g], self.p_att.scale)
+            done += 1
+        el = time.perf_counter() - t0
+        return {"value": done / el, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{done} random query positions (all {self.hq} heads each) of the {self.n}-token "
+                          f"sequence, block means over the whole sequence included; float64 numpy, one "
+                          f"process and thread; {el:.1f} s"}
+
+
+class EsaWorkload(Workload):
+    def __init__(self, name, seed, batch, T, m, H, d, d_c, n_init, W, topk, radius, clip, needles=0):
+        import query_aware_top_amd as qat
+        import synth
+        self.qat = qat
+        self.name = name
+        self.B, self.T, self.m, self.H, self.d, self.d_c = batch, T, m, H, d, d_c
+        self.c0 = T - m
+        self.n_init, self.W, self.topk = n_init, W, topk
+        dtype = torch.bfloat16
+        _, self.k, self.v, _ = synth.esa_inputs(seed, batch, T, 1, H, d, dtype, "cuda")
+        self.q = synth.normal(seed, synth.gen.TID_Q, (batch, m, H, d), dtype, "cuda", start=1 << 40)
+        if needles:
+            for bi in range(batch):
+                pos = synth.needle_positions(seed, bi, needles, n_init, self.c0 - W, 2 * radius + 1)
+                val = (self.q[bi, 0].to(torch.float64) * 0.375).to(dtype)
+                for t in pos:
+                    self.k[bi, t] = val
+        self.Wq = synth.compression_weights(seed, d_c, H * d, synth.gen.TID_W, dtype, "cuda")
+        self.Wk = self.Wq
+        self.p = qat.esa_params(batch=batch, n_heads=H, head_dim=d, d_c=d_c, ctx_len=T, chunk_start=self.c0,
+                                chunk_len=m, n_init=n_init, window=W, topk=topk, radius=radius, clip=clip)
+        # compressed-key cache of the tokens before the chunk: state written by
+        # earlier steps (untimed prologue)
+        self.kc = torch.zeros(batch, T, d_c, dtype=dtype, device="cuda")
+        qat.esa_compress(self.k.view(batch * T, H * d), self.Wk, out=self.kc.view(batch * T, d_c))
+        self.ws = torch.empty(qat.esa_workspace_size(self.p), dtype=torch.uint8, device="cuda")
+        import ctypes
+        nb = ctypes.c_size_t(0)
+        qat.lib().esa_compress_workspace_size(batch * m, H * d, d_c, ctypes.byref(nb))
+        self.ws_c = torch.empty(max(nb.value, 256), dtype=torch.uint8, device="cuda")
+        self.sel = torch.empty(batch, topk, dtype=torch.int32, device="cuda")
+        self.n_sel = torch.empty(batch, dtype=torch.int32, device="cuda")
+        self.out = torch.empty(batch, m, H, d, dtype=dtype, device="cuda")
+        self.lse = torch.empty(batch, m, H, dtype=torch.float32, device="cuda")
+        if m == 1:
+            self.unit, self.higher_is_better = "us/step", False
+            self.dominant, self.bound = "esa_decode_attn", "hbm"
+        else:
+            self.unit = "query-tokens/s"
+            self.dominant, self.bound = "esa_prefill_attn", "mfma"
+
+    def step(self):
+        qat = self.qat
+        B, T, H, d, m = self.B, self.T, self.H, self.d, self.m
+        # compress the chunk's new keys into the cache
+        qat.esa_compress(self.k.view(B * T, H * d)[self.c0:], self.Wk, out=self.kc.view(B * T, -1)[self.c0:],
+                         n=B if m == 1 else m, x_stride=T * H * d if m == 1 else H * d,
+                         out_stride=T * self.d_c if m == 1 else self.d_c, ws=self.ws_c)
+        qat.esa_select(self.p, self.q, self.Wq, None, self.kc, sel=self.sel, n_sel=self.n_sel, ws=self.ws)
+        qat.esa_sparse_attn(self.p, self.q, self.k, self.v, self.sel, self.n_sel, out=self.out, lse=self.lse,
+                            ws=self.ws)
+
+    def value(self, sec):
+        return sec * 1e6 if self.m == 1 else self.B * self.m / sec
+
+    def n_keys(self):
+        n_i = min(self.n_init, self.c0)
+        n_l = self.c0 - max(self.n_init, self.c0 - self.W) if self.c0 > self.n_init else 0
+        return n_i + int(self.n_sel[0]) + n_l
+
+    def dominant_work(self):
+        if self.m == 1:   # gathered K and V rows of every head + q and out
+            return self.B * (self.n_keys() + 1) * self.H * self.d * 2 * 2 + 2 * self.B * self.H * self.d * 2
+        g = self.n_keys()
+        pairs = self.m * g + self.m * (self.m + 1) // 2
+        return pairs * self.H * 4 * self.d
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "ctx_len": self.T, "chunk_len": self.m,
+                "n_heads": self.H, "head_dim": self.d, "d_c": self.d_c, "n_init": self.n_init,
+                "topk": self.topk, "window": self.W}
+
+    def cpu_baseline(self, budget_s=12.0):
+        import numpy as np
+        from oracle import esa as oesa
+        t0 = time.perf_counter()
+        bi = 0
+        W = self.Wq.to("cpu").to(torch.float64).numpy()
+        kc = np.zeros((self.c0, self.d_c))
+        kcpu = self.k[bi, :self.c0]
+        for s in range(0, self.c0, 8192):
+            kc[s:s + 8192] = oesa.key_cache(kcpu[s:s + 8192].to("cpu").to(torch.float64).numpy(), W)
+        qn = self.q[bi].to("cpu").to(torch.float64).numpy()
+        sel, _, _, _ = oesa.select(qn, W, None, kc, self.c0, self.n_init, self.W, self.topk, self.p.radius,
+                                   self.p.clip)
+        t_sel = time.perf_counter() - t0
+        rows = 0
+        kk = _GpuRows(self.k[bi])
+        vv = _GpuRows(self.v[bi])
+        order = np.random.default_rng(0).permutation(self.m)
+        while rows < self.m and (time.perf_counter() - t0 < budget_s or rows < 1):
+            oesa.attend(qn, kk, vv, sel, self.c0, self.n_init, self.W, self.p.scale, rows=[int(order[rows])])
+            rows += 1
+        el = time.perf_counter() - t0
+        cores = _blas_threads()
+        if self.m == 1:
+            per_seq = el
+            return {"value": per_seq * 1e6 * self.B, "unit": "us/step", "cores": cores, "kind": "oracle",
+                    "sample": f"sequence 0 of {self.B} (key compression of the cache, selection, attention), "
+                              f"scaled by {self.B} sequences; float64 numpy with BLAS threads for the matrix products, "
+                              f"BLAS threads for the matrix products, one process; {el:.1f} s"}
+        att_per_row = (el - t_sel) / rows
+        est = t_sel + att_per_row * self.m
+        return {"value": self.m / est, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+                "sample": f"selection for the whole {self.m}-query chunk (with compression of the key cache) "
+                          f"plus attention for {rows} of its rows, extrapolated to the chunk; float64 numpy, "
+                          f"BLAS threads for the matrix products, one process; {el:.1f} s"}
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        return 1
+
+
+class _GpuRows:
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, idx):
+        import numpy as np
+        ix = torch.as_tensor(np.asarray(idx), device=self.t.device, dtype=torch.long)
+        return self.t.index_select(0, ix).to("cpu").to(torch.float64).numpy()
+
+
+def make(name):
+    if name == "moba_gqa_32k":
+        return MobaWorkload(name, 2, 32768, 32, 8, 128, 512, 3, torch.bfloat16, planted=8)
+    if name == "moba_fp32_4k":
+        return MobaWorkload(name, 1, 4096, 4, 4, 64, 256, 3, torch.float32)
+    if name == "moba_long_512k":
+        return MobaWorkload(name, 5, 524288, 8, 8, 128, 8192, 3, torch.bfloat16, attn_rows=8192)
+    if name == "esa_prefill_64k":
+        return EsaWorkload(name, 3, 1, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0)
+    if name == "esa_decode_128k":
+        return EsaWorkload(name, 4, 16, 131072, 1, 32, 128, 128, 128, 4096, 2048, 2, 48.0, needles=16)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="moba_gqa_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="run one plain device-to-device copy of BYTES before warmup (reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              f"see DESIGN.md for how the path would shard.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import query_aware_top_amd as qat
+    qat.lib()
+    w = make(args.workload)
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+    qat.timing_enable(True)
+    qat.timing_reset()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        w.step()
+    stop.record()
+    torch.cuda.synchronize()
+    qat.timing_enable(False)
+    ms = start.elapsed_time(stop) / args.steps
+    kernels = {}
+    for name in ("moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn", "moba_current_attn",
+                 "moba_generic_attn", "esa_compress", "esa_qcompress", "esa_scores", "esa_decode_scan", "esa_topk",
+                 "esa_prefill_attn", "esa_decode_attn", "esa_generic_attn"):
+        tot, n = qat.timing_query(name)
+        if n:
+            kernels[name] = round(tot / n, 4)
+    qat.timing_reset()
+    dom_ms = kernels.get(w.dominant)
+    work = w.dominant_work()
+    if w.bound == "hbm":
+        achieved = work / (dom_ms * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    elif w.bound == "mfma":
+        achieved = work / (dom_ms * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved = work / (dom_ms * 1e-3) / 1e12
+        peak, unit = PEAK_F32_TFLOPS, "TFLOP/s"
+    value = w.value(ms * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": w.unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": w.higher_is_better,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs generated on the GPU; see DESIGN.md for the recipe)",
+        "config": w.config(),
+        "roofline": {"kernel": w.dominant, "bound": w.bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic_for(w.dominant, w.name), "work_per_launch": work,
+                     "avg_launch_ms": dom_ms},
+        "kernels_avg_ms": kernels,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = w.cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -55,6 +55,21 @@ const char* qat_last_error(void);
 /* Returns QAT_ABI_VERSION of the loaded library. */
 int qat_abi_version(void);
 
+/*
+ * Kernel timing for benchmarks: while enabled, the library records a pair of
+ * HIP events on the launch stream around each of its main kernels
+ * (names: "moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn",
+ * "moba_current_attn", "moba_generic_attn", "esa_compress", "esa_scores",
+ * "esa_decode_scan", "esa_topk", "esa_prefill_attn", "esa_decode_attn",
+ * "esa_generic_attn"). qat_timing_query synchronises on the recorded events
+ * and returns the summed milliseconds and the launch count for one name;
+ * qat_timing_reset drops the records. Host memory only; no device memory is
+ * allocated.
+ */
+int qat_timing_enable(int on);
+int qat_timing_reset(void);
+int qat_timing_query(const char* name, double* total_ms, int* count);
+
 /* ======================================================================
  * ESA -- token-level selection by compressed q/k   [ESA]
  * ====================================================================== */

@@ -24,4 +24,7 @@ from ._binding import (  # noqa: F401
     moba_block_select,
     moba_sparse_attn,
     EXPORTED_SYMBOLS,
+    timing_enable,
+    timing_reset,
+    timing_query,
 )

@@ -14,7 +14,7 @@ QAT_F32, QAT_BF16 = 0, 1
 _STATUS = {0: "QAT_OK", -1: "QAT_EINVAL", -2: "QAT_EUNSUPPORTED", -3: "QAT_EWORKSPACE", -4: "QAT_EHIP"}
 
 EXPORTED_SYMBOLS = (
-    "qat_last_error", "qat_abi_version",
+    "qat_last_error", "qat_abi_version", "qat_timing_enable", "qat_timing_reset", "qat_timing_query",
     "esa_workspace_size", "esa_compress_workspace_size", "esa_compress", "esa_select", "esa_sparse_attn",
     "moba_workspace_size", "moba_block_select", "moba_sparse_attn",
 )
@@ -66,6 +66,9 @@ def lib():
         L.esa_sparse_attn.argtypes = [ctypes.POINTER(EsaParams), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moba_workspace_size.argtypes = [ctypes.POINTER(MobaParams), ctypes.POINTER(sz)]
         L.moba_block_select.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, sz, vp]
+        L.qat_timing_enable.argtypes = [ctypes.c_int]
+        L.qat_timing_reset.argtypes = []
+        L.qat_timing_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         L.moba_sparse_attn.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTED_SYMBOLS:
             getattr(L, name).restype = ctypes.c_int if name != "qat_last_error" else ctypes.c_char_p
@@ -75,6 +78,22 @@ def lib():
 
 def abi_version() -> int:
     return lib().qat_abi_version()
+
+
+def timing_enable(on: bool = True):
+    """Per-kernel HIP-event timing inside the library (see qat_timing_enable)."""
+    _check(lib().qat_timing_enable(1 if on else 0))
+
+
+def timing_reset():
+    _check(lib().qat_timing_reset())
+
+
+def timing_query(name: str):
+    """Returns (total_ms, launches) recorded for one kernel name."""
+    tot, n = ctypes.c_double(0), ctypes.c_int(0)
+    _check(lib().qat_timing_query(name.encode(), ctypes.byref(tot), ctypes.byref(n)))
+    return tot.value, n.value
 
 
 def _check(rc: int):

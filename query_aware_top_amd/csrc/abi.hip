@@ -3,7 +3,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/qat.h"
 #include "common.h"
@@ -181,11 +184,92 @@ MobaLayout moba_layout(const qat_moba_params* p, void* ws) {
   return L;
 }
 
+// ---------------------------------------------------------------- timing
+struct TimerRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimerRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+std::map<std::string, hipEvent_t> g_open;
+
+hipEvent_t pool_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
 }  // namespace
+
+namespace qat {
+void ktimer_start(const char* name, hipStream_t s) {
+  if (!g_timing) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  hipEvent_t e = pool_event();
+  if (!e) return;
+  (void)hipEventRecord(e, s);
+  g_open[name] = e;
+}
+void ktimer_stop(const char* name, hipStream_t s) {
+  if (!g_timing) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  auto it = g_open.find(name);
+  if (it == g_open.end()) return;
+  hipEvent_t e = pool_event();
+  if (!e) return;
+  (void)hipEventRecord(e, s);
+  g_recs.push_back({name, it->second, e});
+  g_open.erase(it);
+}
+}  // namespace qat
 
 // ======================================================================
 QAT_EXPORT const char* qat_last_error(void) { return g_last_error.c_str(); }
 QAT_EXPORT int qat_abi_version(void) { return QAT_ABI_VERSION; }
+
+QAT_EXPORT int qat_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = on != 0;
+  return ok();
+}
+
+QAT_EXPORT int qat_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto& r : g_recs) {
+    (void)hipEventSynchronize(r.b);
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return ok();
+}
+
+QAT_EXPORT int qat_timing_query(const char* name, double* total_ms, int* count) {
+  if (!name || !total_ms || !count) return fail(QAT_EINVAL, "name, total_ms and count must be non-NULL");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  double tot = 0.0;
+  int n = 0;
+  for (auto& r : g_recs) {
+    if (r.name != name) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_status(e, "qat_timing_query");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_status(e, "qat_timing_query");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *count = n;
+  return ok();
+}
 
 // ---------------------------------------------------------------- ESA
 QAT_EXPORT int esa_workspace_size(const qat_esa_params* p, size_t* bytes) {
@@ -223,6 +307,7 @@ QAT_EXPORT int esa_compress(const void* x, int64_t n, int64_t x_stride, int64_t 
   hipStream_t s = (hipStream_t)stream;
   const int ns = qat::compress_splits(n, d_model, d_c);
   const bool bf = in_dtype == QAT_BF16;
+  qat::KTimer tm("esa_compress", s);
   hipError_t e = qat::launch_compress_partial(x, n, x_stride, d_model, bf, W, bf, d_c, ns, (double*)ws, s);
   if (e == hipSuccess)
     e = qat::launch_compress_finalize((const double*)ws, ns, n, d_c, bias, out, out_stride,
@@ -243,21 +328,28 @@ QAT_EXPORT int esa_select(const qat_esa_params* p, const void* q, const void* Wq
   const bool bf = p->dtype == QAT_BF16;
   const int64_t D = p->n_heads * p->head_dim;
   // q~ = Wq concat_h(q) + bq, float64 accumulation -> float32 + hi/lo bf16
-  hipError_t e = qat::launch_compress_partial(q, L.rows, D, D, bf, Wq, bf, p->d_c, L.nsplit_q, L.qpart, s);
-  if (e == hipSuccess)
-    e = qat::launch_compress_finalize(L.qpart, L.nsplit_q, L.rows, p->d_c, bq, L.qc, p->d_c, 2, L.qhi, L.qlo, s);
+  hipError_t e;
+  {
+    qat::KTimer tm("esa_qcompress", s);
+    e = qat::launch_compress_partial(q, L.rows, D, D, bf, Wq, bf, p->d_c, L.nsplit_q, L.qpart, s);
+    if (e == hipSuccess)
+      e = qat::launch_compress_finalize(L.qpart, L.nsplit_q, L.rows, p->d_c, bq, L.qc, p->d_c, 2, L.qhi, L.qlo, s);
+  }
   if (e != hipSuccess) return hip_status(e, "esa_select: query compression");
   const qat::bf16* kc = (const qat::bf16*)kc_cache;
   int mode;
   if (p->chunk_len > 1) {
     mode = 0;
+    qat::KTimer tm("esa_scores", s);
     e = qat::launch_esa_prefill_scores(L.qhi, L.qlo, kc, p->batch, p->chunk_len, p->ctx_len, L.mid0, L.n_mid,
                                        p->d_c, p->clip, L.rowmax_part, L.rowmax, L.upart, s);
   } else {
     mode = 1;
+    qat::KTimer tm("esa_decode_scan", s);
     e = qat::launch_esa_decode_scan(L.qc, kc, p->batch, p->ctx_len, L.mid0, L.n_mid, p->d_c, L.sraw, L.smax, s);
   }
   if (e != hipSuccess) return hip_status(e, "esa_select: scoring");
+  qat::KTimer tm("esa_topk", s);
   e = qat::launch_esa_topk(mode, L.upart, L.nqsplit, L.sraw, L.smax, L.nscan, p->clip, p->batch, L.n_mid,
                            p->radius, p->topk, L.mid0, L.u_tmp, L.keys, scores, sel, n_sel, s);
   return hip_status(e, "esa_select: top-k");
@@ -277,14 +369,17 @@ QAT_EXPORT int esa_sparse_attn(const qat_esa_params* p, const void* q, const voi
   const bool bf = p->dtype == QAT_BF16;
   hipError_t e;
   if (bf && p->chunk_len == 1 && qat::esa_decode_supported(p->n_heads, p->head_dim)) {
+    qat::KTimer tm("esa_decode_attn", s);
     e = qat::launch_esa_decode_attn(q, k_cache, v_cache, sel, n_sel, L.po, L.pm, L.pl, out, lse, p->batch,
                                     p->n_heads, p->head_dim, p->ctx_len, p->chunk_start, p->n_init, p->window,
                                     p->topk, p->scale, s);
   } else if (bf) {
+    qat::KTimer tm("esa_prefill_attn", s);
     e = qat::launch_esa_prefill_attn(q, k_cache, v_cache, sel, n_sel, out, lse, p->batch, p->n_heads, p->head_dim,
                                      p->ctx_len, p->chunk_start, p->chunk_len, p->n_init, p->window, p->topk,
                                      p->scale, s);
   } else {
+    qat::KTimer tm("esa_generic_attn", s);
     e = qat::launch_esa_generic(q, k_cache, v_cache, sel, n_sel, out, lse, false, p->batch, p->n_heads,
                                 p->head_dim, p->ctx_len, p->chunk_start, p->chunk_len, p->n_init, p->window,
                                 p->topk, p->scale, s);
@@ -315,10 +410,12 @@ QAT_EXPORT int moba_block_select(const qat_moba_params* p, const void* q, const 
   const int64_t nbc_need = std::min<int64_t>(L.nbc, (p->q_start + p->q_len - 1) / p->block);
   hipError_t e = hipSuccess;
   if (p->topk > 1 && nbc_need > 0) {
+    qat::KTimer tm("moba_meanpool", s);
     e = qat::launch_moba_meanpool(k, bf, p->batch, p->seq_len, p->n_kv_heads, p->head_dim, p->block, nbc_need,
                                   L.mp_part, L.kbar, s);
     if (e != hipSuccess) return hip_status(e, "moba_block_select: mean pool");
   }
+  qat::KTimer tm("moba_select", s);
   e = qat::launch_moba_select(q, bf, L.kbar, blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim,
                               nbc_need, p->q_start, p->q_len, p->block, p->topk, s);
   return hip_status(e, "moba_block_select: scoring");
@@ -337,6 +434,7 @@ QAT_EXPORT int moba_sparse_attn(const qat_moba_params* p, const void* q, const v
   hipError_t e;
   if (bf && p->window == 0) {
     if (p->topk > 1 && L.nbuckets > 0) {
+      qat::KTimer tm("moba_dispatch", s);
       e = qat::launch_moba_dispatch(blk, p->batch, p->n_q_heads, p->n_kv_heads, p->q_start, p->q_len, p->block,
                                     p->topk, L.nbc, L.counts, L.offsets, L.cursor, L.entries, L.tiles, L.ntiles, s);
       if (e != hipSuccess) return hip_status(e, "moba_sparse_attn: dispatch");
@@ -346,6 +444,7 @@ QAT_EXPORT int moba_sparse_attn(const qat_moba_params* p, const void* q, const v
                                    p->q_start, p->q_len, p->block, p->topk, p->scale,
                                    L.nbuckets > 0 ? L.max_tiles : 0, s);
   } else {
+    qat::KTimer tm("moba_generic_attn", s);
     e = qat::launch_moba_generic(q, k, v, blk, out, lse, bf, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads,
                                  p->head_dim, p->q_start, p->q_len, p->block, p->topk, p->window, p->scale, s);
   }

@@ -59,4 +59,16 @@ struct Carver {
   __host__ size_t bytes() const { return (off + 255) & ~(size_t)255; }
 };
 
+// Optional per-kernel timing with HIP events on the launch stream (enabled
+// through qat_timing_enable); no-ops when disabled.
+void ktimer_start(const char* name, hipStream_t s);
+void ktimer_stop(const char* name, hipStream_t s);
+
+struct KTimer {
+  const char* name;
+  hipStream_t s;
+  KTimer(const char* n, hipStream_t st) : name(n), s(st) { ktimer_start(name, s); }
+  ~KTimer() { ktimer_stop(name, s); }
+};
+
 }  // namespace qat

@@ -295,9 +295,12 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
     e = hipFuncSetAttribute((const void*)moba_past_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moba_past_kernel<D>, dim3((unsigned)max_tiles), dim3(256), smem, s, q, k, v, tiles,
-                       ntiles, offsets, entries, part_o, part_lse, seq_len, hq, hkv, nbc, q_start, q_len,
-                       block, topk, sl2);
+    {
+      KTimer tm("moba_past_attn", s);
+      hipLaunchKernelGGL(moba_past_kernel<D>, dim3((unsigned)max_tiles), dim3(256), smem, s, q, k, v, tiles,
+                         ntiles, offsets, entries, part_o, part_lse, seq_len, hq, hkv, nbc, q_start, q_len,
+                         block, topk, sl2);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   e = hipFuncSetAttribute((const void*)moba_current_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -306,8 +309,11 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
   const int64_t c_first = q_start / block;
   const int64_t c_last = (q_start + q_len - 1) / block;
   dim3 grid((unsigned)cdiv(block, kRowsPerTile), (unsigned)(c_last - c_first + 1), (unsigned)(batch * hq));
-  hipLaunchKernelGGL(moba_current_kernel<D>, grid, dim3(256), smem, s, q, k, v, blk, part_o, part_lse, out,
-                     lse, seq_len, hq, hkv, q_start, q_len, block, topk, sl2);
+  {
+    KTimer tm("moba_current_attn", s);
+    hipLaunchKernelGGL(moba_current_kernel<D>, grid, dim3(256), smem, s, q, k, v, blk, part_o, part_lse, out,
+                       lse, seq_len, hq, hkv, q_start, q_len, block, topk, sl2);
+  }
   return hipGetLastError();
 }
 
