@@ -96,7 +96,7 @@ typedef struct {
   int32_t topk;         /* middle tokens selected, >= 1 */
   int32_t radius;       /* neighbour-influence radius r >= 0 */
   float clip;           /* score-correction floor C > 0 (may be +inf) */
-  float scale;          /* softmax scale, e.g. 1/sqrt(d) */
+  float scale;          /* softmax scale > 0, e.g. 1/sqrt(d) */
   int32_t dtype;        /* qat_dtype of q, K, V and outputs */
 } qat_esa_params;
 
@@ -174,7 +174,7 @@ typedef struct {
   int32_t block;        /* B >= 1 */
   int32_t topk;         /* blocks per query INCLUDING the forced current one, 1..16 */
   int32_t window;       /* extra local keys [t - window + 1, t], >= 0 */
-  float scale;          /* softmax scale */
+  float scale;          /* softmax scale > 0 */
   int32_t dtype;        /* qat_dtype of q, k, v and out */
 } qat_moba_params;
 

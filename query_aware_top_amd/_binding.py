@@ -8,7 +8,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_HERE, "libqat.so")
+lib_path = os.environ.get("QAT_LIB_PATH") or os.path.join(_HERE, "libqat.so")
 
 QAT_F32, QAT_BF16 = 0, 1
 _STATUS = {0: "QAT_OK", -1: "QAT_EINVAL", -2: "QAT_EUNSUPPORTED", -3: "QAT_EWORKSPACE", -4: "QAT_EHIP"}

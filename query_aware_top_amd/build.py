@@ -39,20 +39,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = OUT, defines=()) -> str:
+    global FLAGS
+    base_flags = FLAGS
+    FLAGS = FLAGS + [f"-D{d}" for d in defines]
+    try:
+        return _build(verbose, out)
+    finally:
+        FLAGS = base_flags
+
+
+def _build(verbose: bool, out: str) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -74,7 +74,7 @@ int esa_check(const qat_esa_params* p) {
   if (p->n_init < 0 || p->window < 0 || p->radius < 0) return fail(QAT_EINVAL, "n_init, window, radius must be >= 0");
   if (p->topk < 1) return fail(QAT_EINVAL, "topk must be >= 1");
   if (!(p->clip > 0.f)) return fail(QAT_EINVAL, "clip must be > 0 (or +inf)");
-  if (!std::isfinite(p->scale)) return fail(QAT_EINVAL, "scale must be finite");
+  if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return fail(QAT_EINVAL, "scale must be finite and > 0");
   if (p->dtype != QAT_F32 && p->dtype != QAT_BF16) return fail(QAT_EINVAL, "unknown dtype %d", p->dtype);
   if (p->batch * p->chunk_len * p->n_heads >= (1ll << 31)) return fail(QAT_EUNSUPPORTED, "too many query rows");
   return QAT_OK;
@@ -155,7 +155,7 @@ int moba_check(const qat_moba_params* p) {
   if (p->block < 1) return fail(QAT_EINVAL, "block must be >= 1");
   if (p->topk < 1 || p->topk > 16) return fail(QAT_EINVAL, "topk must be in 1..16");
   if (p->window < 0) return fail(QAT_EINVAL, "window must be >= 0");
-  if (!std::isfinite(p->scale)) return fail(QAT_EINVAL, "scale must be finite");
+  if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return fail(QAT_EINVAL, "scale must be finite and > 0");
   if (p->dtype != QAT_F32 && p->dtype != QAT_BF16) return fail(QAT_EINVAL, "unknown dtype %d", p->dtype);
   if (p->batch * p->q_len * p->n_q_heads >= (1ll << 27)) return fail(QAT_EUNSUPPORTED, "too many query rows");
   return QAT_OK;

@@ -8,15 +8,20 @@
 // result equals one joint softmax over the union of the segments (the
 // fusion of the ESA write-up and the CCA write-up's unified K/V).
 //
-// Layout (one workgroup = 4 waves = 128 query rows; one wave = 32 rows):
+// Layout (one workgroup = NW waves = 32*NW query rows; one wave = 32 rows):
 // the wave computes S^T = K Q^T (A = K tile from LDS, B = Q from
 // registers) so that each lane owns ONE query (lane % 32) and 16 key
 // scores per 32-key subtile; row max / row sum are lane-local plus one
-// exchange with lane ^ 32. Then O^T += V^T P^T (A = V^T from LDS, B = P
-// from registers); the key order inside each 16-key chunk is permuted
-// (bits 2 and 3 of the key offset swapped) so that the probabilities a lane
-// already holds form its B operand without any data movement, and V is
-// stored transposed in LDS in that permuted order.
+// exchange with lane ^ 32. Then O^T += V^T P^T (A = V^T, B = P from
+// registers). The probabilities a lane holds for a 16-key chunk are the
+// keys 16kc + 8(j/4) + 4h + j%4 (j = 0..7, h = lane / 32); V stays row-major
+// in LDS and the matching V^T operand is fetched with two transposing LDS
+// reads (ds_read_b64_tr_b16), each giving a lane 4 keys of one d column.
+//
+// K/V tiles go from global memory straight into LDS (global_load_lds, 16
+// bytes per lane, no staging registers); rows are unpadded and the 16-byte
+// chunks of row r are stored at chunk ^ swz(r), which spreads both the
+// K-operand reads and the transposing V reads over all LDS banks.
 #pragma once
 
 #include "common.h"
@@ -24,39 +29,66 @@
 namespace qat {
 
 constexpr int kKT = 64;          // keys per tile
-constexpr int kKPad = 8;         // bf16 padding of a K row in LDS
-constexpr int kVPad = 8;         // bf16 padding of a V^T row in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.f;   // log2 units a stale running max may lag
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+// The four LDS tile buffers (K and V, double-buffered) are separate
+// __shared__ variables so that alias analysis can see that reads of one
+// buffer never depend on the in-flight direct loads into the other; with a
+// single array the compiler would wait for those loads before every read.
 template <int D>
 struct FaSmem {
-  bf16 k[2][kKT][D + kKPad];
-  bf16 vt[2][D][kKT + kVPad];
+  bf16* k0;
+  bf16* v0;
+  bf16* k1;
+  bf16* v1;
 };
 
+#define QAT_FA_SMEM(D, name)                                         \
+  __shared__ __align__(16) qat::bf16 name##_k0[qat::kKT * (D)];      \
+  __shared__ __align__(16) qat::bf16 name##_v0[qat::kKT * (D)];      \
+  __shared__ __align__(16) qat::bf16 name##_k1[qat::kKT * (D)];      \
+  __shared__ __align__(16) qat::bf16 name##_v1[qat::kKT * (D)];      \
+  qat::FaSmem<D> name{name##_k0, name##_v0, name##_k1, name##_v1}
+
+// Chunk swizzle of row r. D = 128 (16 chunks per 256-byte row = all 64
+// banks): swz swaps the two 2-bit halves of r & 15, so (a) rows r & 15 =
+// 0..15 read at one chunk index land on 16 distinct chunks (K-operand
+// reads), and (b) the 4 consecutive rows 4a..4a+3 read by one transposing
+// group get distinct bits 2-3, so their chunks 4t..4t+3 never collide.
 template <int D>
-struct FaState {
-  f32x16 o[D / 32];   // O^T: lane's query (lane%32), d = 32*dt + 8*(i/4) + 4*(lane/32) + i%4
-  bf16x8 q[D / 16];   // B operand of S^T: q[row][16c + 8*(lane/32) .. +8]
-  float m;            // running max of scaled scores, log2 units
-  float l;            // lane-partial running sum (combine with lane^32 at the end)
-};
-
-__device__ __forceinline__ int swap23(int o) {
-  return (o & ~0xC) | ((o & 4) << 1) | ((o & 8) >> 1);
+__device__ __forceinline__ int fa_swz(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r & 3) << 1) | ((r >> 2) & 1)) & (D / 8 - 1);
 }
 
 template <int D>
+struct FaState {
+  f32x16 o[D / 32];   // O^T: lane's query (lane%32), d = 32*t + 8*(i/4) + 4*(lane/32) + i%4
+  bf16x8 q[D / 16];   // B operand of S^T: q[row][16c + 8*(lane/32) .. +8]
+  float m;            // running max of scaled scores, log2 units (may lag by kRescaleSlack)
+  float l;            // lane-partial running sum (combine with lane^32 at the end)
+  int kofs[D / 16];   // LDS byte offsets of this lane's K-operand reads
+  int vofs[D / 32][2];   // LDS byte offsets of this lane's transposing V reads
+};
+
+template <int D>
 __device__ __forceinline__ void fa_init(FaState<D>& st, const bf16* qrow, bool valid) {
-  const int h = (threadIdx.x & 63) >> 5;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, r32 = lane & 31;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     if (valid) {
       st.q[c] = *(const bf16x8*)(qrow + 16 * c + 8 * h);
     } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) st.q[c][j] = (bf16)0.f;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      st.q[c] = __builtin_bit_cast(bf16x8, z);
     }
   }
 #pragma unroll
@@ -65,177 +97,281 @@ __device__ __forceinline__ void fa_init(FaState<D>& st, const bf16* qrow, bool v
     for (int i = 0; i < 16; ++i) st.o[t][i] = 0.f;
   st.m = -__builtin_inff();
   st.l = 0.f;
+  constexpr int RB = D * 2;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) st.kofs[c] = r32 * RB + 16 * ((2 * c + h) ^ fa_swz<D>(r32));
+  const int i16 = lane & 15, dh = (lane >> 4) & 1;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = 4 * h + (i16 >> 2) + 8 * hi;
+      const int chunk = 4 * t + 2 * dh + ((i16 & 3) >> 1);
+      st.vofs[t][hi] = row * RB + 16 * (chunk ^ fa_swz<D>(row)) + 8 * (i16 & 1);
+    }
 }
 
-// Global -> register staging of one 64-key tile for the whole workgroup
-// (256 threads). K: 4 chunks of 16 B per thread (D = 128), V: 4 keys x 8 d
-// per thread. `row_of(j)` returns the element offset of key j's row (or -1
-// when j is beyond the segment: zeros are staged and the key is masked).
-template <int D>
-struct FaStage {
-  static constexpr int kChunks = kKT * D / 8;            // 16 B chunks of K
-  static constexpr int kKPer = kChunks / 256;             // per thread
-  static constexpr int kVGroups = (kKT / 4) * (D / 8);    // 4 keys x 8 d groups
-  bf16x8 kr[kKPer > 0 ? kKPer : 1];
-  bf16x8 vr[4];
-};
-
-template <int D, typename RowOf>
-__device__ __forceinline__ void fa_load(FaStage<D>& sg, const bf16* __restrict__ K,
-                                        const bf16* __restrict__ V, RowOf row_of) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < FaStage<D>::kKPer; ++i) {
-    const int c = tid + 256 * i;
-    const int key = c / (D / 8), part = c % (D / 8);
-    const int64_t off = row_of(key);
-    if (off >= 0) {
-      sg.kr[i] = *(const bf16x8*)(K + off + part * 8);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sg.kr[i][j] = (bf16)0.f;
-    }
-  }
-  if (tid < FaStage<D>::kVGroups) {
-    const int kg = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t off = row_of(4 * kg + r);
-      if (off >= 0) {
-        sg.vr[r] = *(const bf16x8*)(V + off + dc * 8);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sg.vr[r][j] = (bf16)0.f;
-      }
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void fa_store(const FaStage<D>& sg, FaSmem<D>& sm, int buf) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < FaStage<D>::kKPer; ++i) {
-    const int c = tid + 256 * i;
-    const int key = c / (D / 8), part = c % (D / 8);
-    *(bf16x8*)&sm.k[buf][key][part * 8] = sg.kr[i];
-  }
-  if (tid < FaStage<D>::kVGroups) {
-    const int kg = tid / (D / 8), dc = tid % (D / 8);
-    const int kp = swap23(4 * kg);   // 4 consecutive keys stay consecutive
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bf16x4 v4;
-      v4[0] = sg.vr[0][j];
-      v4[1] = sg.vr[1][j];
-      v4[2] = sg.vr[2][j];
-      v4[3] = sg.vr[3][j];
-      *(bf16x4*)&sm.vt[buf][dc * 8 + j][kp] = v4;
-    }
-  }
-}
-
-// One 64-key tile for one wave. `key_ok(kidx)` says whether key kidx of the
-// tile may be attended by this lane's query (segment bound and causality).
-template <int D, typename KeyOk>
-__device__ __forceinline__ void fa_tile(FaState<D>& st, const FaSmem<D>& sm, int buf, float scale_log2,
-                                        KeyOk key_ok) {
+// Issue the direct-to-LDS loads of one 64-key tile of K or V for the calling
+// wave: wave w of NW fills rows [w*64/NW, (w+1)*64/NW). row_ofs(j) gives key
+// j's element offset from src (32-bit: one sequence's K or V holds fewer
+// than 2^31 elements); rows at or beyond n are clamped to row n - 1 (a valid
+// row whose scores the caller masks).
+template <int D, int NW, typename RowOfs>
+__device__ __forceinline__ void fa_issue_one(bf16* __restrict__ dst, const bf16* __restrict__ src, int64_t j0,
+                                             int64_t n, RowOfs row_ofs) {
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;       // rows per wave instruction
+  constexpr int RPW = kKT / NW;       // rows per wave
+  static_assert(RPW % RPI == 0, "tile rows must split evenly over the waves");
   const int lane = threadIdx.x & 63;
-  const int h = lane >> 5, r32 = lane & 31;
-  f32x16 s[2];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    f32x16 acc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const bf16x8 a = *(const bf16x8*)&sm.k[buf][sb * 32 + r32][16 * c + 8 * h];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.q[c], acc, 0, 0, 0);
-    }
-    s[sb] = acc;
+  for (int i = 0; i < RPW / RPI; ++i) {
+    const int r0 = RPW * wave + i * RPI;
+    const int r = r0 + lane / CPR;
+    const int c = (lane % CPR) ^ fa_swz<D>(r);
+    const int64_t j = j0 + r;
+    const int off = row_ofs(j < n ? j : n - 1) + c * 8;
+    __builtin_amdgcn_global_load_lds((const global_void*)(src + off), (lds_void*)(dst + r0 * D), 16, 0, 0);
   }
-  // scale, mask, tile max
-  float mx = -__builtin_inff();
+}
+
+__device__ __forceinline__ void fa_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Online-softmax step for one 64-key tile held in s[0..1] (16 scores per
+// lane per 32-key half): rescale if the running max moved by more than
+// kRescaleSlack for any lane, then p = exp2(s * scale_log2 - m) packed to
+// bf16 in pw[kc] (the B operand of the PV chunk of keys [16kc, 16kc + 16));
+// the row sum is accumulated in float32 from the unrounded probabilities.
+template <int D, bool MASKED>
+__device__ __forceinline__ void fa_softmax(FaState<D>& st, f32x16* s, u32x4* pw, float scale_log2) {
+  float mx = __builtin_fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int i = (sb == 0 ? 2 : 0); i < 16; ++i) mx = __builtin_fmaxf(mx, s[sb][i]);
+  mx = xor32_max(mx);
+  const float mx_s = mx * scale_log2;   // scale_log2 > 0
+  if (__builtin_amdgcn_ballot_w64(mx_s > st.m + kRescaleSlack) != 0) {
+    const float m_new = __builtin_fmaxf(st.m, mx_s);
+    const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[t][i] *= alpha;
+    st.m = m_new;
+  }
+  const float m_use = MASKED ? ((st.m == -__builtin_inff()) ? 0.f : st.m) : st.m;
+  float psum = 0.f;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i], scale_log2, -m_use));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i + 1], scale_log2, -m_use));
+      pw[sb * 2 + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(e0, e1);
+      psum += e0 + e1;
+    }
+  st.l += psum;
+}
+
+// S^T = K Q^T for one 64-key tile in LDS (two 32-key halves); all K
+// fragments are read before the matrix ops (one LDS latency per tile).
+template <int D>
+__device__ __forceinline__ void fa_scores(const FaState<D>& st, const bf16* __restrict__ ks, f32x16* s) {
+  const char* kb = reinterpret_cast<const char*>(ks);
+  constexpr int RB = D * 2;
+  bf16x8 ka[2][D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) ka[sb][c] = *(const bf16x8*)(kb + st.kofs[c] + sb * 32 * RB);
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[sb][i] = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[sb][c], st.q[c], s[sb], 0, 0, 0);
+  // K reads run one half-tile ahead of the matrix ops that use them
+  __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 3 * (D / 32), 0);
+}
+
+// O^T += V^T P^T for one 64-key tile in LDS.
+template <int D>
+__device__ __forceinline__ void fa_pv(FaState<D>& st, const bf16* __restrict__ vs, const u32x4* pw) {
+  const char* vb = reinterpret_cast<const char*>(vs);
+  constexpr int RB = D * 2;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    const bf16x8 p = __builtin_bit_cast(bf16x8, pw[kc]);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + st.vofs[t][0] + 16 * kc * RB));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + st.vofs[t][1] + 16 * kc * RB));
+      const i16x4 both[2] = {lo, hi};
+      st.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), p, st.o[t], 0, 0, 0);
+    }
+  }
+}
+
+// Masking of a tile's scores: key_ok(kidx) for key kidx of the tile.
+template <typename KeyOk>
+__device__ __forceinline__ void fa_mask(f32x16* s, KeyOk key_ok) {
+  const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kidx = sb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-      const float x = key_ok(kidx) ? s[sb][i] * scale_log2 : -__builtin_inff();
-      s[sb][i] = x;
-      mx = fmaxf(mx, x);
-    }
-  mx = fmaxf(mx, shfl_xor_f(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
-  const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-  const float alpha = exp2f(st.m - m_use);
-  float psum = 0.f;
-  bf16x8 p[4];
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = exp2f(s[sb][i] - m_use);
-      psum += e;
-      p[sb * 2 + (i >> 3)][i & 7] = (bf16)e;
-    }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.o[t][i] *= alpha;
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-      const bf16x8 a = *(const bf16x8*)&sm.vt[buf][32 * t + r32][16 * kc + 8 * h];
-      st.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kc], st.o[t], 0, 0, 0);
+      if (!key_ok(kidx)) s[sb][i] = -__builtin_inff();
     }
 }
 
-// Runs all tiles of one key segment of n keys. row_of(j) -> element offset of
-// key j (0 <= j < n) in K/V; key_ok(j) -> whether this lane's query attends
-// key j. Must be called by all 256 threads of the workgroup.
-template <int D, typename RowOf, typename KeyOk>
-__device__ __forceinline__ void fa_segment(FaState<D>& st, FaSmem<D>& sm, const bf16* __restrict__ K,
-                                           const bf16* __restrict__ V, int64_t n, float scale_log2,
-                                           RowOf row_of, KeyOk key_ok) {
+// Softmax + PV of tile j (scores in s), masked when needed.
+template <int D, bool CAN_MASK, typename KeyOk, typename TileFull>
+__device__ __forceinline__ void fa_finish_tile(FaState<D>& st, f32x16* s, const bf16* __restrict__ vs,
+                                               float scale_log2, int64_t base, int64_t n, KeyOk key_ok,
+                                               TileFull tile_full) {
+  u32x4 pw[4];
+  if (CAN_MASK && !(base + kKT <= n && tile_full(base)))
+    fa_mask(s, [&](int kidx) { return base + kidx < n && key_ok(base + kidx); });
+  fa_softmax<D, CAN_MASK>(st, s, pw, scale_log2);
+  fa_pv<D>(st, vs, pw);
+}
+
+// Runs all tiles of one key segment of n keys. row_ofs(j) -> element offset
+// of key j (0 <= j < n) from K / V; key_ok(j) -> whether this lane's query
+// attends key j; tile_full(j0) -> whether every lane of the calling wave
+// attends all keys [j0, j0 + 64) (wave-uniform; lets the tile skip masking).
+// CAN_MASK = false promises n % 64 == 0 and every key attended by every
+// lane (no masking code is generated).
+//
+// Software pipeline, one barrier per tile: iteration j computes the scores
+// of tile j+1 on the matrix cores while the softmax of tile j runs on the
+// vector ALUs, then O += P_j V_j. K tiles live in two buffers (K_t in
+// buffer t % 2), V tiles in two others (V_t in buffer t % 2); at the end of
+// iteration j the buffers of K_{j+1} and V_j are free and receive K_{j+3} and
+// V_{j+2}, so every direct load has a whole iteration to land. Must be
+// called by all NW*64 threads of the workgroup.
+template <int D, int NW, bool CAN_MASK, typename RowOfs, typename KeyOk, typename TileFull>
+__device__ __forceinline__ void fa_segment(FaState<D>& st, const FaSmem<D>& sm, const bf16* __restrict__ K,
+                                           const bf16* __restrict__ V, int64_t n, float scale_log2, RowOfs row_ofs,
+                                           KeyOk key_ok, TileFull tile_full) {
   if (n <= 0) return;
-  const int64_t ntiles = cdiv(n, kKT);
-  FaStage<D> sg;
-  auto tile_rows = [&](int64_t tile) {
-    return [=](int j) -> int64_t {
-      const int64_t jj = tile * kKT + j;
-      return jj < n ? row_of(jj) : (int64_t)-1;
-    };
+  const int64_t nt = cdiv(n, kKT);
+  auto issue_k = [&](bf16* dst, int64_t t) {
+    if (t < nt) fa_issue_one<D, NW>(dst, K, t * kKT, n, row_ofs);
   };
-  fa_load<D>(sg, K, V, tile_rows(0));
-  fa_store<D>(sg, sm, 0);
+  auto issue_v = [&](bf16* dst, int64_t t) {
+    if (t < nt) fa_issue_one<D, NW>(dst, V, t * kKT, n, row_ofs);
+  };
+  // prologue: K0, V0, K1, V1 resident, S(0) computed, then K2 into K0's
+  // buffer (after every wave has read K0)
+  issue_k(sm.k0, 0);
+  issue_v(sm.v0, 0);
+  issue_k(sm.k1, 1);
+  issue_v(sm.v1, 1);
+  fa_wait_loads();
   __syncthreads();
-  for (int64_t tile = 0; tile < ntiles; ++tile) {
-    const int buf = (int)(tile & 1);
-    if (tile + 1 < ntiles) fa_load<D>(sg, K, V, tile_rows(tile + 1));
-    const int64_t base = tile * kKT;
-    fa_tile<D>(st, sm, buf, scale_log2, [&](int kidx) { return base + kidx < n && key_ok(base + kidx); });
-    if (tile + 1 < ntiles) fa_store<D>(sg, sm, buf ^ 1);
+  f32x16 s_cur[2], s_nxt[2];
+  fa_scores<D>(st, sm.k0, s_cur);
+  __syncthreads();
+  issue_k(sm.k0, 2);
+  for (int64_t j = 0; j < nt; j += 2) {
+    // ---- even j: S(j+1) from K buffer 1, PV(j) from V buffer 0. The score
+    // tile is computed unconditionally (past the end it reads a buffer no
+    // load is writing and the result is unused) so that it shares a basic
+    // block with the softmax it should overlap.
+    fa_scores<D>(st, sm.k1, s_nxt);
+    fa_finish_tile<D, CAN_MASK>(st, s_cur, sm.v0, scale_log2, j * kKT, n, key_ok, tile_full);
+    if (j + 1 >= nt) break;
+    fa_wait_loads();
     __syncthreads();
+    issue_k(sm.k1, j + 3);
+    issue_v(sm.v0, j + 2);
+    // ---- odd j+1: S(j+2) from K buffer 0, PV(j+1) from V buffer 1
+    fa_scores<D>(st, sm.k0, s_cur);
+    fa_finish_tile<D, CAN_MASK>(st, s_nxt, sm.v1, scale_log2, (j + 1) * kKT, n, key_ok, tile_full);
+    if (j + 2 >= nt) break;
+    fa_wait_loads();
+    __syncthreads();
+    issue_k(sm.k0, j + 4);
+    issue_v(sm.v1, j + 3);
   }
+  fa_wait_loads();
+  __syncthreads();
 }
 
 // Final normalisation: returns the lane's 1/l and natural-log lse.
 template <int D>
 __device__ __forceinline__ void fa_finish(FaState<D>& st, float& inv_l, float& lse) {
-  const float l = st.l + shfl_xor_f(st.l, 32);
+  const float l = xor32_sum(st.l);
   inv_l = l > 0.f ? 1.f / l : 0.f;
   lse = l > 0.f ? st.m * kLn2 + logf(l) : -__builtin_inff();
 }
 
-// d index held in st.o[t][i] by this lane.
-__device__ __forceinline__ int fa_d_of(int t, int i) {
-  const int h = (threadIdx.x & 63) >> 5;
-  return 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);
+// Epilogue staging, one group of 4 waves (128 rows) at a time: waves
+// [4*half, 4*half + 4) write their rows of O (each scaled by `mul`) to LDS as
+// float rows of D, wave w%4 into tile buffer w%4 (32 rows of D floats fit in
+// one 64-key bf16 tile), with the 16-byte chunk q of row r stored at
+// q ^ (r & 31); read back with fa_row_chunk. Call after the last fa_segment
+// (whose trailing barrier frees the buffers) or after the previous half has
+// been consumed; follow with __syncthreads().
+template <int D>
+__device__ __forceinline__ float* fa_row_buf(const FaSmem<D>& sm, int r) {
+  bf16* b = (r >> 5) == 0 ? sm.k0 : (r >> 5) == 1 ? sm.v0 : (r >> 5) == 2 ? sm.k1 : sm.v1;
+  return reinterpret_cast<float*>(b) + (r & 31) * D;
+}
+
+template <int D>
+__device__ __forceinline__ void fa_rows_to_lds(FaState<D>& st, const FaSmem<D>& sm, float mul, int half) {
+  static_assert(kKT * D * sizeof(bf16) >= 32 * D * sizeof(float), "tile buffer too small for 32 float rows");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if ((wave >> 2) != half) return;
+  const int h = lane >> 5;
+  const int row = (wave & 3) * 32 + (lane & 31);
+  float* dst = fa_row_buf<D>(sm, row);
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = st.o[t][i4 * 4 + e] * mul;
+      const int q = 8 * t + 2 * i4 + h;
+      *(f32x4*)(dst + 4 * (q ^ (row & 31) & (D / 4 - 1))) = w;
+    }
+}
+
+// Workgroup id remapped so that consecutive logical ids run on the same XCD:
+// the hardware deals workgroups to the 8 XCDs round-robin, and tiles that
+// share K/V then share that XCD's L2.
+__device__ __forceinline__ int64_t xcd_logical_id(int64_t bid, int64_t nwg) {
+  constexpr int kXcd = 8;
+  const int64_t x = bid % kXcd, local = bid / kXcd;
+  const int64_t per = nwg / kXcd, rem = nwg % kXcd;
+  const int64_t start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return start + local;
+}
+
+// 4 floats [4q, 4q + 4) of staged row r (0 <= r < 128).
+template <int D>
+__device__ __forceinline__ f32x4 fa_row_chunk(const FaSmem<D>& sm, int r, int q) {
+  return *(const f32x4*)(fa_row_buf<D>(sm, r) + 4 * (q ^ (r & 31) & (D / 4 - 1)));
 }
 
 }  // namespace qat

@@ -42,6 +42,18 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// Combine lanes l and l ^ 32 without LDS: v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second, so
+// for (v, v) the two results hold v[l] and v[l ^ 32] in some order.
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Workspace carving helper: 256-byte aligned regions.

@@ -51,17 +51,29 @@ __device__ __forceinline__ EsaKeys esa_keys(const int32_t* sel, const int32_t* n
 // ---------------------------------------------------------------------------
 // Prefill / chunk attention on the matrix cores: grid (128-row tiles of the
 // chunk, head, sequence).
+#ifndef QAT_ESA_NW
+#define QAT_ESA_NW 8
+#endif
+constexpr int kNW = QAT_ESA_NW;
+constexpr int kThreads = 64 * kNW;
+constexpr int kRows = 32 * kNW;
+
 template <int D>
-__global__ __launch_bounds__(256, 2) void esa_prefill_kernel(
+__global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, bf16* __restrict__ out,
     float* __restrict__ lse_out, int64_t H, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
     int64_t window, int topk, float scale_log2) {
-  extern __shared__ __align__(16) char smem_raw[];
-  FaSmem<D>& sm = *reinterpret_cast<FaSmem<D>*>(smem_raw);
-  const int64_t bi = blockIdx.z, h = blockIdx.y;
-  const int64_t i0 = (int64_t)blockIdx.x * 128;
-  const int64_t i_last = min(m, i0 + 128) - 1;
+  QAT_FA_SMEM(D, sm);
+  // logical id -> (row tile, head, sequence); the row tiles of one head are
+  // adjacent and share an XCD (its L2 holds the head's gathered K/V)
+  int64_t id = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int64_t ntile = cdiv(m, kRows);
+  const int64_t qt = id % ntile;
+  id /= ntile;
+  const int64_t h = id % H, bi = id / H;
+  const int64_t i0 = qt * kRows;
+  const int64_t i_last = min(m, i0 + kRows) - 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t i = i0 + wave * 32 + (lane & 31);
   const bool valid = i <= i_last;
@@ -69,28 +81,42 @@ __global__ __launch_bounds__(256, 2) void esa_prefill_kernel(
   FaState<D> st;
   fa_init<D>(st, qrow, valid);
   const EsaKeys kl = esa_keys(sel, n_sel, bi, topk, c0, n_init, window);
-  const int64_t seq0 = bi * ctx_len;
-  fa_segment<D>(st, sm, kc, vc, kl.count(), scale_log2,
-                [=](int64_t j) -> int64_t { return ((seq0 + kl.pos(j)) * H + h) * D; },
-                [=](int64_t) { return valid; });
+  const bf16* kb = kc + (bi * ctx_len * H + h) * D;
+  const bf16* vb = vc + (bi * ctx_len * H + h) * D;
+  // one key segment: the gathered keys (all before the chunk, never masked)
+  // followed by the chunk's own keys under the causal mask
+  const int HD = (int)(H * D);
+  const int64_t ng = kl.count();
   const int64_t qi = valid ? i : -1;
-  fa_segment<D>(st, sm, kc, vc, i_last + 1, scale_log2,
-                [=](int64_t j) -> int64_t { return ((seq0 + c0 + j) * H + h) * D; },
-                [=](int64_t j) { return j <= qi; });
+  const int64_t wave_first = i0 + wave * 32;
+  fa_segment<D, kNW, true>(
+      st, sm, kb, vb, ng + i_last + 1, scale_log2,
+      [=](int64_t j) { return (int)(j < ng ? kl.pos(j) : c0 + (j - ng)) * HD; },
+      [=](int64_t j) { return j < ng || j - ng <= qi; },
+      [=](int64_t j0) { return j0 + kKT - 1 < ng || j0 + kKT - 1 - ng <= wave_first; });
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
-  if (!valid) return;
-  bf16* dst = out + ((bi * m + i) * H + h) * D;
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      bf16x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (bf16)(st.o[t][i4 * 4 + e] * inv_l);
-      *(bf16x4*)(dst + fa_d_of(t, i4 * 4)) = w;
+  if (lse_out && valid && (lane >> 5) == 0) lse_out[(bi * m + i) * H + h] = lse;
+  constexpr int TPR = D / 8;
+  constexpr int RPP = kThreads / TPR;
+  const int sub = threadIdx.x % TPR;
+  const int nrows = (int)(i_last - i0 + 1);
+  for (int half = 0; half < kNW / 4; ++half) {
+    fa_rows_to_lds<D>(st, sm, inv_l, half);
+    __syncthreads();
+    for (int rr = threadIdx.x / TPR; rr < 128; rr += RPP) {
+      const int tr = half * 128 + rr;
+      if (tr >= nrows) continue;
+      const f32x4 a = fa_row_chunk<D>(sm, rr, 2 * sub), cc = fa_row_chunk<D>(sm, rr, 2 * sub + 1);
+      u32x4 w;
+      w[0] = pack_bf16x2(a[0], a[1]);
+      w[1] = pack_bf16x2(a[2], a[3]);
+      w[2] = pack_bf16x2(cc[0], cc[1]);
+      w[3] = pack_bf16x2(cc[2], cc[3]);
+      *(u32x4*)(out + ((bi * m + i0 + tr) * H + h) * D + sub * 8) = w;
     }
-  if (lse_out && (lane >> 5) == 0) lse_out[(bi * m + i) * H + h] = lse;
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -215,24 +241,14 @@ hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, 
                                    const int32_t* n_sel, void* out, float* lse, int64_t batch, int64_t H,
                                    int64_t D, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
                                    int64_t window, int topk, float scale, hipStream_t s) {
-  dim3 grid((unsigned)cdiv(m, 128), (unsigned)H, (unsigned)batch);
+  dim3 grid((unsigned)(cdiv(m, kRows) * H * batch));
   const float sl2 = scale * kLog2e;
-  hipError_t e;
-  if (D == 64) {
-    const size_t smem = sizeof(FaSmem<64>);
-    e = hipFuncSetAttribute((const void*)esa_prefill_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)smem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(esa_prefill_kernel<64>, grid, dim3(256), smem, s, (const bf16*)q, (const bf16*)k,
+  if (D == 64)
+    hipLaunchKernelGGL(esa_prefill_kernel<64>, grid, dim3(kThreads), 0, s, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                       sel, n_sel, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2);
+  else
+    hipLaunchKernelGGL(esa_prefill_kernel<128>, grid, dim3(kThreads), 0, s, (const bf16*)q, (const bf16*)k,
                        (const bf16*)v, sel, n_sel, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2);
-  } else {
-    const size_t smem = sizeof(FaSmem<128>);
-    e = hipFuncSetAttribute((const void*)esa_prefill_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)smem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(esa_prefill_kernel<128>, grid, dim3(256), smem, s, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, sel, n_sel, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2);
-  }
   return hipGetLastError();
 }
 

@@ -19,28 +19,60 @@
 
 namespace qat {
 
-constexpr int kRowsPerTile = 128;
+#ifndef QAT_PAST_NW
+#define QAT_PAST_NW 4
+#endif
+constexpr int kNW = QAT_PAST_NW;          // waves per past-block workgroup
+constexpr int kThreads = 64 * kNW;
+constexpr int kRowsPerTile = 32 * kNW;    // query rows per attention workgroup
 
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
 }
 
-// (row, slot) pairs of earlier blocks -> bucket counts.
-__global__ void moba_count_kernel(const int32_t* __restrict__ blk, int64_t nrows, int64_t hq, int64_t hkv,
-                                  int64_t q_len, int64_t q_start, int block, int topk, int64_t nbc,
-                                  int32_t* __restrict__ counts) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= nrows * topk) return;
+// Dispatch keys: (row, slot) pairs whose gated block is an earlier block go
+// to bucket (sequence, KV head, block). Counting and scattering aggregate in
+// LDS per workgroup first (one global atomic per bucket and workgroup), since
+// strongly preferred blocks collect most rows of the sequence.
+constexpr int kDispatchLdsBuckets = 4096;
+
+__device__ __forceinline__ int64_t moba_bucket_of(const int32_t* __restrict__ blk, int64_t idx, int64_t hq,
+                                                  int64_t hkv, int64_t q_len, int64_t q_start, int block, int topk,
+                                                  int64_t nbc) {
   const int64_t row = idx / topk;
   const int32_t b = blk[idx];
   const int64_t h = row % hq;
   const int64_t r = (row / hq) % q_len;
   const int64_t bi = row / (hq * q_len);
   const int64_t cur = (q_start + r) / block;
-  if (b < 0 || b >= cur) return;
-  const int64_t g = h / (hq / hkv);
-  atomicAdd(&counts[(bi * hkv + g) * nbc + b], 1);
+  if (b < 0 || b >= cur) return -1;
+  return (bi * hkv + h / (hq / hkv)) * nbc + b;
+}
+
+__global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restrict__ blk, int64_t total, int64_t hq,
+                                                         int64_t hkv, int64_t q_len, int64_t q_start, int block,
+                                                         int topk, int64_t nbc, int64_t nbuckets,
+                                                         int32_t* __restrict__ counts) {
+  __shared__ int32_t loc[kDispatchLdsBuckets];
+  const bool use_lds = nbuckets <= kDispatchLdsBuckets;
+  if (use_lds) {
+    for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = 0;
+    __syncthreads();
+  }
+  const int64_t per = (int64_t)blockDim.x * 16;
+  const int64_t i0 = (int64_t)blockIdx.x * per;
+  for (int64_t idx = i0 + threadIdx.x; idx < min(total, i0 + per); idx += blockDim.x) {
+    const int64_t bk = moba_bucket_of(blk, idx, hq, hkv, q_len, q_start, block, topk, nbc);
+    if (bk < 0) continue;
+    if (use_lds) atomicAdd(&loc[bk], 1);
+    else atomicAdd(&counts[bk], 1);
+  }
+  if (use_lds) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < nbuckets; i += blockDim.x)
+      if (loc[i]) atomicAdd(&counts[i], loc[i]);
+  }
 }
 
 // Single workgroup: exclusive scans of the bucket counts and of their tile
@@ -84,37 +116,57 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(const int32_t* __restri
   if (threadIdx.x == 0) { offsets[nb] = carry[0]; ntiles[0] = carry[1]; }
 }
 
-// (row, slot) -> entries[cursor[bucket]++] = row * 16 + slot.
-__global__ void moba_scatter_kernel(const int32_t* __restrict__ blk, int64_t nrows, int64_t hq, int64_t hkv,
-                                    int64_t q_len, int64_t q_start, int block, int topk, int64_t nbc,
-                                    int32_t* __restrict__ cursor, int32_t* __restrict__ entries) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= nrows * topk) return;
-  const int64_t row = idx / topk;
-  const int slot = (int)(idx % topk);
-  const int32_t b = blk[idx];
-  const int64_t h = row % hq;
-  const int64_t r = (row / hq) % q_len;
-  const int64_t bi = row / (hq * q_len);
-  const int64_t cur = (q_start + r) / block;
-  if (b < 0 || b >= cur) return;
-  const int64_t g = h / (hq / hkv);
-  const int32_t pos = atomicAdd(&cursor[(bi * hkv + g) * nbc + b], 1);
-  entries[pos] = (int32_t)(row * 16 + slot);
+// (row, slot) -> entries[...] = row * 16 + slot. Each workgroup reserves one
+// range per bucket with a single global atomic and places its entries with
+// LDS atomics (the order inside a bucket is irrelevant: every row's result is
+// independent of the other rows sharing its tile).
+__global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __restrict__ blk, int64_t total,
+                                                           int64_t hq, int64_t hkv, int64_t q_len, int64_t q_start,
+                                                           int block, int topk, int64_t nbc, int64_t nbuckets,
+                                                           int32_t* __restrict__ cursor,
+                                                           int32_t* __restrict__ entries) {
+  __shared__ int32_t loc[kDispatchLdsBuckets];
+  __shared__ int32_t base_of[kDispatchLdsBuckets];
+  const bool use_lds = nbuckets <= kDispatchLdsBuckets;
+  const int64_t per = (int64_t)blockDim.x * 16;
+  const int64_t i0 = (int64_t)blockIdx.x * per;
+  const int64_t i1 = min(total, i0 + per);
+  if (use_lds) {
+    for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = 0;
+    __syncthreads();
+    for (int64_t idx = i0 + threadIdx.x; idx < i1; idx += blockDim.x) {
+      const int64_t bk = moba_bucket_of(blk, idx, hq, hkv, q_len, q_start, block, topk, nbc);
+      if (bk >= 0) atomicAdd(&loc[bk], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) {
+      base_of[i] = loc[i] ? atomicAdd(&cursor[i], loc[i]) : 0;
+      loc[i] = 0;
+    }
+    __syncthreads();
+  }
+  for (int64_t idx = i0 + threadIdx.x; idx < i1; idx += blockDim.x) {
+    const int64_t bk = moba_bucket_of(blk, idx, hq, hkv, q_len, q_start, block, topk, nbc);
+    if (bk < 0) continue;
+    const int32_t pos = use_lds ? base_of[bk] + atomicAdd(&loc[bk], 1) : atomicAdd(&cursor[bk], 1);
+    entries[pos] = (int32_t)((idx / topk) * 16 + idx % topk);
+  }
 }
 
-// Past-block attention: one workgroup per tile of up to 128 dispatched rows
-// of one (sequence, KV head, block); full block, no mask.
-template <int D>
-__global__ __launch_bounds__(256, 2) void moba_past_kernel(
+// Past-block attention: one workgroup per tile of up to 256 dispatched rows
+// of one (sequence, KV head, block); full block, no mask. Partials are
+// written row-contiguous through LDS. Tiles of one bucket are adjacent in the
+// tile table and run on one XCD (shared L2 for the block's K/V).
+template <int D, bool FULL>
+__global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ entries, bf16* __restrict__ part_o, float* __restrict__ part_lse,
     int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block,
     int topk, float scale_log2) {
-  extern __shared__ __align__(16) char smem_raw[];
-  FaSmem<D>& sm = *reinterpret_cast<FaSmem<D>*>(smem_raw);
-  const int tile = blockIdx.x;
+  QAT_FA_SMEM(D, sm);
+  __shared__ int64_t s_pidx[kRowsPerTile];
+  const int64_t tile = xcd_logical_id(blockIdx.x, gridDim.x);
   if (tile >= ntiles[0]) return;
   const int2 td = tiles[tile];
   const int bucket = td.x;
@@ -136,113 +188,172 @@ __global__ __launch_bounds__(256, 2) void moba_past_kernel(
 
   FaState<D> st;
   fa_init<D>(st, qrow, valid);
-  const int64_t kv_row0 = ((bi * seq_len + b * block) * hkv + g) * D;
-  const int64_t kv_stride = hkv * D;
-  fa_segment<D>(st, sm, k, v, block, scale_log2,
-                [=](int64_t j) -> int64_t { return kv_row0 + j * kv_stride; },
-                [](int64_t) { return true; });
+  const bf16* kb = k + ((bi * seq_len + b * block) * hkv + g) * D;
+  const bf16* vb = v + ((bi * seq_len + b * block) * hkv + g) * D;
+  const int kv_stride = (int)(hkv * D);
+  // FULL: block % 64 == 0, so no tile of the block needs masking
+  fa_segment<D, kNW, !FULL>(st, sm, kb, vb, block, scale_log2, [=](int64_t j) { return (int)j * kv_stride; },
+                            [](int64_t) { return true; }, [](int64_t) { return true; });
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
-  if (!valid) return;
-  const int64_t pidx = row * (topk - 1) + slot;
-  bf16* dst = part_o + pidx * D;
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      bf16x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (bf16)(st.o[t][i4 * 4 + i] * inv_l);
-      *(bf16x4*)(dst + fa_d_of(t, i4 * 4)) = w;
+  if ((lane >> 5) == 0) {
+    s_pidx[myrow] = valid ? row * (topk - 1) + slot : -1;
+    if (valid) part_lse[row * (topk - 1) + slot] = lse;
+  }
+  constexpr int TPR = D / 8;                  // threads per row
+  constexpr int RPP = kThreads / TPR;         // rows per pass
+  const int sub = threadIdx.x % TPR;
+  for (int half = 0; half < kNW / 4; ++half) {
+    fa_rows_to_lds<D>(st, sm, inv_l, half);
+    __syncthreads();
+    for (int rr = threadIdx.x / TPR; rr < 128; rr += RPP) {
+      const int64_t pi = s_pidx[half * 128 + rr];
+      if (pi < 0) continue;
+      const f32x4 a = fa_row_chunk<D>(sm, rr, 2 * sub), c = fa_row_chunk<D>(sm, rr, 2 * sub + 1);
+      u32x4 w;
+      w[0] = pack_bf16x2(a[0], a[1]);
+      w[1] = pack_bf16x2(a[2], a[3]);
+      w[2] = pack_bf16x2(c[0], c[1]);
+      w[3] = pack_bf16x2(c[2], c[3]);
+      *(u32x4*)(part_o + pi * D + sub * 8) = w;
     }
-  if ((lane >> 5) == 0) part_lse[pidx] = lse;
+    __syncthreads();
+  }
 }
 
 // Current-block attention (causal) plus the log-sum-exp merge of the row's
-// past-block partials. grid.x: 128-row tile within the block, grid.y: block
-// index relative to the first block touched, grid.z: sequence * Hq + head.
+// past-block partials. A workgroup holds 32*NW rows = 32*NW/P consecutive
+// tokens x P query heads of one KV group (GQA packing: the heads share K/V).
+// Logical id -> (token tile, block, sequence, KV head, head pack). NW = 4
+// lets two workgroups share a CU, so one's merge epilogue (memory-bound)
+// overlaps the other's matrix-core work.
+constexpr int kCurNW = 4;
+constexpr int kCurRows = 32 * kCurNW;
+constexpr int kMergeMax = 3;   // past slots merged with batched loads (more: looped)
+
 template <int D>
-__global__ __launch_bounds__(256, 2) void moba_current_kernel(
+__global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ blk, const bf16* __restrict__ part_o, const float* __restrict__ part_lse,
     bf16* __restrict__ out, float* __restrict__ lse_out, int64_t seq_len, int64_t hq, int64_t hkv,
-    int64_t q_start, int64_t q_len, int block, int topk, float scale_log2) {
-  extern __shared__ __align__(16) char smem_raw[];
-  FaSmem<D>& sm = *reinterpret_cast<FaSmem<D>*>(smem_raw);
-  const int64_t bi = blockIdx.z / hq;
-  const int64_t h = blockIdx.z % hq;
-  const int64_t g = h / (hq / hkv);
-  const int64_t c = q_start / block + blockIdx.y;
+    int64_t q_start, int64_t q_len, int block, int topk, float scale_log2, int pack, int tiles_per_block,
+    int64_t nblocks) {
+  constexpr int NW = kCurNW;
+  constexpr int THREADS = 64 * NW;
+  QAT_FA_SMEM(D, sm);
+  __shared__ float s_lse[kCurRows];
+  int64_t id = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int tt = (int)(id % tiles_per_block);
+  id /= tiles_per_block;
+  const int64_t cb = id % nblocks;
+  id /= nblocks;
+  const int64_t gs = hq / hkv;
+  const int64_t npk = gs / pack;
+  const int64_t hp = id % npk;
+  id /= npk;
+  const int64_t g = id % hkv;
+  const int64_t bi = id / hkv;
+  const int64_t c = q_start / block + cb;
   const int64_t q_end = q_start + q_len;
   const int64_t lo = max(c * block, q_start);
   const int64_t hi = min((c + 1) * block, q_end);
-  const int64_t t0 = lo + (int64_t)blockIdx.x * kRowsPerTile;
+  const int tok_per_tile = kCurRows / pack;
+  const int64_t t0 = lo + (int64_t)tt * tok_per_tile;
   if (t0 >= hi) return;
-  const int64_t t_last = min(hi, t0 + kRowsPerTile) - 1;
+  const int64_t t_last = min(hi, t0 + tok_per_tile) - 1;
+  const int64_t h0 = g * gs + hp * pack;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = t0 + wave * 32 + (lane & 31);
+  const int myrow = wave * 32 + (lane & 31);
+  const int64_t t = t0 + myrow / pack;
+  const int64_t h = h0 + myrow % pack;
   const bool valid = t <= t_last;
   const bf16* qrow = q + ((bi * seq_len + (valid ? t : t0)) * hq + h) * D;
 
   FaState<D> st;
   fa_init<D>(st, qrow, valid);
   const int64_t kpos0 = c * block;
-  const int64_t kv_row0 = ((bi * seq_len + kpos0) * hkv + g) * D;
-  const int64_t kv_stride = hkv * D;
+  const bf16* kb = k + ((bi * seq_len + kpos0) * hkv + g) * D;
+  const bf16* vb = v + ((bi * seq_len + kpos0) * hkv + g) * D;
+  const int kv_stride = (int)(hkv * D);
   const int64_t qpos = valid ? t : -1;
-  fa_segment<D>(st, sm, k, v, t_last - kpos0 + 1, scale_log2,
-                [=](int64_t j) -> int64_t { return kv_row0 + j * kv_stride; },
-                [=](int64_t j) { return kpos0 + j <= qpos; });
+  const int64_t wave_first = t0 + (wave * 32) / pack;   // smallest query position of this wave
+  fa_segment<D, NW, true>(st, sm, kb, vb, t_last - kpos0 + 1, scale_log2,
+                          [=](int64_t j) { return (int)j * kv_stride; },
+                          [=](int64_t j) { return kpos0 + j <= qpos; },
+                          [=](int64_t j0) { return kpos0 + j0 + kKT - 1 <= wave_first; });
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
-  if (!valid) return;
+  if ((lane >> 5) == 0) s_lse[myrow] = lse;
+  fa_rows_to_lds<D>(st, sm, inv_l, 0);
+  __syncthreads();
 
-  // Merge with the past-block partials of this row.
-  const int64_t row = (bi * q_len + (t - q_start)) * hq + h;
-  const int32_t* br = blk + row * topk;
-  float lse_tot = lse;
-  for (int s = 0; s < topk; ++s) {
-    const int32_t b = br[s];
-    if (b >= 0 && b < c) {
-      const float l2 = part_lse[row * (topk - 1) + s];
-      const float mx = fmaxf(lse_tot, l2);
-      lse_tot = mx + logf(expf(lse_tot - mx) + expf(l2 - mx));
+  // merge: TPR threads per row, 8 d each; all loads of a row are issued
+  // before any is consumed (partial rows are read contiguous)
+  constexpr int TPR = D / 8;
+  constexpr int RPP = THREADS / TPR;
+  const int sub = threadIdx.x % TPR;
+  const int nrows = (int)(t_last - t0 + 1) * pack;
+  const int km = topk - 1;
+  for (int rr = threadIdx.x / TPR; rr < nrows; rr += RPP) {
+    const int64_t tq = t0 + rr / pack;
+    const int64_t row = (bi * q_len + (tq - q_start)) * hq + h0 + rr % pack;
+    const int32_t* br = blk + row * topk;
+    const float l_cur = s_lse[rr];
+    const f32x4 a = fa_row_chunk<D>(sm, rr, 2 * sub), cc = fa_row_chunk<D>(sm, rr, 2 * sub + 1);
+    bool use[kMergeMax];
+    float pl[kMergeMax];
+    bf16x8 pv[kMergeMax];
+#pragma unroll
+    for (int s = 0; s < kMergeMax; ++s) {
+      const int32_t b = s < km ? br[s] : -1;
+      use[s] = b >= 0 && b < c;
+      const int64_t pidx = row * km + s;
+      pl[s] = use[s] ? part_lse[pidx] : -__builtin_inff();
+      if (use[s]) pv[s] = *(const bf16x8*)(part_o + pidx * D + sub * 8);
     }
+    float lse_tot = l_cur;
+#pragma unroll
+    for (int s = 0; s < kMergeMax; ++s)
+      if (use[s]) {
+        const float mx = fmaxf(lse_tot, pl[s]);
+        lse_tot = mx + logf(expf(lse_tot - mx) + expf(pl[s] - mx));
+      }
+    for (int s = kMergeMax; s < km; ++s) {
+      const int32_t b = br[s];
+      if (b >= 0 && b < c) {
+        const float l2 = part_lse[row * km + s];
+        const float mx = fmaxf(lse_tot, l2);
+        lse_tot = mx + logf(expf(lse_tot - mx) + expf(l2 - mx));
+      }
+    }
+    const float w_cur = expf(l_cur - lse_tot);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { acc[e] = a[e] * w_cur; acc[4 + e] = cc[e] * w_cur; }
+#pragma unroll
+    for (int s = 0; s < kMergeMax; ++s)
+      if (use[s]) {
+        const float w = expf(pl[s] - lse_tot);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * (float)pv[s][e];
+      }
+    for (int s = kMergeMax; s < km; ++s) {
+      const int32_t b = br[s];
+      if (b >= 0 && b < c) {
+        const int64_t pidx = row * km + s;
+        const float w = expf(part_lse[pidx] - lse_tot);
+        const bf16x8 p2 = *(const bf16x8*)(part_o + pidx * D + sub * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * (float)p2[e];
+      }
+    }
+    u32x4 wv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wv[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    *(u32x4*)(out + row * D + sub * 8) = wv;
+    if (lse_out && sub == 0) lse_out[row] = lse_tot;
   }
-  const float w_cur = expf(lse - lse_tot) * inv_l;
-  float acc[D / 32][16];
-#pragma unroll
-  for (int tt = 0; tt < D / 32; ++tt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[tt][i] = st.o[tt][i] * w_cur;
-  for (int s = 0; s < topk; ++s) {
-    const int32_t b = br[s];
-    if (b >= 0 && b < c) {
-      const int64_t pidx = row * (topk - 1) + s;
-      const float w = expf(part_lse[pidx] - lse_tot);
-      const bf16* src = part_o + pidx * D;
-#pragma unroll
-      for (int tt = 0; tt < D / 32; ++tt)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const bf16x4 pv = *(const bf16x4*)(src + fa_d_of(tt, i4 * 4));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[tt][i4 * 4 + i] += w * (float)pv[i];
-        }
-    }
-  }
-  bf16* dst = out + row * D;
-#pragma unroll
-  for (int tt = 0; tt < D / 32; ++tt)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      bf16x4 w4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w4[i] = (bf16)acc[tt][i4 * 4 + i];
-      *(bf16x4*)(dst + fa_d_of(tt, i4 * 4)) = w4;
-    }
-  if (lse_out && (lane >> 5) == 0) lse_out[row] = lse_tot;
 }
 
 // ---------------------------------------------------------------------------
@@ -257,25 +368,23 @@ int64_t moba_max_tiles(int64_t nrows, int topk, int64_t nbuckets) {
 }
 
 hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t hq, int64_t hkv, int64_t q_start,
-                                int64_t q_len, int block, int topk, int64_t nbc, int32_t* counts,
-                                int32_t* offsets, int32_t* cursor, int32_t* entries, int2* tiles,
-                                int32_t* ntiles, hipStream_t s) {
-  const int64_t nrows = batch * q_len * hq;
+                                int64_t q_len, int block, int topk, int64_t nbc, int32_t* counts, int32_t* offsets,
+                                int32_t* cursor, int32_t* entries, int2* tiles, int32_t* ntiles, hipStream_t s) {
+  const int64_t total = batch * q_len * hq * topk;
   const int64_t nbuckets = batch * hkv * nbc;
   hipError_t e = launch_fill_i32(counts, nbuckets, 0, s);
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)cdiv(nrows * topk, 256);
+  const unsigned grid = (unsigned)cdiv(total, 256 * 16);
   if (nbuckets > 0) {
-    hipLaunchKernelGGL(moba_count_kernel, dim3(grid), dim3(256), 0, s, blk, nrows, hq, hkv, q_len, q_start,
-                       block, topk, nbc, counts);
+    hipLaunchKernelGGL(moba_count_kernel, dim3(grid), dim3(256), 0, s, blk, total, hq, hkv, q_len, q_start, block,
+                       topk, nbc, nbuckets, counts);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(moba_scan_kernel, dim3(1), dim3(1024), 0, s, counts, nbuckets, offsets, cursor, tiles,
-                     ntiles);
+  hipLaunchKernelGGL(moba_scan_kernel, dim3(1), dim3(1024), 0, s, counts, nbuckets, offsets, cursor, tiles, ntiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (nbuckets > 0) {
-    hipLaunchKernelGGL(moba_scatter_kernel, dim3(grid), dim3(256), 0, s, blk, nrows, hq, hkv, q_len, q_start,
-                       block, topk, nbc, cursor, entries);
+    hipLaunchKernelGGL(moba_scatter_kernel, dim3(grid), dim3(256), 0, s, blk, total, hq, hkv, q_len, q_start,
+                       block, topk, nbc, nbuckets, cursor, entries);
     e = hipGetLastError();
   }
   return e;
@@ -288,31 +397,34 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
                                      float* lse, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
                                      int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk,
                                      float scale, int64_t max_tiles, hipStream_t s) {
-  const size_t smem = sizeof(FaSmem<D>);
   const float sl2 = scale * kLog2e;
   hipError_t e;
   if (topk > 1 && max_tiles > 0 && nbc > 0) {
-    e = hipFuncSetAttribute((const void*)moba_past_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)smem);
-    if (e != hipSuccess) return e;
     {
       KTimer tm("moba_past_attn", s);
-      hipLaunchKernelGGL(moba_past_kernel<D>, dim3((unsigned)max_tiles), dim3(256), smem, s, q, k, v, tiles,
-                         ntiles, offsets, entries, part_o, part_lse, seq_len, hq, hkv, nbc, q_start, q_len,
-                         block, topk, sl2);
+      if (block % kKT == 0)
+        hipLaunchKernelGGL((moba_past_kernel<D, true>), dim3((unsigned)max_tiles), dim3(kThreads), 0, s, q, k, v,
+                           tiles, ntiles, offsets, entries, part_o, part_lse, seq_len, hq, hkv, nbc, q_start, q_len,
+                           block, topk, sl2);
+      else
+        hipLaunchKernelGGL((moba_past_kernel<D, false>), dim3((unsigned)max_tiles), dim3(kThreads), 0, s, q, k, v,
+                           tiles, ntiles, offsets, entries, part_o, part_lse, seq_len, hq, hkv, nbc, q_start, q_len,
+                           block, topk, sl2);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  e = hipFuncSetAttribute((const void*)moba_current_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)smem);
-  if (e != hipSuccess) return e;
+  const int64_t gs = hq / hkv;
+  const int pack = (kCurRows % gs == 0) ? (int)gs : 1;
+  const int tok_per_tile = kCurRows / pack;
+  const int tiles_per_block = (int)cdiv(block, tok_per_tile);
   const int64_t c_first = q_start / block;
-  const int64_t c_last = (q_start + q_len - 1) / block;
-  dim3 grid((unsigned)cdiv(block, kRowsPerTile), (unsigned)(c_last - c_first + 1), (unsigned)(batch * hq));
+  const int64_t nblocks = (q_start + q_len - 1) / block - c_first + 1;
+  const int64_t nwg = (int64_t)tiles_per_block * nblocks * batch * hkv * (gs / pack);
   {
     KTimer tm("moba_current_attn", s);
-    hipLaunchKernelGGL(moba_current_kernel<D>, grid, dim3(256), smem, s, q, k, v, blk, part_o, part_lse, out,
-                       lse, seq_len, hq, hkv, q_start, q_len, block, topk, sl2);
+    hipLaunchKernelGGL(moba_current_kernel<D>, dim3((unsigned)nwg), dim3(64 * kCurNW), 0, s, q, k, v, blk, part_o,
+                       part_lse, out, lse, seq_len, hq, hkv, q_start, q_len, block, topk, sl2, pack,
+                       tiles_per_block, nblocks);
   }
   return hipGetLastError();
 }
