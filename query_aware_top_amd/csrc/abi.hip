@@ -58,6 +58,7 @@ struct EsaLayout {
   float* po = nullptr;
   float* pm = nullptr;
   float* pl = nullptr;
+  int32_t* keylist = nullptr;
   size_t bytes = 0;
 };
 
@@ -108,6 +109,7 @@ EsaLayout esa_layout(const qat_esa_params* p, void* ws) {
   }
   L.u_tmp = c.take<float>((size_t)B * nm);
   L.keys = c.take<uint32_t>((size_t)B * nm);
+  L.keylist = c.take<int32_t>((size_t)B * qat::esa_keylist_len(p->n_init, p->topk, p->window, m));
   if (m == 1) {
     L.po = c.take<float>((size_t)B * L.ndec * D);
     L.pm = c.take<float>((size_t)B * L.ndec * p->n_heads);
@@ -373,14 +375,16 @@ QAT_EXPORT int esa_sparse_attn(const qat_esa_params* p, const void* q, const voi
     e = qat::launch_esa_decode_attn(q, k_cache, v_cache, sel, n_sel, L.po, L.pm, L.pl, out, lse, p->batch,
                                     p->n_heads, p->head_dim, p->ctx_len, p->chunk_start, p->n_init, p->window,
                                     p->topk, p->scale, s);
-  } else if (bf) {
+  } else if (bf && p->ctx_len * p->n_heads * p->head_dim < (1ll << 31)) {
+    // the matrix-core kernel addresses K/V rows of one sequence with 32-bit offsets
     qat::KTimer tm("esa_prefill_attn", s);
-    e = qat::launch_esa_prefill_attn(q, k_cache, v_cache, sel, n_sel, out, lse, p->batch, p->n_heads, p->head_dim,
+    e = qat::launch_esa_prefill_attn(q, k_cache, v_cache, sel, n_sel, L.keylist, out, lse, p->batch, p->n_heads,
+                                     p->head_dim,
                                      p->ctx_len, p->chunk_start, p->chunk_len, p->n_init, p->window, p->topk,
                                      p->scale, s);
   } else {
     qat::KTimer tm("esa_generic_attn", s);
-    e = qat::launch_esa_generic(q, k_cache, v_cache, sel, n_sel, out, lse, false, p->batch, p->n_heads,
+    e = qat::launch_esa_generic(q, k_cache, v_cache, sel, n_sel, out, lse, bf, p->batch, p->n_heads,
                                 p->head_dim, p->ctx_len, p->chunk_start, p->chunk_len, p->n_init, p->window,
                                 p->topk, p->scale, s);
   }

@@ -117,8 +117,8 @@ __device__ __forceinline__ void fa_init(FaState<D>& st, const bf16* qrow, bool v
 // than 2^31 elements); rows at or beyond n are clamped to row n - 1 (a valid
 // row whose scores the caller masks).
 template <int D, int NW, typename RowOfs>
-__device__ __forceinline__ void fa_issue_one(bf16* __restrict__ dst, const bf16* __restrict__ src, int64_t j0,
-                                             int64_t n, RowOfs row_ofs) {
+__device__ __forceinline__ void fa_issue_one(bf16* __restrict__ dst, const bf16* __restrict__ src, int j0, int n,
+                                             RowOfs row_ofs) {
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;       // rows per wave instruction
   constexpr int RPW = kKT / NW;       // rows per wave
@@ -130,7 +130,7 @@ __device__ __forceinline__ void fa_issue_one(bf16* __restrict__ dst, const bf16*
     const int r0 = RPW * wave + i * RPI;
     const int r = r0 + lane / CPR;
     const int c = (lane % CPR) ^ fa_swz<D>(r);
-    const int64_t j = j0 + r;
+    const int j = j0 + r;
     const int off = row_ofs(j < n ? j : n - 1) + c * 8;
     __builtin_amdgcn_global_load_lds((const global_void*)(src + off), (lds_void*)(dst + r0 * D), 16, 0, 0);
   }
@@ -244,8 +244,7 @@ __device__ __forceinline__ void fa_mask(f32x16* s, KeyOk key_ok) {
 // Softmax + PV of tile j (scores in s), masked when needed.
 template <int D, bool CAN_MASK, typename KeyOk, typename TileFull>
 __device__ __forceinline__ void fa_finish_tile(FaState<D>& st, f32x16* s, const bf16* __restrict__ vs,
-                                               float scale_log2, int64_t base, int64_t n, KeyOk key_ok,
-                                               TileFull tile_full) {
+                                               float scale_log2, int base, int n, KeyOk key_ok, TileFull tile_full) {
   u32x4 pw[4];
   if (CAN_MASK && !(base + kKT <= n && tile_full(base)))
     fa_mask(s, [&](int kidx) { return base + kidx < n && key_ok(base + kidx); });
@@ -269,14 +268,14 @@ __device__ __forceinline__ void fa_finish_tile(FaState<D>& st, f32x16* s, const 
 // called by all NW*64 threads of the workgroup.
 template <int D, int NW, bool CAN_MASK, typename RowOfs, typename KeyOk, typename TileFull>
 __device__ __forceinline__ void fa_segment(FaState<D>& st, const FaSmem<D>& sm, const bf16* __restrict__ K,
-                                           const bf16* __restrict__ V, int64_t n, float scale_log2, RowOfs row_ofs,
+                                           const bf16* __restrict__ V, int n, float scale_log2, RowOfs row_ofs,
                                            KeyOk key_ok, TileFull tile_full) {
   if (n <= 0) return;
-  const int64_t nt = cdiv(n, kKT);
-  auto issue_k = [&](bf16* dst, int64_t t) {
+  const int nt = (n + kKT - 1) / kKT;
+  auto issue_k = [&](bf16* dst, int t) {
     if (t < nt) fa_issue_one<D, NW>(dst, K, t * kKT, n, row_ofs);
   };
-  auto issue_v = [&](bf16* dst, int64_t t) {
+  auto issue_v = [&](bf16* dst, int t) {
     if (t < nt) fa_issue_one<D, NW>(dst, V, t * kKT, n, row_ofs);
   };
   // prologue: K0, V0, K1, V1 resident, S(0) computed, then K2 into K0's
@@ -291,7 +290,7 @@ __device__ __forceinline__ void fa_segment(FaState<D>& st, const FaSmem<D>& sm, 
   fa_scores<D>(st, sm.k0, s_cur);
   __syncthreads();
   issue_k(sm.k0, 2);
-  for (int64_t j = 0; j < nt; j += 2) {
+  for (int j = 0; j < nt; j += 2) {
     // ---- even j: S(j+1) from K buffer 1, PV(j) from V buffer 0. The score
     // tile is computed unconditionally (past the end it reads a buffer no
     // load is writing and the result is unused) so that it shares a basic

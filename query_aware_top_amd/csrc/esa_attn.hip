@@ -48,6 +48,20 @@ __device__ __forceinline__ EsaKeys esa_keys(const int32_t* sel, const int32_t* n
   return kl;
 }
 
+// Key positions of one sequence in attention order: the gathered keys
+// (initial, selected, local) then the chunk [c0, c0 + m). grid (cdiv(len, 256),
+// batch).
+__global__ void esa_keylist_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
+                                   int32_t* __restrict__ keylist, int64_t stride, int topk, int64_t c0, int64_t m,
+                                   int64_t n_init, int64_t window) {
+  const int64_t bi = blockIdx.y;
+  const EsaKeys kl = esa_keys(sel, n_sel, bi, topk, c0, n_init, window);
+  const int64_t ng = kl.count();
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= ng + m) return;
+  keylist[bi * stride + j] = (int32_t)(j < ng ? kl.pos(j) : c0 + (j - ng));
+}
+
 // ---------------------------------------------------------------------------
 // Prefill / chunk attention on the matrix cores: grid (128-row tiles of the
 // chunk, head, sequence).
@@ -61,9 +75,9 @@ constexpr int kRows = 32 * kNW;
 template <int D>
 __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, bf16* __restrict__ out,
-    float* __restrict__ lse_out, int64_t H, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
-    int64_t window, int topk, float scale_log2) {
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, const int32_t* __restrict__ keylist,
+    int64_t keylist_stride, bf16* __restrict__ out, float* __restrict__ lse_out, int64_t H, int64_t ctx_len,
+    int64_t c0, int64_t m, int64_t n_init, int64_t window, int topk, float scale_log2) {
   QAT_FA_SMEM(D, sm);
   // logical id -> (row tile, head, sequence); the row tiles of one head are
   // adjacent and share an XCD (its L2 holds the head's gathered K/V)
@@ -84,16 +98,16 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
   const bf16* kb = kc + (bi * ctx_len * H + h) * D;
   const bf16* vb = vc + (bi * ctx_len * H + h) * D;
   // one key segment: the gathered keys (all before the chunk, never masked)
-  // followed by the chunk's own keys under the causal mask
+  // followed by the chunk's own keys under the causal mask; positions come
+  // from the key list built by esa_keylist_kernel
   const int HD = (int)(H * D);
-  const int64_t ng = kl.count();
-  const int64_t qi = valid ? i : -1;
-  const int64_t wave_first = i0 + wave * 32;
-  fa_segment<D, kNW, true>(
-      st, sm, kb, vb, ng + i_last + 1, scale_log2,
-      [=](int64_t j) { return (int)(j < ng ? kl.pos(j) : c0 + (j - ng)) * HD; },
-      [=](int64_t j) { return j < ng || j - ng <= qi; },
-      [=](int64_t j0) { return j0 + kKT - 1 < ng || j0 + kKT - 1 - ng <= wave_first; });
+  const int ng = (int)kl.count();
+  const int32_t* lst = keylist + bi * keylist_stride;
+  const int lim = ng + (valid ? (int)i : -1);        // this lane attends keys j <= lim
+  const int wlim = ng + (int)(i0 + wave * 32);       // every lane of the wave attends j <= wlim
+  fa_segment<D, kNW, true>(st, sm, kb, vb, ng + (int)(i_last + 1), scale_log2,
+                           [=](int j) { return lst[j] * HD; }, [=](int j) { return j <= lim; },
+                           [=](int j0) { return j0 + kKT - 1 <= wlim; });
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
   if (lse_out && valid && (lane >> 5) == 0) lse_out[(bi * m + i) * H + h] = lse;
@@ -237,18 +251,28 @@ int esa_decode_splits(int64_t n_init, int64_t topk, int64_t window) {
   return (int)cdiv(n_init + topk + window + 1, kDecKeysPerSplit);
 }
 
+int64_t esa_keylist_len(int64_t n_init, int64_t topk, int64_t window, int64_t m) {
+  return n_init + topk + window + m;
+}
+
 hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, const int32_t* sel,
-                                   const int32_t* n_sel, void* out, float* lse, int64_t batch, int64_t H,
-                                   int64_t D, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
+                                   const int32_t* n_sel, int32_t* keylist, void* out, float* lse, int64_t batch,
+                                   int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
                                    int64_t window, int topk, float scale, hipStream_t s) {
+  const int64_t kls = esa_keylist_len(n_init, topk, window, m);
+  hipLaunchKernelGGL(esa_keylist_kernel, dim3((unsigned)cdiv(kls, 256), (unsigned)batch), dim3(256), 0, s, sel,
+                     n_sel, keylist, kls, topk, c0, m, n_init, window);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)(cdiv(m, kRows) * H * batch));
   const float sl2 = scale * kLog2e;
   if (D == 64)
     hipLaunchKernelGGL(esa_prefill_kernel<64>, grid, dim3(kThreads), 0, s, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                       sel, n_sel, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2);
+                       sel, n_sel, keylist, kls, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2);
   else
     hipLaunchKernelGGL(esa_prefill_kernel<128>, grid, dim3(kThreads), 0, s, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, sel, n_sel, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2);
+                       (const bf16*)v, sel, n_sel, keylist, kls, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window,
+                       topk, sl2);
   return hipGetLastError();
 }
 

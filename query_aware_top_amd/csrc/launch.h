@@ -67,10 +67,11 @@ hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const floa
 // ---- ESA attention (esa_attn.hip) -----------------------------------------
 int esa_decode_splits(int64_t n_init, int64_t topk, int64_t window);
 bool esa_decode_supported(int64_t H, int64_t D);
+int64_t esa_keylist_len(int64_t n_init, int64_t topk, int64_t window, int64_t m);
 hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, const int32_t* sel,
-                                   const int32_t* n_sel, void* out, float* lse, int64_t batch, int64_t H, int64_t D,
-                                   int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init, int64_t window, int topk,
-                                   float scale, hipStream_t s);
+                                   const int32_t* n_sel, int32_t* keylist, void* out, float* lse, int64_t batch,
+                                   int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
+                                   int64_t window, int topk, float scale, hipStream_t s);
 hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, const int32_t* sel,
                                   const int32_t* n_sel, float* po, float* pm, float* pl, void* out, float* lse,
                                   int64_t batch, int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t n_init,

@@ -192,8 +192,8 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_kernel(
   const bf16* vb = v + ((bi * seq_len + b * block) * hkv + g) * D;
   const int kv_stride = (int)(hkv * D);
   // FULL: block % 64 == 0, so no tile of the block needs masking
-  fa_segment<D, kNW, !FULL>(st, sm, kb, vb, block, scale_log2, [=](int64_t j) { return (int)j * kv_stride; },
-                            [](int64_t) { return true; }, [](int64_t) { return true; });
+  fa_segment<D, kNW, !FULL>(st, sm, kb, vb, block, scale_log2, [=](int j) { return j * kv_stride; },
+                            [](int) { return true; }, [](int) { return true; });
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
   if ((lane >> 5) == 0) {
@@ -276,12 +276,13 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
   const bf16* kb = k + ((bi * seq_len + kpos0) * hkv + g) * D;
   const bf16* vb = v + ((bi * seq_len + kpos0) * hkv + g) * D;
   const int kv_stride = (int)(hkv * D);
-  const int64_t qpos = valid ? t : -1;
-  const int64_t wave_first = t0 + (wave * 32) / pack;   // smallest query position of this wave
-  fa_segment<D, NW, true>(st, sm, kb, vb, t_last - kpos0 + 1, scale_log2,
-                          [=](int64_t j) { return (int)j * kv_stride; },
-                          [=](int64_t j) { return kpos0 + j <= qpos; },
-                          [=](int64_t j0) { return kpos0 + j0 + kKT - 1 <= wave_first; });
+  // keys are block-relative: this lane attends keys j <= lim, and every lane
+  // of the wave attends keys j <= wlim
+  const int lim = valid ? (int)(t - kpos0) : -1;
+  const int wlim = (int)(t0 - kpos0) + (wave * 32) / pack;
+  fa_segment<D, NW, true>(st, sm, kb, vb, (int)(t_last - kpos0 + 1), scale_log2,
+                          [=](int j) { return j * kv_stride; }, [=](int j) { return j <= lim; },
+                          [=](int j0) { return j0 + kKT - 1 <= wlim; });
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
   if ((lane >> 5) == 0) s_lse[myrow] = lse;
