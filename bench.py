@@ -263,8 +263,8 @@ class EsaWorkload(Workload):
             per_seq = el
             return {"value": per_seq * 1e6 * self.B, "unit": "us/step", "cores": cores, "kind": "oracle",
                     "sample": f"sequence 0 of {self.B} (key compression of the cache, selection, attention), "
-                              f"scaled by {self.B} sequences; float64 numpy with BLAS threads for the matrix products, "
-                              f"BLAS threads for the matrix products, one process; {el:.1f} s"}
+                              f"scaled by {self.B} sequences; float64 numpy, BLAS threads for the matrix products, "
+                              f"one process; {el:.1f} s"}
         att_per_row = (el - t_sel) / rows
         est = t_sel + att_per_row * self.m
         return {"value": self.m / est, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",

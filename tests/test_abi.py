@@ -1,0 +1,167 @@
+"""CPU checks of the C ABI: the shared library loads, exports every function
+that include/qat.h declares, and rejects invalid arguments with the
+documented status before any device work (no GPU is touched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import query_aware_top_amd as qat
+from query_aware_top_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qat.h")
+
+QAT_OK, QAT_EINVAL, QAT_EUNSUPPORTED, QAT_EWORKSPACE = 0, -1, -2, -3
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+\**([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return [n for n in names if n not in ("if", "return")]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = B.lib_path
+    if not os.path.exists(path):
+        pytest.skip("libqat.so not built")
+    return ctypes.CDLL(path)
+
+
+def test_header_declares_the_entry_points():
+    names = set(header_functions())
+    for n in ("esa_compress", "esa_select", "esa_sparse_attn", "moba_block_select", "moba_sparse_attn",
+              "esa_workspace_size", "moba_workspace_size", "qat_last_error", "qat_abi_version"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = header_functions()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(names) == set(B.EXPORTED_SYMBOLS)
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+QAT_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert m and lib.qat_abi_version() == int(m.group(1))
+
+
+def _moba(**kw):
+    base = dict(batch=1, seq_len=4096, n_q_heads=4, n_kv_heads=2, head_dim=64, block=256, topk=3)
+    base.update(kw)
+    return qat.moba_params(**base)
+
+
+def _esa(**kw):
+    base = dict(batch=1, n_heads=4, head_dim=64, d_c=64, ctx_len=2048, chunk_start=1792, chunk_len=256,
+                n_init=16, window=128, topk=64, radius=2, clip=48.0)
+    base.update(kw)
+    return qat.esa_params(**base)
+
+
+def _size(lib, fn, p):
+    n = ctypes.c_size_t(0)
+    rc = getattr(lib, fn)(ctypes.byref(p), ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,rc", [
+    ({}, QAT_OK),
+    (dict(topk=0), QAT_EINVAL),
+    (dict(topk=17), QAT_EINVAL),
+    (dict(n_kv_heads=3), QAT_EINVAL),
+    (dict(head_dim=96), QAT_EUNSUPPORTED),
+    (dict(block=0), QAT_EINVAL),
+    (dict(q_start=4000, q_len=200), QAT_EINVAL),
+    (dict(window=-1), QAT_EINVAL),
+    (dict(scale=float("inf")), QAT_EINVAL),
+    (dict(scale=-1.0), QAT_EINVAL),
+])
+def test_moba_params_validation(lib, kw, rc):
+    p = _moba(**kw)
+    got, n = _size(lib, "moba_workspace_size", p)
+    assert got == rc
+    if rc == QAT_OK:
+        assert n > 0 and n % 256 == 0
+    else:
+        lib.qat_last_error.restype = ctypes.c_char_p
+        assert lib.qat_last_error()   # a message names the bad argument
+
+
+@pytest.mark.parametrize("kw,rc", [
+    ({}, QAT_OK),
+    (dict(chunk_len=1, chunk_start=2047), QAT_OK),
+    (dict(head_dim=80), QAT_EUNSUPPORTED),
+    (dict(d_c=48), QAT_EUNSUPPORTED),
+    (dict(chunk_start=2000, chunk_len=100), QAT_EINVAL),
+    (dict(topk=0), QAT_EINVAL),
+    (dict(clip=0.0), QAT_EINVAL),
+    (dict(radius=-1), QAT_EINVAL),
+    (dict(scale=0.0), QAT_EINVAL),
+])
+def test_esa_params_validation(lib, kw, rc):
+    got, n = _size(lib, "esa_workspace_size", _esa(**kw))
+    assert got == rc
+    if rc == QAT_OK:
+        assert n > 0
+
+
+def test_workspace_too_small_is_rejected_before_device_work(lib):
+    # dummy non-NULL device pointers: nothing may be dereferenced or launched
+    dummy = ctypes.c_void_p(0x1000)
+    p = _moba()
+    rc, need = _size(lib, "moba_workspace_size", p)
+    assert rc == QAT_OK
+    rc = lib.moba_block_select(ctypes.byref(p), dummy, dummy, dummy, dummy, ctypes.c_size_t(need - 1),
+                               ctypes.c_void_p(0))
+    assert rc == QAT_EWORKSPACE
+    rc = lib.moba_sparse_attn(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, None, dummy,
+                              ctypes.c_size_t(need - 256), ctypes.c_void_p(0))
+    assert rc == QAT_EWORKSPACE
+    pe = _esa()
+    rc, need = _size(lib, "esa_workspace_size", pe)
+    rc = lib.esa_select(ctypes.byref(pe), dummy, dummy, None, dummy, dummy, dummy, None, dummy,
+                        ctypes.c_size_t(need - 1), ctypes.c_void_p(0))
+    assert rc == QAT_EWORKSPACE
+    rc = lib.esa_sparse_attn(ctypes.byref(pe), dummy, dummy, dummy, dummy, dummy, dummy, None, None,
+                             ctypes.c_size_t(0), ctypes.c_void_p(0))
+    assert rc == QAT_EWORKSPACE
+
+
+def test_null_pointers_are_rejected(lib):
+    dummy = ctypes.c_void_p(0x1000)
+    p = _moba()
+    rc = lib.moba_block_select(ctypes.byref(p), None, dummy, dummy, dummy, ctypes.c_size_t(1 << 30),
+                               ctypes.c_void_p(0))
+    assert rc == QAT_EINVAL
+    rc = lib.moba_sparse_attn(ctypes.byref(p), dummy, dummy, dummy, dummy, None, None, dummy,
+                              ctypes.c_size_t(1 << 30), ctypes.c_void_p(0))
+    assert rc == QAT_EINVAL
+    pe = _esa()
+    rc = lib.esa_select(ctypes.byref(pe), dummy, None, None, dummy, dummy, dummy, None, dummy,
+                        ctypes.c_size_t(1 << 30), ctypes.c_void_p(0))
+    assert rc == QAT_EINVAL
+    assert lib.moba_block_select(None, dummy, dummy, dummy, dummy, ctypes.c_size_t(0), None) == QAT_EINVAL
+
+
+def test_compress_validation(lib):
+    dummy = ctypes.c_void_p(0x1000)
+    n = ctypes.c_size_t(0)
+    assert lib.esa_compress_workspace_size(ctypes.c_int64(16), ctypes.c_int64(4096), ctypes.c_int64(128),
+                                           ctypes.byref(n)) == QAT_OK
+    assert n.value > 0
+    # d_c not supported
+    rc = lib.esa_compress(dummy, ctypes.c_int64(16), ctypes.c_int64(4096), ctypes.c_int64(4096), ctypes.c_int32(1),
+                          dummy, None, ctypes.c_int64(100), dummy, ctypes.c_int64(100), ctypes.c_int32(1), dummy,
+                          ctypes.c_size_t(n.value), None)
+    assert rc == QAT_EUNSUPPORTED
+    # row stride shorter than the row
+    rc = lib.esa_compress(dummy, ctypes.c_int64(16), ctypes.c_int64(1024), ctypes.c_int64(4096), ctypes.c_int32(1),
+                          dummy, None, ctypes.c_int64(128), dummy, ctypes.c_int64(128), ctypes.c_int32(1), dummy,
+                          ctypes.c_size_t(n.value), None)
+    assert rc == QAT_EINVAL
