@@ -132,6 +132,7 @@ struct MobaLayout {
   int64_t nbc = 0, nrows = 0, nbuckets = 0, max_tiles = 0;
   double* mp_part = nullptr;
   float* kbar = nullptr;
+  qat::bf16* kplanes = nullptr;
   int32_t* counts = nullptr;
   int32_t* offsets = nullptr;
   int32_t* cursor = nullptr;
@@ -174,6 +175,7 @@ MobaLayout moba_layout(const qat_moba_params* p, void* ws) {
   qat::Carver c(ws);
   L.mp_part = c.take<double>((size_t)p->batch * L.nbc * qat::meanpool_splits(p->block) * cols);
   L.kbar = c.take<float>((size_t)p->batch * L.nbc * cols);
+  L.kplanes = c.take<qat::bf16>((size_t)3 * p->batch * L.nbc * cols);
   L.counts = c.take<int32_t>((size_t)L.nbuckets + 1);
   L.offsets = c.take<int32_t>((size_t)L.nbuckets + 1);
   L.cursor = c.take<int32_t>((size_t)L.nbuckets + 1);
@@ -416,11 +418,11 @@ QAT_EXPORT int moba_block_select(const qat_moba_params* p, const void* q, const 
   if (p->topk > 1 && nbc_need > 0) {
     qat::KTimer tm("moba_meanpool", s);
     e = qat::launch_moba_meanpool(k, bf, p->batch, p->seq_len, p->n_kv_heads, p->head_dim, p->block, nbc_need,
-                                  L.mp_part, L.kbar, s);
+                                  L.mp_part, L.kbar, bf ? L.kplanes : nullptr, s);
     if (e != hipSuccess) return hip_status(e, "moba_block_select: mean pool");
   }
   qat::KTimer tm("moba_select", s);
-  e = qat::launch_moba_select(q, bf, L.kbar, blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim,
+  e = qat::launch_moba_select(q, bf, L.kbar, L.kplanes, blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim,
                               nbc_need, p->q_start, p->q_len, p->block, p->topk, s);
   return hip_status(e, "moba_block_select: scoring");
 }

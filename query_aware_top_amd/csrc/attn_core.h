@@ -266,10 +266,28 @@ __device__ __forceinline__ void fa_finish_tile(FaState<D>& st, f32x16* s, const 
 // iteration j the buffers of K_{j+1} and V_j are free and receive K_{j+3} and
 // V_{j+2}, so every direct load has a whole iteration to land. Must be
 // called by all NW*64 threads of the workgroup.
+//
+// Split form: fa_segment_begin issues the first tiles' direct loads (no
+// registers held), after which the caller may issue loads of its own and
+// fold them into the state (their wait also covers the tiles, which are
+// older); fa_segment_run then computes.
+template <int D, int NW, typename RowOfs>
+__device__ __forceinline__ void fa_segment_begin(const FaSmem<D>& sm, const bf16* __restrict__ K,
+                                                 const bf16* __restrict__ V, int n, RowOfs row_ofs) {
+  if (n <= 0) return;
+  const int nt = (n + kKT - 1) / kKT;
+  fa_issue_one<D, NW>(sm.k0, K, 0, n, row_ofs);
+  fa_issue_one<D, NW>(sm.v0, V, 0, n, row_ofs);
+  if (nt > 1) {
+    fa_issue_one<D, NW>(sm.k1, K, kKT, n, row_ofs);
+    fa_issue_one<D, NW>(sm.v1, V, kKT, n, row_ofs);
+  }
+}
+
 template <int D, int NW, bool CAN_MASK, typename RowOfs, typename KeyOk, typename TileFull>
-__device__ __forceinline__ void fa_segment(FaState<D>& st, const FaSmem<D>& sm, const bf16* __restrict__ K,
-                                           const bf16* __restrict__ V, int n, float scale_log2, RowOfs row_ofs,
-                                           KeyOk key_ok, TileFull tile_full) {
+__device__ __forceinline__ void fa_segment_run(FaState<D>& st, const FaSmem<D>& sm, const bf16* __restrict__ K,
+                                               const bf16* __restrict__ V, int n, float scale_log2,
+                                               RowOfs row_ofs, KeyOk key_ok, TileFull tile_full) {
   if (n <= 0) return;
   const int nt = (n + kKT - 1) / kKT;
   auto issue_k = [&](bf16* dst, int t) {
@@ -278,12 +296,8 @@ __device__ __forceinline__ void fa_segment(FaState<D>& st, const FaSmem<D>& sm, 
   auto issue_v = [&](bf16* dst, int t) {
     if (t < nt) fa_issue_one<D, NW>(dst, V, t * kKT, n, row_ofs);
   };
-  // prologue: K0, V0, K1, V1 resident, S(0) computed, then K2 into K0's
-  // buffer (after every wave has read K0)
-  issue_k(sm.k0, 0);
-  issue_v(sm.v0, 0);
-  issue_k(sm.k1, 1);
-  issue_v(sm.v1, 1);
+  // prologue (K0, V0, K1, V1 issued by fa_segment_begin): S(0) computed,
+  // then K2 into K0's buffer (after every wave has read K0)
   fa_wait_loads();
   __syncthreads();
   f32x16 s_cur[2], s_nxt[2];
@@ -313,6 +327,14 @@ __device__ __forceinline__ void fa_segment(FaState<D>& st, const FaSmem<D>& sm, 
   }
   fa_wait_loads();
   __syncthreads();
+}
+
+template <int D, int NW, bool CAN_MASK, typename RowOfs, typename KeyOk, typename TileFull>
+__device__ __forceinline__ void fa_segment(FaState<D>& st, const FaSmem<D>& sm, const bf16* __restrict__ K,
+                                           const bf16* __restrict__ V, int n, float scale_log2, RowOfs row_ofs,
+                                           KeyOk key_ok, TileFull tile_full) {
+  fa_segment_begin<D, NW>(sm, K, V, n, row_ofs);
+  fa_segment_run<D, NW, CAN_MASK>(st, sm, K, V, n, scale_log2, row_ofs, key_ok, tile_full);
 }
 
 // Final normalisation: returns the lane's 1/l and natural-log lse.

@@ -233,14 +233,33 @@ __global__ void esa_decode_combine_kernel(const float* __restrict__ po, const fl
   if (c0 > n_init) n_l = c0 - max(n_init, c0 - window);
   const int64_t nkeys = n_i + n_sel[bi] + n_l + 1;
   const int ns = (int)min((int64_t)nsplit_max, cdiv(nkeys, kDecKeysPerSplit));
-  float M = -__builtin_inff();
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[(bi * nsplit_max + s) * H + head]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const int64_t p = (bi * nsplit_max + s) * H + head;
-    const float w = exp2f(pm[p] - M);
-    L += pl[p] * w;
-    O += po[p * D + (idx % D)] * w;
+  // online log-sum-exp merge over the splits, 8 splits' loads in flight
+  constexpr int U = 8;
+  float M = -__builtin_inff(), L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float mv[U], lv[U], ov[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = min(s0 + u, ns - 1);
+      const int64_t p = (bi * nsplit_max + sp) * H + head;
+      mv[u] = pm[p];
+      lv[u] = pl[p];
+      ov[u] = po[p * D + (idx % D)];
+      if (s0 + u >= ns) mv[u] = -__builtin_inff();
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) Mn = fmaxf(Mn, mv[u]);
+    const float a = M == -__builtin_inff() ? 0.f : exp2f(M - Mn);
+    L *= a;
+    O *= a;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = mv[u] == -__builtin_inff() ? 0.f : exp2f(mv[u] - Mn);
+      L = fmaf(lv[u], w, L);
+      O = fmaf(ov[u], w, O);
+    }
+    M = Mn;
   }
   out[bi * H * D + idx] = (bf16)(O / L);
   if (lse_out && (idx % D) == 0) lse_out[bi * H + head] = M * kLn2 + logf(L);

@@ -22,11 +22,14 @@ hipError_t launch_compress_finalize(const double* partial, int nsplit, int64_t n
 
 // ---- MoBA gating (moba_select.hip) ----------------------------------------
 int meanpool_splits(int block);
+// planes: NULL, or 3 * batch*nbc*hkv*d bfloat16 (hi/mid/lo split of the means)
 hipError_t launch_moba_meanpool(const void* k, bool bf, int64_t batch, int64_t seq_len, int64_t hkv, int64_t d,
-                                int block, int64_t nbc, double* partial, float* kbar, hipStream_t s);
-hipError_t launch_moba_select(const void* q, bool bf, const float* kbar, int32_t* blk, int64_t batch,
-                              int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t nbc, int64_t q_start,
-                              int64_t q_len, int block, int topk, hipStream_t s);
+                                int block, int64_t nbc, double* partial, float* kbar, bf16* planes,
+                                hipStream_t s);
+// bfloat16 queries score on the matrix cores from `planes`; float32 ones use `kbar`
+hipError_t launch_moba_select(const void* q, bool bf, const float* kbar, const bf16* planes, int32_t* blk,
+                              int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t nbc,
+                              int64_t q_start, int64_t q_len, int block, int topk, hipStream_t s);
 
 // ---- MoBA attention (moba_attn.hip) ---------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);

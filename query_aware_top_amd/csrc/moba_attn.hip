@@ -221,15 +221,15 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_kernel(
   }
 }
 
-// Current-block attention (causal) plus the log-sum-exp merge of the row's
-// past-block partials. A workgroup holds 32*NW rows = 32*NW/P consecutive
+// Current-block attention (causal) merged with the row's past-block
+// partials: the partials seed the online-softmax state (running max, sum and
+// accumulator), so the merge costs no pass of its own and its loads overlap
+// the first K/V tiles. A workgroup holds 32*NW rows = 32*NW/P consecutive
 // tokens x P query heads of one KV group (GQA packing: the heads share K/V).
-// Logical id -> (token tile, block, sequence, KV head, head pack). NW = 4
-// lets two workgroups share a CU, so one's merge epilogue (memory-bound)
-// overlaps the other's matrix-core work.
+// Logical id -> (token tile, block, sequence, KV head, head pack).
 constexpr int kCurNW = 4;
 constexpr int kCurRows = 32 * kCurNW;
-constexpr int kMergeMax = 3;   // past slots merged with batched loads (more: looped)
+constexpr int kPreSlots = 2;   // past partials loaded ahead of the tiles (more: folded in one by one)
 
 template <int D>
 __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
@@ -241,7 +241,6 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
   constexpr int NW = kCurNW;
   constexpr int THREADS = 64 * NW;
   QAT_FA_SMEM(D, sm);
-  __shared__ float s_lse[kCurRows];
   int64_t id = xcd_logical_id(blockIdx.x, gridDim.x);
   const int tt = (int)(id % tiles_per_block);
   id /= tiles_per_block;
@@ -264,96 +263,94 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
   const int64_t h0 = g * gs + hp * pack;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hl = lane >> 5;
   const int myrow = wave * 32 + (lane & 31);
   const int64_t t = t0 + myrow / pack;
   const int64_t h = h0 + myrow % pack;
   const bool valid = t <= t_last;
-  const bf16* qrow = q + ((bi * seq_len + (valid ? t : t0)) * hq + h) * D;
+  const int64_t row = (bi * q_len + ((valid ? t : t0) - q_start)) * hq + h;
+  const int km = topk - 1;
 
-  FaState<D> st;
-  fa_init<D>(st, qrow, valid);
   const int64_t kpos0 = c * block;
   const bf16* kb = k + ((bi * seq_len + kpos0) * hkv + g) * D;
   const bf16* vb = v + ((bi * seq_len + kpos0) * hkv + g) * D;
   const int kv_stride = (int)(hkv * D);
+  const int nkeys = (int)(t_last - kpos0 + 1);
+  auto row_ofs = [=](int j) { return j * kv_stride; };
+  fa_segment_begin<D, NW>(sm, kb, vb, nkeys, row_ofs);
+
+  FaState<D> st;
+  fa_init<D>(st, q + ((bi * seq_len + (valid ? t : t0)) * hq + h) * D, valid);
+  // Seed the online softmax with the row's past-block partials (normalised o
+  // in bf16, natural-log lse): m = max lse in log2 units, l = sum of
+  // 2^(lse - m) (kept by the lower half-wave only: l is summed over the two
+  // halves at the end), o = sum of 2^(lse - m) o_p. The lane's accumulator
+  // holds d = 32 tq + 8 gi + 4 hl + 0..3. These loads are younger than the
+  // tiles', so waiting for them costs no extra latency.
+  auto fold = [&](float l2, const uint2* pov) {
+    const float m_new = fmaxf(st.m, l2);
+    const float a = st.m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
+    const float w = __builtin_amdgcn_exp2f(l2 - m_new);
+    st.l = st.l * a + (hl == 0 ? w : 0.f);
+#pragma unroll
+    for (int tq = 0; tq < D / 32; ++tq)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const uint2 u = pov[tq * 4 + gi];
+        const float v0 = __builtin_bit_cast(float, u.x << 16), v1 = __builtin_bit_cast(float, u.x & 0xffff0000u);
+        const float v2 = __builtin_bit_cast(float, u.y << 16), v3 = __builtin_bit_cast(float, u.y & 0xffff0000u);
+        st.o[tq][4 * gi + 0] = st.o[tq][4 * gi + 0] * a + w * v0;
+        st.o[tq][4 * gi + 1] = st.o[tq][4 * gi + 1] * a + w * v1;
+        st.o[tq][4 * gi + 2] = st.o[tq][4 * gi + 2] * a + w * v2;
+        st.o[tq][4 * gi + 3] = st.o[tq][4 * gi + 3] * a + w * v3;
+      }
+    st.m = m_new;
+  };
+  const int32_t* br = blk + row * topk;
+  for (int s0 = 0; s0 < km; s0 += kPreSlots) {   // one round for k <= kPreSlots + 1
+    float plse[kPreSlots];
+    uint2 po[kPreSlots][D / 8];
+#pragma unroll
+    for (int sl = 0; sl < kPreSlots; ++sl) {
+      const int32_t b = (valid && s0 + sl < km) ? br[s0 + sl] : -1;
+      const bool use = b >= 0 && b < c;
+      const int64_t pidx = row * km + s0 + sl;
+      plse[sl] = use ? part_lse[pidx] : -__builtin_inff();
+      if (use) {
+        const bf16* src = part_o + pidx * D + 4 * hl;
+#pragma unroll
+        for (int gq = 0; gq < D / 8; ++gq) po[sl][gq] = *(const uint2*)(src + 8 * gq);
+      }
+    }
+#pragma unroll
+    for (int sl = 0; sl < kPreSlots; ++sl)
+      if (plse[sl] != -__builtin_inff()) fold(plse[sl] * kLog2e, po[sl]);
+  }
+
   // keys are block-relative: this lane attends keys j <= lim, and every lane
   // of the wave attends keys j <= wlim
   const int lim = valid ? (int)(t - kpos0) : -1;
   const int wlim = (int)(t0 - kpos0) + (wave * 32) / pack;
-  fa_segment<D, NW, true>(st, sm, kb, vb, (int)(t_last - kpos0 + 1), scale_log2,
-                          [=](int j) { return j * kv_stride; }, [=](int j) { return j <= lim; },
-                          [=](int j0) { return j0 + kKT - 1 <= wlim; });
+  fa_segment_run<D, NW, true>(st, sm, kb, vb, nkeys, scale_log2, row_ofs, [=](int j) { return j <= lim; },
+                              [=](int j0) { return j0 + kKT - 1 <= wlim; });
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
-  if ((lane >> 5) == 0) s_lse[myrow] = lse;
+  if (lse_out && valid && hl == 0) lse_out[row] = lse;
   fa_rows_to_lds<D>(st, sm, inv_l, 0);
   __syncthreads();
-
-  // merge: TPR threads per row, 8 d each; all loads of a row are issued
-  // before any is consumed (partial rows are read contiguous)
   constexpr int TPR = D / 8;
   constexpr int RPP = THREADS / TPR;
   const int sub = threadIdx.x % TPR;
   const int nrows = (int)(t_last - t0 + 1) * pack;
-  const int km = topk - 1;
   for (int rr = threadIdx.x / TPR; rr < nrows; rr += RPP) {
-    const int64_t tq = t0 + rr / pack;
-    const int64_t row = (bi * q_len + (tq - q_start)) * hq + h0 + rr % pack;
-    const int32_t* br = blk + row * topk;
-    const float l_cur = s_lse[rr];
+    const int64_t orow = (bi * q_len + (t0 + rr / pack - q_start)) * hq + h0 + rr % pack;
     const f32x4 a = fa_row_chunk<D>(sm, rr, 2 * sub), cc = fa_row_chunk<D>(sm, rr, 2 * sub + 1);
-    bool use[kMergeMax];
-    float pl[kMergeMax];
-    bf16x8 pv[kMergeMax];
-#pragma unroll
-    for (int s = 0; s < kMergeMax; ++s) {
-      const int32_t b = s < km ? br[s] : -1;
-      use[s] = b >= 0 && b < c;
-      const int64_t pidx = row * km + s;
-      pl[s] = use[s] ? part_lse[pidx] : -__builtin_inff();
-      if (use[s]) pv[s] = *(const bf16x8*)(part_o + pidx * D + sub * 8);
-    }
-    float lse_tot = l_cur;
-#pragma unroll
-    for (int s = 0; s < kMergeMax; ++s)
-      if (use[s]) {
-        const float mx = fmaxf(lse_tot, pl[s]);
-        lse_tot = mx + logf(expf(lse_tot - mx) + expf(pl[s] - mx));
-      }
-    for (int s = kMergeMax; s < km; ++s) {
-      const int32_t b = br[s];
-      if (b >= 0 && b < c) {
-        const float l2 = part_lse[row * km + s];
-        const float mx = fmaxf(lse_tot, l2);
-        lse_tot = mx + logf(expf(lse_tot - mx) + expf(l2 - mx));
-      }
-    }
-    const float w_cur = expf(l_cur - lse_tot);
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { acc[e] = a[e] * w_cur; acc[4 + e] = cc[e] * w_cur; }
-#pragma unroll
-    for (int s = 0; s < kMergeMax; ++s)
-      if (use[s]) {
-        const float w = expf(pl[s] - lse_tot);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += w * (float)pv[s][e];
-      }
-    for (int s = kMergeMax; s < km; ++s) {
-      const int32_t b = br[s];
-      if (b >= 0 && b < c) {
-        const int64_t pidx = row * km + s;
-        const float w = expf(part_lse[pidx] - lse_tot);
-        const bf16x8 p2 = *(const bf16x8*)(part_o + pidx * D + sub * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += w * (float)p2[e];
-      }
-    }
-    u32x4 wv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) wv[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
-    *(u32x4*)(out + row * D + sub * 8) = wv;
-    if (lse_out && sub == 0) lse_out[row] = lse_tot;
+    u32x4 w;
+    w[0] = pack_bf16x2(a[0], a[1]);
+    w[1] = pack_bf16x2(a[2], a[3]);
+    w[2] = pack_bf16x2(cc[0], cc[1]);
+    w[3] = pack_bf16x2(cc[2], cc[3]);
+    *(u32x4*)(out + orow * D + sub * 8) = w;
   }
 }
 

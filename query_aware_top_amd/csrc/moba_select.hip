@@ -6,16 +6,41 @@
 // gate; causality (no future blocks); the query's own block is always
 // attended. k counts that forced block, so k - 1 earlier blocks are chosen;
 // the current block never competes.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
 namespace qat {
 
 // ---------------------------------------------------------------------------
-// Mean pool, pass 1: each workgroup sums a slice of one block's tokens for all
-// Hkv*d columns in float64 (HBM-bound stream of K, coalesced rows).
+// Mean pool, pass 1: a workgroup sums a slice of one block's tokens for all
+// Hkv*d columns in float64. A thread owns 8 adjacent columns (one 16-byte
+// load per token for bf16) and keeps kMpUnroll token rows in flight; the
+// stream of K is read once, in whole rows.
+constexpr int kMpThreads = 128;
+constexpr int kMpUnroll = 8;
+
 template <typename T>
-__global__ __launch_bounds__(256) void meanpool_partial_kernel(
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&v)[8]) {
+  const bf16x8 t = *(const bf16x8*)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)t[i];
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kMpThreads) void meanpool_partial_kernel(
     const T* __restrict__ k, int64_t seq_len, int64_t cols, int block, int tokens_per_split,
     int nsplit, int64_t nbc, double* __restrict__ partial) {
   const int split = blockIdx.x;
@@ -25,31 +50,55 @@ __global__ __launch_bounds__(256) void meanpool_partial_kernel(
   const int64_t t1 = min(b * block + (int64_t)block, t0 + tokens_per_split);
   const T* base = k + bi * seq_len * cols;
   double* dst = partial + ((bi * nbc + b) * nsplit + split) * cols;
-  for (int64_t cg = threadIdx.x; cg < cols / 4; cg += blockDim.x) {
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    for (int64_t t = t0; t < t1; ++t) {
-      const T* p = base + t * cols + cg * 4;
-      a0 += (double)to_f32(p[0]);
-      a1 += (double)to_f32(p[1]);
-      a2 += (double)to_f32(p[2]);
-      a3 += (double)to_f32(p[3]);
+  for (int64_t cg = threadIdx.x; cg < cols / 8; cg += kMpThreads) {
+    double a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = 0.0;
+    int64_t t = t0;
+    for (; t + kMpUnroll <= t1; t += kMpUnroll) {   // full groups: all loads issued before any add
+      float v[kMpUnroll][8];
+#pragma unroll
+      for (int u = 0; u < kMpUnroll; ++u) load8<T>(base + (t + u) * cols + cg * 8, v[u]);
+#pragma unroll
+      for (int u = 0; u < kMpUnroll; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] += (double)v[u][i];
     }
-    dst[cg * 4 + 0] = a0;
-    dst[cg * 4 + 1] = a1;
-    dst[cg * 4 + 2] = a2;
-    dst[cg * 4 + 3] = a3;
+    for (; t < t1; ++t) {
+      float v[8];
+      load8<T>(base + t * cols + cg * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] += (double)v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[cg * 8 + i] = a[i];
   }
 }
 
-// Mean pool, pass 2: sum the slices in order and divide by B.
+// Mean pool, pass 2: sum the slices in order and divide by B. Besides the
+// float32 means it writes, when `planes` is non-NULL, three bfloat16 planes
+// hi/mid/lo with hi + mid + lo == mean exactly (each term is the rounded
+// remainder of the previous ones), the operands of the matrix-core scoring.
 __global__ void meanpool_finalize_kernel(const double* __restrict__ partial, int nsplit, int64_t nrows,
-                                         int64_t cols, int block, float* __restrict__ kbar) {
+                                         int64_t cols, int block, float* __restrict__ kbar,
+                                         bf16* __restrict__ planes) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= nrows * cols) return;
+  const int64_t total = nrows * cols;
+  if (idx >= total) return;
   const int64_t r = idx / cols, c = idx % cols;
   double s = 0.0;
   for (int i = 0; i < nsplit; ++i) s += partial[(r * nsplit + i) * cols + c];
-  kbar[idx] = (float)(s / (double)block);
+  const float x = (float)(s / (double)block);
+  kbar[idx] = x;
+  if (planes) {
+    const bf16 hi = (bf16)x;
+    const float r1 = x - (float)hi;
+    const bf16 mid = (bf16)r1;
+    const bf16 lo = (bf16)(r1 - (float)mid);
+    planes[idx] = hi;
+    planes[total + idx] = mid;
+    planes[2 * total + idx] = lo;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -148,27 +197,175 @@ __global__ __launch_bounds__(256) void moba_score_select_kernel(
 }
 
 // ---------------------------------------------------------------------------
-int meanpool_splits(int block) { return (int)cdiv(block, 256); }
+// Scoring and selection on the matrix cores (bfloat16 queries). The block
+// means enter as three bfloat16 planes whose sum is the float32 mean exactly,
+// so every product is exact and only the float32 accumulation rounds, as in
+// a float32 dot product. Transposed tiles S^T = Kbar Q^T: a wave scores 64
+// query rows (two 32-column tiles) against 32 blocks per round with
+// v_mfma_f32_32x32x16_bf16; the scores go through LDS so that each lane then
+// owns one query row and inserts that row's blocks in ascending order into
+// its running top list (same order and tie rule as the scalar kernel).
+constexpr int kSelWaves = 4;
+constexpr int kSelRowsPerWave = 64;
+constexpr int kSelBlocks = 32;   // blocks per round (one MFMA row tile)
+
+template <int D, int KMAX>
+__global__ __launch_bounds__(kSelWaves * 64) void moba_select_mfma_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ planes, int64_t plane_stride, int32_t* __restrict__ blk,
+    int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk) {
+  constexpr int KP = D + 8;   // padded LDS row of one block's mean
+  __shared__ __attribute__((aligned(16))) bf16 kb_s[3][kSelBlocks][KP];
+  __shared__ __attribute__((aligned(16))) float sc_s[kSelWaves][kSelRowsPerWave][kSelBlocks + 4];
+  const int64_t bi = blockIdx.z;
+  const int64_t h = blockIdx.y;
+  const int64_t g = h / (hq / hkv);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * (kSelWaves * kSelRowsPerWave);
+  const int64_t rw = r0 + wave * kSelRowsPerWave;   // first row of this wave
+  const int km = topk - 1;
+
+  // B operands: rows rw + lane%32 (tile 0) and rw + 32 + lane%32 (tile 1);
+  // lane holds d = 16 ks + 8 (lane/32) .. + 8
+  bf16x8 qa[D / 16], qb[D / 16];
+  {
+    const int64_t ra = min(rw + (lane & 31), q_len - 1), rb = min(rw + 32 + (lane & 31), q_len - 1);
+    const bf16* pa = q + ((bi * seq_len + q_start + ra) * hq + h) * D + (lane >> 5) * 8;
+    const bf16* pb = q + ((bi * seq_len + q_start + rb) * hq + h) * D + (lane >> 5) * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qa[ks] = *(const bf16x8*)(pa + ks * 16);
+      qb[ks] = *(const bf16x8*)(pb + ks * 16);
+    }
+  }
+  // selection row of this lane
+  const int64_t r = rw + lane;
+  const bool valid = r < q_len;
+  const int64_t t = q_start + (valid ? r : 0);
+  const int64_t cur = t / block;
+  float tv[KMAX];
+  int ti[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) { tv[i] = -__builtin_inff(); ti[i] = 0x7fffffff; }
+
+  const int64_t t_last = q_start + min(q_len, r0 + kSelWaves * kSelRowsPerWave) - 1;
+  const int64_t nb_wg = km > 0 ? min(nbc, t_last / block) : 0;
+  const bf16* pg = planes + ((bi * nbc) * hkv + g) * D;   // block b at pg + b*hkv*D (+ plane*plane_stride)
+  constexpr int kPieces = 3 * kSelBlocks * D / 8;          // 16-byte pieces per round
+  constexpr int kPer = kPieces / (kSelWaves * 64);
+  static_assert(kPieces % (kSelWaves * 64) == 0, "plane pieces must split evenly over the threads");
+  for (int64_t c0 = 0; c0 < nb_wg; c0 += kSelBlocks) {
+    bf16x8 piece[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {   // all loads in flight before the first LDS write
+      const int i = threadIdx.x + k * kSelWaves * 64;
+      const int pl = i / (kSelBlocks * D / 8);
+      const int rem = i % (kSelBlocks * D / 8);
+      const int bb = rem / (D / 8), dd = (rem % (D / 8)) * 8;
+      const int64_t b = min(c0 + bb, nb_wg - 1);
+      piece[k] = *(const bf16x8*)(pg + pl * plane_stride + b * hkv * D + dd);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = threadIdx.x + k * kSelWaves * 64;
+      const int pl = i / (kSelBlocks * D / 8);
+      const int rem = i % (kSelBlocks * D / 8);
+      const int bb = rem / (D / 8), dd = (rem % (D / 8)) * 8;
+      *(bf16x8*)&kb_s[pl][bb][dd] = piece[k];
+    }
+    __syncthreads();
+    f32x16 sa = {}, sb = {};
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = *(const bf16x8*)&kb_s[pl][lane & 31][ks * 16 + (lane >> 5) * 8];
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qa[ks], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sb, 0, 0, 0);
+      }
+    // C layout: lane holds query column lane%32, block rows 8*gi + 4*(lane/32) + 0..3
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int bcol = gi * 8 + (lane >> 5) * 4;
+      *(f32x4*)&sc_s[wave][lane & 31][bcol] = f32x4{sa[4 * gi], sa[4 * gi + 1], sa[4 * gi + 2], sa[4 * gi + 3]};
+      *(f32x4*)&sc_s[wave][32 + (lane & 31)][bcol] =
+          f32x4{sb[4 * gi], sb[4 * gi + 1], sb[4 * gi + 2], sb[4 * gi + 3]};
+    }
+    __syncthreads();
+    // blocks c0 + bb with bb >= nmine are not candidates of this row; they
+    // enter as -inf and can only fill slots past the first min(k-1, cur)
+    const int64_t nmine = valid ? min((int64_t)kSelBlocks, cur - c0) : 0;
+    float scv[kSelBlocks];
+#pragma unroll
+    for (int j = 0; j < kSelBlocks / 4; ++j) {
+      const f32x4 v = *(const f32x4*)&sc_s[wave][lane][4 * j];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) scv[4 * j + x] = v[x];
+    }
+#pragma unroll
+    for (int bb = 0; bb < kSelBlocks; ++bb) {
+      float cs = bb < nmine ? scv[bb] : -__builtin_inff();
+      int cb = (int)c0 + bb;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        const bool better = (cs > tv[i]) | ((cs == tv[i]) & (cb < ti[i]));
+        const float sv = tv[i];
+        const int sbk = ti[i];
+        tv[i] = better ? cs : sv;
+        ti[i] = better ? cb : sbk;
+        cs = better ? sv : cs;
+        cb = better ? sbk : cb;
+      }
+    }
+  }
+  if (!valid) return;
+  const int npick = (int)min((int64_t)km, cur);
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i)
+    if (i >= npick) ti[i] = 0x7fffffff;
+#pragma unroll
+  for (int a = 0; a < KMAX; ++a)
+#pragma unroll
+    for (int b2 = 0; b2 + 1 < KMAX - a; ++b2) {
+      const int lo = min(ti[b2], ti[b2 + 1]);
+      const int hi = max(ti[b2], ti[b2 + 1]);
+      ti[b2] = lo;
+      ti[b2 + 1] = hi;
+    }
+  int32_t* out = blk + ((bi * q_len + r) * hq + h) * topk;
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i)
+    if (i < npick) out[i] = ti[i];
+  out[npick] = (int32_t)cur;
+  for (int i = npick + 1; i < topk; ++i) out[i] = -1;
+}
+
+// ---------------------------------------------------------------------------
+int meanpool_tokens_per_split(int block) {
+  // 64-token slices for blocks up to 2048 tokens, at most 32 slices beyond
+  return (int)std::max<int64_t>(64, cdiv(block, 32));
+}
+int meanpool_splits(int block) { return (int)cdiv(block, meanpool_tokens_per_split(block)); }
 
 hipError_t launch_moba_meanpool(const void* k, bool bf, int64_t batch, int64_t seq_len, int64_t hkv,
-                                int64_t d, int block, int64_t nbc, double* partial, float* kbar,
+                                int64_t d, int block, int64_t nbc, double* partial, float* kbar, bf16* planes,
                                 hipStream_t s) {
   if (nbc <= 0) return hipSuccess;
   const int nsplit = meanpool_splits(block);
-  const int tps = (int)cdiv(block, nsplit);
+  const int tps = meanpool_tokens_per_split(block);
   const int64_t cols = hkv * d;
   dim3 grid((unsigned)nsplit, (unsigned)nbc, (unsigned)batch);
   if (bf)
-    hipLaunchKernelGGL(meanpool_partial_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)k, seq_len,
+    hipLaunchKernelGGL(meanpool_partial_kernel<bf16>, grid, dim3(kMpThreads), 0, s, (const bf16*)k, seq_len,
                        cols, block, tps, nsplit, nbc, partial);
   else
-    hipLaunchKernelGGL(meanpool_partial_kernel<float>, grid, dim3(256), 0, s, (const float*)k, seq_len,
+    hipLaunchKernelGGL(meanpool_partial_kernel<float>, grid, dim3(kMpThreads), 0, s, (const float*)k, seq_len,
                        cols, block, tps, nsplit, nbc, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = batch * nbc * cols;
   hipLaunchKernelGGL(meanpool_finalize_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
-                     partial, nsplit, batch * nbc, cols, block, kbar);
+                     partial, nsplit, batch * nbc, cols, block, kbar, planes);
   return hipGetLastError();
 }
 
@@ -189,16 +386,34 @@ static hipError_t launch_select_d(const T* q, const float* kbar, int32_t* blk, i
   return hipGetLastError();
 }
 
-hipError_t launch_moba_select(const void* q, bool bf, const float* kbar, int32_t* blk, int64_t batch,
-                              int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t nbc,
+template <int D>
+static hipError_t launch_select_mfma_d(const bf16* q, const bf16* planes, int64_t plane_stride, int32_t* blk,
+                                       int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc,
+                                       int64_t q_start, int64_t q_len, int block, int topk, hipStream_t s) {
+  dim3 grid((unsigned)cdiv(q_len, kSelWaves * kSelRowsPerWave), (unsigned)hq, (unsigned)batch);
+  const int km = topk - 1;
+#define QAT_SEL(KM_)                                                                                        \
+  hipLaunchKernelGGL((moba_select_mfma_kernel<D, KM_>), grid, dim3(kSelWaves * 64), 0, s, q, planes,       \
+                     plane_stride, blk, seq_len, hq, hkv, nbc, q_start, q_len, block, topk)
+  if (km <= 1) QAT_SEL(1);
+  else if (km <= 3) QAT_SEL(3);
+  else if (km <= 7) QAT_SEL(7);
+  else QAT_SEL(15);
+#undef QAT_SEL
+  return hipGetLastError();
+}
+
+hipError_t launch_moba_select(const void* q, bool bf, const float* kbar, const bf16* planes, int32_t* blk,
+                              int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t nbc,
                               int64_t q_start, int64_t q_len, int block, int topk, hipStream_t s) {
   if (q_len <= 0) return hipSuccess;
   if (bf) {
+    const int64_t ps = batch * nbc * hkv * d;
     if (d == 64)
-      return launch_select_d<bf16, 64>((const bf16*)q, kbar, blk, batch, seq_len, hq, hkv, nbc, q_start,
-                                       q_len, block, topk, s);
-    return launch_select_d<bf16, 128>((const bf16*)q, kbar, blk, batch, seq_len, hq, hkv, nbc, q_start,
+      return launch_select_mfma_d<64>((const bf16*)q, planes, ps, blk, batch, seq_len, hq, hkv, nbc, q_start,
                                       q_len, block, topk, s);
+    return launch_select_mfma_d<128>((const bf16*)q, planes, ps, blk, batch, seq_len, hq, hkv, nbc, q_start,
+                                     q_len, block, topk, s);
   }
   if (d == 64)
     return launch_select_d<float, 64>((const float*)q, kbar, blk, batch, seq_len, hq, hkv, nbc, q_start,
