@@ -53,7 +53,8 @@ struct EsaLayout {
   float* upart = nullptr;
   float* sraw = nullptr;
   float* smax = nullptr;
-  float* u_tmp = nullptr;
+  int32_t* tk_hist = nullptr;
+  int2* tk_cnt = nullptr;
   uint32_t* keys = nullptr;
   float* po = nullptr;
   float* pm = nullptr;
@@ -73,6 +74,8 @@ int esa_check(const qat_esa_params* p) {
     return fail(QAT_EINVAL, "chunk [%lld, %lld) outside the cache of %lld rows", (long long)p->chunk_start,
                 (long long)(p->chunk_start + p->chunk_len), (long long)p->ctx_len);
   if (p->n_init < 0 || p->window < 0 || p->radius < 0) return fail(QAT_EINVAL, "n_init, window, radius must be >= 0");
+  if (p->radius > qat::esa_topk_max_radius())
+    return fail(QAT_EUNSUPPORTED, "radius %d above the supported %d", p->radius, qat::esa_topk_max_radius());
   if (p->topk < 1) return fail(QAT_EINVAL, "topk must be >= 1");
   if (!(p->clip > 0.f)) return fail(QAT_EINVAL, "clip must be > 0 (or +inf)");
   if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return fail(QAT_EINVAL, "scale must be finite and > 0");
@@ -107,7 +110,8 @@ EsaLayout esa_layout(const qat_esa_params* p, void* ws) {
     L.sraw = c.take<float>((size_t)B * nm);
     L.smax = c.take<float>((size_t)B * L.nscan);
   }
-  L.u_tmp = c.take<float>((size_t)B * nm);
+  L.tk_hist = c.take<int32_t>((size_t)B * 3 * 2048);
+  L.tk_cnt = c.take<int2>((size_t)B * qat::esa_topk_slices((int64_t)nm));
   L.keys = c.take<uint32_t>((size_t)B * nm);
   L.keylist = c.take<int32_t>((size_t)B * qat::esa_keylist_len(p->n_init, p->topk, p->window, m));
   if (m == 1) {
@@ -355,7 +359,7 @@ QAT_EXPORT int esa_select(const qat_esa_params* p, const void* q, const void* Wq
   if (e != hipSuccess) return hip_status(e, "esa_select: scoring");
   qat::KTimer tm("esa_topk", s);
   e = qat::launch_esa_topk(mode, L.upart, L.nqsplit, L.sraw, L.smax, L.nscan, p->clip, p->batch, L.n_mid,
-                           p->radius, p->topk, L.mid0, L.u_tmp, L.keys, scores, sel, n_sel, s);
+                           p->radius, p->topk, L.mid0, L.tk_hist, L.tk_cnt, L.keys, scores, sel, n_sel, s);
   return hip_status(e, "esa_select: top-k");
 }
 

@@ -18,6 +18,8 @@
 // selection tolerance. Decode scoring is a float32 matrix-vector stream
 // (HBM-bound). Top-k is an exact radix select on order-preserving uint32
 // keys with the lowest index winning ties.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -170,142 +172,259 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one workgroup of 1024 threads per sequence.
-// mode 0 (prefill): u_j = sum of the query-split partials (float64, in order).
-// mode 1 (decode):  u_j = max(s_j - max_j' s_j', -clip).
-// Then u'_j = max over |t - j| <= r; keys = order-preserving uint32 of u';
-// radix select of the k-th largest key (11 + 11 + 10 bits), then a stable
-// compaction in index order taking the lowest-index ties.
-constexpr int kTopkThreads = 1024;
+// Top-k over the middle part, several workgroups per sequence, each owning a
+// slice of kTkSlice consecutive candidates (kTkPer per thread, contiguous):
+//   prep   u_j (mode 0, prefill: the query-split partial sums added in
+//          float64 in split order; mode 1, decode: max(s_j - max s, -clip)),
+//          u'_j = max of u over |t - j| <= r within M (halo recomputed from
+//          the inputs), order-preserving uint32 keys, histogram of the top
+//          11 key bits;
+//   hist   (twice) the next 11 / 10 bits of the keys that match the digits
+//          fixed so far;
+//   count  keys above / equal to the k-th largest key T, per slice;
+//   emit   stable compaction: every key above T, and the lowest-index keys
+//          equal to T up to k, in ascending position order.
+// Each kernel re-derives the digits fixed so far from the global
+// histograms (2048 bins, cheap), so no state passes between them.
+constexpr int kTkThreads = 256;
+constexpr int kTkPer = 8;
+constexpr int kTkSlice = kTkThreads * kTkPer;
+constexpr int kTkMaxRadius = 1024;
+constexpr int kTkBins = 2048;
+__host__ __device__ constexpr int tk_shift(int pass) { return pass == 0 ? 21 : pass == 1 ? 10 : 0; }
+__host__ __device__ constexpr int tk_bits(int pass) { return pass == 2 ? 10 : 11; }
 
-__device__ int32_t block_exclusive_scan(int32_t v, int32_t* s_tmp, int32_t* total) {
-  const int tid = threadIdx.x;
-  s_tmp[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kTopkThreads; off <<= 1) {
-    const int32_t a = tid >= off ? s_tmp[tid - off] : 0;
-    __syncthreads();
-    s_tmp[tid] += a;
-    __syncthreads();
+// exclusive prefix sum over the workgroup's 256 threads; *total = the sum
+__device__ __forceinline__ int32_t tk_scan(int32_t v, int32_t* s_w, int32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  const int32_t incl = s_tmp[tid];
-  if (total) *total = s_tmp[kTopkThreads - 1];
+  if (lane == 63) s_w[wave] = x;
   __syncthreads();
-  return incl - v;
+  int32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kTkThreads / 64; ++w) {
+    before += w < wave ? s_w[w] : 0;
+    all += s_w[w];
+  }
+  __syncthreads();
+  if (total) *total = all;
+  return before + x - v;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void esa_topk_kernel(
-    int mode, const float* __restrict__ upart, int nqsplit, const float* __restrict__ s_in,
-    const float* __restrict__ smax_part, int nsmax, float clip, int64_t n_mid, int radius, int topk,
-    int64_t mid0, float* __restrict__ u_tmp, uint32_t* __restrict__ keys, float* __restrict__ scores_out,
-    int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
-  __shared__ int32_t hist[2048];
-  __shared__ int32_t s_tmp[kTopkThreads];
-  __shared__ float s_red[kTopkThreads / 64];
-  __shared__ uint32_t s_prefix, s_mask;
-  __shared__ int32_t s_kk, s_total;
-  const int tid = threadIdx.x;
-  const int64_t bi = blockIdx.x;
-  int32_t* osel = sel + bi * topk;
-  const int64_t nsel = min((int64_t)topk, n_mid);
-  if (tid == 0) n_sel[bi] = (int32_t)nsel;
-  for (int64_t j = nsel + tid; j < topk; j += kTopkThreads) osel[j] = -1;
-  if (n_mid == 0) return;
+// Digits of the k-th largest key fixed by histogram passes [0, npass):
+// prefix/mask of the fixed bits and how many keys with that prefix are
+// still to be taken (1 <= need). Uniform over the workgroup.
+struct TkCut {
+  uint32_t prefix, mask;
+  int32_t need;
+};
 
-  // pass 0a: importance u
-  float* u = u_tmp + bi * n_mid;
-  if (mode == 0) {
-    for (int64_t j = tid; j < n_mid; j += kTopkThreads) {
-      double acc = 0.0;
-      for (int s = 0; s < nqsplit; ++s) acc += (double)upart[(bi * nqsplit + s) * n_mid + j];
-      u[j] = (float)acc;
-    }
-  } else {
-    float mx = -__builtin_inff();
-    for (int s = tid; s < nsmax; s += kTopkThreads) mx = fmaxf(mx, smax_part[bi * nsmax + s]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-    __syncthreads();
-    mx = s_red[0];
-    for (int w = 1; w < kTopkThreads / 64; ++w) mx = fmaxf(mx, s_red[w]);
-    for (int64_t j = tid; j < n_mid; j += kTopkThreads) u[j] = fmaxf(s_in[bi * n_mid + j] - mx, -clip);
-  }
-  __threadfence_block();
-  __syncthreads();
-  // pass 0b: neighbour max-pool, keys
-  uint32_t* kk_arr = keys + bi * n_mid;
-  for (int64_t j = tid; j < n_mid; j += kTopkThreads) {
-    float v = u[j];
-    const int64_t lo = max((int64_t)0, j - radius), hi = min(n_mid - 1, j + (int64_t)radius);
-    for (int64_t t = lo; t <= hi; ++t) v = fmaxf(v, u[t]);
-    kk_arr[j] = float_key(v);
-    if (scores_out) scores_out[bi * n_mid + j] = v;
-  }
-  __threadfence_block();
-  __syncthreads();
-
-  if (n_mid <= topk) {   // everything is selected
-    for (int64_t j = tid; j < n_mid; j += kTopkThreads) osel[j] = (int32_t)(mid0 + j);
-    return;
-  }
-  // radix select of the topk-th largest key
-  if (tid == 0) { s_prefix = 0; s_mask = 0; s_kk = topk; }
-  __syncthreads();
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass], nbins = 1 << widths[pass];
-    for (int i = tid; i < nbins; i += kTopkThreads) hist[i] = 0;
-    __syncthreads();
-    const uint32_t prefix = s_prefix, mask = s_mask;
-    for (int64_t j = tid; j < n_mid; j += kTopkThreads) {
-      const uint32_t key = kk_arr[j];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nbins - 1)], 1);
-    }
-    __syncthreads();
-    // suffix sums over bins (descending order): thread t owns bins
-    // nbins-1-2t and nbins-2-2t (two per thread for 2048 bins).
-    const int per = nbins / kTopkThreads;   // 2 or 1
+__device__ TkCut tk_cut(const int32_t* __restrict__ hist, int npass, int32_t k, int32_t* s_w, TkCut* s_cut) {
+  TkCut cut{0u, 0u, k};
+  for (int pass = 0; pass < npass; ++pass) {
+    const int nb = 1 << tk_bits(pass);
+    const int per = nb / kTkThreads;   // 8 or 4 bins per thread, descending
+    const int32_t* h = hist + pass * kTkBins;
+    int32_t c[8];
     int32_t local = 0;
-    for (int p = 0; p < per; ++p) local += hist[nbins - 1 - (tid * per + p)];
-    int32_t total;
-    const int32_t before = block_exclusive_scan(local, s_tmp, &total);
-    const int32_t need = s_kk;
-    int32_t acc = before;
-    for (int p = 0; p < per; ++p) {
-      const int bin = nbins - 1 - (tid * per + p);
-      const int32_t c = hist[bin];
-      if (acc < need && acc + c >= need) {
-        s_prefix = prefix | ((uint32_t)bin << shift);
-        s_mask = mask | ((uint32_t)(nbins - 1) << shift);
-        s_total = need - acc;   // still to take from this bin
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      c[p] = p < per ? h[nb - 1 - (threadIdx.x * per + p)] : 0;
+      local += c[p];
+    }
+    int32_t acc = tk_scan(local, s_w, nullptr);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      if (p < per && acc < cut.need && acc + c[p] >= cut.need) {
+        const int bin = nb - 1 - (threadIdx.x * per + p);
+        s_cut->prefix = cut.prefix | ((uint32_t)bin << tk_shift(pass));
+        s_cut->mask = cut.mask | ((uint32_t)(nb - 1) << tk_shift(pass));
+        s_cut->need = cut.need - acc;
       }
-      acc += c;
+      acc += c[p];
     }
     __syncthreads();
-    if (tid == 0) s_kk = s_total;
+    cut = *s_cut;
     __syncthreads();
   }
-  const uint32_t T = s_prefix;
-  const int32_t take_eq = s_kk;
-  // stable compaction: each thread owns a contiguous index range
-  const int64_t per = cdiv(n_mid, kTopkThreads);
-  const int64_t j0 = min(n_mid, (int64_t)tid * per), j1 = min(n_mid, j0 + per);
+  return cut;
+}
+
+__device__ __forceinline__ float tk_u(int mode, const float* __restrict__ upart, int nqsplit,
+                                      const float* __restrict__ s_in, float mx, float clip, int64_t bi,
+                                      int64_t n_mid, int64_t j) {
+  if (mode == 0) {
+    double acc = 0.0;
+    for (int sp = 0; sp < nqsplit; ++sp) acc += (double)upart[(bi * nqsplit + sp) * n_mid + j];
+    return (float)acc;
+  }
+  return fmaxf(s_in[bi * n_mid + j] - mx, -clip);
+}
+
+__global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
+    int mode, const float* __restrict__ upart, int nqsplit, const float* __restrict__ s_in,
+    const float* __restrict__ smax_part, int nsmax, float clip, int64_t n_mid, int radius,
+    uint32_t* __restrict__ keys, float* __restrict__ scores_out, int32_t* __restrict__ hist) {
+  __shared__ float s_u[kTkSlice + 2 * kTkMaxRadius];
+  __shared__ int32_t s_h[kTkBins];
+  __shared__ float s_red[kTkThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t bi = blockIdx.y;
+  const int64_t j0 = (int64_t)blockIdx.x * kTkSlice;
+  float mx = 0.f;
+  if (mode == 1) {   // max of the raw scores over M, from the scan's per-workgroup maxima
+    float m = -__builtin_inff();
+    for (int sp = tid; sp < nsmax; sp += kTkThreads) m = fmaxf(m, smax_part[bi * nsmax + sp]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((tid & 63) == 0) s_red[tid >> 6] = m;
+    __syncthreads();
+    mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  }
+  for (int i = tid; i < kTkBins; i += kTkThreads) s_h[i] = 0;
+  // u over [j0 - r, j0 + slice + r) clipped to M
+  const int64_t lo = max((int64_t)0, j0 - radius);
+  const int64_t hi = min(n_mid, j0 + kTkSlice + radius);
+  for (int64_t j = lo + tid; j < hi; j += kTkThreads)
+    s_u[j - j0 + radius] = tk_u(mode, upart, nqsplit, s_in, mx, clip, bi, n_mid, j);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kTkPer; ++e) {
+    const int64_t j = j0 + tid * kTkPer + e;
+    if (j >= n_mid) break;
+    float v = s_u[j - j0 + radius];
+    const int64_t a = max((int64_t)0, j - radius), b = min(n_mid - 1, j + (int64_t)radius);
+    for (int64_t t = a; t <= b; ++t) v = fmaxf(v, s_u[t - j0 + radius]);
+    const uint32_t key = float_key(v);
+    keys[bi * n_mid + j] = key;
+    if (scores_out) scores_out[bi * n_mid + j] = v;
+    atomicAdd(&s_h[key >> tk_shift(0)], 1);
+  }
+  __syncthreads();
+  int32_t* gh = hist + bi * 3 * kTkBins;
+  for (int i = tid; i < kTkBins; i += kTkThreads)
+    if (s_h[i]) atomicAdd(&gh[i], s_h[i]);
+}
+
+__global__ __launch_bounds__(kTkThreads) void esa_topk_hist_kernel(int pass, const uint32_t* __restrict__ keys,
+                                                                   int64_t n_mid, int topk,
+                                                                   int32_t* __restrict__ hist) {
+  __shared__ int32_t s_h[kTkBins];
+  __shared__ int32_t s_w[kTkThreads / 64];
+  __shared__ TkCut s_cut;
+  const int64_t bi = blockIdx.y;
+  int32_t* gh = hist + bi * 3 * kTkBins;
+  const TkCut cut = tk_cut(gh, pass, topk, s_w, &s_cut);
+  const int nb = 1 << tk_bits(pass);
+  for (int i = threadIdx.x; i < nb; i += kTkThreads) s_h[i] = 0;
+  __syncthreads();
+  const int64_t j0 = (int64_t)blockIdx.x * kTkSlice + threadIdx.x * kTkPer;
+#pragma unroll
+  for (int e = 0; e < kTkPer; ++e) {
+    const int64_t j = j0 + e;
+    if (j >= n_mid) break;
+    const uint32_t key = keys[bi * n_mid + j];
+    if ((key & cut.mask) == cut.prefix) atomicAdd(&s_h[(key >> tk_shift(pass)) & (nb - 1)], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nb; i += kTkThreads)
+    if (s_h[i]) atomicAdd(&gh[pass * kTkBins + i], s_h[i]);
+}
+
+// per slice: (#keys > T, #keys == T)
+__global__ __launch_bounds__(kTkThreads) void esa_topk_count_kernel(const uint32_t* __restrict__ keys,
+                                                                    int64_t n_mid, int topk,
+                                                                    const int32_t* __restrict__ hist,
+                                                                    int2* __restrict__ wgcnt) {
+  __shared__ int32_t s_w[kTkThreads / 64];
+  __shared__ TkCut s_cut;
+  const int64_t bi = blockIdx.y;
+  const TkCut cut = tk_cut(hist + bi * 3 * kTkBins, 3, topk, s_w, &s_cut);
+  const uint32_t T = cut.prefix;
+  const int64_t j0 = (int64_t)blockIdx.x * kTkSlice + threadIdx.x * kTkPer;
   int32_t gt = 0, eq = 0;
-  for (int64_t j = j0; j < j1; ++j) {
-    const uint32_t key = kk_arr[j];
+#pragma unroll
+  for (int e = 0; e < kTkPer; ++e) {
+    const int64_t j = j0 + e;
+    if (j >= n_mid) break;
+    const uint32_t key = keys[bi * n_mid + j];
     gt += key > T;
     eq += key == T;
   }
-  const int32_t eq_before = block_exclusive_scan(eq, s_tmp, nullptr);
-  const int32_t my_eq = max(0, min(eq, take_eq - eq_before));
-  const int32_t out_before = block_exclusive_scan(gt + my_eq, s_tmp, nullptr);
-  int32_t pos = out_before, eq_used = 0;
-  for (int64_t j = j0; j < j1; ++j) {
-    const uint32_t key = kk_arr[j];
-    bool take = key > T;
-    if (key == T && eq_used < my_eq) { take = true; ++eq_used; }
+  int32_t tgt, teq;
+  tk_scan(gt, s_w, &tgt);
+  tk_scan(eq, s_w, &teq);
+  if (threadIdx.x == 0) wgcnt[bi * gridDim.x + blockIdx.x] = make_int2(tgt, teq);
+}
+
+__global__ __launch_bounds__(kTkThreads) void esa_topk_emit_kernel(const uint32_t* __restrict__ keys,
+                                                                   int64_t n_mid, int topk, int64_t mid0,
+                                                                   const int32_t* __restrict__ hist,
+                                                                   const int2* __restrict__ wgcnt,
+                                                                   int32_t* __restrict__ sel,
+                                                                   int32_t* __restrict__ n_sel) {
+  __shared__ int32_t s_w[kTkThreads / 64];
+  __shared__ TkCut s_cut;
+  const int64_t bi = blockIdx.y;
+  const int nwg = gridDim.x;
+  int32_t* osel = sel + bi * topk;
+  const int64_t nsel = min((int64_t)topk, n_mid);
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0) n_sel[bi] = (int32_t)nsel;
+    for (int64_t j = nsel + threadIdx.x; j < topk; j += kTkThreads) osel[j] = -1;
+  }
+  const int64_t j0 = (int64_t)blockIdx.x * kTkSlice + threadIdx.x * kTkPer;
+  if (n_mid <= topk) {   // every candidate is selected
+#pragma unroll
+    for (int e = 0; e < kTkPer; ++e)
+      if (j0 + e < n_mid) osel[j0 + e] = (int32_t)(mid0 + j0 + e);
+    return;
+  }
+  const TkCut cut = tk_cut(hist + bi * 3 * kTkBins, 3, topk, s_w, &s_cut);
+  const uint32_t T = cut.prefix;
+  const int32_t take_eq = cut.need;   // keys equal to T to take, lowest positions first
+  // slices before this one: keys taken and keys equal to T seen
+  int32_t out_before = 0, eq_before = 0;
+  for (int w = threadIdx.x; w < (int)blockIdx.x; w += kTkThreads) {
+    const int2 c = wgcnt[bi * nwg + w];
+    eq_before += c.y;
+    out_before += c.x;
+  }
+  int32_t eq_sum, gt_sum;
+  tk_scan(eq_before, s_w, &eq_sum);
+  tk_scan(out_before, s_w, &gt_sum);
+  // equal keys taken before this slice = min(eq_sum, take_eq)
+  const int32_t base = gt_sum + min(eq_sum, take_eq);
+  int32_t gt = 0, eq = 0;
+  uint32_t kv[kTkPer];
+#pragma unroll
+  for (int e = 0; e < kTkPer; ++e) {
+    const int64_t j = j0 + e;
+    kv[e] = j < n_mid ? keys[bi * n_mid + j] : 0u;
+    if (j < n_mid) {
+      gt += kv[e] > T;
+      eq += kv[e] == T;
+    }
+  }
+  const int32_t eq_local = tk_scan(eq, s_w, nullptr);
+  const int32_t eq_avail = max(0, take_eq - eq_sum - eq_local);   // equal keys this thread may still take
+  const int32_t my_eq = min(eq, eq_avail);
+  int32_t pos = base + tk_scan(gt + my_eq, s_w, nullptr);
+  int32_t used = 0;
+#pragma unroll
+  for (int e = 0; e < kTkPer; ++e) {
+    const int64_t j = j0 + e;
+    if (j >= n_mid) break;
+    bool take = kv[e] > T;
+    if (kv[e] == T && used < my_eq) {
+      take = true;
+      ++used;
+    }
     if (take) osel[pos++] = (int32_t)(mid0 + j);
   }
 }
@@ -403,12 +522,32 @@ hipError_t launch_esa_decode_scan(const float* qc, const bf16* kc, int64_t batch
   return hipGetLastError();
 }
 
+int esa_topk_slices(int64_t n_mid) { return (int)std::max<int64_t>(1, cdiv(n_mid, kTkSlice)); }
+int esa_topk_max_radius() { return kTkMaxRadius; }
+
 hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const float* s_in, const float* smax_part,
                            int nsmax, float clip, int64_t batch, int64_t n_mid, int radius, int topk, int64_t mid0,
-                           float* u_tmp, uint32_t* keys, float* scores_out, int32_t* sel, int32_t* n_sel,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(esa_topk_kernel, dim3((unsigned)batch), dim3(kTopkThreads), 0, s, mode, upart, nqsplit, s_in,
-                     smax_part, nsmax, clip, n_mid, radius, topk, mid0, u_tmp, keys, scores_out, sel, n_sel);
+                           int32_t* hist, int2* wgcnt, uint32_t* keys, float* scores_out, int32_t* sel,
+                           int32_t* n_sel, hipStream_t s) {
+  const int nwg = esa_topk_slices(n_mid);
+  const dim3 grid((unsigned)nwg, (unsigned)batch);
+  hipError_t e;
+  if (n_mid > 0) {
+    if ((e = launch_fill_i32(hist, batch * 3 * kTkBins, 0, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(esa_topk_prep_kernel, grid, dim3(kTkThreads), 0, s, mode, upart, nqsplit, s_in, smax_part,
+                       nsmax, clip, n_mid, radius, keys, scores_out, hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (n_mid > topk) {
+      for (int pass = 1; pass < 3; ++pass) {
+        hipLaunchKernelGGL(esa_topk_hist_kernel, grid, dim3(kTkThreads), 0, s, pass, keys, n_mid, topk, hist);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(esa_topk_count_kernel, grid, dim3(kTkThreads), 0, s, keys, n_mid, topk, hist, wgcnt);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL(esa_topk_emit_kernel, grid, dim3(kTkThreads), 0, s, keys, n_mid, topk, mid0, hist, wgcnt,
+                     sel, n_sel);
   return hipGetLastError();
 }
 

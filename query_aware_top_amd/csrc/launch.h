@@ -62,10 +62,13 @@ hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const b
                                      float* rowmax_part, float* rowmax, float* upart, hipStream_t s);
 hipError_t launch_esa_decode_scan(const float* qc, const bf16* kc, int64_t batch, int64_t ctx_len, int64_t mid0,
                                   int64_t n_mid, int64_t d_c, float* s_out, float* smax_part, hipStream_t s);
+int esa_topk_slices(int64_t n_mid);
+int esa_topk_max_radius();
+// hist: batch*3*2048 int32, wgcnt: batch*esa_topk_slices(n_mid) int2 (scratch)
 hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const float* s_in, const float* smax_part,
                            int nsmax, float clip, int64_t batch, int64_t n_mid, int radius, int topk, int64_t mid0,
-                           float* u_tmp, uint32_t* keys, float* scores_out, int32_t* sel, int32_t* n_sel,
-                           hipStream_t s);
+                           int32_t* hist, int2* wgcnt, uint32_t* keys, float* scores_out, int32_t* sel,
+                           int32_t* n_sel, hipStream_t s);
 
 // ---- ESA attention (esa_attn.hip) -----------------------------------------
 int esa_decode_splits(int64_t n_init, int64_t topk, int64_t window);
