@@ -107,7 +107,8 @@ int esa_workspace_size(const qat_esa_params* p, size_t* bytes);
  * Compression by the one-layer map of [ESA] (paragraph on compressing q and
  * k to about 3.2% with a one-layer MLP; read as one affine map):
  *   out[i, :] = round(W x[i, :] + bias)
- * x: n rows of d_model elements (in_dtype), row i at x + i*x_stride elements.
+ * x: n rows of d_model elements (in_dtype), row i at x + i*x_stride elements;
+ * x and W 16-byte aligned, x_stride a multiple of 8 (QAT_EINVAL otherwise).
  * W: [d_c, d_model] (in_dtype), bias: [d_c] float32 or NULL.
  * out: row i at out + i*out_stride elements, out_dtype QAT_F32 or QAT_BF16.
  * Accumulation is float64, rounded once (nearest even) to out_dtype, so the

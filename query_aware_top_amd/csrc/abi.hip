@@ -306,6 +306,8 @@ QAT_EXPORT int esa_compress(const void* x, int64_t n, int64_t x_stride, int64_t 
   if (n < 1 || d_model < 32 || d_model % 32) return fail(QAT_EINVAL, "n >= 1 and d_model a multiple of 32 required");
   if (!pow2_dc(d_c)) return fail(QAT_EUNSUPPORTED, "d_c %lld not supported", (long long)d_c);
   if (x_stride < d_model || out_stride < d_c) return fail(QAT_EINVAL, "row strides shorter than the rows");
+  if (x_stride % 8 || ((uintptr_t)x | (uintptr_t)W) % 16)
+    return fail(QAT_EINVAL, "x and W must be 16-byte aligned and x_stride a multiple of 8 elements");
   if ((in_dtype != QAT_F32 && in_dtype != QAT_BF16) || (out_dtype != QAT_F32 && out_dtype != QAT_BF16))
     return fail(QAT_EINVAL, "unknown dtype");
   size_t need = 0;
@@ -329,6 +331,8 @@ QAT_EXPORT int esa_select(const qat_esa_params* p, const void* q, const void* Wq
   int rc = esa_check(p);
   if (rc) return rc;
   if (!q || !Wq || !kc_cache || !sel || !n_sel) return fail(QAT_EINVAL, "q, Wq, kc_cache, sel, n_sel must be non-NULL");
+  if (((uintptr_t)q | (uintptr_t)Wq | (uintptr_t)kc_cache) % 16)
+    return fail(QAT_EINVAL, "q, Wq and kc_cache must be 16-byte aligned");
   EsaLayout L = esa_layout(p, nullptr);
   if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
   L = esa_layout(p, ws);

@@ -12,45 +12,92 @@
 
 namespace qat {
 
-// One wave: 16 rows x 16 output columns over k in [k0, k1). The fp64 MFMA
-// 16x16x4 takes A[row = lane%16][k = lane/16], B[k = lane/16][col =
-// lane%16] and returns D[row = lane/16 + 4i][col = lane%16]. Each lane
-// loads 8 consecutive k of its row (and of its W row) per step; step s of 8
-// pairs k-slot j with k = kb + 8 j + s on both operands.
+// The fp64 MFMA 16x16x4 takes A[row = lane%16][k-slot = lane/16],
+// B[k-slot = lane/16][col = lane%16] and returns D[row = lane/16 + 4i][col =
+// lane%16]. Any assignment of k to the four slots works if both operands use
+// it: lane slot j takes k = kb + 8 j + s at step s of a 32-k chunk, so each
+// lane reads 8 consecutive k of its x row and of each W row with one 16-byte
+// load. A wave owns 16 rows x 64 columns (four accumulators sharing the x
+// operand); a workgroup stacks 4 waves over 64 rows. The next chunk's loads
+// are issued before the current chunk's 32 matrix ops.
+constexpr int kCmpRows = 64;
+constexpr int kCmpCols = 64;
+
+template <typename T>
+struct Raw8;   // 8 consecutive elements as loaded
+template <>
+struct Raw8<bf16> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *(const u32x4*)p; }
+  __device__ __forceinline__ double get(int s) const {
+    const uint32_t w = v[s >> 1];
+    return (double)__builtin_bit_cast(float, (s & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *(const f32x4*)p;
+    b = *(const f32x4*)(p + 4);
+  }
+  __device__ __forceinline__ double get(int s) const { return (double)(s < 4 ? a[s] : b[s - 4]); }
+};
+
 template <typename TX, typename TW>
 __global__ __launch_bounds__(256) void compress_partial_kernel(
     const TX* __restrict__ x, int64_t n, int64_t x_stride, int64_t d_model,
     const TW* __restrict__ W, int64_t d_c, int64_t k_per_split, double* __restrict__ partial) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t row0 = (int64_t)blockIdx.x * 16;
-  const int64_t col0 = ((int64_t)blockIdx.y * 4 + wave) * 16;
-  if (col0 >= d_c) return;
+  const int64_t row0 = (int64_t)blockIdx.x * kCmpRows + wave * 16;
+  const int64_t col0 = (int64_t)blockIdx.y * kCmpCols;
   const int split = blockIdx.z;
   const int64_t k0 = (int64_t)split * k_per_split;
   const int64_t k1 = min(d_model, k0 + k_per_split);
   const int r = lane & 15, j = lane >> 4;
   const int64_t row = row0 + r;
-  const bool row_ok = row < n;
-  const TX* xr = x + (row_ok ? row : 0) * x_stride;
-  const TW* wr = W + (col0 + r) * d_model;
-  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-  for (int64_t kb = k0; kb < k1; kb += 32) {
-    const int64_t kk = kb + 8 * j;
-    double a[8], b[8];
+  const TX* xr = x + (row < n ? row : 0) * x_stride + 8 * j;
+  const int ncb = (int)min((int64_t)4, (d_c - col0) / 16);   // column blocks of 16 in range
+  const TW* wr[4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      a[s] = row_ok ? (double)to_f32(xr[kk + s]) : 0.0;
-      b[s] = (double)to_f32(wr[kk + s]);
+  for (int cb = 0; cb < 4; ++cb) wr[cb] = W + (col0 + 16 * min(cb, ncb - 1) + r) * d_model + 8 * j;
+  f64x4 acc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = f64x4{0.0, 0.0, 0.0, 0.0};
+  Raw8<TX> xa;
+  Raw8<TW> wa[4];
+  if (k0 < k1) {
+    xa.load(xr + k0);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) wa[cb].load(wr[cb] + k0);
+  }
+  for (int64_t kb = k0; kb < k1; kb += 32) {
+    const Raw8<TX> xc = xa;
+    Raw8<TW> wc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) wc[cb] = wa[cb];
+    if (kb + 32 < k1) {
+      xa.load(xr + kb + 32);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) wa[cb].load(wr[cb] + kb + 32);
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc, 0, 0, 0);
+    for (int st = 0; st < 8; ++st) {
+      const double av = row < n ? xc.get(st) : 0.0;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, wc[cb].get(st), acc[cb], 0, 0, 0);
+    }
   }
   double* dst = partial + (int64_t)split * n * d_c;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t orow = row0 + j + 4 * i;
-    if (orow < n) dst[orow * d_c + col0 + r] = acc[i];
+  for (int cb = 0; cb < 4; ++cb) {
+    if (cb >= ncb) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t orow = row0 + j + 4 * i;
+      if (orow < n) dst[orow * d_c + col0 + 16 * cb + r] = acc[cb][i];
+    }
   }
 }
 
@@ -81,9 +128,10 @@ __global__ void compress_finalize_kernel(const double* __restrict__ partial, int
 }
 
 int compress_splits(int64_t n, int64_t d_model, int64_t d_c) {
-  const int64_t waves = cdiv(n, 16) * cdiv(d_c, 16);
-  int64_t ns = cdiv(2048, waves);
-  const int64_t max_ns = d_model / 256 > 0 ? d_model / 256 : 1;
+  // about 4096 waves, chunks of at least 64 k
+  const int64_t waves = cdiv(n, 16) * cdiv(d_c, kCmpCols);
+  int64_t ns = cdiv(4096, waves);
+  const int64_t max_ns = d_model / 64 > 0 ? d_model / 64 : 1;
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
   return (int)ns;
@@ -93,7 +141,7 @@ hipError_t launch_compress_partial(const void* x, int64_t n, int64_t x_stride, i
                                    bool x_bf16, const void* W, bool w_bf16, int64_t d_c, int nsplit,
                                    double* partial, hipStream_t s) {
   const int64_t k_per_split = cdiv(d_model / 32, nsplit) * 32;
-  dim3 grid((unsigned)cdiv(n, 16), (unsigned)cdiv(d_c, 64), (unsigned)nsplit);
+  dim3 grid((unsigned)cdiv(n, kCmpRows), (unsigned)cdiv(d_c, kCmpCols), (unsigned)nsplit);
   if (x_bf16 && w_bf16)
     hipLaunchKernelGGL((compress_partial_kernel<bf16, bf16>), grid, dim3(256), 0, s, (const bf16*)x, n,
                        x_stride, d_model, (const bf16*)W, d_c, k_per_split, partial);

@@ -20,24 +20,44 @@
 // keys with the lowest index winning ties.
 #include <algorithm>
 
+#include "attn_core.h"
 #include "common.h"
 #include "launch.h"
 
 namespace qat {
 
 // ---------------------------------------------------------------------------
-// Prefill pass 1: partial row maxima. grid (query tiles of 128, key splits,
-// batch); a wave owns 32 queries and computes S^T = K~ Q~^T so each lane
-// holds one query and 16 key scores per 32-key subtile.
+// Prefill scoring. Both passes stream 64-row tiles of one operand through LDS
+// (direct global->LDS loads, double-buffered, one barrier per tile, the next
+// tile's loads in flight during the current tile's matrix ops) and hold the
+// other operand in registers; rows are stored with the attention engine's
+// chunk swizzle so the A-operand reads are bank-conflict free.
+constexpr int kScWaves = 4;
+constexpr int kScRows = 32 * kScWaves;   // register-held rows per workgroup
+
+// A operand (32 rows x 16 k) of sub-tile sb, k-step c, from a swizzled tile
 template <int DC>
-__global__ __launch_bounds__(256) void esa_rowmax_kernel(
+__device__ __forceinline__ bf16x8 sc_a(const bf16* tile, int sb, int c) {
+  const int lane = threadIdx.x & 63;
+  const int r = sb * 32 + (lane & 31);
+  const int ch = (2 * c + (lane >> 5)) ^ fa_swz<DC>(r);
+  return *(const bf16x8*)(tile + r * DC + ch * 8);
+}
+
+// Pass 1: partial row maxima. grid (query tiles of 128, key splits, batch);
+// S^T = K~ Q~^T with Q~ = hi + lo in registers, so each lane holds one query
+// and 16 key scores per 32-key sub-tile.
+template <int DC>
+__global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
     const bf16* __restrict__ q_hi, const bf16* __restrict__ q_lo, const bf16* __restrict__ kc,
     int64_t m, int64_t ctx_len, int64_t mid0, int64_t n_mid, int64_t keys_per_split, int nsplit,
     float* __restrict__ rowmax_part) {
+  __shared__ __align__(16) bf16 kt0[kKT * DC];
+  __shared__ __align__(16) bf16 kt1[kKT * DC];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, r32 = lane & 31;
   const int64_t bi = blockIdx.z;
-  const int64_t qi = (int64_t)blockIdx.x * 128 + wave * 32 + r32;
+  const int64_t qi = (int64_t)blockIdx.x * kScRows + wave * 32 + r32;
   const bool qvalid = qi < m;
   const int64_t qrow = bi * m + (qvalid ? qi : 0);
   bf16x8 qh[DC / 16], ql[DC / 16];
@@ -47,28 +67,38 @@ __global__ __launch_bounds__(256) void esa_rowmax_kernel(
     ql[c] = *(const bf16x8*)(q_lo + qrow * DC + 16 * c + 8 * h);
   }
   const int64_t k0 = (int64_t)blockIdx.y * keys_per_split;
-  const int64_t k1 = min(n_mid, k0 + keys_per_split);
-  const bf16* kbase = kc + (bi * ctx_len + mid0) * DC;
+  const int n = (int)(min(n_mid, k0 + keys_per_split) - k0);
+  const bf16* kbase = kc + (bi * ctx_len + mid0 + k0) * DC;
+  auto row_ofs = [](int j) { return j * DC; };
+  const int nt = (n + kKT - 1) / kKT;
   float mx = -__builtin_inff();
-  for (int64_t kb = k0; kb < k1; kb += 32) {
-    const int64_t key = kb + r32;
-    const bf16* kr = kbase + (key < k1 ? key : k0) * DC;
-    f32x16 acc;
+  fa_issue_one<DC, kScWaves>(kt0, kbase, 0, n, row_ofs);
+  for (int t = 0; t < nt; ++t) {
+    fa_wait_loads();
+    __syncthreads();
+    if (t + 1 < nt) fa_issue_one<DC, kScWaves>((t & 1) ? kt0 : kt1, kbase, (t + 1) * kKT, n, row_ofs);
+    const bf16* tile = (t & 1) ? kt1 : kt0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 acc = {};
 #pragma unroll
-    for (int c = 0; c < DC / 16; ++c) {
-      const bf16x8 a = *(const bf16x8*)(kr + 16 * c + 8 * h);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[c], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[c], acc, 0, 0, 0);
-    }
+      for (int c = 0; c < DC / 16; ++c) {
+        const bf16x8 a = sc_a<DC>(tile, sb, c);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[c], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[c], acc, 0, 0, 0);
+      }
+      const int base = t * kKT + sb * 32;
+      if (base + 32 <= n) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t kk = kb + (i >> 2) * 8 + h * 4 + (i & 3);
-      if (kk < k1) mx = fmaxf(mx, acc[i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (base + (i >> 2) * 8 + h * 4 + (i & 3) < n) mx = fmaxf(mx, acc[i]);
+      }
     }
   }
-  mx = fmaxf(mx, shfl_xor_f(mx, 32));
+  mx = xor32_max(mx);
   if (qvalid && h == 0) rowmax_part[(bi * m + qi) * nsplit + blockIdx.y] = mx;
 }
 
@@ -81,48 +111,76 @@ __global__ void esa_rowmax_final_kernel(const float* __restrict__ part, int nspl
   rowmax[i] = mx;
 }
 
-// Prefill pass 2: partial importance. grid (key tiles of 128, query splits,
-// batch); a wave owns 32 keys and computes S = Q~ K~^T so each lane holds one
-// key and 16 query rows per 32-query subtile; corrected scores are summed in
-// float32 per subtile and in float64 across subtiles (fixed order).
+// Pass 2: partial importance. grid (key tiles of 128, query splits, batch);
+// S = Q~ K~^T with the keys in registers, so each lane holds one key and 16
+// query rows per 32-query sub-tile; the corrected scores are summed in
+// float32 per sub-tile and in float64 across sub-tiles (fixed order).
 template <int DC>
-__global__ __launch_bounds__(256) void esa_colsum_kernel(
+__global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
     const bf16* __restrict__ q_hi, const bf16* __restrict__ q_lo, const float* __restrict__ rowmax,
     const bf16* __restrict__ kc, int64_t m, int64_t ctx_len, int64_t mid0, int64_t n_mid,
     int64_t rows_per_split, int nqsplit, float clip, float* __restrict__ upart) {
+  __shared__ __align__(16) bf16 qh0[kKT * DC];
+  __shared__ __align__(16) bf16 qh1[kKT * DC];
+  __shared__ __align__(16) bf16 ql0[kKT * DC];
+  __shared__ __align__(16) bf16 ql1[kKT * DC];
+  __shared__ __align__(16) float rm0[kKT];
+  __shared__ __align__(16) float rm1[kKT];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, r32 = lane & 31;
   const int64_t bi = blockIdx.z;
-  const int64_t key = (int64_t)blockIdx.x * 128 + wave * 32 + r32;
+  const int64_t key = (int64_t)blockIdx.x * kScRows + wave * 32 + r32;
   const bool kvalid = key < n_mid;
   const bf16* kr = kc + (bi * ctx_len + mid0 + (kvalid ? key : 0)) * DC;
   bf16x8 kf[DC / 16];
 #pragma unroll
   for (int c = 0; c < DC / 16; ++c) kf[c] = *(const bf16x8*)(kr + 16 * c + 8 * h);
   const int64_t i0 = (int64_t)blockIdx.y * rows_per_split;
-  const int64_t i1 = min(m, i0 + rows_per_split);
-  const float* rm = rowmax + bi * m;
+  const int n = (int)(min(m, i0 + rows_per_split) - i0);
+  const bf16* hb = q_hi + (bi * m + i0) * DC;
+  const bf16* lb = q_lo + (bi * m + i0) * DC;
+  const float* rb = rowmax + bi * m + i0;
+  auto row_ofs = [](int j) { return j * DC; };
+  auto issue = [&](int t) {
+    const int j0 = t * kKT;
+    fa_issue_one<DC, kScWaves>((t & 1) ? qh1 : qh0, hb, j0, n, row_ofs);
+    fa_issue_one<DC, kScWaves>((t & 1) ? ql1 : ql0, lb, j0, n, row_ofs);
+    if (wave == 0) {
+      const int j = min(j0 + lane, n - 1);
+      __builtin_amdgcn_global_load_lds((const global_void*)(rb + j), (lds_void*)((t & 1) ? rm1 : rm0), 4, 0, 0);
+    }
+  };
+  const int nt = (n + kKT - 1) / kKT;
   double total = 0.0;
-  for (int64_t ib = i0; ib < i1; ib += 32) {
-    const int64_t qi = ib + r32;
-    const int64_t qrow = bi * m + (qi < i1 ? qi : i0);
-    f32x16 acc;
+  issue(0);
+  for (int t = 0; t < nt; ++t) {
+    fa_wait_loads();
+    __syncthreads();
+    if (t + 1 < nt) issue(t + 1);
+    const bf16* th = (t & 1) ? qh1 : qh0;
+    const bf16* tl = (t & 1) ? ql1 : ql0;
+    const float* trm = (t & 1) ? rm1 : rm0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 acc = {};
 #pragma unroll
-    for (int c = 0; c < DC / 16; ++c) {
-      const bf16x8 ah = *(const bf16x8*)(q_hi + qrow * DC + 16 * c + 8 * h);
-      const bf16x8 al = *(const bf16x8*)(q_lo + qrow * DC + 16 * c + 8 * h);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, kf[c], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, kf[c], acc, 0, 0, 0);
+      for (int c = 0; c < DC / 16; ++c) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sc_a<DC>(th, sb, c), kf[c], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sc_a<DC>(tl, sb, c), kf[c], acc, 0, 0, 0);
+      }
+      const int base = t * kKT + sb * 32;
+      float part = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 r4 = *(const f32x4*)(trm + sb * 32 + g * 8 + h * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = fmaxf(acc[4 * g + e] - r4[e], -clip);
+          part += (base + g * 8 + h * 4 + e < n) ? v : 0.f;
+        }
+      }
+      total += (double)part;
     }
-    float part = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t qq = ib + (i >> 2) * 8 + h * 4 + (i & 3);
-      if (qq < i1) part += fmaxf(acc[i] - rm[qq], -clip);
-    }
-    total += (double)part;
   }
   total += __shfl_xor(total, 32, 64);
   if (kvalid && h == 0) upart[(bi * nqsplit + blockIdx.y) * n_mid + key] = (float)total;
@@ -430,17 +488,18 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_emit_kernel(const uint32_
 }
 
 // ---------------------------------------------------------------------------
+// about 1024 workgroups per pass; splits hold whole 64-row tiles
 int esa_key_splits(int64_t n_mid, int64_t m) {
-  const int64_t qt = cdiv(m, 128);
+  const int64_t qt = cdiv(m, kScRows);
   int64_t ks = cdiv(1024, qt);
-  const int64_t max_ks = cdiv(n_mid, 256);
+  const int64_t max_ks = cdiv(n_mid, 4 * kKT);
   if (ks > max_ks) ks = max_ks;
   return (int)(ks < 1 ? 1 : ks);
 }
 int esa_query_splits(int64_t n_mid, int64_t m) {
-  const int64_t kt = cdiv(n_mid, 128);
+  const int64_t kt = cdiv(n_mid, kScRows);
   int64_t qs = cdiv(1024, kt);
-  const int64_t max_qs = cdiv(m, 256);
+  const int64_t max_qs = cdiv(m, 4 * kKT);
   if (qs > max_qs) qs = max_qs;
   return (int)(qs < 1 ? 1 : qs);
 }
@@ -454,20 +513,16 @@ hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const b
                                      float* rowmax_part, float* rowmax, float* upart, hipStream_t s) {
   if (n_mid <= 0) return hipSuccess;
   const int ks = esa_key_splits(n_mid, m);
-  const int64_t kps = cdiv(cdiv(n_mid, ks), 32) * 32;
+  const int64_t kps = cdiv(cdiv(n_mid, ks), kKT) * kKT;
   const int ks_eff = (int)cdiv(n_mid, kps);
-  dim3 g1((unsigned)cdiv(m, 128), (unsigned)ks_eff, (unsigned)batch);
-#define QAT_RM(DC_)                                                                                  \
-  hipLaunchKernelGGL(esa_rowmax_kernel<DC_>, g1, dim3(256), 0, s, q_hi, q_lo, kc, m, ctx_len, mid0, \
+  dim3 g1((unsigned)cdiv(m, kScRows), (unsigned)ks_eff, (unsigned)batch);
+#define QAT_RM(DC_)                                                                                       \
+  hipLaunchKernelGGL(esa_rowmax_kernel<DC_>, g1, dim3(64 * kScWaves), 0, s, q_hi, q_lo, kc, m, ctx_len, mid0, \
                      n_mid, kps, ks_eff, rowmax_part)
   switch (d_c) {
     case 32: QAT_RM(32); break;
     case 64: QAT_RM(64); break;
-    case 96: QAT_RM(96); break;
     case 128: QAT_RM(128); break;
-    case 160: QAT_RM(160); break;
-    case 192: QAT_RM(192); break;
-    case 224: QAT_RM(224); break;
     default: QAT_RM(256); break;
   }
 #undef QAT_RM
@@ -477,20 +532,16 @@ hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const b
                      rowmax_part, ks_eff, batch * m, rowmax);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int qs = esa_query_splits(n_mid, m);
-  const int64_t rps = cdiv(cdiv(m, qs), 32) * 32;
+  const int64_t rps = cdiv(cdiv(m, qs), kKT) * kKT;
   const int qs_eff = (int)cdiv(m, rps);
-  dim3 g2((unsigned)cdiv(n_mid, 128), (unsigned)qs_eff, (unsigned)batch);
-#define QAT_CS(DC_)                                                                                       \
-  hipLaunchKernelGGL(esa_colsum_kernel<DC_>, g2, dim3(256), 0, s, q_hi, q_lo, rowmax, kc, m, ctx_len, mid0, \
-                     n_mid, rps, qs_eff, clip, upart)
+  dim3 g2((unsigned)cdiv(n_mid, kScRows), (unsigned)qs_eff, (unsigned)batch);
+#define QAT_CS(DC_)                                                                                      \
+  hipLaunchKernelGGL(esa_colsum_kernel<DC_>, g2, dim3(64 * kScWaves), 0, s, q_hi, q_lo, rowmax, kc, m,     \
+                     ctx_len, mid0, n_mid, rps, qs_eff, clip, upart)
   switch (d_c) {
     case 32: QAT_CS(32); break;
     case 64: QAT_CS(64); break;
-    case 96: QAT_CS(96); break;
     case 128: QAT_CS(128); break;
-    case 160: QAT_CS(160); break;
-    case 192: QAT_CS(192); break;
-    case 224: QAT_CS(224); break;
     default: QAT_CS(256); break;
   }
 #undef QAT_CS
@@ -499,7 +550,7 @@ hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const b
 
 int esa_prefill_qsplits_eff(int64_t n_mid, int64_t m) {
   const int qs = esa_query_splits(n_mid, m);
-  const int64_t rps = cdiv(cdiv(m, qs), 32) * 32;
+  const int64_t rps = cdiv(cdiv(m, qs), kKT) * kKT;
   return (int)cdiv(m, rps);
 }
 
