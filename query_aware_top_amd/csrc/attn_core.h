@@ -116,7 +116,7 @@ __device__ __forceinline__ void fa_init(FaState<D>& st, const bf16* qrow, bool v
 // j's element offset from src (32-bit: one sequence's K or V holds fewer
 // than 2^31 elements); rows at or beyond n are clamped to row n - 1 (a valid
 // row whose scores the caller masks).
-template <int D, int NW, typename RowOfs>
+template <int D, int NW, typename RowOfs, bool CLAMP = true>
 __device__ __forceinline__ void fa_issue_one(bf16* __restrict__ dst, const bf16* __restrict__ src, int j0, int n,
                                              RowOfs row_ofs) {
   constexpr int CPR = D / 8;          // 16-byte chunks per row
@@ -131,9 +131,49 @@ __device__ __forceinline__ void fa_issue_one(bf16* __restrict__ dst, const bf16*
     const int r = r0 + lane / CPR;
     const int c = (lane % CPR) ^ fa_swz<D>(r);
     const int j = j0 + r;
-    const int off = row_ofs(j < n ? j : n - 1) + c * 8;
+    const int off = row_ofs(CLAMP ? (j < n ? j : n - 1) : j) + c * 8;
     __builtin_amdgcn_global_load_lds((const global_void*)(src + off), (lds_void*)(dst + r0 * D), 16, 0, 0);
   }
+}
+
+// Contiguous rows at a fixed element stride, whole tiles, through a buffer
+// resource: the lane's byte offset inside a tile (row times stride plus its
+// swizzled 16-byte chunk) is fixed, the tile's start goes in the scalar
+// offset, so a load costs no vector instruction and no 64-bit address
+// registers. The resource's record count bounds every access to the region
+// it describes (out-of-range reads return zero).
+constexpr uint32_t kBufWord3 = 0x00020000u;   // raw buffer, gfx9-family format
+
+template <int D, int NW>
+struct FaContig {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int RPW = kKT / NW;
+  static constexpr int NI = RPW / RPI;   // load instructions per wave per tile
+  int off[NI];                           // bytes
+  __device__ __forceinline__ void init(int stride) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = RPW * wave + i * RPI + lane / CPR;
+      off[i] = (r * stride + ((lane % CPR) ^ fa_swz<D>(r)) * 8) * 2;
+    }
+  }
+  // rows [j0, j0 + 64) of the region (row j at j * stride elements) into dst
+  __device__ __forceinline__ void issue(bf16* __restrict__ dst, __amdgpu_buffer_rsrc_t rsrc, int j0,
+                                        int stride) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int soff = __builtin_amdgcn_readfirstlane(j0 * stride * 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (RPW * wave + i * RPI) * D), 16, off[i],
+                                               soff, 0, 0);
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t fa_rsrc(const bf16* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, (int)kBufWord3);
 }
 
 __device__ __forceinline__ void fa_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -203,11 +243,15 @@ __device__ __forceinline__ void fa_scores(const FaState<D>& st, const bf16* __re
   for (int c = 0; c < D / 16; ++c)
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[sb][c], st.q[c], s[sb], 0, 0, 0);
-  // K reads run one half-tile ahead of the matrix ops that use them
-  __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 3 * (D / 32), 0);
+  // K reads run two k-steps ahead of the matrix ops that use them (at most
+  // six fragments live, which keeps the register budget for two waves/SIMD)
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int c = 0; c < D / 16 - 2; ++c) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 // O^T += V^T P^T for one 64-key tile in LDS.
@@ -375,6 +419,41 @@ __device__ __forceinline__ void fa_rows_to_lds(FaState<D>& st, const FaSmem<D>& 
       for (int e = 0; e < 4; ++e) w[e] = st.o[t][i4 * 4 + e] * mul;
       const int q = 8 * t + 2 * i4 + h;
       *(f32x4*)(dst + 4 * (q ^ (row & 31) & (D / 4 - 1))) = w;
+    }
+}
+
+// Partner value across the two half-waves (lane l <-> l ^ 32): the swap
+// returns the own and the partner value in some order, so xor-ing both with
+// the own value leaves the partner's.
+__device__ __forceinline__ uint32_t xchg32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return r[0] ^ r[1] ^ x;
+}
+
+// Stores the lane's query row of O (times mul) as bf16 at dst, straight from
+// the accumulators: the two half-waves trade 4-element groups so that each
+// lane writes whole 16-byte pieces (D/16 stores per lane, no LDS).
+template <int D>
+__device__ __forceinline__ void fa_store_row_bf16(const FaState<D>& st, float mul, bf16* dst, bool ok) {
+  const int h = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      // elements 8p..8p+3: d = 32t + 16p + 4h + 0..3; 8p+4..8p+7: d + 8
+      const uint32_t a0 = pack_bf16x2(st.o[t][8 * p + 0] * mul, st.o[t][8 * p + 1] * mul);
+      const uint32_t a1 = pack_bf16x2(st.o[t][8 * p + 2] * mul, st.o[t][8 * p + 3] * mul);
+      const uint32_t b0 = pack_bf16x2(st.o[t][8 * p + 4] * mul, st.o[t][8 * p + 5] * mul);
+      const uint32_t b1 = pack_bf16x2(st.o[t][8 * p + 6] * mul, st.o[t][8 * p + 7] * mul);
+      // lower half keeps d 16p+0..3 and takes the partner's 4..7; upper half
+      // keeps 12..15 and takes the partner's 8..11
+      const uint32_t r0 = xchg32(h ? a0 : b0), r1 = xchg32(h ? a1 : b1);
+      u32x4 w;
+      w[0] = h ? r0 : a0;
+      w[1] = h ? r1 : a1;
+      w[2] = h ? b0 : r0;
+      w[3] = h ? b1 : r1;
+      if (ok) *(u32x4*)(dst + 32 * t + 16 * p + 8 * h) = w;
     }
 }
 

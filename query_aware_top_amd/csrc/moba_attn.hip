@@ -13,6 +13,8 @@
 // (no mask) and leaves a normalised partial (o, lse) in its slot. The
 // current-block kernel then runs causal attention over each row's own block
 // on plain token tiles and folds the row's partials in by log-sum-exp merge.
+#include <algorithm>
+
 #include "attn_core.h"
 #include "common.h"
 #include "launch.h"
@@ -221,6 +223,148 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_kernel(
   }
 }
 
+// Persistent form of the past-block kernel for blocks of a multiple of 128
+// keys: a fixed grid of workgroups walks the tile table with stride G (the
+// G concurrently processed tiles stay consecutive, so the ones sharing a
+// block's K/V share an XCD's L2), and each workgroup overlaps the end of one
+// tile with the start of the next: once the last K tile has been scored, the
+// next tile's first K/V tiles and its query rows are loaded while the last
+// softmax, PV and the partial's store (straight from the accumulators) run.
+template <int D>
+__global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_persist_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ entries, bf16* __restrict__ part_o, float* __restrict__ part_lse,
+    int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block,
+    int topk, float scale_log2) {
+  QAT_FA_SMEM(D, sm);
+  const int n_items = ntiles[0];
+  const int G = gridDim.x;
+  int item = (int)xcd_logical_id(blockIdx.x, G);
+  if (item >= n_items) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int myrow = wave * 32 + (lane & 31);
+  const int km = topk - 1;
+  const int kv_stride = (int)(hkv * D);
+  const int nt = block / kKT;   // even
+  // whole tiles only (block % 128 == 0): per-lane load offsets fixed
+  FaContig<D, kNW> ctg;
+  ctg.init(kv_stride);
+  // one block's K (or V) rows: (block - 1) * stride + D elements
+  const uint32_t region = (uint32_t)(((int64_t)(block - 1) * kv_stride + D) * 2);
+  auto issue = [&](bf16* dst, const bf16* src, int j0) { ctg.issue(dst, fa_rsrc(src, region), j0, kv_stride); };
+
+  // a tile: its bucket (uniform) and this lane's dispatch entry (-1: padding)
+  struct Item {
+    int bucket;
+    int32_t e;
+  };
+  auto describe = [&](int it) {
+    const int2 td = tiles[it];
+    const int count = min(kRowsPerTile, offsets[td.x + 1] - td.y);
+    return Item{td.x, myrow < count ? entries[td.y + myrow] : -1};
+  };
+  auto kv_base = [&](const bf16* base, int bucket) {
+    const int64_t b = bucket % nbc;
+    const int64_t g = (bucket / nbc) % hkv;
+    const int64_t bi = bucket / (nbc * hkv);
+    return base + ((bi * seq_len + b * block) * hkv + g) * D;
+  };
+  auto q_row = [&](const Item& d) {
+    const int64_t bi = d.bucket / (nbc * hkv);
+    const int64_t row = d.e >= 0 ? (d.e >> 4) : 0;
+    const int64_t h = row % hq;
+    const int64_t r = (row / hq) % q_len;
+    return q + ((bi * seq_len + q_start + r) * hq + h) * D;
+  };
+  auto pidx_of = [&](const Item& d) { return (int64_t)(d.e >> 4) * km + (d.e & 15); };
+  auto load_q = [&](FaState<D>& st, const Item& d) {
+    const bf16* qr = q_row(d);
+    const int hh = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      if (d.e >= 0) {
+        st.q[c] = *(const bf16x8*)(qr + 16 * c + 8 * hh);
+      } else {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        st.q[c] = __builtin_bit_cast(bf16x8, z);
+      }
+    }
+  };
+
+  Item cur = describe(item);
+  FaState<D> st;
+  fa_init<D>(st, q_row(cur), cur.e >= 0);
+  {
+    const bf16* kb = kv_base(k, cur.bucket);
+    const bf16* vb = kv_base(v, cur.bucket);
+    issue(sm.k0, kb, 0);
+    issue(sm.v0, vb, 0);
+    issue(sm.k1, kb, kKT);
+    issue(sm.v1, vb, kKT);
+  }
+  auto ok = [](int) { return true; };
+  while (true) {
+    const int nxt_item = item + G;
+    const bool has_next = nxt_item < n_items;
+    Item nxt = cur;
+    if (has_next) nxt = describe(nxt_item);
+    const bf16* kb = kv_base(k, cur.bucket);
+    const bf16* vb = kv_base(v, cur.bucket);
+    // K0, V0, K1, V1 and the query rows are in flight
+    fa_wait_loads();
+    __syncthreads();
+    f32x16 s_cur[2], s_nxt[2];
+    fa_scores<D>(st, sm.k0, s_cur);
+    __syncthreads();
+    if (nt > 2) issue(sm.k0, kb, 2 * kKT);
+    for (int j = 0; j + 2 < nt; j += 2) {
+      fa_scores<D>(st, sm.k1, s_nxt);
+      fa_finish_tile<D, false>(st, s_cur, sm.v0, scale_log2, j * kKT, block, ok, ok);
+      fa_wait_loads();
+      __syncthreads();
+      issue(sm.k1, kb, (j + 3) * kKT);
+      issue(sm.v0, vb, (j + 2) * kKT);
+      fa_scores<D>(st, sm.k0, s_cur);
+      fa_finish_tile<D, false>(st, s_nxt, sm.v1, scale_log2, (j + 1) * kKT, block, ok, ok);
+      fa_wait_loads();
+      __syncthreads();
+      if (j + 4 < nt) issue(sm.k0, kb, (j + 4) * kKT);
+      issue(sm.v1, vb, (j + 3) * kKT);
+    }
+    // last pair: tiles nt-2 (V in v0) and nt-1 (K in k1, V in v1)
+    fa_scores<D>(st, sm.k1, s_nxt);
+    fa_finish_tile<D, false>(st, s_cur, sm.v0, scale_log2, (nt - 2) * kKT, block, ok, ok);
+    fa_wait_loads();
+    __syncthreads();
+    // every K tile is scored and V_{nt-2} consumed: k0, k1, v0 and the query
+    // registers are free for the next tile
+    if (has_next) {
+      issue(sm.k0, kv_base(k, nxt.bucket), 0);
+      issue(sm.k1, kv_base(k, nxt.bucket), kKT);
+      issue(sm.v0, kv_base(v, nxt.bucket), 0);
+      load_q(st, nxt);
+    }
+    fa_finish_tile<D, false>(st, s_nxt, sm.v1, scale_log2, (nt - 1) * kKT, block, ok, ok);
+    float inv_l, lse;
+    fa_finish<D>(st, inv_l, lse);
+    const int64_t pidx = cur.e >= 0 ? pidx_of(cur) : 0;
+    if ((lane >> 5) == 0 && cur.e >= 0) part_lse[pidx] = lse;
+    fa_store_row_bf16<D>(st, inv_l, part_o + pidx * D, cur.e >= 0);
+    if (!has_next) break;
+    __syncthreads();   // every wave is done with V_{nt-1}
+    issue(sm.v1, kv_base(v, nxt.bucket), kKT);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[t][i] = 0.f;
+    st.m = -__builtin_inff();
+    st.l = 0.f;
+    cur = nxt;
+    item = nxt_item;
+  }
+}
+
 // Current-block attention (causal) merged with the row's past-block
 // partials: the partials seed the online-softmax state (running max, sum and
 // accumulator), so the merge costs no pass of its own and its loads overlap
@@ -400,7 +544,13 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
   if (topk > 1 && max_tiles > 0 && nbc > 0) {
     {
       KTimer tm("moba_past_attn", s);
-      if (block % kKT == 0)
+      if (block % (2 * kKT) == 0 && (int64_t)block * hkv * D * 2 < (1ll << 31)) {
+        // persistent grid: two workgroups per CU (256 CUs), never more than the tiles
+        const int64_t grid = std::min<int64_t>(max_tiles, 512);
+        hipLaunchKernelGGL((moba_past_persist_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, s, q, k, v,
+                           tiles, ntiles, offsets, entries, part_o, part_lse, seq_len, hq, hkv, nbc, q_start,
+                           q_len, block, topk, sl2);
+      } else if (block % kKT == 0)
         hipLaunchKernelGGL((moba_past_kernel<D, true>), dim3((unsigned)max_tiles), dim3(kThreads), 0, s, q, k, v,
                            tiles, ntiles, offsets, entries, part_o, part_lse, seq_len, hq, hkv, nbc, q_start, q_len,
                            block, topk, sl2);
