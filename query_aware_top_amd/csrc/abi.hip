@@ -140,8 +140,8 @@ struct MobaLayout {
   int32_t* counts = nullptr;
   int32_t* offsets = nullptr;
   int32_t* cursor = nullptr;
-  int32_t* entries = nullptr;
-  int2* tiles = nullptr;
+  int2* entries = nullptr;
+  int4* tiles = nullptr;
   int32_t* ntiles = nullptr;
   void* part_o = nullptr;
   float* part_lse = nullptr;
@@ -165,6 +165,7 @@ int moba_check(const qat_moba_params* p) {
   if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return fail(QAT_EINVAL, "scale must be finite and > 0");
   if (p->dtype != QAT_F32 && p->dtype != QAT_BF16) return fail(QAT_EINVAL, "unknown dtype %d", p->dtype);
   if (p->batch * p->q_len * p->n_q_heads >= (1ll << 27)) return fail(QAT_EUNSUPPORTED, "too many query rows");
+  if (p->batch * p->seq_len * p->n_q_heads >= (1ll << 31)) return fail(QAT_EUNSUPPORTED, "q holds too many rows");
   return QAT_OK;
 }
 
@@ -183,8 +184,8 @@ MobaLayout moba_layout(const qat_moba_params* p, void* ws) {
   L.counts = c.take<int32_t>((size_t)L.nbuckets + 1);
   L.offsets = c.take<int32_t>((size_t)L.nbuckets + 1);
   L.cursor = c.take<int32_t>((size_t)L.nbuckets + 1);
-  L.entries = c.take<int32_t>((size_t)L.nrows * (p->topk - 1) + 1);
-  L.tiles = c.take<int2>((size_t)L.max_tiles + 1);
+  L.entries = c.take<int2>((size_t)L.nrows * (p->topk - 1) + 1);
+  L.tiles = c.take<int4>((size_t)L.max_tiles + 1);
   L.ntiles = c.take<int32_t>(1);
   L.part_o = (void*)c.take<char>((size_t)L.nrows * (p->topk - 1) * p->head_dim * esz + 1);
   L.part_lse = c.take<float>((size_t)L.nrows * (p->topk - 1) + 1);
@@ -449,12 +450,13 @@ QAT_EXPORT int moba_sparse_attn(const qat_moba_params* p, const void* q, const v
   if (bf && p->window == 0) {
     if (p->topk > 1 && L.nbuckets > 0) {
       qat::KTimer tm("moba_dispatch", s);
-      e = qat::launch_moba_dispatch(blk, p->batch, p->n_q_heads, p->n_kv_heads, p->q_start, p->q_len, p->block,
-                                    p->topk, L.nbc, L.counts, L.offsets, L.cursor, L.entries, L.tiles, L.ntiles, s);
+      e = qat::launch_moba_dispatch(blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim,
+                                    p->q_start, p->q_len, p->block, p->topk, L.nbc, L.counts, L.offsets, L.cursor,
+                                    L.entries, L.tiles, L.ntiles, s);
       if (e != hipSuccess) return hip_status(e, "moba_sparse_attn: dispatch");
     }
-    e = qat::launch_moba_attn_mfma(q, k, v, blk, L.tiles, L.ntiles, L.offsets, L.entries, L.part_o, L.part_lse, out,
-                                   lse, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim, L.nbc,
+    e = qat::launch_moba_attn_mfma(q, k, v, blk, L.tiles, L.ntiles, L.entries, L.part_o, L.part_lse, out, lse,
+                                   p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim, L.nbc,
                                    p->q_start, p->q_len, p->block, p->topk, p->scale,
                                    L.nbuckets > 0 ? L.max_tiles : 0, s);
   } else {

@@ -176,7 +176,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t fa_rsrc(const bf16* base, uint
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, (int)kBufWord3);
 }
 
-__device__ __forceinline__ void fa_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits for every outstanding vector memory operation of the wave. The
+// builtin (encoding of vmcnt(0), other counters untouched) lets the compiler's
+// own wait insertion know the counter is drained; the empty asm statements
+// keep memory accesses from moving across it.
+__device__ __forceinline__ void fa_wait_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for LDS hand-offs only: the wave's LDS operations are
+// complete when it arrives (lgkmcnt), but its global stores are not waited
+// for (a __syncthreads would wait for every outstanding memory operation).
+// Direct-to-LDS loads must be waited for with fa_wait_loads() first. The
+// memory clobber keeps memory accesses from moving across it.
+__device__ __forceinline__ void fa_lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -343,10 +363,10 @@ __device__ __forceinline__ void fa_segment_run(FaState<D>& st, const FaSmem<D>& 
   // prologue (K0, V0, K1, V1 issued by fa_segment_begin): S(0) computed,
   // then K2 into K0's buffer (after every wave has read K0)
   fa_wait_loads();
-  __syncthreads();
+  fa_lds_barrier();
   f32x16 s_cur[2], s_nxt[2];
   fa_scores<D>(st, sm.k0, s_cur);
-  __syncthreads();
+  fa_lds_barrier();
   issue_k(sm.k0, 2);
   for (int j = 0; j < nt; j += 2) {
     // ---- even j: S(j+1) from K buffer 1, PV(j) from V buffer 0. The score
@@ -357,7 +377,7 @@ __device__ __forceinline__ void fa_segment_run(FaState<D>& st, const FaSmem<D>& 
     fa_finish_tile<D, CAN_MASK>(st, s_cur, sm.v0, scale_log2, j * kKT, n, key_ok, tile_full);
     if (j + 1 >= nt) break;
     fa_wait_loads();
-    __syncthreads();
+    fa_lds_barrier();
     issue_k(sm.k1, j + 3);
     issue_v(sm.v0, j + 2);
     // ---- odd j+1: S(j+2) from K buffer 0, PV(j+1) from V buffer 1
@@ -365,12 +385,12 @@ __device__ __forceinline__ void fa_segment_run(FaState<D>& st, const FaSmem<D>& 
     fa_finish_tile<D, CAN_MASK>(st, s_nxt, sm.v1, scale_log2, (j + 1) * kKT, n, key_ok, tile_full);
     if (j + 2 >= nt) break;
     fa_wait_loads();
-    __syncthreads();
+    fa_lds_barrier();
     issue_k(sm.k0, j + 4);
     issue_v(sm.v1, j + 3);
   }
   fa_wait_loads();
-  __syncthreads();
+  fa_lds_barrier();
 }
 
 template <int D, int NW, bool CAN_MASK, typename RowOfs, typename KeyOk, typename TileFull>
@@ -455,6 +475,39 @@ __device__ __forceinline__ void fa_store_row_bf16(const FaState<D>& st, float mu
       w[3] = h ? b1 : r1;
       if (ok) *(u32x4*)(dst + 32 * t + 16 * p + 8 * h) = w;
     }
+}
+
+// Stores the wave's 32 query rows of O (times mul) as bf16 rows through an
+// LDS staging area: each lane first writes its accumulator groups into its
+// row (rows padded by 16 bytes, so the writes spread over the banks), then
+// 16 lanes per row read back whole 16-byte chunks and write them out, so
+// each store instruction covers four complete 2*D-byte rows instead of 32
+// fragments. stage: this wave's 32 rows of D + 8 bf16; rows: its 32 output
+// row indices (a lane's row index < 0 skips that row).
+template <int D>
+__device__ __forceinline__ void fa_store_rows_staged(const FaState<D>& st, float mul, bf16* stage, int64_t* rows,
+                                                     int64_t my_row, bf16* __restrict__ out) {
+  constexpr int RS = D + 8;   // padded row stride (elements)
+  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
+  if (h == 0) rows[r] = my_row;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      uint2 w;
+      w.x = pack_bf16x2(st.o[t][4 * gi + 0] * mul, st.o[t][4 * gi + 1] * mul);
+      w.y = pack_bf16x2(st.o[t][4 * gi + 2] * mul, st.o[t][4 * gi + 3] * mul);
+      *(uint2*)(stage + r * RS + 32 * t + 8 * gi + 4 * h) = w;
+    }
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int row = k * RPI + lane / CPR, c = lane % CPR;
+    const int64_t dst = rows[row];
+    const u32x4 v = *(const u32x4*)(stage + row * RS + 8 * c);
+    if (dst >= 0) *(u32x4*)(out + dst * D + 8 * c) = v;
+  }
 }
 
 // Workgroup id remapped so that consecutive logical ids run on the same XCD:

@@ -34,14 +34,17 @@ hipError_t launch_moba_select(const void* q, bool bf, const float* kbar, const b
 // ---- MoBA attention (moba_attn.hip) ---------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 int64_t moba_max_tiles(int64_t nrows, int topk, int64_t nbuckets);
-hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t hq, int64_t hkv, int64_t q_start,
-                                int64_t q_len, int block, int topk, int64_t nbc, int32_t* counts, int32_t* offsets,
-                                int32_t* cursor, int32_t* entries, int2* tiles, int32_t* ntiles, hipStream_t s);
-hipError_t launch_moba_attn_mfma(const void* q, const void* k, const void* v, const int32_t* blk, const int2* tiles,
-                                 const int32_t* ntiles, const int32_t* offsets, const int32_t* entries,
-                                 void* part_o, float* part_lse, void* out, float* lse, int64_t batch,
-                                 int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t nbc, int64_t q_start,
-                                 int64_t q_len, int block, int topk, float scale, int64_t max_tiles, hipStream_t s);
+// tiles: {element offset of the block's K/V rows (low, high word), first
+// entry, row count}; entries: {row * 16 + slot, row index of the query in q}
+hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
+                                int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int64_t nbc,
+                                int32_t* counts, int32_t* offsets, int32_t* cursor, int2* entries, int4* tiles,
+                                int32_t* ntiles, hipStream_t s);
+hipError_t launch_moba_attn_mfma(const void* q, const void* k, const void* v, const int32_t* blk,
+                                 const int4* tiles, const int32_t* ntiles, const int2* entries, void* part_o,
+                                 float* part_lse, void* out, float* lse, int64_t batch, int64_t seq_len, int64_t hq,
+                                 int64_t hkv, int64_t d, int64_t nbc, int64_t q_start, int64_t q_len, int block,
+                                 int topk, float scale, int64_t max_tiles, hipStream_t s);
 
 // ---- generic per-row attention (attn_generic.hip) -------------------------
 hipError_t launch_moba_generic(const void* q, const void* k, const void* v, const int32_t* blk, void* out,

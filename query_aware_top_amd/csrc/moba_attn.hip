@@ -22,7 +22,7 @@
 namespace qat {
 
 #ifndef QAT_PAST_NW
-#define QAT_PAST_NW 4
+#define QAT_PAST_NW 8
 #endif
 constexpr int kNW = QAT_PAST_NW;          // waves per past-block workgroup
 constexpr int kThreads = 64 * kNW;
@@ -78,12 +78,14 @@ __global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restri
 }
 
 // Single workgroup: exclusive scans of the bucket counts and of their tile
-// counts, the tile table {bucket, first entry}, scatter cursors and the
-// number of tiles.
+// counts, the tile table, scatter cursors and the number of tiles. A tile
+// descriptor is {low, high word of the element offset of its block's K/V
+// rows (the same for V), first entry, row count}.
 __global__ __launch_bounds__(1024) void moba_scan_kernel(const int32_t* __restrict__ counts, int64_t nb,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ cursor,
-                                                         int2* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+                                                         int64_t nbc, int64_t hkv, int64_t seq_len, int block,
+                                                         int64_t d, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ cursor, int4* __restrict__ tiles,
+                                                         int32_t* __restrict__ ntiles) {
   __shared__ int32_t s_cnt[1024];
   __shared__ int32_t s_til[1024];
   __shared__ int32_t carry[2];
@@ -109,7 +111,11 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(const int32_t* __restri
     if (i < nb) {
       offsets[i] = ex_c;
       cursor[i] = ex_c;
-      for (int32_t j = 0; j < tcount; ++j) tiles[ex_t + j] = make_int2((int)i, ex_c + j * kRowsPerTile);
+      const int64_t b = i % nbc, g = (i / nbc) % hkv, bi = i / (nbc * hkv);
+      const int64_t kv = ((bi * seq_len + b * block) * hkv + g) * d;
+      for (int32_t j = 0; j < tcount; ++j)
+        tiles[ex_t + j] = make_int4((int)(uint32_t)kv, (int)(kv >> 32), ex_c + j * kRowsPerTile,
+                                    min(kRowsPerTile, c - j * kRowsPerTile));
     }
     __syncthreads();
     if (threadIdx.x == 1023) { carry[0] += s_cnt[1023]; carry[1] += s_til[1023]; }
@@ -118,15 +124,16 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(const int32_t* __restri
   if (threadIdx.x == 0) { offsets[nb] = carry[0]; ntiles[0] = carry[1]; }
 }
 
-// (row, slot) -> entries[...] = row * 16 + slot. Each workgroup reserves one
+// (row, slot) -> entries[...] = {row * 16 + slot, index of the row's query
+// vector in q (that is (sequence * seq_len + position) * Hq + head)}. Each workgroup reserves one
 // range per bucket with a single global atomic and places its entries with
 // LDS atomics (the order inside a bucket is irrelevant: every row's result is
 // independent of the other rows sharing its tile).
 __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __restrict__ blk, int64_t total,
                                                            int64_t hq, int64_t hkv, int64_t q_len, int64_t q_start,
                                                            int block, int topk, int64_t nbc, int64_t nbuckets,
-                                                           int32_t* __restrict__ cursor,
-                                                           int32_t* __restrict__ entries) {
+                                                           int64_t seq_len, int32_t* __restrict__ cursor,
+                                                           int2* __restrict__ entries) {
   __shared__ int32_t loc[kDispatchLdsBuckets];
   __shared__ int32_t base_of[kDispatchLdsBuckets];
   const bool use_lds = nbuckets <= kDispatchLdsBuckets;
@@ -151,7 +158,9 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __rest
     const int64_t bk = moba_bucket_of(blk, idx, hq, hkv, q_len, q_start, block, topk, nbc);
     if (bk < 0) continue;
     const int32_t pos = use_lds ? base_of[bk] + atomicAdd(&loc[bk], 1) : atomicAdd(&cursor[bk], 1);
-    entries[pos] = (int32_t)((idx / topk) * 16 + idx % topk);
+    const int64_t row = idx / topk;
+    const int64_t h = row % hq, r = (row / hq) % q_len, bi = row / (hq * q_len);
+    entries[pos] = make_int2((int32_t)(row * 16 + idx % topk), (int32_t)((bi * seq_len + q_start + r) * hq + h));
   }
 }
 
@@ -162,36 +171,30 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __rest
 template <int D, bool FULL>
 __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ entries, bf16* __restrict__ part_o, float* __restrict__ part_lse,
-    int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block,
-    int topk, float scale_log2) {
+    const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, const int2* __restrict__ entries,
+    bf16* __restrict__ part_o, float* __restrict__ part_lse, int64_t hkv, int block, int topk,
+    float scale_log2) {
   QAT_FA_SMEM(D, sm);
   __shared__ int64_t s_pidx[kRowsPerTile];
   const int64_t tile = xcd_logical_id(blockIdx.x, gridDim.x);
   if (tile >= ntiles[0]) return;
-  const int2 td = tiles[tile];
-  const int bucket = td.x;
-  const int first = td.y;
-  const int count = min(kRowsPerTile, offsets[bucket + 1] - first);
-  const int64_t b = bucket % nbc;
-  const int64_t g = (bucket / nbc) % hkv;
-  const int64_t bi = bucket / (nbc * hkv);
+  const int4 td = tiles[tile];
+  const int64_t kv_off = (int64_t)(uint32_t)td.x | ((int64_t)td.y << 32);
+  const int first = td.z;
+  const int count = td.w;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int myrow = wave * 32 + (lane & 31);
   const bool valid = myrow < count;
-  const int32_t e = valid ? entries[first + myrow] : 0;
-  const int64_t row = e >> 4;
-  const int slot = e & 15;
-  const int64_t h = row % hq;
-  const int64_t r = (row / hq) % q_len;
-  const bf16* qrow = q + ((bi * seq_len + q_start + r) * hq + h) * D;
+  const int2 e2 = valid ? entries[first + myrow] : make_int2(0, 0);
+  const int64_t row = e2.x >> 4;
+  const int slot = e2.x & 15;
+  const bf16* qrow = q + (int64_t)e2.y * D;
 
   FaState<D> st;
   fa_init<D>(st, qrow, valid);
-  const bf16* kb = k + ((bi * seq_len + b * block) * hkv + g) * D;
-  const bf16* vb = v + ((bi * seq_len + b * block) * hkv + g) * D;
+  const bf16* kb = k + kv_off;
+  const bf16* vb = v + kv_off;
   const int kv_stride = (int)(hkv * D);
   // FULL: block % 64 == 0, so no tile of the block needs masking
   fa_segment<D, kNW, !FULL>(st, sm, kb, vb, block, scale_log2, [=](int j) { return j * kv_stride; },
@@ -233,57 +236,56 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_kernel(
 template <int D>
 __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_persist_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ entries, bf16* __restrict__ part_o, float* __restrict__ part_lse,
-    int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block,
-    int topk, float scale_log2) {
+    const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, const int2* __restrict__ entries,
+    bf16* __restrict__ part_o, float* __restrict__ part_lse, int64_t hkv, int block, int topk,
+    float scale_log2) {
   QAT_FA_SMEM(D, sm);
+  __shared__ __align__(16) bf16 s_stage[kNW * 32 * (D + 8)];
+  __shared__ int64_t s_rows[kNW * 32];
   const int n_items = ntiles[0];
   const int G = gridDim.x;
   int item = (int)xcd_logical_id(blockIdx.x, G);
   if (item >= n_items) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int myrow = wave * 32 + (lane & 31);
+  const int lane = threadIdx.x & 63;
+  const int myrow = (threadIdx.x >> 6) * 32 + (lane & 31);
   const int km = topk - 1;
   const int kv_stride = (int)(hkv * D);
   const int nt = block / kKT;   // even
-  // whole tiles only (block % 128 == 0): per-lane load offsets fixed
+  // whole tiles only (block % 128 == 0): per-lane load offsets fixed; one
+  // block's K (or V) rows span (block - 1) * stride + D elements
   FaContig<D, kNW> ctg;
   ctg.init(kv_stride);
-  // one block's K (or V) rows: (block - 1) * stride + D elements
   const uint32_t region = (uint32_t)(((int64_t)(block - 1) * kv_stride + D) * 2);
   auto issue = [&](bf16* dst, const bf16* src, int j0) { ctg.issue(dst, fa_rsrc(src, region), j0, kv_stride); };
 
-  // a tile: its bucket (uniform) and this lane's dispatch entry (-1: padding)
-  struct Item {
-    int bucket;
-    int32_t e;
+  // Descriptors run one tile ahead of use, loaded by plain vector loads that
+  // the per-tile waits cover: at the top of tile i its own entry and the
+  // next tile's descriptor are resident; the next tile's entry and the
+  // descriptor after it are then requested.
+  struct Tile {
+    int64_t kv;   // element offset of the block's K/V rows
+    int first, count;
   };
-  auto describe = [&](int it) {
-    const int2 td = tiles[it];
-    const int count = min(kRowsPerTile, offsets[td.x + 1] - td.y);
-    return Item{td.x, myrow < count ? entries[td.y + myrow] : -1};
+  struct Entry {
+    int32_t rs;   // row * 16 + slot, -1 for a padding lane
+    int32_t qrow;
   };
-  auto kv_base = [&](const bf16* base, int bucket) {
-    const int64_t b = bucket % nbc;
-    const int64_t g = (bucket / nbc) % hkv;
-    const int64_t bi = bucket / (nbc * hkv);
-    return base + ((bi * seq_len + b * block) * hkv + g) * D;
+  auto tile_at = [=](int it) {
+    const int4 t = tiles[it];
+    return Tile{(int64_t)(uint32_t)t.x | ((int64_t)t.y << 32), t.z, t.w};
   };
-  auto q_row = [&](const Item& d) {
-    const int64_t bi = d.bucket / (nbc * hkv);
-    const int64_t row = d.e >= 0 ? (d.e >> 4) : 0;
-    const int64_t h = row % hq;
-    const int64_t r = (row / hq) % q_len;
-    return q + ((bi * seq_len + q_start + r) * hq + h) * D;
+  // loaded unconditionally (a padding lane re-reads the tile's first entry)
+  // so that nothing waits for it until its first use
+  auto entry_of = [=](Tile t) {
+    const int2 x = entries[t.first + (myrow < t.count ? myrow : 0)];
+    return Entry{myrow < t.count ? x.x : -1, x.y};
   };
-  auto pidx_of = [&](const Item& d) { return (int64_t)(d.e >> 4) * km + (d.e & 15); };
-  auto load_q = [&](FaState<D>& st, const Item& d) {
-    const bf16* qr = q_row(d);
+  auto load_q = [=](FaState<D>& st, Entry e) {
+    const bf16* qr = q + (int64_t)e.qrow * D;
     const int hh = lane >> 5;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      if (d.e >= 0) {
+      if (e.rs >= 0) {
         st.q[c] = *(const bf16x8*)(qr + 16 * c + 8 * hh);
       } else {
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -292,43 +294,70 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_persist_kernel(
     }
   };
 
-  Item cur = describe(item);
+  Tile t_cur = tile_at(item);
+  Entry e_cur = entry_of(t_cur);
+  Tile t_nxt = tile_at(item + G < n_items ? item + G : item);
   FaState<D> st;
-  fa_init<D>(st, q_row(cur), cur.e >= 0);
+  fa_init<D>(st, q, false);
+  load_q(st, e_cur);
   {
-    const bf16* kb = kv_base(k, cur.bucket);
-    const bf16* vb = kv_base(v, cur.bucket);
-    issue(sm.k0, kb, 0);
-    issue(sm.v0, vb, 0);
-    issue(sm.k1, kb, kKT);
-    issue(sm.v1, vb, kKT);
+    const int64_t kv = t_cur.kv;
+    issue(sm.k0, k + kv, 0);
+    issue(sm.v0, v + kv, 0);
+    issue(sm.k1, k + kv, kKT);
+    issue(sm.v1, v + kv, kKT);
   }
   auto ok = [](int) { return true; };
+  // A tile's partial output is written at the top of the next tile, once
+  // that tile's first K/V and query rows have been waited for: writes are
+  // never waited on by the wait that guards those loads.
+  auto epilogue = [&](const Entry& e) {
+    float inv_l, lse;
+    fa_finish<D>(st, inv_l, lse);
+    const bool mine = e.rs >= 0;
+    const int64_t pidx = mine ? (int64_t)(e.rs >> 4) * km + (e.rs & 15) : 0;
+    if ((lane >> 5) == 0 && mine) part_lse[pidx] = lse;
+    const int wv = threadIdx.x >> 6;
+    fa_store_rows_staged<D>(st, inv_l, s_stage + wv * 32 * (D + 8), s_rows + wv * 32, mine ? pidx : -1, part_o);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[t][i] = 0.f;
+    st.m = -__builtin_inff();
+    st.l = 0.f;
+  };
+  bool pending = false;
+  Entry e_prev = e_cur;
   while (true) {
     const int nxt_item = item + G;
     const bool has_next = nxt_item < n_items;
-    Item nxt = cur;
-    if (has_next) nxt = describe(nxt_item);
-    const bf16* kb = kv_base(k, cur.bucket);
-    const bf16* vb = kv_base(v, cur.bucket);
+    const int64_t kv = t_cur.kv;
+    const bf16* kb = k + kv;
+    const bf16* vb = v + kv;
     // K0, V0, K1, V1 and the query rows are in flight
     fa_wait_loads();
-    __syncthreads();
+    fa_lds_barrier();
+    if (pending) epilogue(e_prev);
+    // the next tile's descriptors, first used at this tile's last pair (no
+    // select on the loaded values: that would wait for them right here; when
+    // there is no next tile, t_nxt repeats the current one and e_nxt is unused)
+    const Entry e_nxt = entry_of(t_nxt);
+    const Tile t_nn = tile_at(nxt_item + G < n_items ? nxt_item + G : item);
     f32x16 s_cur[2], s_nxt[2];
     fa_scores<D>(st, sm.k0, s_cur);
-    __syncthreads();
+    fa_lds_barrier();
     if (nt > 2) issue(sm.k0, kb, 2 * kKT);
     for (int j = 0; j + 2 < nt; j += 2) {
       fa_scores<D>(st, sm.k1, s_nxt);
       fa_finish_tile<D, false>(st, s_cur, sm.v0, scale_log2, j * kKT, block, ok, ok);
       fa_wait_loads();
-      __syncthreads();
+      fa_lds_barrier();
       issue(sm.k1, kb, (j + 3) * kKT);
       issue(sm.v0, vb, (j + 2) * kKT);
       fa_scores<D>(st, sm.k0, s_cur);
       fa_finish_tile<D, false>(st, s_nxt, sm.v1, scale_log2, (j + 1) * kKT, block, ok, ok);
       fa_wait_loads();
-      __syncthreads();
+      fa_lds_barrier();
       if (j + 4 < nt) issue(sm.k0, kb, (j + 4) * kKT);
       issue(sm.v1, vb, (j + 3) * kKT);
     }
@@ -336,31 +365,28 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_persist_kernel(
     fa_scores<D>(st, sm.k1, s_nxt);
     fa_finish_tile<D, false>(st, s_cur, sm.v0, scale_log2, (nt - 2) * kKT, block, ok, ok);
     fa_wait_loads();
-    __syncthreads();
+    fa_lds_barrier();
     // every K tile is scored and V_{nt-2} consumed: k0, k1, v0 and the query
     // registers are free for the next tile
+    const int64_t kv_n = t_nxt.kv;
     if (has_next) {
-      issue(sm.k0, kv_base(k, nxt.bucket), 0);
-      issue(sm.k1, kv_base(k, nxt.bucket), kKT);
-      issue(sm.v0, kv_base(v, nxt.bucket), 0);
-      load_q(st, nxt);
+      issue(sm.k0, k + kv_n, 0);
+      issue(sm.k1, k + kv_n, kKT);
+      issue(sm.v0, v + kv_n, 0);
+      load_q(st, e_nxt);
     }
     fa_finish_tile<D, false>(st, s_nxt, sm.v1, scale_log2, (nt - 1) * kKT, block, ok, ok);
-    float inv_l, lse;
-    fa_finish<D>(st, inv_l, lse);
-    const int64_t pidx = cur.e >= 0 ? pidx_of(cur) : 0;
-    if ((lane >> 5) == 0 && cur.e >= 0) part_lse[pidx] = lse;
-    fa_store_row_bf16<D>(st, inv_l, part_o + pidx * D, cur.e >= 0);
-    if (!has_next) break;
-    __syncthreads();   // every wave is done with V_{nt-1}
-    issue(sm.v1, kv_base(v, nxt.bucket), kKT);
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.o[t][i] = 0.f;
-    st.m = -__builtin_inff();
-    st.l = 0.f;
-    cur = nxt;
+    if (!has_next) {
+      epilogue(e_cur);
+      break;
+    }
+    fa_lds_barrier();   // every wave is done with V_{nt-1}
+    issue(sm.v1, v + kv_n, kKT);
+    pending = true;
+    e_prev = e_cur;
+    t_cur = t_nxt;
+    e_cur = e_nxt;
+    t_nxt = t_nn;
     item = nxt_item;
   }
 }
@@ -509,9 +535,10 @@ int64_t moba_max_tiles(int64_t nrows, int topk, int64_t nbuckets) {
   return cdiv(nrows * (topk - 1), kRowsPerTile) + nbuckets;
 }
 
-hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t hq, int64_t hkv, int64_t q_start,
-                                int64_t q_len, int block, int topk, int64_t nbc, int32_t* counts, int32_t* offsets,
-                                int32_t* cursor, int32_t* entries, int2* tiles, int32_t* ntiles, hipStream_t s) {
+hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
+                                int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int64_t nbc,
+                                int32_t* counts, int32_t* offsets, int32_t* cursor, int2* entries, int4* tiles,
+                                int32_t* ntiles, hipStream_t s) {
   const int64_t total = batch * q_len * hq * topk;
   const int64_t nbuckets = batch * hkv * nbc;
   hipError_t e = launch_fill_i32(counts, nbuckets, 0, s);
@@ -522,11 +549,12 @@ hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t hq, i
                        topk, nbc, nbuckets, counts);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(moba_scan_kernel, dim3(1), dim3(1024), 0, s, counts, nbuckets, offsets, cursor, tiles, ntiles);
+  hipLaunchKernelGGL(moba_scan_kernel, dim3(1), dim3(1024), 0, s, counts, nbuckets, nbc, hkv, seq_len, block, d,
+                     offsets, cursor, tiles, ntiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (nbuckets > 0) {
     hipLaunchKernelGGL(moba_scatter_kernel, dim3(grid), dim3(256), 0, s, blk, total, hq, hkv, q_len, q_start,
-                       block, topk, nbc, nbuckets, cursor, entries);
+                       block, topk, nbc, nbuckets, seq_len, cursor, entries);
     e = hipGetLastError();
   }
   return e;
@@ -534,30 +562,27 @@ hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t hq, i
 
 template <int D>
 static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v, const int32_t* blk,
-                                     const int2* tiles, const int32_t* ntiles, const int32_t* offsets,
-                                     const int32_t* entries, bf16* part_o, float* part_lse, bf16* out,
-                                     float* lse, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
-                                     int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk,
-                                     float scale, int64_t max_tiles, hipStream_t s) {
+                                     const int4* tiles, const int32_t* ntiles, const int2* entries, bf16* part_o,
+                                     float* part_lse, bf16* out, float* lse, int64_t batch, int64_t seq_len,
+                                     int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block,
+                                     int topk, float scale, int64_t max_tiles, hipStream_t s) {
   const float sl2 = scale * kLog2e;
   hipError_t e;
   if (topk > 1 && max_tiles > 0 && nbc > 0) {
     {
       KTimer tm("moba_past_attn", s);
       if (block % (2 * kKT) == 0 && (int64_t)block * hkv * D * 2 < (1ll << 31)) {
-        // persistent grid: two workgroups per CU (256 CUs), never more than the tiles
-        const int64_t grid = std::min<int64_t>(max_tiles, 512);
+        // persistent grid: the workgroups that fit at once (256 CUs x 8 waves), never more than the tiles
+        const int64_t grid = std::min<int64_t>(max_tiles, 2048 / kNW);
         hipLaunchKernelGGL((moba_past_persist_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, s, q, k, v,
-                           tiles, ntiles, offsets, entries, part_o, part_lse, seq_len, hq, hkv, nbc, q_start,
-                           q_len, block, topk, sl2);
-      } else if (block % kKT == 0)
+                           tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
+      } else if (block % kKT == 0) {
         hipLaunchKernelGGL((moba_past_kernel<D, true>), dim3((unsigned)max_tiles), dim3(kThreads), 0, s, q, k, v,
-                           tiles, ntiles, offsets, entries, part_o, part_lse, seq_len, hq, hkv, nbc, q_start, q_len,
-                           block, topk, sl2);
-      else
+                           tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
+      } else {
         hipLaunchKernelGGL((moba_past_kernel<D, false>), dim3((unsigned)max_tiles), dim3(kThreads), 0, s, q, k, v,
-                           tiles, ntiles, offsets, entries, part_o, part_lse, seq_len, hq, hkv, nbc, q_start, q_len,
-                           block, topk, sl2);
+                           tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
+      }
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -578,18 +603,17 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
 }
 
 hipError_t launch_moba_attn_mfma(const void* q, const void* k, const void* v, const int32_t* blk,
-                                 const int2* tiles, const int32_t* ntiles, const int32_t* offsets,
-                                 const int32_t* entries, void* part_o, float* part_lse, void* out, float* lse,
-                                 int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t nbc,
-                                 int64_t q_start, int64_t q_len, int block, int topk, float scale,
-                                 int64_t max_tiles, hipStream_t s) {
+                                 const int4* tiles, const int32_t* ntiles, const int2* entries, void* part_o,
+                                 float* part_lse, void* out, float* lse, int64_t batch, int64_t seq_len, int64_t hq,
+                                 int64_t hkv, int64_t d, int64_t nbc, int64_t q_start, int64_t q_len, int block,
+                                 int topk, float scale, int64_t max_tiles, hipStream_t s) {
   if (d == 64)
-    return launch_moba_attn_d<64>((const bf16*)q, (const bf16*)k, (const bf16*)v, blk, tiles, ntiles, offsets,
-                                  entries, (bf16*)part_o, part_lse, (bf16*)out, lse, batch, seq_len, hq, hkv,
-                                  nbc, q_start, q_len, block, topk, scale, max_tiles, s);
-  return launch_moba_attn_d<128>((const bf16*)q, (const bf16*)k, (const bf16*)v, blk, tiles, ntiles, offsets,
-                                 entries, (bf16*)part_o, part_lse, (bf16*)out, lse, batch, seq_len, hq, hkv,
-                                 nbc, q_start, q_len, block, topk, scale, max_tiles, s);
+    return launch_moba_attn_d<64>((const bf16*)q, (const bf16*)k, (const bf16*)v, blk, tiles, ntiles, entries,
+                                  (bf16*)part_o, part_lse, (bf16*)out, lse, batch, seq_len, hq, hkv, nbc, q_start,
+                                  q_len, block, topk, scale, max_tiles, s);
+  return launch_moba_attn_d<128>((const bf16*)q, (const bf16*)k, (const bf16*)v, blk, tiles, ntiles, entries,
+                                 (bf16*)part_o, part_lse, (bf16*)out, lse, batch, seq_len, hq, hkv, nbc, q_start,
+                                 q_len, block, topk, scale, max_tiles, s);
 }
 
 }  // namespace qat
