@@ -484,6 +484,11 @@ __device__ __forceinline__ void fa_store_row_bf16(const FaState<D>& st, float mu
 // each store instruction covers four complete 2*D-byte rows instead of 32
 // fragments. stage: this wave's 32 rows of D + 8 bf16; rows: its 32 output
 // row indices (a lane's row index < 0 skips that row).
+//
+// Row layout ("split halves"): the D/2 values a lower-half lane holds (d with
+// d % 8 < 4, in accumulator order) come first, then the upper half's, so a
+// reader with the same register layout fetches its values as D/16
+// contiguous 16-byte pieces.
 template <int D>
 __device__ __forceinline__ void fa_store_rows_staged(const FaState<D>& st, float mul, bf16* stage, int64_t* rows,
                                                      int64_t my_row, bf16* __restrict__ out) {
@@ -497,7 +502,7 @@ __device__ __forceinline__ void fa_store_rows_staged(const FaState<D>& st, float
       uint2 w;
       w.x = pack_bf16x2(st.o[t][4 * gi + 0] * mul, st.o[t][4 * gi + 1] * mul);
       w.y = pack_bf16x2(st.o[t][4 * gi + 2] * mul, st.o[t][4 * gi + 3] * mul);
-      *(uint2*)(stage + r * RS + 32 * t + 8 * gi + 4 * h) = w;
+      *(uint2*)(stage + r * RS + h * (D / 2) + 4 * (4 * t + gi)) = w;
     }
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;

@@ -175,7 +175,8 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_kernel(
     bf16* __restrict__ part_o, float* __restrict__ part_lse, int64_t hkv, int block, int topk,
     float scale_log2) {
   QAT_FA_SMEM(D, sm);
-  __shared__ int64_t s_pidx[kRowsPerTile];
+  __shared__ __align__(16) bf16 s_stage[kNW * 32 * (D + 8)];
+  __shared__ int64_t s_rows[kNW * 32];
   const int64_t tile = xcd_logical_id(blockIdx.x, gridDim.x);
   if (tile >= ntiles[0]) return;
   const int4 td = tiles[tile];
@@ -201,29 +202,9 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_kernel(
                             [](int) { return true; }, [](int) { return true; });
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
-  if ((lane >> 5) == 0) {
-    s_pidx[myrow] = valid ? row * (topk - 1) + slot : -1;
-    if (valid) part_lse[row * (topk - 1) + slot] = lse;
-  }
-  constexpr int TPR = D / 8;                  // threads per row
-  constexpr int RPP = kThreads / TPR;         // rows per pass
-  const int sub = threadIdx.x % TPR;
-  for (int half = 0; half < kNW / 4; ++half) {
-    fa_rows_to_lds<D>(st, sm, inv_l, half);
-    __syncthreads();
-    for (int rr = threadIdx.x / TPR; rr < 128; rr += RPP) {
-      const int64_t pi = s_pidx[half * 128 + rr];
-      if (pi < 0) continue;
-      const f32x4 a = fa_row_chunk<D>(sm, rr, 2 * sub), c = fa_row_chunk<D>(sm, rr, 2 * sub + 1);
-      u32x4 w;
-      w[0] = pack_bf16x2(a[0], a[1]);
-      w[1] = pack_bf16x2(a[2], a[3]);
-      w[2] = pack_bf16x2(c[0], c[1]);
-      w[3] = pack_bf16x2(c[2], c[3]);
-      *(u32x4*)(part_o + pi * D + sub * 8) = w;
-    }
-    __syncthreads();
-  }
+  const int64_t pidx = row * (topk - 1) + slot;
+  if ((lane >> 5) == 0 && valid) part_lse[pidx] = lse;
+  fa_store_rows_staged<D>(st, inv_l, s_stage + wave * 32 * (D + 8), s_rows + wave * 32, valid ? pidx : -1, part_o);
 }
 
 // Persistent form of the past-block kernel for blocks of a multiple of 128
@@ -476,26 +457,32 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
       }
     st.m = m_new;
   };
-  const int32_t* br = blk + row * topk;
+  // every (row, slot) partial lse is -inf unless the slot's block was
+  // dispatched (the lse array is cleared before the past-block pass), so the
+  // loads need no look at the gating: one memory round trip, beside the tiles'
   for (int s0 = 0; s0 < km; s0 += kPreSlots) {   // one round for k <= kPreSlots + 1
     float plse[kPreSlots];
     uint2 po[kPreSlots][D / 8];
 #pragma unroll
     for (int sl = 0; sl < kPreSlots; ++sl) {
-      const int32_t b = (valid && s0 + sl < km) ? br[s0 + sl] : -1;
-      const bool use = b >= 0 && b < c;
-      const int64_t pidx = row * km + s0 + sl;
-      plse[sl] = use ? part_lse[pidx] : -__builtin_inff();
-      if (use) {
-        const bf16* src = part_o + pidx * D + 4 * hl;
+      const int64_t pidx = row * km + min(s0 + sl, km - 1);
+      const float lv = part_lse[pidx];
+      plse[sl] = (valid && s0 + sl < km) ? lv : -__builtin_inff();
+      // partial rows are stored in split halves: this lane's D/2 values are
+      // contiguous, in accumulator order
+      const bf16* src = part_o + pidx * D + hl * (D / 2);
 #pragma unroll
-        for (int gq = 0; gq < D / 8; ++gq) po[sl][gq] = *(const uint2*)(src + 8 * gq);
+      for (int i = 0; i < D / 16; ++i) {
+        const u32x4 w = *(const u32x4*)(src + 8 * i);
+        po[sl][2 * i] = make_uint2(w[0], w[1]);
+        po[sl][2 * i + 1] = make_uint2(w[2], w[3]);
       }
     }
 #pragma unroll
     for (int sl = 0; sl < kPreSlots; ++sl)
       if (plse[sl] != -__builtin_inff()) fold(plse[sl] * kLog2e, po[sl]);
   }
+
 
   // keys are block-relative: this lane attends keys j <= lim, and every lane
   // of the wave attends keys j <= wlim
@@ -571,6 +558,10 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
   if (topk > 1 && max_tiles > 0 && nbc > 0) {
     {
       KTimer tm("moba_past_attn", s);
+      // partial lse of slots that get no partial stay -inf (read by the
+      // current-block pass without consulting the gating)
+      e = launch_fill_i32((int32_t*)part_lse, batch * q_len * hq * (topk - 1), (int32_t)0xff800000u, s);
+      if (e != hipSuccess) return e;
       if (block % (2 * kKT) == 0 && (int64_t)block * hkv * D * 2 < (1ll << 31)) {
         // persistent grid: the workgroups that fit at once (256 CUs x 8 waves), never more than the tiles
         const int64_t grid = std::min<int64_t>(max_tiles, 2048 / kNW);
