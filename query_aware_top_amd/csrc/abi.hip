@@ -95,7 +95,7 @@ EsaLayout esa_layout(const qat_esa_params* p, void* ws) {
   L.nkeysplit = qat::esa_key_splits(L.n_mid > 0 ? L.n_mid : 1, m);
   L.nqsplit = qat::esa_prefill_qsplits_eff(L.n_mid > 0 ? L.n_mid : 1, m);
   L.nscan = qat::esa_scan_wgs(L.n_mid > 0 ? L.n_mid : 1);
-  L.ndec = qat::esa_decode_splits(p->n_init, p->topk, p->window);
+  L.ndec = qat::esa_decode_splits(p->batch, p->n_init, p->topk, p->window);
   qat::Carver c(ws);
   L.qpart = c.take<double>((size_t)L.nsplit_q * L.rows * p->d_c);
   L.qc = c.take<float>((size_t)L.rows * p->d_c);

@@ -14,6 +14,8 @@
 //   j <  n_I + n_sel         -> sel[j - n_I]           (selected middle)
 //   j <  n_I + n_sel + n_L   -> L0 + (j - n_I - n_sel) (local window)
 // followed by the chunk's own keys [c0, t] under the causal mask.
+#include <algorithm>
+
 #include "attn_core.h"
 #include "common.h"
 #include "launch.h"
@@ -140,7 +142,18 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
 // every gathered key row is one contiguous H*D*2-byte read. Partial
 // (o, m, l) per (sequence, split, head) go to scratch; a second kernel merges
 // them by log-sum-exp.
-constexpr int kDecKeysPerSplit = 64;
+// keys per split: the fewest whole rounds of resident workgroups (two per CU
+// at this kernel's register use) that give splits of 32..128 keys; 64 keys
+// when no round count does
+int esa_decode_keys_per_split(int64_t batch, int64_t nkeys_max) {
+  constexpr int64_t kSlots = 2 * 256;
+  for (int64_t rounds = 1; rounds <= 8; ++rounds) {
+    const int64_t ns = std::max<int64_t>(1, rounds * kSlots / batch);
+    const int64_t kps = cdiv(nkeys_max, ns);
+    if (kps >= 32 && kps <= 128) return (int)kps;
+  }
+  return 64;
+}
 constexpr int kDecUnroll = 4;
 
 template <int E>
@@ -148,15 +161,15 @@ __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, float* __restrict__ po,
     float* __restrict__ pm, float* __restrict__ pl, int64_t H, int64_t D, int64_t ctx_len, int64_t c0,
-    int64_t n_init, int64_t window, int topk, int nsplit, float scale_log2) {
+    int64_t n_init, int64_t window, int topk, int nsplit, int kps, float scale_log2) {
   const int64_t bi = blockIdx.y;
   const int split = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t HD = H * D;
   const EsaKeys kl = esa_keys(sel, n_sel, bi, topk, c0, n_init, window);
   const int64_t nkeys = kl.count() + 1;   // + the query's own position c0
-  const int64_t j0 = (int64_t)split * kDecKeysPerSplit;
-  const int64_t j1 = min(nkeys, j0 + kDecKeysPerSplit);
+  const int64_t j0 = (int64_t)split * kps;
+  const int64_t j1 = min(nkeys, j0 + kps);
   const int lph = (int)(D / E);          // lanes per head
   const int64_t e0 = (int64_t)tid * E;   // element offset in the row
   float qv[E], o[E];
@@ -174,29 +187,35 @@ __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
   float m = -__builtin_inff(), l = 0.f;
   const bf16* kb = kc + bi * ctx_len * HD + e0;
   const bf16* vb = vc + bi * ctx_len * HD + e0;
-  for (int64_t jb = j0; jb < j1; jb += kDecUnroll) {
-    bf16x8 kr[kDecUnroll][E / 8], vr[kDecUnroll][E / 8];
-    bool ok[kDecUnroll];
+  // kDecUnroll key rows per batch; the next batch's loads are issued before
+  // the current batch is consumed (registers double-buffered)
+  bf16x8 kr[kDecUnroll][E / 8], vr[kDecUnroll][E / 8];
+  auto load_batch = [&](int64_t jb, bf16x8 (&kk)[kDecUnroll][E / 8], bf16x8 (&vv)[kDecUnroll][E / 8]) {
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
       const int64_t j = jb + u;
-      ok[u] = j < j1;
-      const int64_t p = ok[u] ? (j < nkeys - 1 ? kl.pos(j) : c0) : c0;
+      const int64_t p = j < j1 ? (j < nkeys - 1 ? kl.pos(j) : c0) : c0;
 #pragma unroll
       for (int e = 0; e < E / 8; ++e) {
-        kr[u][e] = *(const bf16x8*)(kb + p * HD + 8 * e);
-        vr[u][e] = *(const bf16x8*)(vb + p * HD + 8 * e);
+        kk[u][e] = *(const bf16x8*)(kb + p * HD + 8 * e);
+        vv[u][e] = *(const bf16x8*)(vb + p * HD + 8 * e);
       }
     }
+  };
+  if (j0 < j1) load_batch(j0, kr, vr);
+  for (int64_t jb = j0; jb < j1; jb += kDecUnroll) {
+    bf16x8 kn[kDecUnroll][E / 8], vn[kDecUnroll][E / 8];
+    if (jb + kDecUnroll < j1) load_batch(jb + kDecUnroll, kn, vn);
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
+      const bool ok = jb + u < j1;
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < E / 8; ++e)
 #pragma unroll
         for (int x = 0; x < 8; ++x) s = fmaf(qv[8 * e + x], (float)kr[u][e][x], s);
       for (int off = 1; off < lph; off <<= 1) s += __shfl_xor(s, off, 64);
-      const float x = ok[u] ? s * scale_log2 : -__builtin_inff();
+      const float x = ok ? s * scale_log2 : -__builtin_inff();
       const float m_new = fmaxf(m, x);
       const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
       const float alpha = exp2f(m - m_use);
@@ -208,6 +227,13 @@ __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
         for (int xx = 0; xx < 8; ++xx) o[8 * e + xx] = o[8 * e + xx] * alpha + p * (float)vr[u][e][xx];
       m = m_new;
     }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u)
+#pragma unroll
+      for (int e = 0; e < E / 8; ++e) {
+        kr[u][e] = kn[u][e];
+        vr[u][e] = vn[u][e];
+      }
   }
   const int64_t head = e0 / D;
   const int64_t pidx = (bi * nsplit + split) * H + head;
@@ -223,7 +249,7 @@ __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
 __global__ void esa_decode_combine_kernel(const float* __restrict__ po, const float* __restrict__ pm,
                                           const float* __restrict__ pl, const int32_t* __restrict__ n_sel,
                                           bf16* __restrict__ out, float* __restrict__ lse_out, int64_t H, int64_t D,
-                                          int64_t c0, int64_t n_init, int64_t window, int nsplit_max) {
+                                          int64_t c0, int64_t n_init, int64_t window, int nsplit_max, int kps) {
   const int64_t bi = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // element of the H*D row
   if (idx >= H * D) return;
@@ -232,7 +258,7 @@ __global__ void esa_decode_combine_kernel(const float* __restrict__ po, const fl
   int64_t n_i = min(n_init, c0), n_l = 0;
   if (c0 > n_init) n_l = c0 - max(n_init, c0 - window);
   const int64_t nkeys = n_i + n_sel[bi] + n_l + 1;
-  const int ns = (int)min((int64_t)nsplit_max, cdiv(nkeys, kDecKeysPerSplit));
+  const int ns = (int)min((int64_t)nsplit_max, cdiv(nkeys, kps));
   // online log-sum-exp merge over the splits, 8 splits' loads in flight
   constexpr int U = 8;
   float M = -__builtin_inff(), L = 0.f, O = 0.f;
@@ -266,8 +292,9 @@ __global__ void esa_decode_combine_kernel(const float* __restrict__ po, const fl
 }
 
 // ---------------------------------------------------------------------------
-int esa_decode_splits(int64_t n_init, int64_t topk, int64_t window) {
-  return (int)cdiv(n_init + topk + window + 1, kDecKeysPerSplit);
+int esa_decode_splits(int64_t batch, int64_t n_init, int64_t topk, int64_t window) {
+  const int64_t nk = n_init + topk + window + 1;
+  return (int)cdiv(nk, esa_decode_keys_per_split(batch, nk));
 }
 
 int64_t esa_keylist_len(int64_t n_init, int64_t topk, int64_t window, int64_t m) {
@@ -306,13 +333,14 @@ hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, c
                                   const int32_t* n_sel, float* po, float* pm, float* pl, void* out, float* lse,
                                   int64_t batch, int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t n_init,
                                   int64_t window, int topk, float scale, hipStream_t s) {
-  const int nsplit = esa_decode_splits(n_init, topk, window);
+  const int nsplit = esa_decode_splits(batch, n_init, topk, window);
+  const int kps = esa_decode_keys_per_split(batch, n_init + topk + window + 1);
   dim3 grid((unsigned)nsplit, (unsigned)batch);
   const float sl2 = scale * kLog2e;
   const int64_t E = H * D / 256;
 #define QAT_DEC(E_)                                                                                         \
   hipLaunchKernelGGL(esa_decode_attn_kernel<E_>, grid, dim3(256), 0, s, (const bf16*)q, (const bf16*)k,     \
-                     (const bf16*)v, sel, n_sel, po, pm, pl, H, D, ctx_len, c0, n_init, window, topk, nsplit, \
+                     (const bf16*)v, sel, n_sel, po, pm, pl, H, D, ctx_len, c0, n_init, window, topk, nsplit, kps, \
                      sl2)
   if (E == 8) QAT_DEC(8);
   else if (E == 16) QAT_DEC(16);
@@ -322,7 +350,7 @@ hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, c
   if (e != hipSuccess) return e;
   dim3 g2((unsigned)cdiv(H * D, 256), (unsigned)batch);
   hipLaunchKernelGGL(esa_decode_combine_kernel, g2, dim3(256), 0, s, po, pm, pl, n_sel, (bf16*)out, lse, H, D, c0,
-                     n_init, window, nsplit);
+                     n_init, window, nsplit, kps);
   return hipGetLastError();
 }
 

@@ -186,6 +186,8 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
   if (kvalid && h == 0) upart[(bi * nqsplit + blockIdx.y) * n_mid + key] = (float)total;
 }
 
+constexpr int kScanUnroll = 8;
+
 // ---------------------------------------------------------------------------
 // Decode scoring: s_j = <q~, k~_j> (float32) for every middle token, plus the
 // workgroup maxima. DC/8 lanes per key, 8 elements (16 B) per lane.
@@ -206,19 +208,33 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
   const int64_t k1 = min(n_mid, k0 + keys_per_wg);
   const bf16* kbase = kc + (bi * ctx_len + mid0) * DC;
   float mx = -__builtin_inff();
-  for (int64_t kb = k0; kb < k1; kb += KPW) {
-    const int64_t key = kb + tid / LPK;
-    float acc = 0.f;
-    if (key < k1) {
-      const bf16x8 kv = *(const bf16x8*)(kbase + key * DC + sub * 8);
+  // kScanUnroll keys per lane group in flight at once
+  constexpr int U = kScanUnroll;
+  for (int64_t kb = k0; kb < k1; kb += (int64_t)KPW * U) {
+    bf16x8 kv[U];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = fmaf(qv[j], (float)kv[j], acc);
+    for (int u = 0; u < U; ++u) {
+      const int64_t key = min(kb + (int64_t)u * KPW + tid / LPK, k1 - 1);
+      kv[u] = *(const bf16x8*)(kbase + key * DC + sub * 8);
+    }
+    float acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc[u] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[u] = fmaf(qv[j], (float)kv[u][j], acc[u]);
     }
 #pragma unroll
-    for (int off = 1; off < LPK; off <<= 1) acc += __shfl_xor(acc, off, 64);
-    if (key < k1) {
-      if (sub == 0) s_out[bi * n_mid + key] = acc;
-      mx = fmaxf(mx, acc);
+    for (int off = 1; off < LPK; off <<= 1)
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] += __shfl_xor(acc[u], off, 64);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t key = kb + (int64_t)u * KPW + tid / LPK;
+      if (key < k1) {
+        if (sub == 0) s_out[bi * n_mid + key] = acc[u];
+        mx = fmaxf(mx, acc[u]);
+      }
     }
   }
 #pragma unroll
