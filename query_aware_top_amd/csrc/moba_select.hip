@@ -102,6 +102,31 @@ __global__ void meanpool_finalize_kernel(const double* __restrict__ partial, int
 }
 
 // ---------------------------------------------------------------------------
+// Running top list, descending score. Candidates arrive in ascending block
+// order, so an equal score never displaces an earlier (smaller) block: the
+// candidate goes before the first entry it strictly exceeds and the entries
+// from there on shift down one slot (the scores are sorted, so "strictly
+// exceeds" is false up to the insertion point and true after it). -inf
+// candidates (not candidates of the row) never enter.
+template <int KMAX>
+__device__ __forceinline__ void top_insert(float (&tv)[KMAX], int (&ti)[KMAX], float cs, int cb) {
+  bool prev = false;
+  float pv = 0.f;
+  int pi = 0;
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    const bool b = cs > tv[i];
+    const float ov = tv[i];
+    const int oi = ti[i];
+    tv[i] = b ? (prev ? pv : cs) : ov;
+    ti[i] = b ? (prev ? pi : cb) : oi;
+    prev = b;
+    pv = ov;
+    pi = oi;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Scoring and selection: one thread per query row (t, h); a workgroup covers
 // 256 consecutive positions of one query head, so all its threads read the
 // same KV head's block means (staged in LDS, broadcast reads).
@@ -161,16 +186,7 @@ __global__ __launch_bounds__(256) void moba_score_select_kernel(
       }
       float cs = (a0 + a1) + (a2 + a3);
       int cb = (int)(c0 + bb);
-#pragma unroll
-      for (int i = 0; i < KMAX; ++i) {
-        const bool better = (cs > tv[i]) || (cs == tv[i] && cb < ti[i]);
-        const float sv = tv[i];
-        const int sb = ti[i];
-        tv[i] = better ? cs : sv;
-        ti[i] = better ? cb : sb;
-        cs = better ? sv : cs;
-        cb = better ? sb : cb;
-      }
+      top_insert<KMAX>(tv, ti, cs, cb);
     }
   }
   if (!valid) return;
@@ -306,16 +322,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void moba_select_mfma_kernel(
     for (int bb = 0; bb < kSelBlocks; ++bb) {
       float cs = bb < nmine ? scv[bb] : -__builtin_inff();
       int cb = (int)c0 + bb;
-#pragma unroll
-      for (int i = 0; i < KMAX; ++i) {
-        const bool better = (cs > tv[i]) | ((cs == tv[i]) & (cb < ti[i]));
-        const float sv = tv[i];
-        const int sbk = ti[i];
-        tv[i] = better ? cs : sv;
-        ti[i] = better ? cb : sbk;
-        cs = better ? sv : cs;
-        cb = better ? sbk : cb;
-      }
+      top_insert<KMAX>(tv, ti, cs, cb);
     }
   }
   if (!valid) return;
@@ -379,7 +386,8 @@ static hipError_t launch_select_d(const T* q, const float* kbar, int32_t* blk, i
   hipLaunchKernelGGL((moba_score_select_kernel<T, D, KM_>), grid, dim3(256), 0, s, q, kbar, blk, seq_len, \
                      hq, hkv, nbc, q_start, q_len, block, topk)
   if (km <= 1) QAT_SEL(1);
-  else if (km <= 3) QAT_SEL(3);
+  else if (km == 2) QAT_SEL(2);
+  else if (km == 3) QAT_SEL(3);
   else if (km <= 7) QAT_SEL(7);
   else QAT_SEL(15);
 #undef QAT_SEL
@@ -396,7 +404,8 @@ static hipError_t launch_select_mfma_d(const bf16* q, const bf16* planes, int64_
   hipLaunchKernelGGL((moba_select_mfma_kernel<D, KM_>), grid, dim3(kSelWaves * 64), 0, s, q, planes,       \
                      plane_stride, blk, seq_len, hq, hkv, nbc, q_start, q_len, block, topk)
   if (km <= 1) QAT_SEL(1);
-  else if (km <= 3) QAT_SEL(3);
+  else if (km == 2) QAT_SEL(2);
+  else if (km == 3) QAT_SEL(3);
   else if (km <= 7) QAT_SEL(7);
   else QAT_SEL(15);
 #undef QAT_SEL
