@@ -226,12 +226,19 @@ constexpr int kSelRowsPerWave = 64;
 constexpr int kSelBlocks = 32;   // blocks per round (one MFMA row tile)
 
 template <int D, int KMAX>
-__global__ __launch_bounds__(kSelWaves * 64) void moba_select_mfma_kernel(
+__global__ __launch_bounds__(kSelWaves * 64, 3) void moba_select_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ planes, int64_t plane_stride, int32_t* __restrict__ blk,
     int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk) {
   constexpr int KP = D + 8;   // padded LDS row of one block's mean
-  __shared__ __attribute__((aligned(16))) bf16 kb_s[3][kSelBlocks][KP];
-  __shared__ __attribute__((aligned(16))) float sc_s[kSelWaves][kSelRowsPerWave][kSelBlocks + 4];
+  // the block-mean planes and the score transposes share one LDS area (a
+  // barrier separates the last plane read from the first score write), so
+  // four workgroups fit on a CU
+  typedef bf16 PlaneT[kSelBlocks][KP];
+  typedef float ScoreT[kSelRowsPerWave][kSelBlocks + 4];
+  constexpr size_t kPlaneBytes = 3 * sizeof(PlaneT), kScoreBytes = kSelWaves * sizeof(ScoreT);
+  __shared__ __attribute__((aligned(16))) char s_area[kPlaneBytes > kScoreBytes ? kPlaneBytes : kScoreBytes];
+  PlaneT* kb_s = reinterpret_cast<PlaneT*>(s_area);
+  ScoreT* sc_s = reinterpret_cast<ScoreT*>(s_area);
   const int64_t bi = blockIdx.z;
   const int64_t h = blockIdx.y;
   const int64_t g = h / (hq / hkv);
@@ -299,6 +306,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void moba_select_mfma_kernel(
         sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qa[ks], sa, 0, 0, 0);
         sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sb, 0, 0, 0);
       }
+    __syncthreads();   // every wave's plane reads are done before scores overwrite them
     // C layout: lane holds query column lane%32, block rows 8*gi + 4*(lane/32) + 0..3
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
