@@ -200,7 +200,9 @@ int moba_block_select(const qat_moba_params* p, const void* q, const void* k, in
  * attends the union of its gated earlier blocks (whole), the causal part
  * [cur(t)*block, t] of its own block and, if window > 0, the keys
  * [max(0, t - window + 1), t]; one softmax per (t, h), each key once.
- * blk: as written by moba_block_select for the same q_start/q_len.
+ * blk: as written by moba_block_select for the same q_start/q_len (earlier
+ * blocks distinct and ahead of the current block; the last of the topk slots
+ * is taken for the current block and never attended as an earlier one).
  * out: [batch, q_len, Hq, d] (dtype); lse: [batch, q_len, Hq] float32 or NULL.
  */
 int moba_sparse_attn(const qat_moba_params* p, const void* q, const void* k, const void* v,

@@ -68,14 +68,16 @@ __global__ __launch_bounds__(128) void moba_generic_kernel(
     const int64_t off = ((bi * seq_len + pos) * hkv + g) * D;
     ra.key(k + off, v + off);
   };
+  // earlier blocks sit in the first topk - 1 slots (the last one is taken by
+  // the current block)
   auto gated = [&](int64_t b) {
-    for (int s = 0; s < topk; ++s)
+    for (int s = 0; s < topk - 1; ++s)
       if (br[s] == b) return true;
     return false;
   };
   // gated earlier blocks whole; window keys before the own block whose
   // block is not gated; the own block causally. Each key once.
-  for (int s = 0; s < topk; ++s) {
+  for (int s = 0; s < topk - 1; ++s) {
     const int32_t b = br[s];
     if (b < 0 || b >= cur) continue;
     for (int64_t p = (int64_t)b * block; p < (int64_t)(b + 1) * block; ++p) kv(p);

@@ -34,27 +34,40 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
 }
 
 // Dispatch keys: (row, slot) pairs whose gated block is an earlier block go
-// to bucket (sequence, KV head, block). Counting and scattering aggregate in
-// LDS per workgroup first (one global atomic per bucket and workgroup), since
-// strongly preferred blocks collect most rows of the sequence.
+// to bucket (sequence, KV head, block). One thread takes whole rows (the
+// row's head, position and block bounds are decoded once for all its slots,
+// in 32-bit arithmetic: rows < 2^27 and every index below fits in int32).
+// Counting and scattering aggregate in LDS per workgroup first (one global
+// atomic per bucket and workgroup), since strongly preferred blocks collect
+// most rows of the sequence. Gated lists are ascending with the current
+// block last among the valid entries, so earlier blocks sit in the first
+// topk - 1 slots; the last slot is never dispatched, which bounds the entry
+// and partial arrays at topk - 1 per row whatever the list holds.
 constexpr int kDispatchLdsBuckets = 4096;
+constexpr int kDispatchRowsPerThread = 8;
 
-__device__ __forceinline__ int64_t moba_bucket_of(const int32_t* __restrict__ blk, int64_t idx, int64_t hq,
-                                                  int64_t hkv, int64_t q_len, int64_t q_start, int block, int topk,
-                                                  int64_t nbc) {
-  const int64_t row = idx / topk;
-  const int32_t b = blk[idx];
-  const int64_t h = row % hq;
-  const int64_t r = (row / hq) % q_len;
-  const int64_t bi = row / (hq * q_len);
-  const int64_t cur = (q_start + r) / block;
-  if (b < 0 || b >= cur) return -1;
-  return (bi * hkv + h / (hq / hkv)) * nbc + b;
+struct MobaRowMap {
+  uint32_t hq, q_len, q_start, block, group, hkv, nbc, seq_len;
+};
+
+struct MobaRow {
+  int32_t bucket0;   // bucket of block 0 of the row's (sequence, KV head)
+  int32_t cur;       // the row's own block (attended by the current-block pass)
+  int32_t qrow;      // index of the row's query vector in q
+};
+
+__device__ __forceinline__ MobaRow moba_row(const MobaRowMap& m, uint32_t row) {
+  const uint32_t h = row % m.hq, t = row / m.hq;
+  const uint32_t r = t % m.q_len, bi = t / m.q_len;
+  MobaRow o;
+  o.cur = (int32_t)((m.q_start + r) / m.block);
+  o.bucket0 = (int32_t)((bi * m.hkv + h / m.group) * m.nbc);
+  o.qrow = (int32_t)((bi * m.seq_len + m.q_start + r) * m.hq + h);
+  return o;
 }
 
-__global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restrict__ blk, int64_t total, int64_t hq,
-                                                         int64_t hkv, int64_t q_len, int64_t q_start, int block,
-                                                         int topk, int64_t nbc, int64_t nbuckets,
+__global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restrict__ blk, int32_t nrows,
+                                                         MobaRowMap m, int topk, int32_t nbuckets,
                                                          int32_t* __restrict__ counts) {
   __shared__ int32_t loc[kDispatchLdsBuckets];
   const bool use_lds = nbuckets <= kDispatchLdsBuckets;
@@ -62,13 +75,16 @@ __global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restri
     for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = 0;
     __syncthreads();
   }
-  const int64_t per = (int64_t)blockDim.x * 16;
-  const int64_t i0 = (int64_t)blockIdx.x * per;
-  for (int64_t idx = i0 + threadIdx.x; idx < min(total, i0 + per); idx += blockDim.x) {
-    const int64_t bk = moba_bucket_of(blk, idx, hq, hkv, q_len, q_start, block, topk, nbc);
-    if (bk < 0) continue;
-    if (use_lds) atomicAdd(&loc[bk], 1);
-    else atomicAdd(&counts[bk], 1);
+  const int32_t r0 = blockIdx.x * (256 * kDispatchRowsPerThread);
+  const int32_t r1 = min(nrows, r0 + 256 * kDispatchRowsPerThread);
+  for (int32_t row = r0 + threadIdx.x; row < r1; row += 256) {
+    const MobaRow mr = moba_row(m, (uint32_t)row);
+    for (int s = 0; s < topk - 1; ++s) {
+      const int32_t b = blk[row * topk + s];
+      if (b < 0 || b >= mr.cur) continue;
+      if (use_lds) atomicAdd(&loc[mr.bucket0 + b], 1);
+      else atomicAdd(&counts[mr.bucket0 + b], 1);
+    }
   }
   if (use_lds) {
     __syncthreads();
@@ -77,22 +93,20 @@ __global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restri
   }
 }
 
-// Single workgroup: exclusive scans of the bucket counts and of their tile
-// counts, the tile table, scatter cursors and the number of tiles. A tile
-// descriptor is {low, high word of the element offset of its block's K/V
-// rows (the same for V), first entry, row count}.
-__global__ __launch_bounds__(1024) void moba_scan_kernel(const int32_t* __restrict__ counts, int64_t nb,
-                                                         int64_t nbc, int64_t hkv, int64_t seq_len, int block,
-                                                         int64_t d, int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ cursor, int4* __restrict__ tiles,
+// Exclusive prefix sums of the bucket sizes (entry offsets) and of their tile
+// counts; one workgroup, 1024 buckets per pass. `counts` is overwritten with
+// the tile prefix (counts[nb] = number of tiles), which the tile pass reads.
+__global__ __launch_bounds__(1024) void moba_scan_kernel(int32_t* __restrict__ counts, int32_t nb,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ cursor,
                                                          int32_t* __restrict__ ntiles) {
   __shared__ int32_t s_cnt[1024];
   __shared__ int32_t s_til[1024];
   __shared__ int32_t carry[2];
   if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; }
   __syncthreads();
-  for (int64_t base = 0; base < nb; base += 1024) {
-    const int64_t i = base + threadIdx.x;
+  for (int32_t base = 0; base < nb; base += 1024) {
+    const int32_t i = base + threadIdx.x;
     const int32_t c = i < nb ? counts[i] : 0;
     const int32_t tcount = (c + kRowsPerTile - 1) / kRowsPerTile;
     s_cnt[threadIdx.x] = c;
@@ -106,22 +120,52 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(const int32_t* __restri
       s_til[threadIdx.x] += b;
       __syncthreads();
     }
-    const int32_t ex_c = carry[0] + s_cnt[threadIdx.x] - c;
-    const int32_t ex_t = carry[1] + s_til[threadIdx.x] - tcount;
     if (i < nb) {
+      const int32_t ex_c = carry[0] + s_cnt[threadIdx.x] - c;
       offsets[i] = ex_c;
       cursor[i] = ex_c;
-      const int64_t b = i % nbc, g = (i / nbc) % hkv, bi = i / (nbc * hkv);
-      const int64_t kv = ((bi * seq_len + b * block) * hkv + g) * d;
-      for (int32_t j = 0; j < tcount; ++j)
-        tiles[ex_t + j] = make_int4((int)(uint32_t)kv, (int)(kv >> 32), ex_c + j * kRowsPerTile,
-                                    min(kRowsPerTile, c - j * kRowsPerTile));
+      counts[i] = carry[1] + s_til[threadIdx.x] - tcount;
     }
     __syncthreads();
     if (threadIdx.x == 1023) { carry[0] += s_cnt[1023]; carry[1] += s_til[1023]; }
     __syncthreads();
   }
-  if (threadIdx.x == 0) { offsets[nb] = carry[0]; ntiles[0] = carry[1]; }
+  if (threadIdx.x == 0) {
+    offsets[nb] = carry[0];
+    counts[nb] = carry[1];
+    ntiles[0] = carry[1];
+  }
+}
+
+// Tile table, one thread per tile: the tile's bucket is the last one whose
+// first tile is not after it (binary search over the tile prefix, staged in
+// LDS when it fits). Tiles of one bucket stay adjacent and in order.
+__global__ __launch_bounds__(256) void moba_tiles_kernel(const int32_t* __restrict__ tile_off, int32_t nb,
+                                                         const int32_t* __restrict__ offsets, int32_t nbc,
+                                                         int32_t hkv, int64_t seq_len, int block, int64_t d,
+                                                         int4* __restrict__ tiles) {
+  __shared__ int32_t s_off[kDispatchLdsBuckets + 1];
+  const int32_t nt = tile_off[nb];
+  const int32_t t = blockIdx.x * 256 + threadIdx.x;
+  if ((int32_t)(blockIdx.x * 256) >= nt) return;   // uniform per workgroup
+  const bool use_lds = nb <= kDispatchLdsBuckets;
+  if (use_lds) {
+    for (int i = threadIdx.x; i <= nb; i += 256) s_off[i] = tile_off[i];
+    __syncthreads();
+  }
+  if (t >= nt) return;
+  const int32_t* off = use_lds ? s_off : tile_off;
+  int32_t lo = 0, hi = nb - 1;   // invariant: off[lo] <= t, and off[hi + 1] > t
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  const int32_t i = lo, j = t - off[i];
+  const int32_t e0 = offsets[i], c = offsets[i + 1] - e0;
+  const int64_t b = i % nbc, g = (i / nbc) % hkv, bi = i / (nbc * hkv);
+  const int64_t kv = ((bi * seq_len + b * block) * hkv + g) * d;
+  tiles[t] = make_int4((int)(uint32_t)kv, (int)(kv >> 32), e0 + j * kRowsPerTile, min(kRowsPerTile, c - j * kRowsPerTile));
 }
 
 // (row, slot) -> entries[...] = {row * 16 + slot, index of the row's query
@@ -129,23 +173,24 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(const int32_t* __restri
 // range per bucket with a single global atomic and places its entries with
 // LDS atomics (the order inside a bucket is irrelevant: every row's result is
 // independent of the other rows sharing its tile).
-__global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __restrict__ blk, int64_t total,
-                                                           int64_t hq, int64_t hkv, int64_t q_len, int64_t q_start,
-                                                           int block, int topk, int64_t nbc, int64_t nbuckets,
-                                                           int64_t seq_len, int32_t* __restrict__ cursor,
+__global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __restrict__ blk, int32_t nrows,
+                                                           MobaRowMap m, int topk, int32_t nbuckets,
+                                                           int32_t* __restrict__ cursor,
                                                            int2* __restrict__ entries) {
   __shared__ int32_t loc[kDispatchLdsBuckets];
   __shared__ int32_t base_of[kDispatchLdsBuckets];
   const bool use_lds = nbuckets <= kDispatchLdsBuckets;
-  const int64_t per = (int64_t)blockDim.x * 16;
-  const int64_t i0 = (int64_t)blockIdx.x * per;
-  const int64_t i1 = min(total, i0 + per);
+  const int32_t r0 = blockIdx.x * (256 * kDispatchRowsPerThread);
+  const int32_t r1 = min(nrows, r0 + 256 * kDispatchRowsPerThread);
   if (use_lds) {
     for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = 0;
     __syncthreads();
-    for (int64_t idx = i0 + threadIdx.x; idx < i1; idx += blockDim.x) {
-      const int64_t bk = moba_bucket_of(blk, idx, hq, hkv, q_len, q_start, block, topk, nbc);
-      if (bk >= 0) atomicAdd(&loc[bk], 1);
+    for (int32_t row = r0 + threadIdx.x; row < r1; row += 256) {
+      const MobaRow mr = moba_row(m, (uint32_t)row);
+      for (int s = 0; s < topk - 1; ++s) {
+        const int32_t b = blk[row * topk + s];
+        if (b >= 0 && b < mr.cur) atomicAdd(&loc[mr.bucket0 + b], 1);
+      }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) {
@@ -154,13 +199,15 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __rest
     }
     __syncthreads();
   }
-  for (int64_t idx = i0 + threadIdx.x; idx < i1; idx += blockDim.x) {
-    const int64_t bk = moba_bucket_of(blk, idx, hq, hkv, q_len, q_start, block, topk, nbc);
-    if (bk < 0) continue;
-    const int32_t pos = use_lds ? base_of[bk] + atomicAdd(&loc[bk], 1) : atomicAdd(&cursor[bk], 1);
-    const int64_t row = idx / topk;
-    const int64_t h = row % hq, r = (row / hq) % q_len, bi = row / (hq * q_len);
-    entries[pos] = make_int2((int32_t)(row * 16 + idx % topk), (int32_t)((bi * seq_len + q_start + r) * hq + h));
+  for (int32_t row = r0 + threadIdx.x; row < r1; row += 256) {
+    const MobaRow mr = moba_row(m, (uint32_t)row);
+    for (int s = 0; s < topk - 1; ++s) {
+      const int32_t b = blk[row * topk + s];
+      if (b < 0 || b >= mr.cur) continue;
+      const int32_t bk = mr.bucket0 + b;
+      const int32_t pos = use_lds ? base_of[bk] + atomicAdd(&loc[bk], 1) : atomicAdd(&cursor[bk], 1);
+      entries[pos] = make_int2(row * 16 + s, mr.qrow);
+    }
   }
 }
 
@@ -526,22 +573,28 @@ hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_l
                                 int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int64_t nbc,
                                 int32_t* counts, int32_t* offsets, int32_t* cursor, int2* entries, int4* tiles,
                                 int32_t* ntiles, hipStream_t s) {
-  const int64_t total = batch * q_len * hq * topk;
+  const int64_t nrows = batch * q_len * hq;
   const int64_t nbuckets = batch * hkv * nbc;
+  const MobaRowMap m{(uint32_t)hq, (uint32_t)q_len, (uint32_t)q_start, (uint32_t)block, (uint32_t)(hq / hkv),
+                     (uint32_t)hkv, (uint32_t)nbc, (uint32_t)seq_len};
   hipError_t e = launch_fill_i32(counts, nbuckets, 0, s);
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)cdiv(total, 256 * 16);
+  const unsigned grid = (unsigned)cdiv(nrows, 256 * kDispatchRowsPerThread);
   if (nbuckets > 0) {
-    hipLaunchKernelGGL(moba_count_kernel, dim3(grid), dim3(256), 0, s, blk, total, hq, hkv, q_len, q_start, block,
-                       topk, nbc, nbuckets, counts);
+    hipLaunchKernelGGL(moba_count_kernel, dim3(grid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
+                       (int32_t)nbuckets, counts);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(moba_scan_kernel, dim3(1), dim3(1024), 0, s, counts, nbuckets, nbc, hkv, seq_len, block, d,
-                     offsets, cursor, tiles, ntiles);
+  hipLaunchKernelGGL(moba_scan_kernel, dim3(1), dim3(1024), 0, s, counts, (int32_t)nbuckets, offsets, cursor,
+                     ntiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (nbuckets > 0) {
-    hipLaunchKernelGGL(moba_scatter_kernel, dim3(grid), dim3(256), 0, s, blk, total, hq, hkv, q_len, q_start,
-                       block, topk, nbc, nbuckets, seq_len, cursor, entries);
+    const int64_t max_tiles = moba_max_tiles(nrows, topk, nbuckets);
+    hipLaunchKernelGGL(moba_tiles_kernel, dim3((unsigned)cdiv(max_tiles, 256)), dim3(256), 0, s, counts,
+                       (int32_t)nbuckets, offsets, (int32_t)nbc, (int32_t)hkv, seq_len, block, d, tiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(moba_scatter_kernel, dim3(grid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
+                       (int32_t)nbuckets, cursor, entries);
     e = hipGetLastError();
   }
   return e;
