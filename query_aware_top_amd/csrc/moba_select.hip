@@ -355,6 +355,189 @@ __global__ __launch_bounds__(kSelWaves * 64, 3) void moba_select_mfma_kernel(
   for (int i = npick + 1; i < topk; ++i) out[i] = -1;
 }
 
+
+// Resident variant for up to kSelLdsBytes of block means: a workgroup serves
+// one (sequence, KV head) and stages the three planes of every block its rows
+// can gate in LDS once; after that its waves run without barriers, each over
+// its own strided list of 64-row chunks (chunk c = 64-row slice c / (Hq/Hkv)
+// of query head c % (Hq/Hkv) of the group), loading the next chunk's queries
+// while it ranks the current one's blocks. The scores stay in the accumulators: the
+// lane of query column j holds 16 of each 32 blocks (rows 8gi + 4(lane/32) +
+// 0..3), builds a top list over those in ascending block order for both of
+// its query columns, and the two half-waves then trade the lists so that
+// each lane merges the two halves of one query's candidates. The merge uses
+// the full (score desc, block asc) order, so the result equals one pass of
+// ordered insertion over all blocks.
+constexpr int kSelPWaves = 4;
+constexpr int kSelLdsBytes = 53248;   // three workgroups per CU
+
+template <int KMAX>
+__device__ __forceinline__ void top_merge(float (&tv)[KMAX], int (&ti)[KMAX], float cs, int cb) {
+  bool prev = false;
+  float pv = 0.f;
+  int pi = 0;
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    const bool b = cs > tv[i] || (cs == tv[i] && cb < ti[i]);
+    const float ov = tv[i];
+    const int oi = ti[i];
+    tv[i] = b ? (prev ? pv : cs) : ov;
+    ti[i] = b ? (prev ? pi : cb) : oi;
+    prev = b;
+    pv = ov;
+    pi = oi;
+  }
+}
+
+__device__ __forceinline__ uint32_t sel_swap_halves(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return r[0] ^ r[1] ^ x;   // the value of lane (l + 32) mod 64
+}
+
+template <int D, int KMAX>
+__global__ __launch_bounds__(kSelPWaves * 64, KMAX >= 7 ? 2 : 3) void moba_select_resident_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ planes, int64_t plane_stride, int32_t* __restrict__ blk,
+    int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk,
+    int nb_lds) {
+  constexpr int KP = D + 8;   // padded LDS row of one block's mean
+  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
+  bf16* kb_s = reinterpret_cast<bf16*>(s_dyn);   // [3][nb_lds][KP]
+  const int64_t bi = blockIdx.y / hkv, g = blockIdx.y % hkv;
+  const int64_t gs = hq / hkv;
+  const int km = topk - 1;
+  {
+    const bf16* pg = planes + ((bi * nbc) * hkv + g) * D;
+    const int pieces = 3 * nb_lds * (D / 8);
+    constexpr int U = 8;
+    for (int i0 = threadIdx.x; i0 < pieces; i0 += U * kSelPWaves * 64) {
+      bf16x8 pc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {   // clamped index: every load is in bounds, all in flight at once
+        const int i = min(i0 + u * kSelPWaves * 64, pieces - 1);
+        const int pl = i / (nb_lds * (D / 8)), rem = i % (nb_lds * (D / 8));
+        pc[u] = *(const bf16x8*)(pg + pl * plane_stride + (int64_t)(rem / (D / 8)) * hkv * D + (rem % (D / 8)) * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kSelPWaves * 64;
+        if (i < pieces) {
+          const int pl = i / (nb_lds * (D / 8)), rem = i % (nb_lds * (D / 8));
+          *(bf16x8*)&kb_s[(pl * nb_lds + rem / (D / 8)) * KP + (rem % (D / 8)) * 8] = pc[u];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int64_t nchunks = gs * ((q_len + 63) / 64);
+  const int64_t stride = (int64_t)gridDim.x * kSelPWaves;
+  auto load_q = [&](int64_t c, bf16x8 (&xa)[D / 16], bf16x8 (&xb)[D / 16]) {
+    const int64_t rc = c / gs, h = g * gs + c % gs;
+    const int64_t ra = min(rc * 64 + l32, q_len - 1), rb = min(rc * 64 + 32 + l32, q_len - 1);
+    const bf16* pa = q + ((bi * seq_len + q_start + ra) * hq + h) * D + hl * 8;
+    const bf16* pb = q + ((bi * seq_len + q_start + rb) * hq + h) * D + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      xa[ks] = *(const bf16x8*)(pa + ks * 16);
+      xb[ks] = *(const bf16x8*)(pb + ks * 16);
+    }
+  };
+  int64_t c = (int64_t)blockIdx.x * kSelPWaves + wave;
+  bf16x8 qa[D / 16], qb[D / 16];
+  if (c < nchunks) load_q(c, qa, qb);
+  for (; c < nchunks; c += stride) {
+    const bool more = c + stride < nchunks;
+    // positions and block indices fit in 32 bits (seq_len < 2^31)
+    const int rc = (int)(c / gs), h = (int)(g * gs + c % gs);
+    const int ra = rc * 64 + l32, rb = ra + 32;   // query columns of the two score tiles
+    const int ql = (int)q_len, qs = (int)q_start;
+    const int cur_a = (qs + min(ra, ql - 1)) / block;
+    const int cur_b = (qs + min(rb, ql - 1)) / block;
+    const int t_last = qs + min(ql, rc * 64 + 64) - 1;
+    const int nbr = km > 0 ? min((int)nbc, t_last / block) : 0;   // <= nb_lds
+    float tva[KMAX], tvb[KMAX];
+    int tia[KMAX], tib[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      tva[i] = tvb[i] = -__builtin_inff();
+      tia[i] = tib[i] = 0x7fffffff;
+    }
+    for (int c0 = 0; c0 < nbr; c0 += 32) {
+      const bf16* arow = kb_s + min(c0 + l32, nb_lds - 1) * KP + hl * 8;
+      f32x16 sa = {}, sb = {};
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8 a = *(const bf16x8*)(arow + pl * nb_lds * KP + ks * 16);
+          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qa[ks], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sb, 0, 0, 0);
+        }
+      // plane reads run three fragments ahead of the matrix ops using them
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int i = 0; i < 3 * (D / 16) - 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+      // the next chunk's queries replace these once the last round's matrix
+      // ops have read them: their loads overlap the selection work below
+      if (c0 + 32 >= nbr && more) load_q(c + stride, qa, qb);
+      // blocks c0 + bb with bb >= n are not candidates of the column's row
+      const int n_a = cur_a - c0, n_b = cur_b - c0;
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int bb = gi * 8 + hl * 4 + i;
+          top_insert<KMAX>(tva, tia, bb < n_a ? sa[4 * gi + i] : -__builtin_inff(), c0 + bb);
+          top_insert<KMAX>(tvb, tib, bb < n_b ? sb[4 * gi + i] : -__builtin_inff(), c0 + bb);
+        }
+    }
+    if (nbr <= 0 && more) load_q(c + stride, qa, qb);
+    // lane l < 32 keeps query ra (its list of column a), lane l + 32 keeps
+    // query rb; each receives the other half's list of its query
+    float ov[KMAX], rv[KMAX];
+    int oi[KMAX], ri[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      ov[i] = hl ? tvb[i] : tva[i];
+      oi[i] = hl ? tib[i] : tia[i];
+      rv[i] = __builtin_bit_cast(float, sel_swap_halves(__builtin_bit_cast(uint32_t, hl ? tva[i] : tvb[i])));
+      ri[i] = (int)sel_swap_halves((uint32_t)(hl ? tia[i] : tib[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) top_merge<KMAX>(ov, oi, rv[i], ri[i]);
+
+    const int r = hl ? rb : ra;
+    if (r < ql) {
+      const int cur = hl ? cur_b : cur_a;
+      const int npick = min(km, cur);
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i)
+        if (i >= npick) oi[i] = 0x7fffffff;
+#pragma unroll
+      for (int a = 0; a < KMAX; ++a)
+#pragma unroll
+        for (int b2 = 0; b2 + 1 < KMAX - a; ++b2) {
+          const int lo = min(oi[b2], oi[b2 + 1]);
+          const int hi = max(oi[b2], oi[b2 + 1]);
+          oi[b2] = lo;
+          oi[b2 + 1] = hi;
+        }
+      int32_t* out = blk + ((bi * q_len + r) * hq + h) * topk;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i)
+        if (i < npick) out[i] = oi[i];
+      out[npick] = cur;
+      for (int i = npick + 1; i < topk; ++i) out[i] = -1;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 int meanpool_tokens_per_split(int block) {
   // 64-token slices for blocks up to 2048 tokens, at most 32 slices beyond
@@ -406,8 +589,29 @@ template <int D>
 static hipError_t launch_select_mfma_d(const bf16* q, const bf16* planes, int64_t plane_stride, int32_t* blk,
                                        int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc,
                                        int64_t q_start, int64_t q_len, int block, int topk, hipStream_t s) {
-  dim3 grid((unsigned)cdiv(q_len, kSelWaves * kSelRowsPerWave), (unsigned)hq, (unsigned)batch);
   const int km = topk - 1;
+  // blocks any row can gate: 0 .. (last position) / block - 1
+  const int64_t nb_gate = std::min<int64_t>(nbc, (q_start + q_len - 1) / block);
+  const size_t lds = (size_t)3 * nb_gate * (D + 8) * sizeof(bf16);
+  if (lds <= (size_t)kSelLdsBytes && batch * hkv <= 65535) {
+    const int64_t nchunks = (hq / hkv) * cdiv(q_len, 64);
+    // three resident workgroups per CU over 256 CUs, shared by the groups
+    const int64_t per_group = std::max<int64_t>(
+        1, std::min<int64_t>(cdiv(768, batch * hkv), cdiv(nchunks, kSelPWaves)));
+    dim3 rgrid((unsigned)per_group, (unsigned)(batch * hkv));
+    const size_t lds_launch = std::max<size_t>(lds, 16);
+#define QAT_SELR(KM_)                                                                                      \
+  hipLaunchKernelGGL((moba_select_resident_kernel<D, KM_>), rgrid, dim3(kSelPWaves * 64), lds_launch, s, q, \
+                     planes, plane_stride, blk, seq_len, hq, hkv, nbc, q_start, q_len, block, topk, (int)nb_gate)
+    if (km <= 1) QAT_SELR(1);
+    else if (km == 2) QAT_SELR(2);
+    else if (km == 3) QAT_SELR(3);
+    else if (km <= 7) QAT_SELR(7);
+    else QAT_SELR(15);
+#undef QAT_SELR
+    return hipGetLastError();
+  }
+  dim3 grid((unsigned)cdiv(q_len, kSelWaves * kSelRowsPerWave), (unsigned)hq, (unsigned)batch);
 #define QAT_SEL(KM_)                                                                                        \
   hipLaunchKernelGGL((moba_select_mfma_kernel<D, KM_>), grid, dim3(kSelWaves * 64), 0, s, q, planes,       \
                      plane_stride, blk, seq_len, hq, hkv, nbc, q_start, q_len, block, topk)
