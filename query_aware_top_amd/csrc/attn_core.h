@@ -186,6 +186,16 @@ __device__ __forceinline__ void fa_wait_loads() {
   asm volatile("" ::: "memory");
 }
 
+// Waits until at most N vector memory operations of the wave are outstanding
+// (the N most recently issued ones may still be in flight).
+template <int N>
+__device__ __forceinline__ void fa_wait_loads_keep() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier for LDS hand-offs only: the wave's LDS operations are
 // complete when it arrives (lgkmcnt), but its global stores are not waited
 // for (a __syncthreads would wait for every outstanding memory operation).

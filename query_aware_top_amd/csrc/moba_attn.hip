@@ -14,6 +14,7 @@
 // current-block kernel then runs causal attention over each row's own block
 // on plain token tiles and folds the row's partials in by log-sum-exp merge.
 #include <algorithm>
+#include <type_traits>
 
 #include "attn_core.h"
 #include "common.h"
@@ -322,101 +323,137 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_persist_kernel(
     }
   };
 
-  Tile t_cur = tile_at(item);
-  Entry e_cur = entry_of(t_cur);
-  Tile t_nxt = tile_at(item + G < n_items ? item + G : item);
-  FaState<D> st;
-  fa_init<D>(st, q, false);
-  load_q(st, e_cur);
-  {
-    const int64_t kv = t_cur.kv;
-    issue(sm.k0, k + kv, 0);
-    issue(sm.v0, v + kv, 0);
-    issue(sm.k1, k + kv, kKT);
-    issue(sm.v1, v + kv, kKT);
-  }
-  auto ok = [](int) { return true; };
-  // A tile's partial output is written at the top of the next tile, once
-  // that tile's first K/V and query rows have been waited for: writes are
-  // never waited on by the wait that guards those loads.
-  auto epilogue = [&](const Entry& e) {
-    float inv_l, lse;
-    fa_finish<D>(st, inv_l, lse);
-    const bool mine = e.rs >= 0;
-    const int64_t pidx = mine ? (int64_t)(e.rs >> 4) * km + (e.rs & 15) : 0;
-    if ((lane >> 5) == 0 && mine) part_lse[pidx] = lse;
-    const int wv = threadIdx.x >> 6;
-    fa_store_rows_staged<D>(st, inv_l, s_stage + wv * 32 * (D + 8), s_rows + wv * 32, mine ? pidx : -1, part_o);
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.o[t][i] = 0.f;
-    st.m = -__builtin_inff();
-    st.l = 0.f;
-  };
-  bool pending = false;
-  Entry e_prev = e_cur;
-  while (true) {
-    const int nxt_item = item + G;
-    const bool has_next = nxt_item < n_items;
-    const int64_t kv = t_cur.kv;
-    const bf16* kb = k + kv;
-    const bf16* vb = v + kv;
-    // K0, V0, K1, V1 and the query rows are in flight
-    fa_wait_loads();
-    fa_lds_barrier();
-    if (pending) epilogue(e_prev);
-    // the next tile's descriptors, first used at this tile's last pair (no
-    // select on the loaded values: that would wait for them right here; when
-    // there is no next tile, t_nxt repeats the current one and e_nxt is unused)
-    const Entry e_nxt = entry_of(t_nxt);
-    const Tile t_nn = tile_at(nxt_item + G < n_items ? nxt_item + G : item);
-    f32x16 s_cur[2], s_nxt[2];
-    fa_scores<D>(st, sm.k0, s_cur);
-    fa_lds_barrier();
-    if (nt > 2) issue(sm.k0, kb, 2 * kKT);
-    for (int j = 0; j + 2 < nt; j += 2) {
-      fa_scores<D>(st, sm.k1, s_nxt);
-      fa_finish_tile<D, false>(st, s_cur, sm.v0, scale_log2, j * kKT, block, ok, ok);
-      fa_wait_loads();
+  // The item loop exists twice, one copy per issue order (the copies hit
+  // the same barriers in the same sequence); each wave runs one of them.
+  auto run = [&](auto late_c) {
+    constexpr bool kLate = decltype(late_c)::value;
+    Tile t_cur = tile_at(item);
+    Entry e_cur = entry_of(t_cur);
+    Tile t_nxt = tile_at(item + G < n_items ? item + G : item);
+    FaState<D> st;
+    fa_init<D>(st, q, false);
+    load_q(st, e_cur);
+    {
+      const int64_t kv = t_cur.kv;
+      issue(sm.k0, k + kv, 0);
+      issue(sm.k1, k + kv, kKT);
+      issue(sm.v0, v + kv, 0);
+      issue(sm.v1, v + kv, kKT);
+    }
+    // load instructions of one tile per wave: the waits below leave that many
+    // (the most recent tile) in flight
+    constexpr int kNI = FaContig<D, kNW>::NI;
+    auto ok = [](int) { return true; };
+    // A tile's partial output is written at the top of the next tile, once
+    // that tile's first K/V and query rows have been waited for: writes are
+    // never waited on by the wait that guards those loads.
+    auto epilogue = [&](const Entry& e) {
+      float inv_l, lse;
+      fa_finish<D>(st, inv_l, lse);
+      const bool mine = e.rs >= 0;
+      const int64_t pidx = mine ? (int64_t)(e.rs >> 4) * km + (e.rs & 15) : 0;
+      if ((lane >> 5) == 0 && mine) part_lse[pidx] = lse;
+      const int wv = threadIdx.x >> 6;
+      fa_store_rows_staged<D>(st, inv_l, s_stage + wv * 32 * (D + 8), s_rows + wv * 32, mine ? pidx : -1, part_o);
+  #pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) st.o[t][i] = 0.f;
+      st.m = -__builtin_inff();
+      st.l = 0.f;
+    };
+    // Per tile: the scores of the next tile (matrix cores) and the softmax of
+    // this one (vector ALUs) are independent; the two waves that share a SIMD
+    // (waves w and w + kNW/2) issue them in opposite orders, so that one
+    // wave's matrix ops run under the other's vector work; then O += P V.
+    auto step = [&](const bf16* ks_next, f32x16* s_next, f32x16* s_now, const bf16* vs) {
+      u32x4 pw[4];
+      if constexpr (kLate) {
+        fa_softmax<D, false>(st, s_now, pw, scale_log2);
+        fa_scores<D>(st, ks_next, s_next);
+      } else {
+        fa_scores<D>(st, ks_next, s_next);
+        fa_softmax<D, false>(st, s_now, pw, scale_log2);
+      }
+      fa_pv<D>(st, vs, pw);
+    };
+    bool pending = false;
+    Entry e_prev = e_cur;
+    while (true) {
+      const int nxt_item = item + G;
+      const bool has_next = nxt_item < n_items;
+      const int64_t kv = t_cur.kv;
+      const bf16* kb = k + kv;
+      const bf16* vb = v + kv;
+      // the query rows, K0, K1, V0 and (last) V1 are in flight: V1 is not
+      // needed before the first pair and stays in flight
+      fa_wait_loads_keep<kNI>();
       fa_lds_barrier();
-      issue(sm.k1, kb, (j + 3) * kKT);
-      issue(sm.v0, vb, (j + 2) * kKT);
+      if (pending) epilogue(e_prev);
+      // the next tile's descriptors, first used at this tile's last pair (no
+      // select on the loaded values: that would wait for them right here; when
+      // there is no next tile, t_nxt repeats the current one and e_nxt is unused)
+      const Entry e_nxt = entry_of(t_nxt);
+      const Tile t_nn = tile_at(nxt_item + G < n_items ? nxt_item + G : item);
+      f32x16 s_cur[2], s_nxt[2];
       fa_scores<D>(st, sm.k0, s_cur);
-      fa_finish_tile<D, false>(st, s_nxt, sm.v1, scale_log2, (j + 1) * kKT, block, ok, ok);
-      fa_wait_loads();
       fa_lds_barrier();
-      if (j + 4 < nt) issue(sm.k0, kb, (j + 4) * kKT);
-      issue(sm.v1, vb, (j + 3) * kKT);
+      const int64_t kv_n = t_nxt.kv;
+      // K0 of the next tile goes into buffer k0 as soon as the buffer is free,
+      // after every load that this tile still waits for
+      if (nt > 2) {
+        issue(sm.k0, kb, 2 * kKT);
+        int j = 0;
+        do {   // at least one pair (a do loop, so the waits in it cover every path to the last pair)
+          step(sm.k1, s_nxt, s_cur, sm.v0);
+          fa_wait_loads();
+          fa_lds_barrier();
+          issue(sm.k1, kb, (j + 3) * kKT);
+          issue(sm.v0, vb, (j + 2) * kKT);
+          step(sm.k0, s_cur, s_nxt, sm.v1);
+          fa_wait_loads();
+          fa_lds_barrier();
+          issue(sm.v1, vb, (j + 3) * kKT);
+          if (j + 4 < nt) issue(sm.k0, kb, (j + 4) * kKT);
+          else if (has_next) issue(sm.k0, k + kv_n, 0);
+          j += 2;
+        } while (j + 2 < nt);
+      } else {
+        // no pair loop: everything this tile still needs (V1, the
+        // descriptors) is waited for here, so that only K0 of the next tile
+        // is in flight where the paths join
+        fa_wait_loads();
+        if (has_next) issue(sm.k0, k + kv_n, 0);
+      }
+      // last pair: tiles nt-2 (V in v0) and nt-1 (K in k1, V in v1)
+      step(sm.k1, s_nxt, s_cur, sm.v0);
+      if (has_next) fa_wait_loads_keep<kNI>();   // the next tile's K0 (issued last) stays in flight
+      else fa_wait_loads();
+      fa_lds_barrier();
+      // every K tile is scored and V_{nt-2} consumed: k1, v0 and the query
+      // registers are free for the next tile
+      if (has_next) {
+        issue(sm.k1, k + kv_n, kKT);
+        issue(sm.v0, v + kv_n, 0);
+        load_q(st, e_nxt);
+      }
+      fa_finish_tile<D, false>(st, s_nxt, sm.v1, scale_log2, (nt - 1) * kKT, block, ok, ok);
+      if (!has_next) {
+        epilogue(e_cur);
+        break;
+      }
+      fa_lds_barrier();   // every wave is done with V_{nt-1}
+      issue(sm.v1, v + kv_n, kKT);
+      pending = true;
+      e_prev = e_cur;
+      t_cur = t_nxt;
+      e_cur = e_nxt;
+      t_nxt = t_nn;
+      item = nxt_item;
     }
-    // last pair: tiles nt-2 (V in v0) and nt-1 (K in k1, V in v1)
-    fa_scores<D>(st, sm.k1, s_nxt);
-    fa_finish_tile<D, false>(st, s_cur, sm.v0, scale_log2, (nt - 2) * kKT, block, ok, ok);
-    fa_wait_loads();
-    fa_lds_barrier();
-    // every K tile is scored and V_{nt-2} consumed: k0, k1, v0 and the query
-    // registers are free for the next tile
-    const int64_t kv_n = t_nxt.kv;
-    if (has_next) {
-      issue(sm.k0, k + kv_n, 0);
-      issue(sm.k1, k + kv_n, kKT);
-      issue(sm.v0, v + kv_n, 0);
-      load_q(st, e_nxt);
-    }
-    fa_finish_tile<D, false>(st, s_nxt, sm.v1, scale_log2, (nt - 1) * kKT, block, ok, ok);
-    if (!has_next) {
-      epilogue(e_cur);
-      break;
-    }
-    fa_lds_barrier();   // every wave is done with V_{nt-1}
-    issue(sm.v1, v + kv_n, kKT);
-    pending = true;
-    e_prev = e_cur;
-    t_cur = t_nxt;
-    e_cur = e_nxt;
-    t_nxt = t_nn;
-    item = nxt_item;
-  }
+  };
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kNW / 2) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // Current-block attention (causal) merged with the row's past-block
