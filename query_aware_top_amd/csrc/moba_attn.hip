@@ -67,6 +67,43 @@ __device__ __forceinline__ MobaRow moba_row(const MobaRowMap& m, uint32_t row) {
   return o;
 }
 
+// Calls f(row, slot, row descriptor, block) for every dispatched (row, slot)
+// pair among this thread's rows. The gated lists of four rows (their first
+// four slots) are loaded together, from clamped in-bounds indices, before
+// any of them is used, so that the loads overlap.
+template <typename F>
+__device__ __forceinline__ void moba_for_each_pair(const int32_t* __restrict__ blk, int32_t r0, int32_t r1,
+                                                   const MobaRowMap& m, int topk, F f) {
+  constexpr int RB = 4, SB = 4;
+  const int km = topk - 1;   // >= 1
+#pragma unroll 1
+  for (int k0 = 0; k0 < kDispatchRowsPerThread; k0 += RB) {
+    int32_t bv[RB][SB];
+    int32_t rows[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      rows[i] = r0 + (int32_t)threadIdx.x + (k0 + i) * 256;
+      const int32_t rc = min(rows[i], r1 - 1);
+#pragma unroll
+      for (int s = 0; s < SB; ++s) bv[i][s] = blk[rc * topk + min(s, km - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if (rows[i] >= r1) continue;
+      const MobaRow mr = moba_row(m, (uint32_t)rows[i]);
+#pragma unroll
+      for (int s = 0; s < SB; ++s) {
+        const int32_t b = bv[i][s];
+        if (s < km && b >= 0 && b < mr.cur) f(rows[i], s, mr, b);
+      }
+      for (int s = SB; s < km; ++s) {
+        const int32_t b = blk[rows[i] * topk + s];
+        if (b >= 0 && b < mr.cur) f(rows[i], s, mr, b);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restrict__ blk, int32_t nrows,
                                                          MobaRowMap m, int topk, int32_t nbuckets,
                                                          int32_t* __restrict__ counts) {
@@ -78,15 +115,10 @@ __global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restri
   }
   const int32_t r0 = blockIdx.x * (256 * kDispatchRowsPerThread);
   const int32_t r1 = min(nrows, r0 + 256 * kDispatchRowsPerThread);
-  for (int32_t row = r0 + threadIdx.x; row < r1; row += 256) {
-    const MobaRow mr = moba_row(m, (uint32_t)row);
-    for (int s = 0; s < topk - 1; ++s) {
-      const int32_t b = blk[row * topk + s];
-      if (b < 0 || b >= mr.cur) continue;
-      if (use_lds) atomicAdd(&loc[mr.bucket0 + b], 1);
-      else atomicAdd(&counts[mr.bucket0 + b], 1);
-    }
-  }
+  moba_for_each_pair(blk, r0, r1, m, topk, [&](int32_t, int, const MobaRow& mr, int32_t b) {
+    if (use_lds) atomicAdd(&loc[mr.bucket0 + b], 1);
+    else atomicAdd(&counts[mr.bucket0 + b], 1);
+  });
   if (use_lds) {
     __syncthreads();
     for (int i = threadIdx.x; i < nbuckets; i += blockDim.x)
@@ -186,13 +218,8 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __rest
   if (use_lds) {
     for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = 0;
     __syncthreads();
-    for (int32_t row = r0 + threadIdx.x; row < r1; row += 256) {
-      const MobaRow mr = moba_row(m, (uint32_t)row);
-      for (int s = 0; s < topk - 1; ++s) {
-        const int32_t b = blk[row * topk + s];
-        if (b >= 0 && b < mr.cur) atomicAdd(&loc[mr.bucket0 + b], 1);
-      }
-    }
+    moba_for_each_pair(blk, r0, r1, m, topk,
+                       [&](int32_t, int, const MobaRow& mr, int32_t b) { atomicAdd(&loc[mr.bucket0 + b], 1); });
     __syncthreads();
     for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) {
       base_of[i] = loc[i] ? atomicAdd(&cursor[i], loc[i]) : 0;
@@ -200,16 +227,11 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __rest
     }
     __syncthreads();
   }
-  for (int32_t row = r0 + threadIdx.x; row < r1; row += 256) {
-    const MobaRow mr = moba_row(m, (uint32_t)row);
-    for (int s = 0; s < topk - 1; ++s) {
-      const int32_t b = blk[row * topk + s];
-      if (b < 0 || b >= mr.cur) continue;
-      const int32_t bk = mr.bucket0 + b;
-      const int32_t pos = use_lds ? base_of[bk] + atomicAdd(&loc[bk], 1) : atomicAdd(&cursor[bk], 1);
-      entries[pos] = make_int2(row * 16 + s, mr.qrow);
-    }
-  }
+  moba_for_each_pair(blk, r0, r1, m, topk, [&](int32_t row, int s, const MobaRow& mr, int32_t b) {
+    const int32_t bk = mr.bucket0 + b;
+    const int32_t pos = use_lds ? base_of[bk] + atomicAdd(&loc[bk], 1) : atomicAdd(&cursor[bk], 1);
+    entries[pos] = make_int2(row * 16 + s, mr.qrow);
+  });
 }
 
 // Past-block attention: one workgroup per tile of up to 256 dispatched rows
