@@ -74,7 +74,12 @@ constexpr int kNW = QAT_ESA_NW;
 constexpr int kThreads = 64 * kNW;
 constexpr int kRows = 32 * kNW;
 
-template <int D>
+// The sequence's key list is staged in LDS when it fits (kEsaListLds
+// entries): the K/V tile loads then take their row positions from LDS
+// instead of a global read on the path to every tile's loads.
+constexpr int kEsaListLds = 16384;
+
+template <int D, bool LIST_LDS>
 __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, const int32_t* __restrict__ keylist,
@@ -107,9 +112,15 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
   const int32_t* lst = keylist + bi * keylist_stride;
   const int lim = ng + (valid ? (int)i : -1);        // this lane attends keys j <= lim
   const int wlim = ng + (int)(i0 + wave * 32);       // every lane of the wave attends j <= wlim
-  fa_segment<D, kNW, true>(st, sm, kb, vb, ng + (int)(i_last + 1), scale_log2,
-                           [=](int j) { return lst[j] * HD; }, [=](int j) { return j <= lim; },
-                           [=](int j0) { return j0 + kKT - 1 <= wlim; });
+  const int nkeys = ng + (int)(i_last + 1);
+  extern __shared__ int32_t s_list[];
+  if constexpr (LIST_LDS) {
+    for (int j = threadIdx.x; j < nkeys; j += kThreads) s_list[j] = lst[j];
+    __syncthreads();
+  }
+  fa_segment<D, kNW, true>(st, sm, kb, vb, nkeys, scale_log2,
+                           [=](int j) { return (LIST_LDS ? s_list[j] : lst[j]) * HD; },
+                           [=](int j) { return j <= lim; }, [=](int j0) { return j0 + kKT - 1 <= wlim; });
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
   if (lse_out && valid && (lane >> 5) == 0) lse_out[(bi * m + i) * H + h] = lse;
@@ -312,13 +323,20 @@ hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, 
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)(cdiv(m, kRows) * H * batch));
   const float sl2 = scale * kLog2e;
-  if (D == 64)
-    hipLaunchKernelGGL(esa_prefill_kernel<64>, grid, dim3(kThreads), 0, s, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                       sel, n_sel, keylist, kls, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2);
-  else
-    hipLaunchKernelGGL(esa_prefill_kernel<128>, grid, dim3(kThreads), 0, s, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, sel, n_sel, keylist, kls, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window,
-                       topk, sl2);
+  const bool lds = kls <= kEsaListLds;
+  const size_t dyn = lds ? (size_t)kls * sizeof(int32_t) : 0;
+#define QAT_ESA_PF(D_, L_)                                                                                   \
+  hipLaunchKernelGGL((esa_prefill_kernel<D_, L_>), grid, dim3(kThreads), dyn, s, (const bf16*)q, (const bf16*)k, \
+                     (const bf16*)v, sel, n_sel, keylist, kls, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, \
+                     topk, sl2)
+  if (D == 64) {
+    if (lds) QAT_ESA_PF(64, true);
+    else QAT_ESA_PF(64, false);
+  } else {
+    if (lds) QAT_ESA_PF(128, true);
+    else QAT_ESA_PF(128, false);
+  }
+#undef QAT_ESA_PF
   return hipGetLastError();
 }
 
