@@ -102,13 +102,17 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
   if (qvalid && h == 0) rowmax_part[(bi * m + qi) * nsplit + blockIdx.y] = mx;
 }
 
-__global__ void esa_rowmax_final_kernel(const float* __restrict__ part, int nsplit, int64_t rows,
-                                        float* __restrict__ rowmax) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per query row: the row's partial maxima are read contiguously
+// and reduced across the wave.
+__global__ __launch_bounds__(256) void esa_rowmax_final_kernel(const float* __restrict__ part, int nsplit,
+                                                               int64_t rows, float* __restrict__ rowmax) {
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (i >= rows) return;
   float mx = -__builtin_inff();
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part[i * nsplit + s]);
-  rowmax[i] = mx;
+  for (int s = lane; s < nsplit; s += 64) mx = fmaxf(mx, part[i * nsplit + s]);
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) rowmax[i] = mx;
 }
 
 // Pass 2: partial importance. grid (key tiles of 128, query splits, batch);
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
 
 // ---------------------------------------------------------------------------
 // Top-k over the middle part, several workgroups per sequence, each owning a
-// slice of kTkSlice consecutive candidates (kTkPer per thread, contiguous):
+// slice of 256 PER consecutive candidates (PER per thread, contiguous):
 //   prep   u_j (mode 0, prefill: the query-split partial sums added in
 //          float64 in split order; mode 1, decode: max(s_j - max s, -clip)),
 //          u'_j = max of u over |t - j| <= r within M (halo recomputed from
@@ -261,8 +265,7 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
 // Each kernel re-derives the digits fixed so far from the global
 // histograms (2048 bins, cheap), so no state passes between them.
 constexpr int kTkThreads = 256;
-constexpr int kTkPer = 8;
-constexpr int kTkSlice = kTkThreads * kTkPer;
+constexpr int kTkPerMin = 2;   // candidates per thread: 2, 4 or 8, so that a pass has >= 256 workgroups where it can
 constexpr int kTkMaxRadius = 1024;
 constexpr int kTkBins = 2048;
 __host__ __device__ constexpr int tk_shift(int pass) { return pass == 0 ? 21 : pass == 1 ? 10 : 0; }
@@ -300,17 +303,25 @@ struct TkCut {
 
 __device__ TkCut tk_cut(const int32_t* __restrict__ hist, int npass, int32_t k, int32_t* s_w, TkCut* s_cut) {
   TkCut cut{0u, 0u, k};
-  for (int pass = 0; pass < npass; ++pass) {
+  // the bins of all three passes are read at once (one memory round trip;
+  // the histogram array always holds three passes)
+  int32_t cc[3][8];
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
     const int nb = 1 << tk_bits(pass);
     const int per = nb / kTkThreads;   // 8 or 4 bins per thread, descending
-    const int32_t* h = hist + pass * kTkBins;
-    int32_t c[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) cc[pass][p] = p < per ? hist[pass * kTkBins + nb - 1 - (threadIdx.x * per + p)] : 0;
+  }
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    if (pass >= npass) break;
+    const int nb = 1 << tk_bits(pass);
+    const int per = nb / kTkThreads;
+    const int32_t* c = cc[pass];
     int32_t local = 0;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      c[p] = p < per ? h[nb - 1 - (threadIdx.x * per + p)] : 0;
-      local += c[p];
-    }
+    for (int p = 0; p < 8; ++p) local += c[p];
     int32_t acc = tk_scan(local, s_w, nullptr);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -340,16 +351,17 @@ __device__ __forceinline__ float tk_u(int mode, const float* __restrict__ upart,
   return fmaxf(s_in[bi * n_mid + j] - mx, -clip);
 }
 
+template <int PER>
 __global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
     int mode, const float* __restrict__ upart, int nqsplit, const float* __restrict__ s_in,
     const float* __restrict__ smax_part, int nsmax, float clip, int64_t n_mid, int radius,
     uint32_t* __restrict__ keys, float* __restrict__ scores_out, int32_t* __restrict__ hist) {
-  __shared__ float s_u[kTkSlice + 2 * kTkMaxRadius];
+  __shared__ float s_u[kTkThreads * PER + 2 * kTkMaxRadius];
   __shared__ int32_t s_h[kTkBins];
   __shared__ float s_red[kTkThreads / 64];
   const int tid = threadIdx.x;
   const int64_t bi = blockIdx.y;
-  const int64_t j0 = (int64_t)blockIdx.x * kTkSlice;
+  const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER);
   float mx = 0.f;
   if (mode == 1) {   // max of the raw scores over M, from the scan's per-workgroup maxima
     float m = -__builtin_inff();
@@ -363,13 +375,13 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
   for (int i = tid; i < kTkBins; i += kTkThreads) s_h[i] = 0;
   // u over [j0 - r, j0 + slice + r) clipped to M
   const int64_t lo = max((int64_t)0, j0 - radius);
-  const int64_t hi = min(n_mid, j0 + kTkSlice + radius);
+  const int64_t hi = min(n_mid, j0 + (kTkThreads * PER) + radius);
   for (int64_t j = lo + tid; j < hi; j += kTkThreads)
     s_u[j - j0 + radius] = tk_u(mode, upart, nqsplit, s_in, mx, clip, bi, n_mid, j);
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < kTkPer; ++e) {
-    const int64_t j = j0 + tid * kTkPer + e;
+  for (int e = 0; e < PER; ++e) {
+    const int64_t j = j0 + tid * PER + e;
     if (j >= n_mid) break;
     float v = s_u[j - j0 + radius];
     const int64_t a = max((int64_t)0, j - radius), b = min(n_mid - 1, j + (int64_t)radius);
@@ -385,6 +397,7 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
     if (s_h[i]) atomicAdd(&gh[i], s_h[i]);
 }
 
+template <int PER>
 __global__ __launch_bounds__(kTkThreads) void esa_topk_hist_kernel(int pass, const uint32_t* __restrict__ keys,
                                                                    int64_t n_mid, int topk,
                                                                    int32_t* __restrict__ hist) {
@@ -397,9 +410,9 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_hist_kernel(int pass, con
   const int nb = 1 << tk_bits(pass);
   for (int i = threadIdx.x; i < nb; i += kTkThreads) s_h[i] = 0;
   __syncthreads();
-  const int64_t j0 = (int64_t)blockIdx.x * kTkSlice + threadIdx.x * kTkPer;
+  const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER) + threadIdx.x * PER;
 #pragma unroll
-  for (int e = 0; e < kTkPer; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const int64_t j = j0 + e;
     if (j >= n_mid) break;
     const uint32_t key = keys[bi * n_mid + j];
@@ -411,6 +424,7 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_hist_kernel(int pass, con
 }
 
 // per slice: (#keys > T, #keys == T)
+template <int PER>
 __global__ __launch_bounds__(kTkThreads) void esa_topk_count_kernel(const uint32_t* __restrict__ keys,
                                                                     int64_t n_mid, int topk,
                                                                     const int32_t* __restrict__ hist,
@@ -420,10 +434,10 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_count_kernel(const uint32
   const int64_t bi = blockIdx.y;
   const TkCut cut = tk_cut(hist + bi * 3 * kTkBins, 3, topk, s_w, &s_cut);
   const uint32_t T = cut.prefix;
-  const int64_t j0 = (int64_t)blockIdx.x * kTkSlice + threadIdx.x * kTkPer;
+  const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER) + threadIdx.x * PER;
   int32_t gt = 0, eq = 0;
 #pragma unroll
-  for (int e = 0; e < kTkPer; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const int64_t j = j0 + e;
     if (j >= n_mid) break;
     const uint32_t key = keys[bi * n_mid + j];
@@ -436,6 +450,7 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_count_kernel(const uint32
   if (threadIdx.x == 0) wgcnt[bi * gridDim.x + blockIdx.x] = make_int2(tgt, teq);
 }
 
+template <int PER>
 __global__ __launch_bounds__(kTkThreads) void esa_topk_emit_kernel(const uint32_t* __restrict__ keys,
                                                                    int64_t n_mid, int topk, int64_t mid0,
                                                                    const int32_t* __restrict__ hist,
@@ -452,10 +467,10 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_emit_kernel(const uint32_
     if (threadIdx.x == 0) n_sel[bi] = (int32_t)nsel;
     for (int64_t j = nsel + threadIdx.x; j < topk; j += kTkThreads) osel[j] = -1;
   }
-  const int64_t j0 = (int64_t)blockIdx.x * kTkSlice + threadIdx.x * kTkPer;
+  const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER) + threadIdx.x * PER;
   if (n_mid <= topk) {   // every candidate is selected
 #pragma unroll
-    for (int e = 0; e < kTkPer; ++e)
+    for (int e = 0; e < PER; ++e)
       if (j0 + e < n_mid) osel[j0 + e] = (int32_t)(mid0 + j0 + e);
     return;
   }
@@ -475,9 +490,9 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_emit_kernel(const uint32_
   // equal keys taken before this slice = min(eq_sum, take_eq)
   const int32_t base = gt_sum + min(eq_sum, take_eq);
   int32_t gt = 0, eq = 0;
-  uint32_t kv[kTkPer];
+  uint32_t kv[PER];
 #pragma unroll
-  for (int e = 0; e < kTkPer; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const int64_t j = j0 + e;
     kv[e] = j < n_mid ? keys[bi * n_mid + j] : 0u;
     if (j < n_mid) {
@@ -491,7 +506,7 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_emit_kernel(const uint32_
   int32_t pos = base + tk_scan(gt + my_eq, s_w, nullptr);
   int32_t used = 0;
 #pragma unroll
-  for (int e = 0; e < kTkPer; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const int64_t j = j0 + e;
     if (j >= n_mid) break;
     bool take = kv[e] > T;
@@ -544,7 +559,7 @@ hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const b
 #undef QAT_RM
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(esa_rowmax_final_kernel, dim3((unsigned)cdiv(batch * m, 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(esa_rowmax_final_kernel, dim3((unsigned)cdiv(batch * m, 4)), dim3(256), 0, s,
                      rowmax_part, ks_eff, batch * m, rowmax);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int qs = esa_query_splits(n_mid, m);
@@ -589,33 +604,55 @@ hipError_t launch_esa_decode_scan(const float* qc, const bf16* kc, int64_t batch
   return hipGetLastError();
 }
 
-int esa_topk_slices(int64_t n_mid) { return (int)std::max<int64_t>(1, cdiv(n_mid, kTkSlice)); }
+// workgroups per sequence at the finest split (the workspace holds that many per-slice counts)
+int esa_topk_slices(int64_t n_mid) { return (int)std::max<int64_t>(1, cdiv(n_mid, kTkThreads * kTkPerMin)); }
 int esa_topk_max_radius() { return kTkMaxRadius; }
+
+template <int PER>
+static hipError_t launch_esa_topk_per(int mode, const float* upart, int nqsplit, const float* s_in,
+                                      const float* smax_part, int nsmax, float clip, int64_t batch, int64_t n_mid,
+                                      int radius, int topk, int64_t mid0, int32_t* hist, int2* wgcnt,
+                                      uint32_t* keys, float* scores_out, int32_t* sel, int32_t* n_sel,
+                                      hipStream_t s) {
+  const int64_t nwg = std::max<int64_t>(1, cdiv(n_mid, kTkThreads * PER));
+  const dim3 grid((unsigned)nwg, (unsigned)batch);
+  hipError_t e;
+  if (n_mid > 0) {
+    if ((e = launch_fill_i32(hist, batch * 3 * kTkBins, 0, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(esa_topk_prep_kernel<PER>, grid, dim3(kTkThreads), 0, s, mode, upart, nqsplit, s_in,
+                       smax_part, nsmax, clip, n_mid, radius, keys, scores_out, hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (n_mid > topk) {
+      for (int pass = 1; pass < 3; ++pass) {
+        hipLaunchKernelGGL(esa_topk_hist_kernel<PER>, grid, dim3(kTkThreads), 0, s, pass, keys, n_mid, topk, hist);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(esa_topk_count_kernel<PER>, grid, dim3(kTkThreads), 0, s, keys, n_mid, topk, hist, wgcnt);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL(esa_topk_emit_kernel<PER>, grid, dim3(kTkThreads), 0, s, keys, n_mid, topk, mid0, hist, wgcnt,
+                     sel, n_sel);
+  return hipGetLastError();
+}
 
 hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const float* s_in, const float* smax_part,
                            int nsmax, float clip, int64_t batch, int64_t n_mid, int radius, int topk, int64_t mid0,
                            int32_t* hist, int2* wgcnt, uint32_t* keys, float* scores_out, int32_t* sel,
                            int32_t* n_sel, hipStream_t s) {
-  const int nwg = esa_topk_slices(n_mid);
-  const dim3 grid((unsigned)nwg, (unsigned)batch);
-  hipError_t e;
-  if (n_mid > 0) {
-    if ((e = launch_fill_i32(hist, batch * 3 * kTkBins, 0, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(esa_topk_prep_kernel, grid, dim3(kTkThreads), 0, s, mode, upart, nqsplit, s_in, smax_part,
-                       nsmax, clip, n_mid, radius, keys, scores_out, hist);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (n_mid > topk) {
-      for (int pass = 1; pass < 3; ++pass) {
-        hipLaunchKernelGGL(esa_topk_hist_kernel, grid, dim3(kTkThreads), 0, s, pass, keys, n_mid, topk, hist);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-      }
-      hipLaunchKernelGGL(esa_topk_count_kernel, grid, dim3(kTkThreads), 0, s, keys, n_mid, topk, hist, wgcnt);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-  }
-  hipLaunchKernelGGL(esa_topk_emit_kernel, grid, dim3(kTkThreads), 0, s, keys, n_mid, topk, mid0, hist, wgcnt,
-                     sel, n_sel);
-  return hipGetLastError();
+  // the widest split that still gives every pass 256 workgroups (the
+  // passes are latency-bound: fewer candidates per thread when there are
+  // few sequences); wgcnt holds esa_topk_slices(n_mid) >= slices entries
+  // per sequence
+  const int64_t s8 = batch * cdiv(n_mid, kTkThreads * 8), s4 = batch * cdiv(n_mid, kTkThreads * 4);
+  if (s8 >= 256)
+    return launch_esa_topk_per<8>(mode, upart, nqsplit, s_in, smax_part, nsmax, clip, batch, n_mid, radius, topk,
+                                  mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
+  if (s4 >= 256)
+    return launch_esa_topk_per<4>(mode, upart, nqsplit, s_in, smax_part, nsmax, clip, batch, n_mid, radius, topk,
+                                  mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
+  return launch_esa_topk_per<kTkPerMin>(mode, upart, nqsplit, s_in, smax_part, nsmax, clip, batch, n_mid, radius,
+                                        topk, mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
 }
 
 }  // namespace qat
