@@ -111,8 +111,18 @@ __global__ void compress_finalize_kernel(const double* __restrict__ partial, int
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n * d_c) return;
   const int64_t row = idx / d_c, col = idx % d_c;
+  // in split order; sixteen partials are loaded at a time so that their
+  // loads overlap
   double v = 0.0;
-  for (int s = 0; s < nsplit; ++s) v += partial[(int64_t)s * n * d_c + idx];
+  int s = 0;
+  for (; s + 16 <= nsplit; s += 16) {
+    double t[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) t[u] = partial[(int64_t)(s + u) * n * d_c + idx];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v += t[u];
+  }
+  for (; s < nsplit; ++s) v += partial[(int64_t)s * n * d_c + idx];
   if (bias) v += (double)bias[col];
   if (kind == 1) {
     ((bf16*)out)[row * out_stride + col] = f64_to_bf16_rne(v);
