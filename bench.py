@@ -36,9 +36,33 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 CSRC = os.path.join(ROOT, "query_aware_top_amd", "csrc")
 
 
-def kernel_source_sha() -> str:
+# Sources each timed stage is built from (the C ABI and launcher declarations
+# included): a stored counter reading stays valid while these are unchanged.
+_COMMON = ["abi.hip", "launch.h", "common.h"]
+STAGE_SOURCES = {
+    "moba_meanpool": ["moba_select.hip"],
+    "moba_select": ["moba_select.hip"],
+    "moba_dispatch": ["moba_attn.hip"],
+    "moba_past_attn": ["moba_attn.hip", "attn_core.h"],
+    "moba_current_attn": ["moba_attn.hip", "attn_core.h"],
+    "moba_generic_attn": ["attn_generic.hip"],
+    "esa_compress*": ["compress.hip"],
+    "esa_scores": ["esa_select.hip"],
+    "esa_topk": ["esa_select.hip"],
+    "esa_decode_scan": ["esa_select.hip"],
+    "esa_prefill_attn": ["esa_attn.hip", "attn_core.h"],
+    "esa_decode_attn": ["esa_attn.hip"],
+}
+
+
+def kernel_source_sha(stage: str = "") -> str:
+    """Hash of the sources a stage is built from (every source if the stage
+    is unknown or empty)."""
+    files = sorted(os.listdir(CSRC))
+    if stage in STAGE_SOURCES:
+        files = sorted(set(STAGE_SOURCES[stage] + _COMMON))
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
@@ -54,7 +78,7 @@ def traffic_for(kernel: str, workload: str):
     except OSError:
         return None
     e = c.get(f"{workload}/{kernel}")
-    if not e or e.get("source_sha") != kernel_source_sha():
+    if not e or e.get("source_sha") != kernel_source_sha(kernel):
         return None
     return e["hbm_bytes_per_launch"]
 
