@@ -174,3 +174,19 @@ def test_esa_decode_128k_full_size():
     4096 window tokens, 16 planted needles per sequence; oracle check on
     three sequences, needles checked on the GPU for all sixteen."""
     esa_case(4, 16, 131072, 131071, 1, 32, 128, 128, 128, 4096, 2048, 2, 48.0, needles=16, seqs=[0, 7, 15])
+
+
+@pytest.mark.parametrize("T", [20000, 40000], ids=["split4", "split8"])
+def test_esa_decode_topk_split_widths(T):
+    """Sixteen-sequence decode at contexts where the top-k passes take 4
+    (T = 20000) and 8 (T = 40000) candidates per thread (the full-size decode
+    takes 16, the 64k prefill 2); selection and output against the oracle on
+    three sequences."""
+    esa_case(9, 16, T, T - 1, 1, 4, 64, 64, 32, 256, 300, 2, 24.0, seqs=[0, 2, 15])
+
+
+def test_esa_key_list_beyond_lds():
+    """A key list longer than the 16384 entries the chunk kernel stages in
+    LDS (64 initial + 5000 selected + 12000 window + 128 chunk keys): the
+    tile loads take their positions from global memory."""
+    esa_case(10, 1, 40000, 36000, 128, 2, 64, 64, 64, 12000, 5000, 2, 12.0, rows=[0, 1, 63, 127])

@@ -156,3 +156,15 @@ def test_moba_long_512k_full_size():
     rel = [t - qs for t in rows_att]
     assert_close(to64(out[0, rel]), o_ref, BF16_TOL, "output")
     assert_close(to64(lse[0, rel]), lse_ref, 1e-3, "lse")
+
+
+def test_moba_many_buckets_global_dispatch():
+    """More than 4096 (sequence, KV head, block) buckets (8 KV heads x 515
+    blocks of 64): the dispatch counts and places entries through global
+    atomics and the tile table searches the tile prefix in global memory;
+    the block means exceed the LDS budget of the resident scoring kernel,
+    so the streaming one runs. Sampled rows against the oracle."""
+    n, hq, hkv, d, block = 33000, 8, 8, 64, 64
+    q, k, v, _ = synth.moba_inputs(31, 1, n, hq, hkv, d, torch.bfloat16, DEV)
+    rows = sample_rows(n, block, 48, 31)
+    check(q, k, v, block, 3, torch.bfloat16, rows=rows)
