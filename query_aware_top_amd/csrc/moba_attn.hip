@@ -234,6 +234,13 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __rest
   });
 }
 
+// Dynamic LDS of the past-block kernels: bf16 staging rows (padded by 8) and
+// the output row indices of kNW waves x 32 rows.
+template <int D>
+constexpr int kPastStageBytes = kNW * 32 * (D + 8) * 2;
+template <int D>
+constexpr int kPastDynBytes = kPastStageBytes<D> + kNW * 32 * 8;
+
 // Past-block attention: one workgroup per tile of up to 256 dispatched rows
 // of one (sequence, KV head, block); full block, no mask. Partials are
 // written row-contiguous through LDS. Tiles of one bucket are adjacent in the
@@ -245,8 +252,12 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_kernel(
     bf16* __restrict__ part_o, float* __restrict__ part_lse, int64_t hkv, int block, int topk,
     float scale_log2) {
   QAT_FA_SMEM(D, sm);
-  __shared__ __align__(16) bf16 s_stage[kNW * 32 * (D + 8)];
-  __shared__ int64_t s_rows[kNW * 32];
+  // staging area in dynamic LDS, which is placed after the static tile
+  // buffers: those then sit below 64 KiB, where every tile read addresses
+  // its buffer through the instruction's immediate offset
+  extern __shared__ __align__(16) char s_past_dyn[];
+  bf16* s_stage = reinterpret_cast<bf16*>(s_past_dyn);
+  int64_t* s_rows = reinterpret_cast<int64_t*>(s_past_dyn + kPastStageBytes<D>);
   const int64_t tile = xcd_logical_id(blockIdx.x, gridDim.x);
   if (tile >= ntiles[0]) return;
   const int4 td = tiles[tile];
@@ -291,8 +302,12 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_persist_kernel(
     bf16* __restrict__ part_o, float* __restrict__ part_lse, int64_t hkv, int block, int topk,
     float scale_log2) {
   QAT_FA_SMEM(D, sm);
-  __shared__ __align__(16) bf16 s_stage[kNW * 32 * (D + 8)];
-  __shared__ int64_t s_rows[kNW * 32];
+  // staging area in dynamic LDS, which is placed after the static tile
+  // buffers: those then sit below 64 KiB, where every tile read addresses
+  // its buffer through the instruction's immediate offset
+  extern __shared__ __align__(16) char s_past_dyn[];
+  bf16* s_stage = reinterpret_cast<bf16*>(s_past_dyn);
+  int64_t* s_rows = reinterpret_cast<int64_t*>(s_past_dyn + kPastStageBytes<D>);
   const int n_items = ntiles[0];
   const int G = gridDim.x;
   int item = (int)xcd_logical_id(blockIdx.x, G);
@@ -667,6 +682,17 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
                                      int topk, float scale, int64_t max_tiles, hipStream_t s) {
   const float sl2 = scale * kLog2e;
   hipError_t e;
+  // dynamic LDS beyond 64 KiB is declared once per kernel
+  static const bool lds_ok = [] {
+    bool ok = hipFuncSetAttribute((const void*)moba_past_persist_kernel<D>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kPastDynBytes<D>) == hipSuccess;
+    ok &= hipFuncSetAttribute((const void*)moba_past_kernel<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kPastDynBytes<D>) == hipSuccess;
+    ok &= hipFuncSetAttribute((const void*)moba_past_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kPastDynBytes<D>) == hipSuccess;
+    return ok;
+  }();
+  if (!lds_ok) return hipErrorInvalidConfiguration;
   if (topk > 1 && max_tiles > 0 && nbc > 0) {
     {
       KTimer tm("moba_past_attn", s);
@@ -677,13 +703,16 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
       if (block % (2 * kKT) == 0 && (int64_t)block * hkv * D * 2 < (1ll << 31)) {
         // persistent grid: the workgroups that fit at once (256 CUs x 8 waves), never more than the tiles
         const int64_t grid = std::min<int64_t>(max_tiles, 2048 / kNW);
-        hipLaunchKernelGGL((moba_past_persist_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, s, q, k, v,
+        hipLaunchKernelGGL((moba_past_persist_kernel<D>), dim3((unsigned)grid), dim3(kThreads), kPastDynBytes<D>, s,
+                           q, k, v,
                            tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
       } else if (block % kKT == 0) {
-        hipLaunchKernelGGL((moba_past_kernel<D, true>), dim3((unsigned)max_tiles), dim3(kThreads), 0, s, q, k, v,
+        hipLaunchKernelGGL((moba_past_kernel<D, true>), dim3((unsigned)max_tiles), dim3(kThreads), kPastDynBytes<D>,
+                           s, q, k, v,
                            tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
       } else {
-        hipLaunchKernelGGL((moba_past_kernel<D, false>), dim3((unsigned)max_tiles), dim3(kThreads), 0, s, q, k, v,
+        hipLaunchKernelGGL((moba_past_kernel<D, false>), dim3((unsigned)max_tiles), dim3(kThreads), kPastDynBytes<D>,
+                           s, q, k, v,
                            tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
       }
     }
