@@ -486,16 +486,29 @@ __global__ __launch_bounds__(kSelPWaves * 64, KMAX >= 7 ? 2 : 3) void moba_selec
       // the next chunk's queries replace these once the last round's matrix
       // ops have read them: their loads overlap the selection work below
       if (c0 + 32 >= nbr && more) load_q(c + stride, qa, qb);
-      // blocks c0 + bb with bb >= n are not candidates of the column's row
-      const int n_a = cur_a - c0, n_b = cur_b - c0;
+      // blocks c0 + bb with bb >= n are not candidates of the column's row;
+      // when even the chunk's first row (the smallest own block) has all 32
+      // as candidates, the round needs no mask (wave-uniform test)
+      if ((qs + rc * 64) / block - c0 >= 32) {
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
+        for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int bb = gi * 8 + hl * 4 + i;
-          top_insert<KMAX>(tva, tia, bb < n_a ? sa[4 * gi + i] : -__builtin_inff(), c0 + bb);
-          top_insert<KMAX>(tvb, tib, bb < n_b ? sb[4 * gi + i] : -__builtin_inff(), c0 + bb);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int bb = gi * 8 + hl * 4 + i;
+            top_insert<KMAX>(tva, tia, sa[4 * gi + i], c0 + bb);
+            top_insert<KMAX>(tvb, tib, sb[4 * gi + i], c0 + bb);
+          }
+      } else {
+        const int n_a = cur_a - c0, n_b = cur_b - c0;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int bb = gi * 8 + hl * 4 + i;
+            top_insert<KMAX>(tva, tia, bb < n_a ? sa[4 * gi + i] : -__builtin_inff(), c0 + bb);
+            top_insert<KMAX>(tvb, tib, bb < n_b ? sb[4 * gi + i] : -__builtin_inff(), c0 + bb);
+          }
+      }
     }
     if (nbr <= 0 && more) load_q(c + stride, qa, qb);
     // lane l < 32 keeps query ra (its list of column a), lane l + 32 keeps
