@@ -330,6 +330,17 @@ def make(name):
     raise SystemExit(f"unknown workload {name}")
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,7 +372,11 @@ def main():
     for _ in range(args.warmup):
         w.step()
     torch.cuda.synchronize()
+    # timed region: the library brackets only the dominant kernel with events
+    # (on the stream it runs on), so the roofline's launch time is measured
+    # live in this region at the cost of two events per step
     qat.timing_enable(True)
+    qat.timing_select(w.dominant)
     qat.timing_reset()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -370,8 +385,16 @@ def main():
         w.step()
     stop.record()
     torch.cuda.synchronize()
-    qat.timing_enable(False)
     ms = start.elapsed_time(stop) / args.steps
+    tot, n = qat.timing_query(w.dominant)
+    dom_ms = round(tot / n, 4) if n else None
+    # per-stage breakdown from a second, untimed pass with every stage bracketed
+    qat.timing_select(None)
+    qat.timing_reset()
+    for _ in range(args.steps):
+        w.step()
+    torch.cuda.synchronize()
+    qat.timing_enable(False)
     kernels = {}
     for name in ("moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn", "moba_current_attn",
                  "moba_generic_attn", "esa_compress", "esa_qcompress", "esa_scores", "esa_decode_scan", "esa_topk",
@@ -380,7 +403,30 @@ def main():
         if n:
             kernels[name] = round(tot / n, 4)
     qat.timing_reset()
-    dom_ms = kernels.get(w.dominant)
+    # spread of single steps (outside the timed region above): events around
+    # each step; for the HBM-bound workload also with L2 and the 256 MiB
+    # Infinity Cache flushed before every step (1 GiB streamed, untimed)
+    def step_times(flush):
+        buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if flush else None
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            if flush:
+                buf.fill_(1.0)
+            a.record()
+            w.step()
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        return t
+
+    def pct(t, q):
+        return round(t[min(len(t) - 1, int(q * (len(t) - 1) + 0.5))], 4)
+
+    warm = step_times(False)
+    spread = {"p10": pct(warm, 0.1), "p50": pct(warm, 0.5), "p90": pct(warm, 0.9)}
+    if w.bound == "hbm":
+        cold = step_times(True)
+        spread["cold_p50"] = pct(cold, 0.5)
     work = w.dominant_work()
     if w.bound == "hbm":
         achieved = work / (dom_ms * 1e-3) / 1e9
@@ -411,9 +457,12 @@ def main():
                      "traffic": traffic_for(w.dominant, w.name), "work_per_launch": work,
                      "avg_launch_ms": dom_ms},
         "kernels_avg_ms": kernels,
+        "step_ms": spread,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = w.cpu_baseline()
+        cb = w.cpu_baseline()
+        cb["sample"] += f"; host {_cpu_model()}, {os.cpu_count()} logical CPUs"
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 

@@ -61,12 +61,18 @@ int qat_abi_version(void);
  * (names: "moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn",
  * "moba_current_attn", "moba_generic_attn", "esa_compress", "esa_scores",
  * "esa_decode_scan", "esa_topk", "esa_prefill_attn", "esa_decode_attn",
- * "esa_generic_attn"). qat_timing_query synchronises on the recorded events
- * and returns the summed milliseconds and the launch count for one name;
- * qat_timing_reset drops the records. Host memory only; no device memory is
+ * "esa_generic_attn"). The events are timing-only (created without the
+ * system-scope fence on completion, so recording them does not slow the
+ * kernels they bracket); qat_timing_query waits on them and returns the
+ * summed milliseconds and the launch count for one name, and is meant to be
+ * called after the caller has synchronised with the timed work;
+ * qat_timing_reset drops the records. qat_timing_select(name) restricts the
+ * records to that one stage (NULL: every stage), so that a timed region
+ * carries only the events it needs. Host memory only; no device memory is
  * allocated.
  */
 int qat_timing_enable(int on);
+int qat_timing_select(const char* name);
 int qat_timing_reset(void);
 int qat_timing_query(const char* name, double* total_ms, int* count);
 

@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     moba_sparse_attn,
     EXPORTED_SYMBOLS,
     timing_enable,
+    timing_select,
     timing_reset,
     timing_query,
 )

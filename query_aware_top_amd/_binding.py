@@ -14,7 +14,8 @@ QAT_F32, QAT_BF16 = 0, 1
 _STATUS = {0: "QAT_OK", -1: "QAT_EINVAL", -2: "QAT_EUNSUPPORTED", -3: "QAT_EWORKSPACE", -4: "QAT_EHIP"}
 
 EXPORTED_SYMBOLS = (
-    "qat_last_error", "qat_abi_version", "qat_timing_enable", "qat_timing_reset", "qat_timing_query",
+    "qat_last_error", "qat_abi_version", "qat_timing_enable", "qat_timing_select", "qat_timing_reset",
+    "qat_timing_query",
     "esa_workspace_size", "esa_compress_workspace_size", "esa_compress", "esa_select", "esa_sparse_attn",
     "moba_workspace_size", "moba_block_select", "moba_sparse_attn",
 )
@@ -67,6 +68,7 @@ def lib():
         L.moba_workspace_size.argtypes = [ctypes.POINTER(MobaParams), ctypes.POINTER(sz)]
         L.moba_block_select.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, sz, vp]
         L.qat_timing_enable.argtypes = [ctypes.c_int]
+        L.qat_timing_select.argtypes = [ctypes.c_char_p]
         L.qat_timing_reset.argtypes = []
         L.qat_timing_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         L.moba_sparse_attn.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -83,6 +85,11 @@ def abi_version() -> int:
 def timing_enable(on: bool = True):
     """Per-kernel HIP-event timing inside the library (see qat_timing_enable)."""
     _check(lib().qat_timing_enable(1 if on else 0))
+
+
+def timing_select(name=None):
+    """Restrict the library's timing records to one stage (None: every stage)."""
+    _check(lib().qat_timing_select(name.encode() if name else None))
 
 
 def timing_reset():

@@ -200,6 +200,7 @@ struct TimerRec {
 };
 std::mutex g_tmu;
 bool g_timing = false;
+std::string g_timing_only;   // empty: every stage
 std::vector<TimerRec> g_recs;
 std::vector<hipEvent_t> g_pool;
 std::map<std::string, hipEvent_t> g_open;
@@ -210,17 +211,33 @@ hipEvent_t pool_event() {
     g_pool.pop_back();
     return e;
   }
+  // timing-only events: no system-scope fence (cache write-back and
+  // invalidation) when they complete, so recording them does not slow the
+  // kernels they bracket; they are read only after a full synchronisation
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
 }  // namespace
 
 namespace qat {
+bool ktimer_kernel_events(const char* name, hipEvent_t* a, hipEvent_t* b) {
+  if (!g_timing) return false;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (g_timing_only != name) return false;
+  *a = pool_event();
+  *b = pool_event();
+  return *a && *b;
+}
+void ktimer_kernel_record(const char* name, hipEvent_t a, hipEvent_t b) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_recs.push_back({name, a, b});
+}
 void ktimer_start(const char* name, hipStream_t s) {
   if (!g_timing) return;
   std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_timing_only.empty()) return;   // one stage selected: its kernel is timed by its dispatch
   hipEvent_t e = pool_event();
   if (!e) return;
   (void)hipEventRecord(e, s);
@@ -246,6 +263,12 @@ QAT_EXPORT int qat_abi_version(void) { return QAT_ABI_VERSION; }
 QAT_EXPORT int qat_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(g_tmu);
   g_timing = on != 0;
+  return ok();
+}
+
+QAT_EXPORT int qat_timing_select(const char* name) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing_only = name ? name : "";
   return ok();
 }
 

@@ -173,10 +173,10 @@ hipError_t launch_moba_generic(const void* q, const void* k, const void* v, cons
   if (rows == 0) return hipSuccess;
   const float sl2 = scale * 1.4426950408889634f;
   dim3 grid((unsigned)cdiv(rows, 4));
-#define QAT_MG(T_, D_)                                                                                       \
-  hipLaunchKernelGGL((moba_generic_kernel<T_, D_>), grid, dim3(256), 0, s, (const T_*)q, (const T_*)k,       \
-                     (const T_*)v, blk, (T_*)out, lse, batch, seq_len, hq, hkv, q_start, q_len, block, topk, \
-                     window, sl2)
+#define QAT_MG(T_, D_)                                                                                     \
+  launch_timed("moba_generic_attn", moba_generic_kernel<T_, D_>, grid, dim3(256), 0, s, (const T_*)q,        \
+               (const T_*)k, (const T_*)v, blk, (T_*)out, lse, batch, seq_len, hq, hkv, q_start, q_len, block, \
+               topk, window, sl2)
   if (bf) {
     if (d == 64) QAT_MG(bf16, 64);
     else QAT_MG(bf16, 128);
@@ -197,7 +197,7 @@ hipError_t launch_esa_generic(const void* q, const void* k, const void* v, const
   const float sl2 = scale * 1.4426950408889634f;
   dim3 grid((unsigned)cdiv(rows, 4));
 #define QAT_EG(T_, D_)                                                                                          \
-  hipLaunchKernelGGL((esa_generic_kernel<T_, D_>), grid, dim3(256), 0, s, (const T_*)q, (const T_*)k,           \
+  launch_timed("esa_generic_attn", esa_generic_kernel<T_, D_>, grid, dim3(256), 0, s, (const T_*)q, (const T_*)k,           \
                      (const T_*)v, sel, n_sel, (T_*)out, lse, batch, H, ctx_len, c0, m, n_init, window, topk, sl2)
   if (bf) {
     if (d == 64) QAT_EG(bf16, 64);

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace qat {
@@ -82,5 +83,23 @@ struct KTimer {
   KTimer(const char* n, hipStream_t st) : name(n), s(st) { ktimer_start(name, s); }
   ~KTimer() { ktimer_stop(name, s); }
 };
+
+// Kernel-level timing of the one stage chosen with qat_timing_select: that
+// stage's main kernel is launched with start/stop events filled from its own
+// dispatch (hipExtLaunchKernel), so no marker packets enter the stream.
+bool ktimer_kernel_events(const char* name, hipEvent_t* a, hipEvent_t* b);
+void ktimer_kernel_record(const char* name, hipEvent_t a, hipEvent_t b);
+
+template <typename F, typename... Args>
+inline void launch_timed(const char* name, F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s,
+                         Args... args) {
+  hipEvent_t a, b;
+  if (ktimer_kernel_events(name, &a, &b)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, s, a, b, 0, args...);
+    ktimer_kernel_record(name, a, b);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
+  }
+}
 
 }  // namespace qat

@@ -325,10 +325,10 @@ hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, 
   const float sl2 = scale * kLog2e;
   const bool lds = kls <= kEsaListLds;
   const size_t dyn = lds ? (size_t)kls * sizeof(int32_t) : 0;
-#define QAT_ESA_PF(D_, L_)                                                                                   \
-  hipLaunchKernelGGL((esa_prefill_kernel<D_, L_>), grid, dim3(kThreads), dyn, s, (const bf16*)q, (const bf16*)k, \
-                     (const bf16*)v, sel, n_sel, keylist, kls, (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, \
-                     topk, sl2)
+#define QAT_ESA_PF(D_, L_)                                                                                  \
+  launch_timed("esa_prefill_attn", esa_prefill_kernel<D_, L_>, grid, dim3(kThreads), (uint32_t)dyn, s,       \
+               (const bf16*)q, (const bf16*)k, (const bf16*)v, sel, n_sel, (const int32_t*)keylist, kls,   \
+               (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2)
   if (D == 64) {
     if (lds) QAT_ESA_PF(64, true);
     else QAT_ESA_PF(64, false);
@@ -356,10 +356,10 @@ hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, c
   dim3 grid((unsigned)nsplit, (unsigned)batch);
   const float sl2 = scale * kLog2e;
   const int64_t E = H * D / 256;
-#define QAT_DEC(E_)                                                                                         \
-  hipLaunchKernelGGL(esa_decode_attn_kernel<E_>, grid, dim3(256), 0, s, (const bf16*)q, (const bf16*)k,     \
-                     (const bf16*)v, sel, n_sel, po, pm, pl, H, D, ctx_len, c0, n_init, window, topk, nsplit, kps, \
-                     sl2)
+#define QAT_DEC(E_)                                                                                        \
+  launch_timed("esa_decode_attn", esa_decode_attn_kernel<E_>, grid, dim3(256), 0, s, (const bf16*)q,       \
+               (const bf16*)k, (const bf16*)v, sel, n_sel, po, pm, pl, H, D, ctx_len, c0, n_init, window, topk, \
+               nsplit, kps, sl2)
   if (E == 8) QAT_DEC(8);
   else if (E == 16) QAT_DEC(16);
   else QAT_DEC(32);

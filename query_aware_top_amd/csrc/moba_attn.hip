@@ -703,17 +703,14 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
       if (block % (2 * kKT) == 0 && (int64_t)block * hkv * D * 2 < (1ll << 31)) {
         // persistent grid: the workgroups that fit at once (256 CUs x 8 waves), never more than the tiles
         const int64_t grid = std::min<int64_t>(max_tiles, 2048 / kNW);
-        hipLaunchKernelGGL((moba_past_persist_kernel<D>), dim3((unsigned)grid), dim3(kThreads), kPastDynBytes<D>, s,
-                           q, k, v,
-                           tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
+        launch_timed("moba_past_attn", moba_past_persist_kernel<D>, dim3((unsigned)grid), dim3(kThreads),
+                     kPastDynBytes<D>, s, q, k, v, tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
       } else if (block % kKT == 0) {
-        hipLaunchKernelGGL((moba_past_kernel<D, true>), dim3((unsigned)max_tiles), dim3(kThreads), kPastDynBytes<D>,
-                           s, q, k, v,
-                           tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
+        launch_timed("moba_past_attn", moba_past_kernel<D, true>, dim3((unsigned)max_tiles), dim3(kThreads),
+                     kPastDynBytes<D>, s, q, k, v, tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
       } else {
-        hipLaunchKernelGGL((moba_past_kernel<D, false>), dim3((unsigned)max_tiles), dim3(kThreads), kPastDynBytes<D>,
-                           s, q, k, v,
-                           tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
+        launch_timed("moba_past_attn", moba_past_kernel<D, false>, dim3((unsigned)max_tiles), dim3(kThreads),
+                     kPastDynBytes<D>, s, q, k, v, tiles, ntiles, entries, part_o, part_lse, hkv, block, topk, sl2);
       }
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -727,9 +724,9 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
   const int64_t nwg = (int64_t)tiles_per_block * nblocks * batch * hkv * (gs / pack);
   {
     KTimer tm("moba_current_attn", s);
-    hipLaunchKernelGGL(moba_current_kernel<D>, dim3((unsigned)nwg), dim3(64 * kCurNW), 0, s, q, k, v, blk, part_o,
-                       part_lse, out, lse, seq_len, hq, hkv, q_start, q_len, block, topk, sl2, pack,
-                       tiles_per_block, nblocks);
+    launch_timed("moba_current_attn", moba_current_kernel<D>, dim3((unsigned)nwg), dim3(64 * kCurNW), 0, s, q, k,
+                 v, blk, (const bf16*)part_o, (const float*)part_lse, out, lse, seq_len, hq, hkv, q_start, q_len,
+                 block, topk, sl2, pack, tiles_per_block, nblocks);
   }
   return hipGetLastError();
 }
