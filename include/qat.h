@@ -59,7 +59,8 @@ int qat_abi_version(void);
  * Kernel timing for benchmarks: while enabled, the library records a pair of
  * HIP events on the launch stream around each of its main kernels
  * (names: "moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn",
- * "moba_current_attn", "moba_generic_attn", "esa_compress", "esa_scores",
+ * "moba_current_attn", "moba_generic_attn", "moba_decode_select",
+ * "moba_decode_attn", "moba_decode_combine", "esa_compress", "esa_scores",
  * "esa_decode_scan", "esa_topk", "esa_prefill_attn", "esa_decode_attn",
  * "esa_generic_attn"). The events are timing-only (created without the
  * system-scope fence on completion, so recording them does not slow the
@@ -214,6 +215,45 @@ int moba_block_select(const qat_moba_params* p, const void* q, const void* k, in
 int moba_sparse_attn(const qat_moba_params* p, const void* q, const void* k, const void* v,
                      const int32_t* blk, void* out, float* lse, void* ws, size_t ws_bytes,
                      void* stream);
+
+/*
+ * Decode steps ([MoBA] section 3: gating and attention are defined per query
+ * token, so generation applies them to each new token; complete blocks never
+ * change once written, so their means are computed once and kept).
+ *
+ * moba_block_means: the means of complete blocks [first_block, first_block +
+ * n_blocks) into the caller's cache
+ *   kbar: [batch, seq_len / block, Hkv, d] float32, block b at row b,
+ * accumulated in float64 as in moba_block_select. Only those rows are
+ * written. k as in moba_block_select. Requires first_block >= 0, n_blocks >=
+ * 0 and first_block + n_blocks <= seq_len / block (complete blocks only).
+ * Workspace: moba_workspace_size(p).
+ */
+int moba_block_means(const qat_moba_params* p, const void* k, int64_t first_block, int64_t n_blocks,
+                     float* kbar, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moba_decode_select: the gating of moba_block_select (same scores, order,
+ * ties and output) for the rows q_start .. q_start+q_len-1, scored against a
+ * kbar cache filled by moba_block_means for every block below the rows' own
+ * blocks (blocks 0 .. (q_start+q_len-1)/block - 1).
+ * q: [batch, q_len, Hq, d] -- only the processed rows. kbar may be NULL
+ * when no row has an earlier block (topk == 1 or every row in block 0).
+ * No workspace.
+ */
+int moba_decode_select(const qat_moba_params* p, const void* q, const float* kbar, int32_t* blk,
+                       void* stream);
+
+/*
+ * moba_decode_attn: moba_sparse_attn (same key sets and outputs) with
+ * q: [batch, q_len, Hq, d] holding only the processed rows; k, v hold the
+ * whole sequence (the KV cache, positions 0 .. seq_len-1; keys past a row's
+ * position are never read). With q_len <= 8 and no window each row's keys
+ * are cut into pieces of up to 256 keys attended in parallel and merged by
+ * log-sum-exp. Workspace: moba_workspace_size(p).
+ */
+int moba_decode_attn(const qat_moba_params* p, const void* q, const void* k, const void* v,
+                     const int32_t* blk, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

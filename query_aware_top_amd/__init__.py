@@ -23,6 +23,9 @@ from ._binding import (  # noqa: F401
     moba_workspace_size,
     moba_block_select,
     moba_sparse_attn,
+    moba_block_means,
+    moba_decode_select,
+    moba_decode_attn,
     EXPORTED_SYMBOLS,
     timing_enable,
     timing_select,

@@ -17,7 +17,8 @@ EXPORTED_SYMBOLS = (
     "qat_last_error", "qat_abi_version", "qat_timing_enable", "qat_timing_select", "qat_timing_reset",
     "qat_timing_query",
     "esa_workspace_size", "esa_compress_workspace_size", "esa_compress", "esa_select", "esa_sparse_attn",
-    "moba_workspace_size", "moba_block_select", "moba_sparse_attn",
+    "moba_workspace_size", "moba_block_select", "moba_sparse_attn", "moba_block_means", "moba_decode_select",
+    "moba_decode_attn",
 )
 
 
@@ -72,6 +73,9 @@ def lib():
         L.qat_timing_reset.argtypes = []
         L.qat_timing_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         L.moba_sparse_attn.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moba_block_means.argtypes = [ctypes.POINTER(MobaParams), vp, i64, i64, vp, vp, sz, vp]
+        L.moba_decode_select.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp]
+        L.moba_decode_attn.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTED_SYMBOLS:
             getattr(L, name).restype = ctypes.c_int if name != "qat_last_error" else ctypes.c_char_p
         _lib = L
@@ -264,5 +268,51 @@ def moba_sparse_attn(p: MobaParams, q, k, v, blk, out=None, lse=None, want_lse=T
         lse = torch.empty(p.batch, p.q_len, p.n_q_heads, dtype=torch.float32, device=dev)
     ws = _workspace(moba_workspace_size(p), dev, ws)
     _check(lib().moba_sparse_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(blk), _ptr(out), _ptr(lse),
+                                  _ptr(ws), ws.numel(), _stream()))
+    return out, lse
+
+
+def moba_block_means(p: MobaParams, k, first_block, n_blocks, kbar=None, ws=None):
+    """Fills blocks [first_block, first_block + n_blocks) of the mean cache
+    kbar [batch, seq_len // block, Hkv, d] float32 (allocated, zeroed, when
+    None) and returns it."""
+    dt = torch.bfloat16 if p.dtype == QAT_BF16 else torch.float32
+    _need(k, "k", dt)
+    if kbar is None:
+        kbar = torch.zeros(p.batch, p.seq_len // p.block, p.n_kv_heads, p.head_dim, dtype=torch.float32,
+                           device=k.device)
+    _need(kbar, "kbar", torch.float32)
+    ws = _workspace(moba_workspace_size(p), k.device, ws)
+    _check(lib().moba_block_means(ctypes.byref(p), _ptr(k), int(first_block), int(n_blocks), _ptr(kbar), _ptr(ws),
+                                  ws.numel(), _stream()))
+    return kbar
+
+
+def moba_decode_select(p: MobaParams, q, kbar, blk=None):
+    """q: [batch, q_len, Hq, d] (the processed rows only). Returns blk
+    [batch, q_len, Hq, topk] int32, as moba_block_select."""
+    dt = torch.bfloat16 if p.dtype == QAT_BF16 else torch.float32
+    _need(q, "q", dt)
+    _need(kbar, "kbar", torch.float32)
+    if blk is None:
+        blk = torch.empty(p.batch, p.q_len, p.n_q_heads, p.topk, dtype=torch.int32, device=q.device)
+    _check(lib().moba_decode_select(ctypes.byref(p), _ptr(q), _ptr(kbar), _ptr(blk), _stream()))
+    return blk
+
+
+def moba_decode_attn(p: MobaParams, q, k, v, blk, out=None, lse=None, want_lse=True, ws=None):
+    """q: [batch, q_len, Hq, d] (the processed rows only); k, v the whole
+    sequence. Returns (out [batch, q_len, Hq, d], lse [batch, q_len, Hq] or None)."""
+    dt = torch.bfloat16 if p.dtype == QAT_BF16 else torch.float32
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, dt)
+    _need(blk, "blk", torch.int32)
+    dev = q.device
+    if out is None:
+        out = torch.empty(p.batch, p.q_len, p.n_q_heads, p.head_dim, dtype=dt, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(p.batch, p.q_len, p.n_q_heads, dtype=torch.float32, device=dev)
+    ws = _workspace(moba_workspace_size(p), dev, ws)
+    _check(lib().moba_decode_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(blk), _ptr(out), _ptr(lse),
                                   _ptr(ws), ws.numel(), _stream()))
     return out, lse

@@ -145,8 +145,18 @@ struct MobaLayout {
   int32_t* ntiles = nullptr;
   void* part_o = nullptr;
   float* part_lse = nullptr;
+  bool decode = false;        // few rows, no window: split-key kernels
+  int dec_pieces = 0;
+  float* dec_po = nullptr;    // [rows, dec_pieces, d] piece outputs
+  float* dec_plse = nullptr;  // [rows, dec_pieces] piece log-sum-exps
   size_t bytes = 0;
 };
+
+// Few query rows per (sequence, head) and no extra window: the split-key
+// kernels (one wave per row and piece of up to 256 keys) replace the tiled
+// ones, whose tiles would hold one or two rows.
+constexpr int64_t kMobaDecodeMaxQ = 8;
+constexpr int kMobaDecodeMaxPieces = 64;
 
 int moba_check(const qat_moba_params* p) {
   if (!p) return fail(QAT_EINVAL, "params is NULL");
@@ -189,6 +199,12 @@ MobaLayout moba_layout(const qat_moba_params* p, void* ws) {
   L.ntiles = c.take<int32_t>(1);
   L.part_o = (void*)c.take<char>((size_t)L.nrows * (p->topk - 1) * p->head_dim * esz + 1);
   L.part_lse = c.take<float>((size_t)L.nrows * (p->topk - 1) + 1);
+  L.dec_pieces = qat::moba_decode_pieces(p->block, p->topk);
+  L.decode = p->window == 0 && p->q_len <= kMobaDecodeMaxQ && L.dec_pieces <= kMobaDecodeMaxPieces;
+  if (L.decode) {
+    L.dec_po = c.take<float>((size_t)L.nrows * L.dec_pieces * p->head_dim);
+    L.dec_plse = c.take<float>((size_t)L.nrows * L.dec_pieces);
+  }
   L.bytes = c.bytes();
   return L;
 }
@@ -459,6 +475,38 @@ QAT_EXPORT int moba_block_select(const qat_moba_params* p, const void* q, const 
   return hip_status(e, "moba_block_select: scoring");
 }
 
+// Attention for the rows of p with q holding q_seq positions per sequence
+// from position q_off on.
+int moba_attn_rows(const qat_moba_params* p, const void* q, int64_t q_seq, int64_t q_off, const void* k,
+                   const void* v, const int32_t* blk, void* out, float* lse, const MobaLayout& L, hipStream_t s,
+                   const char* who) {
+  const bool bf = p->dtype == QAT_BF16;
+  hipError_t e;
+  if (L.decode) {
+    e = qat::launch_moba_decode(q, k, v, blk, L.dec_po, L.dec_plse, out, lse, bf, p->batch, p->seq_len, q_seq,
+                                q_off, p->n_q_heads, p->n_kv_heads, p->head_dim, p->q_start, p->q_len, p->block,
+                                p->topk, p->scale, s);
+  } else if (bf && p->window == 0 && q_seq == p->seq_len) {
+    if (p->topk > 1 && L.nbuckets > 0) {
+      qat::KTimer tm("moba_dispatch", s);
+      e = qat::launch_moba_dispatch(blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim,
+                                    p->q_start, p->q_len, p->block, p->topk, L.nbc, L.counts, L.offsets, L.cursor,
+                                    L.entries, L.tiles, L.ntiles, s);
+      if (e != hipSuccess) return hip_status(e, who);
+    }
+    e = qat::launch_moba_attn_mfma(q, k, v, blk, L.tiles, L.ntiles, L.entries, L.part_o, L.part_lse, out, lse,
+                                   p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim, L.nbc,
+                                   p->q_start, p->q_len, p->block, p->topk, p->scale,
+                                   L.nbuckets > 0 ? L.max_tiles : 0, s);
+  } else {
+    qat::KTimer tm("moba_generic_attn", s);
+    e = qat::launch_moba_generic(q, k, v, blk, out, lse, bf, p->batch, p->seq_len, q_seq, q_off, p->n_q_heads,
+                                 p->n_kv_heads, p->head_dim, p->q_start, p->q_len, p->block, p->topk, p->window,
+                                 p->scale, s);
+  }
+  return hip_status(e, who);
+}
+
 QAT_EXPORT int moba_sparse_attn(const qat_moba_params* p, const void* q, const void* k, const void* v,
                                 const int32_t* blk, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   int rc = moba_check(p);
@@ -467,25 +515,53 @@ QAT_EXPORT int moba_sparse_attn(const qat_moba_params* p, const void* q, const v
   MobaLayout L = moba_layout(p, nullptr);
   if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
   L = moba_layout(p, ws);
+  return moba_attn_rows(p, q, p->seq_len, 0, k, v, blk, out, lse, L, (hipStream_t)stream, "moba_sparse_attn");
+}
+
+QAT_EXPORT int moba_block_means(const qat_moba_params* p, const void* k, int64_t first_block, int64_t n_blocks,
+                                float* kbar, void* ws, size_t ws_bytes, void* stream) {
+  int rc = moba_check(p);
+  if (rc) return rc;
+  if (!k || !kbar) return fail(QAT_EINVAL, "k, kbar must be non-NULL");
+  const int64_t nbc = p->seq_len / p->block;
+  if (first_block < 0 || n_blocks < 0 || first_block + n_blocks > nbc)
+    return fail(QAT_EINVAL, "blocks [%lld, %lld) are not complete blocks of a %lld-token sequence",
+                (long long)first_block, (long long)(first_block + n_blocks), (long long)p->seq_len);
+  MobaLayout L = moba_layout(p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  L = moba_layout(p, ws);
   hipStream_t s = (hipStream_t)stream;
-  const bool bf = p->dtype == QAT_BF16;
-  hipError_t e;
-  if (bf && p->window == 0) {
-    if (p->topk > 1 && L.nbuckets > 0) {
-      qat::KTimer tm("moba_dispatch", s);
-      e = qat::launch_moba_dispatch(blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim,
-                                    p->q_start, p->q_len, p->block, p->topk, L.nbc, L.counts, L.offsets, L.cursor,
-                                    L.entries, L.tiles, L.ntiles, s);
-      if (e != hipSuccess) return hip_status(e, "moba_sparse_attn: dispatch");
-    }
-    e = qat::launch_moba_attn_mfma(q, k, v, blk, L.tiles, L.ntiles, L.entries, L.part_o, L.part_lse, out, lse,
-                                   p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim, L.nbc,
-                                   p->q_start, p->q_len, p->block, p->topk, p->scale,
-                                   L.nbuckets > 0 ? L.max_tiles : 0, s);
-  } else {
-    qat::KTimer tm("moba_generic_attn", s);
-    e = qat::launch_moba_generic(q, k, v, blk, out, lse, bf, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads,
-                                 p->head_dim, p->q_start, p->q_len, p->block, p->topk, p->window, p->scale, s);
-  }
-  return hip_status(e, "moba_sparse_attn");
+  qat::KTimer tm("moba_meanpool", s);
+  hipError_t e = qat::launch_moba_meanpool(k, p->dtype == QAT_BF16, p->batch, p->seq_len, p->n_kv_heads,
+                                           p->head_dim, p->block, nbc, L.mp_part, kbar, nullptr, s, first_block,
+                                           n_blocks);
+  return hip_status(e, "moba_block_means");
+}
+
+QAT_EXPORT int moba_decode_select(const qat_moba_params* p, const void* q, const float* kbar, int32_t* blk,
+                                  void* stream) {
+  int rc = moba_check(p);
+  if (rc) return rc;
+  if (!q || !blk) return fail(QAT_EINVAL, "q, blk must be non-NULL");
+  // the means are read only when some row has an earlier complete block
+  const bool need_means = p->topk > 1 && (p->q_start + p->q_len - 1) / p->block > 0;
+  if (need_means && !kbar) return fail(QAT_EINVAL, "kbar must be non-NULL");
+  hipStream_t s = (hipStream_t)stream;
+  qat::KTimer tm("moba_decode_select", s);
+  hipError_t e = qat::launch_moba_select_means(q, p->dtype == QAT_BF16, kbar, blk, p->batch, p->seq_len, p->q_len,
+                                               p->q_start, p->n_q_heads, p->n_kv_heads, p->head_dim,
+                                               p->seq_len / p->block, p->q_start, p->q_len, p->block, p->topk, s);
+  return hip_status(e, "moba_decode_select");
+}
+
+QAT_EXPORT int moba_decode_attn(const qat_moba_params* p, const void* q, const void* k, const void* v,
+                                const int32_t* blk, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int rc = moba_check(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !blk || !out) return fail(QAT_EINVAL, "q, k, v, blk, out must be non-NULL");
+  MobaLayout L = moba_layout(p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  L = moba_layout(p, ws);
+  return moba_attn_rows(p, q, p->q_len, p->q_start, k, v, blk, out, lse, L, (hipStream_t)stream,
+                        "moba_decode_attn");
 }

@@ -16,6 +16,8 @@
 
 namespace qat {
 
+constexpr int kMobaDecPiece = 256;   // keys per decode piece
+
 template <typename T, int E>
 __device__ __forceinline__ void load_piece(const T* p, float (&x)[E]) {
 #pragma unroll
@@ -76,7 +78,8 @@ struct WaveRowAttn {
       m = m_new;
     }
   }
-  __device__ void finish(T* dst, float* lse) {
+  template <typename O>
+  __device__ void finish(O* dst, float* lse) {
     float mg = fmaxf(m, __shfl_xor(m, 16, 64));
     mg = fmaxf(mg, __shfl_xor(mg, 32, 64));
     const float a = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - mg);
@@ -89,18 +92,21 @@ struct WaveRowAttn {
       float ot = o[e] * a;
       ot += __shfl_xor(ot, 16, 64);
       ot += __shfl_xor(ot, 32, 64);
-      if (grp == 0) dst[sub * E + e] = from_f32<T>(ot * inv);
+      if (grp == 0) dst[sub * E + e] = from_f32<O>(ot * inv);
     }
     if (lse && (threadIdx.x & 63) == 0) *lse = lt > 0.f ? mg * 0.6931471805599453f + logf(lt) : -__builtin_inff();
   }
 };
 
-// MoBA: row = ((bi * q_len) + r) * hq + h, one wave each.
+// MoBA: row = ((bi * q_len) + r) * hq + h, one wave each. q holds q_seq
+// positions per sequence starting at position q_off (q_seq = seq_len,
+// q_off = 0: the whole sequence; q_seq = q_len, q_off = q_start: only the
+// processed rows).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void moba_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ blk,
-    T* __restrict__ out, float* __restrict__ lse, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
-    int64_t q_start, int64_t q_len, int block, int topk, int window, float scale_log2) {
+    T* __restrict__ out, float* __restrict__ lse, int64_t batch, int64_t seq_len, int64_t q_seq, int64_t q_off,
+    int64_t hq, int64_t hkv, int64_t q_start, int64_t q_len, int block, int topk, int window, float scale_log2) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= batch * q_len * hq) return;
   const int64_t h = row % hq;
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(256) void moba_generic_kernel(
   const int64_t cur = t / block;
   const int32_t* br = blk + row * topk;
   WaveRowAttn<T, D> ra;
-  ra.init(q + ((bi * seq_len + t) * hq + h) * D, scale_log2);
+  ra.init(q + ((bi * q_seq + t - q_off) * hq + h) * D, scale_log2);
   const int64_t base = (bi * seq_len * hkv + g) * D, stride = hkv * D;
   auto span = [&](int64_t a, int64_t b) {   // keys a .. b-1
     ra.keys(k, v, b - a, [=](int64_t j) { return base + (a + j) * stride; });
@@ -164,19 +170,93 @@ __global__ __launch_bounds__(256) void esa_generic_kernel(
   ra.finish(out + row * D, lse ? lse + row : nullptr);
 }
 
+// MoBA with few query rows (decode): the key set of a row is cut into pieces
+// of up to kMobaDecPiece keys (each gated earlier block into ppb pieces, then
+// the own block's causal part); one wave per (row, piece) leaves the piece's
+// normalised o (float32) and lse, and moba_decode_combine_kernel merges a
+// row's pieces by log-sum-exp. A piece past the row's keys leaves lse = -inf.
+// q layout as in moba_generic_kernel.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void moba_decode_piece_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ blk,
+    float* __restrict__ po, float* __restrict__ plse, int64_t rows, int64_t seq_len, int64_t q_seq, int64_t q_off,
+    int64_t hq, int64_t hkv, int64_t q_start, int64_t q_len, int block, int topk, float scale_log2, int ppb,
+    int npieces) {
+  const int64_t row = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int piece = blockIdx.x;
+  const int64_t h = row % hq;
+  const int64_t r = (row / hq) % q_len;
+  const int64_t bi = row / (hq * q_len);
+  const int64_t g = h / (hq / hkv);
+  const int64_t t = q_start + r;
+  const int64_t cur = t / block;
+  const int32_t* br = blk + row * topk;
+  // the piece's key range [a, e): the s-th earlier block among the first
+  // topk - 1 slots (slot order), or the own block from its start to t
+  int64_t a = 0, e = 0;
+  int s = piece / ppb;
+  const int sub = piece % ppb;
+  int nth = 0;
+  bool found = false;
+  for (int sl = 0; sl < topk - 1; ++sl) {
+    const int32_t b = br[sl];
+    if (b < 0 || b >= cur) continue;
+    if (nth++ == s) {
+      a = (int64_t)b * block + (int64_t)sub * kMobaDecPiece;
+      e = min(a + kMobaDecPiece, (int64_t)(b + 1) * block);
+      found = true;
+      break;
+    }
+  }
+  if (!found) {   // past the earlier blocks: pieces of the own block
+    const int64_t own = piece - (int64_t)nth * ppb;
+    a = cur * block + own * kMobaDecPiece;
+    e = min(a + kMobaDecPiece, t + 1);
+  }
+  WaveRowAttn<T, D> ra;
+  ra.init(q + ((bi * q_seq + t - q_off) * hq + h) * D, scale_log2);
+  const int64_t base = (bi * seq_len * hkv + g) * D, stride = hkv * D;
+  ra.keys(k, v, max((int64_t)0, e - a), [=](int64_t j) { return base + (a + j) * stride; });
+  const int64_t pi = row * npieces + piece;
+  ra.finish(po + pi * D, plse + pi);
+}
+
+// One thread per (row, d): log-sum-exp merge of the row's pieces.
+template <typename T, int D>
+__global__ void moba_decode_combine_kernel(const float* __restrict__ po, const float* __restrict__ plse,
+                                           int npieces, int64_t rows, T* __restrict__ out,
+                                           float* __restrict__ lse) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * D) return;
+  const int64_t row = idx / D;
+  const int d = (int)(idx % D);
+  const float* lr = plse + row * npieces;
+  float m = -__builtin_inff();
+  for (int p = 0; p < npieces; ++p) m = fmaxf(m, lr[p]);
+  float l = 0.f, o = 0.f;
+  for (int p = 0; p < npieces; ++p) {
+    const float w = lr[p] == -__builtin_inff() ? 0.f : expf(lr[p] - m);
+    l += w;
+    o = fmaf(w, po[(row * npieces + p) * D + d], o);
+  }
+  out[row * D + d] = from_f32<T>(l > 0.f ? o / l : 0.f);
+  if (lse && d == 0) lse[row] = l > 0.f ? m + logf(l) : -__builtin_inff();
+}
+
 // ---------------------------------------------------------------------------
 hipError_t launch_moba_generic(const void* q, const void* k, const void* v, const int32_t* blk, void* out,
-                               float* lse, bool bf, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
-                               int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int window,
-                               float scale, hipStream_t s) {
+                               float* lse, bool bf, int64_t batch, int64_t seq_len, int64_t q_seq, int64_t q_off,
+                               int64_t hq, int64_t hkv, int64_t d, int64_t q_start, int64_t q_len, int block,
+                               int topk, int window, float scale, hipStream_t s) {
   const int64_t rows = batch * q_len * hq;
   if (rows == 0) return hipSuccess;
   const float sl2 = scale * 1.4426950408889634f;
   dim3 grid((unsigned)cdiv(rows, 4));
 #define QAT_MG(T_, D_)                                                                                     \
   launch_timed("moba_generic_attn", moba_generic_kernel<T_, D_>, grid, dim3(256), 0, s, (const T_*)q,        \
-               (const T_*)k, (const T_*)v, blk, (T_*)out, lse, batch, seq_len, hq, hkv, q_start, q_len, block, \
-               topk, window, sl2)
+               (const T_*)k, (const T_*)v, blk, (T_*)out, lse, batch, seq_len, q_seq, q_off, hq, hkv, q_start,   \
+               q_len, block, topk, window, sl2)
   if (bf) {
     if (d == 64) QAT_MG(bf16, 64);
     else QAT_MG(bf16, 128);
@@ -185,6 +265,47 @@ hipError_t launch_moba_generic(const void* q, const void* k, const void* v, cons
     else QAT_MG(float, 128);
   }
 #undef QAT_MG
+  return hipGetLastError();
+}
+
+int moba_decode_pieces(int block, int topk) {
+  const int ppb = (int)cdiv(block, kMobaDecPiece);
+  return (topk - 1) * ppb + ppb;
+}
+
+hipError_t launch_moba_decode(const void* q, const void* k, const void* v, const int32_t* blk, float* po,
+                              float* plse, void* out, float* lse, bool bf, int64_t batch, int64_t seq_len,
+                              int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv, int64_t d, int64_t q_start,
+                              int64_t q_len, int block, int topk, float scale, hipStream_t s) {
+  const int64_t rows = batch * q_len * hq;
+  if (rows == 0) return hipSuccess;
+  const float sl2 = scale * 1.4426950408889634f;
+  const int ppb = (int)cdiv(block, kMobaDecPiece);
+  const int np = moba_decode_pieces(block, topk);
+  dim3 grid((unsigned)np, (unsigned)cdiv(rows, 4));
+  const unsigned g2 = (unsigned)cdiv(rows * d, 256);
+#define QAT_MD(T_, D_)                                                                                          \
+  do {                                                                                                          \
+    {                                                                                                           \
+      KTimer tm_("moba_decode_attn", s);                                                                        \
+      launch_timed("moba_decode_attn", moba_decode_piece_kernel<T_, D_>, grid, dim3(256), 0, s, (const T_*)q,    \
+                   (const T_*)k, (const T_*)v, blk, po, plse, rows, seq_len, q_seq, q_off, hq, hkv, q_start,      \
+                   q_len, block, topk, sl2, ppb, np);                                                           \
+    }                                                                                                           \
+    hipError_t e_ = hipGetLastError();                                                                          \
+    if (e_ != hipSuccess) return e_;                                                                            \
+    KTimer tc_("moba_decode_combine", s);                                                                       \
+    launch_timed("moba_decode_combine", moba_decode_combine_kernel<T_, D_>, dim3(g2), dim3(256), 0, s,          \
+                 (const float*)po, (const float*)plse, np, rows, (T_*)out, lse);                                \
+  } while (0)
+  if (bf) {
+    if (d == 64) QAT_MD(bf16, 64);
+    else QAT_MD(bf16, 128);
+  } else {
+    if (d == 64) QAT_MD(float, 64);
+    else QAT_MD(float, 128);
+  }
+#undef QAT_MD
   return hipGetLastError();
 }
 

@@ -22,10 +22,18 @@ hipError_t launch_compress_finalize(const double* partial, int nsplit, int64_t n
 
 // ---- MoBA gating (moba_select.hip) ----------------------------------------
 int meanpool_splits(int block);
-// planes: NULL, or 3 * batch*nbc*hkv*d bfloat16 (hi/mid/lo split of the means)
+// Means of blocks [first, first + count) (count < 0: through nbc) into kbar
+// [batch, nbc, hkv*d]; planes: NULL, or 3 * batch*nbc*hkv*d bfloat16 (hi/mid/lo
+// split of the means), written only for the whole range.
 hipError_t launch_moba_meanpool(const void* k, bool bf, int64_t batch, int64_t seq_len, int64_t hkv, int64_t d,
                                 int block, int64_t nbc, double* partial, float* kbar, bf16* planes,
-                                hipStream_t s);
+                                hipStream_t s, int64_t first = 0, int64_t count = -1);
+// Scoring from float32 means kbar [batch, nbc, hkv, d] (a cache of complete
+// blocks); q laid out as for launch_moba_decode.
+hipError_t launch_moba_select_means(const void* q, bool bf, const float* kbar, int32_t* blk, int64_t batch,
+                                    int64_t seq_len, int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv,
+                                    int64_t d, int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk,
+                                    hipStream_t s);
 // bfloat16 queries score on the matrix cores from `planes`; float32 ones use `kbar`
 hipError_t launch_moba_select(const void* q, bool bf, const float* kbar, const bf16* planes, int32_t* blk,
                               int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t nbc,
@@ -47,10 +55,20 @@ hipError_t launch_moba_attn_mfma(const void* q, const void* k, const void* v, co
                                  int topk, float scale, int64_t max_tiles, hipStream_t s);
 
 // ---- generic per-row attention (attn_generic.hip) -------------------------
+// q holds q_seq positions per sequence from position q_off on (the whole
+// sequence: q_seq = seq_len, q_off = 0; only the processed rows: q_seq =
+// q_len, q_off = q_start).
+// MoBA with few query rows (no window): pieces of up to 256 keys, one wave
+// each; po: rows * moba_decode_pieces * d floats, plse: rows * pieces floats.
+int moba_decode_pieces(int block, int topk);
+hipError_t launch_moba_decode(const void* q, const void* k, const void* v, const int32_t* blk, float* po,
+                              float* plse, void* out, float* lse, bool bf, int64_t batch, int64_t seq_len,
+                              int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv, int64_t d, int64_t q_start,
+                              int64_t q_len, int block, int topk, float scale, hipStream_t s);
 hipError_t launch_moba_generic(const void* q, const void* k, const void* v, const int32_t* blk, void* out,
-                               float* lse, bool bf, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
-                               int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int window,
-                               float scale, hipStream_t s);
+                               float* lse, bool bf, int64_t batch, int64_t seq_len, int64_t q_seq, int64_t q_off,
+                               int64_t hq, int64_t hkv, int64_t d, int64_t q_start, int64_t q_len, int block,
+                               int topk, int window, float scale, hipStream_t s);
 hipError_t launch_esa_generic(const void* q, const void* k, const void* v, const int32_t* sel, const int32_t* n_sel,
                               void* out, float* lse, bool bf, int64_t batch, int64_t H, int64_t d, int64_t ctx_len,
                               int64_t c0, int64_t m, int64_t n_init, int64_t window, int topk, float scale,

@@ -79,9 +79,11 @@ __global__ __launch_bounds__(kMpThreads) void meanpool_partial_kernel(
 // float32 means it writes, when `planes` is non-NULL, three bfloat16 planes
 // hi/mid/lo with hi + mid + lo == mean exactly (each term is the rounded
 // remainder of the previous ones), the operands of the matrix-core scoring.
-__global__ void meanpool_finalize_kernel(const double* __restrict__ partial, int nsplit, int64_t nrows,
-                                         int64_t cols, int block, float* __restrict__ kbar,
-                                         bf16* __restrict__ planes) {
+// The partials cover blocks [first, first + count) of each sequence; the
+// means land in a [batch, nbc_total, cols] array.
+__global__ void meanpool_finalize_kernel(const double* __restrict__ partial, int nsplit, int64_t count,
+                                         int64_t nbc_total, int64_t first, int64_t nrows, int64_t cols, int block,
+                                         float* __restrict__ kbar, bf16* __restrict__ planes) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = nrows * cols;
   if (idx >= total) return;
@@ -89,7 +91,7 @@ __global__ void meanpool_finalize_kernel(const double* __restrict__ partial, int
   double s = 0.0;
   for (int i = 0; i < nsplit; ++i) s += partial[(r * nsplit + i) * cols + c];
   const float x = (float)(s / (double)block);
-  kbar[idx] = x;
+  kbar[((r / count) * nbc_total + first + r % count) * cols + c] = x;
   if (planes) {
     const bf16 hi = (bf16)x;
     const float r1 = x - (float)hi;
@@ -138,8 +140,8 @@ constexpr int kSelChunk = 64;   // block means staged per LDS round
 template <typename T, int D, int KMAX>
 __global__ __launch_bounds__(256) void moba_score_select_kernel(
     const T* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ blk,
-    int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block,
-    int topk) {
+    int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len,
+    int block, int topk) {
   __shared__ float kb_s[kSelChunk * D];
   const int64_t bi = blockIdx.z;
   const int64_t h = blockIdx.y;
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(256) void moba_score_select_kernel(
 
   float qf[D];
   {
-    const T* qp = q + ((bi * seq_len + t) * hq + h) * D;
+    const T* qp = q + ((bi * q_seq + t - q_off) * hq + h) * D;
 #pragma unroll
     for (int i = 0; i < D; ++i) qf[i] = to_f32(qp[i]);
   }
@@ -208,6 +210,97 @@ __global__ __launch_bounds__(256) void moba_score_select_kernel(
 #pragma unroll
   for (int i = 0; i < KMAX; ++i)
     if (i < npick) out[i] = ti[i];
+  out[npick] = (int32_t)cur;
+  for (int i = npick + 1; i < topk; ++i) out[i] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// Scoring and selection with one wave per query row, for few rows over many
+// blocks (decode). Lane i scores blocks i, i + 64, ... below the row's own
+// block, in ascending order, into a running top list (the dot product is
+// summed as in moba_score_select_kernel, so the two give the same scores);
+// the wave then takes the row's picks from the 64 lists one at a time by
+// arg-max over the lists' heads (score desc, ties to the smaller block).
+constexpr int kSelRowsMaxQ = 16;   // rows per (sequence, head) up to which this kernel is used
+
+template <typename T, int D, int KMAX>
+__global__ __launch_bounds__(256) void moba_select_rows_kernel(
+    const T* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ blk, int64_t rows,
+    int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len,
+    int block, int topk) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t h = row % hq;
+  const int64_t r = (row / hq) % q_len;
+  const int64_t bi = row / (hq * q_len);
+  const int64_t g = h / (hq / hkv);
+  const int64_t t = q_start + r;
+  const int64_t cur = t / block;
+  const int km = topk - 1;
+  float qf[D];
+  {
+    const T* qp = q + ((bi * q_seq + t - q_off) * hq + h) * D;
+#pragma unroll
+    for (int i = 0; i < D; ++i) qf[i] = to_f32(qp[i]);
+  }
+  float tv[KMAX];
+  int ti[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) { tv[i] = -__builtin_inff(); ti[i] = 0x7fffffff; }
+  const int64_t ncand = km > 0 ? min(cur, nbc) : 0;
+  const float* kb_g = kbar + (bi * nbc * hkv + g) * D;   // block b at kb_g + b*hkv*D
+  for (int64_t b = lane; b < ncand; b += 64) {
+    const float4* kr = reinterpret_cast<const float4*>(kb_g + b * hkv * D);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      const float4 x = kr[i];
+      a0 = fmaf(qf[4 * i + 0], x.x, a0);
+      a1 = fmaf(qf[4 * i + 1], x.y, a1);
+      a2 = fmaf(qf[4 * i + 2], x.z, a2);
+      a3 = fmaf(qf[4 * i + 3], x.w, a3);
+    }
+    top_insert<KMAX>(tv, ti, (a0 + a1) + (a2 + a3), (int)b);
+  }
+  const int npick = (int)min((int64_t)km, cur);
+  int pick[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    pick[i] = 0x7fffffff;
+    if (i < npick) {
+      float bv = tv[0];
+      int bb = ti[0];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int ob = __shfl_xor(bb, off, 64);
+        if (ov > bv || (ov == bv && ob < bb)) { bv = ov; bb = ob; }
+      }
+      pick[i] = bb;
+      if (ti[0] == bb) {   // the winning lane drops its head
+#pragma unroll
+        for (int j = 0; j + 1 < KMAX; ++j) { tv[j] = tv[j + 1]; ti[j] = ti[j + 1]; }
+        tv[KMAX - 1] = -__builtin_inff();
+        ti[KMAX - 1] = 0x7fffffff;
+      }
+    }
+  }
+  // ascending block order, then the own block, -1 padding
+#pragma unroll
+  for (int a = 0; a < KMAX; ++a)
+#pragma unroll
+    for (int b2 = 0; b2 + 1 < KMAX - a; ++b2) {
+      const int lo = min(pick[b2], pick[b2 + 1]);
+      const int hi = max(pick[b2], pick[b2 + 1]);
+      pick[b2] = lo;
+      pick[b2 + 1] = hi;
+    }
+  if (lane != 0) return;
+  int32_t* out = blk + row * topk;
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i)
+    if (i < npick) out[i] = pick[i];
   out[npick] = (int32_t)cur;
   for (int i = npick + 1; i < topk; ++i) out[i] = -1;
 }
@@ -560,35 +653,38 @@ int meanpool_splits(int block) { return (int)cdiv(block, meanpool_tokens_per_spl
 
 hipError_t launch_moba_meanpool(const void* k, bool bf, int64_t batch, int64_t seq_len, int64_t hkv,
                                 int64_t d, int block, int64_t nbc, double* partial, float* kbar, bf16* planes,
-                                hipStream_t s) {
-  if (nbc <= 0) return hipSuccess;
+                                hipStream_t s, int64_t first, int64_t count) {
+  if (count < 0) count = nbc - first;
+  if (count <= 0) return hipSuccess;
   const int nsplit = meanpool_splits(block);
   const int tps = meanpool_tokens_per_split(block);
   const int64_t cols = hkv * d;
-  dim3 grid((unsigned)nsplit, (unsigned)nbc, (unsigned)batch);
+  const int64_t shift = first * block * cols;   // elements: block `first` of sequence 0
+  dim3 grid((unsigned)nsplit, (unsigned)count, (unsigned)batch);
   if (bf)
-    hipLaunchKernelGGL(meanpool_partial_kernel<bf16>, grid, dim3(kMpThreads), 0, s, (const bf16*)k, seq_len,
-                       cols, block, tps, nsplit, nbc, partial);
+    hipLaunchKernelGGL(meanpool_partial_kernel<bf16>, grid, dim3(kMpThreads), 0, s, (const bf16*)k + shift,
+                       seq_len, cols, block, tps, nsplit, count, partial);
   else
-    hipLaunchKernelGGL(meanpool_partial_kernel<float>, grid, dim3(kMpThreads), 0, s, (const float*)k, seq_len,
-                       cols, block, tps, nsplit, nbc, partial);
+    hipLaunchKernelGGL(meanpool_partial_kernel<float>, grid, dim3(kMpThreads), 0, s, (const float*)k + shift,
+                       seq_len, cols, block, tps, nsplit, count, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t total = batch * nbc * cols;
+  const int64_t total = batch * count * cols;
   hipLaunchKernelGGL(meanpool_finalize_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
-                     partial, nsplit, batch * nbc, cols, block, kbar, planes);
+                     partial, nsplit, count, nbc, first, batch * count, cols, block, kbar,
+                     (first == 0 && count == nbc) ? planes : nullptr);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_select_d(const T* q, const float* kbar, int32_t* blk, int64_t batch,
-                                  int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start,
-                                  int64_t q_len, int block, int topk, hipStream_t s) {
+                                  int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv, int64_t nbc,
+                                  int64_t q_start, int64_t q_len, int block, int topk, hipStream_t s) {
   dim3 grid((unsigned)cdiv(q_len, 256), (unsigned)hq, (unsigned)batch);
   const int km = topk - 1;
 #define QAT_SEL(KM_)                                                                                    \
-  hipLaunchKernelGGL((moba_score_select_kernel<T, D, KM_>), grid, dim3(256), 0, s, q, kbar, blk, seq_len, \
-                     hq, hkv, nbc, q_start, q_len, block, topk)
+  hipLaunchKernelGGL((moba_score_select_kernel<T, D, KM_>), grid, dim3(256), 0, s, q, kbar, blk, q_seq,   \
+                     q_off, hq, hkv, nbc, q_start, q_len, block, topk)
   if (km <= 1) QAT_SEL(1);
   else if (km == 2) QAT_SEL(2);
   else if (km == 3) QAT_SEL(3);
@@ -637,6 +733,49 @@ static hipError_t launch_select_mfma_d(const bf16* q, const bf16* planes, int64_
   return hipGetLastError();
 }
 
+template <typename T, int D>
+static hipError_t launch_select_rows_d(const T* q, const float* kbar, int32_t* blk, int64_t batch,
+                                       int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv, int64_t nbc,
+                                       int64_t q_start, int64_t q_len, int block, int topk, hipStream_t s) {
+  const int64_t rows = batch * q_len * hq;
+  dim3 grid((unsigned)cdiv(rows, 4));
+#define QAT_SEL(KM_)                                                                                      \
+  hipLaunchKernelGGL((moba_select_rows_kernel<T, D, KM_>), grid, dim3(256), 0, s, q, kbar, blk, rows,      \
+                     q_seq, q_off, hq, hkv, nbc, q_start, q_len, block, topk)
+  const int km = topk - 1;
+  if (km <= 1) QAT_SEL(1);
+  else if (km == 2) QAT_SEL(2);
+  else if (km == 3) QAT_SEL(3);
+  else if (km <= 7) QAT_SEL(7);
+  else QAT_SEL(15);
+#undef QAT_SEL
+  return hipGetLastError();
+}
+
+// Scoring from a float32 mean cache: few rows per head (decode) take a wave
+// per row; longer row ranges the workgroup-per-256-rows kernel, which shares
+// each staged mean among its rows.
+hipError_t launch_moba_select_means(const void* q, bool bf, const float* kbar, int32_t* blk, int64_t batch,
+                                    int64_t seq_len, int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv,
+                                    int64_t d, int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk,
+                                    hipStream_t s) {
+  (void)seq_len;
+  if (q_len <= 0) return hipSuccess;
+  const bool few = q_len <= kSelRowsMaxQ;
+#define QAT_SM(T_, D_)                                                                                     \
+  return few ? launch_select_rows_d<T_, D_>((const T_*)q, kbar, blk, batch, q_seq, q_off, hq, hkv, nbc,     \
+                                            q_start, q_len, block, topk, s)                                 \
+             : launch_select_d<T_, D_>((const T_*)q, kbar, blk, batch, q_seq, q_off, hq, hkv, nbc, q_start, \
+                                       q_len, block, topk, s)
+  if (bf) {
+    if (d == 64) QAT_SM(bf16, 64);
+    QAT_SM(bf16, 128);
+  }
+  if (d == 64) QAT_SM(float, 64);
+  QAT_SM(float, 128);
+#undef QAT_SM
+}
+
 hipError_t launch_moba_select(const void* q, bool bf, const float* kbar, const bf16* planes, int32_t* blk,
                               int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t nbc,
                               int64_t q_start, int64_t q_len, int block, int topk, hipStream_t s) {
@@ -650,9 +789,9 @@ hipError_t launch_moba_select(const void* q, bool bf, const float* kbar, const b
                                      q_len, block, topk, s);
   }
   if (d == 64)
-    return launch_select_d<float, 64>((const float*)q, kbar, blk, batch, seq_len, hq, hkv, nbc, q_start,
+    return launch_select_d<float, 64>((const float*)q, kbar, blk, batch, seq_len, 0, hq, hkv, nbc, q_start,
                                       q_len, block, topk, s);
-  return launch_select_d<float, 128>((const float*)q, kbar, blk, batch, seq_len, hq, hkv, nbc, q_start,
+  return launch_select_d<float, 128>((const float*)q, kbar, blk, batch, seq_len, 0, hq, hkv, nbc, q_start,
                                      q_len, block, topk, s);
 }
 

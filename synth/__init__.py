@@ -6,8 +6,9 @@ itself, so the oracle and the GPU path stay independent of each other while
 consuming the same input bits.
 """
 from .gen import (normal, normal_np, splitmix64_np, planted_block_ids,
-                  needle_positions, moba_inputs, esa_inputs, compression_weights)
+                  needle_positions, moba_inputs, moba_decode_inputs, esa_inputs,
+                  compression_weights)
 
 __all__ = ["normal", "normal_np", "splitmix64_np", "planted_block_ids",
-           "needle_positions", "moba_inputs", "esa_inputs",
+           "needle_positions", "moba_inputs", "moba_decode_inputs", "esa_inputs",
            "compression_weights"]

@@ -178,6 +178,29 @@ def moba_inputs(seed: int, batch: int, n: int, hq: int, hkv: int, d: int,
     return q, k, v, info
 
 
+def moba_decode_inputs(seed: int, batch: int, n: int, q_len: int, hq: int, hkv: int, d: int,
+                       dtype=torch.bfloat16, device="cpu", planted: int = 0, block: int = 0):
+    """Decode-step inputs: the KV cache k, v [batch, n, hkv, d] as in
+    moba_inputs (same draws and planting for the same seed) and the queries of
+    the last q_len positions only, q [batch, q_len, hq, d], drawn from their
+    own stream (tensor id TID_Q, counters from 1 << 40 on)."""
+    k = normal(seed, TID_K, (batch, n, hkv, d), dtype, device)
+    v = normal(seed, TID_V, (batch, n, hkv, d), dtype, device)
+    info = {}
+    if planted:
+        nb = n // block
+        ids = planted_block_ids(seed, planted, nb - 1)
+        info["planted_blocks"] = ids
+        for r, b in enumerate(ids):
+            centre = normal(seed, TID_STRUCT, (batch, 1, hkv, d), torch.float64,
+                            device, start=(r + 1) << 32)
+            sl = slice(b * block, (b + 1) * block)
+            z = k[:, sl].to(torch.float64)
+            k[:, sl] = (centre + 0.25 * z).to(dtype)
+    q = normal(seed, TID_Q, (batch, q_len, hq, d), dtype, device, start=1 << 40)
+    return q, k, v, info
+
+
 def compression_weights(seed: int, d_c: int, d_model: int, tensor_id: int = TID_W,
                         dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
     """W = G / sqrt(d_model) with G ~ N(0,1) rounded to bf16 first; for a

@@ -165,3 +165,33 @@ def test_compress_validation(lib):
                           dummy, None, ctypes.c_int64(128), dummy, ctypes.c_int64(128), ctypes.c_int32(1), dummy,
                           ctypes.c_size_t(n.value), None)
     assert rc == QAT_EINVAL
+
+
+def test_decode_entry_points_validation(lib):
+    dummy = ctypes.c_void_p(0x1000)
+    p = _moba(q_start=4095, q_len=1)
+    rc, need = _size(lib, "moba_workspace_size", p)
+    assert rc == QAT_OK
+    # block range past the complete blocks (4096 / 256 = 16)
+    for first, n in ((15, 2), (-1, 1), (0, -1)):
+        rc = lib.moba_block_means(ctypes.byref(p), dummy, ctypes.c_int64(first), ctypes.c_int64(n), dummy, dummy,
+                                  ctypes.c_size_t(need), ctypes.c_void_p(0))
+        assert rc == QAT_EINVAL, (first, n)
+    rc = lib.moba_block_means(ctypes.byref(p), dummy, ctypes.c_int64(0), ctypes.c_int64(16), dummy, dummy,
+                              ctypes.c_size_t(need - 1), ctypes.c_void_p(0))
+    assert rc == QAT_EWORKSPACE
+    # the cache is needed once a row has an earlier block
+    assert lib.moba_decode_select(ctypes.byref(p), dummy, None, dummy, ctypes.c_void_p(0)) == QAT_EINVAL
+    rc = lib.moba_decode_attn(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, None, dummy,
+                              ctypes.c_size_t(need - 256), ctypes.c_void_p(0))
+    assert rc == QAT_EWORKSPACE
+    rc = lib.moba_decode_attn(ctypes.byref(p), dummy, None, dummy, dummy, dummy, None, dummy,
+                              ctypes.c_size_t(need), ctypes.c_void_p(0))
+    assert rc == QAT_EINVAL
+
+
+def test_decode_workspace_holds_the_piece_buffers(lib):
+    # few rows: the split-key buffers are part of the workspace
+    few = _size(lib, "moba_workspace_size", _moba(q_start=4095, q_len=1, n_q_heads=2, n_kv_heads=2))[1]
+    many = _size(lib, "moba_workspace_size", _moba(q_start=4000, q_len=9, n_q_heads=2, n_kv_heads=2))[1]
+    assert few > 0 and many > 0
