@@ -11,7 +11,7 @@ Prints one JSON line. Default workload: MoBA prefill at the 8B-style GQA
 shape (32 query / 8 KV heads x 128, N = 32768, block 512, top-k 3 with the
 forced block, 8 planted key blocks), reported as query tokens per second.
 Other workloads (--workload): moba_fp32_4k, esa_prefill_64k,
-esa_decode_128k, moba_long_512k.
+esa_decode_128k, moba_long_512k, moba_decode_128k.
 """
 from __future__ import annotations
 
@@ -46,6 +46,9 @@ STAGE_SOURCES = {
     "moba_past_attn": ["moba_attn.hip", "attn_core.h"],
     "moba_current_attn": ["moba_attn.hip", "attn_core.h"],
     "moba_generic_attn": ["attn_generic.hip"],
+    "moba_decode_select": ["moba_select.hip"],
+    "moba_decode_attn": ["attn_generic.hip"],
+    "moba_decode_combine": ["attn_generic.hip"],
     "esa_compress*": ["compress.hip"],
     "esa_scores": ["esa_select.hip"],
     "esa_topk": ["esa_select.hip"],
@@ -187,6 +190,98 @@ class MobaWorkload(Workload):
                           f"process and thread; {el:.1f} s"}
 
 
+class MobaDecodeWorkload(Workload):
+    """One MoBA decode step for a batch of sequences: the newest complete
+    block's mean enters the kept cache (charged to every step, although a
+    block completes only once per `block` steps), the new token's query rows
+    are gated against the cache, and attend their gated blocks plus their own
+    block up to the token."""
+
+    def __init__(self, name, seed, batch, n, hq, hkv, d, block, topk, planted=0):
+        import query_aware_top_amd as qat
+        import synth
+        self.qat = qat
+        self.name = name
+        self.unit, self.higher_is_better = "us/step", False
+        self.dtype = "bf16"
+        self.B, self.n, self.hq, self.hkv, self.d, self.block, self.topk = batch, n, hq, hkv, d, block, topk
+        self.q, self.k, self.v, _ = synth.moba_decode_inputs(seed, batch, n, 1, hq, hkv, d, torch.bfloat16,
+                                                             "cuda", planted=planted, block=block)
+        self.p = qat.moba_params(batch=batch, seq_len=n, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, q_start=n - 1,
+                                 q_len=1, block=block, topk=topk, dtype=torch.bfloat16)
+        self.ws = torch.empty(qat.moba_workspace_size(self.p), dtype=torch.uint8, device="cuda")
+        # the cache as earlier steps left it: every complete block before the
+        # newest one (untimed prologue)
+        self.newest = (n - 1) // block - 1
+        self.kbar = qat.moba_block_means(self.p, self.k, 0, self.newest, ws=self.ws)
+        self.blk = torch.empty(batch, 1, hq, topk, dtype=torch.int32, device="cuda")
+        self.out = torch.empty(batch, 1, hq, d, dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty(batch, 1, hq, dtype=torch.float32, device="cuda")
+        self.dominant, self.bound = "moba_decode_attn", "hbm"
+
+    def step(self):
+        qat = self.qat
+        qat.moba_block_means(self.p, self.k, self.newest, 1, self.kbar, ws=self.ws)
+        qat.moba_decode_select(self.p, self.q, self.kbar, blk=self.blk)
+        qat.moba_decode_attn(self.p, self.q, self.k, self.v, self.blk, out=self.out, lse=self.lse, ws=self.ws)
+
+    def value(self, sec):
+        return sec * 1e6
+
+    def dominant_work(self):
+        """Distinct K and V rows the step must read (per sequence and KV
+        head: the union of its query heads' gated blocks, plus the own block
+        up to the token) and the query rows, in bytes."""
+        blk = self.blk[:, 0].to("cpu")
+        t = self.n - 1
+        cur = t // self.block
+        own = t - cur * self.block + 1
+        rows = 0
+        grp = self.hq // self.hkv
+        for bi in range(self.B):
+            for g in range(self.hkv):
+                b = blk[bi, g * grp:(g + 1) * grp].flatten().tolist()
+                past = {x for x in b if 0 <= x < cur}
+                rows += len(past) * self.block + own
+        return rows * self.d * 2 * 2 + self.B * self.hq * self.d * 2
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "seq_len": self.n, "n_q_heads": self.hq,
+                "n_kv_heads": self.hkv, "head_dim": self.d, "block": self.block, "topk_incl_current": self.topk,
+                "query_rows_per_sequence": 1}
+
+    def cpu_baseline(self, budget_s=12.0):
+        """The float64 oracle on host cores for sequence 0, with the block
+        means of its complete blocks computed beforehand (the kept cache):
+        the newest block's mean, gating and attention of all heads; scaled by
+        the batch."""
+        import numpy as np
+        from oracle import attention as oatt
+        from oracle import moba as omoba
+        kn = self.k[0].to("cpu").to(torch.float64).numpy()
+        vn = self.v[0].to("cpu").to(torch.float64).numpy()
+        kbar = omoba.block_means(kn, self.block)
+        qt = self.q[0, 0].to("cpu").to(torch.float64).numpy()
+        t = self.n - 1
+        reps = 0
+        t0 = time.perf_counter()
+        while reps < 1 or time.perf_counter() - t0 < budget_s:
+            nb = self.newest
+            omoba.block_means(kn[nb * self.block:(nb + 1) * self.block], self.block)
+            for h in range(self.hq):
+                g = omoba.kv_head(h, self.hq, self.hkv)
+                blk, _ = omoba.select_row(qt[h], kbar[:, g], t, self.block, self.topk)
+                idx = omoba.key_set(blk, t, self.block)
+                oatt.attend(qt[h], kn[idx, g], vn[idx, g], self.p.scale)
+            reps += 1
+        el = time.perf_counter() - t0
+        return {"value": el / reps * 1e6 * self.B, "unit": "us/step", "cores": _blas_threads(), "kind": "oracle",
+                "sample": f"sequence 0 of {self.B}, {reps} repetitions of its step (newest block mean, gating "
+                          f"and attention of all {self.hq} heads; the other block means computed beforehand as "
+                          f"the kept cache), scaled by {self.B} sequences; float64 numpy, one process; "
+                          f"{el:.1f} s"}
+
+
 class EsaWorkload(Workload):
     def __init__(self, name, seed, batch, T, m, H, d, d_c, n_init, W, topk, radius, clip, needles=0):
         import query_aware_top_amd as qat
@@ -323,6 +418,8 @@ def make(name):
         return MobaWorkload(name, 1, 4096, 4, 4, 64, 256, 3, torch.float32)
     if name == "moba_long_512k":
         return MobaWorkload(name, 5, 524288, 8, 8, 128, 8192, 3, torch.bfloat16, attn_rows=8192)
+    if name == "moba_decode_128k":
+        return MobaDecodeWorkload(name, 128, 16, 131072, 32, 8, 128, 512, 3, planted=8)
     if name == "esa_prefill_64k":
         return EsaWorkload(name, 3, 1, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0)
     if name == "esa_decode_128k":
@@ -397,7 +494,8 @@ def main():
     qat.timing_enable(False)
     kernels = {}
     for name in ("moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn", "moba_current_attn",
-                 "moba_generic_attn", "esa_compress", "esa_qcompress", "esa_scores", "esa_decode_scan", "esa_topk",
+                 "moba_generic_attn", "moba_decode_select", "moba_decode_attn", "moba_decode_combine",
+                 "esa_compress", "esa_qcompress", "esa_scores", "esa_decode_scan", "esa_topk",
                  "esa_prefill_attn", "esa_decode_attn", "esa_generic_attn"):
         tot, n = qat.timing_query(name)
         if n:
@@ -405,13 +503,14 @@ def main():
     qat.timing_reset()
     # spread of single steps (outside the timed region above): events around
     # each step; for the HBM-bound workload also with L2 and the 256 MiB
-    # Infinity Cache flushed before every step (1 GiB streamed, untimed)
+    # Infinity Cache flushed before every step by reading 1 GiB of other data
+    # (untimed; a read leaves clean lines, so the step pays no write-back)
     def step_times(flush):
-        buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if flush else None
+        buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if flush else None
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         for a, b in ev:
             if flush:
-                buf.fill_(1.0)
+                buf.sum()
             a.record()
             w.step()
             b.record()
@@ -424,9 +523,18 @@ def main():
 
     warm = step_times(False)
     spread = {"p10": pct(warm, 0.1), "p50": pct(warm, 0.5), "p90": pct(warm, 0.9)}
+    cold_dom_ms = None
     if w.bound == "hbm":
+        # the dominant kernel's launches in these cold steps are timed too
+        qat.timing_enable(True)
+        qat.timing_select(w.dominant)
+        qat.timing_reset()
         cold = step_times(True)
+        tot, n = qat.timing_query(w.dominant)
+        qat.timing_enable(False)
+        qat.timing_reset()
         spread["cold_p50"] = pct(cold, 0.5)
+        cold_dom_ms = round(tot / n, 4) if n else None
     work = w.dominant_work()
     if w.bound == "hbm":
         achieved = work / (dom_ms * 1e-3) / 1e9
@@ -438,6 +546,9 @@ def main():
         achieved = work / (dom_ms * 1e-3) / 1e12
         peak, unit = PEAK_F32_TFLOPS, "TFLOP/s"
     value = w.value(ms * 1e-3)
+    if cold_dom_ms:
+        # the same kernel with L2 and the Infinity Cache flushed before each step
+        cold_rate = work / (cold_dom_ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -459,6 +570,9 @@ def main():
         "kernels_avg_ms": kernels,
         "step_ms": spread,
     }
+    if cold_dom_ms:
+        line["roofline"]["cold_avg_launch_ms"] = cold_dom_ms
+        line["roofline"]["cold_frac"] = round(cold_rate / peak, 4)
     if not args.no_cpu_baseline:
         cb = w.cpu_baseline()
         cb["sample"] += f"; host {_cpu_model()}, {os.cpu_count()} logical CPUs"

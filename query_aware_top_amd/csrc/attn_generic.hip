@@ -16,7 +16,17 @@
 
 namespace qat {
 
-constexpr int kMobaDecPiece = 256;   // keys per decode piece
+#ifndef QAT_DEC_PIECE
+#define QAT_DEC_PIECE 256
+#endif
+#ifndef QAT_DEC_KEYS
+#define QAT_DEC_KEYS 4
+#endif
+#ifndef QAT_DEC_PIPE
+#define QAT_DEC_PIPE 1
+#endif
+constexpr int kMobaDecPiece = QAT_DEC_PIECE;   // keys per decode piece
+constexpr int kMobaDecKeys = QAT_DEC_KEYS;     // keys per 16-lane group and step in a piece
 
 template <typename T, int E>
 __device__ __forceinline__ void load_piece(const T* p, float (&x)[E]) {
@@ -53,29 +63,112 @@ struct WaveRowAttn {
     return s * sl2;
   }
   // The row's keys j = 0 .. n-1; off(j) is key j's element offset in K and V.
-  // Two keys per group and step; a group's missing key (past n) reads key 0
-  // and enters with weight 0.
-  template <typename Off>
-  __device__ void keys(const T* __restrict__ K, const T* __restrict__ V, int64_t n, Off off) {
-    for (int64_t j0 = 0; j0 < n; j0 += 8) {
-      const int64_t ja = j0 + grp, jb = j0 + 4 + grp;
-      const bool oka = ja < n, okb = jb < n;
-      const int64_t fa = off(oka ? ja : 0), fb = off(okb ? jb : 0);
-      float ka[E], kb[E], va[E], vb[E];
-      load_piece<T, E>(K + fa + sub * E, ka);
-      load_piece<T, E>(K + fb + sub * E, kb);
-      load_piece<T, E>(V + fa + sub * E, va);
-      load_piece<T, E>(V + fb + sub * E, vb);
-      const float xa = oka ? score(ka) : -__builtin_inff();
-      const float xb = okb ? score(kb) : -__builtin_inff();
-      const float m_new = fmaxf(m, fmaxf(xa, xb));
+  // NK keys per group and step (all their loads issued before any use); a
+  // group's missing key (past n) reads key 0 and enters with weight 0.
+  template <int NK, typename Off>
+  __device__ void keys_n(const T* __restrict__ K, const T* __restrict__ V, int64_t n, Off off) {
+    for (int64_t j0 = 0; j0 < n; j0 += 4 * NK) {
+      float kx[NK][E], vx[NK][E];
+      bool ok[NK];
+#pragma unroll
+      for (int u = 0; u < NK; ++u) {
+        const int64_t j = j0 + 4 * u + grp;
+        ok[u] = j < n;
+        const int64_t f = off(ok[u] ? j : 0);
+        load_piece<T, E>(K + f + sub * E, kx[u]);
+        load_piece<T, E>(V + f + sub * E, vx[u]);
+      }
+      float x[NK];
+      float m_new = m;
+#pragma unroll
+      for (int u = 0; u < NK; ++u) {
+        x[u] = ok[u] ? score(kx[u]) : -__builtin_inff();
+        m_new = fmaxf(m_new, x[u]);
+      }
       if (m_new == -__builtin_inff()) continue;   // this group has no key yet
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m = -inf
-      const float pa = __builtin_amdgcn_exp2f(xa - m_new), pb = __builtin_amdgcn_exp2f(xb - m_new);
-      l = fmaf(l, alpha, pa + pb);
+      float ps = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = fmaf(o[e], alpha, fmaf(pa, va[e], pb * vb[e]));
+      for (int u = 0; u < NK; ++u) {
+        x[u] = __builtin_amdgcn_exp2f(x[u] - m_new);
+        ps += x[u];
+      }
+      l = fmaf(l, alpha, ps);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float acc = o[e] * alpha;
+#pragma unroll
+        for (int u = 0; u < NK; ++u) acc = fmaf(x[u], vx[u][e], acc);
+        o[e] = acc;
+      }
       m = m_new;
+    }
+  }
+  template <typename Off>
+  __device__ void keys(const T* __restrict__ K, const T* __restrict__ V, int64_t n, Off off) {
+    keys_n<2>(K, V, n, off);
+  }
+  // As keys_n, software-pipelined: the loads of the next step's 4 NK keys
+  // are in flight while the current step is scored and accumulated (two
+  // register buffers of raw K and V pieces, used alternately).
+  typedef T vec_t __attribute__((ext_vector_type(E)));
+  template <int NK, typename Off>
+  __device__ __forceinline__ void issue_step(vec_t (&kx)[NK], vec_t (&vx)[NK], const T* __restrict__ K,
+                                             const T* __restrict__ V, int64_t j0, int64_t n, Off off) {
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int64_t j = j0 + 4 * u + grp;
+      const int64_t f = off(j < n ? j : 0) + sub * E;
+      kx[u] = *reinterpret_cast<const vec_t*>(K + f);
+      vx[u] = *reinterpret_cast<const vec_t*>(V + f);
+    }
+  }
+  template <int NK>
+  __device__ __forceinline__ void consume_step(const vec_t (&kx)[NK], const vec_t (&vx)[NK], int64_t j0,
+                                               int64_t n) {
+    float x[NK];
+    float m_new = m;
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      float kf[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) kf[e] = to_f32(kx[u][e]);
+      x[u] = j0 + 4 * u + grp < n ? score(kf) : -__builtin_inff();
+      m_new = fmaxf(m_new, x[u]);
+    }
+    if (m_new == -__builtin_inff()) return;   // this group has no key yet
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    float ps = 0.f;
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      x[u] = __builtin_amdgcn_exp2f(x[u] - m_new);
+      ps += x[u];
+    }
+    l = fmaf(l, alpha, ps);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float acc = o[e] * alpha;
+#pragma unroll
+      for (int u = 0; u < NK; ++u) acc = fmaf(x[u], to_f32(vx[u][e]), acc);
+      o[e] = acc;
+    }
+    m = m_new;
+  }
+  template <int NK, typename Off>
+  __device__ void keys_pipe(const T* __restrict__ K, const T* __restrict__ V, int64_t n, Off off) {
+    constexpr int S = 4 * NK;
+    if (n <= 0) return;
+    vec_t ka[NK], va[NK], kb[NK], vb[NK];
+    issue_step<NK>(ka, va, K, V, 0, n, off);
+    for (int64_t j0 = 0;; j0 += 2 * S) {
+      const bool more1 = j0 + S < n;
+      if (more1) issue_step<NK>(kb, vb, K, V, j0 + S, n, off);
+      consume_step<NK>(ka, va, j0, n);
+      if (!more1) break;
+      const bool more2 = j0 + 2 * S < n;
+      if (more2) issue_step<NK>(ka, va, K, V, j0 + 2 * S, n, off);
+      consume_step<NK>(kb, vb, j0 + S, n);
+      if (!more2) break;
     }
   }
   template <typename O>
@@ -217,7 +310,11 @@ __global__ __launch_bounds__(256) void moba_decode_piece_kernel(
   WaveRowAttn<T, D> ra;
   ra.init(q + ((bi * q_seq + t - q_off) * hq + h) * D, scale_log2);
   const int64_t base = (bi * seq_len * hkv + g) * D, stride = hkv * D;
-  ra.keys(k, v, max((int64_t)0, e - a), [=](int64_t j) { return base + (a + j) * stride; });
+#if QAT_DEC_PIPE
+  ra.template keys_pipe<kMobaDecKeys>(k, v, max((int64_t)0, e - a), [=](int64_t j) { return base + (a + j) * stride; });
+#else
+  ra.template keys_n<kMobaDecKeys>(k, v, max((int64_t)0, e - a), [=](int64_t j) { return base + (a + j) * stride; });
+#endif
   const int64_t pi = row * npieces + piece;
   ra.finish(po + pi * D, plse + pi);
 }

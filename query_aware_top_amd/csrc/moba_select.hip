@@ -75,6 +75,63 @@ __global__ __launch_bounds__(kMpThreads) void meanpool_partial_kernel(
   }
 }
 
+// Mean pool in one pass, for launches over few blocks (a cache update, a
+// short prefix): a workgroup per (64 columns, block, sequence); thread
+// (lane l, column group c) sums tokens l, l + 32, ... of the block over the
+// group's 8 columns in float64, and the 32 lane sums of a column are added in
+// lane order through LDS. The float64 sums of bfloat16 keys are exact in any
+// order, so the means equal those of the two-pass path.
+constexpr int kMpdLanes = 32;
+template <typename T>
+__global__ __launch_bounds__(256) void meanpool_direct_kernel(
+    const T* __restrict__ k, int64_t seq_len, int64_t cols, int block, int64_t count, int64_t nbc_total,
+    int64_t first, float* __restrict__ kbar, bf16* __restrict__ planes) {
+  __shared__ double red[kMpdLanes][65];
+  const int cg = threadIdx.x & 7, tl = threadIdx.x >> 3;
+  const int64_t c0 = (int64_t)blockIdx.x * 64 + cg * 8;
+  const int64_t b = blockIdx.y, bi = blockIdx.z;
+  const T* base = k + (bi * seq_len + b * block) * cols + c0;
+  double a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = 0.0;
+  int t = tl;
+  for (; t + (kMpUnroll - 1) * kMpdLanes < block; t += kMpUnroll * kMpdLanes) {
+    float v[kMpUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kMpUnroll; ++u) load8<T>(base + (int64_t)(t + u * kMpdLanes) * cols, v[u]);
+#pragma unroll
+    for (int u = 0; u < kMpUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] += (double)v[u][i];
+  }
+  for (; t < block; t += kMpdLanes) {
+    float v[8];
+    load8<T>(base + (int64_t)t * cols, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] += (double)v[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[tl][cg * 8 + i] = a[i];
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int c = threadIdx.x;
+  double s = 0.0;
+  for (int l = 0; l < kMpdLanes; ++l) s += red[l][c];
+  const float x = (float)(s / (double)block);
+  const int64_t col = (int64_t)blockIdx.x * 64 + c;
+  kbar[((bi * nbc_total) + first + b) * cols + col] = x;
+  if (planes) {   // whole range only: row bi * count + b of the planes
+    const int64_t idx = (bi * count + b) * cols + col, total = gridDim.z * count * cols;
+    const bf16 hi = (bf16)x;
+    const float r1 = x - (float)hi;
+    const bf16 mid = (bf16)r1;
+    const bf16 lo = (bf16)(r1 - (float)mid);
+    planes[idx] = hi;
+    planes[total + idx] = mid;
+    planes[2 * total + idx] = lo;
+  }
+}
+
 // Mean pool, pass 2: sum the slices in order and divide by B. Besides the
 // float32 means it writes, when `planes` is non-NULL, three bfloat16 planes
 // hi/mid/lo with hi + mid + lo == mean exactly (each term is the rounded
@@ -215,94 +272,140 @@ __global__ __launch_bounds__(256) void moba_score_select_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Scoring and selection with one wave per query row, for few rows over many
-// blocks (decode). Lane i scores blocks i, i + 64, ... below the row's own
-// block, in ascending order, into a running top list (the dot product is
-// summed as in moba_score_select_kernel, so the two give the same scores);
-// the wave then takes the row's picks from the 64 lists one at a time by
-// arg-max over the lists' heads (score desc, ties to the smaller block).
-constexpr int kSelRowsMaxQ = 16;   // rows per (sequence, head) up to which this kernel is used
+// Scoring and selection for few query positions over many blocks (decode),
+// one workgroup of 16 waves per (sequence, position, KV head): the group's
+// query heads share the position, hence the candidate blocks, and each mean
+// read. Heads go four at a time. A wave scores four blocks per step, 16 lanes
+// per block: lane i of a 16-lane group holds dims [i E, (i + 1) E) (E = D / 16)
+// of the four heads' queries in registers and reads the same dims of its
+// block's mean (each block's mean row is read as one contiguous piece), and
+// the 16 partial sums are added by lane exchanges. Lane j < 4 of a group then
+// inserts head j's score into its running top list (score desc, ties to the
+// smaller block; each list sees its blocks in ascending order). Each pick is
+// the arg-max over all lists of that head: lane exchanges across the wave's
+// four groups, then across the 16 waves through LDS.
+constexpr int kSelRowsMaxQ = 16;   // positions per sequence up to which this kernel is used
+constexpr int kSelGWaves = 16;
 
 template <typename T, int D, int KMAX>
-__global__ __launch_bounds__(256) void moba_select_rows_kernel(
-    const T* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ blk, int64_t rows,
-    int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len,
-    int block, int topk) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
-  const int64_t h = row % hq;
-  const int64_t r = (row / hq) % q_len;
-  const int64_t bi = row / (hq * q_len);
-  const int64_t g = h / (hq / hkv);
+__global__ __launch_bounds__(kSelGWaves * 64) void moba_select_group_kernel(
+    const T* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ blk, int64_t q_seq,
+    int64_t q_off, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk) {
+  constexpr int E = D / 16;
+  __shared__ float red_v[2][kSelGWaves][4];
+  __shared__ int red_i[2][kSelGWaves][4];
+  const int64_t r = blockIdx.x, g = blockIdx.y, bi = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int grp = lane >> 4, sub = lane & 15;
   const int64_t t = q_start + r;
   const int64_t cur = t / block;
   const int km = topk - 1;
-  float qf[D];
-  {
-    const T* qp = q + ((bi * q_seq + t - q_off) * hq + h) * D;
-#pragma unroll
-    for (int i = 0; i < D; ++i) qf[i] = to_f32(qp[i]);
-  }
-  float tv[KMAX];
-  int ti[KMAX];
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i) { tv[i] = -__builtin_inff(); ti[i] = 0x7fffffff; }
   const int64_t ncand = km > 0 ? min(cur, nbc) : 0;
-  const float* kb_g = kbar + (bi * nbc * hkv + g) * D;   // block b at kb_g + b*hkv*D
-  for (int64_t b = lane; b < ncand; b += 64) {
-    const float4* kr = reinterpret_cast<const float4*>(kb_g + b * hkv * D);
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      const float4 x = kr[i];
-      a0 = fmaf(qf[4 * i + 0], x.x, a0);
-      a1 = fmaf(qf[4 * i + 1], x.y, a1);
-      a2 = fmaf(qf[4 * i + 2], x.z, a2);
-      a3 = fmaf(qf[4 * i + 3], x.w, a3);
-    }
-    top_insert<KMAX>(tv, ti, (a0 + a1) + (a2 + a3), (int)b);
-  }
   const int npick = (int)min((int64_t)km, cur);
-  int pick[KMAX];
+  const int64_t G = hq / hkv;
+  const float* kb_g = kbar + (bi * nbc * hkv + g) * D + sub * E;   // block b: + b*hkv*D
+  int round = 0;
+  for (int64_t h0 = 0; h0 < G; h0 += 4) {
+    const int nh = (int)min((int64_t)4, G - h0);
+    float qv[4][E];
 #pragma unroll
-  for (int i = 0; i < KMAX; ++i) {
-    pick[i] = 0x7fffffff;
-    if (i < npick) {
-      float bv = tv[0];
-      int bb = ti[0];
+    for (int j = 0; j < 4; ++j) {
+      const T* qp = q + ((bi * q_seq + t - q_off) * hq + g * G + h0 + min(j, nh - 1)) * D + sub * E;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int ob = __shfl_xor(bb, off, 64);
-        if (ov > bv || (ov == bv && ob < bb)) { bv = ov; bb = ob; }
+      for (int e = 0; e < E; ++e) qv[j][e] = to_f32(qp[e]);
+    }
+    float tv[KMAX];
+    int ti[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) { tv[i] = -__builtin_inff(); ti[i] = 0x7fffffff; }
+    // U steps' mean reads are issued together, then scored in block order
+    constexpr int U = KMAX > 7 ? 1 : 4;   // long top lists leave fewer registers
+    constexpr int64_t STEP = kSelGWaves * 4;
+    for (int64_t b0 = (int64_t)wv * 4; b0 < ncand; b0 += STEP * U) {
+      float x[U][E];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t b = b0 + u * STEP + grp;
+        const float* kr = kb_g + (b < ncand ? b : 0) * hkv * D;
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(kr + e);
+          x[u][e] = v.x; x[u][e + 1] = v.y; x[u][e + 2] = v.z; x[u][e + 3] = v.w;
+        }
       }
-      pick[i] = bb;
-      if (ti[0] == bb) {   // the winning lane drops its head
 #pragma unroll
-        for (int j = 0; j + 1 < KMAX; ++j) { tv[j] = tv[j + 1]; ti[j] = ti[j + 1]; }
-        tv[KMAX - 1] = -__builtin_inff();
-        ti[KMAX - 1] = 0x7fffffff;
+      for (int u = 0; u < U; ++u) {
+        const int64_t b = b0 + u * STEP + grp;
+        float s[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float a = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) a = fmaf(qv[j][e], x[u][e], a);
+          a += __shfl_xor(a, 8, 64);
+          a += __shfl_xor(a, 4, 64);
+          a += __shfl_xor(a, 2, 64);
+          a += __shfl_xor(a, 1, 64);
+          s[j] = a;
+        }
+        const float mine = sub == 0 ? s[0] : sub == 1 ? s[1] : sub == 2 ? s[2] : s[3];
+        if (b < ncand && sub < 4) top_insert<KMAX>(tv, ti, mine, (int)b);
       }
+    }
+    // picks of head slot j = sub (lanes sub < 4); the same in every such lane
+    int pick[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      pick[i] = 0x7fffffff;
+      if (i < npick) {
+        float bv = tv[0];
+        int bb = ti[0];
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {   // the same lane of the other groups
+          const float ov = __shfl_xor(bv, off, 64);
+          const int ob = __shfl_xor(bb, off, 64);
+          if (ov > bv || (ov == bv && ob < bb)) { bv = ov; bb = ob; }
+        }
+        const int slot = round & 1;
+        if (lane < 4) { red_v[slot][wv][lane] = bv; red_i[slot][wv][lane] = bb; }
+        __syncthreads();   // the other slot's last readers are past this barrier too
+        const int hs = sub & 3;
+        bv = red_v[slot][0][hs];
+        bb = red_i[slot][0][hs];
+#pragma unroll
+        for (int w2 = 1; w2 < kSelGWaves; ++w2) {
+          const float ov = red_v[slot][w2][hs];
+          const int ob = red_i[slot][w2][hs];
+          if (ov > bv || (ov == bv && ob < bb)) { bv = ov; bb = ob; }
+        }
+        ++round;
+        pick[i] = bb;
+        if (sub < 4 && ti[0] == bb) {   // the owner of the pick drops its list head
+#pragma unroll
+          for (int m = 0; m + 1 < KMAX; ++m) { tv[m] = tv[m + 1]; ti[m] = ti[m + 1]; }
+          tv[KMAX - 1] = -__builtin_inff();
+          ti[KMAX - 1] = 0x7fffffff;
+        }
+      }
+    }
+    if (tid < nh) {   // lane j of wave 0 holds head slot j's picks
+#pragma unroll
+      for (int a2 = 0; a2 < KMAX; ++a2)
+#pragma unroll
+        for (int b2 = 0; b2 + 1 < KMAX - a2; ++b2) {
+          const int lo = min(pick[b2], pick[b2 + 1]);
+          const int hi = max(pick[b2], pick[b2 + 1]);
+          pick[b2] = lo;
+          pick[b2 + 1] = hi;
+        }
+      int32_t* out = blk + ((bi * q_len + r) * hq + g * G + h0 + tid) * topk;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i)
+        if (i < npick) out[i] = pick[i];
+      out[npick] = (int32_t)cur;
+      for (int i = npick + 1; i < topk; ++i) out[i] = -1;
     }
   }
-  // ascending block order, then the own block, -1 padding
-#pragma unroll
-  for (int a = 0; a < KMAX; ++a)
-#pragma unroll
-    for (int b2 = 0; b2 + 1 < KMAX - a; ++b2) {
-      const int lo = min(pick[b2], pick[b2 + 1]);
-      const int hi = max(pick[b2], pick[b2 + 1]);
-      pick[b2] = lo;
-      pick[b2 + 1] = hi;
-    }
-  if (lane != 0) return;
-  int32_t* out = blk + row * topk;
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i)
-    if (i < npick) out[i] = pick[i];
-  out[npick] = (int32_t)cur;
-  for (int i = npick + 1; i < topk; ++i) out[i] = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -659,6 +762,18 @@ hipError_t launch_moba_meanpool(const void* k, bool bf, int64_t batch, int64_t s
   const int nsplit = meanpool_splits(block);
   const int tps = meanpool_tokens_per_split(block);
   const int64_t cols = hkv * d;
+  bf16* pl = (first == 0 && count == nbc) ? planes : nullptr;
+  if (batch * count * nsplit < 1024) {   // few blocks: one pass, no partials
+    dim3 g1((unsigned)(cols / 64), (unsigned)count, (unsigned)batch);
+    const int64_t shift1 = first * block * cols;
+    if (bf)
+      hipLaunchKernelGGL(meanpool_direct_kernel<bf16>, g1, dim3(256), 0, s, (const bf16*)k + shift1, seq_len,
+                         cols, block, count, nbc, first, kbar, pl);
+    else
+      hipLaunchKernelGGL(meanpool_direct_kernel<float>, g1, dim3(256), 0, s, (const float*)k + shift1, seq_len,
+                         cols, block, count, nbc, first, kbar, pl);
+    return hipGetLastError();
+  }
   const int64_t shift = first * block * cols;   // elements: block `first` of sequence 0
   dim3 grid((unsigned)nsplit, (unsigned)count, (unsigned)batch);
   if (bf)
@@ -671,8 +786,7 @@ hipError_t launch_moba_meanpool(const void* k, bool bf, int64_t batch, int64_t s
   if (e != hipSuccess) return e;
   const int64_t total = batch * count * cols;
   hipLaunchKernelGGL(meanpool_finalize_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
-                     partial, nsplit, count, nbc, first, batch * count, cols, block, kbar,
-                     (first == 0 && count == nbc) ? planes : nullptr);
+                     partial, nsplit, count, nbc, first, batch * count, cols, block, kbar, pl);
   return hipGetLastError();
 }
 
@@ -737,11 +851,10 @@ template <typename T, int D>
 static hipError_t launch_select_rows_d(const T* q, const float* kbar, int32_t* blk, int64_t batch,
                                        int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv, int64_t nbc,
                                        int64_t q_start, int64_t q_len, int block, int topk, hipStream_t s) {
-  const int64_t rows = batch * q_len * hq;
-  dim3 grid((unsigned)cdiv(rows, 4));
+  dim3 grid((unsigned)q_len, (unsigned)hkv, (unsigned)batch);
 #define QAT_SEL(KM_)                                                                                      \
-  hipLaunchKernelGGL((moba_select_rows_kernel<T, D, KM_>), grid, dim3(256), 0, s, q, kbar, blk, rows,      \
-                     q_seq, q_off, hq, hkv, nbc, q_start, q_len, block, topk)
+  hipLaunchKernelGGL((moba_select_group_kernel<T, D, KM_>), grid, dim3(kSelGWaves * 64), 0, s, q, kbar,    \
+                     blk, q_seq, q_off, hq, hkv, nbc, q_start, q_len, block, topk)
   const int km = topk - 1;
   if (km <= 1) QAT_SEL(1);
   else if (km == 2) QAT_SEL(2);
@@ -752,9 +865,9 @@ static hipError_t launch_select_rows_d(const T* q, const float* kbar, int32_t* b
   return hipGetLastError();
 }
 
-// Scoring from a float32 mean cache: few rows per head (decode) take a wave
-// per row; longer row ranges the workgroup-per-256-rows kernel, which shares
-// each staged mean among its rows.
+// Scoring from a float32 mean cache: few positions per sequence (decode)
+// take a workgroup per (sequence, position, KV head); longer ranges the
+// workgroup-per-256-rows kernel, which shares each staged mean among its rows.
 hipError_t launch_moba_select_means(const void* q, bool bf, const float* kbar, int32_t* blk, int64_t batch,
                                     int64_t seq_len, int64_t q_seq, int64_t q_off, int64_t hq, int64_t hkv,
                                     int64_t d, int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk,

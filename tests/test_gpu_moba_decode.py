@@ -85,6 +85,8 @@ DECODE = [
     (2, 1412, 4, 2, 64, 128, 3, 8, torch.float32),       # float32, 8 rows over a block boundary
     (1, 700, 2, 1, 128, 1000, 3, 1, torch.bfloat16),     # no complete block: own block only
     (1, 9000, 2, 2, 128, 1024, 5, 2, torch.bfloat16),    # 4 pieces per block
+    (2, 3333, 24, 2, 128, 128, 4, 3, torch.bfloat16),    # 12 query heads per KV head: three rounds of four
+    (1, 2600, 6, 1, 64, 256, 3, 1, torch.float32),       # 6 heads per KV head: a partial round of four
 ]
 
 
