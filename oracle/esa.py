@@ -26,6 +26,11 @@ One sequence, chunk C = [c0, c0 + m) of queries (decode: m = 1, c0 = T - 1),
 4. Correction (READING; the formula is dropped, the text says it keeps the
    relative size of scores and stops one token from dominating):
    s^_ij = max(s_ij - max_j' s_ij', -clip).
+   Alternative reading, behind a flag (correction="votes"): each query's
+   scores become a softmax over the middle part at temperature tau,
+   s^_ij = exp(tau s_ij) / sum_j' exp(tau s_ij'), so every query casts the
+   same total vote of 1 (tau defaults to 1 / sqrt(d_c), the attention
+   convention on the compressed width).
 5. Importance u_j = sum_i s^_ij over all queries of the chunk ("takes every
    current query into account"); decode has one query.
 6. Neighbour influence (READING; the formula is dropped, the text says a
@@ -78,9 +83,11 @@ def key_cache(k, Wk, bk=None):
     return round_to_bf16(compress(np.asarray(k, np.float64).reshape(T, -1), Wk, bk))
 
 
-def importance(qc, kc_mid, clip, row_chunk=256):
+def importance(qc, kc_mid, clip, row_chunk=256, correction="clamp", tau=None):
     """qc [m, d_c], kc_mid [n_M, d_c] -> (u [n_M], rowmax [m]).
-    Steps 3-5: u_j = sum_i max(s_ij - max_j' s_ij', -clip)."""
+    Steps 3-5: u_j = sum_i max(s_ij - max_j' s_ij', -clip); with
+    correction="votes", u_j = sum_i softmax_j(tau s_i.)_j (tau: None means
+    1 / sqrt(d_c))."""
     qc = np.asarray(qc, np.float64)
     kc_mid = np.asarray(kc_mid, np.float64)
     n_mid = kc_mid.shape[0]
@@ -88,11 +95,19 @@ def importance(qc, kc_mid, clip, row_chunk=256):
     rowmax = np.full(qc.shape[0], -np.inf)
     if n_mid == 0:
         return u, rowmax
+    if correction == "votes" and tau is None:
+        tau = 1.0 / np.sqrt(qc.shape[1])
     for i0 in range(0, qc.shape[0], row_chunk):
         s = qc[i0:i0 + row_chunk] @ kc_mid.T
         mrow = s.max(axis=1)
         rowmax[i0:i0 + row_chunk] = mrow
-        u += np.maximum(s - mrow[:, None], -clip).sum(axis=0)
+        if correction == "votes":
+            # the row max is subtracted only to keep exp in range; the
+            # softmax does not depend on it
+            e = np.exp(tau * (s - mrow[:, None]))
+            u += (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+        else:
+            u += np.maximum(s - mrow[:, None], -clip).sum(axis=0)
     return u, rowmax
 
 
@@ -118,7 +133,7 @@ def top_k(scores, k):
     return np.sort(order[:min(k, scores.shape[0])])
 
 
-def select(q, Wq, bq, kc_cache, c0, n_init, window, topk, radius, clip):
+def select(q, Wq, bq, kc_cache, c0, n_init, window, topk, radius, clip, correction="clamp", tau=None):
     """Selection for one sequence and chunk.
 
     q [m, H, d] the chunk's queries, kc_cache [T, d_c] the compressed key
@@ -128,7 +143,7 @@ def select(q, Wq, bq, kc_cache, c0, n_init, window, topk, radius, clip):
     m = q.shape[0]
     _, M, _ = partition(c0, n_init, window)
     qc = compress(np.asarray(q, np.float64).reshape(m, -1), Wq, bq)
-    u, rowmax = importance(qc, np.asarray(kc_cache, np.float64)[M], clip)
+    u, rowmax = importance(qc, np.asarray(kc_cache, np.float64)[M], clip, correction=correction, tau=tau)
     up = neighbour(u, radius)
     sel = M[top_k(up, topk)] if M.size else np.zeros(0, dtype=np.int64)
     return sel, up, u, rowmax

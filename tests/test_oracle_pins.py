@@ -371,6 +371,83 @@ def test_esa_decode_monotone_correction_keeps_raw_ranking():
     assert np.array_equal(sel, np.sort(M[np.argsort(-raw, kind="stable")[:12]]))
 
 
+# ---- alternative correction reading: per-query softmax votes -------------
+def _votes_case(seed, m, n_mid, d_c=6):
+    r = rng(seed)
+    return r.standard_normal((m, d_c)), round_to_bf16(r.standard_normal((n_mid, d_c)))
+
+
+def test_esa_votes_each_query_casts_one_vote():
+    """Every query's votes sum to 1, so the importances sum to m."""
+    qc, kc = _votes_case(40, 7, 50)
+    for tau in (None, 0.3, 2.0):
+        u, _ = oesa.importance(qc, kc, np.inf, correction="votes", tau=tau)
+        assert abs(u.sum() - 7) < 1e-12
+        assert np.all(u > 0)
+
+
+def test_esa_votes_two_tokens_are_logistic():
+    """One query, two middle tokens: the votes are sigma(+-tau (s0 - s1))."""
+    qc, kc = _votes_case(41, 1, 2)
+    tau = 0.7
+    s = kc @ qc[0]
+    u, _ = oesa.importance(qc, kc, np.inf, correction="votes", tau=tau)
+    want0 = 1.0 / (1.0 + math.exp(-tau * (s[0] - s[1])))
+    assert abs(u[0] - want0) < 1e-14 and abs(u[1] - (1.0 - want0)) < 1e-14
+
+
+def test_esa_votes_temperature_limits():
+    """tau -> 0: every token gets m / n_M; tau -> inf: each query's whole vote
+    goes to its own arg-max token (brute-force count)."""
+    m, n_mid = 9, 40
+    qc, kc = _votes_case(42, m, n_mid)
+    u0, _ = oesa.importance(qc, kc, np.inf, correction="votes", tau=1e-13)
+    assert np.allclose(u0, m / n_mid, rtol=0, atol=1e-9)
+    uinf, _ = oesa.importance(qc, kc, np.inf, correction="votes", tau=1e6)
+    counts = np.zeros(n_mid)
+    for i in range(m):
+        best = max(range(n_mid), key=lambda j: (float(np.dot(qc[i], kc[j])), -j))
+        counts[best] += 1
+    assert np.allclose(uinf, counts, rtol=0, atol=1e-9)
+
+
+def test_esa_votes_default_temperature_is_inverse_sqrt_width():
+    qc, kc = _votes_case(43, 3, 20, d_c=16)
+    a, _ = oesa.importance(qc, kc, np.inf, correction="votes")
+    b, _ = oesa.importance(qc, kc, np.inf, correction="votes", tau=0.25)
+    assert np.allclose(a, b, rtol=1e-14, atol=0)
+
+
+def test_esa_votes_decode_keeps_raw_ranking():
+    """One query: the votes are a monotone map of the raw scores, so the
+    selection (radius 0) is the raw-score top-k."""
+    r = rng(44)
+    T, H, d, d_c = 300, 2, 4, 6
+    q = r.standard_normal((1, H, d))
+    Wq = r.standard_normal((d_c, H * d))
+    kc = round_to_bf16(r.standard_normal((T, d_c)))
+    c0 = T - 1
+    sel, _, _, _ = oesa.select(q, Wq, None, kc, c0, 5, 20, 12, radius=0, clip=1.0, correction="votes")
+    _, M, _ = oesa.partition(c0, 5, 20)
+    raw = kc[M] @ (q.reshape(1, -1) @ Wq.T)[0]
+    assert np.array_equal(sel, np.sort(M[np.argsort(-raw, kind="stable")[:12]]))
+
+
+def test_esa_votes_differ_from_clamp_in_prefill():
+    """Several queries: the two readings rank differently in general (a query
+    with one dominant token gives it a vote near 1 under votes, but only its
+    own clamp range under the clamp)."""
+    r = rng(45)
+    m, H, d, d_c, T = 16, 2, 8, 8, 400
+    q = r.standard_normal((m, H, d))
+    Wq = r.standard_normal((d_c, H * d)) / 4
+    kc = round_to_bf16(r.standard_normal((T, d_c)))
+    c0 = T - m
+    a, _, _, _ = oesa.select(q, Wq, None, kc, c0, 4, 32, 40, radius=0, clip=5.0)
+    b, _, _, _ = oesa.select(q, Wq, None, kc, c0, 4, 32, 40, radius=0, clip=5.0, correction="votes")
+    assert not np.array_equal(a, b)
+
+
 def test_esa_radius_lifts_neighbours_of_a_peak():
     u = np.zeros(20)
     u[7] = 5.0
