@@ -11,7 +11,8 @@ Prints one JSON line. Default workload: MoBA prefill at the 8B-style GQA
 shape (32 query / 8 KV heads x 128, N = 32768, block 512, top-k 3 with the
 forced block, 8 planted key blocks), reported as query tokens per second.
 Other workloads (--workload): moba_fp32_4k, esa_prefill_64k,
-esa_decode_128k, moba_long_512k, moba_decode_128k.
+esa_decode_128k, moba_long_512k, moba_decode_128k, and esa_prefill_64k_votes /
+esa_decode_128k_votes (the softmax-vote reading of ESA's score correction).
 """
 from __future__ import annotations
 
@@ -283,7 +284,8 @@ class MobaDecodeWorkload(Workload):
 
 
 class EsaWorkload(Workload):
-    def __init__(self, name, seed, batch, T, m, H, d, d_c, n_init, W, topk, radius, clip, needles=0):
+    def __init__(self, name, seed, batch, T, m, H, d, d_c, n_init, W, topk, radius, clip, needles=0,
+                 correction="clamp"):
         import query_aware_top_amd as qat
         import synth
         self.qat = qat
@@ -302,8 +304,10 @@ class EsaWorkload(Workload):
                     self.k[bi, t] = val
         self.Wq = synth.compression_weights(seed, d_c, H * d, synth.gen.TID_W, dtype, "cuda")
         self.Wk = self.Wq
+        self.correction = correction
         self.p = qat.esa_params(batch=batch, n_heads=H, head_dim=d, d_c=d_c, ctx_len=T, chunk_start=self.c0,
-                                chunk_len=m, n_init=n_init, window=W, topk=topk, radius=radius, clip=clip)
+                                chunk_len=m, n_init=n_init, window=W, topk=topk, radius=radius, clip=clip,
+                                correction=correction)
         # compressed-key cache of the tokens before the chunk: state written by
         # earlier steps (untimed prologue)
         self.kc = torch.zeros(batch, T, d_c, dtype=dtype, device="cuda")
@@ -353,7 +357,7 @@ class EsaWorkload(Workload):
     def config(self):
         return {"workload": self.name, "batch": self.B, "ctx_len": self.T, "chunk_len": self.m,
                 "n_heads": self.H, "head_dim": self.d, "d_c": self.d_c, "n_init": self.n_init,
-                "topk": self.topk, "window": self.W}
+                "topk": self.topk, "window": self.W, "correction": self.correction}
 
     def cpu_baseline(self, budget_s=12.0):
         import numpy as np
@@ -367,7 +371,7 @@ class EsaWorkload(Workload):
             kc[s:s + 8192] = oesa.key_cache(kcpu[s:s + 8192].to("cpu").to(torch.float64).numpy(), W)
         qn = self.q[bi].to("cpu").to(torch.float64).numpy()
         sel, _, _, _ = oesa.select(qn, W, None, kc, self.c0, self.n_init, self.W, self.topk, self.p.radius,
-                                   self.p.clip)
+                                   self.p.clip, correction=self.correction)
         t_sel = time.perf_counter() - t0
         rows = 0
         kk = _GpuRows(self.k[bi])
@@ -424,6 +428,11 @@ def make(name):
         return EsaWorkload(name, 3, 1, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0)
     if name == "esa_decode_128k":
         return EsaWorkload(name, 4, 16, 131072, 1, 32, 128, 128, 128, 4096, 2048, 2, 48.0, needles=16)
+    if name == "esa_prefill_64k_votes":
+        return EsaWorkload(name, 3, 1, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0, correction="votes")
+    if name == "esa_decode_128k_votes":
+        return EsaWorkload(name, 4, 16, 131072, 1, 32, 128, 128, 128, 4096, 2048, 2, 48.0, needles=16,
+                           correction="votes")
     raise SystemExit(f"unknown workload {name}")
 
 

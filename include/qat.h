@@ -48,7 +48,7 @@ enum qat_status {
 
 enum qat_dtype { QAT_F32 = 0, QAT_BF16 = 1 };
 
-#define QAT_ABI_VERSION 1
+#define QAT_ABI_VERSION 2
 
 /* Thread-local text for the last non-OK status of this thread ("" if none). */
 const char* qat_last_error(void);
@@ -105,7 +105,19 @@ typedef struct {
   float clip;           /* score-correction floor C > 0 (may be +inf) */
   float scale;          /* softmax scale > 0, e.g. 1/sqrt(d) */
   int32_t dtype;        /* qat_dtype of q, K, V and outputs */
+  int32_t correction;   /* qat_esa_correction: reading of the score correction */
+  float vote_tau;       /* QAT_CORR_VOTES temperature; <= 0: 1/sqrt(d_c) */
 } qat_esa_params;
+
+/*
+ * The score correction of [ESA] (paragraph on score correction: keep the
+ * relative size of scores, stop one token from dominating; the formula
+ * itself is not in the text), in one of two readings:
+ *   QAT_CORR_CLAMP  s^_ij = max(s_ij - max_j' s_ij', -clip)        (default)
+ *   QAT_CORR_VOTES  s^_ij = softmax over the middle part of vote_tau * s_i.
+ *                   (each query casts a total vote of 1); `clip` is unused.
+ */
+enum qat_esa_correction { QAT_CORR_CLAMP = 0, QAT_CORR_VOTES = 1 };
 
 /* Workspace bytes for esa_select + esa_sparse_attn with these parameters. */
 int esa_workspace_size(const qat_esa_params* p, size_t* bytes);

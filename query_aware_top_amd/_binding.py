@@ -34,8 +34,12 @@ class EsaParams(ctypes.Structure):
         ("d_c", ctypes.c_int64), ("ctx_len", ctypes.c_int64), ("chunk_start", ctypes.c_int64),
         ("chunk_len", ctypes.c_int64), ("n_init", ctypes.c_int32), ("window", ctypes.c_int32),
         ("topk", ctypes.c_int32), ("radius", ctypes.c_int32), ("clip", ctypes.c_float),
-        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("correction", ctypes.c_int32),
+        ("vote_tau", ctypes.c_float),
     ]
+
+
+QAT_CORR_CLAMP, QAT_CORR_VOTES = 0, 1
 
 
 class MobaParams(ctypes.Structure):
@@ -152,10 +156,13 @@ def _workspace(nbytes: int, device, ws=None):
 
 # ------------------------------------------------------------------ ESA
 def esa_params(*, batch, n_heads, head_dim, d_c, ctx_len, chunk_start, chunk_len, n_init, window, topk,
-               radius, clip, scale=None, dtype=torch.bfloat16) -> EsaParams:
+               radius, clip, scale=None, dtype=torch.bfloat16, correction="clamp", vote_tau=0.0) -> EsaParams:
+    """correction: "clamp" (default reading) or "votes" (per-query softmax
+    votes at temperature vote_tau; 0 means 1/sqrt(d_c))."""
+    corr = {"clamp": QAT_CORR_CLAMP, "votes": QAT_CORR_VOTES}[correction]
     return EsaParams(batch, n_heads, head_dim, d_c, ctx_len, chunk_start, chunk_len, n_init, window, topk,
                      radius, float(clip), float(scale if scale is not None else 1.0 / math.sqrt(head_dim)),
-                     _dt(dtype))
+                     _dt(dtype), corr, float(vote_tau))
 
 
 def esa_workspace_size(p: EsaParams) -> int:

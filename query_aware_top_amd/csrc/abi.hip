@@ -49,10 +49,12 @@ struct EsaLayout {
   qat::bf16* qhi = nullptr;
   qat::bf16* qlo = nullptr;
   float* rowmax_part = nullptr;
+  float* rowsum_part = nullptr;
   float* rowmax = nullptr;
   float* upart = nullptr;
   float* sraw = nullptr;
   float* smax = nullptr;
+  float* ssum = nullptr;
   int32_t* tk_hist = nullptr;
   int2* tk_cnt = nullptr;
   uint32_t* keys = nullptr;
@@ -77,7 +79,11 @@ int esa_check(const qat_esa_params* p) {
   if (p->radius > qat::esa_topk_max_radius())
     return fail(QAT_EUNSUPPORTED, "radius %d above the supported %d", p->radius, qat::esa_topk_max_radius());
   if (p->topk < 1) return fail(QAT_EINVAL, "topk must be >= 1");
-  if (!(p->clip > 0.f)) return fail(QAT_EINVAL, "clip must be > 0 (or +inf)");
+  if (p->correction != QAT_CORR_CLAMP && p->correction != QAT_CORR_VOTES)
+    return fail(QAT_EINVAL, "unknown correction %d", p->correction);
+  if (p->correction == QAT_CORR_CLAMP && !(p->clip > 0.f)) return fail(QAT_EINVAL, "clip must be > 0 (or +inf)");
+  if (p->correction == QAT_CORR_VOTES && !std::isfinite(p->vote_tau))
+    return fail(QAT_EINVAL, "vote_tau must be finite");
   if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return fail(QAT_EINVAL, "scale must be finite and > 0");
   if (p->dtype != QAT_F32 && p->dtype != QAT_BF16) return fail(QAT_EINVAL, "unknown dtype %d", p->dtype);
   if (p->batch * p->chunk_len * p->n_heads >= (1ll << 31)) return fail(QAT_EUNSUPPORTED, "too many query rows");
@@ -104,11 +110,13 @@ EsaLayout esa_layout(const qat_esa_params* p, void* ws) {
   const size_t nm = (size_t)(L.n_mid > 0 ? L.n_mid : 1);
   if (m > 1) {
     L.rowmax_part = c.take<float>((size_t)L.rows * L.nkeysplit);
+    L.rowsum_part = c.take<float>((size_t)L.rows * L.nkeysplit);
     L.rowmax = c.take<float>((size_t)L.rows);
     L.upart = c.take<float>((size_t)B * L.nqsplit * nm);
   } else {
     L.sraw = c.take<float>((size_t)B * nm);
     L.smax = c.take<float>((size_t)B * L.nscan);
+    L.ssum = c.take<float>((size_t)B * L.nscan);
   }
   L.tk_hist = c.take<int32_t>((size_t)B * 3 * 2048);
   L.tk_cnt = c.take<int2>((size_t)B * qat::esa_topk_slices((int64_t)nm));
@@ -389,21 +397,26 @@ QAT_EXPORT int esa_select(const qat_esa_params* p, const void* q, const void* Wq
   }
   if (e != hipSuccess) return hip_status(e, "esa_select: query compression");
   const qat::bf16* kc = (const qat::bf16*)kc_cache;
+  // votes: temperature in log2 units (exp(tau x) = exp2(tau log2(e) x))
+  const bool votes = p->correction == QAT_CORR_VOTES;
+  const float tau = p->vote_tau > 0.f ? p->vote_tau : 1.f / std::sqrt((float)p->d_c);
+  const float tau2 = votes ? tau * 1.4426950408889634f : 0.f;
   int mode;
   if (p->chunk_len > 1) {
     mode = 0;
     qat::KTimer tm("esa_scores", s);
     e = qat::launch_esa_prefill_scores(L.qhi, L.qlo, kc, p->batch, p->chunk_len, p->ctx_len, L.mid0, L.n_mid,
-                                       p->d_c, p->clip, L.rowmax_part, L.rowmax, L.upart, s);
+                                       p->d_c, p->clip, tau2, L.rowmax_part, L.rowsum_part, L.rowmax, L.upart, s);
   } else {
-    mode = 1;
+    mode = votes ? 2 : 1;
     qat::KTimer tm("esa_decode_scan", s);
-    e = qat::launch_esa_decode_scan(L.qc, kc, p->batch, p->ctx_len, L.mid0, L.n_mid, p->d_c, L.sraw, L.smax, s);
+    e = qat::launch_esa_decode_scan(L.qc, kc, p->batch, p->ctx_len, L.mid0, L.n_mid, p->d_c, tau2, L.sraw, L.smax,
+                                    L.ssum, s);
   }
   if (e != hipSuccess) return hip_status(e, "esa_select: scoring");
   qat::KTimer tm("esa_topk", s);
-  e = qat::launch_esa_topk(mode, L.upart, L.nqsplit, L.sraw, L.smax, L.nscan, p->clip, p->batch, L.n_mid,
-                           p->radius, p->topk, L.mid0, L.tk_hist, L.tk_cnt, L.keys, scores, sel, n_sel, s);
+  e = qat::launch_esa_topk(mode, L.upart, L.nqsplit, L.sraw, L.smax, L.ssum, L.nscan, p->clip, tau2, p->batch,
+                           L.n_mid, p->radius, p->topk, L.mid0, L.tk_hist, L.tk_cnt, L.keys, scores, sel, n_sel, s);
   return hip_status(e, "esa_select: top-k");
 }
 

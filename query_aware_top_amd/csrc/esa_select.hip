@@ -10,7 +10,12 @@
 // fixed. The two dropped formulas are read as
 //   correction  s^_ij = max(s_ij - max_j' s_ij', -clip)
 //   neighbours  u'_j  = max{u_t : t in M, |t - j| <= r}
-// and the importance as u_j = sum_i s^_ij.
+// and the importance as u_j = sum_i s^_ij. The alternative reading of the
+// correction (per-query softmax votes, s^_ij = exp(tau s_ij) / sum_j'
+// exp(tau s_ij')) is the VOTE instantiation: pass 1 also keeps each query's
+// running sum of exp2(tau2 (s - running max)) (tau2 = tau log2 e), the final
+// pass turns (max, sum) into the log2 normaliser c_i = tau2 max + log2 sum,
+// and pass 2 adds exp2(tau2 s_ij - c_i).
 //
 // Prefill scoring runs on the bf16 matrix cores with q~ (float32) split into
 // two bf16 terms (hi + lo): the products with the bf16 compressed keys are
@@ -47,11 +52,19 @@ __device__ __forceinline__ bf16x8 sc_a(const bf16* tile, int sb, int c) {
 // Pass 1: partial row maxima. grid (query tiles of 128, key splits, batch);
 // S^T = K~ Q~^T with Q~ = hi + lo in registers, so each lane holds one query
 // and 16 key scores per 32-key sub-tile.
-template <int DC>
+// Online (max, sum of exp2(tau2 (x - max))) pairs: merge of two.
+__device__ __forceinline__ void vote_merge(float& m, float& l, float om, float ol, float tau2) {
+  const float mm = fmaxf(m, om);
+  if (mm == -__builtin_inff()) return;
+  l = l * __builtin_amdgcn_exp2f(tau2 * (m - mm)) + ol * __builtin_amdgcn_exp2f(tau2 * (om - mm));
+  m = mm;
+}
+
+template <int DC, bool VOTE>
 __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
     const bf16* __restrict__ q_hi, const bf16* __restrict__ q_lo, const bf16* __restrict__ kc,
     int64_t m, int64_t ctx_len, int64_t mid0, int64_t n_mid, int64_t keys_per_split, int nsplit,
-    float* __restrict__ rowmax_part) {
+    float tau2, float* __restrict__ rowmax_part, float* __restrict__ rowsum_part) {
   __shared__ __align__(16) bf16 kt0[kKT * DC];
   __shared__ __align__(16) bf16 kt1[kKT * DC];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -71,7 +84,7 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
   const bf16* kbase = kc + (bi * ctx_len + mid0 + k0) * DC;
   auto row_ofs = [](int j) { return j * DC; };
   const int nt = (n + kKT - 1) / kKT;
-  float mx = -__builtin_inff();
+  float mx = -__builtin_inff(), lsum = 0.f;
   fa_issue_one<DC, kScWaves>(kt0, kbase, 0, n, row_ofs);
   for (int t = 0; t < nt; ++t) {
     fa_wait_loads();
@@ -88,7 +101,21 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[c], acc, 0, 0, 0);
       }
       const int base = t * kKT + sb * 32;
-      if (base + 32 <= n) {
+      if constexpr (VOTE) {
+        float tm = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (base + (i >> 2) * 8 + h * 4 + (i & 3) < n) tm = fmaxf(tm, acc[i]);
+        const float mn = fmaxf(mx, tm);
+        if (mn != -__builtin_inff()) {
+          float add = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (base + (i >> 2) * 8 + h * 4 + (i & 3) < n) add += __builtin_amdgcn_exp2f(tau2 * (acc[i] - mn));
+          lsum = lsum * __builtin_amdgcn_exp2f(tau2 * (mx - mn)) + add;
+          mx = mn;
+        }
+      } else if (base + 32 <= n) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[i]);
       } else {
@@ -98,32 +125,46 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
       }
     }
   }
-  mx = xor32_max(mx);
+  if constexpr (VOTE) {
+    vote_merge(mx, lsum, __shfl_xor(mx, 32, 64), __shfl_xor(lsum, 32, 64), tau2);
+    if (qvalid && h == 0) rowsum_part[(bi * m + qi) * nsplit + blockIdx.y] = lsum;
+  } else {
+    mx = xor32_max(mx);
+  }
   if (qvalid && h == 0) rowmax_part[(bi * m + qi) * nsplit + blockIdx.y] = mx;
 }
 
 // One wave per query row: the row's partial maxima are read contiguously
-// and reduced across the wave.
-__global__ __launch_bounds__(256) void esa_rowmax_final_kernel(const float* __restrict__ part, int nsplit,
-                                                               int64_t rows, float* __restrict__ rowmax) {
+// and reduced across the wave. VOTE: the (max, sum) pairs are merged and the
+// row's log2 normaliser tau2 max + log2 sum is stored instead of the max.
+template <bool VOTE>
+__global__ __launch_bounds__(256) void esa_rowmax_final_kernel(const float* __restrict__ part,
+                                                               const float* __restrict__ sum_part, int nsplit,
+                                                               int64_t rows, float tau2, float* __restrict__ rowmax) {
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= rows) return;
-  float mx = -__builtin_inff();
-  for (int s = lane; s < nsplit; s += 64) mx = fmaxf(mx, part[i * nsplit + s]);
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if (lane == 0) rowmax[i] = mx;
+  float mx = -__builtin_inff(), l = 0.f;
+  for (int s = lane; s < nsplit; s += 64) {
+    if constexpr (VOTE) vote_merge(mx, l, part[i * nsplit + s], sum_part[i * nsplit + s], tau2);
+    else mx = fmaxf(mx, part[i * nsplit + s]);
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    if constexpr (VOTE) vote_merge(mx, l, __shfl_xor(mx, off, 64), __shfl_xor(l, off, 64), tau2);
+    else mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  }
+  if (lane == 0) rowmax[i] = VOTE ? tau2 * mx + __builtin_log2f(l) : mx;
 }
 
 // Pass 2: partial importance. grid (key tiles of 128, query splits, batch);
 // S = Q~ K~^T with the keys in registers, so each lane holds one key and 16
 // query rows per 32-query sub-tile; the corrected scores are summed in
 // float32 per sub-tile and in float64 across sub-tiles (fixed order).
-template <int DC>
+template <int DC, bool VOTE>
 __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
     const bf16* __restrict__ q_hi, const bf16* __restrict__ q_lo, const float* __restrict__ rowmax,
     const bf16* __restrict__ kc, int64_t m, int64_t ctx_len, int64_t mid0, int64_t n_mid,
-    int64_t rows_per_split, int nqsplit, float clip, float* __restrict__ upart) {
+    int64_t rows_per_split, int nqsplit, float clip, float tau2, float* __restrict__ upart) {
   __shared__ __align__(16) bf16 qh0[kKT * DC];
   __shared__ __align__(16) bf16 qh1[kKT * DC];
   __shared__ __align__(16) bf16 ql0[kKT * DC];
@@ -179,7 +220,8 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
         const f32x4 r4 = *(const f32x4*)(trm + sb * 32 + g * 8 + h * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float v = fmaxf(acc[4 * g + e] - r4[e], -clip);
+          const float v = VOTE ? __builtin_amdgcn_exp2f(tau2 * acc[4 * g + e] - r4[e])
+                               : fmaxf(acc[4 * g + e] - r4[e], -clip);
           part += (base + g * 8 + h * 4 + e < n) ? v : 0.f;
         }
       }
@@ -195,13 +237,16 @@ constexpr int kScanUnroll = 8;
 // ---------------------------------------------------------------------------
 // Decode scoring: s_j = <q~, k~_j> (float32) for every middle token, plus the
 // workgroup maxima. DC/8 lanes per key, 8 elements (16 B) per lane.
-template <int DC>
+// VOTE: also the workgroup's sum of exp2(tau2 (s - workgroup max)), counted
+// once per key (by the key's first lane).
+template <int DC, bool VOTE>
 __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
     const float* __restrict__ qc, const bf16* __restrict__ kc, int64_t ctx_len, int64_t mid0, int64_t n_mid,
-    int64_t keys_per_wg, float* __restrict__ s_out, float* __restrict__ smax_part) {
+    int64_t keys_per_wg, float tau2, float* __restrict__ s_out, float* __restrict__ smax_part,
+    float* __restrict__ ssum_part) {
   constexpr int LPK = DC / 8;          // lanes per key
   constexpr int KPW = 256 / LPK;       // keys per workgroup pass
-  __shared__ float wmax[4];
+  __shared__ float wmax[4], wsum[4];
   const int64_t bi = blockIdx.y;
   const int tid = threadIdx.x;
   const int sub = tid % LPK;
@@ -211,7 +256,7 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
   const int64_t k0 = (int64_t)blockIdx.x * keys_per_wg;
   const int64_t k1 = min(n_mid, k0 + keys_per_wg);
   const bf16* kbase = kc + (bi * ctx_len + mid0) * DC;
-  float mx = -__builtin_inff();
+  float mx = -__builtin_inff(), lsum = 0.f;
   // kScanUnroll keys per lane group in flight at once
   constexpr int U = kScanUnroll;
   for (int64_t kb = k0; kb < k1; kb += (int64_t)KPW * U) {
@@ -237,23 +282,35 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
       const int64_t key = kb + (int64_t)u * KPW + tid / LPK;
       if (key < k1) {
         if (sub == 0) s_out[bi * n_mid + key] = acc[u];
-        mx = fmaxf(mx, acc[u]);
+        if (VOTE && sub == 0) vote_merge(mx, lsum, acc[u], 1.f, tau2);
+        else mx = fmaxf(mx, acc[u]);
       }
     }
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+  for (int off = 32; off >= 1; off >>= 1) {
+    if constexpr (VOTE) vote_merge(mx, lsum, __shfl_xor(mx, off, 64), __shfl_xor(lsum, off, 64), tau2);
+    else mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  }
+  if ((tid & 63) == 0) { wmax[tid >> 6] = mx; wsum[tid >> 6] = lsum; }
   __syncthreads();
-  if (tid == 0)
-    smax_part[bi * gridDim.x + blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  if (tid == 0) {
+    float m2 = wmax[0], l2 = wsum[0];
+    for (int w = 1; w < 4; ++w) {
+      if constexpr (VOTE) vote_merge(m2, l2, wmax[w], wsum[w], tau2);
+      else m2 = fmaxf(m2, wmax[w]);
+    }
+    smax_part[bi * gridDim.x + blockIdx.x] = m2;
+    if (VOTE) ssum_part[bi * gridDim.x + blockIdx.x] = l2;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Top-k over the middle part, several workgroups per sequence, each owning a
 // slice of 256 PER consecutive candidates (PER per thread, contiguous):
 //   prep   u_j (mode 0, prefill: the query-split partial sums added in
-//          float64 in split order; mode 1, decode: max(s_j - max s, -clip)),
+//          float64 in split order; mode 1, decode: max(s_j - max s, -clip);
+//          mode 2, decode with votes: exp2(tau2 (s_j - max s)) / sum),
 //          u'_j = max of u over |t - j| <= r within M (halo recomputed from
 //          the inputs), order-preserving uint32 keys, histogram of the top
 //          11 key bits;
@@ -341,28 +398,30 @@ __device__ TkCut tk_cut(const int32_t* __restrict__ hist, int npass, int32_t k, 
 }
 
 __device__ __forceinline__ float tk_u(int mode, const float* __restrict__ upart, int nqsplit,
-                                      const float* __restrict__ s_in, float mx, float clip, int64_t bi,
-                                      int64_t n_mid, int64_t j) {
+                                      const float* __restrict__ s_in, float mx, float clip, float tau2,
+                                      float inv_l, int64_t bi, int64_t n_mid, int64_t j) {
   if (mode == 0) {
     double acc = 0.0;
     for (int sp = 0; sp < nqsplit; ++sp) acc += (double)upart[(bi * nqsplit + sp) * n_mid + j];
     return (float)acc;
   }
+  if (mode == 2) return __builtin_amdgcn_exp2f(tau2 * (s_in[bi * n_mid + j] - mx)) * inv_l;
   return fmaxf(s_in[bi * n_mid + j] - mx, -clip);
 }
 
 template <int PER>
 __global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
     int mode, const float* __restrict__ upart, int nqsplit, const float* __restrict__ s_in,
-    const float* __restrict__ smax_part, int nsmax, float clip, int64_t n_mid, int radius,
-    uint32_t* __restrict__ keys, float* __restrict__ scores_out, int32_t* __restrict__ hist) {
+    const float* __restrict__ smax_part, const float* __restrict__ ssum_part, int nsmax, float clip, float tau2,
+    int64_t n_mid, int radius, uint32_t* __restrict__ keys, float* __restrict__ scores_out,
+    int32_t* __restrict__ hist) {
   __shared__ float s_u[kTkThreads * PER + 2 * kTkMaxRadius];
   __shared__ int32_t s_h[kTkBins];
-  __shared__ float s_red[kTkThreads / 64];
+  __shared__ float s_red[kTkThreads / 64], s_rsum[kTkThreads / 64];
   const int tid = threadIdx.x;
   const int64_t bi = blockIdx.y;
   const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER);
-  float mx = 0.f;
+  float mx = 0.f, inv_l = 1.f;
   if (mode == 1) {   // max of the raw scores over M, from the scan's per-workgroup maxima
     float m = -__builtin_inff();
     for (int sp = tid; sp < nsmax; sp += kTkThreads) m = fmaxf(m, smax_part[bi * nsmax + sp]);
@@ -371,13 +430,26 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
     if ((tid & 63) == 0) s_red[tid >> 6] = m;
     __syncthreads();
     mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  } else if (mode == 2) {   // max and softmax denominator over M, from the scan's per-workgroup pairs
+    float m = -__builtin_inff(), l = 0.f;
+    for (int sp = tid; sp < nsmax; sp += kTkThreads)
+      vote_merge(m, l, smax_part[bi * nsmax + sp], ssum_part[bi * nsmax + sp], tau2);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) vote_merge(m, l, __shfl_xor(m, off, 64), __shfl_xor(l, off, 64), tau2);
+    if ((tid & 63) == 0) { s_red[tid >> 6] = m; s_rsum[tid >> 6] = l; }
+    __syncthreads();
+    m = s_red[0];
+    l = s_rsum[0];
+    for (int w = 1; w < kTkThreads / 64; ++w) vote_merge(m, l, s_red[w], s_rsum[w], tau2);
+    mx = m;
+    inv_l = 1.f / l;
   }
   for (int i = tid; i < kTkBins; i += kTkThreads) s_h[i] = 0;
   // u over [j0 - r, j0 + slice + r) clipped to M
   const int64_t lo = max((int64_t)0, j0 - radius);
   const int64_t hi = min(n_mid, j0 + (kTkThreads * PER) + radius);
   for (int64_t j = lo + tid; j < hi; j += kTkThreads)
-    s_u[j - j0 + radius] = tk_u(mode, upart, nqsplit, s_in, mx, clip, bi, n_mid, j);
+    s_u[j - j0 + radius] = tk_u(mode, upart, nqsplit, s_in, mx, clip, tau2, inv_l, bi, n_mid, j);
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -541,15 +613,23 @@ int esa_scan_wgs(int64_t n_mid) {
 
 hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const bf16* kc, int64_t batch, int64_t m,
                                      int64_t ctx_len, int64_t mid0, int64_t n_mid, int64_t d_c, float clip,
-                                     float* rowmax_part, float* rowmax, float* upart, hipStream_t s) {
+                                     float tau2, float* rowmax_part, float* rowsum_part, float* rowmax,
+                                     float* upart, hipStream_t s) {
   if (n_mid <= 0) return hipSuccess;
+  const bool vote = tau2 > 0.f;
   const int ks = esa_key_splits(n_mid, m);
   const int64_t kps = cdiv(cdiv(n_mid, ks), kKT) * kKT;
   const int ks_eff = (int)cdiv(n_mid, kps);
   dim3 g1((unsigned)cdiv(m, kScRows), (unsigned)ks_eff, (unsigned)batch);
 #define QAT_RM(DC_)                                                                                       \
-  hipLaunchKernelGGL(esa_rowmax_kernel<DC_>, g1, dim3(64 * kScWaves), 0, s, q_hi, q_lo, kc, m, ctx_len, mid0, \
-                     n_mid, kps, ks_eff, rowmax_part)
+  do {                                                                                                    \
+    if (vote)                                                                                             \
+      hipLaunchKernelGGL((esa_rowmax_kernel<DC_, true>), g1, dim3(64 * kScWaves), 0, s, q_hi, q_lo, kc, m,  \
+                         ctx_len, mid0, n_mid, kps, ks_eff, tau2, rowmax_part, rowsum_part);              \
+    else                                                                                                  \
+      hipLaunchKernelGGL((esa_rowmax_kernel<DC_, false>), g1, dim3(64 * kScWaves), 0, s, q_hi, q_lo, kc, m, \
+                         ctx_len, mid0, n_mid, kps, ks_eff, tau2, rowmax_part, rowsum_part);              \
+  } while (0)
   switch (d_c) {
     case 32: QAT_RM(32); break;
     case 64: QAT_RM(64); break;
@@ -559,16 +639,26 @@ hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const b
 #undef QAT_RM
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(esa_rowmax_final_kernel, dim3((unsigned)cdiv(batch * m, 4)), dim3(256), 0, s,
-                     rowmax_part, ks_eff, batch * m, rowmax);
+  if (vote)
+    hipLaunchKernelGGL(esa_rowmax_final_kernel<true>, dim3((unsigned)cdiv(batch * m, 4)), dim3(256), 0, s,
+                       rowmax_part, rowsum_part, ks_eff, batch * m, tau2, rowmax);
+  else
+    hipLaunchKernelGGL(esa_rowmax_final_kernel<false>, dim3((unsigned)cdiv(batch * m, 4)), dim3(256), 0, s,
+                       rowmax_part, rowsum_part, ks_eff, batch * m, tau2, rowmax);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int qs = esa_query_splits(n_mid, m);
   const int64_t rps = cdiv(cdiv(m, qs), kKT) * kKT;
   const int qs_eff = (int)cdiv(m, rps);
   dim3 g2((unsigned)cdiv(n_mid, kScRows), (unsigned)qs_eff, (unsigned)batch);
-#define QAT_CS(DC_)                                                                                      \
-  hipLaunchKernelGGL(esa_colsum_kernel<DC_>, g2, dim3(64 * kScWaves), 0, s, q_hi, q_lo, rowmax, kc, m,     \
-                     ctx_len, mid0, n_mid, rps, qs_eff, clip, upart)
+#define QAT_CS(DC_)                                                                                       \
+  do {                                                                                                    \
+    if (vote)                                                                                             \
+      hipLaunchKernelGGL((esa_colsum_kernel<DC_, true>), g2, dim3(64 * kScWaves), 0, s, q_hi, q_lo, rowmax, \
+                         kc, m, ctx_len, mid0, n_mid, rps, qs_eff, clip, tau2, upart);                    \
+    else                                                                                                  \
+      hipLaunchKernelGGL((esa_colsum_kernel<DC_, false>), g2, dim3(64 * kScWaves), 0, s, q_hi, q_lo,        \
+                         rowmax, kc, m, ctx_len, mid0, n_mid, rps, qs_eff, clip, tau2, upart);            \
+  } while (0)
   switch (d_c) {
     case 32: QAT_CS(32); break;
     case 64: QAT_CS(64); break;
@@ -586,14 +676,21 @@ int esa_prefill_qsplits_eff(int64_t n_mid, int64_t m) {
 }
 
 hipError_t launch_esa_decode_scan(const float* qc, const bf16* kc, int64_t batch, int64_t ctx_len, int64_t mid0,
-                                  int64_t n_mid, int64_t d_c, float* s_out, float* smax_part, hipStream_t s) {
+                                  int64_t n_mid, int64_t d_c, float tau2, float* s_out, float* smax_part,
+                                  float* ssum_part, hipStream_t s) {
   if (n_mid <= 0) return hipSuccess;
   const int nw = esa_scan_wgs(n_mid);
   const int64_t kpw = cdiv(n_mid, nw);
   dim3 grid((unsigned)nw, (unsigned)batch);
-#define QAT_DS(DC_)                                                                                       \
-  hipLaunchKernelGGL(esa_decode_scan_kernel<DC_>, grid, dim3(256), 0, s, qc, kc, ctx_len, mid0, n_mid, kpw, \
-                     s_out, smax_part)
+#define QAT_DS(DC_)                                                                                        \
+  do {                                                                                                     \
+    if (tau2 > 0.f)                                                                                        \
+      hipLaunchKernelGGL((esa_decode_scan_kernel<DC_, true>), grid, dim3(256), 0, s, qc, kc, ctx_len, mid0,  \
+                         n_mid, kpw, tau2, s_out, smax_part, ssum_part);                                   \
+    else                                                                                                   \
+      hipLaunchKernelGGL((esa_decode_scan_kernel<DC_, false>), grid, dim3(256), 0, s, qc, kc, ctx_len, mid0, \
+                         n_mid, kpw, tau2, s_out, smax_part, ssum_part);                                   \
+  } while (0)
   switch (d_c) {
     case 32: QAT_DS(32); break;
     case 64: QAT_DS(64); break;
@@ -610,7 +707,8 @@ int esa_topk_max_radius() { return kTkMaxRadius; }
 
 template <int PER>
 static hipError_t launch_esa_topk_per(int mode, const float* upart, int nqsplit, const float* s_in,
-                                      const float* smax_part, int nsmax, float clip, int64_t batch, int64_t n_mid,
+                                      const float* smax_part, const float* ssum_part, int nsmax, float clip,
+                                      float tau2, int64_t batch, int64_t n_mid,
                                       int radius, int topk, int64_t mid0, int32_t* hist, int2* wgcnt,
                                       uint32_t* keys, float* scores_out, int32_t* sel, int32_t* n_sel,
                                       hipStream_t s) {
@@ -620,7 +718,7 @@ static hipError_t launch_esa_topk_per(int mode, const float* upart, int nqsplit,
   if (n_mid > 0) {
     if ((e = launch_fill_i32(hist, batch * 3 * kTkBins, 0, s)) != hipSuccess) return e;
     hipLaunchKernelGGL(esa_topk_prep_kernel<PER>, grid, dim3(kTkThreads), 0, s, mode, upart, nqsplit, s_in,
-                       smax_part, nsmax, clip, n_mid, radius, keys, scores_out, hist);
+                       smax_part, ssum_part, nsmax, clip, tau2, n_mid, radius, keys, scores_out, hist);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (n_mid > topk) {
       for (int pass = 1; pass < 3; ++pass) {
@@ -637,7 +735,8 @@ static hipError_t launch_esa_topk_per(int mode, const float* upart, int nqsplit,
 }
 
 hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const float* s_in, const float* smax_part,
-                           int nsmax, float clip, int64_t batch, int64_t n_mid, int radius, int topk, int64_t mid0,
+                           const float* ssum_part, int nsmax, float clip, float tau2, int64_t batch, int64_t n_mid,
+                           int radius, int topk, int64_t mid0,
                            int32_t* hist, int2* wgcnt, uint32_t* keys, float* scores_out, int32_t* sel,
                            int32_t* n_sel, hipStream_t s) {
   // the widest split that still gives every pass 256 workgroups (the
@@ -646,15 +745,15 @@ hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const floa
   // per sequence
   const int64_t s8 = batch * cdiv(n_mid, kTkThreads * 8), s4 = batch * cdiv(n_mid, kTkThreads * 4);
   if (batch * cdiv(n_mid, kTkThreads * 16) >= 256)
-    return launch_esa_topk_per<16>(mode, upart, nqsplit, s_in, smax_part, nsmax, clip, batch, n_mid, radius, topk,
+    return launch_esa_topk_per<16>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius, topk,
                                    mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
   if (s8 >= 256)
-    return launch_esa_topk_per<8>(mode, upart, nqsplit, s_in, smax_part, nsmax, clip, batch, n_mid, radius, topk,
+    return launch_esa_topk_per<8>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius, topk,
                                   mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
   if (s4 >= 256)
-    return launch_esa_topk_per<4>(mode, upart, nqsplit, s_in, smax_part, nsmax, clip, batch, n_mid, radius, topk,
+    return launch_esa_topk_per<4>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius, topk,
                                   mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
-  return launch_esa_topk_per<kTkPerMin>(mode, upart, nqsplit, s_in, smax_part, nsmax, clip, batch, n_mid, radius,
+  return launch_esa_topk_per<kTkPerMin>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius,
                                         topk, mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
 }
 

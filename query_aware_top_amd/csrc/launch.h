@@ -78,16 +78,23 @@ hipError_t launch_esa_generic(const void* q, const void* k, const void* v, const
 int esa_key_splits(int64_t n_mid, int64_t m);
 int esa_prefill_qsplits_eff(int64_t n_mid, int64_t m);
 int esa_scan_wgs(int64_t n_mid);
+// tau2 > 0: the softmax-vote reading of the correction at temperature
+// tau2 / log2(e) (rowsum_part / ssum_part hold the per-split exp sums);
+// tau2 = 0: the clamp reading.
 hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const bf16* kc, int64_t batch, int64_t m,
                                      int64_t ctx_len, int64_t mid0, int64_t n_mid, int64_t d_c, float clip,
-                                     float* rowmax_part, float* rowmax, float* upart, hipStream_t s);
+                                     float tau2, float* rowmax_part, float* rowsum_part, float* rowmax,
+                                     float* upart, hipStream_t s);
 hipError_t launch_esa_decode_scan(const float* qc, const bf16* kc, int64_t batch, int64_t ctx_len, int64_t mid0,
-                                  int64_t n_mid, int64_t d_c, float* s_out, float* smax_part, hipStream_t s);
+                                  int64_t n_mid, int64_t d_c, float tau2, float* s_out, float* smax_part,
+                                  float* ssum_part, hipStream_t s);
 int esa_topk_slices(int64_t n_mid);
 int esa_topk_max_radius();
 // hist: batch*3*2048 int32, wgcnt: batch*esa_topk_slices(n_mid) int2 (scratch)
+// mode 0: prefill importance sums; 1: decode, clamp; 2: decode, votes
 hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const float* s_in, const float* smax_part,
-                           int nsmax, float clip, int64_t batch, int64_t n_mid, int radius, int topk, int64_t mid0,
+                           const float* ssum_part, int nsmax, float clip, float tau2, int64_t batch, int64_t n_mid,
+                           int radius, int topk, int64_t mid0,
                            int32_t* hist, int2* wgcnt, uint32_t* keys, float* scores_out, int32_t* sel,
                            int32_t* n_sel, hipStream_t s);
 

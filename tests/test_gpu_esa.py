@@ -39,7 +39,7 @@ def gpu_key_cache(k: torch.Tensor, Wk: torch.Tensor) -> torch.Tensor:
 
 
 def esa_case(seed, B, T, c0, m, H, d, d_c, n_init, W, topk, radius, clip, dtype=torch.bfloat16, needles=0,
-             rows=None, seqs=None):
+             rows=None, seqs=None, correction="clamp", vote_tau=0.0):
     q_all, k, v, info = synth.esa_inputs(seed, B, T, 1, H, d, dtype, DEV)
     q = synth.normal(seed, synth.gen.TID_Q, (B, m, H, d), dtype, DEV, start=1 << 40)
     if needles:
@@ -54,7 +54,8 @@ def esa_case(seed, B, T, c0, m, H, d, d_c, n_init, W, topk, radius, clip, dtype=
     Wq = synth.compression_weights(seed, d_c, H * d, synth.gen.TID_W, dtype, DEV)
     Wk = Wq
     p = qat.esa_params(batch=B, n_heads=H, head_dim=d, d_c=d_c, ctx_len=T, chunk_start=c0, chunk_len=m,
-                       n_init=n_init, window=W, topk=topk, radius=radius, clip=clip, dtype=dtype)
+                       n_init=n_init, window=W, topk=topk, radius=radius, clip=clip, dtype=dtype,
+                       correction=correction, vote_tau=vote_tau)
     kc = gpu_key_cache(k, Wk)
     sel, n_sel, scores = qat.esa_select(p, q, Wq, None, kc, want_scores=True)
     out, lse = qat.esa_sparse_attn(p, q, k, v, sel, n_sel)
@@ -74,7 +75,8 @@ def esa_case(seed, B, T, c0, m, H, d, d_c, n_init, W, topk, radius, clip, dtype=
         kc_gpu = to64(kc[bi])
         assert np.array_equal(kc_gpu, kc_ref), f"compressed keys differ in {np.sum(kc_gpu != kc_ref)} entries"
         qn = to64(q[bi])
-        sel_ref, up, _, _ = oesa.select(qn, Wq_n, None, kc_ref, c0, n_init, W, topk, radius, clip)
+        sel_ref, up, _, _ = oesa.select(qn, Wq_n, None, kc_ref, c0, n_init, W, topk, radius, clip,
+                                        correction=correction, tau=vote_tau if vote_tau > 0 else None)
         ns = int(n_sel[bi])
         assert ns == len(sel_ref)
         sg = sel[bi, :ns].cpu().numpy().astype(np.int64)
@@ -85,7 +87,11 @@ def esa_case(seed, B, T, c0, m, H, d, d_c, n_init, W, topk, radius, clip, dtype=
         swaps += n
         if len(M):
             sc = to64(scores[bi, :len(M)])
-            assert_close(sc, up, 1e-4, "importance scores")
+            if correction == "votes":   # votes lie in (0, m]: relative comparison
+                err = np.abs(sc - up) / np.maximum(np.abs(up), 1e-30)
+                assert np.max(err) < 1e-3, f"vote importance: max relative error {np.max(err):.3e}"
+            else:
+                assert_close(sc, up, 1e-4, "importance scores")
         r = rows if rows is not None else list(range(m))
         o_ref, lse_ref = oesa.attend(qn, to64(k[bi]) if T * H * d < 2 ** 26 else _KV(k[bi]),
                                      to64(v[bi]) if T * H * d < 2 ** 26 else _KV(v[bi]), sg, c0, n_init, W,
@@ -190,3 +196,32 @@ def test_esa_key_list_beyond_lds():
     LDS (64 initial + 5000 selected + 12000 window + 128 chunk keys): the
     tile loads take their positions from global memory."""
     esa_case(10, 1, 40000, 36000, 128, 2, 64, 64, 64, 12000, 5000, 2, 12.0, rows=[0, 1, 63, 127])
+
+
+# ---- the alternative correction reading: per-query softmax votes -----------
+VOTES = [
+    # seed, B, T, c0, m, H, d, d_c, n_init, W, topk, radius, clip(unused), vote_tau
+    (31, 1, 2048, 1600, 300, 4, 128, 64, 16, 128, 100, 2, 1.0, 0.0),      # default temperature
+    (32, 2, 1500, 1000, 257, 2, 64, 32, 8, 64, 50, 0, 1.0, 0.5),          # batch 2, ragged chunk, no neighbours
+    (33, 1, 1200, 1000, 64, 2, 128, 256, 4, 100, 77, 3, 1.0, 0.05),      # d_c 256, one partial tile
+    (34, 3, 3000, 2999, 1, 16, 128, 64, 32, 256, 300, 2, 1.0, 0.0),      # decode, three sequences
+    (35, 16, 20000, 19999, 1, 4, 64, 64, 32, 256, 300, 1, 1.0, 0.2),     # decode, 16 sequences, wider top-k split
+]
+
+
+@pytest.mark.parametrize("case", VOTES, ids=[f"v{i}" for i in range(len(VOTES))])
+def test_esa_votes_small(case):
+    """ESA with the softmax-vote reading of the score correction: selection
+    within the tie band, importance within 1e-3 relative, outputs within
+    tolerance, against the oracle's vote reading."""
+    *args, tau = case
+    print(f"[esa votes] {case}", flush=True)
+    seqs = [0, 7, 15] if args[1] == 16 else None
+    esa_case(*args, correction="votes", vote_tau=tau, seqs=seqs)
+
+
+def test_esa_votes_prefill_64k_full_size():
+    """The 64k chunked prefill with the vote reading (default temperature
+    1/sqrt(128)); full selection and sampled output rows."""
+    rows = [0, 1, 1000, 2047]
+    esa_case(3, 1, 65536, 63488, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0, rows=rows, correction="votes")
