@@ -41,6 +41,30 @@ def attend(q, K, V, scale):
     return (w @ V) / l, mx + np.log(l)
 
 
+def attend_grad(q, K, V, scale, do):
+    """Gradient of o = attend(q, K, V, scale)[0] against an upstream
+    gradient do [dv]: returns (dq [d], dK [n, d], dV [n, dv]).
+
+    With s = scale K q, P = softmax(s), o = P V (the definition of
+    ``attend``): dV = P do^T, dP_j = do . v_j, D = sum_j P_j dP_j,
+    dS_j = P_j (dP_j - D), dq = scale sum_j dS_j k_j, dK_j = scale dS_j q.
+    An empty key set has zero gradients.
+    """
+    q = np.asarray(q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    do = np.asarray(do, np.float64)
+    if K.shape[0] == 0:
+        return np.zeros_like(q), np.zeros_like(K), np.zeros_like(V)
+    s = scale * (K @ q)
+    w = np.exp(s - s.max())
+    P = w / w.sum()
+    dV = np.outer(P, do)
+    dP = V @ do
+    dS = P * (dP - P @ dP)
+    return scale * (dS @ K), scale * np.outer(dS, q), dV
+
+
 def attend_heads(Q, K, V, scale):
     """Per-head attention of one query position: Q [H, d], K/V [n, H, d]
     -> o [H, d], lse [H]. Same definition as ``attend`` for every head."""

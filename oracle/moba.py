@@ -34,7 +34,7 @@ inputs; 3 of 64 blocks gives the printed 95.31% sparsity.
 """
 import numpy as np
 
-from .attention import attend
+from .attention import attend, attend_grad
 
 
 def block_means(k, block):
@@ -123,3 +123,29 @@ def forward(q, k, v, block, topk, scale, window=0, rows=None):
     blk, sc = select(q, k, block, topk, rows)
     o, lse = attend_rows(q, k, v, block, blk, rows, scale, window)
     return blk, sc, o, lse
+
+
+def backward_rows(q, k, v, block, blk, rows, scale, do, window=0):
+    """Gradients of the attention of the given rows (gating held fixed: the
+    gated sets blk are a discrete choice, as in the write-up's training,
+    where the gate has no parameters of its own).
+
+    q [N, Hq, d], k/v [N, Hkv, d], blk [len(rows), Hq, topk], do
+    [len(rows), Hq, d]. Returns dq [len(rows), Hq, d] and dk, dv [N, Hkv, d]
+    with every row's and head's contribution added (GQA: the query heads of
+    a KV head add into it)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    hq, hkv = q.shape[1], k.shape[1]
+    dq = np.zeros((len(rows), hq, q.shape[2]))
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for r, t in enumerate(rows):
+        for h in range(hq):
+            idx = key_set(blk[r, h], t, block, window)
+            g = kv_head(h, hq, hkv)
+            dq[r, h], dK, dV = attend_grad(q[t, h], k[idx, g], v[idx, g], scale, do[r, h])
+            dk[idx, g] += dK
+            dv[idx, g] += dV
+    return dq, dk, dv
