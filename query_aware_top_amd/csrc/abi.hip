@@ -157,6 +157,7 @@ struct MobaLayout {
   int dec_pieces = 0;
   float* dec_po = nullptr;    // [rows, dec_pieces, d] piece outputs
   float* dec_plse = nullptr;  // [rows, dec_pieces] piece log-sum-exps
+  float* delta = nullptr;     // [rows] sum_j p_j dp_j of the gradient pass
   size_t bytes = 0;
 };
 
@@ -213,6 +214,7 @@ MobaLayout moba_layout(const qat_moba_params* p, void* ws) {
     L.dec_po = c.take<float>((size_t)L.nrows * L.dec_pieces * p->head_dim);
     L.dec_plse = c.take<float>((size_t)L.nrows * L.dec_pieces);
   }
+  L.delta = c.take<float>((size_t)L.nrows);
   L.bytes = c.bytes();
   return L;
 }
@@ -577,4 +579,31 @@ QAT_EXPORT int moba_decode_attn(const qat_moba_params* p, const void* q, const v
   L = moba_layout(p, ws);
   return moba_attn_rows(p, q, p->q_len, p->q_start, k, v, blk, out, lse, L, (hipStream_t)stream,
                         "moba_decode_attn");
+}
+
+QAT_EXPORT int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, const void* k, const void* v,
+                                    const int32_t* blk, const void* dout, const float* lse, float* dq, float* dk,
+                                    float* dv, void* ws, size_t ws_bytes, void* stream) {
+  int rc = moba_check(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !blk || !dout || !lse || !dq || !dk || !dv)
+    return fail(QAT_EINVAL, "q, k, v, blk, dout, lse, dq, dk, dv must be non-NULL");
+  if (p->window != 0) return fail(QAT_EUNSUPPORTED, "gradients with an extra local window are not implemented");
+  MobaLayout L = moba_layout(p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  L = moba_layout(p, ws);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  const bool gated = p->topk > 1 && L.nbuckets > 0;
+  if (gated) {
+    qat::KTimer tm("moba_dispatch", s);
+    e = qat::launch_moba_dispatch(blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim, p->q_start,
+                                  p->q_len, p->block, p->topk, L.nbc, L.counts, L.offsets, L.cursor, L.entries,
+                                  L.tiles, L.ntiles, s);
+    if (e != hipSuccess) return hip_status(e, "moba_sparse_attn_bwd: dispatch");
+  }
+  e = qat::launch_moba_bwd(q, k, v, blk, dout, lse, L.tiles, L.ntiles, L.entries, gated ? L.max_tiles : 0, dq,
+                           L.delta, dk, dv, p->dtype == QAT_BF16, p->batch, p->seq_len, p->n_q_heads,
+                           p->n_kv_heads, p->head_dim, p->q_start, p->q_len, p->block, p->topk, p->scale, s);
+  return hip_status(e, "moba_sparse_attn_bwd");
 }

@@ -54,6 +54,17 @@ hipError_t launch_moba_attn_mfma(const void* q, const void* k, const void* v, co
                                  int64_t hkv, int64_t d, int64_t nbc, int64_t q_start, int64_t q_len, int block,
                                  int topk, float scale, int64_t max_tiles, hipStream_t s);
 
+// ---- MoBA gradients (moba_bwd.hip) -----------------------------------------
+// dq [rows, d] and delta [rows] written; dk, dv [batch, seq_len, hkv, d]
+// written in full (own-block kernel) and then added to (gated rows over the
+// dispatch tiles).
+int moba_bwd_chunks(int block);
+hipError_t launch_moba_bwd(const void* q, const void* k, const void* v, const int32_t* blk, const void* dout,
+                           const float* lse, const int4* tiles, const int32_t* ntiles, const int2* entries,
+                           int64_t max_tiles, float* dq, float* delta, float* dk, float* dv, bool bf,
+                           int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t q_start,
+                           int64_t q_len, int block, int topk, float scale, hipStream_t s);
+
 // ---- generic per-row attention (attn_generic.hip) -------------------------
 // q holds q_seq positions per sequence from position q_off on (the whole
 // sequence: q_seq = seq_len, q_off = 0; only the processed rows: q_seq =
