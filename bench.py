@@ -11,7 +11,7 @@ Prints one JSON line. Default workload: MoBA prefill at the 8B-style GQA
 shape (32 query / 8 KV heads x 128, N = 32768, block 512, top-k 3 with the
 forced block, 8 planted key blocks), reported as query tokens per second.
 Other workloads (--workload): moba_fp32_4k, esa_prefill_64k,
-esa_decode_128k, moba_long_512k, moba_decode_128k, and esa_prefill_64k_votes /
+esa_decode_128k, moba_long_512k, moba_decode_128k, moba_bwd_32k (gradients), and esa_prefill_64k_votes /
 esa_decode_128k_votes (the softmax-vote reading of ESA's score correction).
 """
 from __future__ import annotations
@@ -50,6 +50,10 @@ STAGE_SOURCES = {
     "moba_decode_select": ["moba_select.hip"],
     "moba_decode_attn": ["attn_generic.hip"],
     "moba_decode_combine": ["attn_generic.hip"],
+    "moba_bwd_dq": ["moba_bwd.hip", "attn_core.h"],
+    "moba_bwd_dq_past": ["moba_bwd.hip", "attn_core.h"],
+    "moba_bwd_own": ["moba_bwd.hip"],
+    "moba_bwd_gated": ["moba_bwd.hip"],
     "esa_compress*": ["compress.hip"],
     "esa_scores": ["esa_select.hip"],
     "esa_topk": ["esa_select.hip"],
@@ -283,6 +287,79 @@ class MobaDecodeWorkload(Workload):
                           f"{el:.1f} s"}
 
 
+class MobaBwdWorkload(Workload):
+    """Gradients of MoBA prefill (gating held fixed) at the 32k GQA shape:
+    the forward (gating, attention, lse) runs once before timing; a step is
+    the backward call (dispatch, dq + D, own-block and gated-row key
+    gradients)."""
+
+    def __init__(self, name, seed, n, hq, hkv, d, block, topk, planted=0):
+        import query_aware_top_amd as qat
+        import synth
+        self.qat = qat
+        self.name = name
+        self.unit = "query-tokens/s"
+        self.dtype = "bf16"
+        self.n, self.hq, self.hkv, self.d, self.block, self.topk = n, hq, hkv, d, block, topk
+        self.q, self.k, self.v, _ = synth.moba_inputs(seed, 1, n, hq, hkv, d, torch.bfloat16, "cuda",
+                                                      planted=planted, block=block)
+        self.p = qat.moba_params(batch=1, seq_len=n, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, block=block,
+                                 topk=topk, dtype=torch.bfloat16)
+        self.ws = torch.empty(qat.moba_bwd_workspace_size(self.p), dtype=torch.uint8, device="cuda")
+        self.blk = qat.moba_block_select(self.p, self.q, self.k, ws=self.ws)
+        self.out, self.lse = qat.moba_sparse_attn(self.p, self.q, self.k, self.v, self.blk, ws=self.ws)
+        self.do = synth.normal(seed, 7, (1, n, hq, d), torch.bfloat16, "cuda")
+        self.dq = torch.empty(1, n, hq, d, dtype=torch.float32, device="cuda")
+        self.dk = torch.empty(1, n, hkv, d, dtype=torch.float32, device="cuda")
+        self.dv = torch.empty(1, n, hkv, d, dtype=torch.float32, device="cuda")
+        self.dominant, self.bound = "moba_bwd_gated", "alu"
+
+    def step(self):
+        self.qat.moba_sparse_attn_bwd(self.p, self.q, self.k, self.v, self.blk, self.out, self.do, self.lse,
+                                      dq=self.dq, dk=self.dk, dv=self.dv, ws=self.ws)
+
+    def value(self, sec):
+        return self.n / sec
+
+    def dominant_work(self):
+        """The gated-row key kernel: 4 products of d per (row, key) pair of
+        the gated blocks (s = q.k, dp = dO.v, dv += p dO, dk += ds q), 2 flops
+        each: 8 d flops per pair."""
+        blk = self.blk[0].to(torch.int64)
+        cur = (torch.arange(self.n, device="cuda") // self.block)[:, None, None]
+        past = ((blk[..., :self.topk - 1] >= 0) & (blk[..., :self.topk - 1] < cur)).sum().item()
+        return past * self.block * 8 * self.d
+
+    def config(self):
+        return {"workload": self.name, "batch": 1, "seq_len": self.n, "n_q_heads": self.hq,
+                "n_kv_heads": self.hkv, "head_dim": self.d, "block": self.block, "topk_incl_current": self.topk,
+                "query_rows": self.n, "pass": "backward"}
+
+    def cpu_baseline(self, budget_s=12.0):
+        """The float64 oracle's gradients on host cores for a bounded sample
+        of query positions (all heads; their dq and their contributions to
+        dk, dv), extrapolated to the sequence."""
+        import numpy as np
+        from oracle import moba as omoba
+        kn = self.k[0].to("cpu").to(torch.float64).numpy()
+        vn = self.v[0].to("cpu").to(torch.float64).numpy()
+        qn = self.q[0].to("cpu").to(torch.float64).numpy()
+        dn = self.do[0].to("cpu").to(torch.float64).numpy()
+        blk = self.blk[0].cpu().numpy()
+        order = np.random.default_rng(0).permutation(self.n)
+        t0 = time.perf_counter()
+        done = 0
+        while done < self.n and (time.perf_counter() - t0 < budget_s or done < 4):
+            t = int(order[done])
+            omoba.backward_rows(qn, kn, vn, self.block, blk[[t]], [t], self.p.scale, dn[[t]])
+            done += 1
+        el = time.perf_counter() - t0
+        return {"value": done / el, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{done} random query positions (all {self.hq} heads) of the {self.n}-token sequence: "
+                          f"their dq and their dk, dv contributions; float64 numpy, one process and thread; "
+                          f"{el:.1f} s"}
+
+
 class EsaWorkload(Workload):
     def __init__(self, name, seed, batch, T, m, H, d, d_c, n_init, W, topk, radius, clip, needles=0,
                  correction="clamp"):
@@ -424,6 +501,8 @@ def make(name):
         return MobaWorkload(name, 5, 524288, 8, 8, 128, 8192, 3, torch.bfloat16, attn_rows=8192)
     if name == "moba_decode_128k":
         return MobaDecodeWorkload(name, 128, 16, 131072, 32, 8, 128, 512, 3, planted=8)
+    if name == "moba_bwd_32k":
+        return MobaBwdWorkload(name, 2, 32768, 32, 8, 128, 512, 3, planted=8)
     if name == "esa_prefill_64k":
         return EsaWorkload(name, 3, 1, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0)
     if name == "esa_decode_128k":
@@ -504,6 +583,7 @@ def main():
     kernels = {}
     for name in ("moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn", "moba_current_attn",
                  "moba_generic_attn", "moba_decode_select", "moba_decode_attn", "moba_decode_combine",
+                 "moba_bwd_delta", "moba_bwd_dq_past", "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated",
                  "esa_compress", "esa_qcompress", "esa_scores", "esa_decode_scan", "esa_topk",
                  "esa_prefill_attn", "esa_decode_attn", "esa_generic_attn"):
         tot, n = qat.timing_query(name)

@@ -60,8 +60,8 @@ int qat_abi_version(void);
  * HIP events on the launch stream around each of its main kernels
  * (names: "moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn",
  * "moba_current_attn", "moba_generic_attn", "moba_decode_select",
- * "moba_decode_attn", "moba_decode_combine", "moba_bwd_dq", "moba_bwd_own",
- * "moba_bwd_gated", "esa_compress", "esa_scores",
+ * "moba_decode_attn", "moba_decode_combine", "moba_bwd_delta", "moba_bwd_dq_past",
+ * "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated", "esa_compress", "esa_scores",
  * "esa_decode_scan", "esa_topk", "esa_prefill_attn", "esa_decode_attn",
  * "esa_generic_attn"). The events are timing-only (created without the
  * system-scope fence on completion, so recording them does not slow the
@@ -238,17 +238,20 @@ int moba_sparse_attn(const qat_moba_params* p, const void* q, const void* k, con
  *   dq = scale sum_j p_j (dp_j - D) k_j,
  *   dk_j += scale p_j (dp_j - D) q,  dv_j += p_j dO  (GQA: the query heads of
  *   a KV head add into it).
- * q, k, v, blk as given to moba_sparse_attn (q the whole sequence); lse: its
- * output for the same rows (required); dout: [batch, q_len, Hq, d] (dtype).
+ * q, k, v, blk as given to moba_sparse_attn (q the whole sequence); out and
+ * lse: its outputs for the same rows (both required; D is taken as dO . out
+ * for bfloat16 inputs); dout: [batch, q_len, Hq, d] (dtype).
  * dq: [batch, q_len, Hq, d] float32; dk, dv: [batch, seq_len, Hkv, d]
  * float32, overwritten in full (zero for keys no processed row attends).
  * window must be 0 (QAT_EUNSUPPORTED otherwise). dk and dv are summed with
  * float atomics across row tiles, so their last bits may differ from run to
- * run. Workspace: moba_workspace_size(p).
+ * run. Workspace: moba_bwd_workspace_size(p) (it holds float32 dq partials,
+ * rows x (topk - 1) x d).
  */
+int moba_bwd_workspace_size(const qat_moba_params* p, size_t* bytes);
 int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, const void* k, const void* v,
-                         const int32_t* blk, const void* dout, const float* lse, float* dq, float* dk,
-                         float* dv, void* ws, size_t ws_bytes, void* stream);
+                         const int32_t* blk, const void* out, const void* dout, const float* lse, float* dq,
+                         float* dk, float* dv, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Decode steps ([MoBA] section 3: gating and attention are defined per query

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     moba_block_means,
     moba_decode_select,
     moba_decode_attn,
+    moba_bwd_workspace_size,
     moba_sparse_attn_bwd,
     EXPORTED_SYMBOLS,
     timing_enable,

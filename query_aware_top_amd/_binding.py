@@ -18,7 +18,7 @@ EXPORTED_SYMBOLS = (
     "qat_timing_query",
     "esa_workspace_size", "esa_compress_workspace_size", "esa_compress", "esa_select", "esa_sparse_attn",
     "moba_workspace_size", "moba_block_select", "moba_sparse_attn", "moba_block_means", "moba_decode_select",
-    "moba_decode_attn", "moba_sparse_attn_bwd",
+    "moba_decode_attn", "moba_bwd_workspace_size", "moba_sparse_attn_bwd",
 )
 
 
@@ -80,8 +80,9 @@ def lib():
         L.moba_block_means.argtypes = [ctypes.POINTER(MobaParams), vp, i64, i64, vp, vp, sz, vp]
         L.moba_decode_select.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp]
         L.moba_decode_attn.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.moba_sparse_attn_bwd.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
-                                           vp]
+        L.moba_bwd_workspace_size.argtypes = [ctypes.POINTER(MobaParams), ctypes.POINTER(sz)]
+        L.moba_sparse_attn_bwd.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           sz, vp]
         for name in EXPORTED_SYMBOLS:
             getattr(L, name).restype = ctypes.c_int if name != "qat_last_error" else ctypes.c_char_p
         _lib = L
@@ -327,12 +328,18 @@ def moba_decode_attn(p: MobaParams, q, k, v, blk, out=None, lse=None, want_lse=T
     return out, lse
 
 
-def moba_sparse_attn_bwd(p: MobaParams, q, k, v, blk, dout, lse, dq=None, dk=None, dv=None, ws=None):
+def moba_bwd_workspace_size(p: MobaParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moba_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def moba_sparse_attn_bwd(p: MobaParams, q, k, v, blk, out, dout, lse, dq=None, dk=None, dv=None, ws=None):
     """Gradients of moba_sparse_attn for the same rows with the gating held
-    fixed. Returns (dq [batch, q_len, Hq, d], dk, dv [batch, seq_len, Hkv, d]),
-    all float32."""
+    fixed (out, lse: that call's outputs). Returns (dq [batch, q_len, Hq, d],
+    dk, dv [batch, seq_len, Hkv, d]), all float32."""
     dt = torch.bfloat16 if p.dtype == QAT_BF16 else torch.float32
-    for t, name in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
         _need(t, name, dt)
     _need(blk, "blk", torch.int32)
     _need(lse, "lse", torch.float32)
@@ -345,7 +352,7 @@ def moba_sparse_attn_bwd(p: MobaParams, q, k, v, blk, dout, lse, dq=None, dk=Non
         dv = torch.empty(p.batch, p.seq_len, p.n_kv_heads, p.head_dim, dtype=torch.float32, device=dev)
     for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _need(t, name, torch.float32)
-    ws = _workspace(moba_workspace_size(p), dev, ws)
-    _check(lib().moba_sparse_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(blk), _ptr(dout), _ptr(lse),
-                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
+    ws = _workspace(moba_bwd_workspace_size(p), dev, ws)
+    _check(lib().moba_sparse_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(blk), _ptr(out), _ptr(dout),
+                                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
     return dq, dk, dv

@@ -157,7 +157,8 @@ struct MobaLayout {
   int dec_pieces = 0;
   float* dec_po = nullptr;    // [rows, dec_pieces, d] piece outputs
   float* dec_plse = nullptr;  // [rows, dec_pieces] piece log-sum-exps
-  float* delta = nullptr;     // [rows] sum_j p_j dp_j of the gradient pass
+  float* delta = nullptr;     // [rows] D = sum_j p_j dp_j of the gradient pass
+  float* dq_part = nullptr;   // gradient pass: float32 dq partials per (row, gated slot)
   size_t bytes = 0;
 };
 
@@ -188,7 +189,7 @@ int moba_check(const qat_moba_params* p) {
   return QAT_OK;
 }
 
-MobaLayout moba_layout(const qat_moba_params* p, void* ws) {
+MobaLayout moba_layout(const qat_moba_params* p, void* ws, bool bwd = false) {
   MobaLayout L;
   L.nbc = p->seq_len / p->block;
   L.nrows = p->batch * p->q_len * p->n_q_heads;
@@ -215,6 +216,7 @@ MobaLayout moba_layout(const qat_moba_params* p, void* ws) {
     L.dec_plse = c.take<float>((size_t)L.nrows * L.dec_pieces);
   }
   L.delta = c.take<float>((size_t)L.nrows);
+  if (bwd) L.dq_part = c.take<float>((size_t)qat::moba_bwd_part_floats(L.nrows, p->topk, p->head_dim) + 1);
   L.bytes = c.bytes();
   return L;
 }
@@ -581,17 +583,25 @@ QAT_EXPORT int moba_decode_attn(const qat_moba_params* p, const void* q, const v
                         "moba_decode_attn");
 }
 
-QAT_EXPORT int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, const void* k, const void* v,
-                                    const int32_t* blk, const void* dout, const float* lse, float* dq, float* dk,
-                                    float* dv, void* ws, size_t ws_bytes, void* stream) {
+QAT_EXPORT int moba_bwd_workspace_size(const qat_moba_params* p, size_t* bytes) {
   int rc = moba_check(p);
   if (rc) return rc;
-  if (!q || !k || !v || !blk || !dout || !lse || !dq || !dk || !dv)
-    return fail(QAT_EINVAL, "q, k, v, blk, dout, lse, dq, dk, dv must be non-NULL");
+  if (!bytes) return fail(QAT_EINVAL, "bytes is NULL");
+  *bytes = moba_layout(p, nullptr, true).bytes;
+  return ok();
+}
+
+QAT_EXPORT int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, const void* k, const void* v,
+                                    const int32_t* blk, const void* out, const void* dout, const float* lse,
+                                    float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+  int rc = moba_check(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !blk || !out || !dout || !lse || !dq || !dk || !dv)
+    return fail(QAT_EINVAL, "q, k, v, blk, out, dout, lse, dq, dk, dv must be non-NULL");
   if (p->window != 0) return fail(QAT_EUNSUPPORTED, "gradients with an extra local window are not implemented");
-  MobaLayout L = moba_layout(p, nullptr);
+  MobaLayout L = moba_layout(p, nullptr, true);
   if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
-  L = moba_layout(p, ws);
+  L = moba_layout(p, ws, true);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   const bool gated = p->topk > 1 && L.nbuckets > 0;
@@ -602,8 +612,8 @@ QAT_EXPORT int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, con
                                   L.tiles, L.ntiles, s);
     if (e != hipSuccess) return hip_status(e, "moba_sparse_attn_bwd: dispatch");
   }
-  e = qat::launch_moba_bwd(q, k, v, blk, dout, lse, L.tiles, L.ntiles, L.entries, gated ? L.max_tiles : 0, dq,
-                           L.delta, dk, dv, p->dtype == QAT_BF16, p->batch, p->seq_len, p->n_q_heads,
+  e = qat::launch_moba_bwd(q, k, v, blk, out, dout, lse, L.tiles, L.ntiles, L.entries, gated ? L.max_tiles : 0,
+                           L.dq_part, dq, L.delta, dk, dv, p->dtype == QAT_BF16, p->batch, p->seq_len, p->n_q_heads,
                            p->n_kv_heads, p->head_dim, p->q_start, p->q_len, p->block, p->topk, p->scale, s);
   return hip_status(e, "moba_sparse_attn_bwd");
 }

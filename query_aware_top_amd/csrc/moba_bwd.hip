@@ -8,10 +8,13 @@
 // MoBA write-up, sections 2-3 (the attention over the gated set); the
 // gradient is that of softmax attention restricted to the set.
 //
-// Three kernels, vector float32 arithmetic:
-//   dq      one wave per row, four 16-lane groups taking every fourth key of
-//           the row's set; p comes straight from the forward lse (no running
-//           max), and D is accumulated in the same pass through
+// Kernels:
+//   dq      bfloat16: on the matrix cores (gated blocks per dispatch tile
+//           into float32 partials, own block + partials per row, below);
+//           float32: one
+//           wave per row, four 16-lane groups taking every fourth key of the
+//           row's set, p straight from the forward lse (no running max) and
+//           D accumulated in the same pass through
 //           dq = scale (sum p dp k - D sum p k);
 //   own     a workgroup per (sequence, KV head, 64 keys of a block): the
 //           block's own rows (positions in the block, every query head of
@@ -21,17 +24,18 @@
 //           the rows that gated the block, as bucketed by the forward
 //           dispatch; adds into dk, dv with float atomics, once per bucket
 //           the run touches.
-// In the two key kernels, lane (key i, quarter c) of a wave holds dims
+// The key kernels run in vector float32 arithmetic: lane (key i, quarter c) of a wave holds dims
 // [c D/4, (c+1) D/4) of key i's K, V, dK and dV; rows pass through LDS 16 at
 // a time as float32 (quarters padded against bank conflicts).
 #include <algorithm>
+#include <type_traits>
 
+#include "attn_core.h"
 #include "common.h"
 #include "launch.h"
 
 namespace qat {
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBwdKeys = 64;   // keys per workgroup of the key kernels (16 per wave)
 constexpr int kBwdRows = 16;   // rows staged per LDS round
 constexpr int kBwdTilesPerWg = 8;
@@ -329,53 +333,367 @@ __global__ __launch_bounds__(256) void moba_bwd_gated_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dq on the bf16 matrix cores (bfloat16 inputs), with the tile engine's
+// layout: per 64-key tile, S^T = K Q^T and dP^T = V dO^T (A = K or V tile
+// from LDS, B = the row's q or dO in registers, so each lane owns one row
+// and 16 keys per 32-key half) and p = exp2(S scale log2e - lse log2e) from
+// the forward's lse. D is not known before the row's last key, so the pass
+// accumulates D = sum p dp, A = sum p dp k and B = sum p k, and
+// dq = scale (A - D B) at the end: A^T += K^T (p dp)^T and B^T += K^T p^T
+// with A = K^T by transposing reads of the same K tile (as V^T in the
+// forward), each B operand split into bfloat16 hi + lo (their sum carries
+// the value to 2^-17 relative, so A - D B keeps its accuracy). Gated blocks
+// (two workgroups per dispatch tile, 128 rows each) leave float32 partials
+// (A, B, D) per (row, slot); the own-block kernel adds its causal part and
+// the row's partials, writes dq and D (which the key kernels read).
+constexpr int kBwdNW = 4;                    // waves of the dq kernels (one per SIMD: 512 registers)
+constexpr int kBwdCurRows = 32 * kBwdNW;
+
+template <int D>
+constexpr int bwd_part_stride() { return 2 * D + 4; }   // A, B, D (+ padding) per (row, slot)
+
+template <int D>
+struct DqState {
+  FaState<D> fa;          // q as B operand, A^T accumulator in fa.o, LDS offsets
+  f32x16 b[D / 32];       // B^T accumulator (same layout as fa.o)
+  bf16x8 dob[D / 16];     // dO as B operand
+  float lse2, dsum;       // dsum: this lane's keys only (halves joined at the end)
+};
+
+template <int D>
+__device__ __forceinline__ void dq_init(DqState<D>& st, const bf16* qrow, const bf16* drow, float lse, bool valid) {
+  fa_init<D>(st.fa, qrow, valid);
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    if (valid) {
+      st.dob[c] = *(const bf16x8*)(drow + 16 * c + 8 * h);
+    } else {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      st.dob[c] = __builtin_bit_cast(bf16x8, z);
+    }
+  }
+#pragma unroll
+  for (int tq = 0; tq < D / 32; ++tq)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.b[tq][i] = 0.f;
+  st.lse2 = valid ? lse * kLog2e : 0.f;
+  st.dsum = 0.f;
+}
+
+// S^T-shaped product of one 64-row LDS tile (A) with per-lane B fragments.
+template <int D>
+__device__ __forceinline__ void dq_tile_prod(const int* kofs, const bf16* __restrict__ tile, const bf16x8* b,
+                                             f32x16* s) {
+  const char* kb = reinterpret_cast<const char*>(tile);
+  constexpr int RB = D * 2;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[sb][i] = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const bf16x8 a = *(const bf16x8*)(kb + kofs[c] + sb * 32 * RB);
+      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[c], s[sb], 0, 0, 0);
+    }
+}
+
+// bfloat16 hi + lo split of a pair: .x = packed hi, .y = packed lo
+__device__ __forceinline__ uint2 split_pack(float x0, float x1) {
+  const bf16 h0 = (bf16)x0, h1 = (bf16)x1;
+  return make_uint2(pack_bf16x2((float)h0, (float)h1), pack_bf16x2(x0 - (float)h0, x1 - (float)h1));
+}
+
+// One 64-key tile: keys with key_ok(kidx) false (kidx 0..63 within the tile)
+// get p = 0.
+template <int D, typename KeyOk>
+__device__ __forceinline__ void dq_tile(DqState<D>& st, const bf16* __restrict__ ks, const bf16* __restrict__ vs,
+                                        float sl2, KeyOk key_ok) {
+  f32x16 s[2], dp[2];
+  dq_tile_prod<D>(st.fa.kofs, ks, st.fa.q, s);
+  dq_tile_prod<D>(st.fa.kofs, vs, st.dob, dp);
+  const int h = (threadIdx.x & 63) >> 5;
+  u32x4 pdh[4], pdl[4], ph[4], pl[4];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      float p2[2], pd2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int kidx = sb * 32 + ((i + u) >> 2) * 8 + h * 4 + ((i + u) & 3);
+        p2[u] = key_ok(kidx) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i + u], sl2, -st.lse2)) : 0.f;
+        pd2[u] = p2[u] * dp[sb][i + u];
+        st.dsum += pd2[u];
+      }
+      const int kc = sb * 2 + (i >> 3), w = (i & 7) >> 1;
+      const uint2 a2 = split_pack(pd2[0], pd2[1]), b2 = split_pack(p2[0], p2[1]);
+      pdh[kc][w] = a2.x;
+      pdl[kc][w] = a2.y;
+      ph[kc][w] = b2.x;
+      pl[kc][w] = b2.y;
+    }
+  const char* kb = reinterpret_cast<const char*>(ks);
+  constexpr int RB = D * 2;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+    for (int tq = 0; tq < D / 32; ++tq) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb + st.fa.vofs[tq][0] + 16 * kc * RB));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb + st.fa.vofs[tq][1] + 16 * kc * RB));
+      const i16x4 both[2] = {lo, hi};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, both);
+      st.fa.o[tq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pdh[kc]), st.fa.o[tq], 0, 0, 0);
+      st.fa.o[tq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pdl[kc]), st.fa.o[tq], 0, 0, 0);
+      st.b[tq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, ph[kc]), st.b[tq], 0, 0, 0);
+      st.b[tq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pl[kc]), st.b[tq], 0, 0, 0);
+    }
+  }
+}
+
+// All tiles of n keys from K / V (row_ofs(j): key j's element offset), K and
+// V tiles double-buffered in LDS, one barrier per tile. Called by all NW*64
+// threads of the workgroup.
+template <int D, int NW, typename RowOfs, typename KeyOk>
+__device__ __forceinline__ void dq_segment(DqState<D>& st, const FaSmem<D>& sm, const bf16* __restrict__ K,
+                                           const bf16* __restrict__ V, int n, float sl2, RowOfs row_ofs,
+                                           KeyOk key_ok) {
+  if (n <= 0) return;
+  const int nt = (n + kKT - 1) / kKT;
+  fa_issue_one<D, NW>(sm.k0, K, 0, n, row_ofs);
+  fa_issue_one<D, NW>(sm.v0, V, 0, n, row_ofs);
+  for (int j = 0; j < nt; j += 2) {
+    fa_wait_loads();
+    fa_lds_barrier();
+    if (j + 1 < nt) {
+      fa_issue_one<D, NW>(sm.k1, K, (j + 1) * kKT, n, row_ofs);
+      fa_issue_one<D, NW>(sm.v1, V, (j + 1) * kKT, n, row_ofs);
+    }
+    dq_tile<D>(st, sm.k0, sm.v0, sl2, [&](int kidx) { return j * kKT + kidx < n && key_ok(j * kKT + kidx); });
+    if (j + 1 >= nt) break;
+    fa_wait_loads();
+    fa_lds_barrier();
+    if (j + 2 < nt) {
+      fa_issue_one<D, NW>(sm.k0, K, (j + 2) * kKT, n, row_ofs);
+      fa_issue_one<D, NW>(sm.v0, V, (j + 2) * kKT, n, row_ofs);
+    }
+    dq_tile<D>(st, sm.k1, sm.v1, sl2,
+               [&](int kidx) { return (j + 1) * kKT + kidx < n && key_ok((j + 1) * kKT + kidx); });
+  }
+  fa_wait_loads();
+  fa_lds_barrier();
+}
+
+// Gated blocks: two workgroups per dispatch tile (rows [128 half, 128 half +
+// 128)); part[(row * (topk-1) + slot) * PS + ...] = A, B (accumulator layout
+// d = 32 t + 8 (i/4) + 4 (lane/32) + i%4), D.
+template <int D>
+__global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_dq_past_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ ntiles, const int2* __restrict__ entries, float* __restrict__ part, int64_t hkv,
+    int block, int topk, float scale) {
+  constexpr int PS = bwd_part_stride<D>();
+  QAT_FA_SMEM(D, sm);
+  const int64_t id = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int64_t tile = id >> 1;
+  if (tile >= ntiles[0]) return;
+  const int4 td = tiles[tile];
+  const int64_t kv_off = (int64_t)(uint32_t)td.x | ((int64_t)td.y << 32);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int myrow = (int)(id & 1) * kBwdCurRows + wave * 32 + (lane & 31);
+  if ((int)(id & 1) * kBwdCurRows >= td.w) return;   // uniform: no rows in this half
+  const bool valid = myrow < td.w;
+  const int2 e2 = valid ? entries[td.z + myrow] : make_int2(0, 0);
+  const int64_t row = e2.x >> 4;
+  const int slot = e2.x & 15;
+  DqState<D> st;
+  dq_init<D>(st, q + (int64_t)e2.y * D, dout + row * D, valid ? lse[row] : 0.f, valid);
+  const int kv_stride = (int)(hkv * D);
+  dq_segment<D, kBwdNW>(st, sm, k + kv_off, v + kv_off, block, scale * kLog2e,
+                        [=](int j) { return j * kv_stride; }, [](int) { return true; });
+  const float dsum = xor32_sum(st.dsum);
+  if (!valid) return;
+  float* dst = part + (row * (topk - 1) + slot) * PS;
+  const int h = lane >> 5;
+#pragma unroll
+  for (int tq = 0; tq < D / 32; ++tq)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      f32x4 wa, wb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wa[e] = st.fa.o[tq][4 * gi + e];
+        wb[e] = st.b[tq][4 * gi + e];
+      }
+      *(f32x4*)(dst + 32 * tq + 8 * gi + 4 * h) = wa;
+      *(f32x4*)(dst + D + 32 * tq + 8 * gi + 4 * h) = wb;
+    }
+  if (h == 0) dst[2 * D] = dsum;
+}
+
+// Own block (causal) plus the row's gated partials -> dq and D. Row mapping
+// as the forward's current-block kernel: a workgroup holds 32*NW rows =
+// 32*NW/P consecutive positions x P query heads of one KV group.
+template <int D>
+__global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_dq_cur_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const int32_t* __restrict__ blk,
+    const float* __restrict__ part, float* __restrict__ dq, float* __restrict__ delta, int64_t seq_len, int64_t hq,
+    int64_t hkv, int64_t q_start, int64_t q_len, int block, int topk, float scale, int pack, int tiles_per_block,
+    int64_t nblocks) {
+  constexpr int NW = kBwdNW;
+  constexpr int PS = bwd_part_stride<D>();
+  QAT_FA_SMEM(D, sm);
+  int64_t id = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int tt = (int)(id % tiles_per_block);
+  id /= tiles_per_block;
+  const int64_t cb = id % nblocks;
+  id /= nblocks;
+  const int64_t gs = hq / hkv;
+  const int64_t npk = gs / pack;
+  const int64_t hp = id % npk;
+  id /= npk;
+  const int64_t g = id % hkv;
+  const int64_t bi = id / hkv;
+  const int64_t c = q_start / block + cb;
+  const int64_t lo = max(c * block, q_start);
+  const int64_t hi = min((c + 1) * block, q_start + q_len);
+  const int tok_per_tile = kBwdCurRows / pack;
+  const int64_t t0 = lo + (int64_t)tt * tok_per_tile;
+  if (t0 >= hi) return;   // uniform
+  const int64_t t_last = min(hi, t0 + tok_per_tile) - 1;
+  const int64_t h0 = g * gs + hp * pack;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int myrow = wave * 32 + (lane & 31);
+  const int64_t t = t0 + myrow / pack;
+  const int64_t h = h0 + myrow % pack;
+  const bool valid = t <= t_last;
+  const int64_t tv = valid ? t : t0;
+  const int64_t row = (bi * q_len + (tv - q_start)) * hq + h;
+  DqState<D> st;
+  dq_init<D>(st, q + ((bi * seq_len + tv) * hq + h) * D, dout + row * D, lse[row], valid);
+  const int64_t kpos0 = c * block;
+  const int kv_stride = (int)(hkv * D);
+  const int lim = valid ? (int)(t - kpos0) : -1;
+  dq_segment<D, NW>(st, sm, k + ((bi * seq_len + kpos0) * hkv + g) * D, v + ((bi * seq_len + kpos0) * hkv + g) * D,
+                    (int)(t_last - kpos0 + 1), scale * kLog2e, [=](int j) { return j * kv_stride; },
+                    [=](int j) { return j <= lim; });
+  float dsum = xor32_sum(st.dsum);
+  if (!valid) return;
+  const int hl = lane >> 5;
+  const int km = topk - 1;
+  const int64_t cur = t / block;
+  for (int s = 0; s < km; ++s) {   // gated blocks sit in the first topk - 1 slots
+    const int32_t b = blk[row * topk + s];
+    if (b < 0 || b >= cur) continue;
+    const float* src = part + (row * km + s) * PS;
+#pragma unroll
+    for (int tq = 0; tq < D / 32; ++tq)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const f32x4 wa = *(const f32x4*)(src + 32 * tq + 8 * gi + 4 * hl);
+        const f32x4 wb = *(const f32x4*)(src + D + 32 * tq + 8 * gi + 4 * hl);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          st.fa.o[tq][4 * gi + e] += wa[e];
+          st.b[tq][4 * gi + e] += wb[e];
+        }
+      }
+    dsum += src[2 * D];
+  }
+  float* dst = dq + row * D;
+#pragma unroll
+  for (int tq = 0; tq < D / 32; ++tq)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = scale * (st.fa.o[tq][4 * gi + e] - dsum * st.b[tq][4 * gi + e]);
+      *(f32x4*)(dst + 32 * tq + 8 * gi + 4 * hl) = w;
+    }
+  if (hl == 0) delta[row] = dsum;
+}
+
+// ---------------------------------------------------------------------------
 int moba_bwd_chunks(int block) { return (int)cdiv(block, kBwdKeys); }
 
-hipError_t launch_moba_bwd(const void* q, const void* k, const void* v, const int32_t* blk, const void* dout,
-                           const float* lse, const int4* tiles, const int32_t* ntiles, const int2* entries,
-                           int64_t max_tiles, float* dq, float* delta, float* dk, float* dv, bool bf,
-                           int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t q_start,
-                           int64_t q_len, int block, int topk, float scale, hipStream_t s) {
+template <typename T, int D>
+static hipError_t launch_moba_bwd_d(const T* q, const T* k, const T* v, const int32_t* blk, const T* out,
+                                    const T* dout, const float* lse, const int4* tiles, const int32_t* ntiles,
+                                    const int2* entries, int64_t max_tiles, float* dq_part, float* dq, float* delta,
+                                    float* dk, float* dv, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
+                                    int64_t q_start, int64_t q_len, int block, int topk, float scale,
+                                    hipStream_t s) {
+  constexpr bool kMfma = std::is_same<T, bf16>::value;
   const int64_t rows = batch * q_len * hq;
   const int cpb = moba_bwd_chunks(block);
   const int64_t nb_all = cdiv(seq_len, block);
-  dim3 g_dq((unsigned)cdiv(rows, 4));
-  dim3 g_own((unsigned)(nb_all * cpb), (unsigned)hkv, (unsigned)batch);
-  dim3 g_gt((unsigned)std::max<int64_t>(1, cdiv(max_tiles, kBwdTilesPerWg)), (unsigned)cpb);
-#define QAT_BWD(T_, D_)                                                                                      \
-  do {                                                                                                       \
-    {                                                                                                        \
-      KTimer tm_("moba_bwd_dq", s);                                                                          \
-      launch_timed("moba_bwd_dq", moba_bwd_dq_kernel<T_, D_>, g_dq, dim3(256), 0, s, (const T_*)q,           \
-                   (const T_*)k, (const T_*)v, blk, (const T_*)dout, lse, dq, delta, rows, seq_len, hq, hkv,  \
-                   q_start, q_len, block, topk, scale);                                                      \
-    }                                                                                                        \
-    if ((e = hipGetLastError()) != hipSuccess) return e;                                                     \
-    {                                                                                                        \
-      KTimer tm_("moba_bwd_own", s);                                                                         \
-      launch_timed("moba_bwd_own", moba_bwd_own_kernel<T_, D_>, g_own, dim3(256), 0, s, (const T_*)q,        \
-                   (const T_*)k, (const T_*)v, (const T_*)dout, lse, (const float*)delta, dk, dv, seq_len,  \
-                   hq, hkv, q_start, q_len, block, cpb, scale);                                              \
-    }                                                                                                        \
-    if ((e = hipGetLastError()) != hipSuccess) return e;                                                     \
-    if (topk > 1 && max_tiles > 0) {                                                                         \
-      KTimer tm_("moba_bwd_gated", s);                                                                       \
-      launch_timed("moba_bwd_gated", moba_bwd_gated_kernel<T_, D_>, g_gt, dim3(256), 0, s, (const T_*)q,     \
-                   (const T_*)k, (const T_*)v, (const T_*)dout, lse, (const float*)delta, tiles, ntiles,     \
-                   entries, dk, dv, hkv, block, scale);                                                      \
-    }                                                                                                        \
-  } while (0)
-  hipError_t e = hipSuccess;
-  if (rows == 0) return e;
+  const bool gated = topk > 1 && max_tiles > 0;
+  hipError_t e;
+  if constexpr (kMfma) {
+    (void)out;
+    if (gated) {
+      KTimer tm("moba_bwd_dq_past", s);
+      launch_timed("moba_bwd_dq_past", moba_bwd_dq_past_kernel<D>, dim3((unsigned)(2 * max_tiles)),
+                   dim3(64 * kBwdNW), 0, s, q, k, v, dout, lse, tiles, ntiles, entries, dq_part, hkv, block, topk,
+                   scale);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const int64_t gs = hq / hkv;
+    const int pack = (kBwdCurRows % gs == 0) ? (int)gs : 1;
+    const int tiles_per_block = (int)cdiv(block, kBwdCurRows / pack);
+    const int64_t nblocks = (q_start + q_len - 1) / block - q_start / block + 1;
+    const int64_t nwg = (int64_t)tiles_per_block * nblocks * batch * hkv * (gs / pack);
+    {
+      KTimer tm("moba_bwd_dq", s);
+      launch_timed("moba_bwd_dq", moba_bwd_dq_cur_kernel<D>, dim3((unsigned)nwg), dim3(64 * kBwdNW), 0, s, q, k, v,
+                   dout, lse, blk, (const float*)dq_part, dq, delta, seq_len, hq, hkv, q_start, q_len, block, topk,
+                   scale, pack, tiles_per_block, nblocks);
+    }
+  } else {
+    KTimer tm("moba_bwd_dq", s);
+    launch_timed("moba_bwd_dq", moba_bwd_dq_kernel<T, D>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s, q, k, v,
+                 blk, dout, lse, dq, delta, rows, seq_len, hq, hkv, q_start, q_len, block, topk, scale);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    KTimer tm("moba_bwd_own", s);
+    launch_timed("moba_bwd_own", moba_bwd_own_kernel<T, D>, dim3((unsigned)(nb_all * cpb), (unsigned)hkv,
+                 (unsigned)batch), dim3(256), 0, s, q, k, v, dout, lse, (const float*)delta, dk, dv, seq_len, hq,
+                 hkv, q_start, q_len, block, cpb, scale);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (gated) {
+    KTimer tm("moba_bwd_gated", s);
+    launch_timed("moba_bwd_gated", moba_bwd_gated_kernel<T, D>,
+                 dim3((unsigned)std::max<int64_t>(1, cdiv(max_tiles, kBwdTilesPerWg)), (unsigned)cpb), dim3(256), 0,
+                 s, q, k, v, dout, lse, (const float*)delta, tiles, ntiles, entries, dk, dv, hkv, block, scale);
+  }
+  return hipGetLastError();
+}
+
+int64_t moba_bwd_part_floats(int64_t rows, int topk, int64_t d) { return rows * (topk - 1) * (2 * d + 4); }
+
+hipError_t launch_moba_bwd(const void* q, const void* k, const void* v, const int32_t* blk, const void* out,
+                           const void* dout, const float* lse, const int4* tiles, const int32_t* ntiles,
+                           const int2* entries, int64_t max_tiles, float* dq_part, float* dq, float* delta, float* dk,
+                           float* dv, bool bf, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d,
+                           int64_t q_start, int64_t q_len, int block, int topk, float scale, hipStream_t s) {
+  if (batch * q_len * hq == 0) return hipSuccess;
+#define QAT_BWD(T_, D_)                                                                                     \
+  return launch_moba_bwd_d<T_, D_>((const T_*)q, (const T_*)k, (const T_*)v, blk, (const T_*)out,          \
+                                   (const T_*)dout, lse, tiles, ntiles, entries, max_tiles, dq_part, dq, delta, \
+                                   dk, dv, batch, seq_len, hq, hkv, q_start, q_len, block, topk, scale, s)
   if (bf) {
     if (d == 64) QAT_BWD(bf16, 64);
-    else QAT_BWD(bf16, 128);
-  } else {
-    if (d == 64) QAT_BWD(float, 64);
-    else QAT_BWD(float, 128);
+    QAT_BWD(bf16, 128);
   }
+  if (d == 64) QAT_BWD(float, 64);
+  QAT_BWD(float, 128);
 #undef QAT_BWD
-  return hipGetLastError();
 }
 
 }  // namespace qat
