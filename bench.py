@@ -312,7 +312,7 @@ class MobaBwdWorkload(Workload):
         self.dq = torch.empty(1, n, hq, d, dtype=torch.float32, device="cuda")
         self.dk = torch.empty(1, n, hkv, d, dtype=torch.float32, device="cuda")
         self.dv = torch.empty(1, n, hkv, d, dtype=torch.float32, device="cuda")
-        self.dominant, self.bound = "moba_bwd_gated", "alu"
+        self.dominant, self.bound = "moba_bwd_gated", "mfma"
 
     def step(self):
         self.qat.moba_sparse_attn_bwd(self.p, self.q, self.k, self.v, self.blk, self.out, self.do, self.lse,
@@ -324,7 +324,8 @@ class MobaBwdWorkload(Workload):
     def dominant_work(self):
         """The gated-row key kernel: 4 products of d per (row, key) pair of
         the gated blocks (s = q.k, dp = dO.v, dv += p dO, dk += ds q), 2 flops
-        each: 8 d flops per pair."""
+        each: 8 d flops per pair (the hi + lo split of p and ds executes two
+        of them twice; that is not counted)."""
         blk = self.blk[0].to(torch.int64)
         cur = (torch.arange(self.n, device="cuda") // self.block)[:, None, None]
         past = ((blk[..., :self.topk - 1] >= 0) & (blk[..., :self.topk - 1] < cur)).sum().item()

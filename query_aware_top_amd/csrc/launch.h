@@ -42,6 +42,7 @@ hipError_t launch_moba_select(const void* q, bool bf, const float* kbar, const b
 // ---- MoBA attention (moba_attn.hip) ---------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 int64_t moba_max_tiles(int64_t nrows, int topk, int64_t nbuckets);
+int moba_rows_per_tile();   // query rows per dispatch tile
 // tiles: {element offset of the block's K/V rows (low, high word), first
 // entry, row count}; entries: {row * 16 + slot, row index of the query in q}
 hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,

@@ -639,6 +639,8 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
+int moba_rows_per_tile() { return kRowsPerTile; }
+
 int64_t moba_max_tiles(int64_t nrows, int topk, int64_t nbuckets) {
   return cdiv(nrows * (topk - 1), kRowsPerTile) + nbuckets;
 }

@@ -39,6 +39,7 @@ namespace qat {
 constexpr int kBwdKeys = 64;   // keys per workgroup of the key kernels (16 per wave)
 constexpr int kBwdRows = 16;   // rows staged per LDS round
 constexpr int kBwdTilesPerWg = 8;
+constexpr int kRowsPerTileBwd = 256;   // rows per forward dispatch tile
 
 template <typename T, int N>
 __device__ __forceinline__ void load_f32(const T* p, float (&x)[N]) {
@@ -618,6 +619,299 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_dq_cur_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dK and dV on the matrix cores (bfloat16 inputs): the tile engine with the
+// roles of rows and keys exchanged. A wave holds 32 keys of the block as B
+// operands (K^T and V^T fragments, lane = key) and its dK^T, dV^T
+// accumulators; the rows stream through LDS 64 at a time (q and dO tiles,
+// double-buffered direct loads, with each row's lse and D). Per row tile:
+// S = Q K^T and dP = dO V^T (A = the q / dO tile, so each lane holds one key
+// and 16 rows per 32-row half), p = exp2(S scale log2e - lse log2e),
+// ds = p (dp - D), then dV^T += dO^T p and dK^T += Q^T ds with A = dO^T /
+// Q^T by transposing reads of the tiles (as V^T in the forward) and p, ds
+// split into bfloat16 hi + lo.
+constexpr int kKvKeys = 32 * kBwdNW;   // keys per workgroup (32 per wave)
+constexpr int kKvRun = 8;              // dispatch tiles per gated workgroup
+constexpr int kKvDynBytes = 6 * 64 * 4 + kKvRun * kRowsPerTileBwd * 8;
+
+template <int D>
+struct KvState {
+  FaState<D> fa;          // K^T fragments in fa.q, dK^T in fa.o, LDS offsets
+  bf16x8 vq[D / 16];      // V^T fragments
+  f32x16 dv[D / 32];      // dV^T
+};
+
+template <int D>
+__device__ __forceinline__ void kv_load(KvState<D>& st, const bf16* krow, const bf16* vrow) {
+  fa_init<D>(st.fa, krow, true);
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) st.vq[c] = *(const bf16x8*)(vrow + 16 * c + 8 * h);
+#pragma unroll
+  for (int tq = 0; tq < D / 32; ++tq)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.dv[tq][i] = 0.f;
+}
+
+// One tile of up to 64 rows: rows m with row_ok(m) false get p = 0. lse_t /
+// di_t: the tile's lse (natural log) and D per row, in LDS.
+template <int D, typename RowOk>
+__device__ __forceinline__ void kv_tile(KvState<D>& st, const bf16* __restrict__ qt, const bf16* __restrict__ dt,
+                                        const float* lse_t, const float* di_t, float sl2, RowOk row_ok) {
+  f32x16 s[2], dp[2];
+  dq_tile_prod<D>(st.fa.kofs, qt, st.fa.q, s);
+  dq_tile_prod<D>(st.fa.kofs, dt, st.vq, dp);
+  const int h = (threadIdx.x & 63) >> 5;
+  const char* qb = reinterpret_cast<const char*>(qt);
+  const char* db = reinterpret_cast<const char*>(dt);
+  constexpr int RB = D * 2;
+  // one 32-row half at a time: its p and ds packs feed the row chunks
+  // kc = 2 sb, 2 sb + 1 of the accumulations
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    u32x4 pph[2], ppl[2], dsh[2], dsl[2];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      float p2[2], ds2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int m = sb * 32 + ((i + u) >> 2) * 8 + h * 4 + ((i + u) & 3);
+        p2[u] = row_ok(m) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i + u], sl2, -lse_t[m] * kLog2e)) : 0.f;
+        ds2[u] = p2[u] * (dp[sb][i + u] - di_t[m]);
+      }
+      const int kk = i >> 3, w = (i & 7) >> 1;
+      const uint2 a2 = split_pack(p2[0], p2[1]), b2 = split_pack(ds2[0], ds2[1]);
+      pph[kk][w] = a2.x;
+      ppl[kk][w] = a2.y;
+      dsh[kk][w] = b2.x;
+      dsl[kk][w] = b2.y;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kc = 2 * sb + kk;
+#pragma unroll
+      for (int tq = 0; tq < D / 32; ++tq) {
+        const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(db + st.fa.vofs[tq][0] + 16 * kc * RB));
+        const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(db + st.fa.vofs[tq][1] + 16 * kc * RB));
+        const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(qb + st.fa.vofs[tq][0] + 16 * kc * RB));
+        const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(qb + st.fa.vofs[tq][1] + 16 * kc * RB));
+        const i16x4 dd[2] = {d0, d1}, qq[2] = {q0, q1};
+        const bf16x8 ad = __builtin_bit_cast(bf16x8, dd), aq = __builtin_bit_cast(bf16x8, qq);
+        st.dv[tq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, __builtin_bit_cast(bf16x8, pph[kk]), st.dv[tq], 0, 0, 0);
+        st.dv[tq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, __builtin_bit_cast(bf16x8, ppl[kk]), st.dv[tq], 0, 0, 0);
+        st.fa.o[tq] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, __builtin_bit_cast(bf16x8, dsh[kk]), st.fa.o[tq], 0, 0, 0);
+        st.fa.o[tq] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, __builtin_bit_cast(bf16x8, dsl[kk]), st.fa.o[tq], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// This lane's key's dK, dV (accumulator layout d = 32 tq + 8 gi + 4 h + e)
+// stored (ADD = false) or added with float atomics.
+template <int D, bool ADD>
+__device__ __forceinline__ void kv_write(const KvState<D>& st, float* dkr, float* dvr, float scale) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int tq = 0; tq < D / 32; ++tq)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int d0 = 32 * tq + 8 * gi + 4 * h;
+      if constexpr (ADD) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          unsafeAtomicAdd(dkr + d0 + e, scale * st.fa.o[tq][4 * gi + e]);
+          unsafeAtomicAdd(dvr + d0 + e, st.dv[tq][4 * gi + e]);
+        }
+      } else {
+        f32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = scale * st.fa.o[tq][4 * gi + e];
+          b[e] = st.dv[tq][4 * gi + e];
+        }
+        *(f32x4*)(dkr + d0) = a;
+        *(f32x4*)(dvr + d0) = b;
+      }
+    }
+}
+
+// Own-block rows. grid (blocks * key chunks, hkv, batch); rows = positions
+// [max(chunk start, q_start), min(block end, q_start + q_len)) x the group's
+// heads, row r = position t0 + r / G, head g G + r % G.
+template <int D>
+__global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_own_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* __restrict__ dk, float* __restrict__ dv, int64_t seq_len, int64_t hq, int64_t hkv, int64_t q_start,
+    int64_t q_len, int block, int cpb, float scale) {
+  QAT_FA_SMEM(D, sm);
+  extern __shared__ __align__(16) char kv_dyn[];
+  float* s_lse = reinterpret_cast<float*>(kv_dyn);          // [2][64]
+  float* s_di = s_lse + 128;                                 // [2][64]
+  const int64_t b = blockIdx.x / cpb, c = blockIdx.x % cpb, g = blockIdx.y, bi = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t blk0 = b * block, blk1 = min(blk0 + block, seq_len);
+  const int64_t c0 = blk0 + c * kKvKeys;
+  if (c0 >= blk1) return;   // uniform
+  const int64_t c1 = min(c0 + kKvKeys, blk1);
+  const int64_t key = c0 + wave * 32 + (lane & 31);
+  const bool kvalid = key < c1;
+  const int64_t krow = ((bi * seq_len + (kvalid ? key : c0)) * hkv + g) * D;
+  KvState<D> st;
+  kv_load<D>(st, k + krow, v + krow);
+  const int64_t G = hq / hkv;
+  const int64_t t0 = max(c0, q_start), t1 = min(blk1, q_start + q_len);
+  const int nrows = t1 > t0 ? (int)((t1 - t0) * G) : 0;
+  const int nt = (nrows + 63) / 64;
+  const bf16* qbase = q + bi * seq_len * hq * D;
+  const bf16* dbase = dout + bi * q_len * hq * D;
+  const float sl2 = scale * kLog2e;
+  // row r: position t0 + r / G, head g G + r % G; offsets in 32 bits (one
+  // sequence's q rows hold fewer than 2^31 elements)
+  const int Gi = (int)G, hqi = (int)hq;
+  const int q0 = (int)(t0 * hq + g * G), d0 = (int)((t0 - q_start) * hq + g * G);
+  auto issue = [&](bf16* qdst, bf16* ddst, int buf, int rt) {
+    const int r0 = rt * 64, n = min(64, nrows - r0);
+    fa_issue_one<D, kBwdNW>(qdst, qbase, 0, n, [=](int j) {
+      const int r = r0 + j, ti = r / Gi;
+      return (q0 + ti * hqi + (r - ti * Gi)) * D;
+    });
+    fa_issue_one<D, kBwdNW>(ddst, dbase, 0, n, [=](int j) {
+      const int r = r0 + j, ti = r / Gi;
+      return (d0 + ti * hqi + (r - ti * Gi)) * D;
+    });
+    if (wave == 0) {
+      // rows past the tile's end repeat its last row (masked)
+      const int r = r0 + min(lane, n - 1), ti = r / Gi;
+      const int64_t tt = t0 + ti;
+      const int64_t row = (bi * q_len + (tt - q_start)) * hq + g * G + (r - ti * Gi);
+      __builtin_amdgcn_global_load_lds((const global_void*)(lse + row), (lds_void*)(s_lse + buf * 64), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const global_void*)(delta + row), (lds_void*)(s_di + buf * 64), 4, 0, 0);
+    }
+  };
+  // causal mask: row m of tile rt (position t0 + (64 rt + m) / G) sees this
+  // lane's key iff m >= (key - t0) G - 64 rt
+  const int kfirst = (int)(key - t0) * Gi;
+  auto row_ok = [=](int rt) {
+    const int n = min(64, nrows - rt * 64), m0 = kfirst - rt * 64;
+    return [=](int m) { return m < n && m >= m0; };
+  };
+  if (nt > 0) issue(sm.k0, sm.v0, 0, 0);
+  for (int rt = 0; rt < nt; rt += 2) {
+    fa_wait_loads();
+    fa_lds_barrier();
+    if (rt + 1 < nt) issue(sm.k1, sm.v1, 1, rt + 1);
+    kv_tile<D>(st, sm.k0, sm.v0, s_lse, s_di, sl2, row_ok(rt));
+    if (rt + 1 >= nt) break;
+    fa_wait_loads();
+    fa_lds_barrier();
+    if (rt + 2 < nt) issue(sm.k0, sm.v0, 0, rt + 2);
+    kv_tile<D>(st, sm.k1, sm.v1, s_lse + 64, s_di + 64, sl2, row_ok(rt + 1));
+  }
+  if (kvalid) kv_write<D, false>(st, dk + krow, dv + krow, scale);
+}
+
+// Gated rows over the dispatch tiles: grid (runs of kKvRun tiles, key chunks
+// of the block). The run's entries are staged in LDS; a bucket change inside
+// the run adds the finished keys' sums with float atomics and loads the next
+// block's keys.
+template <int D>
+__global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_gated_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, const int2* __restrict__ entries,
+    float* __restrict__ dk, float* __restrict__ dv, int64_t seq_len, int64_t hq, int64_t hkv, int64_t q_len,
+    int block, float scale) {
+  QAT_FA_SMEM(D, sm);
+  extern __shared__ __align__(16) char kv_dyn[];
+  float* s_lse = reinterpret_cast<float*>(kv_dyn);   // [2][64]
+  float* s_di = s_lse + 128;                          // [2][64]
+  int2* s_ent = reinterpret_cast<int2*>(s_di + 256);  // the run's entries (after [2][64] unused ints)
+  const int nt_all = ntiles[0];
+  const int tb = blockIdx.x * kKvRun;
+  if (tb >= nt_all) return;   // uniform
+  const int te = min(nt_all, tb + kKvRun);
+  const int c = blockIdx.y;
+  if (c * kKvKeys >= block) return;   // uniform
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kl = c * kKvKeys + wave * 32 + (lane & 31);   // key within the block
+  const bool kvalid = kl < block;
+  const int e_first = tiles[tb].z;
+  {
+    const int4 tl = tiles[te - 1];
+    const int nent = tl.z + tl.w - e_first;
+    for (int i = threadIdx.x; i < nent; i += 64 * kBwdNW) s_ent[i] = entries[e_first + i];
+  }
+  __syncthreads();
+  const int64_t seq_kv = seq_len * hkv * D;   // elements of one sequence's K
+  const float sl2 = scale * kLog2e;
+  auto issue = [&](bf16* qdst, bf16* ddst, int buf, int ti, int r0) {
+    const int4 tl = tiles[ti];
+    const int n = min(64, tl.w - r0);
+    const int e0 = tl.z - e_first + r0;
+    const int64_t kv = (int64_t)(uint32_t)tl.x | ((int64_t)tl.y << 32);
+    const int64_t bi = kv / seq_kv;
+    const int64_t qo = bi * seq_len * hq, dof = bi * q_len * hq;
+    fa_issue_one<D, kBwdNW>(qdst, q + qo * D, 0, n, [=](int j) { return (int)((s_ent[e0 + j].y - qo) * D); });
+    fa_issue_one<D, kBwdNW>(ddst, dout + dof * D, 0, n,
+                            [=](int j) { return (int)(((int64_t)(s_ent[e0 + j].x >> 4) - dof) * D); });
+    if (wave == 0) {
+      const int64_t row = s_ent[e0 + min(lane, n - 1)].x >> 4;
+      __builtin_amdgcn_global_load_lds((const global_void*)(lse + row), (lds_void*)(s_lse + buf * 64), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const global_void*)(delta + row), (lds_void*)(s_di + buf * 64), 4, 0, 0);
+    }
+  };
+  KvState<D> st;
+  int64_t cur_kv = -1;
+  const int64_t koff = (int64_t)(kvalid ? kl : 0) * hkv * D;
+  auto enter = [&](int ti) {   // the tile's bucket: flush the previous one's sums, load its keys
+    const int4 tl = tiles[ti];
+    const int64_t kv = (int64_t)(uint32_t)tl.x | ((int64_t)tl.y << 32);
+    if (kv == cur_kv) return;
+    if (cur_kv >= 0 && kvalid) kv_write<D, true>(st, dk + cur_kv + koff, dv + cur_kv + koff, scale);
+    cur_kv = kv;
+    kv_load<D>(st, k + kv + koff, v + kv + koff);
+  };
+  auto advance = [&](int& ti, int& r0) {
+    r0 += 64;
+    if (r0 >= tiles[ti].w) { ++ti; r0 = 0; }
+  };
+  auto rows_of = [&](int ti, int r0) { return min(64, tiles[ti].w - r0); };
+  int ti = tb, r0 = 0;
+  issue(sm.k0, sm.v0, 0, ti, r0);
+  for (;;) {
+    fa_wait_loads();
+    fa_lds_barrier();
+    int tn = ti, rn = r0;
+    advance(tn, rn);
+    if (tn < te) issue(sm.k1, sm.v1, 1, tn, rn);
+    enter(ti);
+    {
+      const int n = rows_of(ti, r0);
+      kv_tile<D>(st, sm.k0, sm.v0, s_lse, s_di, sl2, [=](int m) { return m < n; });
+    }
+    ti = tn;
+    r0 = rn;
+    if (ti >= te) break;
+    fa_wait_loads();
+    fa_lds_barrier();
+    advance(tn, rn);
+    if (tn < te) issue(sm.k0, sm.v0, 0, tn, rn);
+    enter(ti);
+    {
+      const int n = rows_of(ti, r0);
+      kv_tile<D>(st, sm.k1, sm.v1, s_lse + 64, s_di + 64, sl2, [=](int m) { return m < n; });
+    }
+    ti = tn;
+    r0 = rn;
+    if (ti >= te) break;
+  }
+  fa_wait_loads();
+  if (kvalid) kv_write<D, true>(st, dk + cur_kv + koff, dv + cur_kv + koff, scale);
+}
+
+// ---------------------------------------------------------------------------
 int moba_bwd_chunks(int block) { return (int)cdiv(block, kBwdKeys); }
 
 template <typename T, int D>
@@ -659,6 +953,37 @@ static hipError_t launch_moba_bwd_d(const T* q, const T* k, const T* v, const in
                  blk, dout, lse, dq, delta, rows, seq_len, hq, hkv, q_start, q_len, block, topk, scale);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if constexpr (kMfma) {
+    // the matrix-core key kernels address one sequence's q / dO rows with
+    // 32-bit offsets from the sequence's base
+    if (seq_len * hq * D < (1ll << 31) && moba_rows_per_tile() == kRowsPerTileBwd) {
+      static const bool lds_ok = [] {
+        bool ok = hipFuncSetAttribute((const void*)moba_bwd_kv_own_kernel<D>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kKvDynBytes) == hipSuccess;
+        ok &= hipFuncSetAttribute((const void*)moba_bwd_kv_gated_kernel<D>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kKvDynBytes) == hipSuccess;
+        return ok;
+      }();
+      if (!lds_ok) return hipErrorInvalidConfiguration;
+      const int cpk = (int)cdiv(block, kKvKeys);
+      {
+        KTimer tm("moba_bwd_own", s);
+        launch_timed("moba_bwd_own", moba_bwd_kv_own_kernel<D>,
+                     dim3((unsigned)(nb_all * cpk), (unsigned)hkv, (unsigned)batch), dim3(64 * kBwdNW), 1536, s, q,
+                     k, v, dout, lse, (const float*)delta, dk, dv, seq_len, hq, hkv, q_start, q_len, block, cpk,
+                     scale);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (gated) {
+        KTimer tm("moba_bwd_gated", s);
+        launch_timed("moba_bwd_gated", moba_bwd_kv_gated_kernel<D>,
+                     dim3((unsigned)std::max<int64_t>(1, cdiv(max_tiles, kKvRun)), (unsigned)cpk), dim3(64 * kBwdNW),
+                     kKvDynBytes, s, q, k, v, dout, lse, (const float*)delta, tiles, ntiles, entries, dk, dv, seq_len,
+                     hq, hkv, q_len, block, scale);
+      }
+      return hipGetLastError();
+    }
+  }
   {
     KTimer tm("moba_bwd_own", s);
     launch_timed("moba_bwd_own", moba_bwd_own_kernel<T, D>, dim3((unsigned)(nb_all * cpb), (unsigned)hkv,
