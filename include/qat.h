@@ -243,10 +243,12 @@ int moba_sparse_attn(const qat_moba_params* p, const void* q, const void* k, con
  * for bfloat16 inputs); dout: [batch, q_len, Hq, d] (dtype).
  * dq: [batch, q_len, Hq, d] float32; dk, dv: [batch, seq_len, Hkv, d]
  * float32, overwritten in full (zero for keys no processed row attends).
- * window must be 0 (QAT_EUNSUPPORTED otherwise). dk and dv are summed with
- * float atomics across row tiles, so their last bits may differ from run to
- * run. Workspace: moba_bwd_workspace_size(p) (it holds float32 dq partials,
- * rows x (topk - 1) x d).
+ * window must be 0 (QAT_EUNSUPPORTED otherwise). For bfloat16 inputs the
+ * results are deterministic (every sum in a fixed order); the float32 path
+ * adds dk, dv across row tiles with float atomics, so its last bits may vary
+ * from run to run. Workspace: moba_bwd_workspace_size(p) (it holds float32
+ * partials: rows x (topk - 1) x (2 d + 4) for dq, and per run of 8 dispatch
+ * tiles and 128-key chunk the dk, dv sums).
  */
 int moba_bwd_workspace_size(const qat_moba_params* p, size_t* bytes);
 int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, const void* k, const void* v,

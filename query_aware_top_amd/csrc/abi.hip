@@ -159,6 +159,8 @@ struct MobaLayout {
   float* dec_plse = nullptr;  // [rows, dec_pieces] piece log-sum-exps
   float* delta = nullptr;     // [rows] D = sum_j p_j dp_j of the gradient pass
   float* dq_part = nullptr;   // gradient pass: float32 dq partials per (row, gated slot)
+  int32_t* run_off = nullptr; // gradient pass: runs of dispatch tiles per bucket
+  float* kv_part = nullptr;   // gradient pass: dK, dV sums per (run, key chunk)
   size_t bytes = 0;
 };
 
@@ -216,7 +218,11 @@ MobaLayout moba_layout(const qat_moba_params* p, void* ws, bool bwd = false) {
     L.dec_plse = c.take<float>((size_t)L.nrows * L.dec_pieces);
   }
   L.delta = c.take<float>((size_t)L.nrows);
-  if (bwd) L.dq_part = c.take<float>((size_t)qat::moba_bwd_part_floats(L.nrows, p->topk, p->head_dim) + 1);
+  if (bwd) {
+    L.dq_part = c.take<float>((size_t)qat::moba_bwd_part_floats(L.nrows, p->topk, p->head_dim) + 1);
+    L.run_off = c.take<int32_t>((size_t)L.nbuckets + 1);
+    L.kv_part = c.take<float>((size_t)qat::moba_bwd_kv_part_floats(L.max_tiles, L.nbuckets, p->block, p->head_dim));
+  }
   L.bytes = c.bytes();
   return L;
 }
@@ -613,7 +619,7 @@ QAT_EXPORT int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, con
     if (e != hipSuccess) return hip_status(e, "moba_sparse_attn_bwd: dispatch");
   }
   e = qat::launch_moba_bwd(q, k, v, blk, out, dout, lse, L.tiles, L.ntiles, L.entries, gated ? L.max_tiles : 0,
-                           L.dq_part, dq, L.delta, dk, dv, p->dtype == QAT_BF16, p->batch, p->seq_len, p->n_q_heads,
+                           L.counts, L.nbuckets, L.run_off, L.kv_part, L.dq_part, dq, L.delta, dk, dv, p->dtype == QAT_BF16, p->batch, p->seq_len, p->n_q_heads,
                            p->n_kv_heads, p->head_dim, p->q_start, p->q_len, p->block, p->topk, p->scale, s);
   return hip_status(e, "moba_sparse_attn_bwd");
 }

@@ -59,11 +59,15 @@ hipError_t launch_moba_attn_mfma(const void* q, const void* k, const void* v, co
 // dq [rows, d] and delta [rows] written; dk, dv [batch, seq_len, hkv, d]
 // written in full (own-block kernel) and then added to (gated rows over the
 // dispatch tiles). dq_part: moba_bwd_part_floats floats (bfloat16 path).
+// tile_off: the dispatch's per-bucket tile prefix (nbuckets + 1 entries);
+// run_off: nbuckets + 1 int32 scratch; kv_part: moba_bwd_kv_part_floats.
 int moba_bwd_chunks(int block);
 int64_t moba_bwd_part_floats(int64_t rows, int topk, int64_t d);
+int64_t moba_bwd_kv_part_floats(int64_t max_tiles, int64_t nbuckets, int block, int64_t d);
 hipError_t launch_moba_bwd(const void* q, const void* k, const void* v, const int32_t* blk, const void* out,
                            const void* dout, const float* lse, const int4* tiles, const int32_t* ntiles,
-                           const int2* entries, int64_t max_tiles, float* dq_part, float* dq, float* delta, float* dk,
+                           const int2* entries, int64_t max_tiles, const int32_t* tile_off, int64_t nbuckets,
+                           int32_t* run_off, float* kv_part, float* dq_part, float* dq, float* delta, float* dk,
                            float* dv, bool bf, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d,
                            int64_t q_start, int64_t q_len, int block, int topk, float scale, hipStream_t s);
 

@@ -20,10 +20,13 @@
 //           block's own rows (positions in the block, every query head of
 //           the group, causal); writes dk, dv of its keys (every key of the
 //           sequence is written by exactly one workgroup);
-//   gated   a workgroup per (run of dispatch tiles, 64 keys of the block):
-//           the rows that gated the block, as bucketed by the forward
-//           dispatch; adds into dk, dv with float atomics, once per bucket
-//           the run touches.
+//   gated   the rows that gated the block, as bucketed by the forward
+//           dispatch: bfloat16, a workgroup per (run of up to 8 dispatch
+//           tiles of one bucket, 128 keys) writing its sums to its own slot,
+//           then one pass adding each bucket's slots in run order (no
+//           atomics, deterministic); float32, a workgroup per (run of
+//           dispatch tiles, 64 keys) adding into dk, dv with float atomics
+//           once per bucket the run touches.
 // The key kernels run in vector float32 arithmetic: lane (key i, quarter c) of a wave holds dims
 // [c D/4, (c+1) D/4) of key i's K, V, dK and dV; rows pass through LDS 16 at
 // a time as float32 (quarters padded against bank conflicts).
@@ -629,6 +632,7 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_dq_cur_kernel(
 // ds = p (dp - D), then dV^T += dO^T p and dK^T += Q^T ds with A = dO^T /
 // Q^T by transposing reads of the tiles (as V^T in the forward) and p, ds
 // split into bfloat16 hi + lo.
+int64_t moba_bwd_max_runs(int64_t max_tiles, int64_t nbuckets);
 constexpr int kKvKeys = 32 * kBwdNW;   // keys per workgroup (32 per wave)
 constexpr int kKvRun = 8;              // dispatch tiles per gated workgroup
 constexpr int kKvDynBytes = 6 * 64 * 4 + kKvRun * kRowsPerTileBwd * 8;
@@ -759,7 +763,6 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_own_kernel(
   const bool kvalid = key < c1;
   const int64_t krow = ((bi * seq_len + (kvalid ? key : c0)) * hkv + g) * D;
   KvState<D> st;
-  kv_load<D>(st, k + krow, v + krow);
   const int64_t G = hq / hkv;
   const int64_t t0 = max(c0, q_start), t1 = min(blk1, q_start + q_len);
   const int nrows = t1 > t0 ? (int)((t1 - t0) * G) : 0;
@@ -798,6 +801,7 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_own_kernel(
     return [=](int m) { return m < n && m >= m0; };
   };
   if (nt > 0) issue(sm.k0, sm.v0, 0, 0);
+  kv_load<D>(st, k + krow, v + krow);   // after the first tile's loads, which then overlap it
   for (int rt = 0; rt < nt; rt += 2) {
     fa_wait_loads();
     fa_lds_barrier();
@@ -812,28 +816,65 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_own_kernel(
   if (kvalid) kv_write<D, false>(st, dk + krow, dv + krow, scale);
 }
 
-// Gated rows over the dispatch tiles: grid (runs of kKvRun tiles, key chunks
-// of the block). The run's entries are staged in LDS; a bucket change inside
-// the run adds the finished keys' sums with float atomics and loads the next
-// block's keys.
+// Runs of the gated key kernel: bucket b's dispatch tiles [tile_off[b],
+// tile_off[b + 1]) cut into runs of kKvRun; run_off[b] = runs before bucket b,
+// run_off[nb] = all runs. One workgroup, 1024 buckets per pass (inclusive
+// Hillis-Steele scan in LDS).
+__global__ __launch_bounds__(1024) void moba_bwd_runs_kernel(const int32_t* __restrict__ tile_off, int32_t nb,
+                                                             int32_t* __restrict__ run_off) {
+  __shared__ int32_t s[1024];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int32_t base = 0; base < nb; base += 1024) {
+    const int32_t i = base + threadIdx.x;
+    const int32_t c = i < nb ? (tile_off[i + 1] - tile_off[i] + kKvRun - 1) / kKvRun : 0;
+    s[threadIdx.x] = c;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int32_t a = threadIdx.x >= off ? s[threadIdx.x - off] : 0;
+      __syncthreads();
+      s[threadIdx.x] += a;
+      __syncthreads();
+    }
+    if (i < nb) run_off[i] = carry + s[threadIdx.x] - c;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += s[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) run_off[nb] = carry;
+}
+
+// Gated rows: grid (runs, key chunks of the block); a run is up to kKvRun
+// dispatch tiles of one bucket (sequence, KV head, block). The run's entries
+// are staged in LDS; its sums (dK already scaled) go to its own slot of
+// `part` ([run][chunk][dK, dV][kKvKeys][D]) with plain stores, and
+// moba_bwd_kv_reduce_kernel adds the slots of each bucket in run order.
 template <int D>
 __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_gated_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, const int2* __restrict__ entries,
-    float* __restrict__ dk, float* __restrict__ dv, int64_t seq_len, int64_t hq, int64_t hkv, int64_t q_len,
-    int block, float scale) {
+    const int4* __restrict__ tiles, const int32_t* __restrict__ tile_off, const int32_t* __restrict__ run_off,
+    int32_t nb, const int2* __restrict__ entries, float* __restrict__ part, int64_t seq_len, int64_t hq,
+    int64_t hkv, int64_t q_len, int block, float scale) {
   QAT_FA_SMEM(D, sm);
   extern __shared__ __align__(16) char kv_dyn[];
   float* s_lse = reinterpret_cast<float*>(kv_dyn);   // [2][64]
   float* s_di = s_lse + 128;                          // [2][64]
   int2* s_ent = reinterpret_cast<int2*>(s_di + 256);  // the run's entries (after [2][64] unused ints)
-  const int nt_all = ntiles[0];
-  const int tb = blockIdx.x * kKvRun;
-  if (tb >= nt_all) return;   // uniform
-  const int te = min(nt_all, tb + kKvRun);
+  const int32_t w = blockIdx.x;
+  if (w >= run_off[nb]) return;   // uniform
   const int c = blockIdx.y;
   if (c * kKvKeys >= block) return;   // uniform
+  // the run's bucket: the last one whose first run is not after w
+  int32_t lo = 0, hi = nb - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (run_off[mid] <= w) lo = mid;
+    else hi = mid - 1;
+  }
+  const int tb = tile_off[lo] + (w - run_off[lo]) * kKvRun;
+  const int te = min(tb + kKvRun, tile_off[lo + 1]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kl = c * kKvKeys + wave * 32 + (lane & 31);   // key within the block
   const bool kvalid = kl < block;
@@ -844,34 +885,25 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_gated_kernel(
     for (int i = threadIdx.x; i < nent; i += 64 * kBwdNW) s_ent[i] = entries[e_first + i];
   }
   __syncthreads();
-  const int64_t seq_kv = seq_len * hkv * D;   // elements of one sequence's K
+  const int4 t0d = tiles[tb];
+  const int64_t kv = (int64_t)(uint32_t)t0d.x | ((int64_t)t0d.y << 32);
+  const int64_t bi = kv / (seq_len * hkv * D);
+  const int64_t qo = bi * seq_len * hq, dof = bi * q_len * hq;
+  const bf16* qbase = q + qo * D;
+  const bf16* dbase = dout + dof * D;
   const float sl2 = scale * kLog2e;
   auto issue = [&](bf16* qdst, bf16* ddst, int buf, int ti, int r0) {
     const int4 tl = tiles[ti];
     const int n = min(64, tl.w - r0);
     const int e0 = tl.z - e_first + r0;
-    const int64_t kv = (int64_t)(uint32_t)tl.x | ((int64_t)tl.y << 32);
-    const int64_t bi = kv / seq_kv;
-    const int64_t qo = bi * seq_len * hq, dof = bi * q_len * hq;
-    fa_issue_one<D, kBwdNW>(qdst, q + qo * D, 0, n, [=](int j) { return (int)((s_ent[e0 + j].y - qo) * D); });
-    fa_issue_one<D, kBwdNW>(ddst, dout + dof * D, 0, n,
+    fa_issue_one<D, kBwdNW>(qdst, qbase, 0, n, [=](int j) { return (int)((s_ent[e0 + j].y - qo) * D); });
+    fa_issue_one<D, kBwdNW>(ddst, dbase, 0, n,
                             [=](int j) { return (int)(((int64_t)(s_ent[e0 + j].x >> 4) - dof) * D); });
     if (wave == 0) {
       const int64_t row = s_ent[e0 + min(lane, n - 1)].x >> 4;
       __builtin_amdgcn_global_load_lds((const global_void*)(lse + row), (lds_void*)(s_lse + buf * 64), 4, 0, 0);
       __builtin_amdgcn_global_load_lds((const global_void*)(delta + row), (lds_void*)(s_di + buf * 64), 4, 0, 0);
     }
-  };
-  KvState<D> st;
-  int64_t cur_kv = -1;
-  const int64_t koff = (int64_t)(kvalid ? kl : 0) * hkv * D;
-  auto enter = [&](int ti) {   // the tile's bucket: flush the previous one's sums, load its keys
-    const int4 tl = tiles[ti];
-    const int64_t kv = (int64_t)(uint32_t)tl.x | ((int64_t)tl.y << 32);
-    if (kv == cur_kv) return;
-    if (cur_kv >= 0 && kvalid) kv_write<D, true>(st, dk + cur_kv + koff, dv + cur_kv + koff, scale);
-    cur_kv = kv;
-    kv_load<D>(st, k + kv + koff, v + kv + koff);
   };
   auto advance = [&](int& ti, int& r0) {
     r0 += 64;
@@ -880,13 +912,15 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_gated_kernel(
   auto rows_of = [&](int ti, int r0) { return min(64, tiles[ti].w - r0); };
   int ti = tb, r0 = 0;
   issue(sm.k0, sm.v0, 0, ti, r0);
+  KvState<D> st;
+  const int64_t koff = (int64_t)(kvalid ? kl : 0) * hkv * D;
+  kv_load<D>(st, k + kv + koff, v + kv + koff);   // after the first tile's loads, which then overlap it
   for (;;) {
     fa_wait_loads();
     fa_lds_barrier();
     int tn = ti, rn = r0;
     advance(tn, rn);
     if (tn < te) issue(sm.k1, sm.v1, 1, tn, rn);
-    enter(ti);
     {
       const int n = rows_of(ti, r0);
       kv_tile<D>(st, sm.k0, sm.v0, s_lse, s_di, sl2, [=](int m) { return m < n; });
@@ -898,7 +932,6 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_gated_kernel(
     fa_lds_barrier();
     advance(tn, rn);
     if (tn < te) issue(sm.k0, sm.v0, 0, tn, rn);
-    enter(ti);
     {
       const int n = rows_of(ti, r0);
       kv_tile<D>(st, sm.k1, sm.v1, s_lse + 64, s_di + 64, sl2, [=](int m) { return m < n; });
@@ -908,7 +941,42 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_gated_kernel(
     if (ti >= te) break;
   }
   fa_wait_loads();
-  if (kvalid) kv_write<D, true>(st, dk + cur_kv + koff, dv + cur_kv + koff, scale);
+  if (kvalid) {
+    float* slot = part + ((int64_t)w * gridDim.y + c) * 2 * kKvKeys * D + (wave * 32 + (lane & 31)) * D;
+    kv_write<D, false>(st, slot, slot + kKvKeys * D, scale);
+  }
+}
+
+// dK, dV of bucket b's keys += the sums of its runs, in run order: grid
+// (buckets, key chunks); a thread adds float4 pieces.
+template <int D>
+__global__ __launch_bounds__(256) void moba_bwd_kv_reduce_kernel(const float* __restrict__ part,
+                                                                 const int32_t* __restrict__ run_off,
+                                                                 const int32_t* __restrict__ tile_off,
+                                                                 const int4* __restrict__ tiles,
+                                                                 float* __restrict__ dk, float* __restrict__ dv,
+                                                                 int64_t hkv, int block) {
+  const int32_t b = blockIdx.x;
+  const int32_t r0 = run_off[b], r1 = run_off[b + 1];
+  if (r0 == r1) return;   // no gated rows in this bucket
+  const int c = blockIdx.y;
+  const int nk = min(kKvKeys, block - c * kKvKeys);
+  if (nk <= 0) return;
+  const int4 td = tiles[tile_off[b]];
+  const int64_t kv = (int64_t)(uint32_t)td.x | ((int64_t)td.y << 32);
+  constexpr int D4 = D / 4;
+  const int ncpk = gridDim.y;
+  for (int e = threadIdx.x; e < 2 * nk * D4; e += 256) {
+    const int tsr = e / (nk * D4), rem = e % (nk * D4), j = rem / D4, d4 = rem % D4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int32_t w = r0; w < r1; ++w) {
+      const f32x4 x = *(const f32x4*)(part + (((int64_t)w * ncpk + c) * 2 + tsr) * kKvKeys * D + j * D + 4 * d4);
+      acc += x;
+    }
+    float* dst = (tsr == 0 ? dk : dv) + kv + (int64_t)(c * kKvKeys + j) * hkv * D + 4 * d4;
+    f32x4 y = *(const f32x4*)dst;
+    *(f32x4*)dst = y + acc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -917,7 +985,9 @@ int moba_bwd_chunks(int block) { return (int)cdiv(block, kBwdKeys); }
 template <typename T, int D>
 static hipError_t launch_moba_bwd_d(const T* q, const T* k, const T* v, const int32_t* blk, const T* out,
                                     const T* dout, const float* lse, const int4* tiles, const int32_t* ntiles,
-                                    const int2* entries, int64_t max_tiles, float* dq_part, float* dq, float* delta,
+                                    const int2* entries, int64_t max_tiles, const int32_t* tile_off,
+                                    int64_t nbuckets, int32_t* run_off, float* kv_part, float* dq_part, float* dq,
+                                    float* delta,
                                     float* dk, float* dv, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
                                     int64_t q_start, int64_t q_len, int block, int topk, float scale,
                                     hipStream_t s) {
@@ -976,10 +1046,17 @@ static hipError_t launch_moba_bwd_d(const T* q, const T* k, const T* v, const in
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (gated) {
         KTimer tm("moba_bwd_gated", s);
+        hipLaunchKernelGGL(moba_bwd_runs_kernel, dim3(1), dim3(1024), 0, s, tile_off, (int32_t)nbuckets, run_off);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         launch_timed("moba_bwd_gated", moba_bwd_kv_gated_kernel<D>,
-                     dim3((unsigned)std::max<int64_t>(1, cdiv(max_tiles, kKvRun)), (unsigned)cpk), dim3(64 * kBwdNW),
-                     kKvDynBytes, s, q, k, v, dout, lse, (const float*)delta, tiles, ntiles, entries, dk, dv, seq_len,
-                     hq, hkv, q_len, block, scale);
+                     dim3((unsigned)moba_bwd_max_runs(max_tiles, nbuckets), (unsigned)cpk), dim3(64 * kBwdNW),
+                     kKvDynBytes, s, q, k, v, dout, lse, (const float*)delta, tiles, (const int32_t*)tile_off,
+                     (const int32_t*)run_off, (int32_t)nbuckets, entries, kv_part, seq_len, hq, hkv, q_len, block,
+                     scale);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(moba_bwd_kv_reduce_kernel<D>, dim3((unsigned)nbuckets, (unsigned)cpk), dim3(256), 0, s,
+                           (const float*)kv_part, (const int32_t*)run_off, (const int32_t*)tile_off, tiles, dk, dv,
+                           hkv, block);
       }
       return hipGetLastError();
     }
@@ -1001,16 +1078,22 @@ static hipError_t launch_moba_bwd_d(const T* q, const T* k, const T* v, const in
 }
 
 int64_t moba_bwd_part_floats(int64_t rows, int topk, int64_t d) { return rows * (topk - 1) * (2 * d + 4); }
+int64_t moba_bwd_max_runs(int64_t max_tiles, int64_t nbuckets) { return cdiv(max_tiles, kKvRun) + nbuckets; }
+int64_t moba_bwd_kv_part_floats(int64_t max_tiles, int64_t nbuckets, int block, int64_t d) {
+  return moba_bwd_max_runs(max_tiles, nbuckets) * cdiv(block, kKvKeys) * 2 * kKvKeys * d;
+}
 
 hipError_t launch_moba_bwd(const void* q, const void* k, const void* v, const int32_t* blk, const void* out,
                            const void* dout, const float* lse, const int4* tiles, const int32_t* ntiles,
-                           const int2* entries, int64_t max_tiles, float* dq_part, float* dq, float* delta, float* dk,
+                           const int2* entries, int64_t max_tiles, const int32_t* tile_off, int64_t nbuckets,
+                           int32_t* run_off, float* kv_part, float* dq_part, float* dq, float* delta, float* dk,
                            float* dv, bool bf, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d,
                            int64_t q_start, int64_t q_len, int block, int topk, float scale, hipStream_t s) {
   if (batch * q_len * hq == 0) return hipSuccess;
 #define QAT_BWD(T_, D_)                                                                                     \
   return launch_moba_bwd_d<T_, D_>((const T_*)q, (const T_*)k, (const T_*)v, blk, (const T_*)out,          \
-                                   (const T_*)dout, lse, tiles, ntiles, entries, max_tiles, dq_part, dq, delta, \
+                                   (const T_*)dout, lse, tiles, ntiles, entries, max_tiles, tile_off, nbuckets, \
+                                   run_off, kv_part, dq_part, dq, delta,                                        \
                                    dk, dv, batch, seq_len, hq, hkv, q_start, q_len, block, topk, scale, s)
   if (bf) {
     if (d == 64) QAT_BWD(bf16, 64);
