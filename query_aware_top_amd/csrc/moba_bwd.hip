@@ -673,14 +673,22 @@ __device__ __forceinline__ void kv_tile(KvState<D>& st, const bf16* __restrict__
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     u32x4 pph[2], ppl[2], dsh[2], dsl[2];
+    // the half's 16 rows of this lane are 4 runs of 4 consecutive rows
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      l4[gi] = *(const f32x4*)(lse_t + sb * 32 + gi * 8 + h * 4);
+      d4[gi] = *(const f32x4*)(di_t + sb * 32 + gi * 8 + h * 4);
+    }
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       float p2[2], ds2[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int m = sb * 32 + ((i + u) >> 2) * 8 + h * 4 + ((i + u) & 3);
-        p2[u] = row_ok(m) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i + u], sl2, -lse_t[m] * kLog2e)) : 0.f;
-        ds2[u] = p2[u] * (dp[sb][i + u] - di_t[m]);
+        const float l2 = l4[(i + u) >> 2][(i + u) & 3] * kLog2e, di = d4[(i + u) >> 2][(i + u) & 3];
+        p2[u] = row_ok(m) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i + u], sl2, -l2)) : 0.f;
+        ds2[u] = p2[u] * (dp[sb][i + u] - di);
       }
       const int kk = i >> 3, w = (i & 7) >> 1;
       const uint2 a2 = split_pack(p2[0], p2[1]), b2 = split_pack(ds2[0], ds2[1]);
