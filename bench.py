@@ -50,10 +50,10 @@ STAGE_SOURCES = {
     "moba_decode_select": ["moba_select.hip"],
     "moba_decode_attn": ["attn_generic.hip"],
     "moba_decode_combine": ["attn_generic.hip"],
-    "moba_bwd_dq": ["moba_bwd.hip", "attn_core.h"],
-    "moba_bwd_dq_past": ["moba_bwd.hip", "attn_core.h"],
-    "moba_bwd_own": ["moba_bwd.hip"],
-    "moba_bwd_gated": ["moba_bwd.hip"],
+    "moba_bwd_dq": ["moba_bwd.hip", "attn_core.h", "attn_bwd.h"],
+    "moba_bwd_dq_past": ["moba_bwd.hip", "attn_core.h", "attn_bwd.h"],
+    "moba_bwd_own": ["moba_bwd.hip", "attn_core.h", "attn_bwd.h"],
+    "moba_bwd_gated": ["moba_bwd.hip", "attn_core.h", "attn_bwd.h"],
     "esa_compress*": ["compress.hip"],
     "esa_scores": ["esa_select.hip"],
     "esa_topk": ["esa_select.hip"],
@@ -315,8 +315,8 @@ class MobaBwdWorkload(Workload):
         self.dominant, self.bound = "moba_bwd_gated", "mfma"
 
     def step(self):
-        self.qat.moba_sparse_attn_bwd(self.p, self.q, self.k, self.v, self.blk, self.out, self.do, self.lse,
-                                      dq=self.dq, dk=self.dk, dv=self.dv, ws=self.ws)
+        self.qat.moba_sparse_attn_bwd(self.p, self.q, self.k, self.v, self.blk, self.do, self.lse, dq=self.dq,
+                                      dk=self.dk, dv=self.dv, ws=self.ws)
 
     def value(self, sec):
         return self.n / sec

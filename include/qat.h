@@ -238,9 +238,10 @@ int moba_sparse_attn(const qat_moba_params* p, const void* q, const void* k, con
  *   dq = scale sum_j p_j (dp_j - D) k_j,
  *   dk_j += scale p_j (dp_j - D) q,  dv_j += p_j dO  (GQA: the query heads of
  *   a KV head add into it).
- * q, k, v, blk as given to moba_sparse_attn (q the whole sequence); out and
- * lse: its outputs for the same rows (both required; D is taken as dO . out
- * for bfloat16 inputs); dout: [batch, q_len, Hq, d] (dtype).
+ * q, k, v, blk as given to moba_sparse_attn (q the whole sequence); lse: its
+ * output for the same rows (required; D is formed from the probabilities in
+ * float32, not from a rounded forward output); dout: [batch, q_len, Hq, d]
+ * (dtype).
  * dq: [batch, q_len, Hq, d] float32; dk, dv: [batch, seq_len, Hkv, d]
  * float32, overwritten in full (zero for keys no processed row attends).
  * window must be 0 (QAT_EUNSUPPORTED otherwise). For bfloat16 inputs the
@@ -252,8 +253,8 @@ int moba_sparse_attn(const qat_moba_params* p, const void* q, const void* k, con
  */
 int moba_bwd_workspace_size(const qat_moba_params* p, size_t* bytes);
 int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, const void* k, const void* v,
-                         const int32_t* blk, const void* out, const void* dout, const float* lse, float* dq,
-                         float* dk, float* dv, void* ws, size_t ws_bytes, void* stream);
+                         const int32_t* blk, const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Decode steps ([MoBA] section 3: gating and attention are defined per query

@@ -81,8 +81,8 @@ def lib():
         L.moba_decode_select.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp]
         L.moba_decode_attn.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moba_bwd_workspace_size.argtypes = [ctypes.POINTER(MobaParams), ctypes.POINTER(sz)]
-        L.moba_sparse_attn_bwd.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                           sz, vp]
+        L.moba_sparse_attn_bwd.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                           vp]
         for name in EXPORTED_SYMBOLS:
             getattr(L, name).restype = ctypes.c_int if name != "qat_last_error" else ctypes.c_char_p
         _lib = L
@@ -334,12 +334,12 @@ def moba_bwd_workspace_size(p: MobaParams) -> int:
     return n.value
 
 
-def moba_sparse_attn_bwd(p: MobaParams, q, k, v, blk, out, dout, lse, dq=None, dk=None, dv=None, ws=None):
+def moba_sparse_attn_bwd(p: MobaParams, q, k, v, blk, dout, lse, dq=None, dk=None, dv=None, ws=None):
     """Gradients of moba_sparse_attn for the same rows with the gating held
-    fixed (out, lse: that call's outputs). Returns (dq [batch, q_len, Hq, d],
+    fixed (lse: that call's output). Returns (dq [batch, q_len, Hq, d],
     dk, dv [batch, seq_len, Hkv, d]), all float32."""
     dt = torch.bfloat16 if p.dtype == QAT_BF16 else torch.float32
-    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, name, dt)
     _need(blk, "blk", torch.int32)
     _need(lse, "lse", torch.float32)
@@ -353,6 +353,5 @@ def moba_sparse_attn_bwd(p: MobaParams, q, k, v, blk, out, dout, lse, dq=None, d
     for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _need(t, name, torch.float32)
     ws = _workspace(moba_bwd_workspace_size(p), dev, ws)
-    _check(lib().moba_sparse_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(blk), _ptr(out), _ptr(dout),
-                                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
+    _check(lib().moba_sparse_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(blk), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
     return dq, dk, dv

@@ -598,12 +598,12 @@ QAT_EXPORT int moba_bwd_workspace_size(const qat_moba_params* p, size_t* bytes) 
 }
 
 QAT_EXPORT int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, const void* k, const void* v,
-                                    const int32_t* blk, const void* out, const void* dout, const float* lse,
-                                    float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+                                    const int32_t* blk, const void* dout, const float* lse, float* dq, float* dk,
+                                    float* dv, void* ws, size_t ws_bytes, void* stream) {
   int rc = moba_check(p);
   if (rc) return rc;
-  if (!q || !k || !v || !blk || !out || !dout || !lse || !dq || !dk || !dv)
-    return fail(QAT_EINVAL, "q, k, v, blk, out, dout, lse, dq, dk, dv must be non-NULL");
+  if (!q || !k || !v || !blk || !dout || !lse || !dq || !dk || !dv)
+    return fail(QAT_EINVAL, "q, k, v, blk, dout, lse, dq, dk, dv must be non-NULL");
   if (p->window != 0) return fail(QAT_EUNSUPPORTED, "gradients with an extra local window are not implemented");
   MobaLayout L = moba_layout(p, nullptr, true);
   if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
@@ -618,7 +618,7 @@ QAT_EXPORT int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, con
                                   L.tiles, L.ntiles, s);
     if (e != hipSuccess) return hip_status(e, "moba_sparse_attn_bwd: dispatch");
   }
-  e = qat::launch_moba_bwd(q, k, v, blk, out, dout, lse, L.tiles, L.ntiles, L.entries, gated ? L.max_tiles : 0,
+  e = qat::launch_moba_bwd(q, k, v, blk, dout, lse, L.tiles, L.ntiles, L.entries, gated ? L.max_tiles : 0,
                            L.counts, L.nbuckets, L.run_off, L.kv_part, L.dq_part, dq, L.delta, dk, dv, p->dtype == QAT_BF16, p->batch, p->seq_len, p->n_q_heads,
                            p->n_kv_heads, p->head_dim, p->q_start, p->q_len, p->block, p->topk, p->scale, s);
   return hip_status(e, "moba_sparse_attn_bwd");

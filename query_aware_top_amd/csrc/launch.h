@@ -64,7 +64,7 @@ hipError_t launch_moba_attn_mfma(const void* q, const void* k, const void* v, co
 int moba_bwd_chunks(int block);
 int64_t moba_bwd_part_floats(int64_t rows, int topk, int64_t d);
 int64_t moba_bwd_kv_part_floats(int64_t max_tiles, int64_t nbuckets, int block, int64_t d);
-hipError_t launch_moba_bwd(const void* q, const void* k, const void* v, const int32_t* blk, const void* out,
+hipError_t launch_moba_bwd(const void* q, const void* k, const void* v, const int32_t* blk,
                            const void* dout, const float* lse, const int4* tiles, const int32_t* ntiles,
                            const int2* entries, int64_t max_tiles, const int32_t* tile_off, int64_t nbuckets,
                            int32_t* run_off, float* kv_part, float* dq_part, float* dq, float* delta, float* dk,

@@ -22,7 +22,7 @@ def forward_backward(q, k, v, block, topk, dtype, q_start=0, q_len=None, seed=0)
     blk = qat.moba_block_select(p, q, k)
     out, lse = qat.moba_sparse_attn(p, q, k, v, blk)
     do = synth.normal(seed, 7, (p.batch, p.q_len, p.n_q_heads, p.head_dim), dtype, DEV)
-    dq, dk, dv = qat.moba_sparse_attn_bwd(p, q, k, v, blk, out, do, lse)
+    dq, dk, dv = qat.moba_sparse_attn_bwd(p, q, k, v, blk, do, lse)
     torch.cuda.synchronize()
     return p, blk, do, dq, dk, dv
 
