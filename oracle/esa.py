@@ -52,7 +52,7 @@ parity unpinned, since the pages do not carry those formulas.
 """
 import numpy as np
 
-from .attention import attend_heads
+from .attention import attend_grad, attend_heads
 from .numerics import round_to_bf16
 
 
@@ -169,3 +169,27 @@ def attend(q, K, V, sel, c0, n_init, window, scale, rows=None):
                                     np.asarray(K[idx], np.float64),
                                     np.asarray(V[idx], np.float64), scale)
     return o, lse
+
+
+def backward(q, K, V, sel, c0, n_init, window, scale, do, rows=None, heads=None):
+    """Gradients of step 8 with the selection held fixed (a discrete top-k):
+    q [m, H, d] chunk rows, K/V [T, H, d], do [len(rows), H, d]. Returns
+    dq [len(rows), H, d] and dK, dV [T, H, d] with every listed row's
+    contribution added (heads: the heads to compute, default all; the others
+    stay zero)."""
+    m, H, d = q.shape
+    if rows is None:
+        rows = list(range(m))
+    if heads is None:
+        heads = list(range(H))
+    dq = np.zeros((len(rows), H, d))
+    dK = np.zeros(K.shape)
+    dV = np.zeros(V.shape)
+    for r, i in enumerate(rows):
+        idx = key_list(sel, c0, n_init, window, c0 + i)
+        for h in heads:
+            dq[r, h], gk, gv = attend_grad(q[i, h], np.asarray(K[idx, h], np.float64),
+                                           np.asarray(V[idx, h], np.float64), scale, do[r, h])
+            dK[idx, h] += gk
+            dV[idx, h] += gv
+    return dq, dK, dV

@@ -292,6 +292,61 @@ def test_moba_backward_matches_torch_autograd_on_masked_dense():
     assert np.allclose(dv, Vt.grad.numpy(), atol=1e-12)
 
 
+def test_esa_backward_matches_finite_differences():
+    """ESA attention with the selection fixed: gradients equal central
+    differences of the oracle forward (tiny chunk, all four parts present)."""
+    r = rng(52)
+    T, m, H, d = 30, 4, 2, 3
+    q = r.standard_normal((m, H, d))
+    K, V = r.standard_normal((T, H, d)), r.standard_normal((T, H, d))
+    c0, n_init, W, scale = T - m, 3, 5, 0.7
+    _, M, _ = oesa.partition(c0, n_init, W)
+    sel = np.sort(r.choice(M, 6, replace=False))
+    do = r.standard_normal((m, H, d))
+
+    def loss(q_, K_, V_):
+        o, _ = oesa.attend(q_, K_, V_, sel, c0, n_init, W, scale)
+        return float(np.sum(o * do))
+
+    dq, dK, dV = oesa.backward(q, K, V, sel, c0, n_init, W, scale, do)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", K, dK), ("v", V, dV)):
+        num = np.zeros_like(x)
+        for i in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[i] += eps
+            xm[i] -= eps
+            args_p = {"q": (xp, K, V), "k": (q, xp, V), "v": (q, K, xp)}[name]
+            args_m = {"q": (xm, K, V), "k": (q, xm, V), "v": (q, K, xm)}[name]
+            num[i] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert np.allclose(g, num, rtol=0, atol=2e-8), (name, np.abs(g - num).max())
+    # keys outside the four parts get no gradient
+    outside = np.setdiff1d(np.arange(T), np.concatenate([np.arange(n_init), sel, np.arange(c0 - W, T)]))
+    assert np.all(dK[outside] == 0) and np.all(dV[outside] == 0)
+
+
+def test_esa_backward_matches_torch_autograd_on_masked_dense():
+    r = rng(53)
+    T, m, H, d = 60, 8, 3, 4
+    q = r.standard_normal((m, H, d))
+    K, V = r.standard_normal((T, H, d)), r.standard_normal((T, H, d))
+    c0, n_init, W, scale = T - m, 4, 10, 0.5
+    _, M, _ = oesa.partition(c0, n_init, W)
+    sel = np.sort(r.choice(M, 12, replace=False))
+    do = r.standard_normal((m, H, d))
+    dq, dK, dV = oesa.backward(q, K, V, sel, c0, n_init, W, scale, do)
+    mask = np.full((m, T), -np.inf)
+    for i in range(m):
+        mask[i, oesa.key_list(sel, c0, n_init, W, c0 + i)] = 0.0
+    Q, Kt, Vt = (torch.tensor(x, requires_grad=True) for x in (q, K, V))
+    s = torch.einsum("ihd,jhd->hij", Q, Kt) * scale + torch.tensor(mask)[None]
+    o = torch.einsum("hij,jhd->ihd", torch.softmax(s, dim=-1), Vt)
+    o.backward(torch.tensor(do))
+    assert np.allclose(dq, Q.grad.numpy(), atol=1e-12)
+    assert np.allclose(dK, Kt.grad.numpy(), atol=1e-12)
+    assert np.allclose(dV, Vt.grad.numpy(), atol=1e-12)
+
+
 def test_moba_is_causal():
     r = rng(9)
     N, H, d, B = 32, 2, 8, 4
