@@ -61,7 +61,8 @@ int qat_abi_version(void);
  * (names: "moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn",
  * "moba_current_attn", "moba_generic_attn", "moba_decode_select",
  * "moba_decode_attn", "moba_decode_combine", "moba_bwd_delta", "moba_bwd_dq_past",
- * "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated", "esa_compress", "esa_scores",
+ * "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated", "esa_bwd_dq", "esa_bwd_kv",
+ * "esa_compress", "esa_scores",
  * "esa_decode_scan", "esa_topk", "esa_prefill_attn", "esa_decode_attn",
  * "esa_generic_attn"). The events are timing-only (created without the
  * system-scope fence on completion, so recording them does not slow the
@@ -173,6 +174,28 @@ int esa_select(const qat_esa_params* p, const void* q, const void* Wq, const flo
 int esa_sparse_attn(const qat_esa_params* p, const void* q, const void* k_cache,
                     const void* v_cache, const int32_t* sel, const int32_t* n_sel,
                     void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Gradients of esa_sparse_attn with the selection held fixed (the top-k is
+ * a discrete choice; [ESA] learns the compression map offline, so no
+ * gradient reaches it): for each chunk query i and head h with key list
+ * I u S u L u [c0, c0 + i] ([ESA] four-part split),
+ *   p_j = exp(scale q.k_j - lse),  dp_j = dO.v_j,  D = sum_j p_j dp_j,
+ *   dq = scale sum_j p_j (dp_j - D) k_j,
+ *   dk_j += scale p_j (dp_j - D) q,  dv_j += p_j dO.
+ * q, k_cache, v_cache, sel, n_sel as given to esa_sparse_attn; lse: its
+ * output for the same queries (required); dout: [batch, chunk_len, H, d].
+ * bfloat16 inputs only (QAT_EUNSUPPORTED otherwise), and one sequence's
+ * cache must hold fewer than 2^31 elements.
+ * dq: [batch, chunk_len, H, d] float32, written. dk, dv: [batch, ctx_len, H,
+ * d] float32, ADDED to at the attended positions (gradient accumulation
+ * over chunks; zero them before the first chunk); other rows untouched.
+ * Deterministic. Workspace: esa_bwd_workspace_size(p).
+ */
+int esa_bwd_workspace_size(const qat_esa_params* p, size_t* bytes);
+int esa_sparse_attn_bwd(const qat_esa_params* p, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* sel, const int32_t* n_sel, const void* dout, const float* lse, float* dq,
+                        float* dk, float* dv, void* ws, size_t ws_bytes, void* stream);
 
 /* ======================================================================
  * MoBA -- block-level selection by mean-pooled keys   [MoBA]

@@ -20,6 +20,8 @@ from ._binding import (  # noqa: F401
     esa_compress,
     esa_select,
     esa_sparse_attn,
+    esa_bwd_workspace_size,
+    esa_sparse_attn_bwd,
     moba_workspace_size,
     moba_block_select,
     moba_sparse_attn,

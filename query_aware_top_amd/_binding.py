@@ -17,6 +17,7 @@ EXPORTED_SYMBOLS = (
     "qat_last_error", "qat_abi_version", "qat_timing_enable", "qat_timing_select", "qat_timing_reset",
     "qat_timing_query",
     "esa_workspace_size", "esa_compress_workspace_size", "esa_compress", "esa_select", "esa_sparse_attn",
+    "esa_bwd_workspace_size", "esa_sparse_attn_bwd",
     "moba_workspace_size", "moba_block_select", "moba_sparse_attn", "moba_block_means", "moba_decode_select",
     "moba_decode_attn", "moba_bwd_workspace_size", "moba_sparse_attn_bwd",
 )
@@ -70,6 +71,9 @@ def lib():
                                    vp, sz, vp]
         L.esa_select.argtypes = [ctypes.POINTER(EsaParams), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.esa_sparse_attn.argtypes = [ctypes.POINTER(EsaParams), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.esa_bwd_workspace_size.argtypes = [ctypes.POINTER(EsaParams), ctypes.POINTER(sz)]
+        L.esa_sparse_attn_bwd.argtypes = [ctypes.POINTER(EsaParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                          vp]
         L.moba_workspace_size.argtypes = [ctypes.POINTER(MobaParams), ctypes.POINTER(sz)]
         L.moba_block_select.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, sz, vp]
         L.qat_timing_enable.argtypes = [ctypes.c_int]
@@ -237,6 +241,38 @@ def esa_sparse_attn(p: EsaParams, q, k_cache, v_cache, sel, n_sel, out=None, lse
     _check(lib().esa_sparse_attn(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sel), _ptr(n_sel),
                                  _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
     return out, lse
+
+
+def esa_bwd_workspace_size(p: EsaParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().esa_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def esa_sparse_attn_bwd(p: EsaParams, q, k_cache, v_cache, sel, n_sel, dout, lse, dq=None, dk=None, dv=None,
+                        ws=None):
+    """Gradients of esa_sparse_attn with the selection held fixed (lse: that
+    call's output). dk, dv [batch, ctx_len, H, d] float32 are ADDED to
+    (allocated zeroed when None). Returns (dq [batch, chunk_len, H, d], dk, dv)."""
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (dout, "dout")):
+        _need(t, name, torch.bfloat16)
+    _need(sel, "sel", torch.int32)
+    _need(n_sel, "n_sel", torch.int32)
+    _need(lse, "lse", torch.float32)
+    dev = q.device
+    if dq is None:
+        dq = torch.empty(p.batch, p.chunk_len, p.n_heads, p.head_dim, dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.zeros(p.batch, p.ctx_len, p.n_heads, p.head_dim, dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.zeros(p.batch, p.ctx_len, p.n_heads, p.head_dim, dtype=torch.float32, device=dev)
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, name, torch.float32)
+    ws = _workspace(esa_bwd_workspace_size(p), dev, ws)
+    _check(lib().esa_sparse_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sel), _ptr(n_sel),
+                                     _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                                     _stream()))
+    return dq, dk, dv
 
 
 # ------------------------------------------------------------------ MoBA

@@ -464,6 +464,40 @@ QAT_EXPORT int esa_sparse_attn(const qat_esa_params* p, const void* q, const voi
   return hip_status(e, "esa_sparse_attn");
 }
 
+QAT_EXPORT int esa_bwd_workspace_size(const qat_esa_params* p, size_t* bytes) {
+  int rc = esa_check(p);
+  if (rc) return rc;
+  if (!bytes) return fail(QAT_EINVAL, "bytes is NULL");
+  qat::Carver c(nullptr);
+  c.take<int32_t>((size_t)p->batch * qat::esa_keylist_len(p->n_init, p->topk, p->window, p->chunk_len));
+  c.take<float>((size_t)p->batch * p->chunk_len * p->n_heads);
+  *bytes = c.bytes();
+  return ok();
+}
+
+QAT_EXPORT int esa_sparse_attn_bwd(const qat_esa_params* p, const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* sel, const int32_t* n_sel, const void* dout, const float* lse,
+                                   float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+  int rc = esa_check(p);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !sel || !n_sel || !dout || !lse || !dq || !dk || !dv)
+    return fail(QAT_EINVAL, "q, k_cache, v_cache, sel, n_sel, dout, lse, dq, dk, dv must be non-NULL");
+  if (p->dtype != QAT_BF16) return fail(QAT_EUNSUPPORTED, "ESA gradients take bfloat16 inputs");
+  if (p->ctx_len * p->n_heads * p->head_dim >= (1ll << 31))
+    return fail(QAT_EUNSUPPORTED, "one sequence's cache must hold fewer than 2^31 elements");
+  size_t need = 0;
+  if ((rc = esa_bwd_workspace_size(p, &need))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  qat::Carver c(ws);
+  int32_t* keylist = c.take<int32_t>((size_t)p->batch * qat::esa_keylist_len(p->n_init, p->topk, p->window,
+                                                                             p->chunk_len));
+  float* delta = c.take<float>((size_t)p->batch * p->chunk_len * p->n_heads);
+  hipError_t e = qat::launch_esa_bwd(q, k_cache, v_cache, sel, n_sel, dout, lse, keylist, dq, delta, dk, dv, p->batch,
+                                     p->n_heads, p->head_dim, p->ctx_len, p->chunk_start, p->chunk_len, p->n_init,
+                                     p->window, p->topk, p->scale, (hipStream_t)stream);
+  return hip_status(e, "esa_sparse_attn_bwd");
+}
+
 // ---------------------------------------------------------------- MoBA
 QAT_EXPORT int moba_workspace_size(const qat_moba_params* p, size_t* bytes) {
   int rc = moba_check(p);

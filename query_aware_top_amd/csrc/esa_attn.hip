@@ -312,6 +312,14 @@ int64_t esa_keylist_len(int64_t n_init, int64_t topk, int64_t window, int64_t m)
   return n_init + topk + window + m;
 }
 
+hipError_t launch_esa_keylist(const int32_t* sel, const int32_t* n_sel, int32_t* keylist, int64_t batch, int64_t c0,
+                              int64_t m, int64_t n_init, int64_t window, int topk, hipStream_t s) {
+  const int64_t kls = esa_keylist_len(n_init, topk, window, m);
+  hipLaunchKernelGGL(esa_keylist_kernel, dim3((unsigned)cdiv(kls, 256), (unsigned)batch), dim3(256), 0, s, sel,
+                     n_sel, keylist, kls, topk, c0, m, n_init, window);
+  return hipGetLastError();
+}
+
 hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, const int32_t* sel,
                                    const int32_t* n_sel, int32_t* keylist, void* out, float* lse, int64_t batch,
                                    int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,

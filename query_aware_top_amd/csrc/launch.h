@@ -123,6 +123,19 @@ hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, 
                                    const int32_t* n_sel, int32_t* keylist, void* out, float* lse, int64_t batch,
                                    int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
                                    int64_t window, int topk, float scale, hipStream_t s);
+// keylist [batch, esa_keylist_len]: per sequence the gathered key positions
+// (initial, selected, local) then the chunk's positions
+hipError_t launch_esa_keylist(const int32_t* sel, const int32_t* n_sel, int32_t* keylist, int64_t batch, int64_t c0,
+                              int64_t m, int64_t n_init, int64_t window, int topk, hipStream_t s);
+
+// ---- ESA gradients (esa_bwd.hip), bfloat16 --------------------------------
+// dq [batch, m, H, D] and delta [batch, m, H] written; dk, dv [batch,
+// ctx_len, H, D] added to at the key lists' positions.
+hipError_t launch_esa_bwd(const void* q, const void* k, const void* v, const int32_t* sel, const int32_t* n_sel,
+                          const void* dout, const float* lse, int32_t* keylist, float* dq, float* delta, float* dk,
+                          float* dv, int64_t batch, int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t m,
+                          int64_t n_init, int64_t window, int topk, float scale, hipStream_t s);
+
 hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, const int32_t* sel,
                                   const int32_t* n_sel, float* po, float* pm, float* pl, void* out, float* lse,
                                   int64_t batch, int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t n_init,
