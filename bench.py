@@ -11,7 +11,8 @@ Prints one JSON line. Default workload: MoBA prefill at the 8B-style GQA
 shape (32 query / 8 KV heads x 128, N = 32768, block 512, top-k 3 with the
 forced block, 8 planted key blocks), reported as query tokens per second.
 Other workloads (--workload): moba_fp32_4k, esa_prefill_64k,
-esa_decode_128k, moba_long_512k, moba_decode_128k, moba_bwd_32k (gradients), and esa_prefill_64k_votes /
+esa_decode_128k, moba_long_512k, moba_decode_128k, moba_bwd_32k and esa_bwd_64k (gradients), and
+esa_prefill_64k_votes /
 esa_decode_128k_votes (the softmax-vote reading of ESA's score correction).
 """
 from __future__ import annotations
@@ -54,6 +55,8 @@ STAGE_SOURCES = {
     "moba_bwd_dq_past": ["moba_bwd.hip", "attn_core.h", "attn_bwd.h"],
     "moba_bwd_own": ["moba_bwd.hip", "attn_core.h", "attn_bwd.h"],
     "moba_bwd_gated": ["moba_bwd.hip", "attn_core.h", "attn_bwd.h"],
+    "esa_bwd_dq": ["esa_bwd.hip", "attn_core.h", "attn_bwd.h"],
+    "esa_bwd_kv": ["esa_bwd.hip", "attn_core.h", "attn_bwd.h"],
     "esa_compress*": ["compress.hip"],
     "esa_scores": ["esa_select.hip"],
     "esa_topk": ["esa_select.hip"],
@@ -361,6 +364,83 @@ class MobaBwdWorkload(Workload):
                           f"{el:.1f} s"}
 
 
+class EsaBwdWorkload(Workload):
+    """Gradients of the ESA chunk attention (selection held fixed) at the 64k
+    prefill shape: compression, selection and attention run once before
+    timing; a step is the backward call (dq + D, then dK/dV of the key
+    list) into zeroed gradient buffers."""
+
+    def __init__(self, name, seed, T, m, H, d, d_c, n_init, W, topk, radius, clip):
+        import query_aware_top_amd as qat
+        import synth
+        self.qat = qat
+        self.name = name
+        self.unit = "query-tokens/s"
+        self.dtype = "bf16"
+        self.T, self.m, self.H, self.d, self.d_c = T, m, H, d, d_c
+        self.c0, self.n_init, self.W, self.topk = T - m, n_init, W, topk
+        _, self.k, self.v, _ = synth.esa_inputs(seed, 1, T, 1, H, d, torch.bfloat16, "cuda")
+        self.q = synth.normal(seed, synth.gen.TID_Q, (1, m, H, d), torch.bfloat16, "cuda", start=1 << 40)
+        Wq = synth.compression_weights(seed, d_c, H * d, synth.gen.TID_W, torch.bfloat16, "cuda")
+        self.p = qat.esa_params(batch=1, n_heads=H, head_dim=d, d_c=d_c, ctx_len=T, chunk_start=self.c0,
+                                chunk_len=m, n_init=n_init, window=W, topk=topk, radius=radius, clip=clip)
+        kc = qat.esa_compress(self.k.view(T, H * d), Wq).view(1, T, d_c)
+        self.sel, self.n_sel, _ = qat.esa_select(self.p, self.q, Wq, None, kc)
+        _, self.lse = qat.esa_sparse_attn(self.p, self.q, self.k, self.v, self.sel, self.n_sel)
+        self.do = synth.normal(seed, 7, (1, m, H, d), torch.bfloat16, "cuda")
+        self.ws = torch.empty(qat.esa_bwd_workspace_size(self.p), dtype=torch.uint8, device="cuda")
+        self.dq = torch.empty(1, m, H, d, dtype=torch.float32, device="cuda")
+        self.dk = torch.zeros(1, T, H, d, dtype=torch.float32, device="cuda")
+        self.dv = torch.zeros(1, T, H, d, dtype=torch.float32, device="cuda")
+        self.dominant, self.bound = "esa_bwd_kv", "mfma"
+
+    def step(self):
+        self.qat.esa_sparse_attn_bwd(self.p, self.q, self.k, self.v, self.sel, self.n_sel, self.do, self.lse,
+                                     dq=self.dq, dk=self.dk, dv=self.dv, ws=self.ws)
+
+    def value(self, sec):
+        return self.m / sec
+
+    def dominant_work(self):
+        """dK/dV kernel: 4 products of d per (query, key, head) pair (s, dp,
+        dv, dk), 8 d flops; pairs per head m (gathered keys) + m (m + 1) / 2."""
+        ng = min(self.n_init, self.c0) + int(self.n_sel[0]) + (self.c0 - max(self.n_init, self.c0 - self.W))
+        pairs = self.m * ng + self.m * (self.m + 1) // 2
+        return pairs * self.H * 8 * self.d
+
+    def config(self):
+        return {"workload": self.name, "batch": 1, "ctx_len": self.T, "chunk_len": self.m, "n_heads": self.H,
+                "head_dim": self.d, "d_c": self.d_c, "n_init": self.n_init, "topk": self.topk, "window": self.W,
+                "pass": "backward"}
+
+    def cpu_baseline(self, budget_s=12.0):
+        """The float64 oracle's gradients on host cores for a bounded sample of
+        the chunk's queries (all heads: dq and their dK, dV contributions),
+        extrapolated to the chunk."""
+        import numpy as np
+        from oracle import esa as oesa
+        sg = self.sel[0, :int(self.n_sel[0])].cpu().numpy().astype(np.int64)
+        idx = oesa.key_list(sg, self.c0, self.n_init, self.W, self.T - 1)
+        kk = np.zeros((self.T, self.H, self.d))
+        vv = np.zeros((self.T, self.H, self.d))
+        ix = torch.as_tensor(idx, device="cuda")
+        kk[idx] = self.k[0, ix].to("cpu").to(torch.float64).numpy()
+        vv[idx] = self.v[0, ix].to("cpu").to(torch.float64).numpy()
+        qn = self.q[0].to("cpu").to(torch.float64).numpy()
+        dn = self.do[0].to("cpu").to(torch.float64).numpy()
+        order = np.random.default_rng(0).permutation(self.m)
+        t0 = time.perf_counter()
+        done = 0
+        while done < self.m and (time.perf_counter() - t0 < budget_s or done < 2):
+            i = int(order[done])
+            oesa.backward(qn, kk, vv, sg, self.c0, self.n_init, self.W, self.p.scale, dn[[i]], rows=[i])
+            done += 1
+        el = time.perf_counter() - t0
+        return {"value": done / el, "unit": "query-tokens/s", "cores": _blas_threads(), "kind": "oracle",
+                "sample": f"{done} random queries (all {self.H} heads) of the {self.m}-query chunk: their dq and "
+                          f"dK, dV contributions; float64 numpy, one process; {el:.1f} s"}
+
+
 class EsaWorkload(Workload):
     def __init__(self, name, seed, batch, T, m, H, d, d_c, n_init, W, topk, radius, clip, needles=0,
                  correction="clamp"):
@@ -508,6 +588,8 @@ def make(name):
         return EsaWorkload(name, 3, 1, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0)
     if name == "esa_decode_128k":
         return EsaWorkload(name, 4, 16, 131072, 1, 32, 128, 128, 128, 4096, 2048, 2, 48.0, needles=16)
+    if name == "esa_bwd_64k":
+        return EsaBwdWorkload(name, 3, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0)
     if name == "esa_prefill_64k_votes":
         return EsaWorkload(name, 3, 1, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0, correction="votes")
     if name == "esa_decode_128k_votes":
@@ -584,7 +666,7 @@ def main():
     kernels = {}
     for name in ("moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn", "moba_current_attn",
                  "moba_generic_attn", "moba_decode_select", "moba_decode_attn", "moba_decode_combine",
-                 "moba_bwd_delta", "moba_bwd_dq_past", "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated",
+                 "moba_bwd_dq_past", "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated", "esa_bwd_dq", "esa_bwd_kv",
                  "esa_compress", "esa_qcompress", "esa_scores", "esa_decode_scan", "esa_topk",
                  "esa_prefill_attn", "esa_decode_attn", "esa_generic_attn"):
         tot, n = qat.timing_query(name)
