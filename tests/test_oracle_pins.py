@@ -20,6 +20,7 @@ import torch.nn.functional as F
 import oracle
 import synth
 from oracle import attention as oatt
+from oracle import cca as occa
 from oracle import esa as oesa
 from oracle import moba as omoba
 from oracle.numerics import round_to_bf16
@@ -345,6 +346,61 @@ def test_esa_backward_matches_torch_autograd_on_masked_dense():
     assert np.allclose(dq, Q.grad.numpy(), atol=1e-12)
     assert np.allclose(dK, Kt.grad.numpy(), atol=1e-12)
     assert np.allclose(dV, Vt.grad.numpy(), atol=1e-12)
+
+
+# ---- CCA-style core-token attention --------------------------------------
+def _cca_case(seed, n=40, hq=2, hkv=1, d=4):
+    r = rng(seed)
+    return r.standard_normal((n, hq, d)), r.standard_normal((n, hkv, d)), r.standard_normal((n, hkv, d))
+
+
+@pytest.mark.parametrize("w", [0, 3, 10])
+def test_cca_group1_equals_dense_causal(w):
+    """g = 1: a group's core token is the token itself, so the core tokens
+    plus the window are all earlier tokens."""
+    q, k, v = _cca_case(60)
+    kc, vc = occa.pool(q, k, v, 1, 0.5)
+    rows = list(range(40))
+    o, lse = occa.attend_rows(q, k, v, kc, vc, 1, w, 0.5, rows)
+    for t in rows:
+        for h in range(2):
+            o_ref, l_ref = oatt.attend(q[t, h], k[:t + 1, 0], v[:t + 1, 0], 0.5)
+            assert np.allclose(o[t, h], o_ref, atol=1e-12) and abs(lse[t, h] - l_ref) < 1e-12
+
+
+def test_cca_wide_window_equals_dense_causal():
+    q, k, v = _cca_case(61)
+    kc, vc = occa.pool(q, k, v, 4, 0.3)
+    o, _ = occa.attend_rows(q, k, v, kc, vc, 4, 64, 0.3, list(range(40)))
+    for t in range(40):
+        o_ref, _ = oatt.attend(q[t, 1], k[:t + 1, 0], v[:t + 1, 0], 0.3)
+        assert np.allclose(o[t, 1], o_ref, atol=1e-12)
+
+
+def test_cca_pool_closed_forms():
+    """Identical keys in a group: the core key is that key and the core value
+    the group's mean value; the core depends on the group's last query only."""
+    q, k, v = _cca_case(62, n=16, hq=1)
+    k[4:8, 0] = k[4, 0]
+    kc, vc = occa.pool(q, k, v, 4, 0.7)
+    assert np.allclose(kc[1, 0], k[4, 0], atol=1e-14)
+    assert np.allclose(vc[1, 0], v[4:8, 0].mean(axis=0), atol=1e-14)
+    q2 = q.copy()
+    q2[8:11] += 5.0        # not the last query of group 2
+    kc2, _ = occa.pool(q2, k, v, 4, 0.7)
+    assert np.array_equal(kc2, kc)
+    q2[11] += 1.0          # the last query of group 2
+    kc3, _ = occa.pool(q2, k, v, 4, 0.7)
+    assert not np.allclose(kc3[2], kc[2])
+
+
+def test_cca_window_is_group_aligned_and_long_enough():
+    for g in (1, 3, 4, 16):
+        for w in (0, 1, 5, 16, 33):
+            for t in range(200):
+                ls = occa.window_start(t, g, w)
+                assert ls % g == 0 and 0 <= ls <= t
+                assert t - ls >= min(t, w)
 
 
 def test_moba_is_causal():
