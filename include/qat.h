@@ -61,7 +61,7 @@ int qat_abi_version(void);
  * (names: "moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn",
  * "moba_current_attn", "moba_generic_attn", "moba_decode_select",
  * "moba_decode_attn", "moba_decode_combine", "moba_bwd_delta", "moba_bwd_dq_past",
- * "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated", "esa_bwd_dq", "esa_bwd_kv",
+ * "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated", "esa_bwd_dq", "esa_bwd_kv", "cca_pool", "cca_attn",
  * "esa_compress", "esa_scores",
  * "esa_decode_scan", "esa_topk", "esa_prefill_attn", "esa_decode_attn",
  * "esa_generic_attn"). The events are timing-only (created without the
@@ -317,6 +317,51 @@ int moba_decode_select(const qat_moba_params* p, const void* q, const float* kba
  */
 int moba_decode_attn(const qat_moba_params* p, const void* q, const void* k, const void* v,
                      const int32_t* blk, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ======================================================================
+ * CCA-style core-token attention   [CCA]
+ * ====================================================================== */
+
+/*
+ * [CCA] sections on global-aware pooling, the locality-preserving module and
+ * the global-local fusion (the page drops the formulas; readings):
+ *   groups of `group` tokens, group i = [i*group, (i+1)*group);
+ *   core key / value of group i and query head h: the group's keys / values
+ *     weighted by a_j = softmax_j(scale <q_{last of group i, h}, k_j>);
+ *   query t attends, in one softmax, the core tokens of groups
+ *     i < ls(t) / group and the raw tokens [ls(t), t], where
+ *     ls(t) = max(0, floor(t/group)*group - ceil(window/group)*group)
+ *     (a group-aligned window of at least `window` earlier tokens).
+ * q: [batch, seq_len, Hq, d], k, v: [batch, seq_len, Hkv, d], bfloat16.
+ */
+typedef struct {
+  int64_t batch;
+  int64_t seq_len;
+  int64_t n_q_heads;
+  int64_t n_kv_heads;   /* divides n_q_heads */
+  int64_t head_dim;     /* 64 or 128 */
+  int64_t q_start;      /* first query position processed */
+  int64_t q_len;
+  int32_t group;        /* g >= 1 */
+  int32_t window;       /* w >= 0 */
+  float scale;          /* softmax scale > 0 (pooling and attention) */
+  int32_t dtype;        /* QAT_BF16 only */
+} qat_cca_params;
+
+/*
+ * Core keys / values of the groups the processed rows read (groups
+ * 0 .. ls(q_start+q_len-1)/group - 1) into kc, vc: [batch, seq_len/group,
+ * Hq, d] bfloat16 (rows of other groups untouched). No workspace.
+ */
+int cca_pool(const qat_cca_params* p, const void* q, const void* k, const void* v, void* kc, void* vc,
+             void* stream);
+/*
+ * Attention of the rows q_start .. q_start+q_len-1 over their core tokens
+ * (from cca_pool) and their window. out: [batch, q_len, Hq, d] bfloat16;
+ * lse: [batch, q_len, Hq] float32 natural log, or NULL. No workspace.
+ */
+int cca_attn(const qat_cca_params* p, const void* q, const void* k, const void* v, const void* kc,
+             const void* vc, void* out, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

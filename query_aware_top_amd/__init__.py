@@ -30,6 +30,10 @@ from ._binding import (  # noqa: F401
     moba_decode_attn,
     moba_bwd_workspace_size,
     moba_sparse_attn_bwd,
+    CcaParams,
+    cca_params,
+    cca_pool,
+    cca_attn,
     EXPORTED_SYMBOLS,
     timing_enable,
     timing_select,

@@ -19,7 +19,7 @@ EXPORTED_SYMBOLS = (
     "esa_workspace_size", "esa_compress_workspace_size", "esa_compress", "esa_select", "esa_sparse_attn",
     "esa_bwd_workspace_size", "esa_sparse_attn_bwd",
     "moba_workspace_size", "moba_block_select", "moba_sparse_attn", "moba_block_means", "moba_decode_select",
-    "moba_decode_attn", "moba_bwd_workspace_size", "moba_sparse_attn_bwd",
+    "moba_decode_attn", "moba_bwd_workspace_size", "moba_sparse_attn_bwd", "cca_pool", "cca_attn",
 )
 
 
@@ -41,6 +41,15 @@ class EsaParams(ctypes.Structure):
 
 
 QAT_CORR_CLAMP, QAT_CORR_VOTES = 0, 1
+
+
+class CcaParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64), ("n_q_heads", ctypes.c_int64),
+        ("n_kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64), ("q_start", ctypes.c_int64),
+        ("q_len", ctypes.c_int64), ("group", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
 
 
 class MobaParams(ctypes.Structure):
@@ -75,6 +84,8 @@ def lib():
         L.esa_sparse_attn_bwd.argtypes = [ctypes.POINTER(EsaParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                           vp]
         L.moba_workspace_size.argtypes = [ctypes.POINTER(MobaParams), ctypes.POINTER(sz)]
+        L.cca_pool.argtypes = [ctypes.POINTER(CcaParams), vp, vp, vp, vp, vp, vp]
+        L.cca_attn.argtypes = [ctypes.POINTER(CcaParams), vp, vp, vp, vp, vp, vp, vp, vp]
         L.moba_block_select.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, sz, vp]
         L.qat_timing_enable.argtypes = [ctypes.c_int]
         L.qat_timing_select.argtypes = [ctypes.c_char_p]
@@ -391,3 +402,39 @@ def moba_sparse_attn_bwd(p: MobaParams, q, k, v, blk, dout, lse, dq=None, dk=Non
     ws = _workspace(moba_bwd_workspace_size(p), dev, ws)
     _check(lib().moba_sparse_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(blk), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
     return dq, dk, dv
+
+
+# ------------------------------------------------------------------ CCA
+def cca_params(*, batch, seq_len, n_q_heads, n_kv_heads, head_dim, group, window, q_start=0, q_len=None,
+               scale=None) -> CcaParams:
+    return CcaParams(batch, seq_len, n_q_heads, n_kv_heads, head_dim, q_start,
+                     seq_len - q_start if q_len is None else q_len, group, window,
+                     float(scale if scale is not None else 1.0 / math.sqrt(head_dim)), QAT_BF16)
+
+
+def cca_pool(p: CcaParams, q, k, v, kc=None, vc=None):
+    """Returns the core keys / values kc, vc [batch, seq_len // group, Hq, d]
+    (bfloat16; allocated when None)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16)
+    ng = p.seq_len // p.group
+    if kc is None:
+        kc = torch.empty(p.batch, max(ng, 1), p.n_q_heads, p.head_dim, dtype=torch.bfloat16, device=q.device)
+    if vc is None:
+        vc = torch.empty_like(kc)
+    _check(lib().cca_pool(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _stream()))
+    return kc, vc
+
+
+def cca_attn(p: CcaParams, q, k, v, kc, vc, out=None, lse=None, want_lse=True):
+    """Returns (out [batch, q_len, Hq, d] bfloat16, lse [batch, q_len, Hq] or None)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (kc, "kc"), (vc, "vc")):
+        _need(t, name, torch.bfloat16)
+    dev = q.device
+    if out is None:
+        out = torch.empty(p.batch, p.q_len, p.n_q_heads, p.head_dim, dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(p.batch, p.q_len, p.n_q_heads, dtype=torch.float32, device=dev)
+    _check(lib().cca_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(lse),
+                          _stream()))
+    return out, lse

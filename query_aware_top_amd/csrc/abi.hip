@@ -657,3 +657,52 @@ QAT_EXPORT int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, con
                            p->n_kv_heads, p->head_dim, p->q_start, p->q_len, p->block, p->topk, p->scale, s);
   return hip_status(e, "moba_sparse_attn_bwd");
 }
+
+// ---------------------------------------------------------------- CCA
+int cca_check(const qat_cca_params* p) {
+  if (!p) return fail(QAT_EINVAL, "params is NULL");
+  if (p->batch < 1 || p->seq_len < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1)
+    return fail(QAT_EINVAL, "batch, seq_len and head counts must be >= 1");
+  if (p->n_q_heads % p->n_kv_heads) return fail(QAT_EINVAL, "n_kv_heads must divide n_q_heads");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(QAT_EUNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)p->head_dim);
+  if (p->dtype != QAT_BF16) return fail(QAT_EUNSUPPORTED, "CCA attention takes bfloat16 inputs");
+  if (p->q_start < 0 || p->q_len < 1 || p->q_start + p->q_len > p->seq_len)
+    return fail(QAT_EINVAL, "query rows [%lld, %lld) outside the sequence of %lld", (long long)p->q_start,
+                (long long)(p->q_start + p->q_len), (long long)p->seq_len);
+  if (p->group < 1) return fail(QAT_EINVAL, "group must be >= 1");
+  if (p->window < 0) return fail(QAT_EINVAL, "window must be >= 0");
+  if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return fail(QAT_EINVAL, "scale must be finite and > 0");
+  if (p->seq_len * p->n_q_heads * p->head_dim >= (1ll << 31))
+    return fail(QAT_EUNSUPPORTED, "one sequence's q must hold fewer than 2^31 elements");
+  return QAT_OK;
+}
+
+QAT_EXPORT int cca_pool(const qat_cca_params* p, const void* q, const void* k, const void* v, void* kc, void* vc,
+                        void* stream) {
+  int rc = cca_check(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !kc || !vc) return fail(QAT_EINVAL, "q, k, v, kc, vc must be non-NULL");
+  const int64_t ngroups = p->seq_len / p->group;
+  const int64_t need = qat::cca_groups_needed(p->seq_len, p->q_start, p->q_len, p->group, p->window);
+  hipStream_t s = (hipStream_t)stream;
+  qat::KTimer tm("cca_pool", s);
+  hipError_t e = qat::launch_cca_pool(q, k, v, kc, vc, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads,
+                                      p->head_dim, ngroups, need, p->group, p->scale, s);
+  return hip_status(e, "cca_pool");
+}
+
+QAT_EXPORT int cca_attn(const qat_cca_params* p, const void* q, const void* k, const void* v, const void* kc,
+                        const void* vc, void* out, float* lse, void* stream) {
+  int rc = cca_check(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !out) return fail(QAT_EINVAL, "q, k, v, out must be non-NULL");
+  const int64_t need = qat::cca_groups_needed(p->seq_len, p->q_start, p->q_len, p->group, p->window);
+  if (need > 0 && (!kc || !vc)) return fail(QAT_EINVAL, "kc, vc must be non-NULL");
+  hipStream_t s = (hipStream_t)stream;
+  qat::KTimer tm("cca_attn", s);
+  hipError_t e = qat::launch_cca_attn(q, k, v, kc, vc, out, lse, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads,
+                                      p->head_dim, p->q_start, p->q_len, p->seq_len / p->group, p->group,
+                                      p->window, p->scale, s);
+  return hip_status(e, "cca_attn");
+}

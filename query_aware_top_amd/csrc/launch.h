@@ -128,6 +128,17 @@ hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, 
 hipError_t launch_esa_keylist(const int32_t* sel, const int32_t* n_sel, int32_t* keylist, int64_t batch, int64_t c0,
                               int64_t m, int64_t n_init, int64_t window, int topk, hipStream_t s);
 
+// ---- CCA-style core-token attention (cca.hip), bfloat16 -------------------
+// groups [0, cca_groups_needed) pooled for the processed positions
+int64_t cca_groups_needed(int64_t seq_len, int64_t q_start, int64_t q_len, int group, int window);
+hipError_t launch_cca_pool(const void* q, const void* k, const void* v, void* kc, void* vc, int64_t batch,
+                           int64_t seq_len, int64_t hq, int64_t hkv, int64_t d, int64_t ngroups, int64_t npool,
+                           int group, float scale, hipStream_t s);
+hipError_t launch_cca_attn(const void* q, const void* k, const void* v, const void* kc, const void* vc, void* out,
+                           float* lse, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv, int64_t d,
+                           int64_t q_start, int64_t q_len, int64_t ngroups, int group, int window, float scale,
+                           hipStream_t s);
+
 // ---- ESA gradients (esa_bwd.hip), bfloat16 --------------------------------
 // dq [batch, m, H, D] and delta [batch, m, H] written; dk, dv [batch,
 // ctx_len, H, D] added to at the key lists' positions.
