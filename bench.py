@@ -11,7 +11,8 @@ Prints one JSON line. Default workload: MoBA prefill at the 8B-style GQA
 shape (32 query / 8 KV heads x 128, N = 32768, block 512, top-k 3 with the
 forced block, 8 planted key blocks), reported as query tokens per second.
 Other workloads (--workload): moba_fp32_4k, esa_prefill_64k,
-esa_decode_128k, moba_long_512k, moba_decode_128k, moba_bwd_32k and esa_bwd_64k (gradients), and
+esa_decode_128k, moba_long_512k, moba_decode_128k, moba_bwd_32k and esa_bwd_64k (gradients), cca_64k
+(CCA-style core-token attention), and
 esa_prefill_64k_votes /
 esa_decode_128k_votes (the softmax-vote reading of ESA's score correction).
 """
@@ -57,6 +58,8 @@ STAGE_SOURCES = {
     "moba_bwd_gated": ["moba_bwd.hip", "attn_core.h", "attn_bwd.h"],
     "esa_bwd_dq": ["esa_bwd.hip", "attn_core.h", "attn_bwd.h"],
     "esa_bwd_kv": ["esa_bwd.hip", "attn_core.h", "attn_bwd.h"],
+    "cca_pool": ["cca.hip"],
+    "cca_attn": ["cca.hip", "attn_core.h"],
     "esa_compress*": ["compress.hip"],
     "esa_scores": ["esa_select.hip"],
     "esa_topk": ["esa_select.hip"],
@@ -364,6 +367,77 @@ class MobaBwdWorkload(Workload):
                           f"{el:.1f} s"}
 
 
+class CcaWorkload(Workload):
+    """CCA-style core-token attention over a whole prefill: the core tokens of
+    every group are pooled (each group's last query weighting its keys and
+    values), then every position attends its core tokens plus its
+    group-aligned window in one softmax."""
+
+    def __init__(self, name, seed, n, h, d, group, window):
+        import query_aware_top_amd as qat
+        import synth
+        self.qat = qat
+        self.name = name
+        self.unit = "query-tokens/s"
+        self.dtype = "bf16"
+        self.n, self.h, self.d, self.g, self.w = n, h, d, group, window
+        self.q, self.k, self.v, _ = synth.moba_inputs(seed, 1, n, h, h, d, torch.bfloat16, "cuda")
+        self.p = qat.cca_params(batch=1, seq_len=n, n_q_heads=h, n_kv_heads=h, head_dim=d, group=group,
+                                window=window)
+        self.kc = torch.empty(1, n // group, h, d, dtype=torch.bfloat16, device="cuda")
+        self.vc = torch.empty_like(self.kc)
+        self.out = torch.empty(1, n, h, d, dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty(1, n, h, dtype=torch.float32, device="cuda")
+        self.dominant, self.bound = "cca_attn", "mfma"
+
+    def step(self):
+        self.qat.cca_pool(self.p, self.q, self.k, self.v, self.kc, self.vc)
+        self.qat.cca_attn(self.p, self.q, self.k, self.v, self.kc, self.vc, out=self.out, lse=self.lse)
+
+    def value(self, sec):
+        return self.n / sec
+
+    def _keys(self):
+        t = torch.arange(self.n, dtype=torch.int64)
+        wg = -(-self.w // self.g) * self.g
+        ls = torch.clamp((t // self.g) * self.g - wg, min=0)
+        return (ls // self.g) + (t - ls + 1)
+
+    def dominant_work(self):
+        """One (query, key, head) pair of the attention: 4 d flops (q.k and
+        p v); keys per query = its core tokens + its window."""
+        return int(self._keys().sum()) * self.h * 4 * self.d
+
+    def config(self):
+        return {"workload": self.name, "batch": 1, "seq_len": self.n, "n_heads": self.h, "head_dim": self.d,
+                "group": self.g, "window": self.w}
+
+    def cpu_baseline(self, budget_s=12.0):
+        """The float64 oracle on host cores: pooling of the groups the
+        sampled rows read plus attention of random rows (all heads),
+        extrapolated to the sequence."""
+        import numpy as np
+        from oracle import cca as occa
+        qn = self.q[0].to("cpu").to(torch.float64).numpy()
+        kn = self.k[0].to("cpu").to(torch.float64).numpy()
+        vn = self.v[0].to("cpu").to(torch.float64).numpy()
+        t0 = time.perf_counter()
+        need = occa.window_start(self.n - 1, self.g, self.w) // self.g
+        kc, vc = occa.pool(qn, kn, vn, self.g, self.p.scale, need)
+        t_pool = time.perf_counter() - t0
+        order = np.random.default_rng(0).permutation(self.n)
+        done = 0
+        while done < self.n and (time.perf_counter() - t0 < budget_s or done < 2):
+            occa.attend_rows(qn, kn, vn, kc, vc, self.g, self.w, self.p.scale, [int(order[done])])
+            done += 1
+        el = time.perf_counter() - t0
+        est = t_pool + (el - t_pool) / done * self.n
+        return {"value": self.n / est, "unit": "query-tokens/s", "cores": _blas_threads(), "kind": "oracle",
+                "sample": f"pooling of all {need} groups ({t_pool:.1f} s) plus attention of {done} random rows "
+                          f"(all {self.h} heads), extrapolated to the {self.n} rows; float64 numpy, one process; "
+                          f"{el:.1f} s"}
+
+
 class EsaBwdWorkload(Workload):
     """Gradients of the ESA chunk attention (selection held fixed) at the 64k
     prefill shape: compression, selection and attention run once before
@@ -588,6 +662,8 @@ def make(name):
         return EsaWorkload(name, 3, 1, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0)
     if name == "esa_decode_128k":
         return EsaWorkload(name, 4, 16, 131072, 1, 32, 128, 128, 128, 4096, 2048, 2, 48.0, needles=16)
+    if name == "cca_64k":
+        return CcaWorkload(name, 6, 65536, 32, 128, 16, 1024)
     if name == "esa_bwd_64k":
         return EsaBwdWorkload(name, 3, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0)
     if name == "esa_prefill_64k_votes":
@@ -667,6 +743,7 @@ def main():
     for name in ("moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn", "moba_current_attn",
                  "moba_generic_attn", "moba_decode_select", "moba_decode_attn", "moba_decode_combine",
                  "moba_bwd_dq_past", "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated", "esa_bwd_dq", "esa_bwd_kv",
+                 "cca_pool", "cca_attn",
                  "esa_compress", "esa_qcompress", "esa_scores", "esa_decode_scan", "esa_topk",
                  "esa_prefill_attn", "esa_decode_attn", "esa_generic_attn"):
         tot, n = qat.timing_query(name)
