@@ -42,6 +42,13 @@ One sequence, chunk C = [c0, c0 + m) of queries (decode: m = 1, c0 = T - 1),
    head with the same S for every head (global part I u S and window part
    L u chunk fused, see oracle.attention.merge).
 
+Per-head selection (the comparison arm of the write-up's ablation on head
+merging; READING: with no per-head compression map on the page, each head h
+scores the middle part with its own uncompressed q^h and k^h, s^h_ij =
+<q_i^h, k_j^h>, then steps 4-7 run per head; in step 8 head h attends its
+own selection). ``select_heads`` returns one selection per head and
+``attend`` / ``backward`` take such a list in place of the shared one.
+
 Parity: steps 1-3 and 5, 7, 8 are pinned by CPU tests (k >= |M| equals dense
 causal attention; clip = inf and r = 0 reduce selection to one matrix-vector
 product and a sort; exhaustive sort on tiny inputs; maximum_filter1d for the
@@ -52,6 +59,7 @@ parity unpinned, since the pages do not carry those formulas.
 """
 import numpy as np
 
+from .attention import attend as attend_row
 from .attention import attend_grad, attend_heads
 from .numerics import round_to_bf16
 
@@ -149,6 +157,31 @@ def select(q, Wq, bq, kc_cache, c0, n_init, window, topk, radius, clip, correcti
     return sel, up, u, rowmax
 
 
+def select_heads(q, K, c0, n_init, window, topk, radius, clip, correction="clamp", tau=None):
+    """Per-head selection for one sequence and chunk. q [m, H, d] the chunk's
+    queries, K [T, H, d] the key cache (or a view whose K[rows, h] returns
+    those rows of head h). Returns (sels: H ascending position arrays,
+    ups [H, |M|] the per-head u')."""
+    m, H, d = q.shape
+    _, M, _ = partition(c0, n_init, window)
+    q = np.asarray(q, np.float64)
+    sels, ups = [], np.zeros((H, M.size))
+    for h in range(H):
+        if M.size == 0:
+            sels.append(np.zeros(0, dtype=np.int64))
+            continue
+        u, _ = importance(q[:, h], np.asarray(K[M, h], np.float64), clip, correction=correction, tau=tau)
+        ups[h] = neighbour(u, radius)
+        sels.append(M[top_k(ups[h], topk)])
+    return sels, ups
+
+
+def _per_head(sel):
+    """A list / tuple of arrays is one selection per head; anything else is
+    the selection shared by every head."""
+    return isinstance(sel, (list, tuple))
+
+
 def key_list(sel, c0, n_init, window, t):
     I, _, L = partition(c0, n_init, window)
     return np.concatenate([I, np.asarray(sel, np.int64), L, np.arange(c0, t + 1)])
@@ -156,14 +189,22 @@ def key_list(sel, c0, n_init, window, t):
 
 def attend(q, K, V, sel, c0, n_init, window, scale, rows=None):
     """Step 8 for one sequence. q [m, H, d] (chunk rows), K/V [T, H, d].
-    rows: chunk-relative query indices (default all). Returns o [len(rows),
-    H, d], lse [len(rows), H]."""
+    rows: chunk-relative query indices (default all); sel: the shared
+    selection, or a list of one per head. Returns o [len(rows), H, d],
+    lse [len(rows), H]."""
     m, H, d = q.shape
     if rows is None:
         rows = list(range(m))
     o = np.zeros((len(rows), H, V.shape[2]))
     lse = np.zeros((len(rows), H))
     for r, i in enumerate(rows):
+        if _per_head(sel):
+            for h in range(H):
+                idx = key_list(sel[h], c0, n_init, window, c0 + i)
+                o[r, h], lse[r, h] = attend_row(np.asarray(q[i, h], np.float64),
+                                                np.asarray(K[idx, h], np.float64),
+                                                np.asarray(V[idx, h], np.float64), scale)
+            continue
         idx = key_list(sel, c0, n_init, window, c0 + i)
         o[r], lse[r] = attend_heads(np.asarray(q[i], np.float64),
                                     np.asarray(K[idx], np.float64),
@@ -186,8 +227,8 @@ def backward(q, K, V, sel, c0, n_init, window, scale, do, rows=None, heads=None)
     dK = np.zeros(K.shape)
     dV = np.zeros(V.shape)
     for r, i in enumerate(rows):
-        idx = key_list(sel, c0, n_init, window, c0 + i)
         for h in heads:
+            idx = key_list(sel[h] if _per_head(sel) else sel, c0, n_init, window, c0 + i)
             dq[r, h], gk, gv = attend_grad(q[i, h], np.asarray(K[idx, h], np.float64),
                                            np.asarray(V[idx, h], np.float64), scale, do[r, h])
             dK[idx, h] += gk

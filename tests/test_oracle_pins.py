@@ -542,6 +542,95 @@ def test_esa_decode_monotone_correction_keeps_raw_ranking():
     assert np.array_equal(sel, np.sort(M[np.argsort(-raw, kind="stable")[:12]]))
 
 
+# ---- per-head selection (the head-merging ablation's other arm) ----------
+def test_esa_per_head_single_head_is_merged_with_identity_map():
+    """H = 1 with the identity as compression map (d_c = d, k bf16 so the
+    rounded cache is k itself): per-head selection = the merged selection,
+    for both correction readings."""
+    r = rng(60)
+    T, d, m = 160, 8, 5
+    q = round_to_bf16(r.standard_normal((m, 1, d)))
+    k = round_to_bf16(r.standard_normal((T, 1, d)))
+    eye = np.eye(d)
+    kc = oesa.key_cache(k, eye)
+    assert np.array_equal(kc, k[:, 0])
+    c0, n_init, W = T - m, 6, 20
+    for corr in ("clamp", "votes"):
+        sel, up, _, _ = oesa.select(q, eye, None, kc, c0, n_init, W, 9, radius=1, clip=2.5, correction=corr)
+        sels, ups = oesa.select_heads(q, k, c0, n_init, W, 9, radius=1, clip=2.5, correction=corr)
+        assert len(sels) == 1
+        assert np.array_equal(sels[0], sel)
+        np.testing.assert_allclose(ups[0], up, rtol=1e-12, atol=1e-12)
+
+
+def test_esa_per_head_planted_needles_are_per_head():
+    """Head h's queries all point along a_h and head h's key at p_h is
+    3 a_h (other heads' keys at p_h are noise): with top-1 and radius 0,
+    head h selects exactly p_h -- a transposed head index selects another
+    head's needle."""
+    r = rng(61)
+    T, H, d, m = 200, 4, 16, 3
+    k = 0.1 * r.standard_normal((T, H, d))
+    q = np.zeros((m, H, d))
+    pos = [30, 77, 101, 140]
+    for h in range(H):
+        a = r.standard_normal(d)
+        a /= np.linalg.norm(a)
+        q[:, h] = a
+        k[pos[h], h] = 3 * a
+    sels, _ = oesa.select_heads(q, k, T - m, 4, 16, 1, radius=0, clip=48.0)
+    assert [list(s) for s in sels] == [[p] for p in pos]
+
+
+def test_esa_per_head_heads_are_independent():
+    """Changing one head's keys leaves the other heads' selections alone, and
+    head h's selection is the single-head selection of its own slice."""
+    r = rng(62)
+    T, H, d, m = 180, 3, 8, 4
+    q = r.standard_normal((m, H, d))
+    k = r.standard_normal((T, H, d))
+    args = (T - m, 5, 24, 11)
+    sels, _ = oesa.select_heads(q, k, *args, radius=2, clip=3.0)
+    k2 = k.copy()
+    k2[:, 2] = r.standard_normal((T, d))
+    sels2, _ = oesa.select_heads(q, k2, *args, radius=2, clip=3.0)
+    assert np.array_equal(sels[0], sels2[0]) and np.array_equal(sels[1], sels2[1])
+    for h in range(H):
+        one, _ = oesa.select_heads(q[:, h:h + 1], k[:, h:h + 1], *args, radius=2, clip=3.0)
+        assert np.array_equal(one[0], sels[h])
+
+
+def test_esa_per_head_attention_reduces_to_shared_and_single_head():
+    """Per-head lists that are all equal give the shared-selection attention;
+    with different lists, head h's output is the single-head attention over
+    its own list. Gradients reduce the same way."""
+    r = rng(63)
+    T, H, d, m = 120, 3, 8, 5
+    c0, n_init, W, scale = T - m, 4, 12, 0.35
+    q = r.standard_normal((m, H, d))
+    K = r.standard_normal((T, H, d))
+    V = r.standard_normal((T, H, d))
+    _, M, _ = oesa.partition(c0, n_init, W)
+    shared = np.sort(r.choice(M, 9, replace=False))
+    o1, l1 = oesa.attend(q, K, V, shared, c0, n_init, W, scale)
+    o2, l2 = oesa.attend(q, K, V, [shared] * H, c0, n_init, W, scale)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=1e-12, atol=1e-12)
+    sels = [np.sort(r.choice(M, 9, replace=False)) for _ in range(H)]
+    o, lse = oesa.attend(q, K, V, sels, c0, n_init, W, scale)
+    do = r.standard_normal((m, H, d))
+    dq, dK, dV = oesa.backward(q, K, V, sels, c0, n_init, W, scale, do)
+    for h in range(H):
+        sl = slice(h, h + 1)
+        oh, lh = oesa.attend(q[:, sl], K[:, sl], V[:, sl], sels[h], c0, n_init, W, scale)
+        np.testing.assert_allclose(o[:, sl], oh, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[:, sl], lh, rtol=1e-12, atol=1e-12)
+        gq, gK, gV = oesa.backward(q[:, sl], K[:, sl], V[:, sl], sels[h], c0, n_init, W, scale, do[:, sl])
+        np.testing.assert_allclose(dq[:, sl], gq, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dK[:, sl], gK, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dV[:, sl], gV, rtol=1e-12, atol=1e-12)
+
+
 # ---- alternative correction reading: per-query softmax votes -------------
 def _votes_case(seed, m, n_mid, d_c=6):
     r = rng(seed)
