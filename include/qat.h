@@ -48,7 +48,7 @@ enum qat_status {
 
 enum qat_dtype { QAT_F32 = 0, QAT_BF16 = 1 };
 
-#define QAT_ABI_VERSION 2
+#define QAT_ABI_VERSION 3
 
 /* Thread-local text for the last non-OK status of this thread ("" if none). */
 const char* qat_last_error(void);
@@ -108,7 +108,10 @@ typedef struct {
   float scale;          /* softmax scale > 0, e.g. 1/sqrt(d) */
   int32_t dtype;        /* qat_dtype of q, K, V and outputs */
   int32_t correction;   /* qat_esa_correction: reading of the score correction */
-  float vote_tau;       /* QAT_CORR_VOTES temperature; <= 0: 1/sqrt(d_c) */
+  float vote_tau;       /* QAT_CORR_VOTES temperature; <= 0: 1/sqrt(d_c) (per head: 1/sqrt(d)) */
+  int32_t per_head;     /* 0: one selection per sequence, all heads merged (esa_select);
+                           1: one selection per (sequence, head) (esa_select_heads);
+                           sel / n_sel then hold [batch, H, topk] / [batch, H] */
 } qat_esa_params;
 
 /*
@@ -121,7 +124,8 @@ typedef struct {
  */
 enum qat_esa_correction { QAT_CORR_CLAMP = 0, QAT_CORR_VOTES = 1 };
 
-/* Workspace bytes for esa_select + esa_sparse_attn with these parameters. */
+/* Workspace bytes for esa_select (or esa_select_heads) + esa_sparse_attn with
+ * these parameters. */
 int esa_workspace_size(const qat_esa_params* p, size_t* bytes);
 
 /*
@@ -154,18 +158,39 @@ int esa_compress(const void* x, int64_t n, int64_t x_stride, int64_t d_model, in
  * q: [batch, chunk_len, H, d] (dtype), Wq: [d_c, H*d] (dtype), bq: [d_c]
  * float32 or NULL, kc_cache: [batch, ctx_len, d_c] bfloat16 (as written by
  * esa_compress). Outputs: sel [batch, topk] int32, n_sel [batch] int32,
- * scores [batch, |M|] float32 (u'_j, may be NULL).
+ * scores [batch, |M|] float32 (u'_j, may be NULL). Requires p->per_head == 0.
  */
 int esa_select(const qat_esa_params* p, const void* q, const void* Wq, const float* bq,
                const void* kc_cache, int32_t* sel, int32_t* n_sel, float* scores,
                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Per-head token selection, the comparison arm of [ESA]'s ablation on head
+ * merging (the write-up scores with all heads merged and reports that doing
+ * so changes little against selecting per head). READING: with no per-head
+ * compression map given, head h scores the middle part with its own
+ * uncompressed rows, s^h_ij = <q_i^h, k_j^h> (bf16 products, float32 sums),
+ * then the correction (vote_tau <= 0 means 1/sqrt(d)), the sum over the
+ * chunk's queries, the neighbour step and the top-k run per head, exactly as
+ * in esa_select.
+ * Requires p->per_head == 1, bfloat16 (QAT_EUNSUPPORTED otherwise) and one
+ * sequence's cache below 2^31 elements; d_c is ignored.
+ * q: [batch, chunk_len, H, d], k_cache: [batch, ctx_len, H, d]. Outputs:
+ * sel [batch, H, topk] int32 (ascending, -1 padded), n_sel [batch, H]
+ * int32, scores [batch, H, |M|] float32 (u'_j per head, may be NULL).
+ * esa_sparse_attn / esa_sparse_attn_bwd with the same params (per_head = 1)
+ * let head h attend its own selection.
+ */
+int esa_select_heads(const qat_esa_params* p, const void* q, const void* k_cache, int32_t* sel, int32_t* n_sel,
+                     float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Attention over the fused parts ([ESA], global attention over initial plus
  * selected tokens fused with window attention over local tokens; [CCA],
  * global-local fusion into one unified K/V): query t = c0 + i attends
  * I u S u L u [c0, t] with one joint softmax per head, S = sel[0:n_sel]
- * shared by all heads.
+ * shared by all heads (p->per_head == 1: head h uses its own selection,
+ * bfloat16 and caches below 2^31 elements per sequence only).
  * q: [batch, chunk_len, H, d]; k_cache, v_cache: [batch, ctx_len, H, d];
  * sel/n_sel: as produced by esa_select (positions must lie in M).
  * out: [batch, chunk_len, H, d] (dtype); lse: [batch, chunk_len, H] float32

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     esa_workspace_size,
     esa_compress,
     esa_select,
+    esa_select_heads,
     esa_sparse_attn,
     esa_bwd_workspace_size,
     esa_sparse_attn_bwd,

@@ -16,7 +16,8 @@ _STATUS = {0: "QAT_OK", -1: "QAT_EINVAL", -2: "QAT_EUNSUPPORTED", -3: "QAT_EWORK
 EXPORTED_SYMBOLS = (
     "qat_last_error", "qat_abi_version", "qat_timing_enable", "qat_timing_select", "qat_timing_reset",
     "qat_timing_query",
-    "esa_workspace_size", "esa_compress_workspace_size", "esa_compress", "esa_select", "esa_sparse_attn",
+    "esa_workspace_size", "esa_compress_workspace_size", "esa_compress", "esa_select", "esa_select_heads",
+    "esa_sparse_attn",
     "esa_bwd_workspace_size", "esa_sparse_attn_bwd",
     "moba_workspace_size", "moba_block_select", "moba_sparse_attn", "moba_block_means", "moba_decode_select",
     "moba_decode_attn", "moba_bwd_workspace_size", "moba_sparse_attn_bwd", "cca_pool", "cca_attn",
@@ -36,7 +37,7 @@ class EsaParams(ctypes.Structure):
         ("chunk_len", ctypes.c_int64), ("n_init", ctypes.c_int32), ("window", ctypes.c_int32),
         ("topk", ctypes.c_int32), ("radius", ctypes.c_int32), ("clip", ctypes.c_float),
         ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("correction", ctypes.c_int32),
-        ("vote_tau", ctypes.c_float),
+        ("vote_tau", ctypes.c_float), ("per_head", ctypes.c_int32),
     ]
 
 
@@ -174,13 +175,15 @@ def _workspace(nbytes: int, device, ws=None):
 
 # ------------------------------------------------------------------ ESA
 def esa_params(*, batch, n_heads, head_dim, d_c, ctx_len, chunk_start, chunk_len, n_init, window, topk,
-               radius, clip, scale=None, dtype=torch.bfloat16, correction="clamp", vote_tau=0.0) -> EsaParams:
+               radius, clip, scale=None, dtype=torch.bfloat16, correction="clamp", vote_tau=0.0,
+               per_head=False) -> EsaParams:
     """correction: "clamp" (default reading) or "votes" (per-query softmax
-    votes at temperature vote_tau; 0 means 1/sqrt(d_c))."""
+    votes at temperature vote_tau; 0 means 1/sqrt(d_c), per head 1/sqrt(d)).
+    per_head: one selection per (sequence, head) by esa_select_heads."""
     corr = {"clamp": QAT_CORR_CLAMP, "votes": QAT_CORR_VOTES}[correction]
     return EsaParams(batch, n_heads, head_dim, d_c, ctx_len, chunk_start, chunk_len, n_init, window, topk,
                      radius, float(clip), float(scale if scale is not None else 1.0 / math.sqrt(head_dim)),
-                     _dt(dtype), corr, float(vote_tau))
+                     _dt(dtype), corr, float(vote_tau), 1 if per_head else 0)
 
 
 def esa_workspace_size(p: EsaParams) -> int:
@@ -233,6 +236,25 @@ def esa_select(p: EsaParams, q, Wq, bq, kc_cache, sel=None, n_sel=None, scores=N
     ws = _workspace(esa_workspace_size(p), dev, ws)
     _check(lib().esa_select(ctypes.byref(p), _ptr(q), _ptr(Wq), _ptr(bq), _ptr(kc_cache), _ptr(sel),
                             _ptr(n_sel), _ptr(scores), _ptr(ws), ws.numel(), _stream()))
+    return sel, n_sel, scores
+
+
+def esa_select_heads(p: EsaParams, q, k_cache, sel=None, n_sel=None, scores=None, want_scores=False, ws=None):
+    """Per-head selection. Returns (sel [batch, H, topk] int32, n_sel
+    [batch, H] int32, scores [batch, H, |M|] or None)."""
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16)
+    dev = q.device
+    if sel is None:
+        sel = torch.empty(p.batch, p.n_heads, p.topk, dtype=torch.int32, device=dev)
+    if n_sel is None:
+        n_sel = torch.empty(p.batch, p.n_heads, dtype=torch.int32, device=dev)
+    if scores is None and want_scores:
+        n_mid = max(0, max(p.n_init, p.chunk_start - p.window) - p.n_init) if p.chunk_start > p.n_init else 0
+        scores = torch.empty(p.batch, p.n_heads, max(n_mid, 1), dtype=torch.float32, device=dev)
+    ws = _workspace(esa_workspace_size(p), dev, ws)
+    _check(lib().esa_select_heads(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(sel), _ptr(n_sel), _ptr(scores),
+                                  _ptr(ws), ws.numel(), _stream()))
     return sel, n_sel, scores
 
 

@@ -70,7 +70,9 @@ int esa_check(const qat_esa_params* p) {
   if (p->batch < 1 || p->n_heads < 1) return fail(QAT_EINVAL, "batch and n_heads must be >= 1");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(QAT_EUNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)p->head_dim);
-  if (!pow2_dc(p->d_c)) return fail(QAT_EUNSUPPORTED, "d_c %lld not supported (32, 64, 128, 256)", (long long)p->d_c);
+  if (p->per_head != 0 && p->per_head != 1) return fail(QAT_EINVAL, "per_head must be 0 or 1");
+  if (!p->per_head && !pow2_dc(p->d_c))
+    return fail(QAT_EUNSUPPORTED, "d_c %lld not supported (32, 64, 128, 256)", (long long)p->d_c);
   if (p->ctx_len < 1 || p->ctx_len >= (1ll << 31)) return fail(QAT_EINVAL, "ctx_len out of range");
   if (p->chunk_start < 0 || p->chunk_len < 1 || p->chunk_start + p->chunk_len > p->ctx_len)
     return fail(QAT_EINVAL, "chunk [%lld, %lld) outside the cache of %lld rows", (long long)p->chunk_start,
@@ -87,26 +89,31 @@ int esa_check(const qat_esa_params* p) {
   if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return fail(QAT_EINVAL, "scale must be finite and > 0");
   if (p->dtype != QAT_F32 && p->dtype != QAT_BF16) return fail(QAT_EINVAL, "unknown dtype %d", p->dtype);
   if (p->batch * p->chunk_len * p->n_heads >= (1ll << 31)) return fail(QAT_EUNSUPPORTED, "too many query rows");
+  if (p->per_head && p->dtype != QAT_BF16) return fail(QAT_EUNSUPPORTED, "per-head selection takes bfloat16 inputs");
+  if (p->per_head && p->ctx_len * p->n_heads * p->head_dim >= (1ll << 31))
+    return fail(QAT_EUNSUPPORTED, "per-head selection: one sequence's cache must hold fewer than 2^31 elements");
   return QAT_OK;
 }
 
 EsaLayout esa_layout(const qat_esa_params* p, void* ws) {
   EsaLayout L;
-  const int64_t B = p->batch, m = p->chunk_len, c0 = p->chunk_start;
+  // B: selections (one per sequence, or one per (sequence, head))
+  const int64_t B = p->per_head ? p->batch * p->n_heads : p->batch, m = p->chunk_len, c0 = p->chunk_start;
   L.rows = B * m;
   L.mid0 = p->n_init;
   L.n_mid = c0 > p->n_init ? std::max<int64_t>(p->n_init, c0 - p->window) - p->n_init : 0;
   const int64_t D = p->n_heads * p->head_dim;
-  L.nsplit_q = qat::compress_splits(L.rows, D, p->d_c);
+  L.nsplit_q = p->per_head ? 0 : qat::compress_splits(L.rows, D, p->d_c);
+  const int64_t dcq = p->per_head ? 0 : p->d_c;   // per head: no compressed queries
   L.nkeysplit = qat::esa_key_splits(L.n_mid > 0 ? L.n_mid : 1, m);
   L.nqsplit = qat::esa_prefill_qsplits_eff(L.n_mid > 0 ? L.n_mid : 1, m);
   L.nscan = qat::esa_scan_wgs(L.n_mid > 0 ? L.n_mid : 1);
   L.ndec = qat::esa_decode_splits(p->batch, p->n_init, p->topk, p->window);
   qat::Carver c(ws);
-  L.qpart = c.take<double>((size_t)L.nsplit_q * L.rows * p->d_c);
-  L.qc = c.take<float>((size_t)L.rows * p->d_c);
-  L.qhi = c.take<qat::bf16>((size_t)L.rows * p->d_c);
-  L.qlo = c.take<qat::bf16>((size_t)L.rows * p->d_c);
+  L.qpart = c.take<double>((size_t)L.nsplit_q * L.rows * dcq);
+  L.qc = c.take<float>((size_t)L.rows * dcq);
+  L.qhi = c.take<qat::bf16>((size_t)L.rows * dcq);
+  L.qlo = c.take<qat::bf16>((size_t)L.rows * dcq);
   const size_t nm = (size_t)(L.n_mid > 0 ? L.n_mid : 1);
   if (m > 1) {
     L.rowmax_part = c.take<float>((size_t)L.rows * L.nkeysplit);
@@ -123,9 +130,9 @@ EsaLayout esa_layout(const qat_esa_params* p, void* ws) {
   L.keys = c.take<uint32_t>((size_t)B * nm);
   L.keylist = c.take<int32_t>((size_t)B * qat::esa_keylist_len(p->n_init, p->topk, p->window, m));
   if (m == 1) {
-    L.po = c.take<float>((size_t)B * L.ndec * D);
-    L.pm = c.take<float>((size_t)B * L.ndec * p->n_heads);
-    L.pl = c.take<float>((size_t)B * L.ndec * p->n_heads);
+    L.po = c.take<float>((size_t)p->batch * L.ndec * D);
+    L.pm = c.take<float>((size_t)p->batch * L.ndec * p->n_heads);
+    L.pl = c.take<float>((size_t)p->batch * L.ndec * p->n_heads);
   }
   L.bytes = c.bytes();
   return L;
@@ -383,11 +390,44 @@ QAT_EXPORT int esa_compress(const void* x, int64_t n, int64_t x_stride, int64_t 
   return hip_status(e, "esa_compress");
 }
 
+// Scoring, correction, importance, neighbour step and top-k of nsel
+// selections whose operands ScGeom g places (shared by the merged and the
+// per-head selection). q_hi / q_lo: bf16 query rows for the prefill passes
+// (q_lo NULL: one exact term); q_dec: the decode query rows (float32, or
+// bfloat16 when dec_bf16).
+static int esa_score_and_select(const qat_esa_params* p, const EsaLayout& L, const qat::bf16* q_hi,
+                                const qat::bf16* q_lo, const void* q_dec, bool dec_bf16, const qat::bf16* kc,
+                                const qat::ScGeom& g, int64_t nsel, int64_t dc, float tau, int32_t* sel,
+                                int32_t* n_sel, float* scores, hipStream_t s) {
+  // votes: temperature in log2 units (exp(tau x) = exp2(tau log2(e) x))
+  const bool votes = p->correction == QAT_CORR_VOTES;
+  const float tau2 = votes ? tau * 1.4426950408889634f : 0.f;
+  hipError_t e;
+  int mode;
+  if (p->chunk_len > 1) {
+    mode = 0;
+    qat::KTimer tm("esa_scores", s);
+    e = qat::launch_esa_prefill_scores(q_hi, q_lo, kc, g, nsel, p->chunk_len, L.mid0, L.n_mid, dc, p->clip, tau2,
+                                       L.rowmax_part, L.rowsum_part, L.rowmax, L.upart, s);
+  } else {
+    mode = votes ? 2 : 1;
+    qat::KTimer tm("esa_decode_scan", s);
+    e = qat::launch_esa_decode_scan(q_dec, dec_bf16, kc, g, nsel, L.mid0, L.n_mid, dc, tau2, L.sraw, L.smax, L.ssum,
+                                    s);
+  }
+  if (e != hipSuccess) return hip_status(e, "esa selection: scoring");
+  qat::KTimer tm("esa_topk", s);
+  e = qat::launch_esa_topk(mode, L.upart, L.nqsplit, L.sraw, L.smax, L.ssum, L.nscan, p->clip, tau2, nsel, L.n_mid,
+                           p->radius, p->topk, L.mid0, L.tk_hist, L.tk_cnt, L.keys, scores, sel, n_sel, s);
+  return hip_status(e, "esa selection: top-k");
+}
+
 QAT_EXPORT int esa_select(const qat_esa_params* p, const void* q, const void* Wq, const float* bq,
                           const void* kc_cache, int32_t* sel, int32_t* n_sel, float* scores, void* ws,
                           size_t ws_bytes, void* stream) {
   int rc = esa_check(p);
   if (rc) return rc;
+  if (p->per_head) return fail(QAT_EINVAL, "esa_select merges the heads: per_head must be 0 (esa_select_heads)");
   if (!q || !Wq || !kc_cache || !sel || !n_sel) return fail(QAT_EINVAL, "q, Wq, kc_cache, sel, n_sel must be non-NULL");
   if (((uintptr_t)q | (uintptr_t)Wq | (uintptr_t)kc_cache) % 16)
     return fail(QAT_EINVAL, "q, Wq and kc_cache must be 16-byte aligned");
@@ -407,27 +447,29 @@ QAT_EXPORT int esa_select(const qat_esa_params* p, const void* q, const void* Wq
   }
   if (e != hipSuccess) return hip_status(e, "esa_select: query compression");
   const qat::bf16* kc = (const qat::bf16*)kc_cache;
-  // votes: temperature in log2 units (exp(tau x) = exp2(tau log2(e) x))
-  const bool votes = p->correction == QAT_CORR_VOTES;
-  const float tau = p->vote_tau > 0.f ? p->vote_tau : 1.f / std::sqrt((float)p->d_c);
-  const float tau2 = votes ? tau * 1.4426950408889634f : 0.f;
-  int mode;
-  if (p->chunk_len > 1) {
-    mode = 0;
-    qat::KTimer tm("esa_scores", s);
-    e = qat::launch_esa_prefill_scores(L.qhi, L.qlo, kc, p->batch, p->chunk_len, p->ctx_len, L.mid0, L.n_mid,
-                                       p->d_c, p->clip, tau2, L.rowmax_part, L.rowsum_part, L.rowmax, L.upart, s);
-  } else {
-    mode = votes ? 2 : 1;
-    qat::KTimer tm("esa_decode_scan", s);
-    e = qat::launch_esa_decode_scan(L.qc, kc, p->batch, p->ctx_len, L.mid0, L.n_mid, p->d_c, tau2, L.sraw, L.smax,
-                                    L.ssum, s);
-  }
-  if (e != hipSuccess) return hip_status(e, "esa_select: scoring");
-  qat::KTimer tm("esa_topk", s);
-  e = qat::launch_esa_topk(mode, L.upart, L.nqsplit, L.sraw, L.smax, L.ssum, L.nscan, p->clip, tau2, p->batch,
-                           L.n_mid, p->radius, p->topk, L.mid0, L.tk_hist, L.tk_cnt, L.keys, scores, sel, n_sel, s);
-  return hip_status(e, "esa_select: top-k");
+  // q~ rows [B, m, d_c], compressed cache [B, T, d_c]
+  const qat::ScGeom g{p->chunk_len * p->d_c, 0, p->d_c, p->ctx_len * p->d_c, 0, p->d_c, 1};
+  return esa_score_and_select(p, L, L.qhi, L.qlo, L.qc, false, kc, g, p->batch, p->d_c, p->vote_tau > 0.f
+                              ? p->vote_tau : 1.f / std::sqrt((float)p->d_c), sel, n_sel, scores, s);
+}
+
+QAT_EXPORT int esa_select_heads(const qat_esa_params* p, const void* q, const void* k_cache, int32_t* sel,
+                                int32_t* n_sel, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  int rc = esa_check(p);
+  if (rc) return rc;
+  if (!p->per_head) return fail(QAT_EINVAL, "esa_select_heads selects per head: per_head must be 1");
+  if (!q || !k_cache || !sel || !n_sel) return fail(QAT_EINVAL, "q, k_cache, sel, n_sel must be non-NULL");
+  if (((uintptr_t)q | (uintptr_t)k_cache) % 16) return fail(QAT_EINVAL, "q and k_cache must be 16-byte aligned");
+  EsaLayout L = esa_layout(p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  L = esa_layout(p, ws);
+  const int64_t H = p->n_heads, d = p->head_dim;
+  // selection v = b H + h: q rows of head h in [B, m, H, d], K rows in [B, T, H, d]
+  const qat::ScGeom g{p->chunk_len * H * d, d, H * d, p->ctx_len * H * d, d, H * d, H};
+  const qat::bf16* qb = (const qat::bf16*)q;
+  return esa_score_and_select(p, L, qb, nullptr, q, true, (const qat::bf16*)k_cache, g, p->batch * H, d,
+                              p->vote_tau > 0.f ? p->vote_tau : 1.f / std::sqrt((float)d), sel, n_sel, scores,
+                              (hipStream_t)stream);
 }
 
 QAT_EXPORT int esa_sparse_attn(const qat_esa_params* p, const void* q, const void* k_cache, const void* v_cache,
@@ -443,18 +485,21 @@ QAT_EXPORT int esa_sparse_attn(const qat_esa_params* p, const void* q, const voi
   hipStream_t s = (hipStream_t)stream;
   const bool bf = p->dtype == QAT_BF16;
   hipError_t e;
+  const bool ph = p->per_head != 0;
   if (bf && p->chunk_len == 1 && qat::esa_decode_supported(p->n_heads, p->head_dim)) {
     qat::KTimer tm("esa_decode_attn", s);
     e = qat::launch_esa_decode_attn(q, k_cache, v_cache, sel, n_sel, L.po, L.pm, L.pl, out, lse, p->batch,
                                     p->n_heads, p->head_dim, p->ctx_len, p->chunk_start, p->n_init, p->window,
-                                    p->topk, p->scale, s);
+                                    p->topk, p->scale, ph, s);
   } else if (bf && p->ctx_len * p->n_heads * p->head_dim < (1ll << 31)) {
     // the matrix-core kernel addresses K/V rows of one sequence with 32-bit offsets
     qat::KTimer tm("esa_prefill_attn", s);
     e = qat::launch_esa_prefill_attn(q, k_cache, v_cache, sel, n_sel, L.keylist, out, lse, p->batch, p->n_heads,
                                      p->head_dim,
                                      p->ctx_len, p->chunk_start, p->chunk_len, p->n_init, p->window, p->topk,
-                                     p->scale, s);
+                                     p->scale, ph, s);
+  } else if (ph) {
+    return fail(QAT_EUNSUPPORTED, "per-head selection: no attention path for this shape");
   } else {
     qat::KTimer tm("esa_generic_attn", s);
     e = qat::launch_esa_generic(q, k_cache, v_cache, sel, n_sel, out, lse, bf, p->batch, p->n_heads,
@@ -469,7 +514,8 @@ QAT_EXPORT int esa_bwd_workspace_size(const qat_esa_params* p, size_t* bytes) {
   if (rc) return rc;
   if (!bytes) return fail(QAT_EINVAL, "bytes is NULL");
   qat::Carver c(nullptr);
-  c.take<int32_t>((size_t)p->batch * qat::esa_keylist_len(p->n_init, p->topk, p->window, p->chunk_len));
+  const int64_t nsel = p->per_head ? p->batch * p->n_heads : p->batch;
+  c.take<int32_t>((size_t)nsel * qat::esa_keylist_len(p->n_init, p->topk, p->window, p->chunk_len));
   c.take<float>((size_t)p->batch * p->chunk_len * p->n_heads);
   *bytes = c.bytes();
   return ok();
@@ -489,12 +535,13 @@ QAT_EXPORT int esa_sparse_attn_bwd(const qat_esa_params* p, const void* q, const
   if ((rc = esa_bwd_workspace_size(p, &need))) return rc;
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   qat::Carver c(ws);
-  int32_t* keylist = c.take<int32_t>((size_t)p->batch * qat::esa_keylist_len(p->n_init, p->topk, p->window,
-                                                                             p->chunk_len));
+  const int64_t nsel = p->per_head ? p->batch * p->n_heads : p->batch;
+  int32_t* keylist = c.take<int32_t>((size_t)nsel * qat::esa_keylist_len(p->n_init, p->topk, p->window,
+                                                                         p->chunk_len));
   float* delta = c.take<float>((size_t)p->batch * p->chunk_len * p->n_heads);
   hipError_t e = qat::launch_esa_bwd(q, k_cache, v_cache, sel, n_sel, dout, lse, keylist, dq, delta, dk, dv, p->batch,
                                      p->n_heads, p->head_dim, p->ctx_len, p->chunk_start, p->chunk_len, p->n_init,
-                                     p->window, p->topk, p->scale, (hipStream_t)stream);
+                                     p->window, p->topk, p->scale, p->per_head != 0, (hipStream_t)stream);
   return hip_status(e, "esa_sparse_attn_bwd");
 }
 

@@ -14,6 +14,8 @@
 //   j <  n_I + n_sel         -> sel[j - n_I]           (selected middle)
 //   j <  n_I + n_sel + n_L   -> L0 + (j - n_I - n_sel) (local window)
 // followed by the chunk's own keys [c0, t] under the causal mask.
+// With per-head selection (ph) head h of sequence b reads selection
+// v = b H + h (sel [B, H, topk], n_sel [B, H], one key list per (b, h)).
 #include <algorithm>
 
 #include "attn_core.h"
@@ -50,9 +52,9 @@ __device__ __forceinline__ EsaKeys esa_keys(const int32_t* sel, const int32_t* n
   return kl;
 }
 
-// Key positions of one sequence in attention order: the gathered keys
+// Key positions of one selection in attention order: the gathered keys
 // (initial, selected, local) then the chunk [c0, c0 + m). grid (cdiv(len, 256),
-// batch).
+// selections).
 __global__ void esa_keylist_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
                                    int32_t* __restrict__ keylist, int64_t stride, int topk, int64_t c0, int64_t m,
                                    int64_t n_init, int64_t window) {
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, const int32_t* __restrict__ keylist,
     int64_t keylist_stride, bf16* __restrict__ out, float* __restrict__ lse_out, int64_t H, int64_t ctx_len,
-    int64_t c0, int64_t m, int64_t n_init, int64_t window, int topk, float scale_log2) {
+    int64_t c0, int64_t m, int64_t n_init, int64_t window, int topk, float scale_log2, int ph) {
   QAT_FA_SMEM(D, sm);
   // logical id -> (row tile, head, sequence); the row tiles of one head are
   // adjacent and share an XCD (its L2 holds the head's gathered K/V)
@@ -101,7 +103,8 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
   const bf16* qrow = q + ((bi * m + (valid ? i : i0)) * H + h) * D;
   FaState<D> st;
   fa_init<D>(st, qrow, valid);
-  const EsaKeys kl = esa_keys(sel, n_sel, bi, topk, c0, n_init, window);
+  const int64_t lv = ph ? bi * H + h : bi;   // the selection this head reads
+  const EsaKeys kl = esa_keys(sel, n_sel, lv, topk, c0, n_init, window);
   const bf16* kb = kc + (bi * ctx_len * H + h) * D;
   const bf16* vb = vc + (bi * ctx_len * H + h) * D;
   // one key segment: the gathered keys (all before the chunk, never masked)
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
   // from the key list built by esa_keylist_kernel
   const int HD = (int)(H * D);
   const int ng = (int)kl.count();
-  const int32_t* lst = keylist + bi * keylist_stride;
+  const int32_t* lst = keylist + lv * keylist_stride;
   const int lim = ng + (valid ? (int)i : -1);        // this lane attends keys j <= lim
   const int wlim = ng + (int)(i0 + wave * 32);       // every lane of the wave attends j <= wlim
   const int nkeys = ng + (int)(i_last + 1);
@@ -172,17 +175,20 @@ __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, float* __restrict__ po,
     float* __restrict__ pm, float* __restrict__ pl, int64_t H, int64_t D, int64_t ctx_len, int64_t c0,
-    int64_t n_init, int64_t window, int topk, int nsplit, int kps, float scale_log2) {
+    int64_t n_init, int64_t window, int topk, int nsplit, int kps, float scale_log2, int ph) {
   const int64_t bi = blockIdx.y;
   const int split = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t HD = H * D;
-  const EsaKeys kl = esa_keys(sel, n_sel, bi, topk, c0, n_init, window);
+  const int lph = (int)(D / E);          // lanes per head
+  const int64_t e0 = (int64_t)tid * E;   // element offset in the row
+  const int64_t head = e0 / D;
+  // per-head selection: each head's lanes walk that head's list (all lists
+  // have the same length, min(topk, |M|) selected)
+  const EsaKeys kl = esa_keys(sel, n_sel, ph ? bi * H + head : bi, topk, c0, n_init, window);
   const int64_t nkeys = kl.count() + 1;   // + the query's own position c0
   const int64_t j0 = (int64_t)split * kps;
   const int64_t j1 = min(nkeys, j0 + kps);
-  const int lph = (int)(D / E);          // lanes per head
-  const int64_t e0 = (int64_t)tid * E;   // element offset in the row
   float qv[E], o[E];
   {
     const bf16* qr = q + bi * HD + e0;
@@ -246,7 +252,6 @@ __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
         vr[u][e] = vn[u][e];
       }
   }
-  const int64_t head = e0 / D;
   const int64_t pidx = (bi * nsplit + split) * H + head;
   float* dst = po + pidx * D + (e0 % D);
 #pragma unroll
@@ -260,7 +265,8 @@ __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
 __global__ void esa_decode_combine_kernel(const float* __restrict__ po, const float* __restrict__ pm,
                                           const float* __restrict__ pl, const int32_t* __restrict__ n_sel,
                                           bf16* __restrict__ out, float* __restrict__ lse_out, int64_t H, int64_t D,
-                                          int64_t c0, int64_t n_init, int64_t window, int nsplit_max, int kps) {
+                                          int64_t c0, int64_t n_init, int64_t window, int nsplit_max, int kps,
+                                          int ph) {
   const int64_t bi = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // element of the H*D row
   if (idx >= H * D) return;
@@ -268,7 +274,7 @@ __global__ void esa_decode_combine_kernel(const float* __restrict__ po, const fl
   // number of splits actually holding keys for this sequence
   int64_t n_i = min(n_init, c0), n_l = 0;
   if (c0 > n_init) n_l = c0 - max(n_init, c0 - window);
-  const int64_t nkeys = n_i + n_sel[bi] + n_l + 1;
+  const int64_t nkeys = n_i + n_sel[ph ? bi * H : bi] + n_l + 1;
   const int ns = (int)min((int64_t)nsplit_max, cdiv(nkeys, kps));
   // online log-sum-exp merge over the splits, 8 splits' loads in flight
   constexpr int U = 8;
@@ -312,10 +318,10 @@ int64_t esa_keylist_len(int64_t n_init, int64_t topk, int64_t window, int64_t m)
   return n_init + topk + window + m;
 }
 
-hipError_t launch_esa_keylist(const int32_t* sel, const int32_t* n_sel, int32_t* keylist, int64_t batch, int64_t c0,
+hipError_t launch_esa_keylist(const int32_t* sel, const int32_t* n_sel, int32_t* keylist, int64_t nsel, int64_t c0,
                               int64_t m, int64_t n_init, int64_t window, int topk, hipStream_t s) {
   const int64_t kls = esa_keylist_len(n_init, topk, window, m);
-  hipLaunchKernelGGL(esa_keylist_kernel, dim3((unsigned)cdiv(kls, 256), (unsigned)batch), dim3(256), 0, s, sel,
+  hipLaunchKernelGGL(esa_keylist_kernel, dim3((unsigned)cdiv(kls, 256), (unsigned)nsel), dim3(256), 0, s, sel,
                      n_sel, keylist, kls, topk, c0, m, n_init, window);
   return hipGetLastError();
 }
@@ -323,9 +329,10 @@ hipError_t launch_esa_keylist(const int32_t* sel, const int32_t* n_sel, int32_t*
 hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, const int32_t* sel,
                                    const int32_t* n_sel, int32_t* keylist, void* out, float* lse, int64_t batch,
                                    int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
-                                   int64_t window, int topk, float scale, hipStream_t s) {
+                                   int64_t window, int topk, float scale, bool per_head, hipStream_t s) {
   const int64_t kls = esa_keylist_len(n_init, topk, window, m);
-  hipLaunchKernelGGL(esa_keylist_kernel, dim3((unsigned)cdiv(kls, 256), (unsigned)batch), dim3(256), 0, s, sel,
+  const int64_t nsel = per_head ? batch * H : batch;
+  hipLaunchKernelGGL(esa_keylist_kernel, dim3((unsigned)cdiv(kls, 256), (unsigned)nsel), dim3(256), 0, s, sel,
                      n_sel, keylist, kls, topk, c0, m, n_init, window);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -336,7 +343,7 @@ hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, 
 #define QAT_ESA_PF(D_, L_)                                                                                  \
   launch_timed("esa_prefill_attn", esa_prefill_kernel<D_, L_>, grid, dim3(kThreads), (uint32_t)dyn, s,       \
                (const bf16*)q, (const bf16*)k, (const bf16*)v, sel, n_sel, (const int32_t*)keylist, kls,   \
-               (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2)
+               (bf16*)out, lse, H, ctx_len, c0, m, n_init, window, topk, sl2, per_head ? 1 : 0)
   if (D == 64) {
     if (lds) QAT_ESA_PF(64, true);
     else QAT_ESA_PF(64, false);
@@ -358,7 +365,7 @@ bool esa_decode_supported(int64_t H, int64_t D) {
 hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, const int32_t* sel,
                                   const int32_t* n_sel, float* po, float* pm, float* pl, void* out, float* lse,
                                   int64_t batch, int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t n_init,
-                                  int64_t window, int topk, float scale, hipStream_t s) {
+                                  int64_t window, int topk, float scale, bool per_head, hipStream_t s) {
   const int nsplit = esa_decode_splits(batch, n_init, topk, window);
   const int kps = esa_decode_keys_per_split(batch, n_init + topk + window + 1);
   dim3 grid((unsigned)nsplit, (unsigned)batch);
@@ -367,7 +374,7 @@ hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, c
 #define QAT_DEC(E_)                                                                                        \
   launch_timed("esa_decode_attn", esa_decode_attn_kernel<E_>, grid, dim3(256), 0, s, (const bf16*)q,       \
                (const bf16*)k, (const bf16*)v, sel, n_sel, po, pm, pl, H, D, ctx_len, c0, n_init, window, topk, \
-               nsplit, kps, sl2)
+               nsplit, kps, sl2, per_head ? 1 : 0)
   if (E == 8) QAT_DEC(8);
   else if (E == 16) QAT_DEC(16);
   else QAT_DEC(32);
@@ -376,7 +383,7 @@ hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, c
   if (e != hipSuccess) return e;
   dim3 g2((unsigned)cdiv(H * D, 256), (unsigned)batch);
   hipLaunchKernelGGL(esa_decode_combine_kernel, g2, dim3(256), 0, s, po, pm, pl, n_sel, (bf16*)out, lse, H, D, c0,
-                     n_init, window, nsplit, kps);
+                     n_init, window, nsplit, kps, per_head ? 1 : 0);
   return hipGetLastError();
 }
 

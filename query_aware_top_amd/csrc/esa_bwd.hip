@@ -25,7 +25,8 @@ namespace qat {
 
 constexpr int kEsaBwdRows = 32 * kBwdNW;
 
-// gathered keys of sequence bi (initial + selected + local)
+// gathered keys of selection lv (initial + selected + local); with per-head
+// selection (ph) head h of sequence b reads selection lv = b H + h
 __device__ __forceinline__ int esa_bwd_ngather(const int32_t* n_sel, int64_t bi, int64_t c0, int64_t n_init,
                                                int64_t window) {
   const int64_t ni = min(n_init, c0);
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const int32_t* __restrict__ keylist,
     int64_t kls, const int32_t* __restrict__ n_sel, float* __restrict__ dq, float* __restrict__ delta, int64_t H,
-    int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init, int64_t window, float scale) {
+    int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init, int64_t window, float scale, int ph) {
   QAT_FA_SMEM(D, sm);
   int64_t id = xcd_logical_id(blockIdx.x, gridDim.x);
   const int64_t ntile = cdiv(m, kEsaBwdRows);
@@ -53,9 +54,10 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_dq_kernel(
   const int64_t row = (bi * m + (valid ? i : i0)) * H + h;
   DqState<D> st;
   dq_init<D>(st, q + row * D, dout + row * D, lse[row], valid);
-  const int ng = esa_bwd_ngather(n_sel, bi, c0, n_init, window);
+  const int64_t lv = ph ? bi * H + h : bi;
+  const int ng = esa_bwd_ngather(n_sel, lv, c0, n_init, window);
   const int HD = (int)(H * D);
-  const int32_t* lst = keylist + bi * kls;
+  const int32_t* lst = keylist + lv * kls;
   const int lim = ng + (valid ? (int)i : -1);   // this lane attends list entries j <= lim
   dq_segment<D, kBwdNW>(st, sm, k + (bi * ctx_len * H + h) * D, v + (bi * ctx_len * H + h) * D,
                         ng + (int)(i_last + 1), scale * kLog2e, [=](int j) { return lst[j] * HD; },
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_kv_kernel(
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ keylist, int64_t kls, const int32_t* __restrict__ n_sel, float* __restrict__ dk,
     float* __restrict__ dv, int64_t H, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init, int64_t window,
-    float scale) {
+    float scale, int ph) {
   QAT_FA_SMEM(D, sm);
   extern __shared__ __align__(16) char eb_dyn[];   // beyond the 64 KiB of tile buffers
   float* s_lse = reinterpret_cast<float*>(eb_dyn);   // [2][64]
@@ -92,14 +94,15 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_kv_kernel(
   const int64_t kt = id % nkt;
   id /= nkt;
   const int64_t h = id % H, bi = id / H;
-  const int ng = esa_bwd_ngather(n_sel, bi, c0, n_init, window);
+  const int64_t lv = ph ? bi * H + h : bi;
+  const int ng = esa_bwd_ngather(n_sel, lv, c0, n_init, window);
   const int nlist = ng + (int)m;
   const int j0 = (int)kt * kKvKeys;
   if (j0 >= nlist) return;   // uniform
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = j0 + wave * 32 + (lane & 31);
   const bool kvalid = j < nlist;
-  const int32_t* lst = keylist + bi * kls;
+  const int32_t* lst = keylist + lv * kls;
   const int64_t pos = lst[kvalid ? j : j0];
   const int64_t krow = ((bi * ctx_len + pos) * H + h) * D;
   // rows: the chunk's queries of head h; a chunk key j >= ng is seen by
@@ -166,9 +169,9 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_kv_kernel(
 hipError_t launch_esa_bwd(const void* q, const void* k, const void* v, const int32_t* sel, const int32_t* n_sel,
                           const void* dout, const float* lse, int32_t* keylist, float* dq, float* delta, float* dk,
                           float* dv, int64_t batch, int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t m,
-                          int64_t n_init, int64_t window, int topk, float scale, hipStream_t s) {
+                          int64_t n_init, int64_t window, int topk, float scale, bool per_head, hipStream_t s) {
   const int64_t kls = esa_keylist_len(n_init, topk, window, m);
-  hipError_t e = launch_esa_keylist(sel, n_sel, keylist, batch, c0, m, n_init, window, topk, s);
+  hipError_t e = launch_esa_keylist(sel, n_sel, keylist, per_head ? batch * H : batch, c0, m, n_init, window, topk, s);
   if (e != hipSuccess) return e;
   static const bool lds_ok = [] {
     bool ok = hipFuncSetAttribute((const void*)esa_bwd_kv_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -186,13 +189,14 @@ hipError_t launch_esa_bwd(const void* q, const void* k, const void* v, const int
       KTimer tm("esa_bwd_dq", s);                                                                             \
       launch_timed("esa_bwd_dq", esa_bwd_dq_kernel<D_>, g_dq, dim3(64 * kBwdNW), 0, s, (const bf16*)q,        \
                    (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, (const int32_t*)keylist, kls, n_sel, \
-                   dq, delta, H, ctx_len, c0, m, n_init, window, scale);                                      \
+                   dq, delta, H, ctx_len, c0, m, n_init, window, scale, per_head ? 1 : 0);                    \
     }                                                                                                         \
     if ((e = hipGetLastError()) != hipSuccess) return e;                                                      \
     KTimer tm("esa_bwd_kv", s);                                                                               \
     launch_timed("esa_bwd_kv", esa_bwd_kv_kernel<D_>, g_kv, dim3(64 * kBwdNW), 1024, s, (const bf16*)q,       \
                  (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, (const float*)delta,                 \
-                 (const int32_t*)keylist, kls, n_sel, dk, dv, H, ctx_len, c0, m, n_init, window, scale);      \
+                 (const int32_t*)keylist, kls, n_sel, dk, dv, H, ctx_len, c0, m, n_init, window, scale,       \
+                 per_head ? 1 : 0);                                                                           \
   } while (0)
   if (D == 64) QAT_EB(64);
   else QAT_EB(128);

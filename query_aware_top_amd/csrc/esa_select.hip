@@ -23,6 +23,12 @@
 // selection tolerance. Decode scoring is a float32 matrix-vector stream
 // (HBM-bound). Top-k is an exact radix select on order-preserving uint32
 // keys with the lowest index winning ties.
+//
+// Per-head selection (the other arm of the write-up's ablation on head
+// merging): each (sequence, head) is its own selection, scored with the
+// head's uncompressed bf16 q and k rows (one bf16 term, products exact), so
+// the same kernels run over "selections" v = b H + h with the operands'
+// addresses given by ScGeom.
 #include <algorithm>
 
 #include "attn_core.h"
@@ -38,6 +44,7 @@ namespace qat {
 // other operand in registers; rows are stored with the attention engine's
 // chunk swizzle so the A-operand reads are bank-conflict free.
 constexpr int kScWaves = 4;
+
 constexpr int kScRows = 32 * kScWaves;   // register-held rows per workgroup
 
 // A operand (32 rows x 16 k) of sub-tile sb, k-step c, from a swizzled tile
@@ -60,10 +67,10 @@ __device__ __forceinline__ void vote_merge(float& m, float& l, float om, float o
   m = mm;
 }
 
-template <int DC, bool VOTE>
+template <int DC, bool VOTE, bool HILO>
 __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
-    const bf16* __restrict__ q_hi, const bf16* __restrict__ q_lo, const bf16* __restrict__ kc,
-    int64_t m, int64_t ctx_len, int64_t mid0, int64_t n_mid, int64_t keys_per_split, int nsplit,
+    const bf16* __restrict__ q_hi, const bf16* __restrict__ q_lo, const bf16* __restrict__ kc, ScGeom g,
+    int64_t m, int64_t mid0, int64_t n_mid, int64_t keys_per_split, int nsplit,
     float tau2, float* __restrict__ rowmax_part, float* __restrict__ rowsum_part) {
   __shared__ __align__(16) bf16 kt0[kKT * DC];
   __shared__ __align__(16) bf16 kt1[kKT * DC];
@@ -72,17 +79,18 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
   const int64_t bi = blockIdx.z;
   const int64_t qi = (int64_t)blockIdx.x * kScRows + wave * 32 + r32;
   const bool qvalid = qi < m;
-  const int64_t qrow = bi * m + (qvalid ? qi : 0);
+  const int64_t qofs = g.qoff(bi) + (qvalid ? qi : 0) * g.q_row;
   bf16x8 qh[DC / 16], ql[DC / 16];
 #pragma unroll
   for (int c = 0; c < DC / 16; ++c) {
-    qh[c] = *(const bf16x8*)(q_hi + qrow * DC + 16 * c + 8 * h);
-    ql[c] = *(const bf16x8*)(q_lo + qrow * DC + 16 * c + 8 * h);
+    qh[c] = *(const bf16x8*)(q_hi + qofs + 16 * c + 8 * h);
+    if constexpr (HILO) ql[c] = *(const bf16x8*)(q_lo + qofs + 16 * c + 8 * h);
   }
   const int64_t k0 = (int64_t)blockIdx.y * keys_per_split;
   const int n = (int)(min(n_mid, k0 + keys_per_split) - k0);
-  const bf16* kbase = kc + (bi * ctx_len + mid0 + k0) * DC;
-  auto row_ofs = [](int j) { return j * DC; };
+  const bf16* kbase = kc + g.koff(bi) + (mid0 + k0) * g.k_row;
+  const int krow = (int)g.k_row;
+  auto row_ofs = [krow](int j) { return j * krow; };
   const int nt = (n + kKT - 1) / kKT;
   float mx = -__builtin_inff(), lsum = 0.f;
   fa_issue_one<DC, kScWaves>(kt0, kbase, 0, n, row_ofs);
@@ -98,7 +106,7 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
       for (int c = 0; c < DC / 16; ++c) {
         const bf16x8 a = sc_a<DC>(tile, sb, c);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[c], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[c], acc, 0, 0, 0);
+        if constexpr (HILO) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[c], acc, 0, 0, 0);
       }
       const int base = t * kKT + sb * 32;
       if constexpr (VOTE) {
@@ -160,15 +168,15 @@ __global__ __launch_bounds__(256) void esa_rowmax_final_kernel(const float* __re
 // S = Q~ K~^T with the keys in registers, so each lane holds one key and 16
 // query rows per 32-query sub-tile; the corrected scores are summed in
 // float32 per sub-tile and in float64 across sub-tiles (fixed order).
-template <int DC, bool VOTE>
+template <int DC, bool VOTE, bool HILO>
 __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
     const bf16* __restrict__ q_hi, const bf16* __restrict__ q_lo, const float* __restrict__ rowmax,
-    const bf16* __restrict__ kc, int64_t m, int64_t ctx_len, int64_t mid0, int64_t n_mid,
+    const bf16* __restrict__ kc, ScGeom g, int64_t m, int64_t mid0, int64_t n_mid,
     int64_t rows_per_split, int nqsplit, float clip, float tau2, float* __restrict__ upart) {
   __shared__ __align__(16) bf16 qh0[kKT * DC];
   __shared__ __align__(16) bf16 qh1[kKT * DC];
-  __shared__ __align__(16) bf16 ql0[kKT * DC];
-  __shared__ __align__(16) bf16 ql1[kKT * DC];
+  __shared__ __align__(16) bf16 ql0[HILO ? kKT * DC : 8];
+  __shared__ __align__(16) bf16 ql1[HILO ? kKT * DC : 8];
   __shared__ __align__(16) float rm0[kKT];
   __shared__ __align__(16) float rm1[kKT];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -176,20 +184,21 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
   const int64_t bi = blockIdx.z;
   const int64_t key = (int64_t)blockIdx.x * kScRows + wave * 32 + r32;
   const bool kvalid = key < n_mid;
-  const bf16* kr = kc + (bi * ctx_len + mid0 + (kvalid ? key : 0)) * DC;
+  const bf16* kr = kc + g.koff(bi) + (mid0 + (kvalid ? key : 0)) * g.k_row;
   bf16x8 kf[DC / 16];
 #pragma unroll
   for (int c = 0; c < DC / 16; ++c) kf[c] = *(const bf16x8*)(kr + 16 * c + 8 * h);
   const int64_t i0 = (int64_t)blockIdx.y * rows_per_split;
   const int n = (int)(min(m, i0 + rows_per_split) - i0);
-  const bf16* hb = q_hi + (bi * m + i0) * DC;
-  const bf16* lb = q_lo + (bi * m + i0) * DC;
+  const bf16* hb = q_hi + g.qoff(bi) + i0 * g.q_row;
+  const bf16* lb = HILO ? q_lo + g.qoff(bi) + i0 * g.q_row : nullptr;
   const float* rb = rowmax + bi * m + i0;
-  auto row_ofs = [](int j) { return j * DC; };
+  const int qrow = (int)g.q_row;
+  auto row_ofs = [qrow](int j) { return j * qrow; };
   auto issue = [&](int t) {
     const int j0 = t * kKT;
     fa_issue_one<DC, kScWaves>((t & 1) ? qh1 : qh0, hb, j0, n, row_ofs);
-    fa_issue_one<DC, kScWaves>((t & 1) ? ql1 : ql0, lb, j0, n, row_ofs);
+    if constexpr (HILO) fa_issue_one<DC, kScWaves>((t & 1) ? ql1 : ql0, lb, j0, n, row_ofs);
     if (wave == 0) {
       const int j = min(j0 + lane, n - 1);
       __builtin_amdgcn_global_load_lds((const global_void*)(rb + j), (lds_void*)((t & 1) ? rm1 : rm0), 4, 0, 0);
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
 #pragma unroll
       for (int c = 0; c < DC / 16; ++c) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sc_a<DC>(th, sb, c), kf[c], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sc_a<DC>(tl, sb, c), kf[c], acc, 0, 0, 0);
+        if constexpr (HILO) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sc_a<DC>(tl, sb, c), kf[c], acc, 0, 0, 0);
       }
       const int base = t * kKT + sb * 32;
       float part = 0.f;
@@ -239,9 +248,9 @@ constexpr int kScanUnroll = 8;
 // workgroup maxima. DC/8 lanes per key, 8 elements (16 B) per lane.
 // VOTE: also the workgroup's sum of exp2(tau2 (s - workgroup max)), counted
 // once per key (by the key's first lane).
-template <int DC, bool VOTE>
+template <int DC, bool VOTE, typename QT>
 __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
-    const float* __restrict__ qc, const bf16* __restrict__ kc, int64_t ctx_len, int64_t mid0, int64_t n_mid,
+    const QT* __restrict__ qc, const bf16* __restrict__ kc, ScGeom g, int64_t mid0, int64_t n_mid,
     int64_t keys_per_wg, float tau2, float* __restrict__ s_out, float* __restrict__ smax_part,
     float* __restrict__ ssum_part) {
   constexpr int LPK = DC / 8;          // lanes per key
@@ -252,10 +261,10 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
   const int sub = tid % LPK;
   float qv[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) qv[j] = qc[bi * DC + sub * 8 + j];
+  for (int j = 0; j < 8; ++j) qv[j] = (float)qc[g.qoff(bi) + sub * 8 + j];
   const int64_t k0 = (int64_t)blockIdx.x * keys_per_wg;
   const int64_t k1 = min(n_mid, k0 + keys_per_wg);
-  const bf16* kbase = kc + (bi * ctx_len + mid0) * DC;
+  const bf16* kbase = kc + g.koff(bi) + mid0 * g.k_row;
   float mx = -__builtin_inff(), lsum = 0.f;
   // kScanUnroll keys per lane group in flight at once
   constexpr int U = kScanUnroll;
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t key = min(kb + (int64_t)u * KPW + tid / LPK, k1 - 1);
-      kv[u] = *(const bf16x8*)(kbase + key * DC + sub * 8);
+      kv[u] = *(const bf16x8*)(kbase + key * g.k_row + sub * 8);
     }
     float acc[U];
 #pragma unroll
@@ -611,8 +620,21 @@ int esa_scan_wgs(int64_t n_mid) {
   return (int)(w < 1 ? 1 : w);
 }
 
-hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const bf16* kc, int64_t batch, int64_t m,
-                                     int64_t ctx_len, int64_t mid0, int64_t n_mid, int64_t d_c, float clip,
+template <int DC, bool VOTE, bool HILO>
+static void launch_scores_dc(const bf16* q_hi, const bf16* q_lo, const bf16* kc, const ScGeom& g, dim3 g1, dim3 g2,
+                             int64_t m, int64_t mid0, int64_t n_mid, int64_t kps, int ks_eff, int64_t rps, int qs_eff,
+                             int64_t rows, float clip, float tau2, float* rowmax_part, float* rowsum_part,
+                             float* rowmax, float* upart, hipStream_t s) {
+  hipLaunchKernelGGL((esa_rowmax_kernel<DC, VOTE, HILO>), g1, dim3(64 * kScWaves), 0, s, q_hi, q_lo, kc, g, m, mid0,
+                     n_mid, kps, ks_eff, tau2, rowmax_part, rowsum_part);
+  hipLaunchKernelGGL(esa_rowmax_final_kernel<VOTE>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s, rowmax_part,
+                     rowsum_part, ks_eff, rows, tau2, rowmax);
+  hipLaunchKernelGGL((esa_colsum_kernel<DC, VOTE, HILO>), g2, dim3(64 * kScWaves), 0, s, q_hi, q_lo, rowmax, kc, g,
+                     m, mid0, n_mid, rps, qs_eff, clip, tau2, upart);
+}
+
+hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const bf16* kc, const ScGeom& g,
+                                     int64_t nsel, int64_t m, int64_t mid0, int64_t n_mid, int64_t dc, float clip,
                                      float tau2, float* rowmax_part, float* rowsum_part, float* rowmax,
                                      float* upart, hipStream_t s) {
   if (n_mid <= 0) return hipSuccess;
@@ -620,52 +642,33 @@ hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const b
   const int ks = esa_key_splits(n_mid, m);
   const int64_t kps = cdiv(cdiv(n_mid, ks), kKT) * kKT;
   const int ks_eff = (int)cdiv(n_mid, kps);
-  dim3 g1((unsigned)cdiv(m, kScRows), (unsigned)ks_eff, (unsigned)batch);
-#define QAT_RM(DC_)                                                                                       \
-  do {                                                                                                    \
-    if (vote)                                                                                             \
-      hipLaunchKernelGGL((esa_rowmax_kernel<DC_, true>), g1, dim3(64 * kScWaves), 0, s, q_hi, q_lo, kc, m,  \
-                         ctx_len, mid0, n_mid, kps, ks_eff, tau2, rowmax_part, rowsum_part);              \
-    else                                                                                                  \
-      hipLaunchKernelGGL((esa_rowmax_kernel<DC_, false>), g1, dim3(64 * kScWaves), 0, s, q_hi, q_lo, kc, m, \
-                         ctx_len, mid0, n_mid, kps, ks_eff, tau2, rowmax_part, rowsum_part);              \
-  } while (0)
-  switch (d_c) {
-    case 32: QAT_RM(32); break;
-    case 64: QAT_RM(64); break;
-    case 128: QAT_RM(128); break;
-    default: QAT_RM(256); break;
-  }
-#undef QAT_RM
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (vote)
-    hipLaunchKernelGGL(esa_rowmax_final_kernel<true>, dim3((unsigned)cdiv(batch * m, 4)), dim3(256), 0, s,
-                       rowmax_part, rowsum_part, ks_eff, batch * m, tau2, rowmax);
-  else
-    hipLaunchKernelGGL(esa_rowmax_final_kernel<false>, dim3((unsigned)cdiv(batch * m, 4)), dim3(256), 0, s,
-                       rowmax_part, rowsum_part, ks_eff, batch * m, tau2, rowmax);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 g1((unsigned)cdiv(m, kScRows), (unsigned)ks_eff, (unsigned)nsel);
   const int qs = esa_query_splits(n_mid, m);
   const int64_t rps = cdiv(cdiv(m, qs), kKT) * kKT;
   const int qs_eff = (int)cdiv(m, rps);
-  dim3 g2((unsigned)cdiv(n_mid, kScRows), (unsigned)qs_eff, (unsigned)batch);
-#define QAT_CS(DC_)                                                                                       \
-  do {                                                                                                    \
-    if (vote)                                                                                             \
-      hipLaunchKernelGGL((esa_colsum_kernel<DC_, true>), g2, dim3(64 * kScWaves), 0, s, q_hi, q_lo, rowmax, \
-                         kc, m, ctx_len, mid0, n_mid, rps, qs_eff, clip, tau2, upart);                    \
-    else                                                                                                  \
-      hipLaunchKernelGGL((esa_colsum_kernel<DC_, false>), g2, dim3(64 * kScWaves), 0, s, q_hi, q_lo,        \
-                         rowmax, kc, m, ctx_len, mid0, n_mid, rps, qs_eff, clip, tau2, upart);            \
+  const dim3 g2((unsigned)cdiv(n_mid, kScRows), (unsigned)qs_eff, (unsigned)nsel);
+#define QAT_SC(DC_, HL_)                                                                                       \
+  do {                                                                                                         \
+    if (vote)                                                                                                  \
+      launch_scores_dc<DC_, true, HL_>(q_hi, q_lo, kc, g, g1, g2, m, mid0, n_mid, kps, ks_eff, rps, qs_eff,    \
+                                       nsel * m, clip, tau2, rowmax_part, rowsum_part, rowmax, upart, s);      \
+    else                                                                                                       \
+      launch_scores_dc<DC_, false, HL_>(q_hi, q_lo, kc, g, g1, g2, m, mid0, n_mid, kps, ks_eff, rps, qs_eff,   \
+                                        nsel * m, clip, tau2, rowmax_part, rowsum_part, rowmax, upart, s);     \
   } while (0)
-  switch (d_c) {
-    case 32: QAT_CS(32); break;
-    case 64: QAT_CS(64); break;
-    case 128: QAT_CS(128); break;
-    default: QAT_CS(256); break;
+  if (q_lo) {
+    switch (dc) {
+      case 32: QAT_SC(32, true); break;
+      case 64: QAT_SC(64, true); break;
+      case 128: QAT_SC(128, true); break;
+      default: QAT_SC(256, true); break;
+    }
+  } else if (dc == 64) {
+    QAT_SC(64, false);
+  } else {
+    QAT_SC(128, false);
   }
-#undef QAT_CS
+#undef QAT_SC
   return hipGetLastError();
 }
 
@@ -675,29 +678,37 @@ int esa_prefill_qsplits_eff(int64_t n_mid, int64_t m) {
   return (int)cdiv(m, rps);
 }
 
-hipError_t launch_esa_decode_scan(const float* qc, const bf16* kc, int64_t batch, int64_t ctx_len, int64_t mid0,
-                                  int64_t n_mid, int64_t d_c, float tau2, float* s_out, float* smax_part,
-                                  float* ssum_part, hipStream_t s) {
+template <int DC, typename QT>
+static void launch_scan_dc(const QT* q, const bf16* kc, const ScGeom& g, dim3 grid, int64_t mid0, int64_t n_mid,
+                           int64_t kpw, float tau2, float* s_out, float* smax_part, float* ssum_part, hipStream_t s) {
+  if (tau2 > 0.f)
+    hipLaunchKernelGGL((esa_decode_scan_kernel<DC, true, QT>), grid, dim3(256), 0, s, q, kc, g, mid0, n_mid, kpw,
+                       tau2, s_out, smax_part, ssum_part);
+  else
+    hipLaunchKernelGGL((esa_decode_scan_kernel<DC, false, QT>), grid, dim3(256), 0, s, q, kc, g, mid0, n_mid, kpw,
+                       tau2, s_out, smax_part, ssum_part);
+}
+
+hipError_t launch_esa_decode_scan(const void* q, bool q_bf16, const bf16* kc, const ScGeom& g, int64_t nsel,
+                                  int64_t mid0, int64_t n_mid, int64_t dc, float tau2, float* s_out,
+                                  float* smax_part, float* ssum_part, hipStream_t s) {
   if (n_mid <= 0) return hipSuccess;
   const int nw = esa_scan_wgs(n_mid);
   const int64_t kpw = cdiv(n_mid, nw);
-  dim3 grid((unsigned)nw, (unsigned)batch);
-#define QAT_DS(DC_)                                                                                        \
-  do {                                                                                                     \
-    if (tau2 > 0.f)                                                                                        \
-      hipLaunchKernelGGL((esa_decode_scan_kernel<DC_, true>), grid, dim3(256), 0, s, qc, kc, ctx_len, mid0,  \
-                         n_mid, kpw, tau2, s_out, smax_part, ssum_part);                                   \
-    else                                                                                                   \
-      hipLaunchKernelGGL((esa_decode_scan_kernel<DC_, false>), grid, dim3(256), 0, s, qc, kc, ctx_len, mid0, \
-                         n_mid, kpw, tau2, s_out, smax_part, ssum_part);                                   \
-  } while (0)
-  switch (d_c) {
-    case 32: QAT_DS(32); break;
-    case 64: QAT_DS(64); break;
-    case 128: QAT_DS(128); break;
-    default: QAT_DS(256); break;
+  const dim3 grid((unsigned)nw, (unsigned)nsel);
+  const float* qf = (const float*)q;
+  const bf16* qb = (const bf16*)q;
+  if (q_bf16) {
+    if (dc == 64) launch_scan_dc<64>(qb, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s);
+    else launch_scan_dc<128>(qb, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s);
+  } else {
+    switch (dc) {
+      case 32: launch_scan_dc<32>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s); break;
+      case 64: launch_scan_dc<64>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s); break;
+      case 128: launch_scan_dc<128>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s); break;
+      default: launch_scan_dc<256>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s); break;
+    }
   }
-#undef QAT_DS
   return hipGetLastError();
 }
 

@@ -95,16 +95,30 @@ hipError_t launch_esa_generic(const void* q, const void* k, const void* v, const
 int esa_key_splits(int64_t n_mid, int64_t m);
 int esa_prefill_qsplits_eff(int64_t n_mid, int64_t m);
 int esa_scan_wgs(int64_t n_mid);
-// tau2 > 0: the softmax-vote reading of the correction at temperature
-// tau2 / log2(e) (rowsum_part / ssum_part hold the per-split exp sums);
-// tau2 = 0: the clamp reading.
-hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const bf16* kc, int64_t batch, int64_t m,
-                                     int64_t ctx_len, int64_t mid0, int64_t n_mid, int64_t d_c, float clip,
+// Where selection v's scoring operands live: q rows at
+// q + (v / vh) q_outer + (v % vh) q_inner + i q_row, key rows likewise.
+// Merged heads: one selection per sequence, vh = 1, rows of d_c elements
+// (q~ [B, m, d_c], compressed cache [B, T, d_c]). Per head: one selection per
+// (sequence, head), vh = H, q [B, m, H, d] and K [B, T, H, d], rows of H d.
+struct ScGeom {
+  int64_t q_outer, q_inner, q_row;
+  int64_t k_outer, k_inner, k_row;
+  int64_t vh;
+  __device__ __forceinline__ int64_t qoff(int64_t v) const { return (v / vh) * q_outer + (v % vh) * q_inner; }
+  __device__ __forceinline__ int64_t koff(int64_t v) const { return (v / vh) * k_outer + (v % vh) * k_inner; }
+};
+// nsel selections; dc: the scored width (d_c, or d per head). q_lo NULL:
+// q is exactly bf16 (one term). tau2 > 0: the softmax-vote reading of the
+// correction at temperature tau2 / log2(e) (rowsum_part / ssum_part hold the
+// per-split exp sums); tau2 = 0: the clamp reading.
+hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const bf16* kc, const ScGeom& g,
+                                     int64_t nsel, int64_t m, int64_t mid0, int64_t n_mid, int64_t dc, float clip,
                                      float tau2, float* rowmax_part, float* rowsum_part, float* rowmax,
                                      float* upart, hipStream_t s);
-hipError_t launch_esa_decode_scan(const float* qc, const bf16* kc, int64_t batch, int64_t ctx_len, int64_t mid0,
-                                  int64_t n_mid, int64_t d_c, float tau2, float* s_out, float* smax_part,
-                                  float* ssum_part, hipStream_t s);
+// q: float32 (q_bf16 false) or bfloat16 rows
+hipError_t launch_esa_decode_scan(const void* q, bool q_bf16, const bf16* kc, const ScGeom& g, int64_t nsel,
+                                  int64_t mid0, int64_t n_mid, int64_t dc, float tau2, float* s_out,
+                                  float* smax_part, float* ssum_part, hipStream_t s);
 int esa_topk_slices(int64_t n_mid);
 int esa_topk_max_radius();
 // hist: batch*3*2048 int32, wgcnt: batch*esa_topk_slices(n_mid) int2 (scratch)
@@ -122,10 +136,10 @@ int64_t esa_keylist_len(int64_t n_init, int64_t topk, int64_t window, int64_t m)
 hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, const int32_t* sel,
                                    const int32_t* n_sel, int32_t* keylist, void* out, float* lse, int64_t batch,
                                    int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t m, int64_t n_init,
-                                   int64_t window, int topk, float scale, hipStream_t s);
-// keylist [batch, esa_keylist_len]: per sequence the gathered key positions
+                                   int64_t window, int topk, float scale, bool per_head, hipStream_t s);
+// keylist [nsel, esa_keylist_len]: per selection the gathered key positions
 // (initial, selected, local) then the chunk's positions
-hipError_t launch_esa_keylist(const int32_t* sel, const int32_t* n_sel, int32_t* keylist, int64_t batch, int64_t c0,
+hipError_t launch_esa_keylist(const int32_t* sel, const int32_t* n_sel, int32_t* keylist, int64_t nsel, int64_t c0,
                               int64_t m, int64_t n_init, int64_t window, int topk, hipStream_t s);
 
 // ---- CCA-style core-token attention (cca.hip), bfloat16 -------------------
@@ -145,11 +159,13 @@ hipError_t launch_cca_attn(const void* q, const void* k, const void* v, const vo
 hipError_t launch_esa_bwd(const void* q, const void* k, const void* v, const int32_t* sel, const int32_t* n_sel,
                           const void* dout, const float* lse, int32_t* keylist, float* dq, float* delta, float* dk,
                           float* dv, int64_t batch, int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t m,
-                          int64_t n_init, int64_t window, int topk, float scale, hipStream_t s);
+                          int64_t n_init, int64_t window, int topk, float scale, bool per_head,
+                          hipStream_t s);
 
 hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, const int32_t* sel,
                                   const int32_t* n_sel, float* po, float* pm, float* pl, void* out, float* lse,
                                   int64_t batch, int64_t H, int64_t D, int64_t ctx_len, int64_t c0, int64_t n_init,
-                                  int64_t window, int topk, float scale, hipStream_t s);
+                                  int64_t window, int topk, float scale, bool per_head,
+                                  hipStream_t s);
 
 }  // namespace qat

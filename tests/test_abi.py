@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import query_aware_top_amd as qat
 from query_aware_top_amd import _binding as B
@@ -103,6 +104,9 @@ def test_moba_params_validation(lib, kw, rc):
     (dict(clip=0.0), QAT_EINVAL),
     (dict(radius=-1), QAT_EINVAL),
     (dict(scale=0.0), QAT_EINVAL),
+    (dict(per_head=True), QAT_OK),
+    (dict(per_head=True, d_c=48), QAT_OK),                        # d_c is unused per head
+    (dict(per_head=True, dtype=torch.float32), QAT_EUNSUPPORTED),
 ])
 def test_esa_params_validation(lib, kw, rc):
     got, n = _size(lib, "esa_workspace_size", _esa(**kw))
@@ -147,6 +151,25 @@ def test_null_pointers_are_rejected(lib):
                         ctypes.c_size_t(1 << 30), ctypes.c_void_p(0))
     assert rc == QAT_EINVAL
     assert lib.moba_block_select(None, dummy, dummy, dummy, dummy, ctypes.c_size_t(0), None) == QAT_EINVAL
+
+
+def test_per_head_flag_picks_the_selection_entry(lib):
+    """esa_select merges the heads (per_head 0), esa_select_heads selects
+    per head (per_head 1); the other combination and per_head values other
+    than 0 / 1 are rejected before any device work. The per-head gradient
+    workspace holds one key list per (sequence, head)."""
+    dummy = ctypes.c_void_p(0x1000)
+    big = ctypes.c_size_t(1 << 40)
+    pm, ph = _esa(), _esa(per_head=True)
+    assert lib.esa_select(ctypes.byref(ph), dummy, dummy, None, dummy, dummy, dummy, None, dummy, big,
+                          ctypes.c_void_p(0)) == QAT_EINVAL
+    assert lib.esa_select_heads(ctypes.byref(pm), dummy, dummy, dummy, dummy, None, dummy, big,
+                                ctypes.c_void_p(0)) == QAT_EINVAL
+    bad = _esa()
+    bad.per_head = 2
+    assert _size(lib, "esa_workspace_size", bad)[0] == QAT_EINVAL
+    assert _size(lib, "esa_workspace_size", ph)[0] == QAT_OK
+    assert _size(lib, "esa_bwd_workspace_size", ph)[1] > _size(lib, "esa_bwd_workspace_size", pm)[1]
 
 
 def test_compress_validation(lib):
