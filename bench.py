@@ -14,7 +14,8 @@ Other workloads (--workload): moba_fp32_4k, esa_prefill_64k,
 esa_decode_128k, moba_long_512k, moba_decode_128k, moba_bwd_32k and esa_bwd_64k (gradients), cca_64k
 (CCA-style core-token attention), and
 esa_prefill_64k_votes /
-esa_decode_128k_votes (the softmax-vote reading of ESA's score correction).
+esa_decode_128k_votes (the softmax-vote reading of ESA's score correction),
+esa_prefill_64k_heads / esa_decode_128k_heads (one selection per head).
 """
 from __future__ import annotations
 
@@ -62,6 +63,7 @@ STAGE_SOURCES = {
     "cca_attn": ["cca.hip", "attn_core.h"],
     "esa_compress*": ["compress.hip"],
     "esa_scores": ["esa_select.hip"],
+    "esa_colsum": ["esa_select.hip"],
     "esa_topk": ["esa_select.hip"],
     "esa_decode_scan": ["esa_select.hip"],
     "esa_prefill_attn": ["esa_attn.hip", "attn_core.h"],
@@ -517,7 +519,7 @@ class EsaBwdWorkload(Workload):
 
 class EsaWorkload(Workload):
     def __init__(self, name, seed, batch, T, m, H, d, d_c, n_init, W, topk, radius, clip, needles=0,
-                 correction="clamp"):
+                 correction="clamp", per_head=False):
         import query_aware_top_amd as qat
         import synth
         self.qat = qat
@@ -534,35 +536,44 @@ class EsaWorkload(Workload):
                 val = (self.q[bi, 0].to(torch.float64) * 0.375).to(dtype)
                 for t in pos:
                     self.k[bi, t] = val
-        self.Wq = synth.compression_weights(seed, d_c, H * d, synth.gen.TID_W, dtype, "cuda")
-        self.Wk = self.Wq
         self.correction = correction
+        self.per_head = per_head
         self.p = qat.esa_params(batch=batch, n_heads=H, head_dim=d, d_c=d_c, ctx_len=T, chunk_start=self.c0,
                                 chunk_len=m, n_init=n_init, window=W, topk=topk, radius=radius, clip=clip,
-                                correction=correction)
-        # compressed-key cache of the tokens before the chunk: state written by
-        # earlier steps (untimed prologue)
-        self.kc = torch.zeros(batch, T, d_c, dtype=dtype, device="cuda")
-        qat.esa_compress(self.k.view(batch * T, H * d), self.Wk, out=self.kc.view(batch * T, d_c))
+                                correction=correction, per_head=per_head)
         self.ws = torch.empty(qat.esa_workspace_size(self.p), dtype=torch.uint8, device="cuda")
-        import ctypes
-        nb = ctypes.c_size_t(0)
-        qat.lib().esa_compress_workspace_size(batch * m, H * d, d_c, ctypes.byref(nb))
-        self.ws_c = torch.empty(max(nb.value, 256), dtype=torch.uint8, device="cuda")
-        self.sel = torch.empty(batch, topk, dtype=torch.int32, device="cuda")
-        self.n_sel = torch.empty(batch, dtype=torch.int32, device="cuda")
+        if not per_head:
+            self.Wq = synth.compression_weights(seed, d_c, H * d, synth.gen.TID_W, dtype, "cuda")
+            self.Wk = self.Wq
+            # compressed-key cache of the tokens before the chunk: state written
+            # by earlier steps (untimed prologue)
+            self.kc = torch.zeros(batch, T, d_c, dtype=dtype, device="cuda")
+            qat.esa_compress(self.k.view(batch * T, H * d), self.Wk, out=self.kc.view(batch * T, d_c))
+            import ctypes
+            nb = ctypes.c_size_t(0)
+            qat.lib().esa_compress_workspace_size(batch * m, H * d, d_c, ctypes.byref(nb))
+            self.ws_c = torch.empty(max(nb.value, 256), dtype=torch.uint8, device="cuda")
+        nsel = (batch, H) if per_head else (batch,)
+        self.sel = torch.empty(*nsel, topk, dtype=torch.int32, device="cuda")
+        self.n_sel = torch.empty(*nsel, dtype=torch.int32, device="cuda")
         self.out = torch.empty(batch, m, H, d, dtype=dtype, device="cuda")
         self.lse = torch.empty(batch, m, H, dtype=torch.float32, device="cuda")
+        self.n_mid = max(n_init, self.c0 - W) - n_init if self.c0 > n_init else 0
         if m == 1:
             self.unit, self.higher_is_better = "us/step", False
-            self.dominant, self.bound = "esa_decode_attn", "hbm"
+            self.dominant, self.bound = ("esa_decode_scan" if per_head else "esa_decode_attn"), "hbm"
         else:
             self.unit = "query-tokens/s"
-            self.dominant, self.bound = "esa_prefill_attn", "mfma"
+            self.dominant, self.bound = ("esa_colsum" if per_head else "esa_prefill_attn"), "mfma"
 
     def step(self):
         qat = self.qat
         B, T, H, d, m = self.B, self.T, self.H, self.d, self.m
+        if self.per_head:   # one selection per (sequence, head) from the raw q, k; then attention
+            qat.esa_select_heads(self.p, self.q, self.k, sel=self.sel, n_sel=self.n_sel, ws=self.ws)
+            qat.esa_sparse_attn(self.p, self.q, self.k, self.v, self.sel, self.n_sel, out=self.out, lse=self.lse,
+                                ws=self.ws)
+            return
         # compress the chunk's new keys into the cache
         qat.esa_compress(self.k.view(B * T, H * d)[self.c0:], self.Wk, out=self.kc.view(B * T, -1)[self.c0:],
                          n=B if m == 1 else m, x_stride=T * H * d if m == 1 else H * d,
@@ -577,9 +588,14 @@ class EsaWorkload(Workload):
     def n_keys(self):
         n_i = min(self.n_init, self.c0)
         n_l = self.c0 - max(self.n_init, self.c0 - self.W) if self.c0 > self.n_init else 0
-        return n_i + int(self.n_sel[0]) + n_l
+        return n_i + int(self.n_sel.flatten()[0]) + n_l
 
     def dominant_work(self):
+        if self.per_head:
+            if self.m == 1:   # decode scan: every head's K row of every middle token, + the query rows
+                return self.B * self.H * self.n_mid * self.d * 2 + self.B * self.H * self.d * 2
+            # second scoring pass: q.k of every (query, middle token, head), 2 d flop
+            return 2 * self.m * self.n_mid * self.H * self.d * self.B
         if self.m == 1:   # gathered K and V rows of every head + q and out
             return self.B * (self.n_keys() + 1) * self.H * self.d * 2 * 2 + 2 * self.B * self.H * self.d * 2
         g = self.n_keys()
@@ -589,9 +605,12 @@ class EsaWorkload(Workload):
     def config(self):
         return {"workload": self.name, "batch": self.B, "ctx_len": self.T, "chunk_len": self.m,
                 "n_heads": self.H, "head_dim": self.d, "d_c": self.d_c, "n_init": self.n_init,
-                "topk": self.topk, "window": self.W, "correction": self.correction}
+                "topk": self.topk, "window": self.W, "correction": self.correction,
+                "selection": "per_head" if self.per_head else "merged_heads"}
 
     def cpu_baseline(self, budget_s=12.0):
+        if self.per_head:
+            return self._cpu_baseline_heads(budget_s)
         import numpy as np
         from oracle import esa as oesa
         t0 = time.perf_counter()
@@ -628,6 +647,51 @@ class EsaWorkload(Workload):
                           f"BLAS threads for the matrix products, one process; {el:.1f} s"}
 
 
+    def _cpu_baseline_heads(self, budget_s):
+        """Per-head selection of sequence 0 for as many heads as fit in about
+        two thirds of the budget (at least one), scaled to all heads; then
+        attention rows over per-head lists (the computed heads' lists reused
+        for the others, which costs the same), scaled to the chunk."""
+        import numpy as np
+        from oracle import esa as oesa
+        bi = 0
+        _, M, _ = oesa.partition(self.c0, self.n_init, self.W)
+        qn = self.q[bi].to("cpu").to(torch.float64).numpy()
+        t0 = time.perf_counter()
+        sels = []
+        while len(sels) < self.H and (time.perf_counter() - t0 < budget_s * 2 / 3 or not sels):
+            h = len(sels)
+            kh = self.k[bi, int(M[0]):int(M[-1]) + 1, h:h + 1].to("cpu").to(torch.float64).numpy() if M.size else None
+
+            class _View:   # K[M, 0] of the one head loaded above
+                def __getitem__(self, idx, kh=kh):
+                    return kh[np.asarray(idx[0]) - int(M[0]), 0]
+
+            s, _ = oesa.select_heads(qn[:, h:h + 1], _View(), self.c0, self.n_init, self.W, self.topk,
+                                     self.p.radius, self.p.clip, correction=self.correction)
+            sels.append(s[0])
+        t_sel = (time.perf_counter() - t0) * self.H / len(sels)
+        nh = len(sels)
+        all_sels = [sels[h % nh] for h in range(self.H)]
+        kk, vv = _GpuRows(self.k[bi]), _GpuRows(self.v[bi])
+        order = np.random.default_rng(0).permutation(self.m)
+        t1 = time.perf_counter()
+        rows = 0
+        while rows < self.m and (time.perf_counter() - t0 < budget_s or rows < 1):
+            oesa.attend(qn, kk, vv, all_sels, self.c0, self.n_init, self.W, self.p.scale, rows=[int(order[rows])])
+            rows += 1
+        t_att = (time.perf_counter() - t1) / rows * self.m
+        el = time.perf_counter() - t0
+        cores = _blas_threads()
+        what = (f"per-head selection of sequence 0 for {nh} of {self.H} heads, scaled to all heads, plus "
+                f"attention for {rows} of {self.m} rows, scaled to the chunk")
+        if self.m == 1:
+            return {"value": (t_sel + t_att) * 1e6 * self.B, "unit": "us/step", "cores": cores, "kind": "oracle",
+                    "sample": f"{what}, times {self.B} sequences; float64 numpy, one process; {el:.1f} s"}
+        return {"value": self.m / (t_sel + t_att), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+                "sample": f"{what}; float64 numpy, BLAS threads for the matrix products, one process; {el:.1f} s"}
+
+
 def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -643,8 +707,11 @@ class _GpuRows:
 
     def __getitem__(self, idx):
         import numpy as np
+        rest = ()
+        if isinstance(idx, tuple):   # rows, then an index into the remaining dimensions
+            idx, rest = idx[0], idx[1:]
         ix = torch.as_tensor(np.asarray(idx), device=self.t.device, dtype=torch.long)
-        return self.t.index_select(0, ix).to("cpu").to(torch.float64).numpy()
+        return self.t.index_select(0, ix)[(slice(None),) + rest].to("cpu").to(torch.float64).numpy()
 
 
 def make(name):
@@ -671,6 +738,11 @@ def make(name):
     if name == "esa_decode_128k_votes":
         return EsaWorkload(name, 4, 16, 131072, 1, 32, 128, 128, 128, 4096, 2048, 2, 48.0, needles=16,
                            correction="votes")
+    if name == "esa_prefill_64k_heads":
+        return EsaWorkload(name, 3, 1, 65536, 2048, 32, 128, 128, 128, 4096, 2048, 2, 48.0, per_head=True)
+    if name == "esa_decode_128k_heads":
+        return EsaWorkload(name, 4, 16, 131072, 1, 32, 128, 128, 128, 4096, 2048, 2, 48.0, needles=16,
+                           per_head=True)
     raise SystemExit(f"unknown workload {name}")
 
 

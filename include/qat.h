@@ -62,7 +62,7 @@ int qat_abi_version(void);
  * "moba_current_attn", "moba_generic_attn", "moba_decode_select",
  * "moba_decode_attn", "moba_decode_combine", "moba_bwd_delta", "moba_bwd_dq_past",
  * "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated", "esa_bwd_dq", "esa_bwd_kv", "cca_pool", "cca_attn",
- * "esa_compress", "esa_scores",
+ * "esa_compress", "esa_scores" (its two passes' kernels: "esa_rowmax", "esa_colsum"),
  * "esa_decode_scan", "esa_topk", "esa_prefill_attn", "esa_decode_attn",
  * "esa_generic_attn"). The events are timing-only (created without the
  * system-scope fence on completion, so recording them does not slow the

@@ -625,12 +625,12 @@ static void launch_scores_dc(const bf16* q_hi, const bf16* q_lo, const bf16* kc,
                              int64_t m, int64_t mid0, int64_t n_mid, int64_t kps, int ks_eff, int64_t rps, int qs_eff,
                              int64_t rows, float clip, float tau2, float* rowmax_part, float* rowsum_part,
                              float* rowmax, float* upart, hipStream_t s) {
-  hipLaunchKernelGGL((esa_rowmax_kernel<DC, VOTE, HILO>), g1, dim3(64 * kScWaves), 0, s, q_hi, q_lo, kc, g, m, mid0,
-                     n_mid, kps, ks_eff, tau2, rowmax_part, rowsum_part);
+  launch_timed("esa_rowmax", esa_rowmax_kernel<DC, VOTE, HILO>, g1, dim3(64 * kScWaves), 0, s, q_hi, q_lo, kc, g, m,
+               mid0, n_mid, kps, ks_eff, tau2, rowmax_part, rowsum_part);
   hipLaunchKernelGGL(esa_rowmax_final_kernel<VOTE>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s, rowmax_part,
                      rowsum_part, ks_eff, rows, tau2, rowmax);
-  hipLaunchKernelGGL((esa_colsum_kernel<DC, VOTE, HILO>), g2, dim3(64 * kScWaves), 0, s, q_hi, q_lo, rowmax, kc, g,
-                     m, mid0, n_mid, rps, qs_eff, clip, tau2, upart);
+  launch_timed("esa_colsum", esa_colsum_kernel<DC, VOTE, HILO>, g2, dim3(64 * kScWaves), 0, s, q_hi, q_lo, rowmax, kc,
+               g, m, mid0, n_mid, rps, qs_eff, clip, tau2, upart);
 }
 
 hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const bf16* kc, const ScGeom& g,
@@ -682,11 +682,11 @@ template <int DC, typename QT>
 static void launch_scan_dc(const QT* q, const bf16* kc, const ScGeom& g, dim3 grid, int64_t mid0, int64_t n_mid,
                            int64_t kpw, float tau2, float* s_out, float* smax_part, float* ssum_part, hipStream_t s) {
   if (tau2 > 0.f)
-    hipLaunchKernelGGL((esa_decode_scan_kernel<DC, true, QT>), grid, dim3(256), 0, s, q, kc, g, mid0, n_mid, kpw,
-                       tau2, s_out, smax_part, ssum_part);
+    launch_timed("esa_decode_scan", esa_decode_scan_kernel<DC, true, QT>, grid, dim3(256), 0, s, q, kc, g, mid0,
+                 n_mid, kpw, tau2, s_out, smax_part, ssum_part);
   else
-    hipLaunchKernelGGL((esa_decode_scan_kernel<DC, false, QT>), grid, dim3(256), 0, s, q, kc, g, mid0, n_mid, kpw,
-                       tau2, s_out, smax_part, ssum_part);
+    launch_timed("esa_decode_scan", esa_decode_scan_kernel<DC, false, QT>, grid, dim3(256), 0, s, q, kc, g, mid0,
+                 n_mid, kpw, tau2, s_out, smax_part, ssum_part);
 }
 
 hipError_t launch_esa_decode_scan(const void* q, bool q_bf16, const bf16* kc, const ScGeom& g, int64_t nsel,
