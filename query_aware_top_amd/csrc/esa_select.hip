@@ -329,7 +329,11 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
 //   emit   stable compaction: every key above T, and the lowest-index keys
 //          equal to T up to k, in ascending position order.
 // Each kernel re-derives the digits fixed so far from the global
-// histograms (2048 bins, cheap), so no state passes between them.
+// histograms (2048 bins, cheap), so no state passes between them. prep,
+// hist and count visit the slice with stride 256 (element e of thread t is
+// candidate e*256 + t: every load and store is coalesced); emit stages the
+// slice's keys in LDS with the same coalesced loads and then gives each
+// thread PER consecutive candidates, as the stable compaction needs.
 constexpr int kTkThreads = 256;
 constexpr int kTkPerMin = 2;   // candidates per thread: 2 to 16, so that a pass has >= 256 workgroups where it can
 constexpr int kTkMaxRadius = 1024;
@@ -462,7 +466,7 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int64_t j = j0 + tid * PER + e;
+    const int64_t j = j0 + e * kTkThreads + tid;
     if (j >= n_mid) break;
     float v = s_u[j - j0 + radius];
     const int64_t a = max((int64_t)0, j - radius), b = min(n_mid - 1, j + (int64_t)radius);
@@ -491,10 +495,10 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_hist_kernel(int pass, con
   const int nb = 1 << tk_bits(pass);
   for (int i = threadIdx.x; i < nb; i += kTkThreads) s_h[i] = 0;
   __syncthreads();
-  const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER) + threadIdx.x * PER;
+  const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER) + threadIdx.x;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int64_t j = j0 + e;
+    const int64_t j = j0 + e * kTkThreads;
     if (j >= n_mid) break;
     const uint32_t key = keys[bi * n_mid + j];
     if ((key & cut.mask) == cut.prefix) atomicAdd(&s_h[(key >> tk_shift(pass)) & (nb - 1)], 1);
@@ -515,11 +519,11 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_count_kernel(const uint32
   const int64_t bi = blockIdx.y;
   const TkCut cut = tk_cut(hist + bi * 3 * kTkBins, 3, topk, s_w, &s_cut);
   const uint32_t T = cut.prefix;
-  const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER) + threadIdx.x * PER;
+  const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER) + threadIdx.x;
   int32_t gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int64_t j = j0 + e;
+    const int64_t j = j0 + e * kTkThreads;
     if (j >= n_mid) break;
     const uint32_t key = keys[bi * n_mid + j];
     gt += key > T;
@@ -540,6 +544,7 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_emit_kernel(const uint32_
                                                                    int32_t* __restrict__ n_sel) {
   __shared__ int32_t s_w[kTkThreads / 64];
   __shared__ TkCut s_cut;
+  __shared__ uint32_t s_k[kTkThreads * (PER + 1)];   // one pad word per PER: conflict-free reads
   const int64_t bi = blockIdx.y;
   const int nwg = gridDim.x;
   int32_t* osel = sel + bi * topk;
@@ -572,10 +577,20 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_emit_kernel(const uint32_
   const int32_t base = gt_sum + min(eq_sum, take_eq);
   int32_t gt = 0, eq = 0;
   uint32_t kv[PER];
+  {   // the slice's keys through LDS: coalesced loads, then PER consecutive per thread
+    const int64_t s0 = (int64_t)blockIdx.x * (kTkThreads * PER);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int64_t j = s0 + e * kTkThreads + threadIdx.x;
+      const int jl = e * kTkThreads + threadIdx.x;
+      s_k[jl + jl / PER] = j < n_mid ? keys[bi * n_mid + j] : 0u;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int64_t j = j0 + e;
-    kv[e] = j < n_mid ? keys[bi * n_mid + j] : 0u;
+    kv[e] = s_k[threadIdx.x * (PER + 1) + e];
     if (j < n_mid) {
       gt += kv[e] > T;
       eq += kv[e] == T;
