@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
 // slice's keys in LDS with the same coalesced loads and then gives each
 // thread PER consecutive candidates, as the stable compaction needs.
 constexpr int kTkThreads = 256;
-constexpr int kTkPerMin = 2;   // candidates per thread: 2 to 16, so that a pass has >= 256 workgroups where it can
+constexpr int kTkPerMin = 2;   // candidates per thread: 2 to 32, so that a pass has >= 256 workgroups where it can
 constexpr int kTkMaxRadius = 1024;
 constexpr int kTkBins = 2048;
 __host__ __device__ constexpr int tk_shift(int pass) { return pass == 0 ? 21 : pass == 1 ? 10 : 0; }
@@ -770,6 +770,11 @@ hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const floa
   // few sequences); wgcnt holds esa_topk_slices(n_mid) >= slices entries
   // per sequence
   const int64_t s8 = batch * cdiv(n_mid, kTkThreads * 8), s4 = batch * cdiv(n_mid, kTkThreads * 4);
+  // many selections (one per head): 32 per thread halves the passes'
+  // per-workgroup cost (reading the histograms, clearing the bins)
+  if (batch * cdiv(n_mid, kTkThreads * 32) >= 1024)
+    return launch_esa_topk_per<32>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius, topk,
+                                   mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
   if (batch * cdiv(n_mid, kTkThreads * 16) >= 256)
     return launch_esa_topk_per<16>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius, topk,
                                    mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
