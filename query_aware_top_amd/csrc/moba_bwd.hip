@@ -689,7 +689,10 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_gated_kernel(
 }
 
 // dK, dV of bucket b's keys += the sums of its runs, in run order: grid
-// (buckets, key chunks); a thread adds float4 pieces.
+// (buckets, key chunks, kRedSlices); a thread adds float4 pieces, the
+// slices split a chunk's pieces so that a bucket with many runs (a block
+// many rows gated) is spread over several workgroups.
+constexpr int kRedSlices = 8;
 template <int D>
 __global__ __launch_bounds__(256) void moba_bwd_kv_reduce_kernel(const float* __restrict__ part,
                                                                  const int32_t* __restrict__ run_off,
@@ -707,13 +710,22 @@ __global__ __launch_bounds__(256) void moba_bwd_kv_reduce_kernel(const float* __
   const int64_t kv = (int64_t)(uint32_t)td.x | ((int64_t)td.y << 32);
   constexpr int D4 = D / 4;
   const int ncpk = gridDim.y;
-  for (int e = threadIdx.x; e < 2 * nk * D4; e += 256) {
+  const int64_t rstride = (int64_t)ncpk * 2 * kKvKeys * D;   // floats between consecutive runs' slots
+#pragma unroll 2
+  for (int e = threadIdx.x + blockIdx.z * 256; e < 2 * nk * D4; e += 256 * kRedSlices) {
     const int tsr = e / (nk * D4), rem = e % (nk * D4), j = rem / D4, d4 = rem % D4;
+    const float* src = part + (((int64_t)r0 * ncpk + c) * 2 + tsr) * kKvKeys * D + j * D + 4 * d4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int32_t w = r0; w < r1; ++w) {
-      const f32x4 x = *(const f32x4*)(part + (((int64_t)w * ncpk + c) * 2 + tsr) * kKvKeys * D + j * D + 4 * d4);
-      acc += x;
+    int32_t w = r0;
+    for (; w + 4 <= r1; w += 4, src += 4 * rstride) {   // four runs' loads in flight, added in run order
+      const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + rstride);
+      const f32x4 x2 = *(const f32x4*)(src + 2 * rstride), x3 = *(const f32x4*)(src + 3 * rstride);
+      acc += x0;
+      acc += x1;
+      acc += x2;
+      acc += x3;
     }
+    for (; w < r1; ++w, src += rstride) acc += *(const f32x4*)src;
     float* dst = (tsr == 0 ? dk : dv) + kv + (int64_t)(c * kKvKeys + j) * hkv * D + 4 * d4;
     f32x4 y = *(const f32x4*)dst;
     *(f32x4*)dst = y + acc;
@@ -794,7 +806,8 @@ static hipError_t launch_moba_bwd_d(const T* q, const T* k, const T* v, const in
                      (const int32_t*)run_off, (int32_t)nbuckets, entries, kv_part, seq_len, hq, hkv, q_len, block,
                      scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(moba_bwd_kv_reduce_kernel<D>, dim3((unsigned)nbuckets, (unsigned)cpk), dim3(256), 0, s,
+        hipLaunchKernelGGL(moba_bwd_kv_reduce_kernel<D>, dim3((unsigned)nbuckets, (unsigned)cpk, kRedSlices), dim3(256),
+                           0, s,
                            (const float*)kv_part, (const int32_t*)run_off, (const int32_t*)tile_off, tiles, dk, dv,
                            hkv, block);
       }
