@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     MobaParams,
     lib,
     lib_path,
+    plan,
     abi_version,
     esa_params,
     moba_params,

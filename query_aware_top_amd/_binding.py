@@ -135,6 +135,57 @@ def _check(rc: int):
         raise QatError(rc, lib().qat_last_error().decode())
 
 
+class _Recorder:
+    """Stands in for the loaded library while a binding function runs under
+    plan(): workspace-size queries go to the library at once (their results
+    shape the call), every other entry point is recorded with its marshalled
+    arguments and reported as successful."""
+
+    def __init__(self, real):
+        self._real = real
+        self.calls = []
+
+    def __getattr__(self, name):
+        f = getattr(self._real, name)
+        if name.endswith("workspace_size") or name.startswith("qat_"):
+            return f
+
+        def record(*args):
+            self.calls.append((name, f, args))
+            return 0
+
+        return record
+
+
+def plan(fn, *args, **kwargs):
+    """Marshals one binding call once and returns a callable that re-issues
+    the same C ABI call(s) with the same arguments: the same tensors (by
+    pointer), parameters and the stream current now. For loops that repeat
+    one call on fixed buffers (decode steps), where the per-call Python
+    checks cost as much host time as the kernels take; every output and the
+    workspace must be passed in, and the tensors must stay alive. The library
+    still validates each call and a failing status raises."""
+    global lib
+    real = lib()
+    rec = _Recorder(real)
+    saved = lib
+    lib = lambda: rec  # noqa: E731  (the binding functions look lib up at call time)
+    try:
+        fn(*args, **kwargs)
+    finally:
+        lib = saved
+    calls = rec.calls
+
+    def replay():
+        for name, f, a in calls:
+            rc = f(*a)
+            if rc != 0:
+                raise QatError(rc, f"{name}: " + real.qat_last_error().decode())
+
+    replay.calls = [c[0] for c in calls]
+    return replay
+
+
 def _dt(t: torch.dtype) -> int:
     if t == torch.bfloat16:
         return QAT_BF16

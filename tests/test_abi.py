@@ -172,6 +172,25 @@ def test_per_head_flag_picks_the_selection_entry(lib):
     assert _size(lib, "esa_bwd_workspace_size", ph)[1] > _size(lib, "esa_bwd_workspace_size", pm)[1]
 
 
+def test_plan_defers_the_call_and_raises_on_replay(lib):
+    """qat.plan records the entry-point call instead of making it (size
+    queries run at once); the replay makes it and turns a failing status
+    into QatError. Invalid parameters fail before any device work."""
+    p = _esa(topk=0)
+    dummy = ctypes.c_void_p(0x1000)
+
+    def call():
+        n = ctypes.c_size_t(0)
+        assert B.lib().esa_workspace_size(ctypes.byref(_esa()), ctypes.byref(n)) == QAT_OK and n.value > 0
+        return B.lib().esa_select(ctypes.byref(p), dummy, dummy, None, dummy, dummy, dummy, None, dummy,
+                                  ctypes.c_size_t(1 << 40), ctypes.c_void_p(0))
+
+    replay = qat.plan(call)
+    assert replay.calls == ["esa_select"]
+    with pytest.raises(qat.QatError):
+        replay()
+
+
 def test_compress_validation(lib):
     dummy = ctypes.c_void_p(0x1000)
     n = ctypes.c_size_t(0)

@@ -124,6 +124,35 @@ def test_moba_decode_matches_full_layout_entry_points():
     assert (blk_d != blk_f).float().mean().item() < 0.05
 
 
+def test_planned_calls_match_direct_calls():
+    """qat.plan re-issues the marshalled C ABI calls: a planned decode step
+    (cache update, gating, attention) gives bit-identical results to the
+    direct calls, on repeated replays."""
+    b, n, hq, hkv, d, block, topk = 3, 5000, 8, 2, 128, 256, 3
+    q, k, v, _ = synth.moba_inputs(78, b, n, hq, hkv, d, torch.bfloat16, DEV)
+    p = params(b, n, hq, hkv, d, block, topk, 1, torch.bfloat16)
+    qr = q[:, n - 1:].contiguous()
+    ws = torch.empty(qat.moba_workspace_size(p), dtype=torch.uint8, device=DEV)
+    last = (n - 1) // block - 1
+    kbar = qat.moba_block_means(p, k, 0, last, ws=ws)
+    blk = torch.empty(b, 1, hq, topk, dtype=torch.int32, device=DEV)
+    out = torch.empty(b, 1, hq, d, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(b, 1, hq, dtype=torch.float32, device=DEV)
+    steps = [qat.plan(qat.moba_block_means, p, k, last, 1, kbar, ws=ws),
+             qat.plan(qat.moba_decode_select, p, qr, kbar, blk=blk),
+             qat.plan(qat.moba_decode_attn, p, qr, k, v, blk, out=out, lse=lse, ws=ws)]
+    assert [s.calls for s in steps] == [["moba_block_means"], ["moba_decode_select"], ["moba_decode_attn"]]
+    qat.moba_block_means(p, k, last, 1, kbar, ws=ws)
+    blk_d = qat.moba_decode_select(p, qr, kbar)
+    out_d, lse_d = qat.moba_decode_attn(p, qr, k, v, blk_d)
+    for _ in range(3):
+        out.zero_()
+        for s in steps:
+            s()
+        torch.cuda.synchronize()
+        assert torch.equal(blk, blk_d) and torch.equal(out, out_d) and torch.equal(lse, lse_d)
+
+
 def test_moba_decode_window_and_generic_layout():
     """An extra local window takes the per-row kernel with the rows-only q."""
     b, n, hq, hkv, d, block, topk, ql, w = 1, 2500, 4, 2, 64, 128, 3, 2, 300
