@@ -777,7 +777,7 @@ def main():
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
               f"see DESIGN.md for how the path would shard.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():

@@ -41,7 +41,7 @@ extern "C" {
 enum qat_status {
   QAT_OK = 0,
   QAT_EINVAL = -1,        /* bad argument (null pointer, size, range) */
-  QAT_EUNSUPPORTED = -2,  /* valid request this build does not implement */
+  QAT_EUNSUPPORTED = -2,  /* valid request this library does not implement */
   QAT_EWORKSPACE = -3,    /* workspace null, misaligned or too small */
   QAT_EHIP = -4           /* a HIP launch failed */
 };
