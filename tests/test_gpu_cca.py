@@ -47,6 +47,9 @@ SMALL = [
     (1, 512, 2, 2, 64, 32, 0, 0, None),         # w = 0: own group only in the window
     (1, 300, 4, 4, 128, 7, 1000, 0, None),      # window beyond the sequence: dense causal
     (1, 2000, 2, 2, 128, 64, 256, 1500, 500),   # large groups, final chunk only
+    (3, 3001, 8, 2, 128, 16, 1024, 3000, 1),    # one new row per sequence (decode-like), GQA 4:1
+    (1, 1500, 2, 2, 64, 128, 64, 0, None),      # window shorter than a group
+    (2, 4097, 4, 4, 128, 32, 512, 4000, 97),    # ragged tail rows over several tiles' worth of core tokens
 ]
 
 
