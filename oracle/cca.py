@@ -31,7 +31,12 @@ of the pages):
 Pins (tests/test_oracle_pins.py): g = 1 equals dense causal attention for any
 w; w >= t equals dense causal attention; identical keys in a group give that
 key and the group's mean value; the core depends on the group's last query
-only; the window starts on a group boundary and holds >= min(t, w) tokens.
+only; the window start equals the latest group boundary, found by search,
+from which every query of the group still sees >= min(t, w) earlier tokens
+(a window one group wider or narrower fails); the rows equal attention over
+a key set enumerated position by position; with Hq = 4 over Hkv = 2 the
+result equals MHA with each KV head repeated in place (an interleaved head
+map fails).
 """
 import numpy as np
 

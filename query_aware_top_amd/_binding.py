@@ -4,6 +4,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import threading
 
 import torch
 
@@ -63,11 +64,16 @@ class MobaParams(ctypes.Structure):
 
 
 _lib = None
+_tls = threading.local()   # .recorder: the _Recorder of a plan() running on this thread
 
 
 def lib():
-    """Loads libqat.so once; raises if it has not been built."""
+    """Loads libqat.so once; raises if it has not been built. Inside plan(),
+    on the planning thread only, returns that plan's recorder instead."""
     global _lib
+    rec = getattr(_tls, "recorder", None)
+    if rec is not None:
+        return rec
     if _lib is None:
         if not os.path.exists(lib_path):
             raise RuntimeError(f"{lib_path} is missing: build it with `python -m query_aware_top_amd.build`")
@@ -144,6 +150,7 @@ class _Recorder:
     def __init__(self, real):
         self._real = real
         self.calls = []
+        self.keep = []   # every tensor whose pointer a recorded call holds
 
     def __getattr__(self, name):
         f = getattr(self._real, name)
@@ -162,19 +169,26 @@ def plan(fn, *args, **kwargs):
     the same C ABI call(s) with the same arguments: the same tensors (by
     pointer), parameters and the stream current now. For loops that repeat
     one call on fixed buffers (decode steps), where the per-call Python
-    checks cost as much host time as the kernels take; every output and the
-    workspace must be passed in, and the tensors must stay alive. The library
-    still validates each call and a failing status raises."""
-    global lib
+    checks cost as much host time as the kernels take. The library still
+    validates each call and a failing status raises.
+
+    Every tensor whose pointer the recorded calls hold (inputs, and outputs
+    or workspaces the binding function allocated when they were not passed
+    in) is kept alive by the returned callable, so its memory cannot be
+    handed to another tensor while the plan exists; fn's own return value
+    (its outputs) is the callable's `result`. Recording is per thread: other
+    threads calling the binding meanwhile run their calls normally."""
     real = lib()
+    if getattr(_tls, "recorder", None) is not None:
+        raise RuntimeError("plan() cannot be nested")
     rec = _Recorder(real)
-    saved = lib
-    lib = lambda: rec  # noqa: E731  (the binding functions look lib up at call time)
+    _tls.recorder = rec
     try:
-        fn(*args, **kwargs)
+        result = fn(*args, **kwargs)
     finally:
-        lib = saved
+        _tls.recorder = None
     calls = rec.calls
+    keep = rec.keep
 
     def replay():
         for name, f, a in calls:
@@ -183,6 +197,8 @@ def plan(fn, *args, **kwargs):
                 raise QatError(rc, f"{name}: " + real.qat_last_error().decode())
 
     replay.calls = [c[0] for c in calls]
+    replay.result = result
+    replay.tensors = keep
     return replay
 
 
@@ -195,7 +211,12 @@ def _dt(t: torch.dtype) -> int:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    if t is None:
+        return None
+    rec = getattr(_tls, "recorder", None)
+    if rec is not None:
+        rec.keep.append(t)
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _need(t, name, dtype=None, device=True):

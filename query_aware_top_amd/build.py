@@ -15,7 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libqat.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-ARCH = os.environ.get("QAT_OFFLOAD_ARCH", "gfx950")
+# the kernels use gfx950-only instructions (bf16 MFMA 32x32x16, transposing
+# LDS reads, permlane32_swap): no other target is built
+ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [
@@ -39,17 +41,7 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False, out: str = OUT, defines=()) -> str:
-    global FLAGS
-    base_flags = FLAGS
-    FLAGS = FLAGS + [f"-D{d}" for d in defines]
-    try:
-        return _build(verbose, out)
-    finally:
-        FLAGS = base_flags
-
-
-def _build(verbose: bool, out: str) -> str:
+def build(verbose: bool = False, out: str = OUT) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:

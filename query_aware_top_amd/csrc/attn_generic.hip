@@ -16,17 +16,8 @@
 
 namespace qat {
 
-#ifndef QAT_DEC_PIECE
-#define QAT_DEC_PIECE 256
-#endif
-#ifndef QAT_DEC_KEYS
-#define QAT_DEC_KEYS 4
-#endif
-#ifndef QAT_DEC_PIPE
-#define QAT_DEC_PIPE 1
-#endif
-constexpr int kMobaDecPiece = QAT_DEC_PIECE;   // keys per decode piece
-constexpr int kMobaDecKeys = QAT_DEC_KEYS;     // keys per 16-lane group and step in a piece
+constexpr int kMobaDecPiece = 256;   // keys per decode piece
+constexpr int kMobaDecKeys = 4;      // keys per 16-lane group and step in a piece
 
 template <typename T, int E>
 __device__ __forceinline__ void load_piece(const T* p, float (&x)[E]) {
@@ -310,11 +301,7 @@ __global__ __launch_bounds__(256) void moba_decode_piece_kernel(
   WaveRowAttn<T, D> ra;
   ra.init(q + ((bi * q_seq + t - q_off) * hq + h) * D, scale_log2);
   const int64_t base = (bi * seq_len * hkv + g) * D, stride = hkv * D;
-#if QAT_DEC_PIPE
   ra.template keys_pipe<kMobaDecKeys>(k, v, max((int64_t)0, e - a), [=](int64_t j) { return base + (a + j) * stride; });
-#else
-  ra.template keys_n<kMobaDecKeys>(k, v, max((int64_t)0, e - a), [=](int64_t j) { return base + (a + j) * stride; });
-#endif
   const int64_t pi = row * npieces + piece;
   ra.finish(po + pi * D, plse + pi);
 }

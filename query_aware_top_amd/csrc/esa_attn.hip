@@ -69,10 +69,7 @@ __global__ void esa_keylist_kernel(const int32_t* __restrict__ sel, const int32_
 // ---------------------------------------------------------------------------
 // Prefill / chunk attention on the matrix cores: grid (128-row tiles of the
 // chunk, head, sequence).
-#ifndef QAT_ESA_NW
-#define QAT_ESA_NW 8
-#endif
-constexpr int kNW = QAT_ESA_NW;
+constexpr int kNW = 8;   // waves per workgroup
 constexpr int kThreads = 64 * kNW;
 constexpr int kRows = 32 * kNW;
 

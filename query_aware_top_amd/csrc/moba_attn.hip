@@ -22,10 +22,7 @@
 
 namespace qat {
 
-#ifndef QAT_PAST_NW
-#define QAT_PAST_NW 8
-#endif
-constexpr int kNW = QAT_PAST_NW;          // waves per past-block workgroup
+constexpr int kNW = 8;                    // waves per past-block workgroup
 constexpr int kThreads = 64 * kNW;
 constexpr int kRowsPerTile = 32 * kNW;    // query rows per attention workgroup
 

@@ -191,6 +191,43 @@ def test_plan_defers_the_call_and_raises_on_replay(lib):
         replay()
 
 
+def test_plan_keeps_allocated_buffers_alive_and_records_per_thread(lib):
+    """A buffer the planned function allocates itself (an output or a
+    workspace it was not given) stays referenced by the plan, so the
+    replays never write into memory the allocator has handed on; the
+    function's return value is the plan's `result`; and a binding call made
+    from another thread while the plan records is not recorded."""
+    import gc
+    import threading
+    import weakref
+
+    import torch
+    seen = {}
+
+    def call():
+        ws = torch.empty(64, dtype=torch.uint8)   # allocated inside, like an omitted workspace
+        seen["ws"] = weakref.ref(ws)
+        other = {}
+        th = threading.Thread(target=lambda: other.setdefault("lib", B.lib()))
+        th.start()
+        th.join()
+        seen["other_is_recorder"] = isinstance(other["lib"], B._Recorder)
+        B.lib().esa_select(None, B._ptr(ws), None, None, None, None, None, None, None, ctypes.c_size_t(0),
+                           ctypes.c_void_p(0))
+        return "outputs"
+
+    replay = qat.plan(call)
+    gc.collect()
+    assert replay.calls == ["esa_select"]
+    assert replay.result == "outputs"
+    assert seen["ws"]() is not None, "a buffer the recorded call points at was freed"
+    assert not seen["other_is_recorder"], "another thread's binding call was recorded"
+    assert not isinstance(B.lib(), B._Recorder)
+    del replay
+    gc.collect()
+    assert seen["ws"]() is None
+
+
 def test_compress_validation(lib):
     dummy = ctypes.c_void_p(0x1000)
     n = ctypes.c_size_t(0)

@@ -115,6 +115,19 @@ def test_moba_gqa_32k_planted_full_size():
     assert len(top8 & set(info["planted_blocks"])) >= 6
 
 
+def test_moba_gqa_32k_planted_topk4():
+    """The same 32k GQA planted shape under the other reading of "top-k 3 +
+    forced current block": three past blocks plus the current one (k = 4);
+    sampled rows against the oracle."""
+    n, hq, hkv, d, block = 32768, 32, 8, 128, 512
+    q, k, v, _ = synth.moba_inputs(2, 1, n, hq, hkv, d, torch.bfloat16, DEV, planted=8, block=block)
+    rows = sample_rows(n, block, 40, 4)
+    print(f"[moba 32k k=4] rows={len(rows)}", flush=True)
+    blk, _, _ = check(q, k, v, block, 4, torch.bfloat16, rows=rows)
+    # every row past the third block attends three past blocks and its own
+    assert int((blk[0, 3 * block:] >= 0).sum(-1).min()) == 4
+
+
 def test_moba_long_512k_full_size():
     """MoBA fixed sparsity, bf16: 8 heads x 128, N 524288 in 64 blocks of 8192,
     top-k 3 (95.31% sparsity); block gating over all queries, attention for

@@ -403,6 +403,70 @@ def test_cca_window_is_group_aligned_and_long_enough():
                 assert t - ls >= min(t, w)
 
 
+def _window_start_by_search(t, g, w):
+    """The window start found by search from the locality module's two
+    requirements alone: it is a group boundary, every query of t's group sees
+    at least min(t', w) earlier raw tokens from it, and no later boundary
+    would do (the window is the shortest such one, shared by the group)."""
+    grp0 = (t // g) * g
+    members = range(grp0, grp0 + g)
+    best = None
+    for s in range(0, grp0 + 1, g):
+        if all(tp - s >= min(tp, w) for tp in members):
+            best = s
+    return best
+
+
+def test_cca_window_start_is_the_latest_boundary_that_keeps_w_tokens():
+    """Pins window_start itself: a window one group wider (or narrower) than
+    the shortest group-aligned one with >= w tokens for every query of the
+    group fails here."""
+    for g in (1, 2, 3, 4, 16):
+        for w in (0, 1, 2, 5, 16, 17, 33):
+            for t in range(160):
+                assert occa.window_start(t, g, w) == _window_start_by_search(t, g, w), (t, g, w)
+
+
+def test_cca_rows_attend_the_enumerated_key_set():
+    """attend_rows against attention over a key set enumerated position by
+    position: the core token of every complete group that lies wholly before
+    the searched window start, then every raw token from that start to t."""
+    q, k, v = _cca_case(63, n=48, hq=2, hkv=1)
+    g, w, scale = 4, 6, 0.4
+    kc, vc = occa.pool(q, k, v, g, scale)
+    rows = list(range(48))
+    o, lse = occa.attend_rows(q, k, v, kc, vc, g, w, scale, rows)
+    for t in rows:
+        s = _window_start_by_search(t, g, w)
+        cores = [i for i in range(48 // g) if (i + 1) * g <= s]
+        raw = [j for j in range(48) if s <= j <= t]
+        for h in range(2):
+            K = np.array([kc[i, h] for i in cores] + [k[j, 0] for j in raw]).reshape(-1, k.shape[2])
+            V = np.array([vc[i, h] for i in cores] + [v[j, 0] for j in raw]).reshape(-1, v.shape[2])
+            o_ref, l_ref = oatt.attend(q[t, h], K, V, scale)
+            assert np.allclose(o[t, h], o_ref, atol=1e-12) and abs(lse[t, h] - l_ref) < 1e-12
+
+
+def test_cca_gqa_equals_mha_with_repeated_kv():
+    """Hq = 4 query heads over Hkv = 2 KV heads: heads 0, 1 use KV head 0 and
+    heads 2, 3 KV head 1 (contiguous groups), so the result equals the
+    one-KV-head-per-query-head case with each KV head repeated in place."""
+    q, k, v = _cca_case(64, n=40, hq=4, hkv=2)
+    g, w, scale = 4, 5, 0.35
+    kr, vr = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    kc, vc = occa.pool(q, k, v, g, scale)
+    kc_r, vc_r = occa.pool(q, kr, vr, g, scale)
+    assert np.allclose(kc, kc_r, atol=1e-14) and np.allclose(vc, vc_r, atol=1e-14)
+    rows = list(range(40))
+    o, lse = occa.attend_rows(q, k, v, kc, vc, g, w, scale, rows)
+    o_r, lse_r = occa.attend_rows(q, kr, vr, kc_r, vc_r, g, w, scale, rows)
+    assert np.allclose(o, o_r, atol=1e-13) and np.allclose(lse, lse_r, atol=1e-13)
+    # the interleaved map (head h -> KV head h % Hkv) gives a different result
+    ki, vi = np.tile(k, (1, 2, 1)), np.tile(v, (1, 2, 1))
+    kc_i, vc_i = occa.pool(q, ki, vi, g, scale)
+    assert not np.allclose(kc, kc_i)
+
+
 def test_moba_is_causal():
     r = rng(9)
     N, H, d, B = 32, 2, 8, 4
