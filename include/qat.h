@@ -343,6 +343,24 @@ int moba_decode_select(const qat_moba_params* p, const void* q, const float* kba
 int moba_decode_attn(const qat_moba_params* p, const void* q, const void* k, const void* v,
                      const int32_t* blk, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moba_decode_attn_noalloc: moba_decode_attn for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, serving
+ * loops and harnesses that forbid allocation). Same arguments, key sets and
+ * outputs as moba_decode_attn without ws / ws_bytes; it calls no allocator.
+ * Its partial results go to a fixed 16 MiB device array inside the library
+ * (one per GPU, held until the process ends), so it takes only the
+ * split-key case: q_len <= 8, window 0, at most 64 pieces of 256 keys per
+ * row, and rows * pieces * (head_dim + 1) * 4 bytes (pieces = topk *
+ * ceil(block / 256)) within the 16 MiB; anything else returns
+ * QAT_EUNSUPPORTED before any device work. Every call on one GPU shares that
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and give wrong results; serialise them. The array needs no clearing (each
+ * call writes every piece it reads).
+ */
+int moba_decode_attn_noalloc(const qat_moba_params* p, const void* q, const void* k, const void* v,
+                             const int32_t* blk, void* out, float* lse, void* stream);
+
 /* ======================================================================
  * CCA-style core-token attention   [CCA]
  * ====================================================================== */

@@ -21,7 +21,7 @@ EXPORTED_SYMBOLS = (
     "esa_sparse_attn",
     "esa_bwd_workspace_size", "esa_sparse_attn_bwd",
     "moba_workspace_size", "moba_block_select", "moba_sparse_attn", "moba_block_means", "moba_decode_select",
-    "moba_decode_attn", "moba_bwd_workspace_size", "moba_sparse_attn_bwd", "cca_pool", "cca_attn",
+    "moba_decode_attn", "moba_decode_attn_noalloc", "moba_bwd_workspace_size", "moba_sparse_attn_bwd", "cca_pool", "cca_attn",
 )
 
 
@@ -102,6 +102,7 @@ def lib():
         L.moba_block_means.argtypes = [ctypes.POINTER(MobaParams), vp, i64, i64, vp, vp, sz, vp]
         L.moba_decode_select.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp]
         L.moba_decode_attn.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moba_decode_attn_noalloc.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp]
         L.moba_bwd_workspace_size.argtypes = [ctypes.POINTER(MobaParams), ctypes.POINTER(sz)]
         L.moba_sparse_attn_bwd.argtypes = [ctypes.POINTER(MobaParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                            vp]
@@ -531,4 +532,18 @@ def cca_attn(p: CcaParams, q, k, v, kc, vc, out=None, lse=None, want_lse=True):
         lse = torch.empty(p.batch, p.q_len, p.n_q_heads, dtype=torch.float32, device=dev)
     _check(lib().cca_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(lse),
                           _stream()))
+    return out, lse
+
+
+def moba_decode_attn_noalloc(p: MobaParams, q, k, v, blk, out, lse=None):
+    """moba_decode_attn through the entry point that allocates nothing (its
+    partials live in the library's fixed per-GPU scratch array): out (and
+    lse, if wanted) must be given. Returns (out, lse)."""
+    dt = torch.bfloat16 if p.dtype == QAT_BF16 else torch.float32
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, name, dt)
+    _need(blk, "blk", torch.int32)
+    _need(lse, "lse", torch.float32)
+    _check(lib().moba_decode_attn_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(blk), _ptr(out),
+                                          _ptr(lse), _stream()))
     return out, lse

@@ -670,6 +670,64 @@ QAT_EXPORT int moba_decode_attn(const qat_moba_params* p, const void* q, const v
                         "moba_decode_attn");
 }
 
+// ---------------------------------------------------------------- no allocation
+// Fixed device scratch of moba_decode_attn_noalloc: the split-key pieces'
+// float32 partial outputs and log-sum-exps. Every GPU holds its own copy for
+// the life of the process. Host code never names the array (its name on the
+// host is not a device address): the address of the current device's copy
+// is fetched once per device and kept.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "moba_decode_attn_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(QAT_EUNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "moba_decode_attn_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QAT_OK;
+}
+}  // namespace
+
+QAT_EXPORT int moba_decode_attn_noalloc(const qat_moba_params* p, const void* q, const void* k, const void* v,
+                                        const int32_t* blk, void* out, float* lse, void* stream) {
+  int rc = moba_check(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !blk || !out) return fail(QAT_EINVAL, "q, k, v, blk, out must be non-NULL");
+  const MobaLayout L = moba_layout(p, nullptr);
+  if (!L.decode)
+    return fail(QAT_EUNSUPPORTED,
+                "moba_decode_attn_noalloc takes the split-key case only (q_len <= %lld, window 0, at most %d "
+                "pieces of 256 keys per row)",
+                (long long)kMobaDecodeMaxQ, kMobaDecodeMaxPieces);
+  const size_t po_bytes = ((size_t)L.nrows * L.dec_pieces * p->head_dim * sizeof(float) + 255) & ~size_t(255);
+  const size_t need = po_bytes + (size_t)L.nrows * L.dec_pieces * sizeof(float);
+  if (need > kNoAllocScratchBytes)
+    return fail(QAT_EUNSUPPORTED, "moba_decode_attn_noalloc needs %zu bytes of scratch; its fixed buffer holds %zu",
+                need, kNoAllocScratchBytes);
+  void* base = nullptr;
+  if ((rc = noalloc_scratch(&base))) return rc;
+  float* po = static_cast<float*>(base);
+  float* plse = reinterpret_cast<float*>(static_cast<char*>(base) + po_bytes);
+  const hipError_t e = qat::launch_moba_decode(q, k, v, blk, po, plse, out, lse, p->dtype == QAT_BF16, p->batch,
+                                               p->seq_len, p->q_len, p->q_start, p->n_q_heads, p->n_kv_heads,
+                                               p->head_dim, p->q_start, p->q_len, p->block, p->topk, p->scale,
+                                               (hipStream_t)stream);
+  return hip_status(e, "moba_decode_attn_noalloc");
+}
+
 QAT_EXPORT int moba_bwd_workspace_size(const qat_moba_params* p, size_t* bytes) {
   int rc = moba_check(p);
   if (rc) return rc;
