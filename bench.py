@@ -175,32 +175,39 @@ class MobaWorkload(Workload):
                 "query_rows": self.n - self.q_start}
 
     def cpu_baseline(self, budget_s=12.0):
-        """The float64 oracle on host cores over a bounded sample of query rows
-        (block gating + attention for every head of each sampled row)."""
+        """The float64 oracle on all host cores (one worker process each) over
+        the workload's query rows in random order, as many 128-row chunks as
+        the budget allows (block gating + attention, every head of each
+        row); the block means over the whole sequence are computed first,
+        inside the timed region."""
         import numpy as np
-        from oracle import attention as oatt
         from oracle import moba as omoba
-        t0 = time.perf_counter()
-        kn = self.k[0].to("cpu").to(torch.float64).numpy()
-        vn = self.v[0].to("cpu").to(torch.float64).numpy()
-        kbar = omoba.block_means(kn, self.block)
+        qp = _stage_gpu("moba_q", self.q[0])
+        kp = _stage_gpu("moba_k", self.k[0])
+        vp = _stage_gpu("moba_v", self.v[0])
         rows_all = np.random.default_rng(0).permutation(np.arange(self.q_start, self.n))
-        qcpu = self.q[0].to("cpu")
-        done = 0
-        while done < len(rows_all) and (time.perf_counter() - t0 < budget_s or done < 16):
-            t = int(rows_all[done])
-            qt = qcpu[t].to(torch.float64).numpy()
-            for h in range(self.hq):
-                g = omoba.kv_head(h, self.hq, self.hkv)
-                blk, _ = omoba.select_row(qt[h], kbar[:, g], t, self.block, self.topk)
-                idx = omoba.key_set(blk, t, self.block)
-                oatt.attend(qt[h], kn[idx, g], vn[idx, g], self.p_att.scale)
-            done += 1
-        el = time.perf_counter() - t0
-        return {"value": done / el, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
-                "sample": f"{done} random query positions (all {self.hq} heads each) of the {self.n}-token "
-                          f"sequence, block means over the whole sequence included; float64 numpy, one "
-                          f"process and thread; {el:.1f} s"}
+        chunks = [rows_all[i:i + 128].tolist() for i in range(0, len(rows_all), 128)]
+        _, ncores = cpu_pool()
+        t0 = time.perf_counter()
+        kbar = omoba.block_means(np.load(kp).astype(np.float64), self.block)
+        t_means = time.perf_counter() - t0
+        items = [(qp, kp, vp, kbar, c, self.block, self.topk, self.p_att.scale) for c in chunks]
+        res, el = _run_parallel(_moba_rows_task, items, budget_s - t_means)
+        done = sum(res)
+        el += t_means
+        whole = done == len(rows_all)
+        what = (f"all {done} query rows" if whole else
+                f"{done} of the {len(rows_all)} query rows (random 128-row chunks)")
+        return {"value": done / el, "unit": "query-tokens/s", "cores": ncores, "kind": "oracle",
+                "sample": f"{what} of the {self.n}-token sequence, all {self.hq} heads each, block means over "
+                          f"the whole sequence included; float64 numpy, {ncores} worker processes of one "
+                          f"thread; {el:.1f} s"}
+
+    def selection_bytes(self):
+        """Gating of every row reads K once (mean pool) and Q once (block
+        scores) and writes the gated lists."""
+        el = 2 if self.dtype == "bf16" else 4
+        return (self.n * self.hkv * self.d + self.n * self.hq * self.d) * el + self.n * self.hq * self.topk * 4
 
 
 class MobaDecodeWorkload(Workload):
@@ -617,42 +624,84 @@ class EsaWorkload(Workload):
                 "selection": "per_head" if self.per_head else "merged_heads"}
 
     def cpu_baseline(self, budget_s=12.0):
+        """The float64 oracle doing the GPU step's work on all host cores:
+        compression of the chunk's new keys into the cache of earlier keys
+        (that cache is state, staged from the library's bit-identical
+        cache), the selection, and attention of the chunk's rows. Prefill:
+        compression and selection in this process (its BLAS on every core),
+        attention rows over the worker pool. Decode: the sequences' selections
+        over the pool, then their attention over the pool. Staging the
+        inputs, and the selected K/V rows between the two phases, is not
+        timed."""
         if self.per_head:
             return self._cpu_baseline_heads(budget_s)
         import numpy as np
         from oracle import esa as oesa
-        t0 = time.perf_counter()
-        bi = 0
+        _, ncores = cpu_pool()
         W = self.Wq.to("cpu").to(torch.float64).numpy()
-        kc = np.zeros((self.c0, self.d_c))
-        kcpu = self.k[bi, :self.c0]
-        for s in range(0, self.c0, 8192):
-            kc[s:s + 8192] = oesa.key_cache(kcpu[s:s + 8192].to("cpu").to(torch.float64).numpy(), W)
-        qn = self.q[bi].to("cpu").to(torch.float64).numpy()
-        sel, _, _, _ = oesa.select(qn, W, None, kc, self.c0, self.n_init, self.W, self.topk, self.p.radius,
-                                   self.p.clip, correction=self.correction)
-        t_sel = time.perf_counter() - t0
-        rows = 0
-        kk = _GpuRows(self.k[bi])
-        vv = _GpuRows(self.v[bi])
-        order = np.random.default_rng(0).permutation(self.m)
-        while rows < self.m and (time.perf_counter() - t0 < budget_s or rows < 1):
-            oesa.attend(qn, kk, vv, sel, self.c0, self.n_init, self.W, self.p.scale, rows=[int(order[rows])])
-            rows += 1
-        el = time.perf_counter() - t0
-        cores = _blas_threads()
-        if self.m == 1:
-            per_seq = el
-            return {"value": per_seq * 1e6 * self.B, "unit": "us/step", "cores": cores, "kind": "oracle",
-                    "sample": f"sequence 0 of {self.B} (key compression of the cache, selection, attention), "
-                              f"scaled by {self.B} sequences; float64 numpy, BLAS threads for the matrix products, "
-                              f"one process; {el:.1f} s"}
-        att_per_row = (el - t_sel) / rows
-        est = t_sel + att_per_row * self.m
-        return {"value": self.m / est, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
-                "sample": f"selection for the whole {self.m}-query chunk (with compression of the key cache) "
-                          f"plus attention for {rows} of its rows, extrapolated to the chunk; float64 numpy, "
-                          f"BLAS threads for the matrix products, one process; {el:.1f} s"}
+        if self.m > 1:
+            bi = 0
+            kc = self.kc[bi].to("cpu").to(torch.float64).numpy()
+            knew = self.k[bi, self.c0:].to("cpu").to(torch.float64).numpy()
+            qn = self.q[bi].to("cpu").to(torch.float64).numpy()
+            qp = _stage("esa_q", qn.astype(np.float32))
+            t0 = time.perf_counter()
+            kc[self.c0:] = oesa.key_cache(knew, W)
+            sel, _, _, _ = oesa.select(qn, W, None, kc, self.c0, self.n_init, self.W, self.topk, self.p.radius,
+                                       self.p.clip, correction=self.correction)
+            t_sel = time.perf_counter() - t0
+            pos = oesa.key_list(sel, self.c0, self.n_init, self.W, self.T - 1)
+            ix = torch.as_tensor(pos, device="cuda")
+            kp = _stage_gpu("esa_k", self.k[bi].index_select(0, ix))
+            vp = _stage_gpu("esa_v", self.v[bi].index_select(0, ix))
+            order = np.random.default_rng(0).permutation(self.m)
+            items = [(qp, kp, vp, pos, sel, self.c0, self.n_init, self.W, self.p.scale, order[i:i + 16].tolist())
+                     for i in range(0, self.m, 16)]
+            res, t_att = _run_parallel(_esa_attend_task, items, budget_s - t_sel)
+            rows = sum(res)
+            est = t_sel + t_att * self.m / rows
+            what = (f"compression of the chunk's {self.m} new keys and the selection ({t_sel:.1f} s, this "
+                    f"process, BLAS threads {_blas_threads()}), then attention of "
+                    + (f"all {rows} rows" if rows == self.m else f"{rows} of the {self.m} rows, extrapolated")
+                    + f" over {ncores} worker processes")
+            return {"value": self.m / est, "unit": "query-tokens/s", "cores": ncores, "kind": "oracle",
+                    "sample": f"{what}; float64 numpy; {t_sel + t_att:.1f} s"}
+        # decode: every sequence of the batch
+        qp = _stage_gpu("esa_q", self.q[:, 0])
+        kcp = _stage_gpu("esa_kc", self.kc)
+        knp = _stage_gpu("esa_knew", self.k[:, self.c0:self.c0 + 1])
+        Wp = _stage("esa_W", W)
+        items = [(qp, kcp, knp, Wp, bi, self.c0, self.n_init, self.W, self.topk, self.p.radius, self.p.clip,
+                  self.correction) for bi in range(self.B)]
+        res, t_sel = _run_parallel(_esa_select_task, items, 1e9)
+        sels = dict(res)
+        items = []
+        for bi in range(self.B):
+            pos = oesa.key_list(sels[bi], self.c0, self.n_init, self.W, self.T - 1)
+            ix = torch.as_tensor(pos, device="cuda")
+            q1 = _stage_gpu(f"esa_q{bi}", self.q[bi])
+            kp = _stage_gpu(f"esa_k{bi}", self.k[bi].index_select(0, ix))
+            vp = _stage_gpu(f"esa_v{bi}", self.v[bi].index_select(0, ix))
+            items.append((q1, kp, vp, pos, sels[bi], self.c0, self.n_init, self.W, self.p.scale, [0]))
+        res, t_att = _run_parallel(_esa_attend_task, items, 1e9)
+        el = t_sel + t_att
+        return {"value": el * 1e6, "unit": "us/step", "cores": ncores, "kind": "oracle",
+                "sample": f"all {self.B} sequences: compression of the new key into each cache and the "
+                          f"selection ({t_sel:.2f} s), then attention of all {self.H} heads ({t_att:.2f} s), "
+                          f"one sequence per task over {ncores} worker processes; float64 numpy"}
+
+    def step_bytes(self):
+        """Algorithmic bytes of one decode step: the compressed keys of the
+        middle part (scan), the gathered K and V rows of every head, the new
+        token's key row compressed into the cache, q, out and the two
+        compression maps."""
+        B, H, d, dc = self.B, self.H, self.d, self.d_c
+        scan = B * self.n_mid * dc * 2
+        kv = B * (self.n_keys() + 1) * H * d * 2 * 2
+        newkey = B * (H * d * 2 + dc * 2)
+        qo = 2 * B * H * d * 2
+        maps = 2 * dc * H * d * 2
+        return scan + kv + newkey + qo + maps
 
 
     def _cpu_baseline_heads(self, budget_s):
@@ -698,6 +747,153 @@ class EsaWorkload(Workload):
                     "sample": f"{what}, times {self.B} sequences; float64 numpy, one process; {el:.1f} s"}
         return {"value": self.m / (t_sel + t_att), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
                 "sample": f"{what}; float64 numpy, BLAS threads for the matrix products, one process; {el:.1f} s"}
+
+
+# ------------------------------------------------------- oracle on host cores
+# The oracle baseline runs in worker processes, one per host core, forked at
+# the start of main() before anything touches the GPU (they never do). The
+# inputs they read are staged into .npy files under TMPDIR and memory-mapped,
+# so every worker shares one page-cached copy. The box gives one GPU process
+# 16 CPUs whatever the host reports.
+_POOL = None
+_POOL_N = 0
+_STAGE_DIR = None
+
+
+def _worker_init():
+    os.environ["OMP_NUM_THREADS"] = "1"
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    # the oracle's modules, imported once per worker before any timed task
+    import oracle.attention  # noqa: F401
+    import oracle.esa  # noqa: F401
+    import oracle.moba  # noqa: F401
+
+
+def cpu_pool():
+    global _POOL, _POOL_N
+    if _POOL is None:
+        import multiprocessing as mp
+        _POOL_N = max(1, min(16, os.cpu_count() or 1))
+        _POOL = mp.get_context("fork").Pool(_POOL_N, initializer=_worker_init)
+    return _POOL, _POOL_N
+
+
+def close_cpu_pool():
+    global _POOL, _STAGE_DIR
+    if _POOL is not None:
+        _POOL.close()
+        _POOL.join()
+        _POOL = None
+    if _STAGE_DIR is not None:
+        import shutil
+        shutil.rmtree(_STAGE_DIR, ignore_errors=True)
+        _STAGE_DIR = None
+
+
+def _stage(name, arr):
+    """Writes arr (numpy) to a staging .npy file and returns its path."""
+    global _STAGE_DIR
+    import tempfile
+    import numpy as np
+    if _STAGE_DIR is None:
+        _STAGE_DIR = tempfile.mkdtemp(prefix="qat_oracle_", dir=os.environ.get("TMPDIR", "/tmp"))
+    path = os.path.join(_STAGE_DIR, name + ".npy")
+    np.save(path, arr)
+    return path
+
+
+def _stage_gpu(name, t):
+    """A device tensor staged as float32 (bf16 values widen exactly)."""
+    return _stage(name, t.to(torch.float32).cpu().numpy())
+
+
+def _run_parallel(task, items, budget_s, min_items=1):
+    """Runs task(item) over the pool, keeping every worker busy until
+    budget_s has passed (and at least min_items are done); returns (results
+    in completion order, wall seconds)."""
+    pool, n = cpu_pool()
+    t0 = time.perf_counter()
+    pending, results, nxt = [], [], 0
+    while nxt < len(items) or pending:
+        while (nxt < len(items) and len(pending) < 2 * n
+               and (time.perf_counter() - t0 < budget_s or len(results) + len(pending) < min_items)):
+            pending.append(pool.apply_async(task, (items[nxt],)))
+            nxt += 1
+        if not pending:
+            break
+        pending[0].wait()
+        done = [p for p in pending if p.ready()]
+        pending = [p for p in pending if not p.ready()]
+        results.extend(p.get() for p in done)
+    return results, time.perf_counter() - t0
+
+
+def _moba_rows_task(a):
+    """Oracle gating + attention of some query rows, all heads."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import moba as omoba
+    qp, kp, vp, kbar, rows, block, topk, scale = a
+    q, k, v = (np.load(x, mmap_mode="r") for x in (qp, kp, vp))
+    hq, hkv = q.shape[1], k.shape[1]
+    for t in rows:
+        qt = np.asarray(q[t], np.float64)
+        for h in range(hq):
+            g = omoba.kv_head(h, hq, hkv)
+            blk, _ = omoba.select_row(qt[h], kbar[:, g], t, block, topk)
+            idx = omoba.key_set(blk, t, block)
+            oatt.attend(qt[h], np.asarray(k[idx, g], np.float64), np.asarray(v[idx, g], np.float64), scale)
+    return len(rows)
+
+
+class _ListedRows:
+    """A K or V cache seen through the rows of listed positions only: x[i]
+    holds position pos[i]; indexing by positions (and optionally heads)
+    returns float64 rows."""
+
+    def __init__(self, x, pos):
+        self.x = x
+        self.shape = x.shape
+        self.where = {int(p): i for i, p in enumerate(pos)}
+
+    def __getitem__(self, idx):
+        import numpy as np
+        rest = ()
+        if isinstance(idx, tuple):
+            idx, rest = idx[0], idx[1:]
+        ii = [self.where[int(j)] for j in np.asarray(idx).reshape(-1)]
+        return np.asarray(self.x[ii], np.float64)[(slice(None),) + rest]
+
+
+def _esa_attend_task(a):
+    """Oracle attention of some chunk rows (all heads) over one sequence's
+    key list; kp / vp hold only the listed rows, pos their positions."""
+    import numpy as np
+    from oracle import esa as oesa
+    qp, kp, vp, pos, sel, c0, n_init, W, scale, rows = a
+    q = np.load(qp, mmap_mode="r")
+    k, v = np.load(kp, mmap_mode="r"), np.load(vp, mmap_mode="r")
+    qn = np.asarray(q, np.float64)
+    oesa.attend(qn, _ListedRows(k, pos), _ListedRows(v, pos), sel, c0, n_init, W, scale, rows=list(rows))
+    return len(rows)
+
+
+def _esa_select_task(a):
+    """Oracle step for one sequence of a decode batch up to the selection:
+    compression of the new key into the cache, then the selection."""
+    import numpy as np
+    from oracle import esa as oesa
+    qp, kcp, knewp, Wp, bi, c0, n_init, W, topk, radius, clip, correction = a
+    q = np.asarray(np.load(qp, mmap_mode="r")[bi], np.float64)
+    kc = np.asarray(np.load(kcp, mmap_mode="r")[bi], np.float64)
+    Wn = np.load(Wp)
+    kc[c0:c0 + 1] = oesa.key_cache(np.asarray(np.load(knewp, mmap_mode="r")[bi], np.float64), Wn)
+    sel, _, _, _ = oesa.select(q, Wn, None, kc, c0, n_init, W, topk, radius, clip, correction=correction)
+    return bi, sel
 
 
 def _blas_threads() -> int:
@@ -765,78 +961,51 @@ def _cpu_model() -> str:
     return "unknown CPU"
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="moba_gqa_32k")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="run one plain device-to-device copy of BYTES before warmup (reference kernel for "
-                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
-              f"see DESIGN.md for how the path would shard.", file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    import query_aware_top_amd as qat
-    qat.lib()
-    w = make(args.workload)
-    torch.cuda.synchronize()
-    if args.copy_calibration:
-        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    for _ in range(args.warmup):
+def measure(w, steps, warmup):
+    """Times one workload: warmup, then `steps` timed steps (the library
+    brackets only the dominant kernel with events, on the stream it runs on,
+    so the roofline's launch time is measured live in this region), a second
+    untimed pass with every stage bracketed, and the spread of single steps
+    (for HBM-bound workloads also with L2 and the Infinity Cache flushed
+    before each step). Returns the fields of the bench line."""
+    qat = w.qat
+    for _ in range(warmup):
         w.step()
     torch.cuda.synchronize()
-    # timed region: the library brackets only the dominant kernel with events
-    # (on the stream it runs on), so the roofline's launch time is measured
-    # live in this region at the cost of two events per step
     qat.timing_enable(True)
     qat.timing_select(w.dominant)
     qat.timing_reset()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         w.step()
     stop.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    ms = start.elapsed_time(stop) / steps
     tot, n = qat.timing_query(w.dominant)
     dom_ms = round(tot / n, 4) if n else None
     # per-stage breakdown from a second, untimed pass with every stage bracketed
     qat.timing_select(None)
     qat.timing_reset()
-    for _ in range(args.steps):
+    for _ in range(steps):
         w.step()
     torch.cuda.synchronize()
     qat.timing_enable(False)
     kernels = {}
-    for name in ("moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn", "moba_current_attn",
-                 "moba_generic_attn", "moba_decode_select", "moba_decode_attn", "moba_decode_combine",
-                 "moba_bwd_dq_past", "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated", "esa_bwd_dq", "esa_bwd_kv",
-                 "cca_pool", "cca_attn",
-                 "esa_compress", "esa_qcompress", "esa_scores", "esa_decode_scan", "esa_topk",
-                 "esa_prefill_attn", "esa_decode_attn", "esa_generic_attn"):
+    for name in STAGES:
         tot, n = qat.timing_query(name)
         if n:
             kernels[name] = round(tot / n, 4)
     qat.timing_reset()
+
     # spread of single steps (outside the timed region above): events around
-    # each step; for the HBM-bound workload also with L2 and the 256 MiB
+    # each step; for the HBM-bound workloads also with L2 and the 256 MiB
     # Infinity Cache flushed before every step by reading 1 GiB of other data
     # (untimed; a read leaves clean lines, so the step pays no write-back)
     def step_times(flush):
         buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if flush else None
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in ev:
             if flush:
                 buf.sum()
@@ -844,8 +1013,7 @@ def main():
             w.step()
             b.record()
         torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in ev)
-        return t
+        return sorted(a.elapsed_time(b) for a, b in ev)
 
     def pct(t, q):
         return round(t[min(len(t) - 1, int(q * (len(t) - 1) + 0.5))], 4)
@@ -874,39 +1042,132 @@ def main():
     else:
         achieved = work / (dom_ms * 1e-3) / 1e12
         peak, unit = PEAK_F32_TFLOPS, "TFLOP/s"
-    value = w.value(ms * 1e-3)
+    roof = {"kernel": w.dominant, "bound": w.bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(w.dominant, w.name),
+            "work_per_launch": work, "avg_launch_ms": dom_ms}
     if cold_dom_ms:
         # the same kernel with L2 and the Infinity Cache flushed before each step
-        cold_rate = work / (cold_dom_ms * 1e-3) / 1e9
+        roof["cold_avg_launch_ms"] = cold_dom_ms
+        roof["cold_frac"] = round(work / (cold_dom_ms * 1e-3) / 1e9 / peak, 4)
+    return {"value": w.value(ms * 1e-3), "ms_per_step": ms, "roofline": roof, "kernels_avg_ms": kernels,
+            "step_ms": spread}
+
+
+STAGES = ("moba_meanpool", "moba_select", "moba_dispatch", "moba_past_attn", "moba_current_attn",
+          "moba_generic_attn", "moba_decode_select", "moba_decode_attn", "moba_decode_combine",
+          "moba_bwd_dq_past", "moba_bwd_dq", "moba_bwd_own", "moba_bwd_gated", "esa_bwd_dq", "esa_bwd_kv",
+          "cca_pool", "cca_attn",
+          "esa_compress", "esa_qcompress", "esa_scores", "esa_decode_scan", "esa_topk",
+          "esa_prefill_attn", "esa_decode_attn", "esa_generic_attn")
+
+# Workloads summarised in the default line beside moba_gqa_32k: the ESA
+# decode step (the metric's decode half), ESA chunked prefill and MoBA's
+# 512k fixed-sparsity case.
+EXTRA = ("esa_decode_128k", "esa_prefill_64k", "moba_long_512k")
+
+
+def summary(w, r):
+    """Compact record of one extra workload's measurement."""
+    roof = r["roofline"]
+    out = {"workload": w.name, "value": round(r["value"], 3), "unit": w.unit,
+           "ms_per_step": round(r["ms_per_step"], 4), "step_ms": r["step_ms"],
+           "dominant": {k: roof[k] for k in ("kernel", "bound", "achieved", "unit", "frac", "avg_launch_ms",
+                                             "traffic", "cold_frac", "cold_avg_launch_ms") if k in roof},
+           "kernels_avg_ms": r["kernels_avg_ms"]}
+    sb = getattr(w, "step_bytes", None)
+    if sb is not None and w.bound == "hbm" and not getattr(w, "per_head", False):
+        # HBM-bound step: algorithmic bytes of the whole step against its time
+        b = sb()
+        out["step_bytes"] = b
+        out["step_hbm_frac"] = round(b / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        if "cold_p50" in r["step_ms"]:
+            out["cold_step_hbm_frac"] = round(b / (r["step_ms"]["cold_p50"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    sel = getattr(w, "selection_bytes", None)
+    if sel is not None:   # MoBA gating over all rows: mean pool + block scores, HBM-bound
+        b = sel()
+        k = r["kernels_avg_ms"]
+        t = k.get("moba_meanpool", 0.0) + k.get("moba_select", 0.0)
+        if t > 0:
+            out["selection"] = {"bytes": b, "ms": round(t, 4), "GBps": round(b / (t * 1e-3) / 1e9, 1),
+                                "frac": round(b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="moba_gqa_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="measure only --workload (the default line otherwise also summarises "
+                         + ", ".join(EXTRA) + ")")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="run one plain device-to-device copy of BYTES before warmup (reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
+              f"see DESIGN.md for how the path would shard.", file=sys.stderr)
+        sys.exit(2)
+    # the oracle's worker processes are forked before anything touches the GPU
+    if not args.no_cpu_baseline:
+        cpu_pool()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import query_aware_top_amd as qat
+    qat.lib()
+    w = make(args.workload)
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    r = measure(w, args.steps, args.warmup)
     line = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": round(r["value"], 3),
         "unit": w.unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": w.higher_is_better,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs generated on the GPU; see DESIGN.md for the recipe)",
         "config": w.config(),
-        "roofline": {"kernel": w.dominant, "bound": w.bound, "achieved": round(achieved, 2), "peak": peak,
-                     "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": traffic_for(w.dominant, w.name), "work_per_launch": work,
-                     "avg_launch_ms": dom_ms},
-        "kernels_avg_ms": kernels,
-        "step_ms": spread,
+        "roofline": r["roofline"],
+        "kernels_avg_ms": r["kernels_avg_ms"],
+        "step_ms": r["step_ms"],
     }
-    if cold_dom_ms:
-        line["roofline"]["cold_avg_launch_ms"] = cold_dom_ms
-        line["roofline"]["cold_frac"] = round(cold_rate / peak, 4)
     if not args.no_cpu_baseline:
         cb = w.cpu_baseline()
         cb["sample"] += f"; host {_cpu_model()}, {os.cpu_count()} logical CPUs"
         line["cpu_baseline"] = cb
+    if args.workload == "moba_gqa_32k" and not args.no_extra:
+        del w
+        torch.cuda.empty_cache()
+        configs = {}
+        for name in EXTRA:
+            w2 = make(name)
+            torch.cuda.synchronize()
+            s2 = summary(w2, measure(w2, args.steps, args.warmup))
+            s2["config"] = w2.config()
+            if name == "esa_decode_128k":
+                line["decode"] = s2
+            else:
+                configs[name] = s2
+            del w2
+            torch.cuda.empty_cache()
+        line["configs"] = configs
     print(json.dumps(line), flush=True)
+    close_cpu_pool()
 
 
 if __name__ == "__main__":

@@ -44,3 +44,38 @@ def test_committed_counters_name_known_stages():
         workload, stage = key.split("/", 1)
         assert e["hbm_bytes_per_launch"] > 0 or stage in ("moba_bwd_runs",), key
         assert len(e["source_sha"]) == 16
+
+
+def test_oracle_tasks_run_over_the_worker_pool():
+    """The oracle baseline's worker pool and tasks on tiny staged inputs:
+    every row is processed once, and the ESA task's view of the staged key
+    rows returns the rows of the requested positions."""
+    import numpy as np
+    from oracle import esa as oesa
+    r = np.random.default_rng(3)
+    try:
+        n, hq, hkv, d, block = 64, 4, 2, 8, 16
+        qp = bench._stage("t_q", r.standard_normal((n, hq, d)).astype(np.float32))
+        kp = bench._stage("t_k", r.standard_normal((n, hkv, d)).astype(np.float32))
+        vp = bench._stage("t_v", r.standard_normal((n, hkv, d)).astype(np.float32))
+        from oracle import moba as omoba
+        kbar = omoba.block_means(np.load(kp).astype(np.float64), block)
+        items = [(qp, kp, vp, kbar, list(range(i, i + 8)), block, 3, 0.3) for i in range(0, n, 8)]
+        res, el = bench._run_parallel(bench._moba_rows_task, items, 60.0)
+        assert sum(res) == n and el > 0
+        # ESA: attention over a staged subset of rows equals attention over the full cache
+        T, m, H = 40, 4, 2
+        K, V = r.standard_normal((T, H, d)), r.standard_normal((T, H, d))
+        q = r.standard_normal((m, H, d))
+        c0, n_init, W, sel = T - m, 2, 6, np.array([5, 9, 20])
+        pos = oesa.key_list(sel, c0, n_init, W, T - 1)
+        a = (bench._stage("e_q", q), bench._stage("e_k", K[pos]), bench._stage("e_v", V[pos]), pos, sel, c0,
+             n_init, W, 0.5, [0, 3])
+        assert bench._esa_attend_task(a) == 2
+        # the view the task builds maps positions to the staged rows: same result as the full cache
+        o_full, _ = oesa.attend(q, K, V, sel, c0, n_init, W, 0.5, rows=[0, 3])
+        o_list, _ = oesa.attend(q, bench._ListedRows(K[pos], pos), bench._ListedRows(V[pos], pos), sel, c0,
+                                n_init, W, 0.5, rows=[0, 3])
+        assert np.array_equal(o_full, o_list)
+    finally:
+        bench.close_cpu_pool()
