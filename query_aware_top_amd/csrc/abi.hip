@@ -195,6 +195,9 @@ int moba_check(const qat_moba_params* p) {
   if (p->dtype != QAT_F32 && p->dtype != QAT_BF16) return fail(QAT_EINVAL, "unknown dtype %d", p->dtype);
   if (p->batch * p->q_len * p->n_q_heads >= (1ll << 27)) return fail(QAT_EUNSUPPORTED, "too many query rows");
   if (p->batch * p->seq_len * p->n_q_heads >= (1ll << 31)) return fail(QAT_EUNSUPPORTED, "q holds too many rows");
+  // one block's K (or V) rows are addressed with 32-bit byte offsets
+  if ((int64_t)p->block * p->n_kv_heads * p->head_dim * 4 >= (1ll << 31))
+    return fail(QAT_EUNSUPPORTED, "block * n_kv_heads * head_dim too large");
   return QAT_OK;
 }
 

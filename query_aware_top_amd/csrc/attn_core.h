@@ -160,6 +160,18 @@ struct FaContig {
       off[i] = (r * stride + ((lane % CPR) ^ fa_swz<D>(r)) * 8) * 2;
     }
   }
+  // As issue, with the tile's start in the per-lane offset, which the
+  // resource's range check covers (the scalar offset is not checked): rows
+  // of the tile past the region read as zero.
+  __device__ __forceinline__ void issue_checked(bf16* __restrict__ dst, __amdgpu_buffer_rsrc_t rsrc, int j0,
+                                                int stride) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int base = j0 * stride * 2;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (RPW * wave + i * RPI) * D), 16,
+                                               off[i] + base, 0, 0, 0);
+  }
   // rows [j0, j0 + 64) of the region (row j at j * stride elements) into dst
   __device__ __forceinline__ void issue(bf16* __restrict__ dst, __amdgpu_buffer_rsrc_t rsrc, int j0,
                                         int stride) const {
@@ -345,30 +357,31 @@ __device__ __forceinline__ void fa_finish_tile(FaState<D>& st, f32x16* s, const 
 // registers held), after which the caller may issue loads of its own and
 // fold them into the state (their wait also covers the tiles, which are
 // older); fa_segment_run then computes.
-template <int D, int NW, typename RowOfs>
-__device__ __forceinline__ void fa_segment_begin(const FaSmem<D>& sm, const bf16* __restrict__ K,
-                                                 const bf16* __restrict__ V, int n, RowOfs row_ofs) {
+//
+// The _tiles forms take an issuer: issue(dst, is_v, t) loads tile t of K
+// (is_v false) or V into the LDS buffer dst for the calling wave.
+template <int D, typename Issue>
+__device__ __forceinline__ void fa_segment_begin_tiles(const FaSmem<D>& sm, int n, Issue issue) {
   if (n <= 0) return;
   const int nt = (n + kKT - 1) / kKT;
-  fa_issue_one<D, NW>(sm.k0, K, 0, n, row_ofs);
-  fa_issue_one<D, NW>(sm.v0, V, 0, n, row_ofs);
+  issue(sm.k0, false, 0);
+  issue(sm.v0, true, 0);
   if (nt > 1) {
-    fa_issue_one<D, NW>(sm.k1, K, kKT, n, row_ofs);
-    fa_issue_one<D, NW>(sm.v1, V, kKT, n, row_ofs);
+    issue(sm.k1, false, 1);
+    issue(sm.v1, true, 1);
   }
 }
 
-template <int D, int NW, bool CAN_MASK, typename RowOfs, typename KeyOk, typename TileFull>
-__device__ __forceinline__ void fa_segment_run(FaState<D>& st, const FaSmem<D>& sm, const bf16* __restrict__ K,
-                                               const bf16* __restrict__ V, int n, float scale_log2,
-                                               RowOfs row_ofs, KeyOk key_ok, TileFull tile_full) {
+template <int D, bool CAN_MASK, typename Issue, typename KeyOk, typename TileFull>
+__device__ __forceinline__ void fa_segment_run_tiles(FaState<D>& st, const FaSmem<D>& sm, int n, float scale_log2,
+                                                     Issue issue, KeyOk key_ok, TileFull tile_full) {
   if (n <= 0) return;
   const int nt = (n + kKT - 1) / kKT;
   auto issue_k = [&](bf16* dst, int t) {
-    if (t < nt) fa_issue_one<D, NW>(dst, K, t * kKT, n, row_ofs);
+    if (t < nt) issue(dst, false, t);
   };
   auto issue_v = [&](bf16* dst, int t) {
-    if (t < nt) fa_issue_one<D, NW>(dst, V, t * kKT, n, row_ofs);
+    if (t < nt) issue(dst, true, t);
   };
   // prologue (K0, V0, K1, V1 issued by fa_segment_begin): S(0) computed,
   // then K2 into K0's buffer (after every wave has read K0)
@@ -401,6 +414,25 @@ __device__ __forceinline__ void fa_segment_run(FaState<D>& st, const FaSmem<D>& 
   }
   fa_wait_loads();
   fa_lds_barrier();
+}
+
+// Row-offset forms: key j of the segment at element offset row_ofs(j) from
+// K / V (fa_issue_one).
+template <int D, int NW, typename RowOfs>
+__device__ __forceinline__ void fa_segment_begin(const FaSmem<D>& sm, const bf16* __restrict__ K,
+                                                 const bf16* __restrict__ V, int n, RowOfs row_ofs) {
+  fa_segment_begin_tiles<D>(sm, n, [&](bf16* dst, bool is_v, int t) {
+    fa_issue_one<D, NW>(dst, is_v ? V : K, t * kKT, n, row_ofs);
+  });
+}
+
+template <int D, int NW, bool CAN_MASK, typename RowOfs, typename KeyOk, typename TileFull>
+__device__ __forceinline__ void fa_segment_run(FaState<D>& st, const FaSmem<D>& sm, const bf16* __restrict__ K,
+                                               const bf16* __restrict__ V, int n, float scale_log2,
+                                               RowOfs row_ofs, KeyOk key_ok, TileFull tile_full) {
+  fa_segment_run_tiles<D, CAN_MASK>(st, sm, n, scale_log2, [&](bf16* dst, bool is_v, int t) {
+    fa_issue_one<D, NW>(dst, is_v ? V : K, t * kKT, n, row_ofs);
+  }, key_ok, tile_full);
 }
 
 template <int D, int NW, bool CAN_MASK, typename RowOfs, typename KeyOk, typename TileFull>

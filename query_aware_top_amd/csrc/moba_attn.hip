@@ -545,8 +545,16 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
   const bf16* vb = v + ((bi * seq_len + kpos0) * hkv + g) * D;
   const int kv_stride = (int)(hkv * D);
   const int nkeys = (int)(t_last - kpos0 + 1);
-  auto row_ofs = [=](int j) { return j * kv_stride; };
-  fa_segment_begin<D, NW>(sm, kb, vb, nkeys, row_ofs);
+  // The block's rows [kpos0, t_last] through buffer resources: fixed
+  // per-lane offsets, the tile's start added to the range-checked vector
+  // offset, so rows of the last tile past t_last read as zero (their scores
+  // are masked) and nothing past the region is touched.
+  FaContig<D, NW> ctg;
+  ctg.init(kv_stride);
+  const uint32_t region = (uint32_t)(((int64_t)(nkeys - 1) * kv_stride + D) * 2);
+  const __amdgpu_buffer_rsrc_t rk = fa_rsrc(kb, region), rv = fa_rsrc(vb, region);
+  auto issue = [&](bf16* dst, bool is_v, int tile) { ctg.issue_checked(dst, is_v ? rv : rk, tile * kKT, kv_stride); };
+  fa_segment_begin_tiles<D>(sm, nkeys, issue);
 
   FaState<D> st;
   fa_init<D>(st, q + ((bi * seq_len + (valid ? t : t0)) * hq + h) * D, valid);
@@ -555,37 +563,22 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
   // 2^(lse - m) (kept by the lower half-wave only: l is summed over the two
   // halves at the end), o = sum of 2^(lse - m) o_p. The lane's accumulator
   // holds d = 32 tq + 8 gi + 4 hl + 0..3. These loads are younger than the
-  // tiles', so waiting for them costs no extra latency.
-  auto fold = [&](float l2, const uint2* pov) {
-    const float m_new = fmaxf(st.m, l2);
-    const float a = st.m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
-    const float w = __builtin_amdgcn_exp2f(l2 - m_new);
-    st.l = st.l * a + (hl == 0 ? w : 0.f);
-#pragma unroll
-    for (int tq = 0; tq < D / 32; ++tq)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const uint2 u = pov[tq * 4 + gi];
-        const float v0 = __builtin_bit_cast(float, u.x << 16), v1 = __builtin_bit_cast(float, u.x & 0xffff0000u);
-        const float v2 = __builtin_bit_cast(float, u.y << 16), v3 = __builtin_bit_cast(float, u.y & 0xffff0000u);
-        st.o[tq][4 * gi + 0] = st.o[tq][4 * gi + 0] * a + w * v0;
-        st.o[tq][4 * gi + 1] = st.o[tq][4 * gi + 1] * a + w * v1;
-        st.o[tq][4 * gi + 2] = st.o[tq][4 * gi + 2] * a + w * v2;
-        st.o[tq][4 * gi + 3] = st.o[tq][4 * gi + 3] * a + w * v3;
-      }
-    st.m = m_new;
+  // tiles', so waiting for them costs no extra latency. Every (row, slot)
+  // partial lse is -inf unless the slot's block was dispatched (the lse
+  // array is cleared before the past-block pass), so the loads need no look
+  // at the gating.
+  auto unpack = [](const uint2 u, float* f) {
+    f[0] = __builtin_bit_cast(float, u.x << 16);
+    f[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+    f[2] = __builtin_bit_cast(float, u.y << 16);
+    f[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
   };
-  // every (row, slot) partial lse is -inf unless the slot's block was
-  // dispatched (the lse array is cleared before the past-block pass), so the
-  // loads need no look at the gating: one memory round trip, beside the tiles'
-  for (int s0 = 0; s0 < km; s0 += kPreSlots) {   // one round for k <= kPreSlots + 1
-    float plse[kPreSlots];
-    uint2 po[kPreSlots][D / 8];
+  auto load_slots = [&](int s0, float* plse, uint2 (*po)[D / 8]) {
 #pragma unroll
     for (int sl = 0; sl < kPreSlots; ++sl) {
       const int64_t pidx = row * km + min(s0 + sl, km - 1);
       const float lv = part_lse[pidx];
-      plse[sl] = (valid && s0 + sl < km) ? lv : -__builtin_inff();
+      plse[sl] = (valid && s0 + sl < km) ? lv * kLog2e : -__builtin_inff();
       // partial rows are stored in split halves: this lane's D/2 values are
       // contiguous, in accumulator order
       const bf16* src = part_o + pidx * D + hl * (D / 2);
@@ -596,18 +589,73 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
         po[sl][2 * i + 1] = make_uint2(w[2], w[3]);
       }
     }
+  };
+  {
+    // first round: the state is empty, so o = sum_s w_s o_s under one max
+    // (no rescale of a zero accumulator)
+    float plse[kPreSlots];
+    uint2 po[kPreSlots][D / 8];
+    load_slots(0, plse, po);
+    float mx = plse[0];
 #pragma unroll
-    for (int sl = 0; sl < kPreSlots; ++sl)
-      if (plse[sl] != -__builtin_inff()) fold(plse[sl] * kLog2e, po[sl]);
+    for (int sl = 1; sl < kPreSlots; ++sl) mx = fmaxf(mx, plse[sl]);
+    const float base = mx == -__builtin_inff() ? 0.f : mx;   // all empty: every weight 0
+    float w[kPreSlots], wsum = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kPreSlots; ++sl) {
+      w[sl] = __builtin_amdgcn_exp2f(plse[sl] - base);
+      wsum += w[sl];
+    }
+    st.m = mx;
+    st.l = hl == 0 ? wsum : 0.f;
+#pragma unroll
+    for (int tq = 0; tq < D / 32; ++tq)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        float f[4];
+        unpack(po[0][tq * 4 + gi], f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.o[tq][4 * gi + e] = w[0] * f[e];
+#pragma unroll
+        for (int sl = 1; sl < kPreSlots; ++sl) {
+          unpack(po[sl][tq * 4 + gi], f);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.o[tq][4 * gi + e] = __builtin_fmaf(w[sl], f[e], st.o[tq][4 * gi + e]);
+        }
+      }
   }
-
+  // later rounds (k > kPreSlots + 1): folded into the running state
+  for (int s0 = kPreSlots; s0 < km; s0 += kPreSlots) {
+    float plse[kPreSlots];
+    uint2 po[kPreSlots][D / 8];
+    load_slots(s0, plse, po);
+#pragma unroll
+    for (int sl = 0; sl < kPreSlots; ++sl) {
+      if (plse[sl] == -__builtin_inff()) continue;
+      const float m_new = fmaxf(st.m, plse[sl]);
+      const float a = st.m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
+      const float wt = __builtin_amdgcn_exp2f(plse[sl] - m_new);
+      st.l = st.l * a + (hl == 0 ? wt : 0.f);
+#pragma unroll
+      for (int tq = 0; tq < D / 32; ++tq)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          float f[4];
+          unpack(po[sl][tq * 4 + gi], f);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            st.o[tq][4 * gi + e] = __builtin_fmaf(wt, f[e], st.o[tq][4 * gi + e] * a);
+        }
+      st.m = m_new;
+    }
+  }
 
   // keys are block-relative: this lane attends keys j <= lim, and every lane
   // of the wave attends keys j <= wlim
   const int lim = valid ? (int)(t - kpos0) : -1;
   const int wlim = (int)(t0 - kpos0) + (wave * 32) / pack;
-  fa_segment_run<D, NW, true>(st, sm, kb, vb, nkeys, scale_log2, row_ofs, [=](int j) { return j <= lim; },
-                              [=](int j0) { return j0 + kKT - 1 <= wlim; });
+  fa_segment_run_tiles<D, true>(st, sm, nkeys, scale_log2, issue, [=](int j) { return j <= lim; },
+                                [=](int j0) { return j0 + kKT - 1 <= wlim; });
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
   if (lse_out && valid && hl == 0) lse_out[row] = lse;
