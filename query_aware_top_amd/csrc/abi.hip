@@ -45,6 +45,7 @@ struct EsaLayout {
   int nsplit_q = 1, nkeysplit = 1, nqsplit = 1, nscan = 1, ndec = 1;
   int64_t n_mid = 0, mid0 = 0, rows = 0;
   double* qpart = nullptr;
+  float* qpart32 = nullptr;   // float32 split partials of the matrix-core query compression
   float* qc = nullptr;
   qat::bf16* qhi = nullptr;
   qat::bf16* qlo = nullptr;
@@ -111,6 +112,8 @@ EsaLayout esa_layout(const qat_esa_params* p, void* ws) {
   L.ndec = qat::esa_decode_splits(p->batch, p->n_init, p->topk, p->window);
   qat::Carver c(ws);
   L.qpart = c.take<double>((size_t)L.nsplit_q * L.rows * dcq);
+  L.qpart32 = c.take<float>(dcq && qat::compress_bf16_rows_ok(L.rows, D, p->d_c)
+                                ? qat::compress_bf16_rows_part_floats(L.rows, p->d_c) : 0);
   L.qc = c.take<float>((size_t)L.rows * dcq);
   L.qhi = c.take<qat::bf16>((size_t)L.rows * dcq);
   L.qlo = c.take<qat::bf16>((size_t)L.rows * dcq);
@@ -440,13 +443,19 @@ QAT_EXPORT int esa_select(const qat_esa_params* p, const void* q, const void* Wq
   hipStream_t s = (hipStream_t)stream;
   const bool bf = p->dtype == QAT_BF16;
   const int64_t D = p->n_heads * p->head_dim;
-  // q~ = Wq concat_h(q) + bq, float64 accumulation -> float32 + hi/lo bf16
+  // q~ = Wq concat_h(q) + bq -> float32 + hi/lo bf16: a chunk's rows on the
+  // bf16 matrix cores (float32 accumulation), decode rows in float64
   hipError_t e;
   {
     qat::KTimer tm("esa_qcompress", s);
-    e = qat::launch_compress_partial(q, L.rows, D, D, bf, Wq, bf, p->d_c, L.nsplit_q, L.qpart, s);
-    if (e == hipSuccess)
-      e = qat::launch_compress_finalize(L.qpart, L.nsplit_q, L.rows, p->d_c, bq, L.qc, p->d_c, 2, L.qhi, L.qlo, s);
+    if (bf && qat::compress_bf16_rows_ok(L.rows, D, p->d_c)) {
+      e = qat::launch_compress_bf16_rows(q, L.rows, D, D, Wq, p->d_c, bq, L.qpart32, L.qc, L.qhi, L.qlo, s);
+    } else {
+      e = qat::launch_compress_partial(q, L.rows, D, D, bf, Wq, bf, p->d_c, L.nsplit_q, L.qpart, s);
+      if (e == hipSuccess)
+        e = qat::launch_compress_finalize(L.qpart, L.nsplit_q, L.rows, p->d_c, bq, L.qc, p->d_c, 2, L.qhi, L.qlo,
+                                          s);
+    }
   }
   if (e != hipSuccess) return hip_status(e, "esa_select: query compression");
   const qat::bf16* kc = (const qat::bf16*)kc_cache;

@@ -154,14 +154,15 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
 // (o, m, l) per (sequence, split, head) go to scratch; a second kernel merges
 // them by log-sum-exp.
 // keys per split: the fewest whole rounds of resident workgroups (two per CU
-// at this kernel's register use) that give splits of 32..128 keys; 64 keys
-// when no round count does
+// at this kernel's register use) that give splits of 32..256 keys (one round
+// of 512 workgroups at the 16-sequence 128k shape: 197 keys each, measured
+// faster than two rounds of 98); 64 keys when no round count does
 int esa_decode_keys_per_split(int64_t batch, int64_t nkeys_max) {
   constexpr int64_t kSlots = 2 * 256;
   for (int64_t rounds = 1; rounds <= 8; ++rounds) {
     const int64_t ns = std::max<int64_t>(1, rounds * kSlots / batch);
     const int64_t kps = cdiv(nkeys_max, ns);
-    if (kps >= 32 && kps <= 128) return (int)kps;
+    if (kps >= 32 && kps <= 256) return (int)kps;
   }
   return 64;
 }
@@ -273,8 +274,8 @@ __global__ void esa_decode_combine_kernel(const float* __restrict__ po, const fl
   if (c0 > n_init) n_l = c0 - max(n_init, c0 - window);
   const int64_t nkeys = n_i + n_sel[ph ? bi * H : bi] + n_l + 1;
   const int ns = (int)min((int64_t)nsplit_max, cdiv(nkeys, kps));
-  // online log-sum-exp merge over the splits, 8 splits' loads in flight
-  constexpr int U = 8;
+  // online log-sum-exp merge over the splits, 16 splits' loads in flight
+  constexpr int U = 16;
   float M = -__builtin_inff(), L = 0.f, O = 0.f;
   for (int s0 = 0; s0 < ns; s0 += U) {
     float mv[U], lv[U], ov[U];
