@@ -114,10 +114,17 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_kv_kernel(
   const bf16* dbase = dout + ((bi * m + i_start) * H + h) * D;
   const int HD = (int)(H * D);
   const float sl2 = scale * kLog2e;
+  // the q / dO rows [i_start, m) of head h through buffer resources: fixed
+  // per-lane offsets, the tile start in the range-checked offset (rows past
+  // m read as zero; their p is masked)
+  FaContig<D, kBwdNW> ctg;
+  ctg.init(HD);
+  const uint32_t region = nrows > 0 ? (uint32_t)(((int64_t)(nrows - 1) * HD + D) * 2) : 0u;
+  const __amdgpu_buffer_rsrc_t rq = fa_rsrc(qbase, region), rd = fa_rsrc(dbase, region);
   auto issue = [&](bf16* qdst, bf16* ddst, int buf, int rt) {
     const int r0 = rt * 64, n = min(64, nrows - r0);
-    fa_issue_one<D, kBwdNW>(qdst, qbase, 0, n, [=](int jj) { return (r0 + jj) * HD; });
-    fa_issue_one<D, kBwdNW>(ddst, dbase, 0, n, [=](int jj) { return (r0 + jj) * HD; });
+    ctg.issue_checked(qdst, rq, r0, HD);
+    ctg.issue_checked(ddst, rd, r0, HD);
     if (wave == 0) {   // rows past the tile's end repeat its last row (masked)
       const int64_t row = (bi * m + i_start + r0 + min(lane, n - 1)) * H + h;
       __builtin_amdgcn_global_load_lds((const global_void*)(lse + row), (lds_void*)(s_lse + buf * 64), 4, 0, 0);

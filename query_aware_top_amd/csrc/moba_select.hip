@@ -421,8 +421,10 @@ constexpr int kSelWaves = 4;
 constexpr int kSelRowsPerWave = 64;
 constexpr int kSelBlocks = 32;   // blocks per round (one MFMA row tile)
 
+// Three workgroups per CU fit the registers of top lists up to 3 entries;
+// the 7- and 15-entry lists need the register budget of two.
 template <int D, int KMAX>
-__global__ __launch_bounds__(kSelWaves * 64, 3) void moba_select_mfma_kernel(
+__global__ __launch_bounds__(kSelWaves * 64, (KMAX <= 3 ? 3 : 2)) void moba_select_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ planes, int64_t plane_stride, int32_t* __restrict__ blk,
     int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk) {
   constexpr int KP = D + 8;   // padded LDS row of one block's mean
