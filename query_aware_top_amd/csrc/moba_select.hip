@@ -16,8 +16,8 @@ namespace qat {
 // ---------------------------------------------------------------------------
 // Mean pool, pass 1: a workgroup sums a slice of one block's tokens for all
 // Hkv*d columns in float64. A thread owns 8 adjacent columns (one 16-byte
-// load per token for bf16) and keeps kMpUnroll token rows in flight; the
-// stream of K is read once, in whole rows.
+// load per token for bf16) and keeps up to 2 * kMpUnroll token rows in
+// flight; the stream of K is read once, in whole rows.
 constexpr int kMpThreads = 128;
 constexpr int kMpUnroll = 8;
 
@@ -39,6 +39,34 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
   }
 }
 
+// Raw token pieces (8 columns) as loaded, converted only when summed, so the
+// loads of the next kMpUnroll rows can be in flight during the sums.
+template <typename T>
+struct MpRaw;
+template <>
+struct MpRaw<bf16> {
+  bf16x8 v;
+};
+template <>
+struct MpRaw<float> {
+  f32x4 a, b;
+};
+__device__ __forceinline__ MpRaw<bf16> mp_load(const bf16* p) { return {*(const bf16x8*)p}; }
+__device__ __forceinline__ MpRaw<float> mp_load(const float* p) {
+  return {*(const f32x4*)p, *(const f32x4*)(p + 4)};
+}
+__device__ __forceinline__ void mp_add(double (&a)[8], const MpRaw<bf16>& r) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] += (double)(float)r.v[i];
+}
+__device__ __forceinline__ void mp_add(double (&a)[8], const MpRaw<float>& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] += (double)r.a[i];
+    a[4 + i] += (double)r.b[i];
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kMpThreads) void meanpool_partial_kernel(
     const T* __restrict__ k, int64_t seq_len, int64_t cols, int block, int tokens_per_split,
@@ -51,25 +79,40 @@ __global__ __launch_bounds__(kMpThreads) void meanpool_partial_kernel(
   const T* base = k + bi * seq_len * cols;
   double* dst = partial + ((bi * nbc + b) * nsplit + split) * cols;
   for (int64_t cg = threadIdx.x; cg < cols / 8; cg += kMpThreads) {
+    const T* col = base + cg * 8;
     double a[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = 0.0;
-    int64_t t = t0;
-    for (; t + kMpUnroll <= t1; t += kMpUnroll) {   // full groups: all loads issued before any add
-      float v[kMpUnroll][8];
+    // full groups of kMpUnroll rows, double-buffered: group g + 1 loads while
+    // group g is summed (rows still summed in order)
+    MpRaw<T> ra[kMpUnroll], rb[kMpUnroll];
+    auto load_group = [&](MpRaw<T> (&r)[kMpUnroll], int64_t t) {
 #pragma unroll
-      for (int u = 0; u < kMpUnroll; ++u) load8<T>(base + (t + u) * cols + cg * 8, v[u]);
+      for (int u = 0; u < kMpUnroll; ++u) r[u] = mp_load(col + (t + u) * cols);
+      __builtin_amdgcn_sched_barrier(0);   // issue the loads here, ahead of the sums
+    };
+    auto add_group = [&](const MpRaw<T> (&r)[kMpUnroll]) {
 #pragma unroll
-      for (int u = 0; u < kMpUnroll; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] += (double)v[u][i];
+      for (int u = 0; u < kMpUnroll; ++u) mp_add(a, r[u]);
+    };
+    const int64_t ng = (t1 - t0) / kMpUnroll;
+    int64_t g = 0;
+    if (ng > 0) load_group(ra, t0);
+    for (; g + 2 < ng; g += 2) {   // both prefetches unconditional, so each wait is for one group
+      load_group(rb, t0 + (g + 1) * kMpUnroll);
+      add_group(ra);
+      load_group(ra, t0 + (g + 2) * kMpUnroll);
+      add_group(rb);
     }
-    for (; t < t1; ++t) {
-      float v[8];
-      load8<T>(base + t * cols + cg * 8, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] += (double)v[i];
+    if (g + 1 < ng) {
+      load_group(rb, t0 + (g + 1) * kMpUnroll);
+      add_group(ra);
+      add_group(rb);
+    } else if (g < ng) {
+      add_group(ra);
     }
+    int64_t t = t0 + ng * kMpUnroll;
+    for (; t < t1; ++t) mp_add(a, mp_load(col + t * cols));
 #pragma unroll
     for (int i = 0; i < 8; ++i) dst[cg * 8 + i] = a[i];
   }
@@ -138,6 +181,7 @@ __global__ __launch_bounds__(256) void meanpool_direct_kernel(
 // remainder of the previous ones), the operands of the matrix-core scoring.
 // The partials cover blocks [first, first + count) of each sequence; the
 // means land in a [batch, nbc_total, cols] array.
+constexpr int kMpMaxSplits = 32;   // slices per block: see meanpool_tokens_per_split
 __global__ void meanpool_finalize_kernel(const double* __restrict__ partial, int nsplit, int64_t count,
                                          int64_t nbc_total, int64_t first, int64_t nrows, int64_t cols, int block,
                                          float* __restrict__ kbar, bf16* __restrict__ planes) {
@@ -145,8 +189,15 @@ __global__ void meanpool_finalize_kernel(const double* __restrict__ partial, int
   const int64_t total = nrows * cols;
   if (idx >= total) return;
   const int64_t r = idx / cols, c = idx % cols;
+  // all of the element's slice sums in flight at once, then added in order
+  const double* pp = partial + r * nsplit * cols + c;
+  double v[kMpMaxSplits];
+#pragma unroll
+  for (int i = 0; i < kMpMaxSplits; ++i) v[i] = i < nsplit ? pp[(int64_t)i * cols] : 0.0;
   double s = 0.0;
-  for (int i = 0; i < nsplit; ++i) s += partial[(r * nsplit + i) * cols + c];
+#pragma unroll
+  for (int i = 0; i < kMpMaxSplits; ++i)
+    if (i < nsplit) s += v[i];
   const float x = (float)(s / (double)block);
   kbar[((r / count) * nbc_total + first + r % count) * cols + c] = x;
   if (planes) {
@@ -592,8 +643,36 @@ __device__ __forceinline__ uint32_t sel_swap_halves(uint32_t x) {
   return r[0] ^ r[1] ^ x;   // the value of lane (l + 32) mod 64
 }
 
+// Stages the three planes of blocks 0 .. nb_lds - 1 of one (sequence, KV
+// head) into LDS rows of D + 8 elements (the pad spreads a column of rows over
+// all banks): [plane][block][D + 8].
+template <int D>
+__device__ __forceinline__ void sel_stage_planes(bf16* kb_s, const bf16* pg, int64_t plane_stride, int64_t hkv,
+                                                 int nb_lds) {
+  constexpr int KP = D + 8;
+  const int pieces = 3 * nb_lds * (D / 8);
+  constexpr int U = 8;
+  for (int i0 = threadIdx.x; i0 < pieces; i0 += U * kSelPWaves * 64) {
+    bf16x8 pc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {   // clamped index: every load is in bounds, all in flight at once
+      const int i = min(i0 + u * kSelPWaves * 64, pieces - 1);
+      const int pl = i / (nb_lds * (D / 8)), rem = i % (nb_lds * (D / 8));
+      pc[u] = *(const bf16x8*)(pg + pl * plane_stride + (int64_t)(rem / (D / 8)) * hkv * D + (rem % (D / 8)) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kSelPWaves * 64;
+      if (i < pieces) {
+        const int pl = i / (nb_lds * (D / 8)), rem = i % (nb_lds * (D / 8));
+        *(bf16x8*)&kb_s[(pl * nb_lds + rem / (D / 8)) * KP + (rem % (D / 8)) * 8] = pc[u];
+      }
+    }
+  }
+}
+
 template <int D, int KMAX>
-__global__ __launch_bounds__(kSelPWaves * 64, KMAX >= 7 ? 2 : 3) void moba_select_resident_kernel(
+__global__ __launch_bounds__(kSelPWaves * 64, 2) void moba_select_resident_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ planes, int64_t plane_stride, int32_t* __restrict__ blk,
     int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk,
     int nb_lds) {
@@ -603,56 +682,48 @@ __global__ __launch_bounds__(kSelPWaves * 64, KMAX >= 7 ? 2 : 3) void moba_selec
   const int64_t bi = blockIdx.y / hkv, g = blockIdx.y % hkv;
   const int64_t gs = hq / hkv;
   const int km = topk - 1;
-  {
-    const bf16* pg = planes + ((bi * nbc) * hkv + g) * D;
-    const int pieces = 3 * nb_lds * (D / 8);
-    constexpr int U = 8;
-    for (int i0 = threadIdx.x; i0 < pieces; i0 += U * kSelPWaves * 64) {
-      bf16x8 pc[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {   // clamped index: every load is in bounds, all in flight at once
-        const int i = min(i0 + u * kSelPWaves * 64, pieces - 1);
-        const int pl = i / (nb_lds * (D / 8)), rem = i % (nb_lds * (D / 8));
-        pc[u] = *(const bf16x8*)(pg + pl * plane_stride + (int64_t)(rem / (D / 8)) * hkv * D + (rem % (D / 8)) * 8);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * kSelPWaves * 64;
-        if (i < pieces) {
-          const int pl = i / (nb_lds * (D / 8)), rem = i % (nb_lds * (D / 8));
-          *(bf16x8*)&kb_s[(pl * nb_lds + rem / (D / 8)) * KP + (rem % (D / 8)) * 8] = pc[u];
-        }
-      }
-    }
-  }
+  sel_stage_planes<D>(kb_s, planes + ((bi * nbc) * hkv + g) * D, plane_stride, hkv, nb_lds);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int hl = lane >> 5, l32 = lane & 31;
-  const int64_t nchunks = gs * ((q_len + 63) / 64);
-  const int64_t stride = (int64_t)gridDim.x * kSelPWaves;
-  auto load_q = [&](int64_t c, bf16x8 (&xa)[D / 16], bf16x8 (&xb)[D / 16]) {
-    const int64_t rc = c / gs, h = g * gs + c % gs;
-    const int64_t ra = min(rc * 64 + l32, q_len - 1), rb = min(rc * 64 + 32 + l32, q_len - 1);
-    const bf16* pa = q + ((bi * seq_len + q_start + ra) * hq + h) * D + hl * 8;
-    const bf16* pb = q + ((bi * seq_len + q_start + rb) * hq + h) * D + hl * 8;
+  // Chunk bookkeeping stays in wave-uniform 32-bit integers (positions and
+  // block indices fit in 32 bits, seq_len < 2^31): chunk c is 64-row slice
+  // rc = c / gs of group head hh = c % gs, and a wave steps c by `stride`.
+  const int gsi = (int)gs;
+  const int ql = (int)q_len, qs = (int)q_start;
+  const int nrc = (ql + 63) / 64;
+  const int stride = (int)gridDim.x * kSelPWaves;
+  const int st_rc = stride / gsi, st_hh = stride % gsi;
+  const int c_first = (int)blockIdx.x * kSelPWaves + wave;
+  int rc = c_first / gsi, hh = c_first % gsi;
+  const int64_t row_el = hq * D;   // elements from one position to the next
+  const bf16* qg = q + ((bi * seq_len + q_start) * hq + g * gs) * D + hl * 8;
+  auto load_q = [&](int rc_, int hh_, bf16x8 (&xa)[D / 16], bf16x8 (&xb)[D / 16]) {
+    const int ra = min(rc_ * 64 + l32, ql - 1), rb = min(rc_ * 64 + 32 + l32, ql - 1);
+    const bf16* pa = qg + ra * row_el + hh_ * D;
+    const bf16* pb = qg + rb * row_el + hh_ * D;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       xa[ks] = *(const bf16x8*)(pa + ks * 16);
       xb[ks] = *(const bf16x8*)(pb + ks * 16);
     }
   };
-  int64_t c = (int64_t)blockIdx.x * kSelPWaves + wave;
   bf16x8 qa[D / 16], qb[D / 16];
-  if (c < nchunks) load_q(c, qa, qb);
-  for (; c < nchunks; c += stride) {
-    const bool more = c + stride < nchunks;
-    // positions and block indices fit in 32 bits (seq_len < 2^31)
-    const int rc = (int)(c / gs), h = (int)(g * gs + c % gs);
+  if (rc < nrc) load_q(rc, hh, qa, qb);
+  while (rc < nrc) {
+    int rn = rc + st_rc, hn = hh + st_hh;   // the wave's next chunk
+    if (hn >= gsi) {
+      hn -= gsi;
+      ++rn;
+    }
+    const bool more = rn < nrc;
+    const int h = (int)g * gsi + hh;
     const int ra = rc * 64 + l32, rb = ra + 32;   // query columns of the two score tiles
-    const int ql = (int)q_len, qs = (int)q_start;
     const int cur_a = (qs + min(ra, ql - 1)) / block;
     const int cur_b = (qs + min(rb, ql - 1)) / block;
+    const int own0 = (qs + rc * 64) / block;   // the chunk's smallest own block
     const int t_last = qs + min(ql, rc * 64 + 64) - 1;
     const int nbr = km > 0 ? min((int)nbc, t_last / block) : 0;   // <= nb_lds
     float tva[KMAX], tvb[KMAX];
@@ -683,11 +754,11 @@ __global__ __launch_bounds__(kSelPWaves * 64, KMAX >= 7 ? 2 : 3) void moba_selec
       __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
       // the next chunk's queries replace these once the last round's matrix
       // ops have read them: their loads overlap the selection work below
-      if (c0 + 32 >= nbr && more) load_q(c + stride, qa, qb);
+      if (c0 + 32 >= nbr && more) load_q(rn, hn, qa, qb);
       // blocks c0 + bb with bb >= n are not candidates of the column's row;
       // when even the chunk's first row (the smallest own block) has all 32
       // as candidates, the round needs no mask (wave-uniform test)
-      if ((qs + rc * 64) / block - c0 >= 32) {
+      if (own0 - c0 >= 32) {
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
@@ -708,7 +779,7 @@ __global__ __launch_bounds__(kSelPWaves * 64, KMAX >= 7 ? 2 : 3) void moba_selec
           }
       }
     }
-    if (nbr <= 0 && more) load_q(c + stride, qa, qb);
+    if (nbr <= 0 && more) load_q(rn, hn, qa, qb);
     // lane l < 32 keeps query ra (its list of column a), lane l + 32 keeps
     // query rb; each receives the other half's list of its query
     float ov[KMAX], rv[KMAX];
@@ -746,13 +817,237 @@ __global__ __launch_bounds__(kSelPWaves * 64, KMAX >= 7 ? 2 : 3) void moba_selec
       out[npick] = cur;
       for (int i = npick + 1; i < topk; ++i) out[i] = -1;
     }
+    rc = rn;
+    hh = hn;
   }
+}
+
+// The same resident scheme on the 16x16x32 matrix op, for top lists of up to
+// three past blocks. Its B operand gives each query row to four lanes with
+// 16 consecutive bytes each, so one load instruction reads 64 contiguous
+// bytes of 16 rows (the 32x32x16 layout reads 32 bytes of 32 rows, which
+// streams the queries markedly slower from HBM). A wave works through its
+// 64-row chunk in half-rounds of 16 blocks: per half-round lane l = j + 16 kg
+// holds the scores of blocks 4 kg + 0..3 of the half-round for query rows
+// j, j + 16, j + 32, j + 48 of the chunk, and keeps a top list per row. At
+// the end of the chunk two exchanges (across lane bit 5, then bit 4) bring
+// the four partial lists of row l to lane l, merged in the full (score desc,
+// block asc) order, so the result again equals one ordered insertion pass
+// over all blocks. Half-rounds past the chunk's last candidate block are
+// skipped.
+constexpr int kSel16MaxK = 3;   // longest past-block list of the 16x16x32 variant
+
+// int vectors at the 4-byte alignment of a blk row
+typedef int i32x2_u __attribute__((ext_vector_type(2), aligned(4)));
+typedef int i32x3_u __attribute__((ext_vector_type(3), aligned(4)));
+typedef int i32x4_u __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __forceinline__ uint32_t sel_swap_rows(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return r[0] ^ r[1] ^ x;   // the value of lane l ^ 16
+}
+
+template <int KMAX>
+__device__ __forceinline__ void top_merge_from(float (&tv)[KMAX], int (&ti)[KMAX], const float (&rv)[KMAX],
+                                               const int (&ri)[KMAX]) {
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) top_merge<KMAX>(tv, ti, rv[i], ri[i]);
+}
+
+template <int D, int KMAX>
+__global__ __launch_bounds__(kSelPWaves * 64, 3) void moba_select_resident16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ planes, int64_t plane_stride, int32_t* __restrict__ blk,
+    int64_t seq_len, int64_t hq, int64_t hkv, int64_t nbc, int64_t q_start, int64_t q_len, int block, int topk,
+    int nb_lds) {
+  constexpr int KP = D + 8;
+  constexpr int KS = D / 32;   // k-steps of the matrix op
+  static_assert(KMAX <= kSel16MaxK, "per-row lists of the 16x16x32 variant hold at most three blocks");
+  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
+  bf16* kb_s = reinterpret_cast<bf16*>(s_dyn);   // [3][nb_lds][KP]
+  const int64_t bi = blockIdx.y / hkv, g = blockIdx.y % hkv;
+  const int64_t gs = hq / hkv;
+  const int km = topk - 1;
+  sel_stage_planes<D>(kb_s, planes + ((bi * nbc) * hkv + g) * D, plane_stride, hkv, nb_lds);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int j = lane & 15, kg = lane >> 4;
+  // wave-uniform chunk bookkeeping, as in the 32x32x16 variant
+  const int gsi = (int)gs;
+  const int ql = (int)q_len, qs = (int)q_start;
+  const int nrc = (ql + 63) / 64;
+  const int stride = (int)gridDim.x * kSelPWaves;
+  const int st_rc = stride / gsi, st_hh = stride % gsi;
+  const int c_first = (int)blockIdx.x * kSelPWaves + wave;
+  int rc = c_first / gsi, hh = c_first % gsi;
+  const int64_t row_el = hq * D;
+  const bf16* qg = q + ((bi * seq_len + q_start) * hq + g * gs) * D + kg * 8;
+  // issued in the order the matrix ops consume them (k-step major)
+  auto load_q = [&](int rc_, int hh_, bf16x8 (&x)[4][KS]) {
+    const bf16* p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[u] = qg + min(rc_ * 64 + 16 * u + j, ql - 1) * row_el + hh_ * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u][ks] = *(const bf16x8*)(p[u] + ks * 32);
+  };
+  // A chunk's blk rows leave one chunk later, just before the loads of the
+  // chunk after: the memory counter retires in issue order, so the store is
+  // then older than every load a later wait is for (a store issued behind
+  // the loads would be waited for with them).
+  int pend[4];
+  int32_t* pend_out = nullptr;
+  auto store_pending = [&]() {
+    if (pend_out) {   // topk <= 4 entries in one store
+      if (topk == 4) {
+        *(i32x4_u*)pend_out = i32x4_u{pend[0], pend[1], pend[2], pend[3]};
+      } else if (topk == 3) {
+        *(i32x3_u*)pend_out = i32x3_u{pend[0], pend[1], pend[2]};
+      } else if (topk == 2) {
+        *(i32x2_u*)pend_out = i32x2_u{pend[0], pend[1]};
+      } else {
+        pend_out[0] = pend[0];
+      }
+      pend_out = nullptr;
+    }
+  };
+  bf16x8 qf[4][KS];
+  if (rc < nrc) load_q(rc, hh, qf);
+  while (rc < nrc) {
+    int rn = rc + st_rc, hn = hh + st_hh;   // the wave's next chunk
+    if (hn >= gsi) {
+      hn -= gsi;
+      ++rn;
+    }
+    const bool more = rn < nrc;
+    const int h = (int)g * gsi + hh;
+    int cur[4];   // own block of query rows j + 16 u
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cur[u] = (qs + min(rc * 64 + 16 * u + j, ql - 1)) / block;
+    const int own0 = (qs + rc * 64) / block;   // the chunk's smallest own block
+    const int t_last = qs + min(ql, rc * 64 + 64) - 1;
+    const int nbr = km > 0 ? min((int)nbc, t_last / block) : 0;   // <= nb_lds
+    float tv[4][KMAX];
+    int ti[4][KMAX];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        tv[u][i] = -__builtin_inff();
+        ti[u][i] = 0x7fffffff;
+      }
+    for (int c0 = 0; c0 < nbr; c0 += 16) {
+      const bf16* arow = kb_s + min(c0 + j, nb_lds - 1) * KP + kg * 8;
+      f32x4 acc[4] = {};
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = *(const bf16x8*)(arow + pl * nb_lds * KP + ks * 32);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[u][ks], acc[u], 0, 0, 0);
+        }
+      // plane reads run two fragments ahead of the matrix ops using them
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 3 * KS - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      // the last half-round issues the previous chunk's rows, then the next
+      // chunk's query loads once its matrix ops have read the current
+      // queries: those loads overlap the selection work below
+      if (c0 + 16 >= nbr) {
+        store_pending();
+        if (more) load_q(rn, hn, qf);
+      }
+      const int b0 = c0 + 4 * kg;   // blocks b0 + 0..3 of this lane
+      if (own0 - c0 >= 16) {   // every row of the chunk has all 16 as candidates
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) top_insert<KMAX>(tv[u], ti[u], acc[u][r], b0 + r);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            top_insert<KMAX>(tv[u], ti[u], b0 + r < cur[u] ? acc[u][r] : -__builtin_inff(), b0 + r);
+      }
+    }
+    if (nbr <= 0) {
+      store_pending();
+      if (more) load_q(rn, hn, qf);
+    }
+    // exchange 1 (lane bit 5): keep the lists of rows 32 * (lane / 32) + j + 0, 16
+    const bool hi5 = lane >= 32, hi4 = (lane & 16) != 0;
+    float kv[2][KMAX];
+    int ki[2][KMAX];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      float rv[KMAX];
+      int ri[KMAX];
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        kv[x][i] = hi5 ? tv[2 + x][i] : tv[x][i];
+        ki[x][i] = hi5 ? ti[2 + x][i] : ti[x][i];
+        rv[i] = __builtin_bit_cast(float, sel_swap_halves(__builtin_bit_cast(uint32_t, hi5 ? tv[x][i] : tv[2 + x][i])));
+        ri[i] = (int)sel_swap_halves((uint32_t)(hi5 ? ti[x][i] : ti[2 + x][i]));
+      }
+      top_merge_from<KMAX>(kv[x], ki[x], rv, ri);
+    }
+    // exchange 2 (lane bit 4): keep the list of row `lane`
+    float ov[KMAX];
+    int oi[KMAX];
+    {
+      float rv[KMAX];
+      int ri[KMAX];
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        ov[i] = hi4 ? kv[1][i] : kv[0][i];
+        oi[i] = hi4 ? ki[1][i] : ki[0][i];
+        rv[i] = __builtin_bit_cast(float, sel_swap_rows(__builtin_bit_cast(uint32_t, hi4 ? kv[0][i] : kv[1][i])));
+        ri[i] = (int)sel_swap_rows((uint32_t)(hi4 ? ki[0][i] : ki[1][i]));
+      }
+      top_merge_from<KMAX>(ov, oi, rv, ri);
+    }
+
+    const int r = rc * 64 + lane;
+    if (r < ql) {
+      const int cur_own = (qs + r) / block;
+      const int npick = min(km, cur_own);
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i)
+        if (i >= npick) oi[i] = 0x7fffffff;
+#pragma unroll
+      for (int a = 0; a < KMAX; ++a)
+#pragma unroll
+        for (int b2 = 0; b2 + 1 < KMAX - a; ++b2) {
+          const int lo = min(oi[b2], oi[b2 + 1]);
+          const int hi = max(oi[b2], oi[b2 + 1]);
+          oi[b2] = lo;
+          oi[b2 + 1] = hi;
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int picked = oi[i < KMAX ? i : KMAX - 1];   // used for i < npick <= KMAX only
+        pend[i] = i < npick ? picked : (i == npick ? cur_own : -1);
+      }
+      pend_out = blk + ((bi * q_len + r) * hq + h) * topk;
+    }
+    rc = rn;
+    hh = hn;
+  }
+  store_pending();
 }
 
 // ---------------------------------------------------------------------------
 int meanpool_tokens_per_split(int block) {
-  // 64-token slices for blocks up to 2048 tokens, at most 32 slices beyond
-  return (int)std::max<int64_t>(64, cdiv(block, 32));
+  // 64-token slices for blocks up to 2048 tokens, at most kMpMaxSplits beyond
+  return (int)std::max<int64_t>(64, cdiv(block, kMpMaxSplits));
 }
 int meanpool_splits(int block) { return (int)cdiv(block, meanpool_tokens_per_split(block)); }
 
@@ -763,6 +1058,7 @@ hipError_t launch_moba_meanpool(const void* k, bool bf, int64_t batch, int64_t s
   if (count <= 0) return hipSuccess;
   const int nsplit = meanpool_splits(block);
   const int tps = meanpool_tokens_per_split(block);
+  if (nsplit > kMpMaxSplits) return hipErrorInvalidValue;   // the finalize pass holds them all
   const int64_t cols = hkv * d;
   bf16* pl = (first == 0 && count == nbc) ? planes : nullptr;
   if (batch * count * nsplit < 1024) {   // few blocks: one pass, no partials
@@ -818,22 +1114,31 @@ static hipError_t launch_select_mfma_d(const bf16* q, const bf16* planes, int64_
   // blocks any row can gate: 0 .. (last position) / block - 1
   const int64_t nb_gate = std::min<int64_t>(nbc, (q_start + q_len - 1) / block);
   const size_t lds = (size_t)3 * nb_gate * (D + 8) * sizeof(bf16);
-  if (lds <= (size_t)kSelLdsBytes && batch * hkv <= 65535) {
+  // resident kernels for lists of up to 7 past blocks (longer lists would
+  // spill their registers); the streaming kernel below takes the rest
+  if (lds <= (size_t)kSelLdsBytes && batch * hkv <= 65535 && km <= 7) {
     const int64_t nchunks = (hq / hkv) * cdiv(q_len, 64);
-    // three resident workgroups per CU over 256 CUs, shared by the groups
+    // one wave of workgroups at the kernel's occupancy (three resident per CU
+    // for the 16x16x32 variant, two for the longer lists) over 256 CUs,
+    // shared by the groups
+    const int64_t slots = km <= kSel16MaxK ? 768 : 512;
     const int64_t per_group = std::max<int64_t>(
-        1, std::min<int64_t>(cdiv(768, batch * hkv), cdiv(nchunks, kSelPWaves)));
+        1, std::min<int64_t>(cdiv(slots, batch * hkv), cdiv(nchunks, kSelPWaves)));
     dim3 rgrid((unsigned)per_group, (unsigned)(batch * hkv));
     const size_t lds_launch = std::max<size_t>(lds, 16);
 #define QAT_SELR(KM_)                                                                                      \
   hipLaunchKernelGGL((moba_select_resident_kernel<D, KM_>), rgrid, dim3(kSelPWaves * 64), lds_launch, s, q, \
                      planes, plane_stride, blk, seq_len, hq, hkv, nbc, q_start, q_len, block, topk, (int)nb_gate)
-    if (km <= 1) QAT_SELR(1);
-    else if (km == 2) QAT_SELR(2);
-    else if (km == 3) QAT_SELR(3);
-    else if (km <= 7) QAT_SELR(7);
-    else QAT_SELR(15);
+#define QAT_SELR16(KM_)                                                                                      \
+  hipLaunchKernelGGL((moba_select_resident16_kernel<D, KM_>), rgrid, dim3(kSelPWaves * 64), lds_launch, s, q, \
+                     planes, plane_stride, blk, seq_len, hq, hkv, nbc, q_start, q_len, block, topk, (int)nb_gate)
+    static_assert(kSel16MaxK == 3, "dispatch below covers lists of 1..3 blocks");
+    if (km <= 1) QAT_SELR16(1);
+    else if (km == 2) QAT_SELR16(2);
+    else if (km == 3) QAT_SELR16(3);
+    else QAT_SELR(7);
 #undef QAT_SELR
+#undef QAT_SELR16
     return hipGetLastError();
   }
   dim3 grid((unsigned)cdiv(q_len, kSelWaves * kSelRowsPerWave), (unsigned)hq, (unsigned)batch);
