@@ -71,6 +71,139 @@ STAGE_SOURCES = {
 }
 
 
+# The kernel a stage's roofline times (its main kernel, or all kernels of a
+# stage timed as a whole), by a substring of the (demangled) kernel name, for
+# attributing rocprofv3 per-dispatch counters. Helper kernels of a timed
+# stage get labels of their own so they are not charged to it; the two
+# compression stages share their kernels and count together as "esa_compress*".
+KERNEL_STAGE = (
+    ("moba_past_persist_kernel", "moba_past_attn"), ("moba_past_kernel", "moba_past_attn"),
+    ("moba_current_kernel", "moba_current_attn"),
+    ("meanpool_", "moba_meanpool"),
+    ("moba_select_resident", "moba_select"), ("moba_select_mfma_kernel", "moba_select"),
+    ("moba_score_select_kernel", "moba_select"),
+    ("moba_count_kernel", "moba_dispatch"), ("moba_scan_kernel", "moba_dispatch"),
+    ("moba_tiles_kernel", "moba_dispatch"), ("moba_scatter_kernel", "moba_dispatch"),
+    ("fill_i32_kernel", "fill_i32"),
+    ("moba_generic_kernel", "moba_generic_attn"),
+    ("moba_select_group_kernel", "moba_decode_select"),
+    ("moba_decode_piece_kernel", "moba_decode_attn"), ("moba_decode_combine_kernel", "moba_decode_combine"),
+    ("moba_bwd_dq_past_kernel", "moba_bwd_dq_past"), ("moba_bwd_dq_cur_kernel", "moba_bwd_dq"),
+    ("moba_bwd_dq_kernel", "moba_bwd_dq"), ("moba_bwd_kv_own_kernel", "moba_bwd_own"),
+    ("moba_bwd_own_kernel", "moba_bwd_own"), ("moba_bwd_kv_gated_kernel", "moba_bwd_gated"),
+    ("moba_bwd_gated_kernel", "moba_bwd_gated"), ("moba_bwd_runs_kernel", "moba_bwd_runs"),
+    ("moba_bwd_kv_reduce_kernel", "moba_bwd_kv_reduce"),
+    ("esa_bwd_dq_kernel", "esa_bwd_dq"), ("esa_bwd_kv_kernel", "esa_bwd_kv"),
+    ("cca_pool_kernel", "cca_pool"), ("cca_attn_kernel", "cca_attn"),
+    ("compress_", "esa_compress*"),
+    ("esa_rowmax", "esa_rowmax"), ("esa_colsum_kernel", "esa_colsum"),
+    ("esa_topk_", "esa_topk"), ("esa_decode_scan_kernel", "esa_decode_scan"),
+    ("esa_keylist_kernel", "esa_keylist"), ("esa_prefill_kernel", "esa_prefill_attn"),
+    ("esa_decode_attn_kernel", "esa_decode_attn"), ("esa_decode_combine_kernel", "esa_decode_combine"),
+    ("esa_generic_kernel", "esa_generic_attn"),
+)
+
+
+def stage_of_kernel(name: str):
+    """The timed stage a dispatched kernel belongs to, or None (torch's own
+    kernels, the calibration copy, small helpers)."""
+    for key, stage in KERNEL_STAGE:
+        if key in name:
+            return stage
+    return None
+
+
+def read_pmc_csv(path):
+    """Per-dispatch counters of a rocprofv3 --pmc run (its *counter_collection.csv):
+    a list of (kernel name, {counter: value}) in dispatch order."""
+    import csv
+    rows = {}
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            d = int(r["Dispatch_Id"])
+            name, cnt = rows.setdefault(d, (r["Kernel_Name"], {}))
+            cnt[r["Counter_Name"]] = cnt.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [rows[d] for d in sorted(rows)]
+
+
+def stage_counter_means(dispatches, counter, primary=None):
+    """Per stage: (sum of `counter` over the stage's dispatches) / (launches of
+    the stage), a launch being one dispatch of the stage's first kernel name
+    (a stage that runs several kernels is charged all of them per launch)."""
+    tot, first, launches = {}, {}, {}
+    for name, cnt in dispatches:
+        st = stage_of_kernel(name)
+        if st is None or counter not in cnt:
+            continue
+        tot[st] = tot.get(st, 0.0) + cnt[counter]
+        first.setdefault(st, name)
+        if name == first[st]:
+            launches[st] = launches.get(st, 0) + 1
+    return {st: tot[st] / launches[st] for st in tot}
+
+
+def copy_scale(dispatches, counter, copy_bytes):
+    """Bytes per counter unit from the calibration copy (the dispatch of a
+    kernel with "copy" in its name and the largest reading): the copy reads
+    and writes copy_bytes."""
+    best = None
+    for name, cnt in dispatches:
+        if "copy" in name.lower() and counter in cnt and (best is None or cnt[counter] > best):
+            best = cnt[counter]
+    if not best:
+        raise SystemExit(f"no calibration copy with {counter} in the counter file")
+    return copy_bytes / best
+
+
+def ingest_traffic(workload, fetch_csv, write_csv, copy_bytes, out=None):
+    """HBM bytes per launch of every stage seen in two counter runs of one
+    workload (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same
+    counter reads for the calibration copy; stored in profiles/counters.json
+    with the hash of the stage's sources. Returns the new entries."""
+    out = out or COUNTERS
+    f = read_pmc_csv(fetch_csv)
+    w = read_pmc_csv(write_csv)
+    fs, ws = copy_scale(f, "FETCH_SIZE", copy_bytes), copy_scale(w, "WRITE_SIZE", copy_bytes)
+    fm, wm = stage_counter_means(f, "FETCH_SIZE"), stage_counter_means(w, "WRITE_SIZE")
+    try:
+        with open(out) as fh:
+            c = json.load(fh)
+    except OSError:
+        c = {}
+    new = {}
+    for st in sorted(set(fm) & set(wm)):
+        new[f"{workload}/{st}"] = {"fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+                                   "read_bytes_per_launch": int(fm[st] * fs),
+                                   "write_bytes_per_launch": int(wm[st] * ws),
+                                   "hbm_bytes_per_launch": int(fm[st] * fs + wm[st] * ws),
+                                   "source_sha": kernel_source_sha(st)}
+    c.update(new)
+    with open(out, "w") as fh:
+        json.dump(c, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return new
+
+
+def mfma_table(csv_path, n_simd=1024, n_xcd=8):
+    """Markdown rows from one counter run with SQ_INSTS_MFMA, SQ_INSTS_VALU,
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE: per stage the
+    per-launch instruction counts, the VALU : MFMA instruction ratio, and the
+    matrix-core busy fraction = MFMA busy cycles / (GUI-active cycles of one
+    XCD x the chip's SIMDs); GRBM_GUI_ACTIVE is summed over the XCDs."""
+    d = read_pmc_csv(csv_path)
+    names = ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+    m = {n: stage_counter_means(d, n) for n in names}
+    rows = ["| stage | MFMA instr / launch | VALU instr / launch | VALU : MFMA | GUI-active cycles (one XCD) | "
+            "MFMA busy |", "|---|---|---|---|---|---|"]
+    for st in sorted(m["SQ_INSTS_MFMA"]):
+        mf, va = m["SQ_INSTS_MFMA"][st], m["SQ_INSTS_VALU"].get(st, 0.0)
+        gui = m["GRBM_GUI_ACTIVE"].get(st, 0.0) / n_xcd
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"].get(st, 0.0) / (gui * n_simd) if gui else 0.0
+        ratio = f"{va / mf:.2f}" if mf else "-"
+        rows.append(f"| {st} | {mf:.4g} | {va:.4g} | {ratio} | {gui:.4g} | {busy:.3f} |")
+    return "\n".join(rows)
+
+
 def kernel_source_sha(stage: str = "") -> str:
     """Hash of the sources a stage is built from (every source if the stage
     is unknown or empty)."""
@@ -1106,7 +1239,22 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run one plain device-to-device copy of BYTES before warmup (reference kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: read the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
+                         "rocprofv3 run of --workload (made with --copy-calibration BYTES) and store the "
+                         "per-launch HBM bytes of its stages in profiles/counters.json")
+    ap.add_argument("--mfma-table", metavar="CSV",
+                    help="no GPU work: print per-stage MFMA / VALU counter rows of one rocprofv3 run")
     args = ap.parse_args()
+    if args.ingest_traffic:
+        if not args.copy_calibration:
+            raise SystemExit("--ingest-traffic needs the --copy-calibration size the runs used")
+        for k, v in ingest_traffic(args.workload, *args.ingest_traffic, args.copy_calibration).items():
+            print(k, json.dumps(v))
+        return
+    if args.mfma_table:
+        print(mfma_table(args.mfma_table))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
               f"see DESIGN.md for how the path would shard.", file=sys.stderr)

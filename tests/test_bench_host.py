@@ -79,3 +79,59 @@ def test_oracle_tasks_run_over_the_worker_pool():
         assert np.array_equal(o_full, o_list)
     finally:
         bench.close_cpu_pool()
+
+
+def _pmc_csv(path, rows):
+    """rows: (dispatch id, kernel name, counter, value)."""
+    with open(path, "w") as fh:
+        fh.write("Correlation_Id,Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for d, k, c, v in rows:
+            fh.write(f'{d},{d},"{k}",{c},{v}\n')
+
+
+def test_traffic_ingestion_scales_by_the_copy_and_charges_stage_kernels(tmp_path):
+    """Two counter runs (FETCH_SIZE, WRITE_SIZE): the calibration copy fixes the
+    scales, a stage's several kernels are charged per launch of its first one,
+    torch's kernels are ignored, and the entry carries the source hash."""
+    gib = 1 << 30
+    copy = "__amd_rocclr_copyBuffer"
+    past = "void qat::moba_past_persist_kernel<128>(...)"
+    cnt, scan = "qat::moba_count_kernel(...)", "qat::moba_scan_kernel(...)"
+    f = tmp_path / "f.csv"
+    w = tmp_path / "w.csv"
+    _pmc_csv(f, [(1, copy, "FETCH_SIZE", gib / 2048), (2, "at::native::fill", "FETCH_SIZE", 999.0),
+                 (3, past, "FETCH_SIZE", 100.0), (4, cnt, "FETCH_SIZE", 10.0), (5, scan, "FETCH_SIZE", 2.0),
+                 (6, past, "FETCH_SIZE", 300.0), (7, cnt, "FETCH_SIZE", 30.0), (8, scan, "FETCH_SIZE", 6.0)])
+    _pmc_csv(w, [(1, copy, "WRITE_SIZE", gib / 1024), (3, past, "WRITE_SIZE", 50.0),
+                 (4, cnt, "WRITE_SIZE", 1.0), (6, past, "WRITE_SIZE", 50.0), (7, cnt, "WRITE_SIZE", 1.0)])
+    out = tmp_path / "counters.json"
+    new = bench.ingest_traffic("wl", str(f), str(w), gib, out=str(out))
+    assert set(new) == {"wl/moba_past_attn", "wl/moba_dispatch"}
+    p = new["wl/moba_past_attn"]
+    assert p["fetch_scale"] == 2048.0 and p["write_scale"] == 1024.0
+    assert p["read_bytes_per_launch"] == 200 * 2048 and p["write_bytes_per_launch"] == 50 * 1024
+    assert p["source_sha"] == bench.kernel_source_sha("moba_past_attn")
+    dsp = new["wl/moba_dispatch"]
+    assert dsp["read_bytes_per_launch"] == 24 * 2048   # (10 + 2 + 30 + 6) / 2 launches
+    assert json.loads(out.read_text())["wl/moba_past_attn"]["hbm_bytes_per_launch"] == 200 * 2048 + 50 * 1024
+
+
+def test_mfma_table_normalises_busy_cycles_per_xcd_and_simd(tmp_path):
+    k = "void qat::cca_attn_kernel<128>(...)"
+    c = tmp_path / "m.csv"
+    _pmc_csv(c, [(1, k, "SQ_INSTS_MFMA", 1000.0), (1, k, "SQ_INSTS_VALU", 2500.0),
+                 (1, k, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 100 * 1024), (1, k, "SQ_BUSY_CYCLES", 7.0),
+                 (1, k, "GRBM_GUI_ACTIVE", 100 * 8)])
+    t = bench.mfma_table(str(c))
+    row = [r for r in t.splitlines() if r.startswith("| cca_attn")][0]
+    assert "| 2.50 |" in row and row.endswith("| 0.500 |")
+
+
+def test_every_library_kernel_maps_to_a_stage():
+    import re
+    names = set()
+    for f in os.listdir(bench.CSRC):
+        if f.endswith(".hip"):
+            names |= set(re.findall(r"void ([a-z_0-9]+_kernel)\(", open(os.path.join(bench.CSRC, f)).read()))
+    unmapped = {n for n in names if bench.stage_of_kernel(n) is None}
+    assert not unmapped, unmapped
