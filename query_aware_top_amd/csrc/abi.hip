@@ -45,7 +45,6 @@ struct EsaLayout {
   int nsplit_q = 1, nkeysplit = 1, nqsplit = 1, nscan = 1, ndec = 1;
   int64_t n_mid = 0, mid0 = 0, rows = 0;
   double* qpart = nullptr;
-  float* qpart32 = nullptr;   // float32 split partials of the matrix-core query compression
   float* qc = nullptr;
   qat::bf16* qhi = nullptr;
   qat::bf16* qlo = nullptr;
@@ -112,8 +111,6 @@ EsaLayout esa_layout(const qat_esa_params* p, void* ws) {
   L.ndec = qat::esa_decode_splits(p->batch, p->n_init, p->topk, p->window);
   qat::Carver c(ws);
   L.qpart = c.take<double>((size_t)L.nsplit_q * L.rows * dcq);
-  L.qpart32 = c.take<float>(dcq && qat::compress_bf16_rows_ok(L.rows, D, p->d_c)
-                                ? qat::compress_bf16_rows_part_floats(L.rows, p->d_c) : 0);
   L.qc = c.take<float>((size_t)L.rows * dcq);
   L.qhi = c.take<qat::bf16>((size_t)L.rows * dcq);
   L.qlo = c.take<qat::bf16>((size_t)L.rows * dcq);
@@ -449,7 +446,7 @@ QAT_EXPORT int esa_select(const qat_esa_params* p, const void* q, const void* Wq
   {
     qat::KTimer tm("esa_qcompress", s);
     if (bf && qat::compress_bf16_rows_ok(L.rows, D, p->d_c)) {
-      e = qat::launch_compress_bf16_rows(q, L.rows, D, D, Wq, p->d_c, bq, L.qpart32, L.qc, L.qhi, L.qlo, s);
+      e = qat::launch_compress_bf16_rows(q, L.rows, D, D, Wq, p->d_c, bq, L.qc, L.qhi, L.qlo, s);
     } else {
       e = qat::launch_compress_partial(q, L.rows, D, D, bf, Wq, bf, p->d_c, L.nsplit_q, L.qpart, s);
       if (e == hipSuccess)

@@ -142,105 +142,107 @@ __global__ void compress_finalize_kernel(const double* __restrict__ partial, int
 // are exact in float32 and only the accumulation rounds (about 2^-18
 // relative over 4096 terms, far below what the scores summed over the
 // chunk's queries can resolve), so the fp64 path is kept for the key cache
-// (which must be correctly rounded) and for decode rows. Workgroup (row
-// tile, split) takes 32 rows and one of kCqSplits slices of d_model; its
-// four waves split the slice again and each computes out^T = W x^T over its
-// part (lane: one row, 16 output dims per 32-dim block); the parts are
-// added in LDS in a fixed order into the split's float32 partial, and a
-// second kernel adds the splits in split order.
-constexpr int kCq = 32;         // rows per workgroup
-constexpr int kCqSteps = 4;     // k-steps of 16 whose loads are issued together
-constexpr int kCqSplits = 8;    // slices of d_model (workgroups per row tile)
+// (which must be correctly rounded) and for decode rows. One launch; a
+// workgroup takes 32 rows and 32 output columns (so a CU streams a quarter
+// of W, not all of it), its four waves each a quarter of d_model, computing
+// out^T = W x^T on the 16x16x32 op (A = 16 rows of W, B = 16 rows of x; each
+// lane loads 16 contiguous bytes, four lanes 64 of one row); the quarters are
+// added in wave order in LDS, plus the bias, and the same pass writes the
+// bf16 hi/lo split of the scoring passes.
+constexpr int kCqRows = 32;    // rows per workgroup
+constexpr int kCqWaves = 4;    // d_model quarters
+constexpr int kCqBatch = 2;    // k-steps of 32 whose loads are issued together
+constexpr int kCqCols = 32;    // output columns per workgroup
 
-template <int DC>
-__global__ __launch_bounds__(256) void compress_bf16_rows_kernel(
+__global__ __launch_bounds__(kCqWaves * 64) void compress_bf16_rows_kernel(
     const bf16* __restrict__ x, int64_t n, int64_t x_stride, int64_t d_model, const bf16* __restrict__ W,
-    float* __restrict__ part) {
-  constexpr int NA = DC / 32;
-  __shared__ float red[4][DC][kCq];
+    int64_t d_c, const float* __restrict__ bias, float* __restrict__ out, bf16* __restrict__ hi,
+    bf16* __restrict__ lo) {
+  constexpr int NI = kCqCols / 16;   // output-column tiles
+  __shared__ float red[kCqWaves][kCqRows][kCqCols + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 31, h = lane >> 5;
-  const int64_t row0 = (int64_t)blockIdx.x * kCq;
-  const int64_t row = min(row0 + r, n - 1);
-  const int64_t kw = d_model / (kCqSplits * 4);   // this wave's part
-  const int64_t k0 = ((int64_t)blockIdx.y * 4 + wave) * kw;
-  const bf16* xr = x + row * x_stride + k0 + 8 * h;
-  const bf16* wr = W + (int64_t)r * d_model + k0 + 8 * h;
-  f32x16 acc[NA];
+  const int j = lane & 15, kg = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * kCqRows;
+  const int64_t kq = d_model / kCqWaves;
+  const int64_t k0 = wave * kq + kg * 8;
+  const bf16* xp[2];
 #pragma unroll
-  for (int a = 0; a < NA; ++a)
+  for (int t = 0; t < 2; ++t) xp[t] = x + min(row0 + 16 * t + j, n - 1) * x_stride + k0;
+  const int64_t c0 = (int64_t)blockIdx.y * kCqCols;
+  const bf16* wp = W + (c0 + j) * d_model + k0;
+  f32x4 acc[2][NI];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
-  for (int64_t kk = 0; kk < kw; kk += 16 * kCqSteps) {
-    bf16x8 xb[kCqSteps], wb[kCqSteps][NA];
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int st = 0; st < kCqSteps; ++st) {
-      xb[st] = *(const bf16x8*)(xr + kk + 16 * st);
+    for (int it = 0; it < NI; ++it) acc[t][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // groups of kCqBatch k-steps, double-buffered: group g + 1 loads while
+  // group g runs on the matrix cores (kq / step is even, see _ok)
+  constexpr int64_t step = 32 * kCqBatch;
+  bf16x8 wa0[kCqBatch][NI], xb0[kCqBatch][2], wa1[kCqBatch][NI], xb1[kCqBatch][2];
+  auto load = [&](int64_t kk, bf16x8 (&wa)[kCqBatch][NI], bf16x8 (&xb)[kCqBatch][2]) {
 #pragma unroll
-      for (int a = 0; a < NA; ++a) wb[st][a] = *(const bf16x8*)(wr + (int64_t)32 * a * d_model + kk + 16 * st);
+    for (int b = 0; b < kCqBatch; ++b) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) xb[b][t] = *(const bf16x8*)(xp[t] + kk + 32 * b);
+#pragma unroll
+      for (int it = 0; it < NI; ++it) wa[b][it] = *(const bf16x8*)(wp + (int64_t)16 * it * d_model + kk + 32 * b);
     }
+    __builtin_amdgcn_sched_barrier(0);   // the whole group in flight before the matrix ops
+  };
+  auto mma = [&](const bf16x8 (&wa)[kCqBatch][NI], const bf16x8 (&xb)[kCqBatch][2]) {
 #pragma unroll
-    for (int st = 0; st < kCqSteps; ++st)
+    for (int b = 0; b < kCqBatch; ++b)
 #pragma unroll
-      for (int a = 0; a < NA; ++a) acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[st][a], xb[st], acc[a], 0, 0, 0);
+      for (int it = 0; it < NI; ++it)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t][it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[b][it], xb[b][t], acc[t][it], 0, 0, 0);
+  };
+  const int64_t ng = kq / step;
+  load(0, wa0, xb0);
+  int64_t g = 0;
+  for (; g + 2 < ng; g += 2) {
+    load((g + 1) * step, wa1, xb1);
+    mma(wa0, xb0);
+    load((g + 2) * step, wa0, xb0);
+    mma(wa1, xb1);
   }
-  // lane: row r, dims 32 a + 8 (i / 4) + 4 h + i % 4
+  load((g + 1) * step, wa1, xb1);
+  mma(wa0, xb0);
+  mma(wa1, xb1);
+  // lane: row 16 t + j, output columns 16 it + 4 kg + 0..3
 #pragma unroll
-  for (int a = 0; a < NA; ++a)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[wave][32 * a + 8 * (i >> 2) + 4 * h + (i & 3)][r] = acc[a][i];
+    for (int it = 0; it < NI; ++it)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][16 * t + j][16 * it + 4 * kg + r] = acc[t][it][r];
   __syncthreads();
-  float* dst = part + (int64_t)blockIdx.y * n * DC;
-  for (int idx = threadIdx.x; idx < DC * kCq; idx += 256) {
-    const int rr = idx / DC, c = idx % DC;
+  for (int idx = threadIdx.x; idx < kCqRows * kCqCols; idx += kCqWaves * 64) {
+    const int rr = idx / kCqCols, c = idx % kCqCols;
     const int64_t orow = row0 + rr;
-    if (orow < n) dst[orow * DC + c] = ((red[0][c][rr] + red[1][c][rr]) + red[2][c][rr]) + red[3][c][rr];
+    if (orow >= n) continue;
+    float v = ((red[0][rr][c] + red[1][rr][c]) + red[2][rr][c]) + red[3][rr][c];
+    if (bias) v += bias[c0 + c];
+    const int64_t o = orow * d_c + c0 + c;
+    out[o] = v;
+    const bf16 hv = (bf16)v;
+    hi[o] = hv;
+    lo[o] = (bf16)(v - (float)hv);
   }
-}
-
-// out = sum of the splits in split order (+ bias), float32, with the bf16
-// hi/lo split of the scoring passes.
-__global__ __launch_bounds__(256) void compress_bf16_rows_finalize_kernel(const float* __restrict__ part, int64_t n,
-                                                                          int64_t d_c, const float* __restrict__ bias,
-                                                                          float* __restrict__ out,
-                                                                          bf16* __restrict__ hi,
-                                                                          bf16* __restrict__ lo) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n * d_c) return;
-  float t[kCqSplits];
-#pragma unroll
-  for (int sp = 0; sp < kCqSplits; ++sp) t[sp] = part[(int64_t)sp * n * d_c + idx];
-  float v = t[0];
-#pragma unroll
-  for (int sp = 1; sp < kCqSplits; ++sp) v += t[sp];
-  if (bias) v += bias[idx % d_c];
-  out[idx] = v;
-  const bf16 hv = (bf16)v;
-  hi[idx] = hv;
-  lo[idx] = (bf16)(v - (float)hv);
 }
 
 bool compress_bf16_rows_ok(int64_t n, int64_t d_model, int64_t d_c) {
-  return n >= 64 && (d_c == 32 || d_c == 64 || d_c == 128) && d_model % (kCqSplits * 4 * 16 * kCqSteps) == 0;
+  // whole, even numbers of load groups per wave quarter
+  return n >= 64 && d_c % kCqCols == 0 && d_c <= 4096 && d_model % (kCqWaves * 32 * kCqBatch * 2) == 0;
 }
 
-size_t compress_bf16_rows_part_floats(int64_t n, int64_t d_c) { return (size_t)kCqSplits * n * d_c; }
-
 hipError_t launch_compress_bf16_rows(const void* x, int64_t n, int64_t x_stride, int64_t d_model, const void* W,
-                                     int64_t d_c, const float* bias, float* part, float* out, bf16* hi, bf16* lo,
+                                     int64_t d_c, const float* bias, float* out, bf16* hi, bf16* lo,
                                      hipStream_t s) {
-  dim3 grid((unsigned)cdiv(n, kCq), (unsigned)kCqSplits);
-#define QAT_CQ(DC_)                                                                                        \
-  hipLaunchKernelGGL(compress_bf16_rows_kernel<DC_>, grid, dim3(256), 0, s, (const bf16*)x, n, x_stride,   \
-                     d_model, (const bf16*)W, part)
-  if (d_c == 32) QAT_CQ(32);
-  else if (d_c == 64) QAT_CQ(64);
-  else QAT_CQ(128);
-#undef QAT_CQ
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compress_bf16_rows_finalize_kernel, dim3((unsigned)cdiv(n * d_c, 256)), dim3(256), 0, s,
-                     (const float*)part, n, d_c, bias, out, hi, lo);
+  dim3 grid((unsigned)cdiv(n, kCqRows), (unsigned)(d_c / kCqCols));
+  hipLaunchKernelGGL(compress_bf16_rows_kernel, grid, dim3(kCqWaves * 64), 0, s, (const bf16*)x, n, x_stride,
+                     d_model, (const bf16*)W, d_c, bias, out, hi, lo);
   return hipGetLastError();
 }
 

@@ -18,10 +18,8 @@ hipError_t launch_compress_partial(const void* x, int64_t n, int64_t x_stride, i
                                    hipStream_t s);
 // kind 0: float32 out, 1: bf16 out, 2: float32 out plus bf16 hi/lo rows.
 bool compress_bf16_rows_ok(int64_t n, int64_t d_model, int64_t d_c);
-size_t compress_bf16_rows_part_floats(int64_t n, int64_t d_c);
 hipError_t launch_compress_bf16_rows(const void* x, int64_t n, int64_t x_stride, int64_t d_model, const void* W,
-                                     int64_t d_c, const float* bias, float* part, float* out, bf16* hi, bf16* lo,
-                                     hipStream_t s);
+                                     int64_t d_c, const float* bias, float* out, bf16* hi, bf16* lo, hipStream_t s);
 hipError_t launch_compress_finalize(const double* partial, int nsplit, int64_t n, int64_t d_c, const float* bias,
                                     void* out, int64_t out_stride, int kind, bf16* hi, bf16* lo, hipStream_t s);
 
