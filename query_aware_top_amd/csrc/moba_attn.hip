@@ -566,7 +566,8 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
   // tiles', so waiting for them costs no extra latency. Every (row, slot)
   // partial lse is -inf unless the slot's block was dispatched (the lse
   // array is cleared before the past-block pass), so the loads need no look
-  // at the gating.
+  // at the gating; the o rows of such slots were never written (whatever the
+  // workspace held, NaN included) and are replaced by zeros as they load.
   auto unpack = [](const uint2 u, float* f) {
     f[0] = __builtin_bit_cast(float, u.x << 16);
     f[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
@@ -579,14 +580,15 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
       const int64_t pidx = row * km + min(s0 + sl, km - 1);
       const float lv = part_lse[pidx];
       plse[sl] = (valid && s0 + sl < km) ? lv * kLog2e : -__builtin_inff();
+      const bool live = plse[sl] != -__builtin_inff();
       // partial rows are stored in split halves: this lane's D/2 values are
       // contiguous, in accumulator order
       const bf16* src = part_o + pidx * D + hl * (D / 2);
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) {
         const u32x4 w = *(const u32x4*)(src + 8 * i);
-        po[sl][2 * i] = make_uint2(w[0], w[1]);
-        po[sl][2 * i + 1] = make_uint2(w[2], w[3]);
+        po[sl][2 * i] = live ? make_uint2(w[0], w[1]) : make_uint2(0u, 0u);
+        po[sl][2 * i + 1] = live ? make_uint2(w[2], w[3]) : make_uint2(0u, 0u);
       }
     }
   };
