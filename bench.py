@@ -126,20 +126,26 @@ def read_pmc_csv(path):
     return [rows[d] for d in sorted(rows)]
 
 
-def stage_counter_means(dispatches, counter, primary=None):
-    """Per stage: (sum of `counter` over the stage's dispatches) / (launches of
-    the stage), a launch being one dispatch of the stage's first kernel name
-    (a stage that runs several kernels is charged all of them per launch)."""
-    tot, first, launches = {}, {}, {}
+def stage_counter_means(dispatches, counter):
+    """Per stage: the median over its launches of `counter` summed over the
+    launch's dispatches, a launch being a run of consecutive dispatches of
+    the stage's kernels (a stage that runs several kernels back to back is
+    charged all of them; the median skips one-off launches such as a
+    workload's setup)."""
+    launches, prev = {}, None
     for name, cnt in dispatches:
         st = stage_of_kernel(name)
-        if st is None or counter not in cnt:
-            continue
-        tot[st] = tot.get(st, 0.0) + cnt[counter]
-        first.setdefault(st, name)
-        if name == first[st]:
-            launches[st] = launches.get(st, 0) + 1
-    return {st: tot[st] / launches[st] for st in tot}
+        if st is not None and counter in cnt:
+            if st != prev:
+                launches.setdefault(st, []).append(0.0)
+            launches[st][-1] += cnt[counter]
+        prev = st
+    out = {}
+    for st, v in launches.items():
+        v = sorted(v)
+        n = len(v)
+        out[st] = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return out
 
 
 def copy_scale(dispatches, counter, copy_bytes):

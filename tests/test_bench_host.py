@@ -109,11 +109,22 @@ def test_traffic_ingestion_scales_by_the_copy_and_charges_stage_kernels(tmp_path
     assert set(new) == {"wl/moba_past_attn", "wl/moba_dispatch"}
     p = new["wl/moba_past_attn"]
     assert p["fetch_scale"] == 2048.0 and p["write_scale"] == 1024.0
-    assert p["read_bytes_per_launch"] == 200 * 2048 and p["write_bytes_per_launch"] == 50 * 1024
+    assert p["read_bytes_per_launch"] == 200 * 2048 and p["write_bytes_per_launch"] == 50 * 1024   # medians
     assert p["source_sha"] == bench.kernel_source_sha("moba_past_attn")
     dsp = new["wl/moba_dispatch"]
-    assert dsp["read_bytes_per_launch"] == 24 * 2048   # (10 + 2 + 30 + 6) / 2 launches
+    assert dsp["read_bytes_per_launch"] == 24 * 2048   # median of the launches' sums 12 and 36
     assert json.loads(out.read_text())["wl/moba_past_attn"]["hbm_bytes_per_launch"] == 200 * 2048 + 50 * 1024
+
+
+def test_stage_medians_skip_a_one_off_setup_launch():
+    """A launch is a run of consecutive dispatches of one stage's kernels."""
+    k = "void qat::moba_decode_piece_kernel<bf16, 128>(...)"
+    c = "void qat::moba_decode_combine_kernel<bf16, 128>(...)"
+    d = [(k, {"FETCH_SIZE": 1e9}), (k, {"FETCH_SIZE": 1.0})]   # one setup launch of two dispatches
+    for _ in range(4):
+        d += [(c, {"FETCH_SIZE": 2.0}), (k, {"FETCH_SIZE": 5.0})]
+    m = bench.stage_counter_means(d, "FETCH_SIZE")
+    assert m == {"moba_decode_attn": 5.0, "moba_decode_combine": 2.0}
 
 
 def test_mfma_table_normalises_busy_cycles_per_xcd_and_simd(tmp_path):
