@@ -84,6 +84,7 @@ KERNEL_STAGE = (
     ("moba_score_select_kernel", "moba_select"),
     ("moba_count_kernel", "moba_dispatch"), ("moba_scan_kernel", "moba_dispatch"),
     ("moba_tiles_kernel", "moba_dispatch"), ("moba_scatter_kernel", "moba_dispatch"),
+    ("moba_stable_", "moba_dispatch"), ("moba_wg_scan_kernel", "moba_dispatch"),
     ("fill_i32_kernel", "fill_i32"),
     ("moba_generic_kernel", "moba_generic_attn"),
     ("moba_select_group_kernel", "moba_decode_select"),

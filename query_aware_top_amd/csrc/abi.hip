@@ -167,6 +167,8 @@ struct MobaLayout {
   float* delta = nullptr;     // [rows] D = sum_j p_j dp_j of the gradient pass
   float* dq_part = nullptr;   // gradient pass: float32 dq partials per (row, gated slot)
   int32_t* run_off = nullptr; // gradient pass: runs of dispatch tiles per bucket
+  int32_t* wg_counts = nullptr;   // gradient pass: stable dispatch, per-workgroup bucket counts
+  int32_t* wg_base = nullptr;     // gradient pass: stable dispatch, per-workgroup bucket offsets
   float* kv_part = nullptr;   // gradient pass: dK, dV sums per (run, key chunk)
   size_t bytes = 0;
 };
@@ -231,6 +233,9 @@ MobaLayout moba_layout(const qat_moba_params* p, void* ws, bool bwd = false) {
   if (bwd) {
     L.dq_part = c.take<float>((size_t)qat::moba_bwd_part_floats(L.nrows, p->topk, p->head_dim) + 1);
     L.run_off = c.take<int32_t>((size_t)L.nbuckets + 1);
+    const int64_t sti = qat::moba_dispatch_stable_ints(L.nrows, L.nbuckets, p->topk);
+    L.wg_counts = sti > 0 ? c.take<int32_t>((size_t)sti) : nullptr;
+    L.wg_base = sti > 0 ? c.take<int32_t>((size_t)sti) : nullptr;
     L.kv_part = c.take<float>((size_t)qat::moba_bwd_kv_part_floats(L.max_tiles, L.nbuckets, p->block, p->head_dim));
   }
   L.bytes = c.bytes();
@@ -761,9 +766,10 @@ QAT_EXPORT int moba_sparse_attn_bwd(const qat_moba_params* p, const void* q, con
   const bool gated = p->topk > 1 && L.nbuckets > 0;
   if (gated) {
     qat::KTimer tm("moba_dispatch", s);
+    // stable placement: the gated-key pass sums a bucket's rows in entry order
     e = qat::launch_moba_dispatch(blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim, p->q_start,
                                   p->q_len, p->block, p->topk, L.nbc, L.counts, L.offsets, L.cursor, L.entries,
-                                  L.tiles, L.ntiles, s);
+                                  L.tiles, L.ntiles, s, L.wg_counts, L.wg_base);
     if (e != hipSuccess) return hip_status(e, "moba_sparse_attn_bwd: dispatch");
   }
   e = qat::launch_moba_bwd(q, k, v, blk, dout, lse, L.tiles, L.ntiles, L.entries, gated ? L.max_tiles : 0,

@@ -48,10 +48,18 @@ int64_t moba_max_tiles(int64_t nrows, int topk, int64_t nbuckets);
 int moba_rows_per_tile();   // query rows per dispatch tile
 // tiles: {element offset of the block's K/V rows (low, high word), first
 // entry, row count}; entries: {row * 16 + slot, row index of the query in q}
+// stable (wg_counts, wg_base non-NULL, each moba_dispatch_stable_ints
+// int32): the entries of a bucket are placed in an order fixed by the rows
+// (no atomics decide it), which the gradient pass needs for reproducible
+// dK/dV sums; NULL: the faster atomic placement, order arbitrary.
 hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
                                 int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int64_t nbc,
                                 int32_t* counts, int32_t* offsets, int32_t* cursor, int2* entries, int4* tiles,
-                                int32_t* ntiles, hipStream_t s);
+                                int32_t* ntiles, hipStream_t s, int32_t* wg_counts = nullptr,
+                                int32_t* wg_base = nullptr);
+// int32 elements of each stable-placement array, 0 when the bucket count is
+// too large for it (the atomic placement is then used)
+int64_t moba_dispatch_stable_ints(int64_t nrows, int64_t nbuckets, int topk);
 hipError_t launch_moba_attn_mfma(const void* q, const void* k, const void* v, const int32_t* blk,
                                  const int4* tiles, const int32_t* ntiles, const int2* entries, void* part_o,
                                  float* part_lse, void* out, float* lse, int64_t batch, int64_t seq_len, int64_t hq,

@@ -123,6 +123,47 @@ __global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restri
   }
 }
 
+// Stable placement, step 2: wg_base[w][b] = offsets[b] + sum of the bucket's
+// counts of the workgroups before w (row order). A workgroup takes 64
+// buckets; its 16 waves each sum a sixteenth of the workgroup range (16
+// loads in flight per lane), then write the running offsets of their part.
+constexpr int kScanParts = 16;
+__global__ __launch_bounds__(64 * kScanParts) void moba_wg_scan_kernel(const int32_t* __restrict__ wg_counts,
+                                                                       int32_t nwg, int32_t nbuckets,
+                                                                       const int32_t* __restrict__ offsets,
+                                                                       int32_t* __restrict__ wg_base) {
+  __shared__ int32_t part[kScanParts][64];
+  constexpr int U = 16;
+  const int lane = threadIdx.x & 63, pt = threadIdx.x >> 6;
+  const int32_t b = blockIdx.x * 64 + lane;
+  const int32_t np = (nwg + kScanParts - 1) / kScanParts;
+  const int32_t w0 = pt * np, w1 = min(nwg, w0 + np);
+  const bool bv = b < nbuckets;
+  int32_t sum = 0;
+  for (int32_t wb = w0; wb < w1; wb += U) {
+    int32_t c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) c[u] = (bv && wb + u < w1) ? wg_counts[(int64_t)(wb + u) * nbuckets + b] : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) sum += c[u];
+  }
+  part[pt][lane] = sum;
+  __syncthreads();
+  if (!bv) return;
+  int32_t run = offsets[b];
+  for (int q2 = 0; q2 < pt; ++q2) run += part[q2][lane];
+  for (int32_t wb = w0; wb < w1; wb += U) {
+    int32_t c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) c[u] = wb + u < w1 ? wg_counts[(int64_t)(wb + u) * nbuckets + b] : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (wb + u < w1) wg_base[(int64_t)(wb + u) * nbuckets + b] = run;
+      run += c[u];
+    }
+  }
+}
+
 // Exclusive prefix sums of the bucket sizes (entry offsets) and of their tile
 // counts; one workgroup, 1024 buckets per pass. `counts` is overwritten with
 // the tile prefix (counts[nb] = number of tiles), which the tile pass reads.
@@ -164,6 +205,139 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(int32_t* __restrict__ c
     offsets[nb] = carry[0];
     counts[nb] = carry[1];
     ntiles[0] = carry[1];
+  }
+}
+
+// Stable placement (the gradient pass): a workgroup owns kStableEntries
+// (row, slot) sequence numbers of consecutive rows, seq = (row - r0) * km +
+// slot. Step 1 counts its entries per bucket (wg_counts[w][b], and the
+// bucket totals); step 2 (moba_wg_scan_kernel) turns the counts into the
+// workgroup's first position in every bucket; step 3 sorts the workgroup's
+// (bucket, seq) keys in LDS (bitonic) and writes each entry at its bucket's
+// base plus its rank among the workgroup's entries of that bucket. A
+// bucket's entries thus run in row order, whatever order the hardware
+// schedules the workgroups in.
+constexpr int kStableEntries = 8192;   // widest sort (32-bit keys: 32 KiB of LDS)
+constexpr int kStableSeqBits = 13;     // seq < kStableEntries
+
+int moba_stable_rows_per_wg(int topk) {
+  const int km = topk - 1;
+  int r = 256;
+  while (r * 2 * km <= kStableEntries && r * 2 <= 2048) r *= 2;
+  return r;
+}
+
+__global__ __launch_bounds__(256) void moba_stable_count_kernel(const int32_t* __restrict__ blk, int32_t nrows,
+                                                                MobaRowMap m, int topk, int32_t nbuckets,
+                                                                int rows_per_wg, int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ wg_counts) {
+  __shared__ int32_t loc[kDispatchLdsBuckets];
+  for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = 0;
+  __syncthreads();
+  const int km = topk - 1;
+  const int32_t r0 = blockIdx.x * rows_per_wg;
+  const int32_t r1 = min(nrows, r0 + rows_per_wg);
+  for (int32_t row = r0 + (int32_t)threadIdx.x; row < r1; row += 256) {
+    const MobaRow mr = moba_row(m, (uint32_t)row);
+    for (int sl = 0; sl < km; ++sl) {
+      const int32_t b = blk[row * topk + sl];
+      if (b >= 0 && b < mr.cur) atomicAdd(&loc[mr.bucket0 + b], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) {
+    if (loc[i]) atomicAdd(&counts[i], loc[i]);
+    wg_counts[(int64_t)blockIdx.x * nbuckets + i] = loc[i];
+  }
+}
+
+// Bitonic sort of 256 * E keys held E per thread (thread t: keys t*E ..
+// t*E + E - 1): partners within a thread compare in registers, within a
+// wave through lane shuffles, across waves through LDS.
+template <int E>
+__device__ __forceinline__ void stable_sort_keys(uint32_t (&v)[E], uint32_t* lds) {
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= 256 * E; k <<= 1) {
+    for (int j = k >> 1; j >= E; j >>= 1) {
+      const int tj = j / E;   // partner thread: tid ^ tj, same slot
+      if (tj >= 64) {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) lds[tid * E + e] = v[e];
+        __syncthreads();
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t p = tj < 64 ? (uint32_t)__shfl_xor((int)v[e], tj, 64) : lds[(tid ^ tj) * E + e];
+        const int i = tid * E + e;
+        const bool up = (i & k) == 0, lower = (i & j) == 0;
+        v[e] = lower == up ? min(v[e], p) : max(v[e], p);
+      }
+    }
+#pragma unroll
+    for (int j = E / 2; j > 0; j >>= 1) {
+      if (j >= k) continue;   // uniform
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if ((e & j) == 0) {
+          const bool up = ((tid * E + e) & k) == 0;
+          const uint32_t x = v[e], y = v[e + j];
+          v[e] = up ? min(x, y) : max(x, y);
+          v[e + j] = up ? max(x, y) : min(x, y);
+        }
+      }
+    }
+  }
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void moba_stable_scatter_kernel(const int32_t* __restrict__ blk, int32_t nrows,
+                                                                  MobaRowMap m, int topk, int32_t nbuckets,
+                                                                  int rows_per_wg,
+                                                                  const int32_t* __restrict__ wg_base,
+                                                                  int2* __restrict__ entries) {
+  constexpr int NP = 256 * E;
+  __shared__ uint32_t key[NP];
+  __shared__ int32_t first[kDispatchLdsBuckets];
+  const int km = topk - 1;
+  const int32_t r0 = blockIdx.x * rows_per_wg;
+  const int32_t r1 = min(nrows, r0 + rows_per_wg);
+  const int n = (r1 - r0) * km;   // sequence numbers in use (<= NP)
+  uint32_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = threadIdx.x * E + e;
+    uint32_t kv = 0xffffffffu;   // padding and undispatched slots sort last
+    if (i < n) {
+      const int32_t row = r0 + i / km;
+      const int sl = i % km;
+      const MobaRow mr = moba_row(m, (uint32_t)row);
+      const int32_t b = blk[row * topk + sl];
+      if (b >= 0 && b < mr.cur) kv = ((uint32_t)(mr.bucket0 + b) << kStableSeqBits) | (uint32_t)i;
+    }
+    v[e] = kv;
+  }
+  stable_sort_keys<E>(v, key);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[threadIdx.x * E + e] = v[e];
+  __syncthreads();
+  // first sorted index of every bucket present
+  for (int i = threadIdx.x; i < NP; i += 256) {
+    const uint32_t kv = key[i];
+    if (kv != 0xffffffffu && (i == 0 || (key[i - 1] >> kStableSeqBits) != (kv >> kStableSeqBits)))
+      first[kv >> kStableSeqBits] = i;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NP; i += 256) {
+    const uint32_t kv = key[i];
+    if (kv == 0xffffffffu) continue;
+    const int32_t bk = (int32_t)(kv >> kStableSeqBits);
+    const int seq = (int)(kv & ((1u << kStableSeqBits) - 1u));
+    const int32_t row = r0 + seq / km;
+    const int sl = seq % km;
+    const MobaRow mr = moba_row(m, (uint32_t)row);
+    entries[wg_base[(int64_t)blockIdx.x * nbuckets + bk] + (i - first[bk])] = make_int2(row * 16 + sl, mr.qrow);
   }
 }
 
@@ -692,32 +866,66 @@ int64_t moba_max_tiles(int64_t nrows, int topk, int64_t nbuckets) {
   return cdiv(nrows * (topk - 1), kRowsPerTile) + nbuckets;
 }
 
+int64_t moba_dispatch_stable_ints(int64_t nrows, int64_t nbuckets, int topk) {
+  // bucket ids and sequence numbers share a 32-bit sort key
+  if (nbuckets > kDispatchLdsBuckets || topk < 2 || topk - 1 > 16) return 0;
+  return cdiv(nrows, moba_stable_rows_per_wg(topk)) * nbuckets;
+}
+
 hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
                                 int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int64_t nbc,
                                 int32_t* counts, int32_t* offsets, int32_t* cursor, int2* entries, int4* tiles,
-                                int32_t* ntiles, hipStream_t s) {
+                                int32_t* ntiles, hipStream_t s, int32_t* wg_counts, int32_t* wg_base) {
   const int64_t nrows = batch * q_len * hq;
   const int64_t nbuckets = batch * hkv * nbc;
+  const bool stable = wg_counts && wg_base && moba_dispatch_stable_ints(nrows, nbuckets, topk) > 0;
+  const int srows = moba_stable_rows_per_wg(topk);
+  const unsigned sgrid = (unsigned)cdiv(nrows, srows);
   const MobaRowMap m{(uint32_t)hq, (uint32_t)q_len, (uint32_t)q_start, (uint32_t)block, (uint32_t)(hq / hkv),
                      (uint32_t)hkv, (uint32_t)nbc, (uint32_t)seq_len};
   hipError_t e = launch_fill_i32(counts, nbuckets, 0, s);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)cdiv(nrows, 256 * kDispatchRowsPerThread);
   if (nbuckets > 0) {
-    hipLaunchKernelGGL(moba_count_kernel, dim3(grid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
-                       (int32_t)nbuckets, counts);
+    if (stable)
+      hipLaunchKernelGGL(moba_stable_count_kernel, dim3(sgrid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
+                         (int32_t)nbuckets, srows, counts, wg_counts);
+    else
+      hipLaunchKernelGGL(moba_count_kernel, dim3(grid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
+                         (int32_t)nbuckets, counts);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(moba_scan_kernel, dim3(1), dim3(1024), 0, s, counts, (int32_t)nbuckets, offsets, cursor,
                      ntiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (stable && nbuckets > 0) {
+    hipLaunchKernelGGL(moba_wg_scan_kernel, dim3((unsigned)cdiv(nbuckets, 64)), dim3(64 * kScanParts), 0, s,
+                       (const int32_t*)wg_counts, (int32_t)sgrid, (int32_t)nbuckets, (const int32_t*)offsets,
+                       wg_base);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (nbuckets > 0) {
     const int64_t max_tiles = moba_max_tiles(nrows, topk, nbuckets);
     hipLaunchKernelGGL(moba_tiles_kernel, dim3((unsigned)cdiv(max_tiles, 256)), dim3(256), 0, s, counts,
                        (int32_t)nbuckets, offsets, (int32_t)nbc, (int32_t)hkv, seq_len, block, d, tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(moba_scatter_kernel, dim3(grid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
-                       (int32_t)nbuckets, cursor, entries);
+    if (stable) {
+      // sort width: the workgroup's sequence numbers rounded up to a power of two
+      int np = 256;
+      while (np < srows * (topk - 1)) np <<= 1;
+#define QAT_STS(E_)                                                                                         \
+  hipLaunchKernelGGL(moba_stable_scatter_kernel<E_>, dim3(sgrid), dim3(256), 0, s, blk, (int32_t)nrows, m, \
+                     topk, (int32_t)nbuckets, srows, (const int32_t*)wg_base, entries)
+      if (np <= 256) QAT_STS(1);
+      else if (np <= 512) QAT_STS(2);
+      else if (np <= 1024) QAT_STS(4);
+      else if (np <= 2048) QAT_STS(8);
+      else if (np <= 4096) QAT_STS(16);
+      else QAT_STS(32);
+#undef QAT_STS
+    } else
+      hipLaunchKernelGGL(moba_scatter_kernel, dim3(grid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
+                         (int32_t)nbuckets, cursor, entries);
     e = hipGetLastError();
   }
   return e;

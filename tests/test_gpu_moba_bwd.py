@@ -80,6 +80,12 @@ def test_moba_bwd_gqa_32k_full_size():
     q, k, v, _ = synth.moba_inputs(2, 1, n, hq, hkv, d, torch.bfloat16, DEV, planted=8, block=block)
     p, blk, do, dq, dk, dv = forward_backward(q, k, v, block, topk, torch.bfloat16, seed=62)
     print("[moba bwd 32k] gpu done", flush=True)
+    # reproducible: a second call gives the same bits (the dispatch places a
+    # bucket's rows in row order for the gradient pass)
+    out, lse = qat.moba_sparse_attn(p, q, k, v, blk)
+    dq2, dk2, dv2 = qat.moba_sparse_attn_bwd(p, q, k, v, blk, do, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2), "gradients differ between calls"
     check_identities(p, do, dk, dv)
     qn, kn, vn = to64(q[0]), to64(k[0]), to64(v[0])
     blk_g = blk[0].cpu().numpy()

@@ -3,10 +3,7 @@ every entry point that takes a workspace runs twice on the same inputs, once
 with the workspace zeroed and once filled with 0xFF bytes (NaN as bf16 and
 float32), and the outputs must be bit-identical (and finite). A kernel that
 reads a workspace region it never wrote (a partial of a block that was not
-gated, a slot past a row's selection) fails here. One exception: MoBA's
-dK/dV sum each gated block's rows in the order the dispatch bucketed them,
-and that order comes from atomic cursors, so those two are compared within a
-few float32 roundings instead (a stale NaN read would still show)."""
+gated, a slot past a row's selection) fails here."""
 import pytest
 import torch
 
@@ -70,12 +67,8 @@ def test_moba_decode_and_gradients_ignore_stale_workspace():
     grads = []
     for ws in _two_workspaces(qat.moba_bwd_workspace_size(p)):
         grads.append(qat.moba_sparse_attn_bwd(p, q, k, v, blk, do, lse, ws=ws))
-    _same(grads[0][0], grads[1][0], "moba dq")
-    for a, b, name in zip(grads[0][1:], grads[1][1:], ("dk", "dv")):
-        torch.cuda.synchronize()
-        assert torch.isfinite(a).all() and torch.isfinite(b).all(), f"moba {name}: non-finite values"
-        tol = 1e-5 * a.abs().max().item()
-        assert (a - b).abs().max().item() <= tol, f"moba {name}: depends on the workspace's prior contents"
+    for a, b, name in zip(grads[0], grads[1], ("dq", "dk", "dv")):
+        _same(a, b, f"moba {name}")
 
 
 @pytest.mark.parametrize("m", [256, 1])
