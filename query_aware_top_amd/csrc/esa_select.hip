@@ -410,18 +410,6 @@ __device__ TkCut tk_cut(const int32_t* __restrict__ hist, int npass, int32_t k, 
   return cut;
 }
 
-__device__ __forceinline__ float tk_u(int mode, const float* __restrict__ upart, int nqsplit,
-                                      const float* __restrict__ s_in, float mx, float clip, float tau2,
-                                      float inv_l, int64_t bi, int64_t n_mid, int64_t j) {
-  if (mode == 0) {
-    double acc = 0.0;
-    for (int sp = 0; sp < nqsplit; ++sp) acc += (double)upart[(bi * nqsplit + sp) * n_mid + j];
-    return (float)acc;
-  }
-  if (mode == 2) return __builtin_amdgcn_exp2f(tau2 * (s_in[bi * n_mid + j] - mx)) * inv_l;
-  return fmaxf(s_in[bi * n_mid + j] - mx, -clip);
-}
-
 template <int PER>
 __global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
     int mode, const float* __restrict__ upart, int nqsplit, const float* __restrict__ s_in,
@@ -458,11 +446,39 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
     inv_l = 1.f / l;
   }
   for (int i = tid; i < kTkBins; i += kTkThreads) s_h[i] = 0;
-  // u over [j0 - r, j0 + slice + r) clipped to M
+  // u over [j0 - r, j0 + slice + r) clipped to M, PER values per thread and
+  // round with all their loads in flight (clamped indices, results masked)
   const int64_t lo = max((int64_t)0, j0 - radius);
   const int64_t hi = min(n_mid, j0 + (kTkThreads * PER) + radius);
-  for (int64_t j = lo + tid; j < hi; j += kTkThreads)
-    s_u[j - j0 + radius] = tk_u(mode, upart, nqsplit, s_in, mx, clip, tau2, inv_l, bi, n_mid, j);
+  for (int64_t jb = lo; jb < hi; jb += (int64_t)kTkThreads * PER) {
+    float uv[PER];
+    if (mode == 0) {   // the query-split partial sums, added in float64 in split order
+      double acc[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = 0.0;
+      for (int sp = 0; sp < nqsplit; ++sp) {
+        float t[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) t[e] = upart[(bi * nqsplit + sp) * n_mid + min(jb + e * kTkThreads + tid, hi - 1)];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += (double)t[e];
+      }
+#pragma unroll
+      for (int e = 0; e < PER; ++e) uv[e] = (float)acc[e];
+    } else {
+      float t[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) t[e] = s_in[bi * n_mid + min(jb + e * kTkThreads + tid, hi - 1)];
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        uv[e] = mode == 2 ? __builtin_amdgcn_exp2f(tau2 * (t[e] - mx)) * inv_l : fmaxf(t[e] - mx, -clip);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int64_t j = jb + e * kTkThreads + tid;
+      if (j < hi) s_u[j - j0 + radius] = uv[e];
+    }
+  }
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -496,12 +512,14 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_hist_kernel(int pass, con
   for (int i = threadIdx.x; i < nb; i += kTkThreads) s_h[i] = 0;
   __syncthreads();
   const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER) + threadIdx.x;
+  uint32_t kv[PER];   // all loads in flight at once (clamped indices, masked below)
+#pragma unroll
+  for (int e = 0; e < PER; ++e) kv[e] = keys[bi * n_mid + min(j0 + e * kTkThreads, n_mid - 1)];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int64_t j = j0 + e * kTkThreads;
-    if (j >= n_mid) break;
-    const uint32_t key = keys[bi * n_mid + j];
-    if ((key & cut.mask) == cut.prefix) atomicAdd(&s_h[(key >> tk_shift(pass)) & (nb - 1)], 1);
+    const uint32_t key = kv[e];
+    if (j0 + e * kTkThreads < n_mid && (key & cut.mask) == cut.prefix)
+      atomicAdd(&s_h[(key >> tk_shift(pass)) & (nb - 1)], 1);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nb; i += kTkThreads)
@@ -521,13 +539,14 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_count_kernel(const uint32
   const uint32_t T = cut.prefix;
   const int64_t j0 = (int64_t)blockIdx.x * (kTkThreads * PER) + threadIdx.x;
   int32_t gt = 0, eq = 0;
+  uint32_t kv[PER];   // all loads in flight at once (clamped indices, masked below)
+#pragma unroll
+  for (int e = 0; e < PER; ++e) kv[e] = keys[bi * n_mid + min(j0 + e * kTkThreads, n_mid - 1)];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int64_t j = j0 + e * kTkThreads;
-    if (j >= n_mid) break;
-    const uint32_t key = keys[bi * n_mid + j];
-    gt += key > T;
-    eq += key == T;
+    const bool in = j0 + e * kTkThreads < n_mid;
+    gt += in && kv[e] > T;
+    eq += in && kv[e] == T;
   }
   int32_t tgt, teq;
   tk_scan(gt, s_w, &tgt);
@@ -579,11 +598,14 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_emit_kernel(const uint32_
   uint32_t kv[PER];
   {   // the slice's keys through LDS: coalesced loads, then PER consecutive per thread
     const int64_t s0 = (int64_t)blockIdx.x * (kTkThreads * PER);
+    uint32_t t[PER];   // all loads in flight at once (clamped indices, masked below)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) t[e] = keys[bi * n_mid + min(s0 + e * kTkThreads + threadIdx.x, n_mid - 1)];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int64_t j = s0 + e * kTkThreads + threadIdx.x;
       const int jl = e * kTkThreads + threadIdx.x;
-      s_k[jl + jl / PER] = j < n_mid ? keys[bi * n_mid + j] : 0u;
+      s_k[jl + jl / PER] = j < n_mid ? t[e] : 0u;
     }
     __syncthreads();
   }
