@@ -412,21 +412,23 @@ static int esa_score_and_select(const qat_esa_params* p, const EsaLayout& L, con
   const float tau2 = votes ? tau * 1.4426950408889634f : 0.f;
   hipError_t e;
   int mode;
+  // the scoring kernels also clear the top-k histograms (n_mid > 0: they run)
+  const int64_t nhist = nsel * 3 * 2048;
   if (p->chunk_len > 1) {
     mode = 0;
     qat::KTimer tm("esa_scores", s);
     e = qat::launch_esa_prefill_scores(q_hi, q_lo, kc, g, nsel, p->chunk_len, L.mid0, L.n_mid, dc, p->clip, tau2,
-                                       L.rowmax_part, L.rowsum_part, L.rowmax, L.upart, s);
+                                       L.rowmax_part, L.rowsum_part, L.rowmax, L.upart, L.tk_hist, nhist, s);
   } else {
     mode = votes ? 2 : 1;
     qat::KTimer tm("esa_decode_scan", s);
     e = qat::launch_esa_decode_scan(q_dec, dec_bf16, kc, g, nsel, L.mid0, L.n_mid, dc, tau2, L.sraw, L.smax, L.ssum,
-                                    s);
+                                    L.tk_hist, nhist, s);
   }
   if (e != hipSuccess) return hip_status(e, "esa selection: scoring");
   qat::KTimer tm("esa_topk", s);
   e = qat::launch_esa_topk(mode, L.upart, L.nqsplit, L.sraw, L.smax, L.ssum, L.nscan, p->clip, tau2, nsel, L.n_mid,
-                           p->radius, p->topk, L.mid0, L.tk_hist, L.tk_cnt, L.keys, scores, sel, n_sel, s);
+                           p->radius, p->topk, L.mid0, L.tk_hist, L.tk_cnt, L.keys, scores, sel, n_sel, true, s);
   return hip_status(e, "esa selection: top-k");
 }
 

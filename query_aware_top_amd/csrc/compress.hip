@@ -101,6 +101,55 @@ __global__ __launch_bounds__(256) void compress_partial_kernel(
   }
 }
 
+// Few rows (decode: one row per sequence): the four waves of a workgroup
+// take four 16-column blocks of the same 16 rows, one accumulator each, so a
+// wave runs a quarter of the matrix ops of the row-stacked layout above over
+// the same k range and no wave computes rows past n. Same operand order,
+// same partial layout.
+constexpr int kCmpColRows = 32;   // at most this many rows use the column layout
+
+template <typename TX, typename TW>
+__global__ __launch_bounds__(256) void compress_partial_cols_kernel(
+    const TX* __restrict__ x, int64_t n, int64_t x_stride, int64_t d_model,
+    const TW* __restrict__ W, int64_t d_c, int64_t k_per_split, double* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int64_t col0 = ((int64_t)blockIdx.y * 4 + wave) * 16;
+  if (col0 >= d_c) return;   // wave-uniform; no barrier below
+  const int split = blockIdx.z;
+  const int64_t k0 = (int64_t)split * k_per_split;
+  const int64_t k1 = min(d_model, k0 + k_per_split);
+  const int r = lane & 15, j = lane >> 4;
+  const int64_t row = row0 + r;
+  const TX* xr = x + (row < n ? row : 0) * x_stride + 8 * j;
+  const TW* wr = W + (col0 + r) * d_model + 8 * j;
+  f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+  Raw8<TX> xa;
+  Raw8<TW> wa;
+  if (k0 < k1) {
+    xa.load(xr + k0);
+    wa.load(wr + k0);
+  }
+  for (int64_t kb = k0; kb < k1; kb += 32) {
+    const Raw8<TX> xc = xa;
+    const Raw8<TW> wc = wa;
+    if (kb + 32 < k1) {
+      xa.load(xr + kb + 32);
+      wa.load(wr + kb + 32);
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(row < n ? xc.get(st) : 0.0, wc.get(st), acc, 0, 0, 0);
+  }
+  double* dst = partial + (int64_t)split * n * d_c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t orow = row0 + j + 4 * i;
+    if (orow < n) dst[orow * d_c + col0 + r] = acc[i];
+  }
+}
+
 // Sum the split partials in split order, add the bias, round once.
 // kind 0: float32 out; 1: bf16 out; 2: float32 out plus bf16 hi/lo split
 // (hi = bf16(v), lo = bf16(v - hi)) used by the two-term bf16 scoring.
@@ -260,6 +309,22 @@ hipError_t launch_compress_partial(const void* x, int64_t n, int64_t x_stride, i
                                    bool x_bf16, const void* W, bool w_bf16, int64_t d_c, int nsplit,
                                    double* partial, hipStream_t s) {
   const int64_t k_per_split = cdiv(d_model / 32, nsplit) * 32;
+  if (n <= kCmpColRows && d_c % 16 == 0) {
+    dim3 grid((unsigned)cdiv(n, 16), (unsigned)cdiv(d_c, 64), (unsigned)nsplit);
+    if (x_bf16 && w_bf16)
+      hipLaunchKernelGGL((compress_partial_cols_kernel<bf16, bf16>), grid, dim3(256), 0, s, (const bf16*)x, n,
+                         x_stride, d_model, (const bf16*)W, d_c, k_per_split, partial);
+    else if (!x_bf16 && !w_bf16)
+      hipLaunchKernelGGL((compress_partial_cols_kernel<float, float>), grid, dim3(256), 0, s, (const float*)x, n,
+                         x_stride, d_model, (const float*)W, d_c, k_per_split, partial);
+    else if (x_bf16)
+      hipLaunchKernelGGL((compress_partial_cols_kernel<bf16, float>), grid, dim3(256), 0, s, (const bf16*)x, n,
+                         x_stride, d_model, (const float*)W, d_c, k_per_split, partial);
+    else
+      hipLaunchKernelGGL((compress_partial_cols_kernel<float, bf16>), grid, dim3(256), 0, s, (const float*)x, n,
+                         x_stride, d_model, (const bf16*)W, d_c, k_per_split, partial);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)cdiv(n, kCmpRows), (unsigned)cdiv(d_c, kCmpCols), (unsigned)nsplit);
   if (x_bf16 && w_bf16)
     hipLaunchKernelGGL((compress_partial_kernel<bf16, bf16>), grid, dim3(256), 0, s, (const bf16*)x, n,

@@ -43,6 +43,16 @@ namespace qat {
 // tile's loads in flight during the current tile's matrix ops) and hold the
 // other operand in registers; rows are stored with the attention engine's
 // chunk swizzle so the A-operand reads are bank-conflict free.
+// Clears the top-k histograms of the selections (n ints at h; h may be
+// NULL): the scoring kernels do it as a side job, since the top-k passes
+// that count into them run after the scoring in stream order.
+__device__ __forceinline__ void clear_topk_hist(int32_t* __restrict__ h, int64_t n) {
+  if (!h) return;
+  const int64_t nthr = (int64_t)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+  const int64_t wg = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+  for (int64_t i = wg * blockDim.x + threadIdx.x; i < n; i += nthr) h[i] = 0;
+}
+
 constexpr int kScWaves = 4;
 
 constexpr int kScRows = 32 * kScWaves;   // register-held rows per workgroup
@@ -172,7 +182,8 @@ template <int DC, bool VOTE, bool HILO>
 __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
     const bf16* __restrict__ q_hi, const bf16* __restrict__ q_lo, const float* __restrict__ rowmax,
     const bf16* __restrict__ kc, ScGeom g, int64_t m, int64_t mid0, int64_t n_mid,
-    int64_t rows_per_split, int nqsplit, float clip, float tau2, float* __restrict__ upart) {
+    int64_t rows_per_split, int nqsplit, float clip, float tau2, float* __restrict__ upart,
+    int32_t* __restrict__ hist0, int64_t nhist) {
   __shared__ __align__(16) bf16 qh0[kKT * DC];
   __shared__ __align__(16) bf16 qh1[kKT * DC];
   __shared__ __align__(16) bf16 ql0[HILO ? kKT * DC : 8];
@@ -239,6 +250,7 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
   }
   total += __shfl_xor(total, 32, 64);
   if (kvalid && h == 0) upart[(bi * nqsplit + blockIdx.y) * n_mid + key] = (float)total;
+  clear_topk_hist(hist0, nhist);
 }
 
 constexpr int kScanUnroll = 8;
@@ -252,7 +264,7 @@ template <int DC, bool VOTE, typename QT>
 __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
     const QT* __restrict__ qc, const bf16* __restrict__ kc, ScGeom g, int64_t mid0, int64_t n_mid,
     int64_t keys_per_wg, float tau2, float* __restrict__ s_out, float* __restrict__ smax_part,
-    float* __restrict__ ssum_part) {
+    float* __restrict__ ssum_part, int32_t* __restrict__ hist0, int64_t nhist) {
   constexpr int LPK = DC / 8;          // lanes per key
   constexpr int KPW = 256 / LPK;       // keys per workgroup pass
   __shared__ float wmax[4], wsum[4];
@@ -312,6 +324,7 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
     smax_part[bi * gridDim.x + blockIdx.x] = m2;
     if (VOTE) ssum_part[bi * gridDim.x + blockIdx.x] = l2;
   }
+  clear_topk_hist(hist0, nhist);
 }
 
 // ---------------------------------------------------------------------------
@@ -661,19 +674,19 @@ template <int DC, bool VOTE, bool HILO>
 static void launch_scores_dc(const bf16* q_hi, const bf16* q_lo, const bf16* kc, const ScGeom& g, dim3 g1, dim3 g2,
                              int64_t m, int64_t mid0, int64_t n_mid, int64_t kps, int ks_eff, int64_t rps, int qs_eff,
                              int64_t rows, float clip, float tau2, float* rowmax_part, float* rowsum_part,
-                             float* rowmax, float* upart, hipStream_t s) {
+                             float* rowmax, float* upart, int32_t* hist0, int64_t nhist, hipStream_t s) {
   launch_timed("esa_rowmax", esa_rowmax_kernel<DC, VOTE, HILO>, g1, dim3(64 * kScWaves), 0, s, q_hi, q_lo, kc, g, m,
                mid0, n_mid, kps, ks_eff, tau2, rowmax_part, rowsum_part);
   hipLaunchKernelGGL(esa_rowmax_final_kernel<VOTE>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s, rowmax_part,
                      rowsum_part, ks_eff, rows, tau2, rowmax);
   launch_timed("esa_colsum", esa_colsum_kernel<DC, VOTE, HILO>, g2, dim3(64 * kScWaves), 0, s, q_hi, q_lo, rowmax, kc,
-               g, m, mid0, n_mid, rps, qs_eff, clip, tau2, upart);
+               g, m, mid0, n_mid, rps, qs_eff, clip, tau2, upart, hist0, nhist);
 }
 
 hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const bf16* kc, const ScGeom& g,
                                      int64_t nsel, int64_t m, int64_t mid0, int64_t n_mid, int64_t dc, float clip,
                                      float tau2, float* rowmax_part, float* rowsum_part, float* rowmax,
-                                     float* upart, hipStream_t s) {
+                                     float* upart, int32_t* hist0, int64_t nhist, hipStream_t s) {
   if (n_mid <= 0) return hipSuccess;
   const bool vote = tau2 > 0.f;
   const int ks = esa_key_splits(n_mid, m);
@@ -688,10 +701,10 @@ hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const b
   do {                                                                                                         \
     if (vote)                                                                                                  \
       launch_scores_dc<DC_, true, HL_>(q_hi, q_lo, kc, g, g1, g2, m, mid0, n_mid, kps, ks_eff, rps, qs_eff,    \
-                                       nsel * m, clip, tau2, rowmax_part, rowsum_part, rowmax, upart, s);      \
+                                       nsel * m, clip, tau2, rowmax_part, rowsum_part, rowmax, upart, hist0, nhist, s);      \
     else                                                                                                       \
       launch_scores_dc<DC_, false, HL_>(q_hi, q_lo, kc, g, g1, g2, m, mid0, n_mid, kps, ks_eff, rps, qs_eff,   \
-                                        nsel * m, clip, tau2, rowmax_part, rowsum_part, rowmax, upart, s);     \
+                                        nsel * m, clip, tau2, rowmax_part, rowsum_part, rowmax, upart, hist0, nhist, s);     \
   } while (0)
   if (q_lo) {
     switch (dc) {
@@ -717,18 +730,20 @@ int esa_prefill_qsplits_eff(int64_t n_mid, int64_t m) {
 
 template <int DC, typename QT>
 static void launch_scan_dc(const QT* q, const bf16* kc, const ScGeom& g, dim3 grid, int64_t mid0, int64_t n_mid,
-                           int64_t kpw, float tau2, float* s_out, float* smax_part, float* ssum_part, hipStream_t s) {
+                           int64_t kpw, float tau2, float* s_out, float* smax_part, float* ssum_part,
+                           int32_t* hist0, int64_t nhist, hipStream_t s) {
   if (tau2 > 0.f)
     launch_timed("esa_decode_scan", esa_decode_scan_kernel<DC, true, QT>, grid, dim3(256), 0, s, q, kc, g, mid0,
-                 n_mid, kpw, tau2, s_out, smax_part, ssum_part);
+                 n_mid, kpw, tau2, s_out, smax_part, ssum_part, hist0, nhist);
   else
     launch_timed("esa_decode_scan", esa_decode_scan_kernel<DC, false, QT>, grid, dim3(256), 0, s, q, kc, g, mid0,
-                 n_mid, kpw, tau2, s_out, smax_part, ssum_part);
+                 n_mid, kpw, tau2, s_out, smax_part, ssum_part, hist0, nhist);
 }
 
 hipError_t launch_esa_decode_scan(const void* q, bool q_bf16, const bf16* kc, const ScGeom& g, int64_t nsel,
                                   int64_t mid0, int64_t n_mid, int64_t dc, float tau2, float* s_out,
-                                  float* smax_part, float* ssum_part, hipStream_t s) {
+                                  float* smax_part, float* ssum_part, int32_t* hist0, int64_t nhist,
+                                  hipStream_t s) {
   if (n_mid <= 0) return hipSuccess;
   const int nw = esa_scan_wgs(n_mid);
   const int64_t kpw = cdiv(n_mid, nw);
@@ -736,14 +751,14 @@ hipError_t launch_esa_decode_scan(const void* q, bool q_bf16, const bf16* kc, co
   const float* qf = (const float*)q;
   const bf16* qb = (const bf16*)q;
   if (q_bf16) {
-    if (dc == 64) launch_scan_dc<64>(qb, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s);
-    else launch_scan_dc<128>(qb, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s);
+    if (dc == 64) launch_scan_dc<64>(qb, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, hist0, nhist, s);
+    else launch_scan_dc<128>(qb, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, hist0, nhist, s);
   } else {
     switch (dc) {
-      case 32: launch_scan_dc<32>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s); break;
-      case 64: launch_scan_dc<64>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s); break;
-      case 128: launch_scan_dc<128>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s); break;
-      default: launch_scan_dc<256>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, s); break;
+      case 32: launch_scan_dc<32>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, hist0, nhist, s); break;
+      case 64: launch_scan_dc<64>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, hist0, nhist, s); break;
+      case 128: launch_scan_dc<128>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, hist0, nhist, s); break;
+      default: launch_scan_dc<256>(qf, kc, g, grid, mid0, n_mid, kpw, tau2, s_out, smax_part, ssum_part, hist0, nhist, s); break;
     }
   }
   return hipGetLastError();
@@ -759,12 +774,12 @@ static hipError_t launch_esa_topk_per(int mode, const float* upart, int nqsplit,
                                       float tau2, int64_t batch, int64_t n_mid,
                                       int radius, int topk, int64_t mid0, int32_t* hist, int2* wgcnt,
                                       uint32_t* keys, float* scores_out, int32_t* sel, int32_t* n_sel,
-                                      hipStream_t s) {
+                                      bool hist_clear, hipStream_t s) {
   const int64_t nwg = std::max<int64_t>(1, cdiv(n_mid, kTkThreads * PER));
   const dim3 grid((unsigned)nwg, (unsigned)batch);
   hipError_t e;
   if (n_mid > 0) {
-    if ((e = launch_fill_i32(hist, batch * 3 * kTkBins, 0, s)) != hipSuccess) return e;
+    if (!hist_clear && (e = launch_fill_i32(hist, batch * 3 * kTkBins, 0, s)) != hipSuccess) return e;
     hipLaunchKernelGGL(esa_topk_prep_kernel<PER>, grid, dim3(kTkThreads), 0, s, mode, upart, nqsplit, s_in,
                        smax_part, ssum_part, nsmax, clip, tau2, n_mid, radius, keys, scores_out, hist);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -786,7 +801,7 @@ hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const floa
                            const float* ssum_part, int nsmax, float clip, float tau2, int64_t batch, int64_t n_mid,
                            int radius, int topk, int64_t mid0,
                            int32_t* hist, int2* wgcnt, uint32_t* keys, float* scores_out, int32_t* sel,
-                           int32_t* n_sel, hipStream_t s) {
+                           int32_t* n_sel, bool hist_clear, hipStream_t s) {
   // the widest split that still gives every pass 256 workgroups (the
   // passes are latency-bound: fewer candidates per thread when there are
   // few sequences); wgcnt holds esa_topk_slices(n_mid) >= slices entries
@@ -796,18 +811,18 @@ hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const floa
   // per-workgroup cost (reading the histograms, clearing the bins)
   if (batch * cdiv(n_mid, kTkThreads * 32) >= 1024)
     return launch_esa_topk_per<32>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius, topk,
-                                   mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
+                                   mid0, hist, wgcnt, keys, scores_out, sel, n_sel, hist_clear, s);
   if (batch * cdiv(n_mid, kTkThreads * 16) >= 256)
     return launch_esa_topk_per<16>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius, topk,
-                                   mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
+                                   mid0, hist, wgcnt, keys, scores_out, sel, n_sel, hist_clear, s);
   if (s8 >= 256)
     return launch_esa_topk_per<8>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius, topk,
-                                  mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
+                                  mid0, hist, wgcnt, keys, scores_out, sel, n_sel, hist_clear, s);
   if (s4 >= 256)
     return launch_esa_topk_per<4>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius, topk,
-                                  mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
+                                  mid0, hist, wgcnt, keys, scores_out, sel, n_sel, hist_clear, s);
   return launch_esa_topk_per<kTkPerMin>(mode, upart, nqsplit, s_in, smax_part, ssum_part, nsmax, clip, tau2, batch, n_mid, radius,
-                                        topk, mid0, hist, wgcnt, keys, scores_out, sel, n_sel, s);
+                                        topk, mid0, hist, wgcnt, keys, scores_out, sel, n_sel, hist_clear, s);
 }
 
 }  // namespace qat

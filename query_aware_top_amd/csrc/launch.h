@@ -125,20 +125,23 @@ struct ScGeom {
 hipError_t launch_esa_prefill_scores(const bf16* q_hi, const bf16* q_lo, const bf16* kc, const ScGeom& g,
                                      int64_t nsel, int64_t m, int64_t mid0, int64_t n_mid, int64_t dc, float clip,
                                      float tau2, float* rowmax_part, float* rowsum_part, float* rowmax,
-                                     float* upart, hipStream_t s);
+                                     float* upart, int32_t* hist0, int64_t nhist, hipStream_t s);
 // q: float32 (q_bf16 false) or bfloat16 rows
 hipError_t launch_esa_decode_scan(const void* q, bool q_bf16, const bf16* kc, const ScGeom& g, int64_t nsel,
                                   int64_t mid0, int64_t n_mid, int64_t dc, float tau2, float* s_out,
-                                  float* smax_part, float* ssum_part, hipStream_t s);
+                                  float* smax_part, float* ssum_part, int32_t* hist0, int64_t nhist,
+                                  hipStream_t s);
 int esa_topk_slices(int64_t n_mid);
 int esa_topk_max_radius();
-// hist: batch*3*2048 int32, wgcnt: batch*esa_topk_slices(n_mid) int2 (scratch)
+// hist: batch*3*2048 int32, wgcnt: batch*esa_topk_slices(n_mid) int2 (scratch);
+// hist_clear: the scoring kernels have already zeroed hist (hist0/nhist of
+// the scoring launchers), else a fill runs first
 // mode 0: prefill importance sums; 1: decode, clamp; 2: decode, votes
 hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const float* s_in, const float* smax_part,
                            const float* ssum_part, int nsmax, float clip, float tau2, int64_t batch, int64_t n_mid,
                            int radius, int topk, int64_t mid0,
                            int32_t* hist, int2* wgcnt, uint32_t* keys, float* scores_out, int32_t* sel,
-                           int32_t* n_sel, hipStream_t s);
+                           int32_t* n_sel, bool hist_clear, hipStream_t s);
 
 // ---- ESA attention (esa_attn.hip) -----------------------------------------
 int esa_decode_splits(int64_t batch, int64_t n_init, int64_t topk, int64_t window);

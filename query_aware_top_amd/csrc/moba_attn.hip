@@ -455,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_kernel(
   float inv_l, lse;
   fa_finish<D>(st, inv_l, lse);
   const int64_t pidx = row * (topk - 1) + slot;
-  if ((lane >> 5) == 0 && valid) part_lse[pidx] = lse;
+  if ((lane >> 5) == 0 && valid) __builtin_nontemporal_store(lse, part_lse + pidx);
   fa_store_rows_staged<D>(st, inv_l, s_stage + wave * 32 * (D + 8), s_rows + wave * 32, valid ? pidx : -1, part_o);
 }
 
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void moba_past_persist_kernel(
       fa_finish<D>(st, inv_l, lse);
       const bool mine = e.rs >= 0;
       const int64_t pidx = mine ? (int64_t)(e.rs >> 4) * km + (e.rs & 15) : 0;
-      if ((lane >> 5) == 0 && mine) part_lse[pidx] = lse;
+      if ((lane >> 5) == 0 && mine) __builtin_nontemporal_store(lse, part_lse + pidx);
       const int wv = threadIdx.x >> 6;
       fa_store_rows_staged<D>(st, inv_l, s_stage + wv * 32 * (D + 8), s_rows + wv * 32, mine ? pidx : -1, part_o);
   #pragma unroll
@@ -849,7 +849,9 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
     w[1] = pack_bf16x2(a[2], a[3]);
     w[2] = pack_bf16x2(cc[0], cc[1]);
     w[3] = pack_bf16x2(cc[2], cc[3]);
-    *(u32x4*)(out + orow * D + sub * 8) = w;
+    // non-temporal: nothing in this pass reads out again, and a cached copy
+    // would leave dirty lines whose write-back slows the next kernel's reads
+    __builtin_nontemporal_store(w, (u32x4*)(out + orow * D + sub * 8));
   }
 }
 
