@@ -72,6 +72,30 @@ __device__ __forceinline__ void dq_tile_prod(const int* kofs, const bf16* __rest
     }
 }
 
+// The 32-key (or 32-row) half sb of two such products at once, S from tile
+// a with fragments b and dP from tile c with fragments d (the two chains
+// interleaved; the same operands and order as dq_tile_prod).
+template <int D>
+__device__ __forceinline__ void dq_half_prod(const int* kofs, const bf16* __restrict__ a_tile, const bf16x8* b,
+                                             const bf16* __restrict__ c_tile, const bf16x8* d, int sb, f32x16& s,
+                                             f32x16& dp) {
+  const char* ab = reinterpret_cast<const char*>(a_tile);
+  const char* cb = reinterpret_cast<const char*>(c_tile);
+  constexpr int RB = D * 2;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s[i] = 0.f;
+    dp[i] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const bf16x8 x = *(const bf16x8*)(ab + kofs[c] + sb * 32 * RB);
+    const bf16x8 y = *(const bf16x8*)(cb + kofs[c] + sb * 32 * RB);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, b[c], s, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(y, d[c], dp, 0, 0, 0);
+  }
+}
+
 // bfloat16 hi + lo split of a pair: .x = packed hi, .y = packed lo
 __device__ __forceinline__ uint2 split_pack(float x0, float x1) {
   const bf16 h0 = (bf16)x0, h1 = (bf16)x1;
@@ -195,17 +219,18 @@ __device__ __forceinline__ void kv_load(KvState<D>& st, const bf16* krow, const 
 template <int D, typename RowOk>
 __device__ __forceinline__ void kv_tile(KvState<D>& st, const bf16* __restrict__ qt, const bf16* __restrict__ dt,
                                         const float* lse_t, const float* di_t, float sl2, RowOk row_ok) {
-  f32x16 s[2], dp[2];
-  dq_tile_prod<D>(st.fa.kofs, qt, st.fa.q, s);
-  dq_tile_prod<D>(st.fa.kofs, dt, st.vq, dp);
   const int h = (threadIdx.x & 63) >> 5;
   const char* qb = reinterpret_cast<const char*>(qt);
   const char* db = reinterpret_cast<const char*>(dt);
   constexpr int RB = D * 2;
-  // one 32-row half at a time: its p and ds packs feed the row chunks
-  // kc = 2 sb, 2 sb + 1 of the accumulations
+  // one 32-row half at a time, from its S and dP products to the row chunks
+  // kc = 2 sb, 2 sb + 1 of the accumulations (only one half's scores live)
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
+    // the second half's products are not hoisted above the first half's work
+    if (sb) __builtin_amdgcn_sched_barrier(0);
+    f32x16 s[2], dp[2];
+    dq_half_prod<D>(st.fa.kofs, qt, st.fa.q, dt, st.vq, sb, s[sb], dp[sb]);
     u32x4 pph[2], ppl[2], dsh[2], dsl[2];
     // the half's 16 rows of this lane are 4 runs of 4 consecutive rows
     f32x4 l4[4], d4[4];

@@ -111,19 +111,29 @@ __device__ __forceinline__ void fa_init(FaState<D>& st, const bf16* qrow, bool v
     }
 }
 
+// The lane id as a value the compiler cannot hoist out of a loop: address
+// terms derived from it are recomputed where a load is issued (a few vector
+// ops per tile) instead of being held in registers, or spilled, across a
+// whole tile loop. For kernels at the register limit.
+__device__ __forceinline__ int fa_fresh_lane() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t & 63;
+}
+
 // Issue the direct-to-LDS loads of one 64-key tile of K or V for the calling
 // wave: wave w of NW fills rows [w*64/NW, (w+1)*64/NW). row_ofs(j) gives key
 // j's element offset from src (32-bit: one sequence's K or V holds fewer
 // than 2^31 elements); rows at or beyond n are clamped to row n - 1 (a valid
 // row whose scores the caller masks).
-template <int D, int NW, typename RowOfs, bool CLAMP = true>
+template <int D, int NW, typename RowOfs, bool CLAMP = true, bool FRESH = false>
 __device__ __forceinline__ void fa_issue_one(bf16* __restrict__ dst, const bf16* __restrict__ src, int j0, int n,
                                              RowOfs row_ofs) {
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;       // rows per wave instruction
   constexpr int RPW = kKT / NW;       // rows per wave
   static_assert(RPW % RPI == 0, "tile rows must split evenly over the waves");
-  const int lane = threadIdx.x & 63;
+  const int lane = FRESH ? fa_fresh_lane() : (int)(threadIdx.x & 63);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int i = 0; i < RPW / RPI; ++i) {
@@ -158,6 +168,21 @@ struct FaContig {
     for (int i = 0; i < NI; ++i) {
       const int r = RPW * wave + i * RPI + lane / CPR;
       off[i] = (r * stride + ((lane % CPR) ^ fa_swz<D>(r)) * 8) * 2;
+    }
+  }
+  // issue_checked with the per-lane offsets recomputed from fa_fresh_lane()
+  // (for kernels at the register limit: nothing held across the tile loop)
+  __device__ __forceinline__ static void issue_checked_fresh(bf16* __restrict__ dst, __amdgpu_buffer_rsrc_t rsrc,
+                                                             int j0, int stride) {
+    const int lane = fa_fresh_lane();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int base = j0 * stride * 2;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = RPW * wave + i * RPI + lane / CPR;
+      const int o = (r * stride + ((lane % CPR) ^ fa_swz<D>(r)) * 8) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (RPW * wave + i * RPI) * D), 16, o + base, 0, 0,
+                                               0);
     }
   }
   // As issue, with the tile's start in the per-lane offset, which the

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_kv_kernel(
   const int nlist = ng + (int)m;
   const int j0 = (int)kt * kKvKeys;
   if (j0 >= nlist) return;   // uniform
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int j = j0 + wave * 32 + (lane & 31);
   const bool kvalid = j < nlist;
   const int32_t* lst = keylist + lv * kls;
@@ -114,27 +114,31 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_kv_kernel(
   const bf16* dbase = dout + ((bi * m + i_start) * H + h) * D;
   const int HD = (int)(H * D);
   const float sl2 = scale * kLog2e;
-  // the q / dO rows [i_start, m) of head h through buffer resources: fixed
-  // per-lane offsets, the tile start in the range-checked offset (rows past
-  // m read as zero; their p is masked)
-  FaContig<D, kBwdNW> ctg;
-  ctg.init(HD);
+  // the q / dO rows [i_start, m) of head h through buffer resources: per-lane
+  // offsets recomputed at each issue (this kernel is at the register limit),
+  // the tile start in the range-checked offset (rows past m read as zero;
+  // their p is masked)
   const uint32_t region = nrows > 0 ? (uint32_t)(((int64_t)(nrows - 1) * HD + D) * 2) : 0u;
   const __amdgpu_buffer_rsrc_t rq = fa_rsrc(qbase, region), rd = fa_rsrc(dbase, region);
+  const float* lrow = lse + (bi * m + i_start) * H + h;     // the rows' lse and D, row stride H
+  const float* drow = delta + (bi * m + i_start) * H + h;
   auto issue = [&](bf16* qdst, bf16* ddst, int buf, int rt) {
     const int r0 = rt * 64, n = min(64, nrows - r0);
-    ctg.issue_checked(qdst, rq, r0, HD);
-    ctg.issue_checked(ddst, rd, r0, HD);
+    FaContig<D, kBwdNW>::issue_checked_fresh(qdst, rq, r0, HD);
+    FaContig<D, kBwdNW>::issue_checked_fresh(ddst, rd, r0, HD);
     if (wave == 0) {   // rows past the tile's end repeat its last row (masked)
-      const int64_t row = (bi * m + i_start + r0 + min(lane, n - 1)) * H + h;
-      __builtin_amdgcn_global_load_lds((const global_void*)(lse + row), (lds_void*)(s_lse + buf * 64), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const global_void*)(delta + row), (lds_void*)(s_di + buf * 64), 4, 0, 0);
+      const int ro = (r0 + min(fa_fresh_lane(), n - 1)) * (int)H;
+      __builtin_amdgcn_global_load_lds((const global_void*)(lrow + ro), (lds_void*)(s_lse + buf * 64), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const global_void*)(drow + ro), (lds_void*)(s_di + buf * 64), 4, 0, 0);
     }
   };
   // row m_local of tile rt (query i_start + 64 rt + m_local) sees this lane's
   // key iff it exists and, for a chunk key, i >= j - ng
-  const int kfirst = j >= ng ? j - ng - i_start : -(1 << 30);
+  // (the lane's key index is re-derived per tile from fa_fresh_lane(), and
+  // its cache row after the loop: nothing per lane is held across the loop)
   auto row_ok = [=](int rt) {
+    const int jf = j0 + wave * 32 + (fa_fresh_lane() & 31);
+    const int kfirst = jf >= ng ? jf - ng - i_start : -(1 << 30);
     const int n = min(64, nrows - rt * 64), mm0 = kfirst - rt * 64;
     return [=](int ml) { return ml < n && ml >= mm0; };
   };
@@ -154,6 +158,7 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_kv_kernel(
   }
   fa_wait_loads();
   if (!kvalid) return;
+  const int64_t krow_end = ((bi * ctx_len + lst[j0 + wave * 32 + (fa_fresh_lane() & 31)]) * H + h) * D;
   // add into the caches' gradient rows (accumulator layout d = 32 tq + 8 gi + 4 hl + e)
   const int hl = lane >> 5;
 #pragma unroll
@@ -161,14 +166,14 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_kv_kernel(
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       const int d0 = 32 * tq + 8 * gi + 4 * hl;
-      f32x4 a = *(const f32x4*)(dk + krow + d0), b = *(const f32x4*)(dv + krow + d0);
+      f32x4 a = *(const f32x4*)(dk + krow_end + d0), b = *(const f32x4*)(dv + krow_end + d0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         a[e] += scale * st.fa.o[tq][4 * gi + e];
         b[e] += st.dv[tq][4 * gi + e];
       }
-      *(f32x4*)(dk + krow + d0) = a;
-      *(f32x4*)(dv + krow + d0) = b;
+      *(f32x4*)(dk + krow_end + d0) = a;
+      *(f32x4*)(dv + krow_end + d0) = b;
     }
 }
 

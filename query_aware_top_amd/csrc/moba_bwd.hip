@@ -362,20 +362,28 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_dq_past_kernel(
   if (tile >= ntiles[0]) return;
   const int4 td = tiles[tile];
   const int64_t kv_off = (int64_t)(uint32_t)td.x | ((int64_t)td.y << 32);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int myrow = (int)(id & 1) * kBwdCurRows + wave * 32 + (lane & 31);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int row0 = (int)(id & 1) * kBwdCurRows + wave * 32;   // the wave's first row of the tile
   if ((int)(id & 1) * kBwdCurRows >= td.w) return;   // uniform: no rows in this half
-  const bool valid = myrow < td.w;
-  const int2 e2 = valid ? entries[td.z + myrow] : make_int2(0, 0);
-  const int64_t row = e2.x >> 4;
-  const int slot = e2.x & 15;
   DqState<D> st;
-  dq_init<D>(st, q + (int64_t)e2.y * D, dout + row * D, valid ? lse[row] : 0.f, valid);
+  {
+    const int myrow = row0 + (lane & 31);
+    const bool valid = myrow < td.w;
+    const int2 e2 = valid ? entries[td.z + myrow] : make_int2(0, 0);
+    const int64_t row = e2.x >> 4;
+    dq_init<D>(st, q + (int64_t)e2.y * D, dout + row * D, valid ? lse[row] : 0.f, valid);
+  }
   const int kv_stride = (int)(hkv * D);
   dq_segment<D, kBwdNW>(st, sm, k + kv_off, v + kv_off, block, scale * kLog2e,
                         [=](int j) { return j * kv_stride; }, [](int) { return true; });
   const float dsum = xor32_sum(st.dsum);
-  if (!valid) return;
+  // the row and slot again from the dispatch entry (not held across the loop:
+  // this kernel is at the register limit)
+  const int myrow = row0 + (fa_fresh_lane() & 31);
+  if (myrow >= td.w) return;
+  const int2 e2 = entries[td.z + myrow];
+  const int64_t row = e2.x >> 4;
+  const int slot = e2.x & 15;
   float* dst = part + (row * (topk - 1) + slot) * PS;
   const int h = lane >> 5;
 #pragma unroll
@@ -495,7 +503,7 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_own_kernel(
   float* s_lse = reinterpret_cast<float*>(kv_dyn);          // [2][64]
   float* s_di = s_lse + 128;                                 // [2][64]
   const int64_t b = blockIdx.x / cpb, c = blockIdx.x % cpb, g = blockIdx.y, bi = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t blk0 = b * block, blk1 = min(blk0 + block, seq_len);
   const int64_t c0 = blk0 + c * kKvKeys;
   if (c0 >= blk1) return;   // uniform
@@ -517,14 +525,17 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_own_kernel(
   const int q0 = (int)(t0 * hq + g * G), d0 = (int)((t0 - q_start) * hq + g * G);
   auto issue = [&](bf16* qdst, bf16* ddst, int buf, int rt) {
     const int r0 = rt * 64, n = min(64, nrows - r0);
-    fa_issue_one<D, kBwdNW>(qdst, qbase, 0, n, [=](int j) {
+    // lane terms recomputed at each issue (the kernel is at the register limit)
+    auto qofs = [=](int j) {
       const int r = r0 + j, ti = r / Gi;
       return (q0 + ti * hqi + (r - ti * Gi)) * D;
-    });
-    fa_issue_one<D, kBwdNW>(ddst, dbase, 0, n, [=](int j) {
+    };
+    auto dofs = [=](int j) {
       const int r = r0 + j, ti = r / Gi;
       return (d0 + ti * hqi + (r - ti * Gi)) * D;
-    });
+    };
+    fa_issue_one<D, kBwdNW, decltype(qofs), true, true>(qdst, qbase, 0, n, qofs);
+    fa_issue_one<D, kBwdNW, decltype(dofs), true, true>(ddst, dbase, 0, n, dofs);
     if (wave == 0) {
       // rows past the tile's end repeat its last row (masked)
       const int r = r0 + min(lane, n - 1), ti = r / Gi;
@@ -536,8 +547,11 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_own_kernel(
   };
   // causal mask: row m of tile rt (position t0 + (64 rt + m) / G) sees this
   // lane's key iff m >= (key - t0) G - 64 rt
-  const int kfirst = (int)(key - t0) * Gi;
+  // (the lane's key is re-derived per tile from fa_fresh_lane(), and its row
+  // after the loop: nothing per lane is held across the loop)
   auto row_ok = [=](int rt) {
+    const int64_t kf = c0 + wave * 32 + (fa_fresh_lane() & 31);
+    const int kfirst = (int)(kf - t0) * Gi;
     const int n = min(64, nrows - rt * 64), m0 = kfirst - rt * 64;
     return [=](int m) { return m < n && m >= m0; };
   };
@@ -554,7 +568,11 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void moba_bwd_kv_own_kernel(
     if (rt + 2 < nt) issue(sm.k0, sm.v0, 0, rt + 2);
     kv_tile<D>(st, sm.k1, sm.v1, s_lse + 64, s_di + 64, sl2, row_ok(rt + 1));
   }
-  if (kvalid) kv_write<D, false>(st, dk + krow, dv + krow, scale);
+  if (kvalid) {
+    const int64_t kend = c0 + wave * 32 + (fa_fresh_lane() & 31);
+    const int64_t krow_end = ((bi * seq_len + kend) * hkv + g) * D;
+    kv_write<D, false>(st, dk + krow_end, dv + krow_end, scale);
+  }
 }
 
 // Runs of the gated key kernel: bucket b's dispatch tiles [tile_off[b],
