@@ -766,7 +766,7 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
       }
     }
   };
-  {
+  if (km > 0) {   // topk = 1: no past slots, nothing to load
     // first round: the state is empty, so o = sum_s w_s o_s under one max
     // (no rescale of a zero accumulator)
     float plse[kPreSlots];
