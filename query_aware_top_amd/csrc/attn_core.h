@@ -397,10 +397,27 @@ __device__ __forceinline__ void fa_segment_begin_tiles(const FaSmem<D>& sm, int 
   }
 }
 
-template <int D, bool CAN_MASK, typename Issue, typename KeyOk, typename TileFull>
-__device__ __forceinline__ void fa_segment_run_tiles(FaState<D>& st, const FaSmem<D>& sm, int n, float scale_log2,
-                                                     Issue issue, KeyOk key_ok, TileFull tile_full) {
-  if (n <= 0) return;
+// One pipeline step: scores of the next tile (matrix cores) and the
+// softmax of this one (vector ALUs), then O += P V. LATE issues the softmax
+// first: with eight-wave workgroups the two waves that share a SIMD (w and
+// w + 4) take opposite orders, so one wave's matrix ops run under the
+// other's vector work.
+template <int D, bool CAN_MASK, bool LATE, typename KeyOk, typename TileFull>
+__device__ __forceinline__ void fa_step(FaState<D>& st, f32x16* s_now, f32x16* s_next, const bf16* __restrict__ ks_next,
+                                        const bf16* __restrict__ vs, float scale_log2, int base, int n, KeyOk key_ok,
+                                        TileFull tile_full) {
+  u32x4 pw[4];
+  if constexpr (!LATE) fa_scores<D>(st, ks_next, s_next);
+  if (CAN_MASK && !(base + kKT <= n && tile_full(base)))
+    fa_mask(s_now, [&](int kidx) { return base + kidx < n && key_ok(base + kidx); });
+  fa_softmax<D, CAN_MASK>(st, s_now, pw, scale_log2);
+  if constexpr (LATE) fa_scores<D>(st, ks_next, s_next);
+  fa_pv<D>(st, vs, pw);
+}
+
+template <int D, bool CAN_MASK, bool LATE, typename Issue, typename KeyOk, typename TileFull>
+__device__ __forceinline__ void fa_segment_loop(FaState<D>& st, const FaSmem<D>& sm, int n, float scale_log2,
+                                                Issue issue, KeyOk key_ok, TileFull tile_full) {
   const int nt = (n + kKT - 1) / kKT;
   auto issue_k = [&](bf16* dst, int t) {
     if (t < nt) issue(dst, false, t);
@@ -421,16 +438,14 @@ __device__ __forceinline__ void fa_segment_run_tiles(FaState<D>& st, const FaSme
     // tile is computed unconditionally (past the end it reads a buffer no
     // load is writing and the result is unused) so that it shares a basic
     // block with the softmax it should overlap.
-    fa_scores<D>(st, sm.k1, s_nxt);
-    fa_finish_tile<D, CAN_MASK>(st, s_cur, sm.v0, scale_log2, j * kKT, n, key_ok, tile_full);
+    fa_step<D, CAN_MASK, LATE>(st, s_cur, s_nxt, sm.k1, sm.v0, scale_log2, j * kKT, n, key_ok, tile_full);
     if (j + 1 >= nt) break;
     fa_wait_loads();
     fa_lds_barrier();
     issue_k(sm.k1, j + 3);
     issue_v(sm.v0, j + 2);
     // ---- odd j+1: S(j+2) from K buffer 0, PV(j+1) from V buffer 1
-    fa_scores<D>(st, sm.k0, s_cur);
-    fa_finish_tile<D, CAN_MASK>(st, s_nxt, sm.v1, scale_log2, (j + 1) * kKT, n, key_ok, tile_full);
+    fa_step<D, CAN_MASK, LATE>(st, s_nxt, s_cur, sm.k0, sm.v1, scale_log2, (j + 1) * kKT, n, key_ok, tile_full);
     if (j + 2 >= nt) break;
     fa_wait_loads();
     fa_lds_barrier();
@@ -439,6 +454,21 @@ __device__ __forceinline__ void fa_segment_run_tiles(FaState<D>& st, const FaSme
   }
   fa_wait_loads();
   fa_lds_barrier();
+}
+
+template <int D, bool CAN_MASK, int NW = 0, typename Issue, typename KeyOk, typename TileFull>
+__device__ __forceinline__ void fa_segment_run_tiles(FaState<D>& st, const FaSmem<D>& sm, int n, float scale_log2,
+                                                     Issue issue, KeyOk key_ok, TileFull tile_full) {
+  if (n <= 0) return;
+  if constexpr (NW == 8) {
+    // one copy of the loop per issue order (same barriers in the same sequence)
+    if (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) >= NW / 2)
+      fa_segment_loop<D, CAN_MASK, true>(st, sm, n, scale_log2, issue, key_ok, tile_full);
+    else
+      fa_segment_loop<D, CAN_MASK, false>(st, sm, n, scale_log2, issue, key_ok, tile_full);
+  } else {
+    fa_segment_loop<D, CAN_MASK, false>(st, sm, n, scale_log2, issue, key_ok, tile_full);
+  }
 }
 
 // Row-offset forms: key j of the segment at element offset row_ofs(j) from
@@ -451,21 +481,24 @@ __device__ __forceinline__ void fa_segment_begin(const FaSmem<D>& sm, const bf16
   });
 }
 
-template <int D, int NW, bool CAN_MASK, typename RowOfs, typename KeyOk, typename TileFull>
+// SPLIT: the two issue orders of fa_segment_run_tiles for eight-wave
+// workgroups (false: one order, fewer registers: a kernel with several
+// segments keeps one loop copy per segment and order).
+template <int D, int NW, bool CAN_MASK, bool SPLIT = true, typename RowOfs, typename KeyOk, typename TileFull>
 __device__ __forceinline__ void fa_segment_run(FaState<D>& st, const FaSmem<D>& sm, const bf16* __restrict__ K,
                                                const bf16* __restrict__ V, int n, float scale_log2,
                                                RowOfs row_ofs, KeyOk key_ok, TileFull tile_full) {
-  fa_segment_run_tiles<D, CAN_MASK>(st, sm, n, scale_log2, [&](bf16* dst, bool is_v, int t) {
+  fa_segment_run_tiles<D, CAN_MASK, SPLIT ? NW : 0>(st, sm, n, scale_log2, [&](bf16* dst, bool is_v, int t) {
     fa_issue_one<D, NW>(dst, is_v ? V : K, t * kKT, n, row_ofs);
   }, key_ok, tile_full);
 }
 
-template <int D, int NW, bool CAN_MASK, typename RowOfs, typename KeyOk, typename TileFull>
+template <int D, int NW, bool CAN_MASK, bool SPLIT = true, typename RowOfs, typename KeyOk, typename TileFull>
 __device__ __forceinline__ void fa_segment(FaState<D>& st, const FaSmem<D>& sm, const bf16* __restrict__ K,
                                            const bf16* __restrict__ V, int n, float scale_log2, RowOfs row_ofs,
                                            KeyOk key_ok, TileFull tile_full) {
   fa_segment_begin<D, NW>(sm, K, V, n, row_ofs);
-  fa_segment_run<D, NW, CAN_MASK>(st, sm, K, V, n, scale_log2, row_ofs, key_ok, tile_full);
+  fa_segment_run<D, NW, CAN_MASK, SPLIT>(st, sm, K, V, n, scale_log2, row_ofs, key_ok, tile_full);
 }
 
 // Final normalisation: returns the lane's 1/l and natural-log lse.

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kCcaThreads, 1) void cca_attn_kernel(
   const int nc_wave = tw0 <= t1 ? (int)(cca_window_start(tw0, gg, wg) / gg) : 0;
   const int nc_max = (int)(cca_window_start(t1, gg, wg) / gg);
   const int hd = (int)(hq * D);
-  fa_segment<D, kCcaNW, true>(st, sm, kc + (bi * ngroups * hq + h) * D, vc + (bi * ngroups * hq + h) * D, nc_max,
+  fa_segment<D, kCcaNW, true, false>(st, sm, kc + (bi * ngroups * hq + h) * D, vc + (bi * ngroups * hq + h) * D, nc_max,
                               scale_log2, [=](int c) { return c * hd; }, [=](int c) { return c < nc_lane; },
                               [=](int c0) { return c0 + kKT <= nc_wave; });
   // raw window: keys [lmin, t1] of the tile; this lane sees [ls(t), t]
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kCcaThreads, 1) void cca_attn_kernel(
   const int hi_w = (int)(tw0 - lmin);
   const int kvs = (int)(hkv * D);
   const int64_t rbase = ((bi * seq_len + lmin) * hkv + g) * D;
-  fa_segment<D, kCcaNW, true>(st, sm, k + rbase, v + rbase, n_raw, scale_log2, [=](int j) { return j * kvs; },
+  fa_segment<D, kCcaNW, true, false>(st, sm, k + rbase, v + rbase, n_raw, scale_log2, [=](int j) { return j * kvs; },
                               [=](int j) { return j >= lo && j <= hi; },
                               [=](int j0) { return j0 >= lo_w && j0 + kKT - 1 <= hi_w; });
   float inv_l, lse;
