@@ -217,14 +217,11 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
   };
   const int nt = (n + kKT - 1) / kKT;
   double total = 0.0;
-  issue(0);
-  for (int t = 0; t < nt; ++t) {
-    fa_wait_loads();
-    __syncthreads();
-    if (t + 1 < nt) issue(t + 1);
-    const bf16* th = (t & 1) ? qh1 : qh0;
-    const bf16* tl = (t & 1) ? ql1 : ql0;
-    const float* trm = (t & 1) ? rm1 : rm0;
+  // One tile's scores and their clamped sum; buffers fixed per call site (the
+  // loop below runs tiles in pairs), and only a tile that reaches past the
+  // chunk's last row masks its rows.
+  auto tile_sum = [&](const bf16* th, const bf16* tl, const float* trm, int t, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       f32x16 acc = {};
@@ -242,11 +239,28 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
         for (int e = 0; e < 4; ++e) {
           const float v = VOTE ? __builtin_amdgcn_exp2f(tau2 * acc[4 * g + e] - r4[e])
                                : fmaxf(acc[4 * g + e] - r4[e], -clip);
-          part += (base + g * 8 + h * 4 + e < n) ? v : 0.f;
+          if constexpr (MASKED) part += (base + g * 8 + h * 4 + e < n) ? v : 0.f;
+          else part += v;
         }
       }
       total += (double)part;
     }
+  };
+  auto tile = [&](const bf16* th, const bf16* tl, const float* trm, int t) {
+    if ((t + 1) * kKT <= n) tile_sum(th, tl, trm, t, std::false_type{});
+    else tile_sum(th, tl, trm, t, std::true_type{});
+  };
+  issue(0);
+  for (int t = 0; t < nt; t += 2) {
+    fa_wait_loads();
+    __syncthreads();
+    if (t + 1 < nt) issue(t + 1);
+    tile(qh0, ql0, rm0, t);
+    if (t + 1 >= nt) break;
+    fa_wait_loads();
+    __syncthreads();
+    if (t + 2 < nt) issue(t + 2);
+    tile(qh1, ql1, rm1, t + 1);
   }
   total += __shfl_xor(total, 32, 64);
   if (kvalid && h == 0) upart[(bi * nqsplit + blockIdx.y) * n_mid + key] = (float)total;
