@@ -103,12 +103,9 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
   auto row_ofs = [krow](int j) { return j * krow; };
   const int nt = (n + kKT - 1) / kKT;
   float mx = -__builtin_inff(), lsum = 0.f;
-  fa_issue_one<DC, kScWaves>(kt0, kbase, 0, n, row_ofs);
-  for (int t = 0; t < nt; ++t) {
-    fa_wait_loads();
-    __syncthreads();
-    if (t + 1 < nt) fa_issue_one<DC, kScWaves>((t & 1) ? kt0 : kt1, kbase, (t + 1) * kKT, n, row_ofs);
-    const bf16* tile = (t & 1) ? kt1 : kt0;
+  // one tile's scores folded into the running max (and vote sum); the loop
+  // below runs tiles in pairs so that each call reads a fixed LDS buffer
+  auto tile_max = [&](const bf16* tile, int t) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       f32x16 acc = {};
@@ -120,19 +117,24 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
       }
       const int base = t * kKT + sb * 32;
       if constexpr (VOTE) {
-        float tm = -__builtin_inff();
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (base + (i >> 2) * 8 + h * 4 + (i & 3) < n) tm = fmaxf(tm, acc[i]);
-        const float mn = fmaxf(mx, tm);
-        if (mn != -__builtin_inff()) {
-          float add = 0.f;
+        auto vote = [&](auto masked_c) {   // keys past the split's end only in its last tile
+          constexpr bool MK = decltype(masked_c)::value;
+          float tm = -__builtin_inff();
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (base + (i >> 2) * 8 + h * 4 + (i & 3) < n) add += __builtin_amdgcn_exp2f(tau2 * (acc[i] - mn));
-          lsum = lsum * __builtin_amdgcn_exp2f(tau2 * (mx - mn)) + add;
-          mx = mn;
-        }
+            if (!MK || base + (i >> 2) * 8 + h * 4 + (i & 3) < n) tm = fmaxf(tm, acc[i]);
+          const float mn = fmaxf(mx, tm);
+          if (mn != -__builtin_inff()) {
+            float add = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (!MK || base + (i >> 2) * 8 + h * 4 + (i & 3) < n) add += __builtin_amdgcn_exp2f(tau2 * (acc[i] - mn));
+            lsum = lsum * __builtin_amdgcn_exp2f(tau2 * (mx - mn)) + add;
+            mx = mn;
+          }
+        };
+        if (base + 32 <= n) vote(std::false_type{});
+        else vote(std::true_type{});
       } else if (base + 32 <= n) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[i]);
@@ -142,6 +144,18 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_rowmax_kernel(
           if (base + (i >> 2) * 8 + h * 4 + (i & 3) < n) mx = fmaxf(mx, acc[i]);
       }
     }
+  };
+  fa_issue_one<DC, kScWaves>(kt0, kbase, 0, n, row_ofs);
+  for (int t = 0; t < nt; t += 2) {
+    fa_wait_loads();
+    __syncthreads();
+    if (t + 1 < nt) fa_issue_one<DC, kScWaves>(kt1, kbase, (t + 1) * kKT, n, row_ofs);
+    tile_max(kt0, t);
+    if (t + 1 >= nt) break;
+    fa_wait_loads();
+    __syncthreads();
+    if (t + 2 < nt) fa_issue_one<DC, kScWaves>(kt0, kbase, (t + 2) * kKT, n, row_ofs);
+    tile_max(kt1, t + 1);
   }
   if constexpr (VOTE) {
     vote_merge(mx, lsum, __shfl_xor(mx, 32, 64), __shfl_xor(lsum, 32, 64), tau2);
@@ -251,16 +265,25 @@ __global__ __launch_bounds__(64 * kScWaves) void esa_colsum_kernel(
     else tile_sum(th, tl, trm, t, std::true_type{});
   };
   issue(0);
-  for (int t = 0; t < nt; t += 2) {
-    fa_wait_loads();
-    __syncthreads();
-    if (t + 1 < nt) issue(t + 1);
-    tile(qh0, ql0, rm0, t);
-    if (t + 1 >= nt) break;
-    fa_wait_loads();
-    __syncthreads();
-    if (t + 2 < nt) issue(t + 2);
-    tile(qh1, ql1, rm1, t + 1);
+  if constexpr (DC <= 128) {
+    for (int t = 0; t < nt; t += 2) {
+      fa_wait_loads();
+      __syncthreads();
+      if (t + 1 < nt) issue(t + 1);
+      tile(qh0, ql0, rm0, t);
+      if (t + 1 >= nt) break;
+      fa_wait_loads();
+      __syncthreads();
+      if (t + 2 < nt) issue(t + 2);
+      tile(qh1, ql1, rm1, t + 1);
+    }
+  } else {   // d_c 256: one copy of the tile code (four would not fit the registers)
+    for (int t = 0; t < nt; ++t) {
+      fa_wait_loads();
+      __syncthreads();
+      if (t + 1 < nt) issue(t + 1);
+      tile_sum((t & 1) ? qh1 : qh0, (t & 1) ? ql1 : ql0, (t & 1) ? rm1 : rm0, t, std::true_type{});
+    }
   }
   total += __shfl_xor(total, 32, 64);
   if (kvalid && h == 0) upart[(bi * nqsplit + blockIdx.y) * n_mid + key] = (float)total;
