@@ -387,6 +387,7 @@ __global__ __launch_bounds__(256) void esa_decode_scan_kernel(
 constexpr int kTkThreads = 256;
 constexpr int kTkPerMin = 2;   // candidates per thread: 2 to 32, so that a pass has >= 256 workgroups where it can
 constexpr int kTkMaxRadius = 1024;
+constexpr int kTkWin = 4;      // radii up to this use an unrolled neighbour window
 constexpr int kTkBins = 2048;
 __host__ __device__ constexpr int tk_shift(int pass) { return pass == 0 ? 21 : pass == 1 ? 10 : 0; }
 __host__ __device__ constexpr int tk_bits(int pass) { return pass == 2 ? 10 : 11; }
@@ -530,17 +531,49 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int64_t j = j0 + e * kTkThreads + tid;
-    if (j >= n_mid) break;
-    float v = s_u[j - j0 + radius];
-    const int64_t a = max((int64_t)0, j - radius), b = min(n_mid - 1, j + (int64_t)radius);
-    for (int64_t t = a; t <= b; ++t) v = fmaxf(v, s_u[t - j0 + radius]);
+  // neighbour max in slice-local 32-bit indices: element jl of the slice sits
+  // at s_u[jl + radius]; the window [jl - r, jl + r] is clipped to the middle
+  // part, whose halo holds lo_ok elements before the slice and hi_ok after
+  const int nl = (int)min((int64_t)(kTkThreads * PER), n_mid - j0);
+  const int lo_ok = (int)min((int64_t)radius, j0);
+  const int hi_ok = (int)min((int64_t)radius, n_mid - j0 - nl);
+  auto emit_key = [&](int jl, float v) {
+    const int64_t j = j0 + jl;
     const uint32_t key = float_key(v);
     keys[bi * n_mid + j] = key;
     if (scores_out) scores_out[bi * n_mid + j] = v;
     atomicAdd(&s_h[key >> tk_shift(0)], 1);
+  };
+  if (radius <= kTkWin) {
+    // a fixed window of 2 kTkWin + 1 reads per element, masked to the
+    // radius: every read of the thread's elements is issued at once (a
+    // loop of runtime length would wait for each read in turn)
+    float vv[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int jl = min(e * kTkThreads + tid, nl - 1);
+      float v = s_u[jl + radius];
+#pragma unroll
+      for (int d = -kTkWin; d <= kTkWin; ++d) {
+        const int t = min(max(jl + d, -lo_ok), nl - 1 + hi_ok);
+        const float w = s_u[t + radius];
+        v = (d >= -radius && d <= radius) ? fmaxf(v, w) : v;
+      }
+      vv[e] = v;
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (e * kTkThreads + tid < nl) emit_key(e * kTkThreads + tid, vv[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int jl = e * kTkThreads + tid;
+      if (jl >= nl) break;
+      float v = s_u[jl + radius];
+      const int a = max(jl - radius, -lo_ok), b = min(jl + radius, nl - 1 + hi_ok);
+      for (int t = a; t <= b; ++t) v = fmaxf(v, s_u[t + radius]);
+      emit_key(jl, v);
+    }
   }
   __syncthreads();
   int32_t* gh = hist + bi * 3 * kTkBins;
