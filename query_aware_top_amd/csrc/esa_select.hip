@@ -497,46 +497,87 @@ __global__ __launch_bounds__(kTkThreads) void esa_topk_prep_kernel(
     inv_l = 1.f / l;
   }
   for (int i = tid; i < kTkBins; i += kTkThreads) s_h[i] = 0;
-  // u over [j0 - r, j0 + slice + r) clipped to M, PER values per thread and
-  // round with all their loads in flight (clamped indices, results masked)
-  const int64_t lo = max((int64_t)0, j0 - radius);
-  const int64_t hi = min(n_mid, j0 + (kTkThreads * PER) + radius);
-  for (int64_t jb = lo; jb < hi; jb += (int64_t)kTkThreads * PER) {
-    float uv[PER];
-    if (mode == 0) {   // the query-split partial sums, added in float64 in split order
-      double acc[PER];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = 0.0;
-      for (int sp = 0; sp < nqsplit; ++sp) {
-        float t[PER];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) t[e] = upart[(bi * nqsplit + sp) * n_mid + min(jb + e * kTkThreads + tid, hi - 1)];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += (double)t[e];
-      }
-#pragma unroll
-      for (int e = 0; e < PER; ++e) uv[e] = (float)acc[e];
-    } else {
-      float t[PER];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) t[e] = s_in[bi * n_mid + min(jb + e * kTkThreads + tid, hi - 1)];
-#pragma unroll
-      for (int e = 0; e < PER; ++e)
-        uv[e] = mode == 2 ? __builtin_amdgcn_exp2f(tau2 * (t[e] - mx)) * inv_l : fmaxf(t[e] - mx, -clip);
-    }
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int64_t j = jb + e * kTkThreads + tid;
-      if (j < hi) s_u[j - j0 + radius] = uv[e];
-    }
-  }
-  __syncthreads();
-  // neighbour max in slice-local 32-bit indices: element jl of the slice sits
-  // at s_u[jl + radius]; the window [jl - r, jl + r] is clipped to the middle
-  // part, whose halo holds lo_ok elements before the slice and hi_ok after
+  // element jl of the slice (jl in [-lo_ok, nl + hi_ok): the slice and its
+  // halo of up to r elements on each side, clipped to M) goes to
+  // s_u[jl + radius]
   const int nl = (int)min((int64_t)(kTkThreads * PER), n_mid - j0);
   const int lo_ok = (int)min((int64_t)radius, j0);
   const int hi_ok = (int)min((int64_t)radius, n_mid - j0 - nl);
+  const int nh = lo_ok + hi_ok;
+  if (nh <= kTkThreads) {
+    // one round: PER slice elements per thread plus, for the first nh
+    // threads, one halo element, all loads in flight together (clamped
+    // positions, results masked)
+    const int hh = min(tid, max(nh - 1, 0));
+    const int hl = hh < lo_ok ? hh - lo_ok : nl + (hh - lo_ok);   // slice-local index of the halo element
+    int64_t jg[PER + 1];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) jg[e] = j0 + min(e * kTkThreads + tid, nl - 1);
+    jg[PER] = j0 + min(max(hl, -lo_ok), nl - 1 + hi_ok);
+    float uv[PER + 1];
+    if (mode == 0) {   // the query-split partial sums, added in float64 in split order
+      double acc[PER + 1];
+#pragma unroll
+      for (int e = 0; e <= PER; ++e) acc[e] = 0.0;
+      for (int sp = 0; sp < nqsplit; ++sp) {
+        float t[PER + 1];
+#pragma unroll
+        for (int e = 0; e <= PER; ++e) t[e] = upart[(bi * nqsplit + sp) * n_mid + jg[e]];
+#pragma unroll
+        for (int e = 0; e <= PER; ++e) acc[e] += (double)t[e];
+      }
+#pragma unroll
+      for (int e = 0; e <= PER; ++e) uv[e] = (float)acc[e];
+    } else {
+      float t[PER + 1];
+#pragma unroll
+      for (int e = 0; e <= PER; ++e) t[e] = s_in[bi * n_mid + jg[e]];
+#pragma unroll
+      for (int e = 0; e <= PER; ++e)
+        uv[e] = mode == 2 ? __builtin_amdgcn_exp2f(tau2 * (t[e] - mx)) * inv_l : fmaxf(t[e] - mx, -clip);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (e * kTkThreads + tid < nl) s_u[e * kTkThreads + tid + radius] = uv[e];
+    if (tid < nh) s_u[hl + radius] = uv[PER];
+  } else {
+    // u over [j0 - r, j0 + slice + r) clipped to M, PER values per thread and
+    // round with all their loads in flight (clamped indices, results masked)
+    const int64_t lo = max((int64_t)0, j0 - radius);
+    const int64_t hi = min(n_mid, j0 + (kTkThreads * PER) + radius);
+    for (int64_t jb = lo; jb < hi; jb += (int64_t)kTkThreads * PER) {
+      float uv[PER];
+      if (mode == 0) {   // the query-split partial sums, added in float64 in split order
+        double acc[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = 0.0;
+        for (int sp = 0; sp < nqsplit; ++sp) {
+          float t[PER];
+#pragma unroll
+          for (int e = 0; e < PER; ++e) t[e] = upart[(bi * nqsplit + sp) * n_mid + min(jb + e * kTkThreads + tid, hi - 1)];
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[e] += (double)t[e];
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) uv[e] = (float)acc[e];
+      } else {
+        float t[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) t[e] = s_in[bi * n_mid + min(jb + e * kTkThreads + tid, hi - 1)];
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          uv[e] = mode == 2 ? __builtin_amdgcn_exp2f(tau2 * (t[e] - mx)) * inv_l : fmaxf(t[e] - mx, -clip);
+      }
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int64_t j = jb + e * kTkThreads + tid;
+        if (j < hi) s_u[j - j0 + radius] = uv[e];
+      }
+    }
+  }
+  __syncthreads();
+  // neighbour max in slice-local 32-bit indices: the window [jl - r, jl + r]
+  // of element jl, clipped to the middle part
   auto emit_key = [&](int jl, float v) {
     const int64_t j = j0 + jl;
     const uint32_t key = float_key(v);
