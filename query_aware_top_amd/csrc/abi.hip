@@ -169,6 +169,7 @@ struct MobaLayout {
   int32_t* run_off = nullptr; // gradient pass: runs of dispatch tiles per bucket
   int32_t* wg_counts = nullptr;   // gradient pass: stable dispatch, per-workgroup bucket counts
   int32_t* wg_base = nullptr;     // gradient pass: stable dispatch, per-workgroup bucket offsets
+  int32_t* wg_loc = nullptr;      // forward: per-workgroup bucket counts of the atomic placement
   float* kv_part = nullptr;   // gradient pass: dK, dV sums per (run, key chunk)
   size_t bytes = 0;
 };
@@ -230,6 +231,10 @@ MobaLayout moba_layout(const qat_moba_params* p, void* ws, bool bwd = false) {
     L.dec_plse = c.take<float>((size_t)L.nrows * L.dec_pieces);
   }
   L.delta = c.take<float>((size_t)L.nrows);
+  if (!bwd) {
+    const int64_t wi = qat::moba_dispatch_wg_ints(L.nrows, L.nbuckets);
+    L.wg_loc = wi > 0 ? c.take<int32_t>((size_t)wi) : nullptr;
+  }
   if (bwd) {
     L.dq_part = c.take<float>((size_t)qat::moba_bwd_part_floats(L.nrows, p->topk, p->head_dim) + 1);
     L.run_off = c.take<int32_t>((size_t)L.nbuckets + 1);
@@ -611,7 +616,7 @@ int moba_attn_rows(const qat_moba_params* p, const void* q, int64_t q_seq, int64
       qat::KTimer tm("moba_dispatch", s);
       e = qat::launch_moba_dispatch(blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim,
                                     p->q_start, p->q_len, p->block, p->topk, L.nbc, L.counts, L.offsets, L.cursor,
-                                    L.entries, L.tiles, L.ntiles, s);
+                                    L.entries, L.tiles, L.ntiles, s, nullptr, nullptr, L.wg_loc);
       if (e != hipSuccess) return hip_status(e, who);
     }
     e = qat::launch_moba_attn_mfma(q, k, v, blk, L.tiles, L.ntiles, L.entries, L.part_o, L.part_lse, out, lse,

@@ -101,9 +101,12 @@ __device__ __forceinline__ void moba_for_each_pair(const int32_t* __restrict__ b
   }
 }
 
+// With the counts in LDS, each workgroup also records its own per-bucket
+// counts (wg_loc, may be NULL), which the scatter then reads instead of
+// counting its rows again.
 __global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restrict__ blk, int32_t nrows,
                                                          MobaRowMap m, int topk, int32_t nbuckets,
-                                                         int32_t* __restrict__ counts) {
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ wg_loc) {
   __shared__ int32_t loc[kDispatchLdsBuckets];
   const bool use_lds = nbuckets <= kDispatchLdsBuckets;
   if (use_lds) {
@@ -118,8 +121,10 @@ __global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restri
   });
   if (use_lds) {
     __syncthreads();
-    for (int i = threadIdx.x; i < nbuckets; i += blockDim.x)
+    for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) {
       if (loc[i]) atomicAdd(&counts[i], loc[i]);
+      if (wg_loc) wg_loc[(int64_t)blockIdx.x * nbuckets + i] = loc[i];
+    }
   }
 }
 
@@ -380,17 +385,22 @@ __global__ __launch_bounds__(256) void moba_tiles_kernel(const int32_t* __restri
 __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __restrict__ blk, int32_t nrows,
                                                            MobaRowMap m, int topk, int32_t nbuckets,
                                                            int32_t* __restrict__ cursor,
-                                                           int2* __restrict__ entries) {
+                                                           int2* __restrict__ entries,
+                                                           const int32_t* __restrict__ wg_loc) {
   __shared__ int32_t loc[kDispatchLdsBuckets];
   __shared__ int32_t base_of[kDispatchLdsBuckets];
   const bool use_lds = nbuckets <= kDispatchLdsBuckets;
   const int32_t r0 = blockIdx.x * (256 * kDispatchRowsPerThread);
   const int32_t r1 = min(nrows, r0 + 256 * kDispatchRowsPerThread);
   if (use_lds) {
-    for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = 0;
-    __syncthreads();
-    moba_for_each_pair(blk, r0, r1, m, topk,
-                       [&](int32_t, int, const MobaRow& mr, int32_t b) { atomicAdd(&loc[mr.bucket0 + b], 1); });
+    if (wg_loc) {   // this workgroup's counts, recorded by the count pass
+      for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = wg_loc[(int64_t)blockIdx.x * nbuckets + i];
+    } else {
+      for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = 0;
+      __syncthreads();
+      moba_for_each_pair(blk, r0, r1, m, topk,
+                         [&](int32_t, int, const MobaRow& mr, int32_t b) { atomicAdd(&loc[mr.bucket0 + b], 1); });
+    }
     __syncthreads();
     for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) {
       base_of[i] = loc[i] ? atomicAdd(&cursor[i], loc[i]) : 0;
@@ -868,6 +878,11 @@ int64_t moba_max_tiles(int64_t nrows, int topk, int64_t nbuckets) {
   return cdiv(nrows * (topk - 1), kRowsPerTile) + nbuckets;
 }
 
+int64_t moba_dispatch_wg_ints(int64_t nrows, int64_t nbuckets) {
+  if (nbuckets > kDispatchLdsBuckets) return 0;
+  return cdiv(nrows, 256 * kDispatchRowsPerThread) * nbuckets;
+}
+
 int64_t moba_dispatch_stable_ints(int64_t nrows, int64_t nbuckets, int topk) {
   // bucket ids and sequence numbers share a 32-bit sort key
   if (nbuckets > kDispatchLdsBuckets || topk < 2 || topk - 1 > 16) return 0;
@@ -877,7 +892,8 @@ int64_t moba_dispatch_stable_ints(int64_t nrows, int64_t nbuckets, int topk) {
 hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_len, int64_t hq, int64_t hkv,
                                 int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int64_t nbc,
                                 int32_t* counts, int32_t* offsets, int32_t* cursor, int2* entries, int4* tiles,
-                                int32_t* ntiles, hipStream_t s, int32_t* wg_counts, int32_t* wg_base) {
+                                int32_t* ntiles, hipStream_t s, int32_t* wg_counts, int32_t* wg_base,
+                                int32_t* wg_loc) {
   const int64_t nrows = batch * q_len * hq;
   const int64_t nbuckets = batch * hkv * nbc;
   const bool stable = wg_counts && wg_base && moba_dispatch_stable_ints(nrows, nbuckets, topk) > 0;
@@ -894,7 +910,7 @@ hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_l
                          (int32_t)nbuckets, srows, counts, wg_counts);
     else
       hipLaunchKernelGGL(moba_count_kernel, dim3(grid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
-                         (int32_t)nbuckets, counts);
+                         (int32_t)nbuckets, counts, nbuckets <= kDispatchLdsBuckets ? wg_loc : nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(moba_scan_kernel, dim3(1), dim3(1024), 0, s, counts, (int32_t)nbuckets, offsets, cursor,
@@ -927,7 +943,8 @@ hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_l
 #undef QAT_STS
     } else
       hipLaunchKernelGGL(moba_scatter_kernel, dim3(grid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
-                         (int32_t)nbuckets, cursor, entries);
+                         (int32_t)nbuckets, cursor, entries,
+                         (const int32_t*)(nbuckets <= kDispatchLdsBuckets ? wg_loc : nullptr));
     e = hipGetLastError();
   }
   return e;
