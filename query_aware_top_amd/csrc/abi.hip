@@ -507,7 +507,7 @@ QAT_EXPORT int esa_sparse_attn(const qat_esa_params* p, const void* q, const voi
   const bool bf = p->dtype == QAT_BF16;
   hipError_t e;
   const bool ph = p->per_head != 0;
-  if (bf && p->chunk_len == 1 && qat::esa_decode_supported(p->n_heads, p->head_dim)) {
+  if (bf && p->chunk_len == 1 && qat::esa_decode_supported(p->n_heads, p->head_dim, ph)) {
     qat::KTimer tm("esa_decode_attn", s);
     e = qat::launch_esa_decode_attn(q, k_cache, v_cache, sel, n_sel, L.po, L.pm, L.pl, out, lse, p->batch,
                                     p->n_heads, p->head_dim, p->ctx_len, p->chunk_start, p->n_init, p->window,

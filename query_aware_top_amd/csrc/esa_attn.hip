@@ -167,26 +167,43 @@ int esa_decode_keys_per_split(int64_t batch, int64_t nkeys_max) {
   return 64;
 }
 constexpr int kDecUnroll = 4;
+constexpr int kDecMaxKps = 256;
 
-template <int E>
+// The split's key positions are staged in LDS first ([lists][kps], one list,
+// or one per head under per-head selection), so the gathers of a batch issue
+// back to back instead of each waiting on its own position load; the batches
+// alternate between two register sets, the next one in flight while the
+// current one is consumed.
+template <int E, int D>
 __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, float* __restrict__ po,
-    float* __restrict__ pm, float* __restrict__ pl, int64_t H, int64_t D, int64_t ctx_len, int64_t c0,
+    float* __restrict__ pm, float* __restrict__ pl, int64_t H, int64_t ctx_len, int64_t c0,
     int64_t n_init, int64_t window, int topk, int nsplit, int kps, float scale_log2, int ph) {
+  constexpr int kLph = D / E;   // lanes per head
+  extern __shared__ int32_t lpos[];
   const int64_t bi = blockIdx.y;
   const int split = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t HD = H * D;
-  const int lph = (int)(D / E);          // lanes per head
   const int64_t e0 = (int64_t)tid * E;   // element offset in the row
-  const int64_t head = e0 / D;
-  // per-head selection: each head's lanes walk that head's list (all lists
-  // have the same length, min(topk, |M|) selected)
+  const int head = tid / kLph;
+  const int64_t j0 = (int64_t)split * kps;
+  {
+    // per-head selection: each head's lanes walk that head's list (all lists
+    // have the same length, min(topk, |M|) selected)
+    const int nl = ph ? (int)H : 1;
+    for (int i = tid; i < nl * kps; i += 256) {
+      const int hh = i / kps;
+      const int64_t j = j0 + (i - hh * kps);
+      const EsaKeys kh = esa_keys(sel, n_sel, ph ? bi * H + hh : bi, topk, c0, n_init, window);
+      lpos[i] = (int32_t)(j < kh.count() ? kh.pos(j) : c0);   // the last key is the query's own position
+    }
+  }
   const EsaKeys kl = esa_keys(sel, n_sel, ph ? bi * H + head : bi, topk, c0, n_init, window);
   const int64_t nkeys = kl.count() + 1;   // + the query's own position c0
-  const int64_t j0 = (int64_t)split * kps;
-  const int64_t j1 = min(nkeys, j0 + kps);
+  const int nk = (int)max<int64_t>(0, min<int64_t>(kps, nkeys - j0));
+  const int32_t* mypos = lpos + (ph ? head : 0) * kps;
   float qv[E], o[E];
   {
     const bf16* qr = q + bi * HD + e0;
@@ -202,14 +219,16 @@ __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
   float m = -__builtin_inff(), l = 0.f;
   const bf16* kb = kc + bi * ctx_len * HD + e0;
   const bf16* vb = vc + bi * ctx_len * HD + e0;
-  // kDecUnroll key rows per batch; the next batch's loads are issued before
-  // the current batch is consumed (registers double-buffered)
-  bf16x8 kr[kDecUnroll][E / 8], vr[kDecUnroll][E / 8];
-  auto load_batch = [&](int64_t jb, bf16x8 (&kk)[kDecUnroll][E / 8], bf16x8 (&vv)[kDecUnroll][E / 8]) {
+  __syncthreads();
+  using Batch = bf16x8[kDecUnroll][E / 8];
+  Batch ka, va, kn, vn;
+  // keys past the split's end read the query's own row (always valid) and
+  // are masked in the update
+  auto load_batch = [&](int jb, Batch& kk, Batch& vv) {
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
-      const int64_t j = jb + u;
-      const int64_t p = j < j1 ? (j < nkeys - 1 ? kl.pos(j) : c0) : c0;
+      const int jj = min(jb + u, kps - 1);
+      const int64_t p = jb + u < nk ? mypos[jj] : c0;
 #pragma unroll
       for (int e = 0; e < E / 8; ++e) {
         kk[u][e] = *(const bf16x8*)(kb + p * HD + 8 * e);
@@ -217,20 +236,17 @@ __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
       }
     }
   };
-  if (j0 < j1) load_batch(j0, kr, vr);
-  for (int64_t jb = j0; jb < j1; jb += kDecUnroll) {
-    bf16x8 kn[kDecUnroll][E / 8], vn[kDecUnroll][E / 8];
-    if (jb + kDecUnroll < j1) load_batch(jb + kDecUnroll, kn, vn);
+  auto consume = [&](int jb, const Batch& kk, const Batch& vv) {
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
-      const bool ok = jb + u < j1;
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < E / 8; ++e)
 #pragma unroll
-        for (int x = 0; x < 8; ++x) s = fmaf(qv[8 * e + x], (float)kr[u][e][x], s);
-      for (int off = 1; off < lph; off <<= 1) s += __shfl_xor(s, off, 64);
-      const float x = ok ? s * scale_log2 : -__builtin_inff();
+        for (int x = 0; x < 8; ++x) s = fmaf(qv[8 * e + x], (float)kk[u][e][x], s);
+#pragma unroll
+      for (int off = 1; off < kLph; off <<= 1) s += __shfl_xor(s, off, 64);
+      const float x = jb + u < nk ? s * scale_log2 : -__builtin_inff();
       const float m_new = fmaxf(m, x);
       const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
       const float alpha = exp2f(m - m_use);
@@ -239,16 +255,17 @@ __global__ __launch_bounds__(256) void esa_decode_attn_kernel(
 #pragma unroll
       for (int e = 0; e < E / 8; ++e)
 #pragma unroll
-        for (int xx = 0; xx < 8; ++xx) o[8 * e + xx] = o[8 * e + xx] * alpha + p * (float)vr[u][e][xx];
+        for (int xx = 0; xx < 8; ++xx) o[8 * e + xx] = o[8 * e + xx] * alpha + p * (float)vv[u][e][xx];
       m = m_new;
     }
-#pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u)
-#pragma unroll
-      for (int e = 0; e < E / 8; ++e) {
-        kr[u][e] = kn[u][e];
-        vr[u][e] = vn[u][e];
-      }
+  };
+  if (nk > 0) load_batch(0, ka, va);
+  for (int jb = 0; jb < nk; jb += 2 * kDecUnroll) {
+    if (jb + kDecUnroll < nk) load_batch(jb + kDecUnroll, kn, vn);
+    consume(jb, ka, va);
+    if (jb + kDecUnroll >= nk) break;
+    if (jb + 2 * kDecUnroll < nk) load_batch(jb + 2 * kDecUnroll, ka, va);
+    consume(jb + kDecUnroll, kn, vn);
   }
   const int64_t pidx = (bi * nsplit + split) * H + head;
   float* dst = po + pidx * D + (e0 % D);
@@ -354,11 +371,14 @@ hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, 
   return hipGetLastError();
 }
 
-bool esa_decode_supported(int64_t H, int64_t D) {
+bool esa_decode_supported(int64_t H, int64_t D, bool per_head) {
   const int64_t HD = H * D;
-  if (HD % 256) return false;
+  if (HD % 256 || (D != 64 && D != 128)) return false;
   const int64_t E = HD / 256;
-  return (E == 8 || E == 16 || E == 32) && D % E == 0 && (D / E) <= 64;
+  // the staged positions, one list per head under per-head selection, fit in
+  // 64 KiB of LDS
+  if ((per_head ? H : 1) * kDecMaxKps * 4 > 65536) return false;
+  return (E == 8 || E == 16 || E == 32) && D % E == 0;
 }
 
 hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, const int32_t* sel,
@@ -370,13 +390,20 @@ hipError_t launch_esa_decode_attn(const void* q, const void* k, const void* v, c
   dim3 grid((unsigned)nsplit, (unsigned)batch);
   const float sl2 = scale * kLog2e;
   const int64_t E = H * D / 256;
-#define QAT_DEC(E_)                                                                                        \
-  launch_timed("esa_decode_attn", esa_decode_attn_kernel<E_>, grid, dim3(256), 0, s, (const bf16*)q,       \
-               (const bf16*)k, (const bf16*)v, sel, n_sel, po, pm, pl, H, D, ctx_len, c0, n_init, window, topk, \
+  const uint32_t lds = (uint32_t)((per_head ? H : 1) * kps * sizeof(int32_t));
+#define QAT_DEC(E_, D_)                                                                                     \
+  launch_timed("esa_decode_attn", esa_decode_attn_kernel<E_, D_>, grid, dim3(256), lds, s, (const bf16*)q,  \
+               (const bf16*)k, (const bf16*)v, sel, n_sel, po, pm, pl, H, ctx_len, c0, n_init, window, topk,   \
                nsplit, kps, sl2, per_head ? 1 : 0)
-  if (E == 8) QAT_DEC(8);
-  else if (E == 16) QAT_DEC(16);
-  else QAT_DEC(32);
+  if (D == 64) {
+    if (E == 8) QAT_DEC(8, 64);
+    else if (E == 16) QAT_DEC(16, 64);
+    else QAT_DEC(32, 64);
+  } else {
+    if (E == 8) QAT_DEC(8, 128);
+    else if (E == 16) QAT_DEC(16, 128);
+    else QAT_DEC(32, 128);
+  }
 #undef QAT_DEC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -148,7 +148,7 @@ hipError_t launch_esa_topk(int mode, const float* upart, int nqsplit, const floa
 
 // ---- ESA attention (esa_attn.hip) -----------------------------------------
 int esa_decode_splits(int64_t batch, int64_t n_init, int64_t topk, int64_t window);
-bool esa_decode_supported(int64_t H, int64_t D);
+bool esa_decode_supported(int64_t H, int64_t D, bool per_head);
 int64_t esa_keylist_len(int64_t n_init, int64_t topk, int64_t window, int64_t m);
 hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, const int32_t* sel,
                                    const int32_t* n_sel, int32_t* keylist, void* out, float* lse, int64_t batch,
