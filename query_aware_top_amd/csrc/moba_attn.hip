@@ -969,7 +969,11 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
     return ok;
   }();
   if (!lds_ok) return hipErrorInvalidConfiguration;
-  if (topk > 1 && max_tiles > 0 && nbc > 0) {
+  // past partials exist only if the past-block pass runs (no complete block
+  // before the rows: none is written, and the current-block pass must fold
+  // none)
+  const bool past = topk > 1 && max_tiles > 0 && nbc > 0;
+  if (past) {
     {
       KTimer tm("moba_past_attn", s);
       // partial lse of slots that get no partial stay -inf (read by the
@@ -1002,7 +1006,7 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
     KTimer tm("moba_current_attn", s);
     launch_timed("moba_current_attn", moba_current_kernel<D>, dim3((unsigned)nwg), dim3(64 * kCurNW), 0, s, q, k,
                  v, blk, (const bf16*)part_o, (const float*)part_lse, out, lse, seq_len, hq, hkv, q_start, q_len,
-                 block, topk, sl2, pack, tiles_per_block, nblocks);
+                 block, past ? topk : 1, sl2, pack, tiles_per_block, nblocks);
   }
   return hipGetLastError();
 }

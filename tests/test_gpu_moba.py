@@ -67,6 +67,8 @@ SMALL = [
     (1, 160, 2, 2, 64, 1, 5, 0, None, 0, torch.bfloat16),        # block 1: token-level gating
     (1, 700, 4, 2, 128, 64, 3, 0, None, 0, torch.float32),       # fp32, d 128
     (1, 520, 2, 2, 64, 100, 16, 0, None, 0, torch.bfloat16),     # topk 16 > blocks, block not /64
+    (1, 300, 4, 2, 128, 512, 3, 0, None, 0, torch.bfloat16),     # N below one block: no past block exists
+    (2, 200, 2, 2, 64, 256, 4, 50, 150, 0, torch.bfloat16),      # the same with batch 2 and offset rows
 ]
 
 

@@ -27,9 +27,10 @@ def _same(a, b, what):
 
 @pytest.mark.parametrize("case", [
     # n, hq, hkv, d, block, topk: the smoke shape (all rows of the first block
-    # without past partials), a ragged N, k = 4, d = 64, MHA
+    # without past partials), a ragged N, k = 4, d = 64, MHA, N below one
+    # block (no past block exists, so no past-block pass runs)
     (1024, 4, 2, 128, 128, 3), (1000, 4, 2, 128, 128, 3), (1024, 4, 2, 128, 128, 4),
-    (1024, 4, 2, 64, 128, 3), (2048, 4, 4, 128, 256, 3)])
+    (1024, 4, 2, 64, 128, 3), (2048, 4, 4, 128, 256, 3), (300, 4, 2, 128, 512, 3)])
 def test_moba_prefill_ignores_stale_workspace(case):
     n, hq, hkv, d, block, topk = case
     print(f"[poison moba] {case}", flush=True)
