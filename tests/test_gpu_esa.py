@@ -165,6 +165,29 @@ def test_esa_decode_small(H, d):
     esa_case(8, 3, T, T - 1, 1, H, d, 64, 32, 256, 300, 2, 24.0, needles=4)
 
 
+EDGES = [
+    # seed, B, T, c0, m, H, d, d_c, n_init, W, topk, radius, clip
+    (40, 2, 300, 299, 1, 16, 128, 64, 32, 300, 16, 1, 24.0),     # decode, window reaches the initial part: M empty
+    (41, 2, 100, 99, 1, 16, 128, 64, 128, 64, 16, 1, 24.0),      # decode inside the initial part: no window either
+    (42, 2, 900, 899, 1, 16, 128, 64, 16, 64, 2000, 2, 8.0),     # decode, k >= |M|: every middle token selected
+    (43, 5, 5000, 4999, 1, 32, 64, 128, 100, 1000, 700, 3, 16.0),  # decode, d 64 with 32 heads, radius 3
+    (44, 3, 3000, 2999, 1, 16, 128, 64, 32, 0, 300, 2, 24.0),    # decode, no local window
+    (45, 3, 3000, 2999, 1, 16, 128, 64, 0, 256, 300, 2, 24.0),   # decode, no initial tokens
+    (46, 2, 2000, 1999, 1, 64, 128, 64, 16, 128, 200, 1, 24.0),  # decode, 64 heads (32 elements per thread)
+    (47, 1, 1500, 1000, 200, 2, 64, 64, 0, 0, 100, 1, 6.0),      # chunk, no initial tokens and no window
+    (48, 1, 300, 0, 300, 2, 64, 64, 16, 32, 10, 1, 4.0),         # chunk at position 0: only causal chunk keys
+]
+
+
+@pytest.mark.parametrize("case", EDGES, ids=[f"e{i}" for i in range(len(EDGES))])
+def test_esa_edge_cases(case):
+    """Boundaries of the four-part split: an empty middle part, a query
+    inside the initial part, no window, no initial tokens, everything
+    selected, the widest decode rows, a chunk at the start of the sequence."""
+    print(f"[esa edge] {case}", flush=True)
+    esa_case(*case)
+
+
 def test_esa_prefill_64k_full_size():
     """ESA token-level chunked prefill, bf16: 32 heads x 128, q/k compressed
     4096 -> 128 by a seeded random one-layer map, context 65536, final query

@@ -69,6 +69,10 @@ SMALL = [
     (1, 520, 2, 2, 64, 100, 16, 0, None, 0, torch.bfloat16),     # topk 16 > blocks, block not /64
     (1, 300, 4, 2, 128, 512, 3, 0, None, 0, torch.bfloat16),     # N below one block: no past block exists
     (2, 200, 2, 2, 64, 256, 4, 50, 150, 0, torch.bfloat16),      # the same with batch 2 and offset rows
+    (1, 700, 6, 2, 128, 128, 3, 0, None, 0, torch.bfloat16),     # 3 query heads per KV head (no head packing)
+    (1, 600, 8, 1, 64, 64, 3, 0, None, 0, torch.bfloat16),       # 8 query heads per KV head
+    (1, 1000, 4, 2, 128, 128, 3, 991, 9, 0, torch.bfloat16),     # 9 final rows: just past the decode kernels
+    (1, 4500, 2, 1, 128, 2048, 2, 0, None, 0, torch.bfloat16),   # block 2048, one past block per row
 ]
 
 
