@@ -49,6 +49,8 @@ SMALL = [
     (73, 1, 300, 20, 100, 2, 64, 64, 32, 16, 10, 2, 4.0),          # chunk inside the initial part: M empty
     (74, 3, 3000, 2999, 1, 4, 128, 64, 32, 256, 300, 2, 24.0),     # decode: one query per sequence
     (75, 1, 600, 400, 130, 2, 64, 128, 16, 32, 1000, 2, 5.0),      # k >= |M|: dense causal
+    (76, 1, 300, 0, 300, 2, 64, 64, 16, 32, 10, 1, 4.0),           # chunk at position 0: causal chunk keys only
+    (77, 1, 1500, 1000, 200, 2, 64, 64, 0, 0, 100, 1, 6.0),        # no initial tokens, no window
 ]
 
 

@@ -50,6 +50,8 @@ SMALL = [
     (1, 520, 2, 2, 64, 100, 16, 0, None, torch.bfloat16),      # block not a multiple of 64, k = 16
     (1, 300, 2, 1, 64, 1, 5, 0, None, torch.bfloat16),         # block 1: token-level gating
     (1, 3000, 8, 2, 128, 256, 3, 2990, 10, torch.bfloat16),    # a few rows at the end (decode-like)
+    (1, 300, 4, 2, 128, 512, 3, 0, None, torch.bfloat16),      # N below one block: no past block exists
+    (1, 700, 6, 2, 128, 128, 3, 0, None, torch.bfloat16),      # 3 query heads per KV head
 ]
 
 
