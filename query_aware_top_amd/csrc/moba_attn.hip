@@ -101,9 +101,10 @@ __device__ __forceinline__ void moba_for_each_pair(const int32_t* __restrict__ b
   }
 }
 
-// With the counts in LDS, each workgroup also records its own per-bucket
-// counts (wg_loc, may be NULL), which the scatter then reads instead of
-// counting its rows again.
+// With the counts in LDS, each workgroup also records where its entries
+// start inside each bucket (wg_loc, may be NULL): the value its one atomic
+// add to the bucket's total returns. The scatter then places its entries
+// from there without counting its rows again or taking atomics of its own.
 __global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restrict__ blk, int32_t nrows,
                                                          MobaRowMap m, int topk, int32_t nbuckets,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ wg_loc) {
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(256) void moba_count_kernel(const int32_t* __restri
   if (use_lds) {
     __syncthreads();
     for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) {
-      if (loc[i]) atomicAdd(&counts[i], loc[i]);
-      if (wg_loc) wg_loc[(int64_t)blockIdx.x * nbuckets + i] = loc[i];
+      const int32_t before = loc[i] ? atomicAdd(&counts[i], loc[i]) : 0;
+      if (wg_loc) wg_loc[(int64_t)blockIdx.x * nbuckets + i] = before;
     }
   }
 }
@@ -384,6 +385,7 @@ __global__ __launch_bounds__(256) void moba_tiles_kernel(const int32_t* __restri
 // independent of the other rows sharing its tile).
 __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __restrict__ blk, int32_t nrows,
                                                            MobaRowMap m, int topk, int32_t nbuckets,
+                                                           const int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ cursor,
                                                            int2* __restrict__ entries,
                                                            const int32_t* __restrict__ wg_loc) {
@@ -393,18 +395,21 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __rest
   const int32_t r0 = blockIdx.x * (256 * kDispatchRowsPerThread);
   const int32_t r1 = min(nrows, r0 + 256 * kDispatchRowsPerThread);
   if (use_lds) {
-    if (wg_loc) {   // this workgroup's counts, recorded by the count pass
-      for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = wg_loc[(int64_t)blockIdx.x * nbuckets + i];
+    if (wg_loc) {   // this workgroup's start in each bucket, taken by the count pass
+      for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) {
+        base_of[i] = offsets[i] + wg_loc[(int64_t)blockIdx.x * nbuckets + i];
+        loc[i] = 0;
+      }
     } else {
       for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) loc[i] = 0;
       __syncthreads();
       moba_for_each_pair(blk, r0, r1, m, topk,
                          [&](int32_t, int, const MobaRow& mr, int32_t b) { atomicAdd(&loc[mr.bucket0 + b], 1); });
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) {
-      base_of[i] = loc[i] ? atomicAdd(&cursor[i], loc[i]) : 0;
-      loc[i] = 0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < nbuckets; i += blockDim.x) {
+        base_of[i] = loc[i] ? atomicAdd(&cursor[i], loc[i]) : 0;
+        loc[i] = 0;
+      }
     }
     __syncthreads();
   }
@@ -943,7 +948,7 @@ hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_l
 #undef QAT_STS
     } else
       hipLaunchKernelGGL(moba_scatter_kernel, dim3(grid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
-                         (int32_t)nbuckets, cursor, entries,
+                         (int32_t)nbuckets, (const int32_t*)offsets, cursor, entries,
                          (const int32_t*)(nbuckets <= kDispatchLdsBuckets ? wg_loc : nullptr));
     e = hipGetLastError();
   }
