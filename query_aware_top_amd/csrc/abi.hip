@@ -616,7 +616,7 @@ int moba_attn_rows(const qat_moba_params* p, const void* q, int64_t q_seq, int64
       qat::KTimer tm("moba_dispatch", s);
       e = qat::launch_moba_dispatch(blk, p->batch, p->seq_len, p->n_q_heads, p->n_kv_heads, p->head_dim,
                                     p->q_start, p->q_len, p->block, p->topk, L.nbc, L.counts, L.offsets, L.cursor,
-                                    L.entries, L.tiles, L.ntiles, s, nullptr, nullptr, L.wg_loc);
+                                    L.entries, L.tiles, L.ntiles, s, nullptr, nullptr, L.wg_loc, L.part_lse);
       if (e != hipSuccess) return hip_status(e, who);
     }
     e = qat::launch_moba_attn_mfma(q, k, v, blk, L.tiles, L.ntiles, L.entries, L.part_o, L.part_lse, out, lse,

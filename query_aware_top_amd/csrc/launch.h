@@ -56,7 +56,8 @@ hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_l
                                 int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int64_t nbc,
                                 int32_t* counts, int32_t* offsets, int32_t* cursor, int2* entries, int4* tiles,
                                 int32_t* ntiles, hipStream_t s, int32_t* wg_counts = nullptr,
-                                int32_t* wg_base = nullptr, int32_t* wg_loc = nullptr);
+                                int32_t* wg_base = nullptr, int32_t* wg_loc = nullptr,
+                                float* part_lse = nullptr);
 // int32 elements of the per-workgroup bucket counts that the atomic placement
 // records in its count pass (wg_loc), 0 when the buckets do not fit in LDS
 int64_t moba_dispatch_wg_ints(int64_t nrows, int64_t nbuckets);

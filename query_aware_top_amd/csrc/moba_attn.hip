@@ -64,13 +64,18 @@ __device__ __forceinline__ MobaRow moba_row(const MobaRowMap& m, uint32_t row) {
   return o;
 }
 
+struct MobaNoSkip {
+  __device__ void operator()(int32_t, int) const {}
+};
+
 // Calls f(row, slot, row descriptor, block) for every dispatched (row, slot)
-// pair among this thread's rows. The gated lists of four rows (their first
-// four slots) are loaded together, from clamped in-bounds indices, before
-// any of them is used, so that the loads overlap.
-template <typename F>
+// pair among this thread's rows, and skip(row, slot) for every other slot
+// of those rows. The gated lists of four rows (their first four slots) are
+// loaded together, from clamped in-bounds indices, before any of them is
+// used, so that the loads overlap.
+template <typename F, typename S = MobaNoSkip>
 __device__ __forceinline__ void moba_for_each_pair(const int32_t* __restrict__ blk, int32_t r0, int32_t r1,
-                                                   const MobaRowMap& m, int topk, F f) {
+                                                   const MobaRowMap& m, int topk, F f, S skip = S{}) {
   constexpr int RB = 4, SB = 4;
   const int km = topk - 1;   // >= 1
 #pragma unroll 1
@@ -91,11 +96,15 @@ __device__ __forceinline__ void moba_for_each_pair(const int32_t* __restrict__ b
 #pragma unroll
       for (int s = 0; s < SB; ++s) {
         const int32_t b = bv[i][s];
-        if (s < km && b >= 0 && b < mr.cur) f(rows[i], s, mr, b);
+        if (s < km) {
+          if (b >= 0 && b < mr.cur) f(rows[i], s, mr, b);
+          else skip(rows[i], s);
+        }
       }
       for (int s = SB; s < km; ++s) {
         const int32_t b = blk[rows[i] * topk + s];
         if (b >= 0 && b < mr.cur) f(rows[i], s, mr, b);
+        else skip(rows[i], s);
       }
     }
   }
@@ -388,7 +397,8 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __rest
                                                            const int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ cursor,
                                                            int2* __restrict__ entries,
-                                                           const int32_t* __restrict__ wg_loc) {
+                                                           const int32_t* __restrict__ wg_loc,
+                                                           float* __restrict__ part_lse) {
   __shared__ int32_t loc[kDispatchLdsBuckets];
   __shared__ int32_t base_of[kDispatchLdsBuckets];
   const bool use_lds = nbuckets <= kDispatchLdsBuckets;
@@ -413,11 +423,19 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(const int32_t* __rest
     }
     __syncthreads();
   }
-  moba_for_each_pair(blk, r0, r1, m, topk, [&](int32_t row, int s, const MobaRow& mr, int32_t b) {
-    const int32_t bk = mr.bucket0 + b;
-    const int32_t pos = use_lds ? base_of[bk] + atomicAdd(&loc[bk], 1) : atomicAdd(&cursor[bk], 1);
-    entries[pos] = make_int2(row * 16 + s, mr.qrow);
-  });
+  // slots that are not dispatched get no partial: their lse is set to -inf
+  // here (part_lse may be NULL), so the current-block pass weights them 0
+  const int km = topk - 1;
+  moba_for_each_pair(
+      blk, r0, r1, m, topk,
+      [&](int32_t row, int s, const MobaRow& mr, int32_t b) {
+        const int32_t bk = mr.bucket0 + b;
+        const int32_t pos = use_lds ? base_of[bk] + atomicAdd(&loc[bk], 1) : atomicAdd(&cursor[bk], 1);
+        entries[pos] = make_int2(row * 16 + s, mr.qrow);
+      },
+      [&](int32_t row, int s) {
+        if (part_lse) part_lse[(int64_t)row * km + s] = -__builtin_inff();
+      });
 }
 
 // Dynamic LDS of the past-block kernels: bf16 staging rows (padded by 8) and
@@ -898,7 +916,7 @@ hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_l
                                 int64_t d, int64_t q_start, int64_t q_len, int block, int topk, int64_t nbc,
                                 int32_t* counts, int32_t* offsets, int32_t* cursor, int2* entries, int4* tiles,
                                 int32_t* ntiles, hipStream_t s, int32_t* wg_counts, int32_t* wg_base,
-                                int32_t* wg_loc) {
+                                int32_t* wg_loc, float* part_lse) {
   const int64_t nrows = batch * q_len * hq;
   const int64_t nbuckets = batch * hkv * nbc;
   const bool stable = wg_counts && wg_base && moba_dispatch_stable_ints(nrows, nbuckets, topk) > 0;
@@ -949,7 +967,7 @@ hipError_t launch_moba_dispatch(const int32_t* blk, int64_t batch, int64_t seq_l
     } else
       hipLaunchKernelGGL(moba_scatter_kernel, dim3(grid), dim3(256), 0, s, blk, (int32_t)nrows, m, topk,
                          (int32_t)nbuckets, (const int32_t*)offsets, cursor, entries,
-                         (const int32_t*)(nbuckets <= kDispatchLdsBuckets ? wg_loc : nullptr));
+                         (const int32_t*)(nbuckets <= kDispatchLdsBuckets ? wg_loc : nullptr), part_lse);
     e = hipGetLastError();
   }
   return e;
@@ -981,10 +999,9 @@ static hipError_t launch_moba_attn_d(const bf16* q, const bf16* k, const bf16* v
   if (past) {
     {
       KTimer tm("moba_past_attn", s);
-      // partial lse of slots that get no partial stay -inf (read by the
-      // current-block pass without consulting the gating)
-      e = launch_fill_i32((int32_t*)part_lse, batch * q_len * hq * (topk - 1), (int32_t)0xff800000u, s);
-      if (e != hipSuccess) return e;
+      // every (row, slot) lse is written before the current-block pass reads
+      // it without consulting the gating: by this pass for the dispatched
+      // slots, as -inf by the dispatch's scatter for the others
       if (block % (2 * kKT) == 0 && (int64_t)block * hkv * D * 2 < (1ll << 31)) {
         // persistent grid: the workgroups that fit at once (256 CUs x 8 waves), never more than the tiles
         const int64_t grid = std::min<int64_t>(max_tiles, 2048 / kNW);
