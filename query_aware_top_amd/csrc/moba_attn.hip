@@ -771,9 +771,9 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
   // halves at the end), o = sum of 2^(lse - m) o_p. The lane's accumulator
   // holds d = 32 tq + 8 gi + 4 hl + 0..3. These loads are younger than the
   // tiles', so waiting for them costs no extra latency. Every (row, slot)
-  // partial lse is -inf unless the slot's block was dispatched (the lse
-  // array is cleared before the past-block pass), so the loads need no look
-  // at the gating; the o rows of such slots were never written (whatever the
+  // partial lse is -inf unless the slot's block was dispatched (the
+  // dispatch's scatter writes -inf for the slots it leaves out), so the
+  // loads need no look at the gating; the o rows of such slots were never written (whatever the
   // workspace held, NaN included) and are replaced by zeros as they load.
   auto unpack = [](const uint2 u, float* f) {
     f[0] = __builtin_bit_cast(float, u.x << 16);
