@@ -50,6 +50,10 @@ SMALL = [
     (3, 3001, 8, 2, 128, 16, 1024, 3000, 1),    # one new row per sequence (decode-like), GQA 4:1
     (1, 1500, 2, 2, 64, 128, 64, 0, None),      # window shorter than a group
     (2, 4097, 4, 4, 128, 32, 512, 4000, 97),    # ragged tail rows over several tiles' worth of core tokens
+    (1, 100, 2, 2, 128, 128, 64, 0, None),      # group longer than the sequence: no core token exists
+    (1, 256, 2, 1, 64, 256, 0, 0, None),        # one group spanning the sequence, w = 0
+    (1, 700, 8, 1, 64, 16, 100, 0, None),       # 8 query heads per KV head, d 64
+    (1, 999, 4, 2, 128, 3, 17, 0, None),        # odd group size and window
 ]
 
 
