@@ -105,8 +105,9 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
   const bf16* kb = kc + (bi * ctx_len * H + h) * D;
   const bf16* vb = vc + (bi * ctx_len * H + h) * D;
   // one key segment: the gathered keys (all before the chunk, never masked)
-  // followed by the chunk's own keys under the causal mask; positions come
-  // from the key list built by esa_keylist_kernel
+  // followed by the chunk's own keys under the causal mask; positions are
+  // built here in LDS when they fit, else read from the key list built by
+  // esa_keylist_kernel
   const int HD = (int)(H * D);
   const int ng = (int)kl.count();
   const int32_t* lst = keylist + lv * keylist_stride;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 8 / kNW) void esa_prefill_kernel(
   const int nkeys = ng + (int)(i_last + 1);
   extern __shared__ int32_t s_list[];
   if constexpr (LIST_LDS) {
-    for (int j = threadIdx.x; j < nkeys; j += kThreads) s_list[j] = lst[j];
+    for (int j = threadIdx.x; j < nkeys; j += kThreads) s_list[j] = (int32_t)(j < ng ? kl.pos(j) : c0 + (j - ng));
     __syncthreads();
   }
   fa_segment<D, kNW, true>(st, sm, kb, vb, nkeys, scale_log2,
@@ -348,13 +349,15 @@ hipError_t launch_esa_prefill_attn(const void* q, const void* k, const void* v, 
                                    int64_t window, int topk, float scale, bool per_head, hipStream_t s) {
   const int64_t kls = esa_keylist_len(n_init, topk, window, m);
   const int64_t nsel = per_head ? batch * H : batch;
-  hipLaunchKernelGGL(esa_keylist_kernel, dim3((unsigned)cdiv(kls, 256), (unsigned)nsel), dim3(256), 0, s, sel,
-                     n_sel, keylist, kls, topk, c0, m, n_init, window);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const bool lds = kls <= kEsaListLds;
+  if (!lds) {   // the attention kernel builds a list that fits in LDS itself
+    hipLaunchKernelGGL(esa_keylist_kernel, dim3((unsigned)cdiv(kls, 256), (unsigned)nsel), dim3(256), 0, s, sel,
+                       n_sel, keylist, kls, topk, c0, m, n_init, window);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dim3 grid((unsigned)(cdiv(m, kRows) * H * batch));
   const float sl2 = scale * kLog2e;
-  const bool lds = kls <= kEsaListLds;
   const size_t dyn = lds ? (size_t)kls * sizeof(int32_t) : 0;
 #define QAT_ESA_PF(D_, L_)                                                                                  \
   launch_timed("esa_prefill_attn", esa_prefill_kernel<D_, L_>, grid, dim3(kThreads), (uint32_t)dyn, s,       \
