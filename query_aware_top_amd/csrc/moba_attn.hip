@@ -718,7 +718,9 @@ __global__ __launch_bounds__(64 * kCurNW, 2) void moba_current_kernel(
   constexpr int THREADS = 64 * NW;
   QAT_FA_SMEM(D, sm);
   int64_t id = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int tt = (int)(id % tiles_per_block);
+  // a block's last token tiles attend the most keys: they are dispatched
+  // first, so the launch ends on short tiles
+  const int tt = tiles_per_block - 1 - (int)(id % tiles_per_block);
   id /= tiles_per_block;
   const int64_t cb = id % nblocks;
   id /= nblocks;
