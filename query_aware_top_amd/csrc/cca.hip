@@ -120,7 +120,9 @@ __global__ __launch_bounds__(kCcaThreads, 1) void cca_attn_kernel(
   QAT_FA_SMEM(D, sm);
   int64_t id = xcd_logical_id(blockIdx.x, gridDim.x);
   const int64_t ntile = cdiv(q_len, kCcaRows);
-  const int64_t rt = id % ntile;
+  // later row tiles attend more core tokens: they are dispatched first, so
+  // the launch ends on short tiles
+  const int64_t rt = ntile - 1 - id % ntile;
   id /= ntile;
   const int64_t h = id % hq, bi = id / hq;
   const int64_t g = h / (hq / hkv);

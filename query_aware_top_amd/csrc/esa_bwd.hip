@@ -43,7 +43,8 @@ __global__ __launch_bounds__(64 * kBwdNW, 1) void esa_bwd_dq_kernel(
   QAT_FA_SMEM(D, sm);
   int64_t id = xcd_logical_id(blockIdx.x, gridDim.x);
   const int64_t ntile = cdiv(m, kEsaBwdRows);
-  const int64_t qt = id % ntile;
+  // later row tiles attend more of the chunk's keys: dispatched first
+  const int64_t qt = ntile - 1 - id % ntile;
   id /= ntile;
   const int64_t h = id % H, bi = id / H;
   const int64_t i0 = qt * kEsaBwdRows;
