@@ -296,9 +296,10 @@ hipError_t launch_compress_bf16_rows(const void* x, int64_t n, int64_t x_stride,
 }
 
 int compress_splits(int64_t n, int64_t d_model, int64_t d_c) {
-  // about 4096 waves, chunks of at least 64 k
+  // about 2048 waves (two per SIMD; 4096 and 8192 measured slower, 1024 the
+  // same, 512 much slower at 2048 rows x 4096 -> 128), chunks of at least 64 k
   const int64_t waves = cdiv(n, 16) * cdiv(d_c, kCmpCols);
-  int64_t ns = cdiv(4096, waves);
+  int64_t ns = cdiv(2048, waves);
   const int64_t max_ns = d_model / 64 > 0 ? d_model / 64 : 1;
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
