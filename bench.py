@@ -68,6 +68,13 @@ STAGE_SOURCES = {
     "esa_decode_scan": ["esa_select.hip"],
     "esa_prefill_attn": ["esa_attn.hip", "attn_core.h"],
     "esa_decode_attn": ["esa_attn.hip"],
+    # helper kernels that have counter rows of their own
+    "fill_i32": ["moba_attn.hip"],
+    "esa_rowmax": ["esa_select.hip"],
+    "esa_keylist": ["esa_attn.hip"],
+    "esa_decode_combine": ["esa_attn.hip"],
+    "moba_bwd_runs": ["moba_bwd.hip"],
+    "moba_bwd_kv_reduce": ["moba_bwd.hip"],
 }
 
 
