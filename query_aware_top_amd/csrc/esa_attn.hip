@@ -292,9 +292,10 @@ __global__ void esa_decode_combine_kernel(const float* __restrict__ po, const fl
   if (c0 > n_init) n_l = c0 - max(n_init, c0 - window);
   const int64_t nkeys = n_i + n_sel[ph ? bi * H : bi] + n_l + 1;
   const int ns = (int)min((int64_t)nsplit_max, cdiv(nkeys, kps));
-  // online log-sum-exp merge over the splits, 32 splits' loads in flight
-  // (one round at the usual split counts)
-  constexpr int U = 32;
+  // online log-sum-exp merge over the splits, 8 splits' loads per round
+  // (measured at 32 splits per sequence: rounds of 8 or 4 beat one round of
+  // 32 or two of 16 by 2-5 us per decode step; rounds of 2 are slower)
+  constexpr int U = 8;
   float M = -__builtin_inff(), L = 0.f, O = 0.f;
   for (int s0 = 0; s0 < ns; s0 += U) {
     float mv[U], lv[U], ov[U];
