@@ -167,7 +167,7 @@ int esa_decode_keys_per_split(int64_t batch, int64_t nkeys_max) {
   }
   return 64;
 }
-constexpr int kDecUnroll = 4;
+constexpr int kDecUnroll = 6;   // keys per batch (4: 1-2 us slower per decode step, 2: slower still)
 constexpr int kDecMaxKps = 256;
 
 // The split's key positions are staged in LDS first ([lists][kps], one list,
